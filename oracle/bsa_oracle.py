@@ -1,0 +1,415 @@
+"""Plain float64 reference for block-sparse landmark attention (numpy only).
+
+TEST INFRASTRUCTURE ONLY -- imported by the tests, the smoke check and the benchmark's
+CPU-baseline leg, never by the product path.  Page titles are listed in oracle/__init__.py.
+
+What is computed, step by step, in the pages' order:
+
+1. landmarks   -- neighbouring keys pooled into one vector per block (LSA page, "The index
+                  stops scanning the whole context", paragraph 3: neighbouring keys are merged
+                  first to make indexing cheaper; the HiLS page names such per-chunk vectors
+                  "landmarks").  The pooling is the mean over a block of 64 tokens, stored in
+                  the input dtype (round-to-nearest-even).
+2. selector    -- one query vector per (kv group, query block): the mean of the block's queries,
+                  summed over the query heads that share the kv head.  Kept in float64.
+3. scores      -- selector . landmark for every block up to the current one (SAS page, summary
+                  paragraph 1: a light selector scores the units of context; LSA page, first
+                  section, paragraph 2: the indexer scores each contiguous block).
+4. selection   -- hard top-K over the scores (SAS page, summary paragraph 1, and "How to apply":
+                  hard top-K is what inference uses), plus the start of the context and a recent
+                  window that are always attended (LSA page, first section, paragraph 4), the
+                  current block always kept (SAS page, summary paragraph 3).  Ties: lower block
+                  index wins.
+5. SAS gate    -- a continuous selector score turned into a log-form gate that sits inside the
+                  softmax and is normalised against the always-kept current block (SAS page,
+                  summary paragraph 3 and "Key facts" item 3): g_j = log sigmoid(S_j - S_c).
+6. attention   -- softmax over the attended keys (blocks of A_c, causal inside the current
+                  block), with the gate added to every logit of its block.
+7. HiLS        -- each query attends to each selected chunk on its own, then the chunk outputs
+                  are merged with weights equal to the chunks' retrieval scores (HiLS page,
+                  summary paragraph 2); the retrieval score is softmax_j(q . L_j / sqrt(D)).
+
+Readings taken where the pages are silent (each is listed in the design notes):
+* the selector vector is kept in float64 here (float32 on the device), never rounded to bf16;
+* the selector score carries no 1/sqrt(D) (ranking does not depend on it);
+* K counts the extra blocks beyond the sink and the local window: candidates are the blocks
+  j with n_sink <= j <= c - n_local;
+* the SAS gate is added after the logits are scaled by 1/sqrt(D); the current block's gate
+  is 0; every other attended block (sink, local, top-K) is gated;
+* HiLS retrieval scores use each token's own query of its own head, scaled by 1/sqrt(D),
+  softmax-normalised over all attended chunks, with the current chunk's full-block landmark;
+* a partial last block (T not a multiple of 64) pools over the tokens present.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+BLOCK = 64
+
+
+# --------------------------------------------------------------------------------------
+# rounding to the input dtype
+# --------------------------------------------------------------------------------------
+
+def round_to_dtype(x, dtype: str) -> np.ndarray:
+    """Round float64 values to the nearest value of `dtype` ("f32" or "bf16"), ties to even.
+
+    The result is returned as float64 holding exactly representable values of `dtype`.
+    bf16 keeps 8 significant bits (1 implicit + 7 stored) with float32's exponent range.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if dtype == "f32":
+        return x.astype(np.float32).astype(np.float64)
+    if dtype != "bf16":
+        raise ValueError(f"unknown dtype {dtype!r}")
+    out = np.empty_like(x)
+    finite = np.isfinite(x)
+    xf = x[finite]
+    mant, expo = np.frexp(xf)                     # xf = mant * 2**expo, 0.5 <= |mant| < 1
+    # below the smallest normal (2**-126) the quantum is fixed at 2**-133
+    expo = np.maximum(expo, -125)
+    q = np.ldexp(np.rint(np.ldexp(xf, 8 - expo)), expo - 8)   # np.rint rounds half to even
+    q = np.where(np.abs(q) > 3.3895313892515355e38, np.copysign(np.inf, xf), q)
+    out[finite] = q
+    out[~finite] = x[~finite]
+    return out
+
+
+# --------------------------------------------------------------------------------------
+# 1. landmarks
+# --------------------------------------------------------------------------------------
+
+def n_blocks(T: int, block: int = BLOCK) -> int:
+    return (T + block - 1) // block
+
+
+def landmarks(k: np.ndarray, dtype: str, block: int = BLOCK) -> np.ndarray:
+    """L[b,h,j,:] = mean of k[b,h,t,:] over the tokens t of block j, rounded to `dtype`.
+
+    LSA page, "The index stops scanning the whole context", paragraph 3 (neighbouring keys
+    are pooled before indexing); the pooling is the block mean.  k: [B,H,T,D] float64.
+    """
+    B, H, T, D = k.shape
+    NB = n_blocks(T, block)
+    L = np.empty((B, H, NB, D), dtype=np.float64)
+    for j in range(NB):
+        lo, hi = j * block, min((j + 1) * block, T)
+        L[:, :, j, :] = k[:, :, lo:hi, :].mean(axis=2)
+    return round_to_dtype(L, dtype)
+
+
+# --------------------------------------------------------------------------------------
+# 2. selector vectors
+# --------------------------------------------------------------------------------------
+
+def selector_vectors(q: np.ndarray, n_kv_heads: int, block: int = BLOCK) -> np.ndarray:
+    """qbar[b,g,c,:] = sum over the query heads h of kv group g of mean_{t in block c} q[b,h,t,:].
+
+    Query head h belongs to kv group h // (Hq / Hkv).  q: [B,Hq,T,D] float64.  Float64 result,
+    not rounded.
+    """
+    B, Hq, T, D = q.shape
+    G = Hq // n_kv_heads
+    NQB = n_blocks(T, block)
+    qbar = np.zeros((B, n_kv_heads, NQB, D), dtype=np.float64)
+    for c in range(NQB):
+        lo, hi = c * block, min((c + 1) * block, T)
+        m = q[:, :, lo:hi, :].mean(axis=2)              # [B,Hq,D]
+        qbar[:, :, c, :] = m.reshape(B, n_kv_heads, G, D).sum(axis=2)
+    return qbar
+
+
+def decode_selector_vectors(q: np.ndarray, n_kv_heads: int) -> np.ndarray:
+    """Decode: the one query token per sequence, summed over the heads of each kv group.
+
+    q: [B,Hq,D] -> [B,Hkv,D] float64.
+    """
+    B, Hq, D = q.shape
+    G = Hq // n_kv_heads
+    return q.reshape(B, n_kv_heads, G, D).sum(axis=2)
+
+
+# --------------------------------------------------------------------------------------
+# 3. scores
+# --------------------------------------------------------------------------------------
+
+def block_scores(qbar: np.ndarray, L: np.ndarray) -> np.ndarray:
+    """S[..., c, j] = qbar[..., c, :] . L[..., j, :] in float64 (a plain matrix product).
+
+    SAS page, summary paragraph 1 (a light selector scores each unit of context); LSA page,
+    first section, paragraph 2 (each contiguous block is scored).  Entries with j > c are
+    computed too but are never read.
+    """
+    return np.matmul(qbar, np.swapaxes(L, -1, -2))
+
+
+# --------------------------------------------------------------------------------------
+# 4. selection
+# --------------------------------------------------------------------------------------
+
+def select_row(s_row: np.ndarray, c: int, topk: int, n_sink: int = 1, n_local: int = 2):
+    """Attended block set A_c of query block c, ascending, and the scores aligned with it.
+
+    * hard top-K over the selector scores (SAS page, summary paragraph 1; "How to apply");
+    * the start of the context (n_sink blocks) and a recent window (n_local blocks ending
+      at the current one) are always attended (LSA page, first section, paragraph 4);
+    * the current block c is always kept (SAS page, summary paragraph 3).
+    Candidates are the blocks j with n_sink <= j <= c - n_local; they are ranked by score,
+    descending, and among equal scores the lower block index ranks first.
+    """
+    s_row = np.asarray(s_row, dtype=np.float64)
+    sink = set(range(0, min(n_sink, c + 1)))
+    local = set(range(max(0, c - n_local + 1), c + 1))
+    cand = np.arange(n_sink, c - n_local + 1, dtype=np.int64)
+    if cand.size:
+        # np.lexsort sorts by the last key first: primary -score (descending), then index
+        order = np.lexsort((cand, -s_row[cand]))
+        top = set(cand[order[: min(topk, cand.size)]].tolist())
+    else:
+        top = set()
+    A = np.array(sorted(sink | local | top), dtype=np.int64)
+    return A, s_row[A]
+
+
+def select_all(S: np.ndarray, topk: int, n_sink: int = 1, n_local: int = 2, row_blocks=None):
+    """Selection for every row of S[B,G,R,NB].
+
+    row_blocks[r] is the query block index c of row r (prefill: r itself; decode: the block of
+    the last token).  Returns idx [B,G,R,NA] int64 padded with -1 and sc [B,G,R,NA] float64
+    (NaN in the padding), NA = n_sink + n_local + topk.
+    """
+    B, G, R, NB = S.shape
+    NA = n_sink + n_local + topk
+    if row_blocks is None:
+        row_blocks = list(range(R))
+    idx = np.full((B, G, R, NA), -1, dtype=np.int64)
+    sc = np.full((B, G, R, NA), np.nan, dtype=np.float64)
+    for b in range(B):
+        for g in range(G):
+            for r in range(R):
+                A, sA = select_row(S[b, g, r], row_blocks[r], topk, n_sink, n_local)
+                idx[b, g, r, : A.size] = A
+                sc[b, g, r, : A.size] = sA
+    return idx, sc
+
+
+# --------------------------------------------------------------------------------------
+# 5. SAS gate
+# --------------------------------------------------------------------------------------
+
+def log_sigmoid(x) -> np.ndarray:
+    """log(1 / (1 + exp(-x))), evaluated without overflow on either side."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.where(x >= 0, -np.log1p(np.exp(-np.abs(x))), x - np.log1p(np.exp(-np.abs(x))))
+
+
+def sas_gates(A: np.ndarray, sA: np.ndarray, c: int) -> np.ndarray:
+    """Gate per attended block: log sigmoid(S_j - S_c) for j != c, 0 for the current block.
+
+    SAS page, summary paragraph 3 and "Key facts" item 3: the continuous selector score enters
+    the softmax in log form, normalised so that earlier context is compared with the current
+    block, which is always kept.
+    """
+    A = np.asarray(A)
+    sA = np.asarray(sA, dtype=np.float64)
+    s_c = sA[np.nonzero(A == c)[0][0]]
+    g = log_sigmoid(sA - s_c)
+    g[A == c] = 0.0
+    return g
+
+
+# --------------------------------------------------------------------------------------
+# 6. attention (PLAIN / SAS)
+# --------------------------------------------------------------------------------------
+
+def _block_keys(A, T: int, block: int):
+    """Key positions of the attended blocks (ascending) and the block of each position."""
+    pos, blk = [], []
+    for j in A:
+        lo, hi = int(j) * block, min((int(j) + 1) * block, T)
+        pos.extend(range(lo, hi))
+        blk.extend([int(j)] * (hi - lo))
+    return np.array(pos, dtype=np.int64), np.array(blk, dtype=np.int64)
+
+
+def attend_rows(qrows, tpos, K, V, A, gates, scale: float, block: int = BLOCK):
+    """Softmax attention of query rows over the keys of the attended blocks.
+
+    qrows [m,D] (rows of one head), tpos [m] their token positions, K/V [T,D] that head's kv
+    group, A the attended blocks, gates aligned with A (zeros for PLAIN).  For row t the
+    visible keys are u in the blocks of A with u <= t; logit = scale * q.k_u + gate(block(u)).
+    Returns out [m,D] and lse [m] = log sum_u exp(logit_u).
+    """
+    T = K.shape[0]
+    pos, blk = _block_keys(A, T, block)
+    gate_of = dict(zip([int(a) for a in A], np.asarray(gates, dtype=np.float64)))
+    gvec = np.array([gate_of[int(j)] for j in blk], dtype=np.float64)
+    logits = scale * (qrows @ K[pos].T) + gvec[None, :]            # [m, |U|]
+    visible = pos[None, :] <= np.asarray(tpos)[:, None]
+    logits = np.where(visible, logits, -np.inf)
+    mx = logits.max(axis=1, keepdims=True)
+    e = np.exp(logits - mx)
+    den = e.sum(axis=1, keepdims=True)
+    out = (e / den) @ V[pos]
+    lse = (mx + np.log(den))[:, 0]
+    return out, lse
+
+
+# --------------------------------------------------------------------------------------
+# 7. HiLS
+# --------------------------------------------------------------------------------------
+
+def hils_chunks(qrows, tpos, K, V, A, scale: float, block: int = BLOCK):
+    """Per-chunk attention: each query attends to each attended chunk on its own.
+
+    HiLS page, summary paragraph 2 (each query first looks at each selected chunk
+    independently).  Returns o_j [m,|A|,D] (softmax over the visible keys of chunk j only) and
+    lse_j [m,|A|].  Every chunk in A holds at least one visible key for every row, because the
+    current chunk contains the row's own position.
+    """
+    m = qrows.shape[0]
+    o = np.zeros((m, len(A), V.shape[1]))
+    lse = np.zeros((m, len(A)))
+    for i, j in enumerate(A):
+        o[:, i, :], lse[:, i] = attend_rows(qrows, tpos, K, V, [j], [0.0], scale, block)
+    return o, lse
+
+
+def attend_hils_rows(qrows, tpos, K, V, Lrows, A, scale: float, block: int = BLOCK):
+    """HiLS output: o = sum_j w_j o_j with w = softmax_j(scale * q . L_j) over attended chunks.
+
+    HiLS page, summary paragraph 2: the chunk results are combined with weights equal to the
+    chunks' retrieval scores.  Lrows [|A|,D] are the landmarks of the chunks in A.
+    """
+    o_j, _ = hils_chunks(qrows, tpos, K, V, A, scale, block)
+    r = scale * (qrows @ Lrows.T)                                    # [m, |A|]
+    w = np.exp(r - r.max(axis=1, keepdims=True))
+    w = w / w.sum(axis=1, keepdims=True)
+    return np.einsum("ma,mad->md", w, o_j)
+
+
+# --------------------------------------------------------------------------------------
+# whole path
+# --------------------------------------------------------------------------------------
+
+def _default_scale(D, scale):
+    return 1.0 / math.sqrt(D) if not scale else float(scale)
+
+
+def prefill_rows(q, k, v, rows, *, topk: int, mode: str, dtype: str, block: int = BLOCK,
+                 n_sink: int = 1, n_local: int = 2, scale=None, idx=None, lm=None, qbar=None):
+    """Prefill outputs for a subset of (b, g, c) rows: all query heads of group g, block c.
+
+    q [B,Hq,T,D], k/v [B,Hkv,T,D] float64 holding the exact input values.  `rows` is a list of
+    (b, g, c).  If `idx` [B,Hkv,NQB,NA] is given, those attended sets are used instead of the
+    oracle's own selection (scores and gates still come from the oracle's own landmarks and
+    selector vectors).  Returns a dict of per-row results keyed by (b, g, c):
+    {"A", "sA", "out" [G,nrows,D], "lse" [G,nrows] (PLAIN/SAS)}.
+    """
+    B, Hq, T, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    sc_ = _default_scale(D, scale)
+    if lm is None:
+        lm = landmarks(k, dtype, block)
+    if qbar is None:
+        qbar = selector_vectors(q, Hkv, block)
+    res = {}
+    for (b, g, c) in rows:
+        s_row = block_scores(qbar[b, g, c][None, :], lm[b, g])[0]     # [NB]
+        if idx is None:
+            A, sA = select_row(s_row, c, topk, n_sink, n_local)
+        else:
+            A = np.array([j for j in idx[b, g, c] if j >= 0], dtype=np.int64)
+            sA = s_row[A]
+        lo, hi = c * block, min((c + 1) * block, T)
+        tpos = np.arange(lo, hi)
+        outs, lses = [], []
+        for hh in range(G):
+            h = g * G + hh
+            qr = q[b, h, lo:hi]
+            if mode == "hils":
+                o = attend_hils_rows(qr, tpos, k[b, g], v[b, g], lm[b, g][A], A, sc_, block)
+                lse = np.full(hi - lo, np.nan)
+            else:
+                gates = sas_gates(A, sA, c) if mode == "sas" else np.zeros(len(A))
+                o, lse = attend_rows(qr, tpos, k[b, g], v[b, g], A, gates, sc_, block)
+            outs.append(o)
+            lses.append(lse)
+        res[(b, g, c)] = {"A": A, "sA": sA, "out": np.stack(outs), "lse": np.stack(lses)}
+    return res
+
+
+def prefill(q, k, v, *, topk: int, mode: str, dtype: str, block: int = BLOCK, n_sink: int = 1,
+            n_local: int = 2, scale=None, idx=None):
+    """Whole prefill pass: landmarks, selector vectors, scores, selection and attention.
+
+    Returns a dict with lm [B,Hkv,NB,D], qbar [B,Hkv,NQB,D], S [B,Hkv,NQB,NB], idx/sc
+    [B,Hkv,NQB,NA], out [B,Hq,T,D] and lse [B,Hq,T] (NaN for HiLS).
+    """
+    B, Hq, T, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    NQB = n_blocks(T, block)
+    lm = landmarks(k, dtype, block)
+    qbar = selector_vectors(q, Hkv, block)
+    S = block_scores(qbar, lm)
+    own_idx, own_sc = select_all(S, topk, n_sink, n_local)
+    rows = [(b, g, c) for b in range(B) for g in range(Hkv) for c in range(NQB)]
+    per = prefill_rows(q, k, v, rows, topk=topk, mode=mode, dtype=dtype, block=block,
+                       n_sink=n_sink, n_local=n_local, scale=scale, idx=idx, lm=lm, qbar=qbar)
+    out = np.zeros((B, Hq, T, D))
+    lse = np.zeros((B, Hq, T))
+    for (b, g, c), r in per.items():
+        lo, hi = c * block, min((c + 1) * block, T)
+        out[b, g * G:(g + 1) * G, lo:hi] = r["out"]
+        lse[b, g * G:(g + 1) * G, lo:hi] = r["lse"]
+    return {"lm": lm, "qbar": qbar, "S": S, "idx": own_idx, "sc": own_sc, "out": out, "lse": lse}
+
+
+def decode(q, kc, vc, lm, *, topk: int, mode: str, block: int = BLOCK, n_sink: int = 1,
+           n_local: int = 2, scale=None, idx=None, seqs=None, groups=None):
+    """Decode step: the query is the last cached token (position Tk - 1) of each sequence.
+
+    q [B,Hq,D]; kc/vc [B,Hkv,Tk,D] (the cache includes the query's own key and value);
+    lm [B,Hkv,NB,D] the pooled cache.  Selection uses the heads of each kv group summed;
+    attention covers every key of the attended blocks (all are at or before Tk - 1).
+    Optional `seqs`/`groups` restrict the (b, g) pairs computed.  Returns a dict with
+    idx/sc [B,Hkv,NA] (for the computed pairs), out [B,Hq,D] and lse [B,Hq].
+    """
+    B, Hq, D = q.shape
+    Hkv, Tk = kc.shape[1], kc.shape[2]
+    G = Hq // Hkv
+    sc_ = _default_scale(D, scale)
+    c = (Tk - 1) // block
+    qbar = decode_selector_vectors(q, Hkv)
+    NA = n_sink + n_local + topk
+    out_idx = np.full((B, Hkv, NA), -1, dtype=np.int64)
+    out_sc = np.full((B, Hkv, NA), np.nan)
+    out = np.full((B, Hq, D), np.nan)
+    lse = np.full((B, Hq), np.nan)
+    for b in (range(B) if seqs is None else seqs):
+        for g in (range(Hkv) if groups is None else groups):
+            s_row = block_scores(qbar[b, g][None, :], lm[b, g])[0]
+            if idx is None:
+                A, sA = select_row(s_row, c, topk, n_sink, n_local)
+            else:
+                A = np.array([j for j in idx[b, g] if j >= 0], dtype=np.int64)
+                sA = s_row[A]
+            out_idx[b, g, : A.size] = A
+            out_sc[b, g, : A.size] = sA
+            for hh in range(G):
+                h = g * G + hh
+                qr = q[b, h][None, :]
+                tpos = np.array([Tk - 1])
+                if mode == "hils":
+                    o = attend_hils_rows(qr, tpos, kc[b, g], vc[b, g], lm[b, g][A], A, sc_, block)
+                    out[b, h] = o[0]
+                else:
+                    gates = sas_gates(A, sA, c) if mode == "sas" else np.zeros(len(A))
+                    o, l_ = attend_rows(qr, tpos, kc[b, g], vc[b, g], A, gates, sc_, block)
+                    out[b, h], lse[b, h] = o[0], l_[0]
+    return {"idx": out_idx, "sc": out_sc, "out": out, "lse": lse, "qbar": qbar}

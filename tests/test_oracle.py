@@ -1,0 +1,488 @@
+"""Pins of the float64 oracle against things other than itself (CPU only).
+
+Each test names the oracle step it pins and what it is pinned to: a library routine
+(torch's scaled_dot_product_attention in float64, torch's bf16 cast, scipy's log_expit), a
+closed form, an invariant, or brute force in pure Python on tiny inputs.
+"""
+
+import itertools
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle as O
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _sdpa(q, k, v, mask=None, causal=False, scale=None):
+    """torch SDPA in float64 on the CPU; q [H,T,D], k/v [H,Tk,D]."""
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(torch.float64)
+    m = None if mask is None else t(mask)
+    o = torch.nn.functional.scaled_dot_product_attention(
+        t(q), t(k), t(v), attn_mask=m, is_causal=causal, scale=scale)
+    return o.numpy()
+
+
+# ---------------------------------------------------------------------------------------
+# rounding
+# ---------------------------------------------------------------------------------------
+
+def test_bf16_rounding_matches_torch_cast():
+    """round_to_dtype('bf16') == torch's float32 -> bfloat16 cast (RNE) on float32 inputs."""
+    r = _rng(0)
+    x = np.concatenate([
+        r.standard_normal(20000).astype(np.float32),
+        (r.standard_normal(2000) * 1e-30).astype(np.float32),
+        (r.standard_normal(2000) * 1e30).astype(np.float32),
+        # exact ties: 8 significant bits + a half-ulp
+        (np.arange(1, 2001, dtype=np.float64) * 2 + 1).astype(np.float32) * np.float32(2 ** -9),
+        np.array([0.0, -0.0, 1e-40, -3e-39], dtype=np.float32),
+    ])
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    got = O.round_to_dtype(x.astype(np.float64), "bf16")
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_f32_rounding_matches_numpy_cast():
+    x = _rng(1).standard_normal(1000) * 3.3
+    np.testing.assert_array_equal(O.round_to_dtype(x, "f32"), x.astype(np.float32).astype(np.float64))
+
+
+# ---------------------------------------------------------------------------------------
+# step 1: landmarks
+# ---------------------------------------------------------------------------------------
+
+def test_landmark_constant_block_and_shift():
+    """A constant block pools to that constant; adding a vector to a block shifts its landmark."""
+    r = _rng(2)
+    k = O.round_to_dtype(r.standard_normal((1, 2, 256, 8)), "bf16")
+    const = O.round_to_dtype(r.standard_normal(8), "bf16")
+    k[0, 1, 64:128] = const
+    L = O.landmarks(k, "bf16")
+    np.testing.assert_array_equal(L[0, 1, 1], const)
+    k2 = k.copy()
+    shift = np.array([0.5, -1.0, 2.0, 0.25, 0.0, 1.0, -0.5, 4.0])
+    k2[0, 0, 128:192] += shift
+    L2 = O.landmarks(k2, "f32")
+    L1 = O.landmarks(k, "f32")
+    np.testing.assert_allclose(L2[0, 0, 2] - L1[0, 0, 2], shift, atol=1e-6)
+
+
+def test_landmark_brute_force_loop_and_partial_block():
+    """Landmark == explicit Python-loop mean (including a partial last block), then rounded."""
+    r = _rng(3)
+    T, D = 150, 3
+    k = r.standard_normal((1, 1, T, D))
+    L = O.landmarks(k, "f32")
+    for j in range(3):
+        toks = range(j * 64, min(j * 64 + 64, T))
+        for d in range(D):
+            s = math.fsum(k[0, 0, t, d] for t in toks) / len(toks)
+            assert L[0, 0, j, d] == float(np.float32(s))
+
+
+# ---------------------------------------------------------------------------------------
+# step 2/3: selector vectors and scores
+# ---------------------------------------------------------------------------------------
+
+def test_selector_vector_brute_force():
+    r = _rng(4)
+    B, Hq, Hkv, T, D = 2, 4, 2, 130, 3
+    q = r.standard_normal((B, Hq, T, D))
+    qb = O.selector_vectors(q, Hkv)
+    for b, g, c, d in itertools.product(range(B), range(Hkv), range(3), range(D)):
+        toks = list(range(c * 64, min(c * 64 + 64, T)))
+        heads = [g * 2, g * 2 + 1]
+        s = math.fsum(math.fsum(q[b, h, t, d] for t in toks) / len(toks) for h in heads)
+        assert abs(qb[b, g, c, d] - s) < 1e-13
+    qd = O.decode_selector_vectors(q[:, :, 0], Hkv)
+    np.testing.assert_allclose(qd[1, 1], q[1, 2, 0] + q[1, 3, 0], rtol=0, atol=1e-15)
+
+
+def test_scores_permutation_invariant():
+    """Permuting the D coordinates of selector and landmark together leaves scores unchanged."""
+    r = _rng(5)
+    qb = r.standard_normal((1, 1, 5, 16))
+    L = r.standard_normal((1, 1, 5, 16))
+    p = r.permutation(16)
+    np.testing.assert_allclose(O.block_scores(qb[..., p], L[..., p]), O.block_scores(qb, L), atol=1e-13)
+    S = O.block_scores(qb, L)
+    assert abs(S[0, 0, 3, 2] - math.fsum(qb[0, 0, 3] * L[0, 0, 2])) < 1e-13
+
+
+# ---------------------------------------------------------------------------------------
+# step 4: selection
+# ---------------------------------------------------------------------------------------
+
+def _brute_select(s, c, K, n_sink, n_local):
+    """Rank counting: candidate j is chosen iff fewer than K candidates beat it, where i beats j
+    when S_i > S_j, or S_i == S_j and i < j."""
+    cands = [j for j in range(n_sink, c - n_local + 1)]
+    chosen = []
+    for j in cands:
+        beats = sum(1 for i in cands if (s[i] > s[j]) or (s[i] == s[j] and i < j))
+        if beats < K:
+            chosen.append(j)
+    forced = set(range(min(n_sink, c + 1))) | set(range(max(0, c - n_local + 1), c + 1))
+    return sorted(forced | set(chosen))
+
+
+@pytest.mark.parametrize("n_sink,n_local", [(1, 2), (0, 1), (2, 3), (1, 1)])
+def test_selection_brute_force_with_ties(n_sink, n_local):
+    r = _rng(6)
+    for trial in range(300):
+        n = int(r.integers(1, 20))
+        s = r.integers(-3, 4, size=n).astype(np.float64)      # many exact ties
+        c = int(r.integers(0, n))
+        K = int(r.integers(0, n + 2))
+        A, sA = O.select_row(s, c, K, n_sink, n_local)
+        assert A.tolist() == _brute_select(s, c, K, n_sink, n_local)
+        np.testing.assert_array_equal(sA, s[A])
+
+
+def test_tie_rule_lower_index_wins():
+    """Identical landmarks give equal scores: the lowest candidate indices are chosen."""
+    r = _rng(7)
+    T, D = 64 * 12, 4
+    k = np.tile(O.round_to_dtype(r.standard_normal((1, 1, 1, D)), "bf16"), (1, 1, T, 1))
+    q = r.standard_normal((1, 1, T, D))
+    res = O.prefill(q, k, k, topk=3, mode="plain", dtype="bf16")
+    assert res["idx"][0, 0, 11].tolist() == [0, 1, 2, 3, 10, 11]
+
+
+def test_sink_and_local_always_selected_and_sizes():
+    r = _rng(8)
+    S = r.standard_normal((1, 1, 40, 40))
+    idx, sc = O.select_all(S, topk=5)
+    for c in range(40):
+        row = [j for j in idx[0, 0, c] if j >= 0]
+        assert 0 in row and c in row and (c < 1 or c - 1 in row)
+        assert len(row) == min(c + 1, 5 + 3)
+        assert row == sorted(set(row))
+        assert row[-1] == c
+
+
+# ---------------------------------------------------------------------------------------
+# steps 5/6: gate and attention
+# ---------------------------------------------------------------------------------------
+
+def test_log_sigmoid_matches_scipy():
+    x = np.linspace(-60, 60, 24001)
+    np.testing.assert_allclose(O.log_sigmoid(x), scipy.special.log_expit(x), rtol=1e-14, atol=1e-300)
+
+
+def test_gate_closed_forms():
+    A = np.array([0, 3, 7, 8])
+    g = O.sas_gates(A, np.array([1.5, 1.5, 1.5, 1.5]), 8)
+    np.testing.assert_allclose(g, [-math.log(2)] * 3 + [0.0], rtol=1e-15)
+    g = O.sas_gates(A, np.array([1e6, 1e6, 1e6, 0.0]), 8)
+    np.testing.assert_allclose(g, [0.0, 0.0, 0.0, 0.0], atol=1e-300)
+
+
+def _gqa_expand(k, G):
+    return np.repeat(k, G, axis=1)
+
+
+@pytest.mark.parametrize("G", [1, 2])
+def test_dense_limit_equals_causal_sdpa(G):
+    """K >= number of candidates and no gate: the oracle is dense causal attention (SDPA)."""
+    r = _rng(9)
+    B, Hkv, T, D = 1, 2, 64 * 5 + 17, 8
+    q = r.standard_normal((B, Hkv * G, T, D))
+    k = r.standard_normal((B, Hkv, T, D))
+    v = r.standard_normal((B, Hkv, T, D))
+    res = O.prefill(q, k, v, topk=100, mode="plain", dtype="f32")
+    ref = _sdpa(q[0], _gqa_expand(k, G)[0], _gqa_expand(v, G)[0], causal=True)
+    np.testing.assert_allclose(res["out"][0], ref, rtol=0, atol=1e-12)
+    # lse against a direct log-sum-exp of the causal logits (scipy.special.logsumexp)
+    s = np.einsum("htd,hud->htu", q[0], _gqa_expand(k, G)[0]) / math.sqrt(D)
+    s = np.where(np.tril(np.ones((T, T), bool))[None], s, -np.inf)
+    np.testing.assert_allclose(res["lse"][0], scipy.special.logsumexp(s, axis=-1), atol=1e-12)
+
+
+def _mask_from_sets(idx_row_fn, T, gate_fn=None, block=64):
+    """Additive SDPA mask [T,T]: gate on allowed keys, -inf elsewhere."""
+    m = np.full((T, T), -np.inf)
+    for t in range(T):
+        c = t // block
+        A = idx_row_fn(c)
+        for j in A:
+            for u in range(j * block, min(j * block + block, T)):
+                if u <= t:
+                    m[t, u] = 0.0 if gate_fn is None else gate_fn(c, j)
+    return m
+
+
+@pytest.mark.parametrize("mode", ["plain", "sas"])
+def test_sparse_and_sas_equal_masked_sdpa(mode):
+    """Selected blocks + gates: equals SDPA with an additive mask built from the attended sets
+    and gates computed by scipy's log_expit (library routines for softmax-attention and gate)."""
+    r = _rng(10)
+    B, Hq, Hkv, T, D = 1, 2, 1, 64 * 9 + 5, 8
+    q = r.standard_normal((B, Hq, T, D))
+    k = O.round_to_dtype(r.standard_normal((B, Hkv, T, D)), "bf16")
+    v = r.standard_normal((B, Hkv, T, D))
+    res = O.prefill(q, k, v, topk=2, mode=mode, dtype="bf16")
+    idx, S = res["idx"], res["S"]
+
+    def gate(c, j):
+        if mode == "plain" or j == c:
+            return 0.0
+        return float(scipy.special.log_expit(S[0, 0, c, j] - S[0, 0, c, c]))
+
+    mask = _mask_from_sets(lambda c: [j for j in idx[0, 0, c] if j >= 0], T, gate)
+    ref = _sdpa(q[0], _gqa_expand(k, 2)[0], _gqa_expand(v, 2)[0], mask=np.broadcast_to(mask, (Hq, T, T)))
+    np.testing.assert_allclose(res["out"][0], ref, atol=1e-12)
+
+
+def test_sas_equal_scores_halve_history():
+    """Closed form: when every attended block scores like the current one, each earlier block's
+    keys get exactly half their PLAIN exp-mass."""
+    T, D = 64 * 4, 4
+    r = _rng(11)
+    q = r.standard_normal((1, 1, T, D))
+    k = r.standard_normal((1, 1, T, D))
+    v = r.standard_normal((1, 1, T, D))
+    A = np.array([0, 2, 3])
+    c = 3
+    tpos = np.arange(192, 256)
+    gates = O.sas_gates(A, np.zeros(3), c)
+    out, _ = O.attend_rows(q[0, 0, 192:256], tpos, k[0, 0], v[0, 0], A, gates, 0.5)
+    # closed form with explicit weights
+    keys = list(range(0, 64)) + list(range(128, 256))
+    ref = np.zeros((64, D))
+    for i, t in enumerate(tpos):
+        w = np.array([math.exp(0.5 * q[0, 0, t] @ k[0, 0, u]) * (0.5 if u < 192 else 1.0) if u <= t else 0.0
+                      for u in keys])
+        ref[i] = (w / w.sum()) @ v[0, 0, keys]
+    np.testing.assert_allclose(out, ref, atol=1e-12)
+
+
+@pytest.mark.parametrize("mode", ["plain", "sas", "hils"])
+def test_rows_sum_to_one(mode):
+    """V = all ones gives o = 1; V = identity recovers the weight matrix, whose rows sum to 1 and
+    which is zero outside the attended blocks and above the diagonal."""
+    r = _rng(12)
+    T, D = 64 * 4, 6
+    q = r.standard_normal((1, 1, T, D)) * 2
+    k = O.round_to_dtype(r.standard_normal((1, 1, T, D)), "bf16")
+    ones = np.ones((1, 1, T, D))
+    res = O.prefill(q, k, ones, topk=1, mode=mode, dtype="bf16")
+    np.testing.assert_allclose(res["out"], 1.0, atol=1e-14)
+    # identity V needs D == T: use qk with D=6 but V of width T via the row helpers
+    lm = O.landmarks(k, "bf16")
+    eye = np.eye(T)
+    for c in range(4):
+        A = [j for j in res["idx"][0, 0, c] if j >= 0]
+        tpos = np.arange(c * 64, c * 64 + 64)
+        qr = q[0, 0, c * 64:(c + 1) * 64]
+        if mode == "hils":
+            P = O.attend_hils_rows(qr, tpos, k[0, 0], eye, lm[0, 0][A], np.array(A), 1 / math.sqrt(D))
+        else:
+            gates = O.sas_gates(np.array(A), res["sc"][0, 0, c, :len(A)], c) if mode == "sas" else np.zeros(len(A))
+            P, _ = O.attend_rows(qr, tpos, k[0, 0], eye, np.array(A), gates, 1 / math.sqrt(D))
+        np.testing.assert_allclose(P.sum(axis=1), 1.0, atol=1e-14)
+        allowed = np.zeros((64, T), bool)
+        for j in A:
+            allowed[:, j * 64:(j + 1) * 64] = True
+        allowed &= np.arange(T)[None, :] <= tpos[:, None]
+        assert np.all(P[~allowed] == 0.0)
+        assert np.all(P[allowed] > 0.0)
+        # sink and local blocks carry mass in every row (c >= 1)
+        for j in {0, max(c - 1, 0), c}:
+            assert np.all(P[:, j * 64:(j + 1) * 64].sum(axis=1) > 0)
+
+
+def test_linearity_in_v_and_d_permutation():
+    r = _rng(13)
+    T, D = 64 * 5, 8
+    q = r.standard_normal((1, 2, T, D))
+    k = O.round_to_dtype(r.standard_normal((1, 1, T, D)), "bf16")
+    v1 = r.standard_normal((1, 1, T, D))
+    v2 = r.standard_normal((1, 1, T, D))
+    for mode in ["plain", "sas", "hils"]:
+        a = O.prefill(q, k, v1, topk=1, mode=mode, dtype="bf16")["out"]
+        b = O.prefill(q, k, v2, topk=1, mode=mode, dtype="bf16")["out"]
+        ab = O.prefill(q, k, 2 * v1 - 3 * v2, topk=1, mode=mode, dtype="bf16")["out"]
+        np.testing.assert_allclose(ab, 2 * a - 3 * b, atol=1e-12)
+        p = r.permutation(D)
+        pp = O.prefill(q[..., p], k[..., p], v1, topk=1, mode=mode, dtype="bf16")
+        base = O.prefill(q, k, v1, topk=1, mode=mode, dtype="bf16")
+        np.testing.assert_array_equal(pp["idx"], base["idx"])
+        np.testing.assert_allclose(pp["out"], base["out"], atol=1e-12)
+
+
+# ---------------------------------------------------------------------------------------
+# step 7: HiLS
+# ---------------------------------------------------------------------------------------
+
+def test_hils_single_chunk_is_plain_softmax():
+    r = _rng(14)
+    T, D = 64, 8
+    q = r.standard_normal((1, 1, T, D))
+    k = O.round_to_dtype(r.standard_normal((1, 1, T, D)), "bf16")
+    v = r.standard_normal((1, 1, T, D))
+    h = O.prefill(q, k, v, topk=4, mode="hils", dtype="bf16")["out"]
+    ref = _sdpa(q[0], k[0], v[0], causal=True)
+    np.testing.assert_allclose(h[0], ref, atol=1e-12)
+
+
+def test_hils_chunks_merge_by_lse_gives_dense():
+    """Flash merge identity: weighting the per-chunk outputs by softmax(lse_j) instead of the
+    retrieval scores reproduces dense causal attention (SDPA)."""
+    r = _rng(15)
+    T, D = 64 * 4 + 9, 8
+    q = r.standard_normal((T, D))
+    k = r.standard_normal((T, D))
+    v = r.standard_normal((T, D))
+    tpos = np.arange(T)
+    out = np.zeros((T, D))
+    for c in range(5):
+        rows = tpos[c * 64:(c + 1) * 64]
+        o_j, lse_j = O.hils_chunks(q[rows], rows, k, v, np.arange(c + 1), 0.3)
+        w = scipy.special.softmax(lse_j, axis=1)
+        out[rows] = np.einsum("ma,mad->md", w, o_j)
+    ref = _sdpa(q[None], k[None], v[None], causal=True, scale=0.3)[0]
+    np.testing.assert_allclose(out, ref, atol=1e-12)
+
+
+def test_hils_identical_keys_closed_form():
+    """If every key of chunk j equals kappa_j, each chunk's softmax is uniform over its visible
+    keys and the landmark is kappa_j, so o = sum_j softmax_j(q.kappa_j/sqrt(D)) * mean(visible v_j)."""
+    r = _rng(16)
+    NB, D = 5, 4
+    T = NB * 64
+    kap = O.round_to_dtype(r.standard_normal((NB, D)), "bf16")
+    k = np.repeat(kap, 64, axis=0)[None, None]
+    q = r.standard_normal((1, 1, T, D))
+    v = r.standard_normal((1, 1, T, D))
+    res = O.prefill(q, k, v, topk=1, mode="hils", dtype="bf16")
+    for t in [0, 63, 64, 130, 200, 255, 256, 319]:
+        c = t // 64
+        A = [j for j in res["idx"][0, 0, c] if j >= 0]
+        r_ = np.array([q[0, 0, t] @ kap[j] / 2.0 for j in A])
+        w = np.exp(r_ - r_.max())
+        w /= w.sum()
+        means = [v[0, 0, j * 64:min(j * 64 + 64, t + 1)].mean(axis=0) for j in A]
+        ref = sum(wi * m for wi, m in zip(w, means))
+        np.testing.assert_allclose(res["out"][0, 0, t], ref, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------------------
+# brute force of the whole path on tiny inputs (pure Python, math.exp)
+# ---------------------------------------------------------------------------------------
+
+def _brute_path(q, k, v, K, mode, dtype, n_sink=1, n_local=2):
+    B, Hq, T, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    NB = (T + 63) // 64
+    sc = 1 / math.sqrt(D)
+    out = np.zeros_like(q)
+    for b in range(B):
+        for g in range(Hkv):
+            L = []
+            for j in range(NB):
+                toks = range(j * 64, min(j * 64 + 64, T))
+                L.append(O.round_to_dtype(np.array([math.fsum(k[b, g, t, d] for t in toks) / len(toks)
+                                                    for d in range(D)]), dtype))
+            for c in range(NB):
+                toks = range(c * 64, min(c * 64 + 64, T))
+                qb = [math.fsum(math.fsum(q[b, h, t, d] for t in toks) / len(toks)
+                                for h in range(g * G, g * G + G)) for d in range(D)]
+                s = [math.fsum(qb[d] * L[j][d] for d in range(D)) for j in range(NB)]
+                A = _brute_select(s, c, K, n_sink, n_local)
+                for h in range(g * G, g * G + G):
+                    for t in toks:
+                        if mode == "hils":
+                            rr = {j: sc * math.fsum(q[b, h, t, d] * L[j][d] for d in range(D)) for j in A}
+                            mx = max(rr.values())
+                            den = math.fsum(math.exp(x - mx) for x in rr.values())
+                            acc = np.zeros(D)
+                            for j in A:
+                                us = [u for u in range(j * 64, min(j * 64 + 64, T)) if u <= t]
+                                lg = [sc * math.fsum(q[b, h, t, d] * k[b, g, u, d] for d in range(D)) for u in us]
+                                m2 = max(lg)
+                                e = [math.exp(x - m2) for x in lg]
+                                se = math.fsum(e)
+                                oj = sum(ei / se * v[b, g, u] for ei, u in zip(e, us))
+                                acc += math.exp(rr[j] - mx) / den * oj
+                            out[b, h, t] = acc
+                        else:
+                            lg, us = [], []
+                            for j in A:
+                                gt = 0.0
+                                if mode == "sas" and j != c:
+                                    x = s[j] - s[c]
+                                    gt = -math.log1p(math.exp(-x)) if x >= 0 else x - math.log1p(math.exp(x))
+                                for u in range(j * 64, min(j * 64 + 64, T)):
+                                    if u <= t:
+                                        us.append(u)
+                                        lg.append(sc * math.fsum(q[b, h, t, d] * k[b, g, u, d] for d in range(D)) + gt)
+                            m2 = max(lg)
+                            e = [math.exp(x - m2) for x in lg]
+                            se = math.fsum(e)
+                            out[b, h, t] = sum(ei / se * v[b, g, u] for ei, u in zip(e, us))
+    return out
+
+
+@pytest.mark.parametrize("mode", ["plain", "sas", "hils"])
+def test_whole_path_brute_force_tiny(mode):
+    r = _rng(17)
+    B, Hq, Hkv, T, D = 1, 2, 1, 64 * 6 + 3, 3
+    q = O.round_to_dtype(r.standard_normal((B, Hq, T, D)), "bf16")
+    k = O.round_to_dtype(r.standard_normal((B, Hkv, T, D)), "bf16")
+    v = O.round_to_dtype(r.standard_normal((B, Hkv, T, D)), "bf16")
+    res = O.prefill(q, k, v, topk=2, mode=mode, dtype="bf16")
+    ref = _brute_path(q, k, v, 2, mode, "bf16")
+    np.testing.assert_allclose(res["out"], ref, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------------------
+
+def test_decode_dense_limit_and_selection():
+    """Decode with K >= all candidates equals full attention of the last token (SDPA); with a
+    small K its attended set is the forced blocks plus the top scores of sum-of-heads . L."""
+    r = _rng(18)
+    B, Hq, Hkv, Tk, D = 2, 4, 2, 64 * 7 + 20, 8
+    q = r.standard_normal((B, Hq, D))
+    kc = O.round_to_dtype(r.standard_normal((B, Hkv, Tk, D)), "bf16")
+    vc = r.standard_normal((B, Hkv, Tk, D))
+    lm = O.landmarks(kc, "bf16")
+    d = O.decode(q, kc, vc, lm, topk=100, mode="plain")
+    for b in range(B):
+        ref = _sdpa(q[b][:, None, :], np.repeat(kc[b], 2, axis=0), np.repeat(vc[b], 2, axis=0))[:, 0]
+        np.testing.assert_allclose(d["out"][b], ref, atol=1e-12)
+    d2 = O.decode(q, kc, vc, lm, topk=2, mode="plain")
+    for b, g in itertools.product(range(B), range(Hkv)):
+        qs = q[b, 2 * g] + q[b, 2 * g + 1]
+        s = [float(qs @ lm[b, g, j]) for j in range(8)]
+        assert [j for j in d2["idx"][b, g] if j >= 0] == _brute_select(s, 7, 2, 1, 2)
+
+
+@pytest.mark.parametrize("mode", ["sas", "hils"])
+def test_decode_equals_prefill_rows_when_query_is_last(mode):
+    """A decode step uses the same attention as the prefill rows for the last token once both
+    are given the same attended set."""
+    r = _rng(19)
+    B, Hq, Hkv, T, D = 1, 2, 1, 64 * 6, 4
+    q = r.standard_normal((B, Hq, T, D))
+    k = O.round_to_dtype(r.standard_normal((B, Hkv, T, D)), "bf16")
+    v = r.standard_normal((B, Hkv, T, D))
+    lm = O.landmarks(k, "bf16")
+    d = O.decode(q[:, :, -1], k, v, lm, topk=2, mode=mode)
+    idx = np.full((B, Hkv, 6, 5), -1)
+    idx[0, 0, 5] = d["idx"][0, 0]
+    # prefill rows use the query-block mean for scores; hand them the decode selector instead
+    qbar = np.zeros((B, Hkv, 6, D))
+    qbar[0, 0, 5] = d["qbar"][0, 0]
+    p = O.prefill_rows(q, k, v, [(0, 0, 5)], topk=2, mode=mode, dtype="bf16", idx=idx, lm=lm, qbar=qbar)
+    np.testing.assert_allclose(p[(0, 0, 5)]["out"][:, -1], d["out"][0], atol=1e-13)
