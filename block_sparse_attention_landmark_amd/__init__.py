@@ -1,0 +1,289 @@
+"""Python binding of libbsa: selector-driven block-sparse landmark attention on MI355X.
+
+Argument marshalling only: every step of the computation runs in the HIP kernels of
+libbsa.so (built in-tree by ``python -m block_sparse_attention_landmark_amd.build``).  PyTorch
+provides device memory and the current HIP stream.  If the library is missing, every call
+raises RuntimeError; there is no fallback path.
+
+Entry points mirror the C ABI in include/bsa.h:
+
+* ``pool_landmarks(k)``                           -> lm
+* ``select_topk(q, lm, topk=..., seq_k=...)``      -> (idx, sc)
+* ``attend_prefill(q, k, v, idx, sc, lm, mode)``  -> (out, lse)
+* ``attend_decode(q, kc, vc, idx, sc, lm, mode)`` -> (out, lse)
+
+and ``prefill(q, k, v, ...)`` / ``decode(q, kc, vc, lm, ...)`` chain them.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "MODES", "Params", "library_path", "load_library", "pool_landmarks", "select_topk",
+    "attend_prefill", "attend_decode", "select_workspace_bytes", "decode_workspace_bytes",
+    "prefill", "decode", "BsaError",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+MODES = {"plain": 0, "sas": 1, "hils": 2}
+_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+_LIB = None
+
+
+class BsaError(RuntimeError):
+    """A non-zero status returned by libbsa."""
+
+    def __init__(self, fn: str, status: int, detail: str):
+        super().__init__(f"{fn}: status {status}: {detail}")
+        self.status = status
+
+
+class Params(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("heads_q", ctypes.c_int32), ("heads_kv", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("seq_q", ctypes.c_int32), ("seq_k", ctypes.c_int32),
+        ("block", ctypes.c_int32), ("topk", ctypes.c_int32), ("n_sink", ctypes.c_int32),
+        ("n_local", ctypes.c_int32), ("scale", ctypes.c_float), ("dtype", ctypes.c_int32),
+        ("mode", ctypes.c_int32),
+    ]
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libbsa.so")
+
+
+def load_library():
+    """Load libbsa.so (once).  Raises RuntimeError if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m block_sparse_attention_landmark_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER(Params)
+    vp, st = ctypes.c_void_p, ctypes.c_int
+    lib.bsa_pool_landmarks.argtypes = [P, vp, vp, vp]
+    lib.bsa_pool_landmarks.restype = st
+    lib.bsa_select_workspace_bytes.argtypes = [P]
+    lib.bsa_select_workspace_bytes.restype = ctypes.c_size_t
+    lib.bsa_select_topk.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.bsa_select_topk.restype = st
+    lib.bsa_attend_prefill.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.bsa_attend_prefill.restype = st
+    lib.bsa_decode_workspace_bytes.argtypes = [P]
+    lib.bsa_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.bsa_attend_decode.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.bsa_attend_decode.restype = st
+    lib.bsa_status_string.argtypes = [ctypes.c_int]
+    lib.bsa_status_string.restype = ctypes.c_char_p
+    lib.bsa_last_error.argtypes = []
+    lib.bsa_last_error.restype = ctypes.c_char_p
+    lib.bsa_version.argtypes = []
+    lib.bsa_version.restype = ctypes.c_int
+    _LIB = lib
+    return lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        lib = load_library()
+        raise BsaError(fn, status, f"{lib.bsa_status_string(status).decode()}: "
+                                   f"{lib.bsa_last_error().decode()}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions (got {t.dim()})")
+
+
+def make_params(*, B, Hq, Hkv, D, seq_q, seq_k, dtype, topk=0, n_sink=1, n_local=2, scale=0.0,
+                mode="plain") -> Params:
+    return Params(B, Hq, Hkv, D, seq_q, seq_k, 64, topk, n_sink, n_local, float(scale),
+                  _DTYPES[dtype], MODES[mode] if isinstance(mode, str) else int(mode))
+
+
+def _nblocks(T):
+    return (T + 63) // 64
+
+
+# ---------------------------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------------------------
+
+def pool_landmarks(k: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """k [B,Hkv,T,D] -> landmarks [B,Hkv,ceil(T/64),D] (block means, rounded to k's dtype)."""
+    lib = load_library()
+    _need(k, "k", ndim=4)
+    B, Hkv, T, D = k.shape
+    if out is None:
+        out = torch.empty((B, Hkv, _nblocks(T), D), dtype=k.dtype, device=k.device)
+    _need(out, "lm", dtype=k.dtype, ndim=4)
+    p = make_params(B=B, Hq=Hkv, Hkv=Hkv, D=D, seq_q=T, seq_k=T, dtype=k.dtype)
+    _check("bsa_pool_landmarks", lib.bsa_pool_landmarks(ctypes.byref(p), _ptr(k), _ptr(out),
+                                                        _stream(k.device)))
+    return out
+
+
+def select_workspace_bytes(p: Params) -> int:
+    return int(load_library().bsa_select_workspace_bytes(ctypes.byref(p)))
+
+
+def decode_workspace_bytes(p: Params) -> int:
+    return int(load_library().bsa_decode_workspace_bytes(ctypes.byref(p)))
+
+
+def select_topk(q: torch.Tensor, lm: torch.Tensor, *, topk: int, seq_k: int | None = None,
+                n_sink: int = 1, n_local: int = 2, ws: torch.Tensor | None = None,
+                idx: torch.Tensor | None = None, sc: torch.Tensor | None = None):
+    """Attended block sets.
+
+    Prefill: q [B,Hq,T,D], lm [B,Hkv,ceil(T/64),D] -> idx, sc [B,Hkv,ceil(T/64),NA].
+    Decode:  q [B,Hq,1,D], lm of the seq_k cached keys -> idx, sc [B,Hkv,1,NA].
+    """
+    lib = load_library()
+    _need(q, "q", ndim=4)
+    _need(lm, "lm", dtype=q.dtype, ndim=4)
+    B, Hq, Tq, D = q.shape
+    Hkv = lm.shape[1]
+    Tk = Tq if seq_k is None else int(seq_k)
+    if lm.shape != (B, Hkv, _nblocks(Tk), D):
+        raise ValueError(f"lm shape {tuple(lm.shape)} does not match {(B, Hkv, _nblocks(Tk), D)}")
+    p = make_params(B=B, Hq=Hq, Hkv=Hkv, D=D, seq_q=Tq, seq_k=Tk, dtype=q.dtype, topk=topk,
+                    n_sink=n_sink, n_local=n_local)
+    R = 1 if (Tq == 1 and Tk != 1) else _nblocks(Tq)
+    NA = n_sink + n_local + topk
+    if idx is None:
+        idx = torch.empty((B, Hkv, R, NA), dtype=torch.int32, device=q.device)
+    if sc is None:
+        sc = torch.empty((B, Hkv, R, NA), dtype=torch.float32, device=q.device)
+    _need(idx, "idx", dtype=torch.int32, ndim=4)
+    _need(sc, "sc", dtype=torch.float32, ndim=4)
+    need = select_workspace_bytes(p)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check("bsa_select_topk", lib.bsa_select_topk(ctypes.byref(p), _ptr(q), _ptr(lm), _ptr(idx),
+                                                  _ptr(sc), _ptr(ws), ws.numel(),
+                                                  _stream(q.device)))
+    return idx, sc
+
+
+def attend_prefill(q, k, v, idx, sc=None, lm=None, *, mode="plain", topk=None, n_sink=1,
+                   n_local=2, scale=0.0, want_lse=False, out=None, lse=None):
+    """Block-sparse prefill attention; returns (out [B,Hq,T,D], lse [B,Hq,T] or None)."""
+    lib = load_library()
+    _need(q, "q", ndim=4)
+    _need(k, "k", dtype=q.dtype, ndim=4)
+    _need(v, "v", dtype=q.dtype, ndim=4)
+    _need(idx, "idx", dtype=torch.int32, ndim=4)
+    B, Hq, T, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, T, D) or v.shape != k.shape:
+        raise ValueError("k and v must be [B,Hkv,T,D] matching q")
+    NA = idx.shape[-1]
+    if topk is None:
+        topk = NA - n_sink - n_local
+    if idx.shape != (B, Hkv, _nblocks(T), NA) or NA != n_sink + n_local + topk:
+        raise ValueError(f"idx shape {tuple(idx.shape)} does not match the call")
+    if sc is not None:
+        _need(sc, "sc", dtype=torch.float32, ndim=4)
+        if sc.shape != idx.shape:
+            raise ValueError("sc must have idx's shape")
+    if lm is not None:
+        _need(lm, "lm", dtype=q.dtype, ndim=4)
+        if lm.shape != (B, Hkv, _nblocks(T), D):
+            raise ValueError("lm must be [B,Hkv,ceil(T/64),D]")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", dtype=q.dtype, ndim=4)
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    p = make_params(B=B, Hq=Hq, Hkv=Hkv, D=D, seq_q=T, seq_k=T, dtype=q.dtype, topk=topk,
+                    n_sink=n_sink, n_local=n_local, scale=scale, mode=mode)
+    _check("bsa_attend_prefill",
+           lib.bsa_attend_prefill(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(lm), _ptr(idx),
+                                  _ptr(sc), _ptr(out), _ptr(lse), _stream(q.device)))
+    return out, lse
+
+
+def attend_decode(q, kc, vc, idx, sc=None, lm=None, *, mode="plain", topk=None, n_sink=1,
+                  n_local=2, scale=0.0, want_lse=False, out=None, lse=None, ws=None):
+    """Block-sparse decode attention of the token at position Tk-1; q [B,Hq,1,D]."""
+    lib = load_library()
+    _need(q, "q", ndim=4)
+    _need(kc, "kc", dtype=q.dtype, ndim=4)
+    _need(vc, "vc", dtype=q.dtype, ndim=4)
+    _need(idx, "idx", dtype=torch.int32, ndim=4)
+    B, Hq, one, D = q.shape
+    Hkv, Tk = kc.shape[1], kc.shape[2]
+    if one != 1 or kc.shape != (B, Hkv, Tk, D) or vc.shape != kc.shape:
+        raise ValueError("q must be [B,Hq,1,D] and kc/vc [B,Hkv,Tk,D]")
+    NA = idx.shape[-1]
+    if topk is None:
+        topk = NA - n_sink - n_local
+    if idx.shape != (B, Hkv, 1, NA) or NA != n_sink + n_local + topk:
+        raise ValueError(f"idx shape {tuple(idx.shape)} does not match the call")
+    if sc is not None:
+        _need(sc, "sc", dtype=torch.float32, ndim=4)
+    if lm is not None:
+        _need(lm, "lm", dtype=q.dtype, ndim=4)
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    p = make_params(B=B, Hq=Hq, Hkv=Hkv, D=D, seq_q=1, seq_k=Tk, dtype=q.dtype, topk=topk,
+                    n_sink=n_sink, n_local=n_local, scale=scale, mode=mode)
+    need = decode_workspace_bytes(p)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check("bsa_attend_decode",
+           lib.bsa_attend_decode(ctypes.byref(p), _ptr(q), _ptr(kc), _ptr(vc), _ptr(lm), _ptr(idx),
+                                 _ptr(sc), _ptr(out), _ptr(lse), _ptr(ws),
+                                 0 if ws is None else ws.numel(), _stream(q.device)))
+    return out, lse
+
+
+# ---------------------------------------------------------------------------------------------
+# whole path
+# ---------------------------------------------------------------------------------------------
+
+def prefill(q, k, v, *, topk: int, mode: str = "plain", n_sink: int = 1, n_local: int = 2,
+            scale: float = 0.0, want_lse: bool = False):
+    """Pool, select and attend for a prefill; returns dict(out, lse, idx, sc, lm)."""
+    lm = pool_landmarks(k)
+    idx, sc = select_topk(q, lm, topk=topk, n_sink=n_sink, n_local=n_local)
+    out, lse = attend_prefill(q, k, v, idx, sc, lm if mode == "hils" else None, mode=mode,
+                              topk=topk, n_sink=n_sink, n_local=n_local, scale=scale,
+                              want_lse=want_lse and mode != "hils")
+    return {"out": out, "lse": lse, "idx": idx, "sc": sc, "lm": lm}
+
+
+def decode(q, kc, vc, lm, *, topk: int, mode: str = "plain", n_sink: int = 1, n_local: int = 2,
+           scale: float = 0.0, want_lse: bool = False):
+    """Select and attend for one decode step (q [B,Hq,1,D]); returns dict(out, lse, idx, sc)."""
+    idx, sc = select_topk(q, lm, topk=topk, seq_k=kc.shape[2], n_sink=n_sink, n_local=n_local)
+    out, lse = attend_decode(q, kc, vc, idx, sc, lm if mode == "hils" else None, mode=mode,
+                             topk=topk, n_sink=n_sink, n_local=n_local, scale=scale,
+                             want_lse=want_lse and mode != "hils")
+    return {"out": out, "lse": lse, "idx": idx, "sc": sc}

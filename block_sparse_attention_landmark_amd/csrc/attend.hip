@@ -1,0 +1,701 @@
+// Block-sparse attention over the attended block lists.
+//
+// PLAIN / SAS: softmax over the keys of the attended blocks (causal inside the current
+// block), computed FlashAttention-style, block by block with a running max and sum and no
+// materialised score matrix (SAS page, summary paragraph 4: the kernel works block-wise without
+// building the full square matrix).  SAS adds g_j = log sigmoid(S_j - S_c) to every logit of
+// block j != c, inside the softmax (SAS page, summary paragraph 3, "Key facts" item 3).
+//
+// HiLS: every query attends to each attended chunk separately; the per-chunk results are merged
+// with weights softmax_j(q . L_j / sqrt(D)) over the attended chunks (HiLS page, summary
+// paragraph 2: per-chunk attention combined by the chunks' retrieval scores).
+//
+// bf16 prefill: one workgroup per (batch, kv group, query block, head chunk) holds up to four
+// query heads x 64 tokens (two waves per head, 32 query rows per wave), so every gathered K/V
+// block in LDS feeds up to 256 query rows.  Scores are computed transposed, S^T = K Q^T, on
+// 32x32x16 bf16 MFMA so that each lane owns one query row: the row max and sum need only the
+// lane's own registers and one exchange with the lane 32 apart.  P V is computed as
+// O^T = V^T P^T with P taken straight from the score registers (the contraction order over
+// keys is permuted identically on both operands), V transposed into LDS when staged.
+#include <math.h>
+
+#include "bsa_common.hpp"
+#include "bsa_internal.hpp"
+
+namespace bsa {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// number of valid entries in an attended-set row (stops at the first -1)
+__device__ __forceinline__ int count_valid(const int32_t* row, int NA) {
+  int n = 0;
+  while (n < NA && row[n] >= 0) ++n;
+  return n;
+}
+
+// =============================================================================================
+// bf16 prefill
+// =============================================================================================
+template <int D, int MODE, int HPW>
+__global__ __launch_bounds__(HPW * 128) void attend_prefill_bf16_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ lm, const int32_t* __restrict__ idx, const float* __restrict__ sc,
+    bf16* __restrict__ out, float* __restrict__ lse, int Hq, int Hkv, int G, int T, int NQB,
+    int NA, int n_hc, float scale_log2) {
+  constexpr int NWAVE = HPW * 2;
+  constexpr int NT = NWAVE * kWave;
+  constexpr int KP = D + 8;        // K tile row pitch (elements)
+  constexpr int VP = kBlock + 8;   // V^T tile row pitch (elements)
+  constexpr int C8 = D / 8;        // 16-byte chunks per row
+  __shared__ __attribute__((aligned(16))) bf16 Ks[kBlock * KP];
+  __shared__ __attribute__((aligned(16))) bf16 Vt[D * VP];
+  __shared__ float wbuf[MODE == 2 ? NWAVE * 64 * 32 : 1];
+
+  const int c = NQB - 1 - (int)blockIdx.x;   // heavy (late) query blocks first
+  const int g = blockIdx.y / n_hc;
+  const int hc = blockIdx.y % n_hc;
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int w = tid / kWave;
+  const int lane = tid % kWave;
+  const int half = lane / 32;
+  const int l32 = lane % 32;
+  const int h = g * G + hc * HPW + w / 2;
+  const int tq = c * kBlock + (w % 2) * 32 + l32;
+  const bool row_ok = tq < T;
+
+  bf16x8 qf[D / 16];
+  {
+    const bf16* qrow = q + ((size_t)(b * Hq + h) * T + min(tq, T - 1)) * D;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      u32x4 raw = *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * half);
+      if (!row_ok) raw = u32x4{0u, 0u, 0u, 0u};
+      qf[s] = __builtin_bit_cast(bf16x8, raw);
+    }
+  }
+  const size_t kvbase = (size_t)(b * Hkv + g) * T * D;
+  const size_t rowsel = ((size_t)(b * Hkv + g) * NQB + c) * NA;
+  const int32_t* irow = idx + rowsel;
+  const float* srow = sc + rowsel;
+  const int nval = count_valid(irow, NA);
+  float s_ref = 0.0f;
+  if (MODE == 1 && nval > 0) s_ref = srow[nval - 1];
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[dt][i] = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  if constexpr (MODE == 2) {
+    // retrieval weights of every attended chunk for this wave's 32 query rows
+    for (int ci = tid; ci < kBlock * C8; ci += NT) {
+      const int row = ci / C8, c8 = ci % C8;
+      u32x4 val = u32x4{0u, 0u, 0u, 0u};
+      const int jr = row < nval ? irow[row] : -1;
+      if (jr >= 0 && jr <= c)
+        val = *reinterpret_cast<const u32x4*>(lm + ((size_t)(b * Hkv + g) * NQB + jr) * D + c8 * 8);
+      *reinterpret_cast<u32x4*>(&Ks[row * KP + c8 * 8]) = val;
+    }
+    __syncthreads();
+    f32x16 rt[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) rt[kt][i] = 0.0f;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[(kt * 32 + l32) * KP + 16 * s + 8 * half]);
+        rt[kt] = mfma32(a, qf[s], rt[kt]);
+      }
+    }
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int slot = kt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+        const float x = slot < nval ? rt[kt][i] * scale_log2 : -INFINITY;
+        rt[kt][i] = x;
+        mloc = fmaxf(mloc, x);
+      }
+    const float M = wave_max_xor32(mloc);
+    float den = 0.0f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float e = fast_exp2(rt[kt][i] - M);
+        rt[kt][i] = e;
+        den += e;
+      }
+    den = wave_sum_xor32(den);
+    const float inv = 1.0f / den;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int slot = kt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+        wbuf[(w * 64 + slot) * 32 + l32] = rt[kt][i] * inv;
+      }
+  }
+
+  for (int a = 0; a < nval; ++a) {
+    const int j = irow[a];
+    if (j < 0 || j > c) continue;
+    __syncthreads();
+    // stage K (row-major) and V (transposed) of block j
+    for (int ci = tid; ci < kBlock * C8; ci += NT) {
+      const int row = ci / C8, c8 = ci % C8;
+      const int tok = j * kBlock + row;
+      u32x4 val = u32x4{0u, 0u, 0u, 0u};
+      if (tok < T) val = *reinterpret_cast<const u32x4*>(k + kvbase + (size_t)tok * D + c8 * 8);
+      *reinterpret_cast<u32x4*>(&Ks[row * KP + c8 * 8]) = val;
+    }
+    for (int ci = tid; ci < kBlock * C8; ci += NT) {
+      const int row = ci % kBlock, c8 = ci / kBlock;
+      const int tok = j * kBlock + row;
+      u32x4 val = u32x4{0u, 0u, 0u, 0u};
+      if (tok < T) val = *reinterpret_cast<const u32x4*>(v + kvbase + (size_t)tok * D + c8 * 8);
+      const bf16x8 vv = __builtin_bit_cast(bf16x8, val);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Vt[(c8 * 8 + e) * VP + row] = vv[e];
+    }
+    __syncthreads();
+
+    // S^T = K Q^T: st[kt][i] = score of key kt*32 + 8*(i/4) + 4*half + i%4 for query row l32
+    f32x16 st[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st[kt][i] = 0.0f;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[(kt * 32 + l32) * KP + 16 * s + 8 * half]);
+        st[kt] = mfma32(a, qf[s], st[kt]);
+      }
+    }
+    const bool diag = (j == c);
+    float gate2 = 0.0f;
+    if (MODE == 1 && !diag) gate2 = log_sigmoid(srow[a] - s_ref) * kLog2e;
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+        float x = st[kt][i] * scale_log2 + gate2;
+        if (diag && j * kBlock + key > tq) x = -INFINITY;
+        st[kt][i] = x;
+        mloc = fmaxf(mloc, x);
+      }
+    if constexpr (MODE == 2) {
+      const float mj = wave_max_xor32(mloc);
+      float lsum = 0.0f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float e = fast_exp2(st[kt][i] - mj);
+          st[kt][i] = e;
+          lsum += e;
+        }
+      const float lj = wave_sum_xor32(lsum);
+      const float coef = wbuf[(w * 64 + a) * 32 + l32] / lj;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st[kt][i] *= coef;
+    } else {
+      const float m_new = fmaxf(m_run, wave_max_xor32(mloc));
+      const float alpha = fast_exp2(m_run - m_new);
+      float lsum = 0.0f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = fast_exp2(st[kt][i] - m_new);
+          st[kt][i] = p;
+          lsum += p;
+        }
+      l_run = l_run * alpha + lsum;
+      m_run = m_new;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+    }
+    // O^T += V^T P^T over 4 k-steps of 16 keys; lane half h supplies keys
+    // 16ks + 4h + {0..3} and 16ks + 8 + 4h + {0..3}
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 pb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[e] = f2bf(st[ks / 2][8 * (ks % 2) + e]);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const bf16* vp = &Vt[(dt * 32 + l32) * VP + 16 * ks + 4 * half];
+        const u32x2 x0 = *reinterpret_cast<const u32x2*>(vp);
+        const u32x2 x1 = *reinterpret_cast<const u32x2*>(vp + 8);
+        const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{x0[0], x0[1], x1[0], x1[1]});
+        o[dt] = mfma32(av, pb, o[dt]);
+      }
+    }
+  }
+
+  float inv = 1.0f;
+  float lse_val = 0.0f;
+  if constexpr (MODE != 2) {
+    const float l_tot = wave_sum_xor32(l_run);
+    inv = 1.0f / l_tot;
+    lse_val = (m_run + log2f(l_tot)) * kLn2;
+  }
+  if (row_ok) {
+    bf16* orow = out + ((size_t)(b * Hq + h) * T + tq) * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        bf16x4 ov;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ov[e] = f2bf(o[dt][4 * i4 + e] * inv);
+        *reinterpret_cast<bf16x4*>(orow + dt * 32 + 8 * i4 + 4 * half) = ov;
+      }
+    if (MODE != 2 && lse != nullptr && half == 0) lse[(size_t)(b * Hq + h) * T + tq] = lse_val;
+  }
+}
+
+// =============================================================================================
+// bf16 decode: split-K over the attended blocks, one wave per (sequence, kv group, split)
+// =============================================================================================
+constexpr int kDecodeBlocksPerSplit = 4;
+
+template <int D, int MODE>
+__global__ __launch_bounds__(64) void attend_decode_bf16_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
+    const bf16* __restrict__ lm, const int32_t* __restrict__ idx, const float* __restrict__ sc,
+    float* __restrict__ part_o, float* __restrict__ part_ml, int Hq, int Hkv, int G, int Tk,
+    int NB, int NA, int nsplit, float scale_log2) {
+  constexpr int VP = kBlock + 8;
+  constexpr int C8 = D / 8;
+  __shared__ __attribute__((aligned(16))) bf16 Vt[D * VP];
+
+  const int split = blockIdx.x;
+  const int g = blockIdx.y;
+  const int b = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int half = lane / 32;
+  const int l32 = lane % 32;
+  const bool row_ok = l32 < G;
+  const int h = g * G + min(l32, G - 1);
+  const int c = (Tk - 1) / kBlock;
+
+  bf16x8 qf[D / 16];
+  {
+    const bf16* qrow = q + (size_t)(b * Hq + h) * D;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      u32x4 raw = *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * half);
+      if (!row_ok) raw = u32x4{0u, 0u, 0u, 0u};
+      qf[s] = __builtin_bit_cast(bf16x8, raw);
+    }
+  }
+  const size_t kvbase = (size_t)(b * Hkv + g) * Tk * D;
+  const int32_t* irow = idx + (size_t)(b * Hkv + g) * NA;
+  const float* srow = sc + (size_t)(b * Hkv + g) * NA;
+  const int nval = count_valid(irow, NA);
+  float s_ref = 0.0f;
+  if (MODE == 1 && nval > 0) s_ref = srow[nval - 1];
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[dt][i] = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  const int a_beg = split * kDecodeBlocksPerSplit;
+  const int a_end = min(nval, a_beg + kDecodeBlocksPerSplit);
+  for (int a = a_beg; a < a_end; ++a) {
+    const int j = irow[a];
+    if (j < 0 || j > c) continue;
+    // V block: lane = token row, 16-byte chunks along D
+    u32x4 vraw[C8];
+    {
+      const int tok = j * kBlock + lane;
+#pragma unroll
+      for (int c8 = 0; c8 < C8; ++c8) {
+        vraw[c8] = u32x4{0u, 0u, 0u, 0u};
+        if (tok < Tk) vraw[c8] = *reinterpret_cast<const u32x4*>(vc + kvbase + (size_t)tok * D + c8 * 8);
+      }
+    }
+    // K fragments straight from memory in MFMA A layout
+    f32x16 st[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int tok = j * kBlock + kt * 32 + l32;
+      const bf16* krow = kc + kvbase + (size_t)min(tok, Tk - 1) * D;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st[kt][i] = 0.0f;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        u32x4 raw = *reinterpret_cast<const u32x4*>(krow + 16 * s + 8 * half);
+        if (tok >= Tk) raw = u32x4{0u, 0u, 0u, 0u};
+        st[kt] = mfma32(__builtin_bit_cast(bf16x8, raw), qf[s], st[kt]);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c8 = 0; c8 < C8; ++c8) {
+      const bf16x8 vv = __builtin_bit_cast(bf16x8, vraw[c8]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Vt[(c8 * 8 + e) * VP + lane] = vv[e];
+    }
+    float gate2 = 0.0f;
+    if (MODE == 1 && j != c) gate2 = log_sigmoid(srow[a] - s_ref) * kLog2e;
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+        float x = st[kt][i] * scale_log2 + gate2;
+        if (j * kBlock + key >= Tk) x = -INFINITY;
+        st[kt][i] = x;
+        mloc = fmaxf(mloc, x);
+      }
+    float alpha, coef = 1.0f;
+    if constexpr (MODE == 2) {
+      // per-chunk softmax, then an online softmax over the chunks' retrieval scores
+      const float mj = wave_max_xor32(mloc);
+      float lsum = 0.0f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float e = fast_exp2(st[kt][i] - mj);
+          st[kt][i] = e;
+          lsum += e;
+        }
+      const float lj = wave_sum_xor32(lsum);
+      const bf16* lrow = lm + ((size_t)(b * Hkv + g) * NB + j) * D;
+      float part = 0.0f;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        const bf16x8 lv = *reinterpret_cast<const bf16x8*>(lrow + 16 * s + 8 * half);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part += bf2f(qf[s][e]) * bf2f(lv[e]);
+      }
+      const float r2 = wave_sum_xor32(part) * scale_log2;
+      const float m_new = fmaxf(m_run, r2);
+      alpha = fast_exp2(m_run - m_new);
+      const float wr = fast_exp2(r2 - m_new);
+      l_run = l_run * alpha + wr;
+      m_run = m_new;
+      coef = wr / lj;
+    } else {
+      const float m_new = fmaxf(m_run, wave_max_xor32(mloc));
+      alpha = fast_exp2(m_run - m_new);
+      float lsum = 0.0f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = fast_exp2(st[kt][i] - m_new);
+          st[kt][i] = p;
+          lsum += p;
+        }
+      l_run = l_run * alpha + lsum;
+      m_run = m_new;
+    }
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 pb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[e] = f2bf(st[ks / 2][8 * (ks % 2) + e] * coef);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const bf16* vp = &Vt[(dt * 32 + l32) * VP + 16 * ks + 4 * half];
+        const u32x2 x0 = *reinterpret_cast<const u32x2*>(vp);
+        const u32x2 x1 = *reinterpret_cast<const u32x2*>(vp + 8);
+        const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{x0[0], x0[1], x1[0], x1[1]});
+        o[dt] = mfma32(av, pb, o[dt]);
+      }
+    }
+  }
+  // partial state: O (unnormalised), m (log2 units) and l; PLAIN/SAS sum l over both halves
+  if constexpr (MODE != 2) l_run = wave_sum_xor32(l_run);
+  const size_t pbase = ((size_t)(b * Hkv + g) * nsplit + split) * G;
+  if (row_ok) {
+    float* po = part_o + (pbase + l32) * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        f32x4 ov;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ov[e] = o[dt][4 * i4 + e];
+        *reinterpret_cast<f32x4*>(po + dt * 32 + 8 * i4 + 4 * half) = ov;
+      }
+    if (half == 0) {
+      part_ml[(pbase + l32) * 2 + 0] = m_run;
+      part_ml[(pbase + l32) * 2 + 1] = l_run;
+    }
+  }
+}
+
+template <typename OUT>
+__global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restrict__ part_o,
+                                                           const float* __restrict__ part_ml,
+                                                           OUT* __restrict__ out,
+                                                           float* __restrict__ lse, int Hkv,
+                                                           int G, int D, int nsplit,
+                                                           int write_lse) {
+  const int bg = blockIdx.x;
+  const int b = bg / Hkv, g = bg % Hkv;
+  for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
+    const int row = e / D, d = e % D;
+    float M = -INFINITY;
+    for (int s = 0; s < nsplit; ++s)
+      M = fmaxf(M, part_ml[(((size_t)bg * nsplit + s) * G + row) * 2]);
+    float L = 0.0f, acc = 0.0f;
+    for (int s = 0; s < nsplit; ++s) {
+      const size_t pr = ((size_t)bg * nsplit + s) * G + row;
+      const float m = part_ml[pr * 2];
+      if (m == -INFINITY) continue;
+      const float f = fast_exp2(m - M);
+      L += part_ml[pr * 2 + 1] * f;
+      acc += part_o[pr * D + d] * f;
+    }
+    const int hq = g * G + row;
+    const size_t orow = (size_t)(b * Hkv * G + hq);
+    out[orow * D + d] = (OUT)(acc / L);
+    if (write_lse && d == 0 && lse != nullptr) lse[orow] = (M + log2f(L)) * kLn2;
+  }
+}
+
+// =============================================================================================
+// float32 path (exact-ish reference shapes; one wave, one query row per lane)
+// =============================================================================================
+// prefill: workgroup per (b, query head, query block), lane = token; decode: workgroup per
+// (b, kv group), lane = query head of the group, token = Tk - 1.
+template <int D, int MODE>
+__global__ __launch_bounds__(64) void attend_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    const float* __restrict__ lm, const int32_t* __restrict__ idx, const float* __restrict__ sc,
+    float* __restrict__ out, float* __restrict__ lse, int Hq, int Hkv, int G, int Tq, int Tk,
+    int NB, int R, int NA, int decode, float scale) {
+  __shared__ float Kf[kBlock][D];
+  __shared__ float Vf[kBlock][D];
+  const int lane = threadIdx.x;
+  int b, h, g, c, tq, row_sel;
+  bool row_ok;
+  if (decode) {
+    b = blockIdx.y;
+    g = blockIdx.x;
+    h = g * G + min(lane, G - 1);
+    row_ok = lane < G;
+    tq = Tk - 1;
+    c = tq / kBlock;
+    row_sel = 0;
+  } else {
+    c = blockIdx.x;
+    h = blockIdx.y;
+    b = blockIdx.z;
+    g = h / G;
+    tq = c * kBlock + lane;
+    row_ok = tq < Tq;
+    row_sel = c;
+  }
+  const float* qrow = q + ((size_t)(b * Hq + h) * Tq + (decode ? 0 : min(tq, Tq - 1))) * D;
+  float qv[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) qv[d] = qrow[d];
+  const size_t kvbase = (size_t)(b * Hkv + g) * Tk * D;
+  const size_t rs = ((size_t)(b * Hkv + g) * R + row_sel) * NA;
+  const int nval = count_valid(idx + rs, NA);
+  const float s_ref = (MODE == 1 && nval > 0) ? sc[rs + nval - 1] : 0.0f;
+  float o[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) o[d] = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f;
+  for (int a = 0; a < nval; ++a) {
+    const int j = idx[rs + a];
+    if (j < 0 || j > c) continue;
+    __syncthreads();
+    for (int e = lane; e < kBlock * D; e += 64) {
+      const int r = e / D, d = e % D;
+      const int tok = j * kBlock + r;
+      Kf[r][d] = tok < Tk ? k[kvbase + (size_t)tok * D + d] : 0.0f;
+      Vf[r][d] = tok < Tk ? v[kvbase + (size_t)tok * D + d] : 0.0f;
+    }
+    __syncthreads();
+    const float gate = (MODE == 1 && j != c) ? log_sigmoid(sc[rs + a] - s_ref) : 0.0f;
+    float s[kBlock];
+    float mj = -INFINITY;
+    for (int u = 0; u < kBlock; ++u) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int d = 0; d < D; ++d) acc = fmaf(qv[d], Kf[u][d], acc);
+      const int tok = j * kBlock + u;
+      s[u] = (tok <= tq && tok < Tk) ? acc * scale + gate : -INFINITY;
+      mj = fmaxf(mj, s[u]);
+    }
+    float coef = 1.0f, alpha;
+    if constexpr (MODE == 2) {
+      float lj = 0.0f;
+      for (int u = 0; u < kBlock; ++u) {
+        s[u] = expf(s[u] - mj);
+        lj += s[u];
+      }
+      const float* lrow = lm + ((size_t)(b * Hkv + g) * NB + j) * D;
+      float r = 0.0f;
+#pragma unroll
+      for (int d = 0; d < D; ++d) r = fmaf(qv[d], lrow[d], r);
+      r *= scale;
+      const float m_new = fmaxf(m_run, r);
+      alpha = expf(m_run - m_new);
+      const float wr = expf(r - m_new);
+      l_run = l_run * alpha + wr;
+      m_run = m_new;
+      coef = wr / lj;
+    } else {
+      const float m_new = fmaxf(m_run, mj);
+      alpha = expf(m_run - m_new);
+      float lsum = 0.0f;
+      for (int u = 0; u < kBlock; ++u) {
+        s[u] = expf(s[u] - m_new);
+        lsum += s[u];
+      }
+      l_run = l_run * alpha + lsum;
+      m_run = m_new;
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d) o[d] *= alpha;
+    for (int u = 0; u < kBlock; ++u) {
+      const float p = s[u] * coef;
+#pragma unroll
+      for (int d = 0; d < D; ++d) o[d] = fmaf(p, Vf[u][d], o[d]);
+    }
+  }
+  if (!row_ok) return;
+  const size_t orow = decode ? (size_t)(b * Hq + h) : (size_t)(b * Hq + h) * Tq + tq;
+#pragma unroll
+  for (int d = 0; d < D; ++d) out[orow * D + d] = o[d] / l_run;
+  if (MODE != 2 && lse != nullptr) lse[orow] = m_run + logf(l_run);
+}
+
+// =============================================================================================
+// launchers
+// =============================================================================================
+int decode_splits(const Shape& s) {
+  return (s.NA + kDecodeBlocksPerSplit - 1) / kDecodeBlocksPerSplit;
+}
+
+size_t decode_ws_bytes(const Shape& s) {
+  if (!s.bf16) return 0;
+  const size_t rows = (size_t)s.B * s.Hkv * decode_splits(s) * s.G;
+  const size_t o = (rows * s.D * sizeof(float) + 255) & ~(size_t)255;
+  return o + rows * 2 * sizeof(float);
+}
+
+template <int D>
+static void launch_prefill_bf16_d(const Shape& s, const void* q, const void* k, const void* v,
+                                  const void* lm, const int32_t* idx, const float* sc, void* out,
+                                  float* lse, hipStream_t st) {
+  const int hpw = (s.G % 4 == 0) ? 4 : (s.G % 2 == 0) ? 2 : 1;
+  const int n_hc = s.G / hpw;
+  dim3 grid(s.R, s.Hkv * n_hc, s.B);
+  const float sl2 = s.scale * kLog2e;
+#define BSA_PF(MODE, HPW)                                                                      \
+  hipLaunchKernelGGL((attend_prefill_bf16_kernel<D, MODE, HPW>), grid, dim3(HPW * 128), 0, st, \
+                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)lm, idx, sc,  \
+                     (bf16*)out, lse, s.Hq, s.Hkv, s.G, s.Tq, s.R, s.NA, n_hc, sl2)
+#define BSA_PF_MODE(HPW)              \
+  if (s.mode == 0) BSA_PF(0, HPW);    \
+  else if (s.mode == 1) BSA_PF(1, HPW); \
+  else BSA_PF(2, HPW);
+  if (hpw == 4) {
+    BSA_PF_MODE(4)
+  } else if (hpw == 2) {
+    BSA_PF_MODE(2)
+  } else {
+    BSA_PF_MODE(1)
+  }
+#undef BSA_PF_MODE
+#undef BSA_PF
+}
+
+template <int D>
+static void launch_f32_d(const Shape& s, const void* q, const void* k, const void* v,
+                         const void* lm, const int32_t* idx, const float* sc, void* out,
+                         float* lse, hipStream_t st) {
+  dim3 grid = s.decode ? dim3(s.Hkv, s.B) : dim3(s.R, s.Hq, s.B);
+#define BSA_F32(MODE)                                                                          \
+  hipLaunchKernelGGL((attend_f32_kernel<D, MODE>), grid, dim3(64), 0, st, (const float*)q,     \
+                     (const float*)k, (const float*)v, (const float*)lm, idx, sc, (float*)out, \
+                     lse, s.Hq, s.Hkv, s.G, s.Tq, s.Tk, s.NB, s.R, s.NA, s.decode ? 1 : 0,     \
+                     s.scale)
+  if (s.mode == 0) BSA_F32(0);
+  else if (s.mode == 1) BSA_F32(1);
+  else BSA_F32(2);
+#undef BSA_F32
+}
+
+hipError_t launch_attend_prefill(const Shape& s, const void* q, const void* k, const void* v,
+                                 const void* lm, const int32_t* idx, const float* sc, void* out,
+                                 float* lse, hipStream_t st) {
+  if (s.bf16) {
+    if (s.D == 128) launch_prefill_bf16_d<128>(s, q, k, v, lm, idx, sc, out, lse, st);
+    else launch_prefill_bf16_d<64>(s, q, k, v, lm, idx, sc, out, lse, st);
+  } else {
+    if (s.D == 128) launch_f32_d<128>(s, q, k, v, lm, idx, sc, out, lse, st);
+    else launch_f32_d<64>(s, q, k, v, lm, idx, sc, out, lse, st);
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+static void launch_decode_bf16_d(const Shape& s, const void* q, const void* kc, const void* vc,
+                                 const void* lm, const int32_t* idx, const float* sc, void* out,
+                                 float* lse, void* ws, hipStream_t st) {
+  const int nsplit = decode_splits(s);
+  const size_t rows = (size_t)s.B * s.Hkv * nsplit * s.G;
+  float* part_o = (float*)ws;
+  float* part_ml = (float*)((char*)ws + ((rows * s.D * sizeof(float) + 255) & ~(size_t)255));
+  dim3 grid(nsplit, s.Hkv, s.B);
+  const float sl2 = s.scale * kLog2e;
+#define BSA_DEC(MODE)                                                                          \
+  hipLaunchKernelGGL((attend_decode_bf16_kernel<D, MODE>), grid, dim3(64), 0, st,              \
+                     (const bf16*)q, (const bf16*)kc, (const bf16*)vc, (const bf16*)lm, idx,   \
+                     sc, part_o, part_ml, s.Hq, s.Hkv, s.G, s.Tk, s.NB, s.NA, nsplit, sl2)
+  if (s.mode == 0) BSA_DEC(0);
+  else if (s.mode == 1) BSA_DEC(1);
+  else BSA_DEC(2);
+#undef BSA_DEC
+  hipLaunchKernelGGL(decode_merge_kernel<bf16>, dim3(s.B * s.Hkv), dim3(256), 0, st, part_o,
+                     part_ml, (bf16*)out, lse, s.Hkv, s.G, s.D, nsplit, s.mode != 2 ? 1 : 0);
+}
+
+hipError_t launch_attend_decode(const Shape& s, const void* q, const void* kc, const void* vc,
+                                const void* lm, const int32_t* idx, const float* sc, void* out,
+                                float* lse, void* ws, hipStream_t st) {
+  if (s.bf16) {
+    if (s.D == 128) launch_decode_bf16_d<128>(s, q, kc, vc, lm, idx, sc, out, lse, ws, st);
+    else launch_decode_bf16_d<64>(s, q, kc, vc, lm, idx, sc, out, lse, ws, st);
+  } else {
+    if (s.D == 128) launch_f32_d<128>(s, q, kc, vc, lm, idx, sc, out, lse, st);
+    else launch_f32_d<64>(s, q, kc, vc, lm, idx, sc, out, lse, st);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace bsa

@@ -1,0 +1,229 @@
+// C-ABI entry points: argument validation, workspace sizing and kernel dispatch.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/bsa.h"
+#include "bsa_internal.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+bsa_status_t fail(bsa_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+bsa_status_t fail(bsa_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+bsa_status_t ok() {
+  g_last_error[0] = '\0';
+  return BSA_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+enum Call { kPool, kSelect, kPrefill, kDecode };
+
+// Validate params for a call and fill the derived shape.
+bsa_status_t make_shape(const bsa_params_t* p, Call call, bsa::Shape* s) {
+  if (p == nullptr) return fail(BSA_ERR_NULL, "params is NULL");
+  if (p->batch < 1 || p->heads_q < 1 || p->heads_kv < 1 || p->seq_k < 1 || p->seq_q < 1)
+    return fail(BSA_ERR_SHAPE, "batch, heads_q, heads_kv, seq_q and seq_k must be >= 1");
+  if (p->heads_q % p->heads_kv != 0)
+    return fail(BSA_ERR_SHAPE, "heads_q (%d) is not a multiple of heads_kv (%d)", p->heads_q,
+                p->heads_kv);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(BSA_ERR_UNSUPPORTED, "head_dim %d is not 64 or 128", p->head_dim);
+  if (p->block != 64) return fail(BSA_ERR_UNSUPPORTED, "block %d is not 64", p->block);
+  if (p->dtype != BSA_DTYPE_F32 && p->dtype != BSA_DTYPE_BF16)
+    return fail(BSA_ERR_UNSUPPORTED, "dtype %d is not BSA_DTYPE_F32 or BSA_DTYPE_BF16", p->dtype);
+  if (call != kPool) {
+    if (p->topk < 0 || p->n_sink < 0 || p->n_local < 1)
+      return fail(BSA_ERR_SHAPE, "need topk >= 0, n_sink >= 0, n_local >= 1 (got %d, %d, %d)",
+                  p->topk, p->n_sink, p->n_local);
+    if ((int64_t)p->topk + p->n_sink + p->n_local > 65536)
+      return fail(BSA_ERR_SHAPE, "n_sink + n_local + topk exceeds 65536");
+    if (p->seq_q != 1 && p->seq_q != p->seq_k)
+      return fail(BSA_ERR_SHAPE, "seq_q (%d) must equal seq_k (%d) for prefill or be 1 for decode",
+                  p->seq_q, p->seq_k);
+    if (call == kPrefill && p->seq_q != p->seq_k)
+      return fail(BSA_ERR_SHAPE, "prefill needs seq_q == seq_k (got %d, %d)", p->seq_q, p->seq_k);
+    if (call == kDecode && p->seq_q != 1)
+      return fail(BSA_ERR_SHAPE, "decode needs seq_q == 1 (got %d)", p->seq_q);
+    if (p->mode < BSA_MODE_PLAIN || p->mode > BSA_MODE_HILS)
+      return fail(BSA_ERR_UNSUPPORTED, "mode %d is not PLAIN, SAS or HILS", p->mode);
+    if (!(p->scale >= 0.0f) || !isfinite(p->scale))
+      return fail(BSA_ERR_SHAPE, "scale must be finite and >= 0 (0 = 1/sqrt(head_dim))");
+  }
+  // element counts must stay inside what the kernels index with 64-bit offsets and 32-bit
+  // block counts
+  const int64_t tok_elems = (int64_t)p->batch * p->heads_q * p->seq_k * p->head_dim;
+  if (tok_elems > ((int64_t)1 << 40)) return fail(BSA_ERR_SHAPE, "tensor too large");
+  bsa::Shape& x = *s;
+  x.B = p->batch;
+  x.Hq = p->heads_q;
+  x.Hkv = p->heads_kv;
+  x.G = p->heads_q / p->heads_kv;
+  x.D = p->head_dim;
+  x.Tk = p->seq_k;
+  x.Tq = (call == kPool) ? p->seq_k : p->seq_q;
+  // a one-token query against a longer key sequence is a decode step; seq_q == seq_k == 1 is
+  // the same computation either way and is treated as prefill by the selection call
+  x.decode = (call == kDecode) || (call == kSelect && p->seq_q == 1 && p->seq_k != 1);
+  x.NB = (x.Tk + 63) / 64;
+  x.R = x.decode ? 1 : (x.Tq + 63) / 64;
+  x.c_dec = (x.Tk - 1) / 64;
+  x.topk = p->topk;
+  x.n_sink = p->n_sink;
+  x.n_local = p->n_local;
+  x.NA = p->n_sink + p->n_local + p->topk;
+  x.mode = p->mode;
+  x.bf16 = p->dtype == BSA_DTYPE_BF16;
+  x.scale = (p->scale == 0.0f) ? (float)(1.0 / sqrt((double)p->head_dim)) : p->scale;
+  if (call == kPrefill || call == kDecode) {
+    if (x.mode == BSA_MODE_HILS && x.NA > 64 && (call == kPrefill) && x.bf16)
+      return fail(BSA_ERR_UNSUPPORTED, "HILS prefill supports n_sink + n_local + topk <= 64 (got %d)",
+                  x.NA);
+    if (call == kDecode && x.bf16 && x.G > 32)
+      return fail(BSA_ERR_UNSUPPORTED, "bf16 decode supports heads_q / heads_kv <= 32 (got %d)", x.G);
+  }
+  return BSA_OK;
+}
+
+bsa_status_t check_ptr(const void* p, const char* name) {
+  if (p == nullptr) return fail(BSA_ERR_NULL, "%s is NULL", name);
+  if (!aligned16(p)) return fail(BSA_ERR_ALIGN, "%s is not 16-byte aligned", name);
+  return BSA_OK;
+}
+
+bsa_status_t hip_result(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(BSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+#define BSA_TRY(expr)                  \
+  do {                                 \
+    bsa_status_t st_ = (expr);         \
+    if (st_ != BSA_OK) return st_;     \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* bsa_status_string(int status) {
+  switch (status) {
+    case BSA_OK: return "ok";
+    case BSA_ERR_NULL: return "null pointer";
+    case BSA_ERR_SHAPE: return "invalid shape";
+    case BSA_ERR_UNSUPPORTED: return "unsupported parameter";
+    case BSA_ERR_ALIGN: return "misaligned pointer";
+    case BSA_ERR_WORKSPACE: return "workspace too small";
+    case BSA_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* bsa_last_error(void) { return g_last_error; }
+
+int bsa_version(void) { return 100; }
+
+bsa_status_t bsa_pool_landmarks(const bsa_params_t* params, const void* k, void* lm,
+                                void* stream) {
+  bsa::Shape s;
+  BSA_TRY(make_shape(params, kPool, &s));
+  BSA_TRY(check_ptr(k, "k"));
+  BSA_TRY(check_ptr(lm, "lm"));
+  return hip_result(bsa::launch_pool_landmarks(s, k, lm, (hipStream_t)stream), "pool_landmarks");
+}
+
+size_t bsa_select_workspace_bytes(const bsa_params_t* params) {
+  bsa::Shape s;
+  if (make_shape(params, kSelect, &s) != BSA_OK) return 0;
+  return bsa::select_ws_bytes(s);
+}
+
+bsa_status_t bsa_select_topk(const bsa_params_t* params, const void* q, const void* lm,
+                             int32_t* idx, float* sc, void* ws, size_t ws_bytes, void* stream) {
+  bsa::Shape s;
+  BSA_TRY(make_shape(params, kSelect, &s));
+  BSA_TRY(check_ptr(q, "q"));
+  BSA_TRY(check_ptr(lm, "lm"));
+  BSA_TRY(check_ptr(idx, "idx"));
+  BSA_TRY(check_ptr(sc, "sc"));
+  const size_t need = bsa::select_ws_bytes(s);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(BSA_ERR_WORKSPACE, "select workspace needs %zu bytes (got %zu%s)", need, ws_bytes,
+                ws == nullptr ? ", NULL pointer" : "");
+  if (((uintptr_t)ws & 255u) != 0) return fail(BSA_ERR_ALIGN, "ws is not 256-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  float* qbar = (float*)ws;
+  float* scores = (float*)((char*)ws + bsa::select_ws_qbar_bytes(s));
+  hipError_t e = bsa::launch_selector_vectors(s, q, qbar, st);
+  if (e == hipSuccess) e = bsa::launch_block_scores(s, qbar, lm, scores, st);
+  if (e == hipSuccess) e = bsa::launch_topk(s, scores, idx, sc, st);
+  return hip_result(e, "select_topk");
+}
+
+bsa_status_t bsa_attend_prefill(const bsa_params_t* params, const void* q, const void* k,
+                                const void* v, const void* lm, const int32_t* idx,
+                                const float* sc, void* out, float* lse, void* stream) {
+  bsa::Shape s;
+  BSA_TRY(make_shape(params, kPrefill, &s));
+  BSA_TRY(check_ptr(q, "q"));
+  BSA_TRY(check_ptr(k, "k"));
+  BSA_TRY(check_ptr(v, "v"));
+  BSA_TRY(check_ptr(idx, "idx"));
+  BSA_TRY(check_ptr(out, "out"));
+  if (s.mode == BSA_MODE_SAS) BSA_TRY(check_ptr(sc, "sc"));
+  if (s.mode == BSA_MODE_HILS) {
+    BSA_TRY(check_ptr(lm, "lm"));
+    if (lse != nullptr) return fail(BSA_ERR_UNSUPPORTED, "lse is not defined for HILS; pass NULL");
+  }
+  if (lse != nullptr) BSA_TRY(check_ptr(lse, "lse"));
+  return hip_result(bsa::launch_attend_prefill(s, q, k, v, lm, idx, sc, out, lse,
+                                               (hipStream_t)stream),
+                    "attend_prefill");
+}
+
+size_t bsa_decode_workspace_bytes(const bsa_params_t* params) {
+  bsa::Shape s;
+  if (make_shape(params, kDecode, &s) != BSA_OK) return 0;
+  return bsa::decode_ws_bytes(s);
+}
+
+bsa_status_t bsa_attend_decode(const bsa_params_t* params, const void* q, const void* kc,
+                               const void* vc, const void* lm, const int32_t* idx,
+                               const float* sc, void* out, float* lse, void* ws,
+                               size_t ws_bytes, void* stream) {
+  bsa::Shape s;
+  BSA_TRY(make_shape(params, kDecode, &s));
+  BSA_TRY(check_ptr(q, "q"));
+  BSA_TRY(check_ptr(kc, "kc"));
+  BSA_TRY(check_ptr(vc, "vc"));
+  BSA_TRY(check_ptr(idx, "idx"));
+  BSA_TRY(check_ptr(out, "out"));
+  if (s.mode == BSA_MODE_SAS) BSA_TRY(check_ptr(sc, "sc"));
+  if (s.mode == BSA_MODE_HILS) {
+    BSA_TRY(check_ptr(lm, "lm"));
+    if (lse != nullptr) return fail(BSA_ERR_UNSUPPORTED, "lse is not defined for HILS; pass NULL");
+  }
+  if (lse != nullptr) BSA_TRY(check_ptr(lse, "lse"));
+  const size_t need = bsa::decode_ws_bytes(s);
+  if (need > 0) {
+    if (ws == nullptr || ws_bytes < need)
+      return fail(BSA_ERR_WORKSPACE, "decode workspace needs %zu bytes (got %zu%s)", need,
+                  ws_bytes, ws == nullptr ? ", NULL pointer" : "");
+    if (((uintptr_t)ws & 255u) != 0) return fail(BSA_ERR_ALIGN, "ws is not 256-byte aligned");
+  }
+  return hip_result(bsa::launch_attend_decode(s, q, kc, vc, lm, idx, sc, out, lse, ws,
+                                              (hipStream_t)stream),
+                    "attend_decode");
+}
+
+}  // extern "C"

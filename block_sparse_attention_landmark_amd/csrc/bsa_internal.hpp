@@ -1,0 +1,47 @@
+// Internal (C++) interface between the C-ABI entry points and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bsa {
+
+// Validated sizes of one call, derived from bsa_params_t.
+struct Shape {
+  int B, Hq, Hkv, G, D;
+  int Tq, Tk;       // query tokens (prefill: == Tk; decode: 1) and key tokens
+  int NB;           // key blocks: ceil(Tk / 64)
+  int R;            // selection rows per (b, kv group): prefill ceil(Tq / 64), decode 1
+  int c_dec;        // decode: block of the query token (Tk - 1) / 64
+  int topk, n_sink, n_local, NA;
+  int mode;         // 0 plain, 1 sas, 2 hils
+  bool bf16, decode;
+  float scale;      // softmax scale (already defaulted to 1/sqrt(D))
+};
+
+// Block index of selection row r (prefill: r; decode: the query token's block).
+inline int row_block(const Shape& s, int r) { return s.decode ? s.c_dec : r; }
+
+// Workspace of bsa_select_topk: selector vectors then scores, each 256-byte aligned.
+size_t select_ws_qbar_bytes(const Shape& s);
+size_t select_ws_scores_bytes(const Shape& s);
+size_t select_ws_bytes(const Shape& s);
+// Workspace of bsa_attend_decode: split partials.
+int decode_splits(const Shape& s);
+size_t decode_ws_bytes(const Shape& s);
+
+hipError_t launch_pool_landmarks(const Shape& s, const void* k, void* lm, hipStream_t st);
+hipError_t launch_selector_vectors(const Shape& s, const void* q, float* qbar, hipStream_t st);
+hipError_t launch_block_scores(const Shape& s, const float* qbar, const void* lm, float* scores,
+                               hipStream_t st);
+hipError_t launch_topk(const Shape& s, const float* scores, int32_t* idx, float* sc,
+                       hipStream_t st);
+hipError_t launch_attend_prefill(const Shape& s, const void* q, const void* k, const void* v,
+                                 const void* lm, const int32_t* idx, const float* sc, void* out,
+                                 float* lse, hipStream_t st);
+hipError_t launch_attend_decode(const Shape& s, const void* q, const void* kc, const void* vc,
+                                const void* lm, const int32_t* idx, const float* sc, void* out,
+                                float* lse, void* ws, hipStream_t st);
+
+}  // namespace bsa

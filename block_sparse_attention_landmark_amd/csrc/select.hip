@@ -1,0 +1,317 @@
+// Block scoring and top-K selection.
+//
+// Scores (SAS page, summary paragraph 1: a light selector scores each unit of context; LSA
+// page, "The index stops scanning the whole context", paragraph 2: each contiguous block is
+// scored): S[c][j] = qbar_c . L_j for every block j <= c.  With bf16 landmarks the product runs
+// on the matrix cores: the float32 selector vector is split into three bf16 terms
+// (hi + mid + lo, which together carry its 24 significant bits), so every landmark product is
+// exact in the float32 accumulator and only the float32 summation rounds.
+//
+// Selection (SAS page, summary paragraph 1 and "How to apply": hard top-K; LSA page, first
+// section, paragraph 4: the start of the context and a recent window are always added; SAS
+// page, summary paragraph 3: the current block is always kept): among the candidate blocks
+// n_sink <= j <= c - n_local, take the K highest scores, lower block index first among equal
+// scores, via a 4-pass 8-bit radix select on order-preserving score keys followed by an
+// index-ordered compaction.  The attended set is written ascending: sink blocks, the chosen
+// candidates, then the local window ending at c; padding is -1.
+#include "bsa_common.hpp"
+#include "bsa_internal.hpp"
+
+namespace bsa {
+
+static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+__host__ __device__ inline size_t tri(size_t n) { return n * (n + 1) / 2; }
+
+size_t select_ws_qbar_bytes(const Shape& s) {
+  return align256((size_t)s.B * s.Hkv * s.R * s.D * sizeof(float));
+}
+size_t select_ws_scores_bytes(const Shape& s) {
+  const size_t per = s.decode ? (size_t)s.NB : tri((size_t)s.R);
+  return align256((size_t)s.B * s.Hkv * per * sizeof(float));
+}
+size_t select_ws_bytes(const Shape& s) { return select_ws_qbar_bytes(s) + select_ws_scores_bytes(s); }
+
+// ---------------------------------------------------------------------------------------------
+// scores, bf16 landmarks: 64x64 tiles per workgroup, one 32x32 MFMA sub-tile per wave
+// ---------------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void score_mfma_kernel(const float* __restrict__ qbar,
+                                                         const bf16* __restrict__ lm,
+                                                         float* __restrict__ scores, int R,
+                                                         int NB, int c_dec) {
+  const int bg = blockIdx.y;
+  int ti, tj;
+  if (c_dec >= 0) {
+    ti = 0;
+    tj = blockIdx.x;
+  } else {
+    // linear index p over the lower-triangular tile pairs (ti >= tj)
+    const long p = blockIdx.x;
+    long t = (long)((sqrt(8.0 * (double)p + 1.0) - 1.0) * 0.5);
+    while (tri(t + 1) <= (size_t)p) ++t;
+    while (tri(t) > (size_t)p) --t;
+    ti = (int)t;
+    tj = (int)(p - (long)tri(t));
+  }
+  const int w = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int half = lane / 32;
+  const int l32 = lane % 32;
+  const int row0 = ti * 64 + (w / 2) * 32;
+  const int col0 = tj * 64 + (w % 2) * 32;
+  const int last_row = min(row0 + 31, R - 1);
+  if (row0 >= R) return;
+  const int max_c = (c_dec >= 0) ? c_dec : last_row;
+  if (col0 > max_c || col0 >= NB) return;
+
+  const int r = row0 + l32;
+  const int j = col0 + l32;
+  const float* qrow = qbar + ((size_t)bg * R + min(r, R - 1)) * D;
+  const bf16* lrow = lm + ((size_t)bg * NB + min(j, NB - 1)) * D;
+  f32x16 acc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    const int d0 = 16 * s + 8 * half;
+    bf16x8 hi, mid, lo, bl;
+    f32x4 x0 = *reinterpret_cast<const f32x4*>(qrow + d0);
+    f32x4 x1 = *reinterpret_cast<const f32x4*>(qrow + d0 + 4);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = (e < 4) ? x0[e] : x1[e - 4];
+      if (r >= R) x = 0.0f;
+      const bf16 h = f2bf(x);
+      const float r1 = x - bf2f(h);          // exact in float32
+      const bf16 m = f2bf(r1);
+      hi[e] = h;
+      mid[e] = m;
+      lo[e] = f2bf(r1 - bf2f(m));            // the remaining <= 8 significant bits
+    }
+    u32x4 lraw = *reinterpret_cast<const u32x4*>(lrow + d0);
+    bl = __builtin_bit_cast(bf16x8, lraw);
+    if (j >= NB) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bl[e] = f2bf(0.0f);
+    }
+    acc = mfma32(hi, bl, acc);
+    acc = mfma32(mid, bl, acc);
+    acc = mfma32(lo, bl, acc);
+  }
+  if (j >= NB) return;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int rr = row0 + 8 * (i / 4) + 4 * half + (i % 4);
+    if (rr >= R) continue;
+    const int cc = (c_dec >= 0) ? c_dec : rr;
+    if (j > cc) continue;
+    const size_t off = (c_dec >= 0) ? (size_t)bg * NB : (size_t)bg * tri(R) + tri(rr);
+    scores[off + j] = acc[i];
+  }
+}
+
+// scores, float32 landmarks: one thread per (row, block), float64 accumulation
+template <int D>
+__global__ __launch_bounds__(256) void score_f32_kernel(const float* __restrict__ qbar,
+                                                        const float* __restrict__ lm,
+                                                        float* __restrict__ scores, int R,
+                                                        int NB, int c_dec) {
+  const int r = blockIdx.y;
+  const int bg = blockIdx.z;
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  const int c = (c_dec >= 0) ? c_dec : r;
+  if (j > c || j >= NB) return;
+  const float* qrow = qbar + ((size_t)bg * R + r) * D;
+  const float* lrow = lm + ((size_t)bg * NB + j) * D;
+  double acc = 0.0;
+#pragma unroll 8
+  for (int d = 0; d < D; ++d) acc += (double)qrow[d] * (double)lrow[d];
+  const size_t off = (c_dec >= 0) ? (size_t)bg * NB : (size_t)bg * tri(R) + tri(r);
+  scores[off + j] = (float)acc;
+}
+
+hipError_t launch_block_scores(const Shape& s, const float* qbar, const void* lm, float* scores,
+                               hipStream_t st) {
+  const int c_dec = s.decode ? s.c_dec : -1;
+  if (s.bf16) {
+    dim3 grid;
+    if (s.decode) {
+      grid = dim3((s.c_dec + 1 + 63) / 64, s.B * s.Hkv);
+    } else {
+      const size_t nt = (s.R + 63) / 64;
+      grid = dim3((unsigned)tri(nt), s.B * s.Hkv);
+    }
+    if (s.D == 128)
+      hipLaunchKernelGGL(score_mfma_kernel<128>, grid, dim3(256), 0, st, qbar, (const bf16*)lm,
+                         scores, s.R, s.NB, c_dec);
+    else
+      hipLaunchKernelGGL(score_mfma_kernel<64>, grid, dim3(256), 0, st, qbar, (const bf16*)lm,
+                         scores, s.R, s.NB, c_dec);
+  } else {
+    const int maxc = s.decode ? s.c_dec : s.R - 1;
+    dim3 grid((maxc + 1 + 255) / 256, s.R, s.B * s.Hkv);
+    if (s.D == 128)
+      hipLaunchKernelGGL(score_f32_kernel<128>, grid, dim3(256), 0, st, qbar, (const float*)lm,
+                         scores, s.R, s.NB, c_dec);
+    else
+      hipLaunchKernelGGL(score_f32_kernel<64>, grid, dim3(256), 0, st, qbar, (const float*)lm,
+                         scores, s.R, s.NB, c_dec);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// top-K: one workgroup of 256 threads per selection row
+// ---------------------------------------------------------------------------------------------
+constexpr int kTopkThreads = 256;
+constexpr int kTopkWaves = kTopkThreads / kWave;
+constexpr int kKeyCache = 12288;   // candidate keys held in LDS; longer rows re-read L2
+
+// exclusive prefix sum over the workgroup; *total receives the sum of all x
+__device__ __forceinline__ int block_exclusive_scan(int x, int* sbuf, int* total) {
+  const int lane = threadIdx.x % kWave;
+  const int w = threadIdx.x / kWave;
+  int incl = x;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += y;
+  }
+  if (lane == kWave - 1) sbuf[w] = incl;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kTopkWaves; ++i) {
+    const int v = sbuf[i];
+    base += (i < w) ? v : 0;
+    tot += v;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + incl - x;
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ scores,
+                                                            int32_t* __restrict__ idx,
+                                                            float* __restrict__ sc, int R,
+                                                            int NB, int c_dec, int topk,
+                                                            int n_sink, int n_local, int NA) {
+  __shared__ uint32_t skeys[kKeyCache];
+  __shared__ int hist[256];
+  __shared__ int sbuf[kTopkWaves];
+  __shared__ int sh_digit, sh_krem;
+
+  const int r = blockIdx.x;
+  const int bg = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int c = (c_dec >= 0) ? c_dec : r;
+  const float* srow = scores + ((c_dec >= 0) ? (size_t)bg * NB : (size_t)bg * tri(R) + tri(c));
+  int32_t* oidx = idx + ((size_t)bg * R + r) * NA;
+  float* osc = sc + ((size_t)bg * R + r) * NA;
+
+  const int n_sink_eff = min(n_sink, c + 1);
+  const int lo = n_sink;                       // first candidate
+  const int hi = c - n_local;                  // last candidate
+  const int n = max(0, hi - lo + 1);
+  const int K = min(topk, n);
+  const int loc_beg = max(n_sink, c - n_local + 1);
+  const int n_loc = max(0, c - loc_beg + 1);
+
+  // forced entries and padding
+  for (int i = tid; i < NA; i += kTopkThreads) {
+    int32_t jj = -1;
+    float ss = 0.0f;
+    if (i < n_sink_eff) {
+      jj = i;
+    } else if (i >= n_sink_eff + K && i < n_sink_eff + K + n_loc) {
+      jj = loc_beg + (i - n_sink_eff - K);
+    }
+    if (jj >= 0) ss = srow[jj];
+    if (i < n_sink_eff || i >= n_sink_eff + K) {
+      oidx[i] = jj;
+      osc[i] = ss;
+    }
+  }
+  if (K == 0) return;
+  if (K == n) {
+    for (int i = tid; i < n; i += kTopkThreads) {
+      oidx[n_sink_eff + i] = lo + i;
+      osc[n_sink_eff + i] = srow[lo + i];
+    }
+    return;
+  }
+
+  const bool cached = n <= kKeyCache;
+  if (cached) {
+    for (int i = tid; i < n; i += kTopkThreads) skeys[i] = float_key(srow[lo + i]);
+  }
+  __syncthreads();
+  auto key_at = [&](int i) -> uint32_t { return cached ? skeys[i] : float_key(srow[lo + i]); };
+
+  // radix select of the K-th largest key
+  uint32_t prefix = 0u, mask = 0u;
+  int krem = K;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    hist[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += kTopkThreads) {
+      const uint32_t key = key_at(i);
+      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+    }
+    __syncthreads();
+    const int cnt = hist[255 - tid];         // thread t holds digit 255 - t
+    int tot;
+    const int above = block_exclusive_scan(cnt, sbuf, &tot);   // keys with a larger digit
+    if (above < krem && krem <= above + cnt) {
+      sh_digit = 255 - tid;
+      sh_krem = krem - above;
+    }
+    __syncthreads();
+    prefix |= (uint32_t)sh_digit << shift;
+    mask |= 255u << shift;
+    krem = sh_krem;
+    __syncthreads();
+  }
+  const uint32_t tau = prefix;
+  const int need_eq = krem;                  // keys equal to tau to take, lowest index first
+
+  // index-ordered compaction: each thread owns a contiguous slice
+  const int per = (n + kTopkThreads - 1) / kTopkThreads;
+  const int beg = min(n, tid * per);
+  const int end = min(n, beg + per);
+  int gt = 0, eq = 0;
+  for (int i = beg; i < end; ++i) {
+    const uint32_t key = key_at(i);
+    gt += key > tau;
+    eq += key == tau;
+  }
+  int tot;
+  const int eq_before = block_exclusive_scan(eq, sbuf, &tot);
+  const int take_eq = min(eq, max(0, need_eq - eq_before));
+  int pos = block_exclusive_scan(gt + take_eq, sbuf, &tot);
+  int eq_seen = 0;
+  for (int i = beg; i < end; ++i) {
+    const uint32_t key = key_at(i);
+    bool take = key > tau;
+    if (key == tau) {
+      take = eq_seen < take_eq;
+      ++eq_seen;
+    }
+    if (take) {
+      oidx[n_sink_eff + pos] = lo + i;
+      osc[n_sink_eff + pos] = srow[lo + i];
+      ++pos;
+    }
+  }
+}
+
+hipError_t launch_topk(const Shape& s, const float* scores, int32_t* idx, float* sc,
+                       hipStream_t st) {
+  dim3 grid(s.R, s.B * s.Hkv);
+  hipLaunchKernelGGL(topk_kernel, grid, dim3(kTopkThreads), 0, st, scores, idx, sc, s.R, s.NB,
+                     s.decode ? s.c_dec : -1, s.topk, s.n_sink, s.n_local, s.NA);
+  return hipGetLastError();
+}
+
+}  // namespace bsa

@@ -1,0 +1,156 @@
+/*
+ * bsa.h -- selector-driven block-sparse landmark attention for AMD Instinct MI355X (gfx950).
+ *
+ * The method (from the pages this library implements):
+ *  1. keys are pooled into one landmark per 64-token block (LSA page, "Latent Sparse
+ *     Attention", section "The index stops scanning the whole context", paragraph 3:
+ *     neighbouring keys are merged before indexing; the HiLS page calls such per-chunk
+ *     vectors landmarks);
+ *  2. each query block scores the landmarks with a light selector and keeps the hard top-K
+ *     blocks (SAS page, "Scientists taught transformers to select context directly...",
+ *     summary paragraph 1 and "How to apply");
+ *  3. attention runs only over the chosen blocks plus the start of the context and a recent
+ *     window (LSA page, first section, paragraph 4), the current block always kept (SAS
+ *     page, summary paragraph 3);
+ *  4. variants: SAS adds a log-form gate inside the softmax, normalised against the current
+ *     block (SAS page, summary paragraph 3, "Key facts" item 3); HiLS attends to each chunk
+ *     separately and merges the chunk results by the chunks' retrieval scores (HiLS page,
+ *     "HiLS-Attention: hierarchical sparse attention...", summary paragraph 2).
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers owned by the caller, contiguous, in the layouts
+ *    given below, 16-byte aligned.  The library never allocates, frees, synchronises or keeps
+ *    a pointer after a call returns.  Work is enqueued on `stream` (a hipStream_t passed as
+ *    void*; NULL = the default stream) and completes asynchronously.
+ *  - Layouts are head-major: q [B,Hq,Tq,D]; k, v [B,Hkv,Tk,D]; landmarks [B,Hkv,NB,D] with
+ *    NB = ceil(Tk/64); selection rows [B,Hkv,R,NA] with R = ceil(Tq/64) for prefill and 1 for
+ *    decode and NA = n_sink + n_local + topk.  Query head h uses kv head h / (Hq/Hkv).
+ *  - Element type of q, k, v, landmarks and outputs is params->dtype (float32 or bf16);
+ *    idx is int32, sc and lse are float32.
+ *  - Arguments are checked before anything is launched: on an invalid argument the call
+ *    returns a non-zero status, launches nothing and leaves every buffer untouched;
+ *    bsa_last_error() then describes the failure (thread-local).  A failed kernel launch
+ *    returns BSA_ERR_HIP.  No call aborts, exits or throws.
+ *  - The library holds no state: calls on different streams may run concurrently.
+ */
+#ifndef BSA_H_
+#define BSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum bsa_status {
+  BSA_OK = 0,
+  BSA_ERR_NULL = 1,        /* a required pointer is NULL */
+  BSA_ERR_SHAPE = 2,       /* sizes inconsistent or out of range */
+  BSA_ERR_UNSUPPORTED = 3, /* a value outside what the kernels implement (D, block, dtype, mode) */
+  BSA_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned */
+  BSA_ERR_WORKSPACE = 5,   /* workspace pointer NULL or smaller than required */
+  BSA_ERR_HIP = 6          /* the HIP runtime reported an error at launch */
+} bsa_status_t;
+
+typedef enum bsa_dtype { BSA_DTYPE_F32 = 0, BSA_DTYPE_BF16 = 1 } bsa_dtype_t;
+
+typedef enum bsa_mode {
+  BSA_MODE_PLAIN = 0, /* softmax over the attended keys */
+  BSA_MODE_SAS = 1,   /* + gate log sigmoid(S_j - S_c) on every logit of attended block j != c */
+  BSA_MODE_HILS = 2   /* per-chunk softmax, chunks merged by softmax_j(q . L_j * scale) */
+} bsa_mode_t;
+
+typedef struct bsa_params {
+  int32_t batch;    /* B >= 1 (prefill: sequences; decode: sequences, one query token each) */
+  int32_t heads_q;  /* Hq >= 1, a multiple of heads_kv */
+  int32_t heads_kv; /* Hkv >= 1 */
+  int32_t head_dim; /* D: 64 or 128 */
+  int32_t seq_q;    /* prefill: == seq_k; decode: 1 (the query is the token at seq_k - 1) */
+  int32_t seq_k;    /* Tk >= 1 tokens in k, v (a decode cache includes the query's own k, v) */
+  int32_t block;    /* must be 64 */
+  int32_t topk;     /* K >= 0 blocks chosen beyond the sink and the local window */
+  int32_t n_sink;   /* >= 0 leading blocks always attended (the start of the context) */
+  int32_t n_local;  /* >= 1 blocks ending at the current one always attended */
+  float scale;      /* softmax scale; 0 selects 1/sqrt(head_dim) */
+  int32_t dtype;    /* bsa_dtype_t */
+  int32_t mode;     /* bsa_mode_t (used by the attend calls) */
+} bsa_params_t;
+
+/*
+ * Landmarks: lm[b,g,j,:] = mean of k[b,g,t,:] over the tokens t of block j (a partial last
+ * block averages the tokens present), accumulated in float64 and rounded once, to nearest
+ * even, to the dtype.
+ *   k  [B,Hkv,Tk,D] (input)      lm [B,Hkv,NB,D] (output)
+ */
+bsa_status_t bsa_pool_landmarks(const bsa_params_t* params, const void* k, void* lm,
+                                void* stream);
+
+/* Bytes of workspace bsa_select_topk needs for these params (0 if params are invalid). */
+size_t bsa_select_workspace_bytes(const bsa_params_t* params);
+
+/*
+ * Selection.  Selector vector qbar = sum over the query heads of each kv group of the mean
+ * query of each 64-token query block (decode: of the one query token), kept in float32.
+ * Scores S[c][j] = qbar_c . L_j for j <= c (no softmax scale).  Candidates are the blocks
+ * n_sink <= j <= c - n_local; the K = min(topk, #candidates) highest scores are chosen, the
+ * lower block index first among equal scores.  Row c of idx lists, ascending: blocks
+ * 0..min(n_sink, c+1)-1, the chosen candidates, then blocks max(n_sink, c-n_local+1)..c,
+ * padded with -1; sc holds S[c][j] for each listed block (0 in the padding).  The current
+ * block c is therefore always the last valid entry.
+ *   q    [B,Hq,Tq,D]  (prefill: Tq == Tk; decode: Tq == 1)
+ *   lm   [B,Hkv,NB,D] landmarks of the Tk keys (bsa_pool_landmarks)
+ *   idx  [B,Hkv,R,NA] int32 output, sc [B,Hkv,R,NA] float32 output
+ *   ws   device workspace of at least bsa_select_workspace_bytes(params) bytes (the selector
+ *        vectors and the score rows); contents on entry are ignored.
+ */
+bsa_status_t bsa_select_topk(const bsa_params_t* params, const void* q, const void* lm,
+                             int32_t* idx, float* sc, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Prefill attention (seq_q == seq_k == T).  For query token t of head h in block c = t/64 and
+ * the attended set A_c = row c of idx (entries must be ascending, <= c, end with c and be
+ * followed only by -1 padding):
+ *   PLAIN: o = sum_u softmax_u(scale * q.k_u) v_u over keys u in the blocks of A_c, u <= t;
+ *   SAS:   the logit of each key of block j != c gets + log sigmoid(sc_j - sc_c);
+ *   HILS:  o = sum_{j in A_c} w_j o_j, o_j = softmax attention over the keys u <= t of block
+ *          j alone, w = softmax_j(scale * q.L_j); needs lm and NA <= 64.
+ *   q [B,Hq,T,D], k/v [B,Hkv,T,D], lm [B,Hkv,NB,D] (HILS only, else may be NULL),
+ *   idx/sc [B,Hkv,R,NA] from bsa_select_topk (sc may be NULL for PLAIN and HILS),
+ *   out [B,Hq,T,D] output, lse [B,Hq,T] float32 output = log of the softmax denominator
+ *   (PLAIN/SAS; may be NULL; must be NULL for HILS).
+ */
+bsa_status_t bsa_attend_prefill(const bsa_params_t* params, const void* q, const void* k,
+                                const void* v, const void* lm, const int32_t* idx,
+                                const float* sc, void* out, float* lse, void* stream);
+
+/* Bytes of workspace bsa_attend_decode needs for these params (0 if params are invalid). */
+size_t bsa_decode_workspace_bytes(const bsa_params_t* params);
+
+/*
+ * Decode attention (seq_q == 1): the query of each sequence is the token at position Tk - 1
+ * and sees every key of its attended blocks; same PLAIN / SAS / HILS rules as prefill.  The
+ * attended blocks are split over workgroups and the partial softmax states merged through
+ * their log-sum-exp.
+ *   q [B,Hq,1,D], kc/vc [B,Hkv,Tk,D] cache, lm [B,Hkv,NB,D] (HILS only), idx/sc [B,Hkv,1,NA],
+ *   out [B,Hq,1,D] output, lse [B,Hq] (PLAIN/SAS, may be NULL; NULL for HILS),
+ *   ws device workspace of bsa_decode_workspace_bytes(params) bytes (may be NULL if that is 0).
+ *   The bf16 path needs Hq/Hkv <= 32.
+ */
+bsa_status_t bsa_attend_decode(const bsa_params_t* params, const void* q, const void* kc,
+                               const void* vc, const void* lm, const int32_t* idx,
+                               const float* sc, void* out, float* lse, void* ws,
+                               size_t ws_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* bsa_status_string(int status);
+/* Detail of the last failed call on this thread ("" if none). */
+const char* bsa_last_error(void);
+/* Library version, e.g. 100 for 1.0.0. */
+int bsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSA_H_ */

@@ -1,0 +1,81 @@
+"""Comparison helpers shared by the GPU parity tests.
+
+Bars (written here once, used by every parity test):
+* attended block indices: bit-exact, except where every block in which the two selections
+  differ has an oracle score within 1e-3 * |S_K| of the K-th candidate score S_K (a near tie:
+  both selections are then correct);
+* bf16 outputs: max-abs error <= 2e-2 and mean |error| / mean |reference| <= 5e-3;
+* float32 outputs: max-abs error <= 1e-4;
+* log-sum-exp: abs error <= 1e-3 (bf16 inputs) or 1e-4 (float32);
+* landmarks: bit-exact (bf16); float32 within one float32 ulp of the oracle's rounding.
+"""
+
+import numpy as np
+import torch
+
+import oracle as O
+
+TIE_BAND = 1e-3
+BF16_MAX_ABS = 2e-2
+BF16_MEAN_REL = 5e-3
+F32_MAX_ABS = 1e-4
+
+
+def host64(t: torch.Tensor) -> np.ndarray:
+    """Exact float64 copy of a device tensor (bf16 and float32 are exact in float64)."""
+    return t.detach().to("cpu", torch.float32).numpy().astype(np.float64) if t.dtype != torch.float64 \
+        else t.detach().cpu().numpy()
+
+
+def check_selection(gpu_row, s_row, c, topk, n_sink=1, n_local=2, where=""):
+    """gpu_row: the device's attended set (int list, -1 padded).  s_row: oracle scores [NB].
+
+    Returns the device's attended set as an int64 array (valid entries only).
+    """
+    A_dev = np.array([j for j in gpu_row if j >= 0], dtype=np.int64)
+    A_ref, _ = O.select_row(s_row, c, topk, n_sink, n_local)
+    assert np.all(np.diff(A_dev) > 0), f"{where}: attended set not ascending: {A_dev}"
+    assert A_dev.size == A_ref.size, f"{where}: size {A_dev.size} != {A_ref.size}"
+    if np.array_equal(A_dev, A_ref):
+        return A_dev
+    diff = np.setxor1d(A_dev, A_ref)
+    cand = np.arange(n_sink, c - n_local + 1)
+    order = np.lexsort((cand, -s_row[cand]))
+    K = min(topk, cand.size)
+    s_k = s_row[cand[order[K - 1]]]
+    band = TIE_BAND * abs(s_k)
+    bad = [int(j) for j in diff if abs(s_row[j] - s_k) > band]
+    assert not bad, (f"{where}: selection differs outside the near-tie band at blocks {bad}; "
+                     f"S_K={s_k}, scores={[float(s_row[j]) for j in diff]}")
+    # forced blocks must be there regardless
+    forced = set(range(min(n_sink, c + 1))) | set(range(max(0, c - n_local + 1), c + 1))
+    assert forced <= set(A_dev.tolist()), f"{where}: forced blocks missing"
+    return A_dev
+
+
+def check_out(dev: np.ndarray, ref: np.ndarray, dtype: str, where=""):
+    err = np.abs(dev - ref)
+    if dtype == "bf16":
+        mx = float(err.max()) if err.size else 0.0
+        rel = float(err.mean() / max(np.abs(ref).mean(), 1e-30)) if err.size else 0.0
+        assert mx <= BF16_MAX_ABS, f"{where}: max-abs {mx:.3e} > {BF16_MAX_ABS}"
+        assert rel <= BF16_MEAN_REL, f"{where}: mean-rel {rel:.3e} > {BF16_MEAN_REL}"
+        return mx, rel
+    mx = float(err.max()) if err.size else 0.0
+    assert mx <= F32_MAX_ABS, f"{where}: max-abs {mx:.3e} > {F32_MAX_ABS}"
+    return mx, 0.0
+
+
+def check_lse(dev: np.ndarray, ref: np.ndarray, dtype: str, where=""):
+    tol = 1e-3 if dtype == "bf16" else 1e-4
+    mx = float(np.abs(dev - ref).max()) if dev.size else 0.0
+    assert mx <= tol, f"{where}: lse max-abs {mx:.3e} > {tol}"
+
+
+def check_landmarks(dev: np.ndarray, ref: np.ndarray, dtype: str, where=""):
+    if dtype == "bf16":
+        ndiff = int(np.count_nonzero(dev != ref))
+        assert ndiff == 0, f"{where}: {ndiff} landmark elements differ from the oracle"
+    else:
+        ulp = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
+        assert np.all(np.abs(dev - ref) <= ulp), f"{where}: float32 landmarks off by more than 1 ulp"

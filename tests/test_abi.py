@@ -1,0 +1,168 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function include/bsa.h
+declares, and rejects invalid arguments with the documented status before launching anything.
+
+Every call here fails validation, so no kernel is launched and no pointer is dereferenced
+(the pointers passed are fake, aligned addresses).
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsa.h")
+
+import block_sparse_attention_landmark_amd as bsa  # noqa: E402
+
+OK, NULL, SHAPE, UNSUP, ALIGN, WS, HIP = range(7)
+FAKE = ctypes.c_void_p(1 << 20)          # aligned, never dereferenced
+MIS = ctypes.c_void_p((1 << 20) + 4)     # misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bsa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bsa.library_path()):
+        pytest.fail("libbsa.so is not built; run `python -m block_sparse_attention_landmark_amd.build`")
+    return bsa.load_library()
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for n in ["bsa_pool_landmarks", "bsa_select_topk", "bsa_attend_prefill", "bsa_attend_decode"]:
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", bsa.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (bsa_\w+)", out))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, f"declared but not exported: {missing}"
+    for n in declared_functions():
+        assert hasattr(lib, n)
+
+
+def test_params_struct_matches_header_layout():
+    # 12 int32 fields + 1 float, no padding
+    assert ctypes.sizeof(bsa.Params) == 13 * 4
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct bsa_params \{(.*?)\} bsa_params_t;", text, re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = re.findall(r"(int32_t|float)\s+(\w+);", body)
+    assert [f for _, f in fields] == [f for f, _ in bsa.Params._fields_]
+
+
+def test_status_strings_and_version(lib):
+    for s in range(7):
+        assert lib.bsa_status_string(s)
+    assert lib.bsa_status_string(99) == b"unknown status"
+    assert lib.bsa_version() >= 100
+
+
+def _p(**kw):
+    base = dict(B=1, Hq=4, Hkv=1, D=128, seq_q=256, seq_k=256, dtype=bsa.torch.bfloat16, topk=2)
+    base.update(kw)
+    return bsa.make_params(**base)
+
+
+def _pool(lib, p, k=FAKE, lm=FAKE):
+    return lib.bsa_pool_landmarks(ctypes.byref(p) if p is not None else None, k, lm, None)
+
+
+def test_pool_validation(lib):
+    assert lib.bsa_pool_landmarks(None, FAKE, FAKE, None) == NULL
+    assert b"params" in lib.bsa_last_error()
+    assert _pool(lib, _p(), k=None) == NULL
+    assert _pool(lib, _p(), lm=MIS) == ALIGN
+    assert _pool(lib, _p(D=96)) == UNSUP
+    assert b"head_dim" in lib.bsa_last_error()
+    p = _p()
+    p.block = 32
+    assert _pool(lib, p) == UNSUP
+    p = _p()
+    p.dtype = 7
+    assert _pool(lib, p) == UNSUP
+    assert _pool(lib, _p(Hq=6, Hkv=4)) == SHAPE
+    assert _pool(lib, _p(B=0)) == SHAPE
+
+
+def test_select_validation(lib):
+    def sel(p, ws=FAKE, nbytes=1 << 40, q=FAKE):
+        return lib.bsa_select_topk(ctypes.byref(p), q, FAKE, FAKE, FAKE, ws, nbytes, None)
+
+    assert sel(_p(topk=-1)) == SHAPE
+    p = _p()
+    p.n_local = 0
+    assert sel(p) == SHAPE
+    assert sel(_p(seq_q=128)) == SHAPE          # neither prefill nor decode
+    assert sel(_p(), q=None) == NULL
+    need = lib.bsa_select_workspace_bytes(ctypes.byref(_p()))
+    assert need > 0
+    assert sel(_p(), nbytes=need - 1) == WS
+    assert sel(_p(), ws=None) == WS
+    assert sel(_p(), ws=ctypes.c_void_p((1 << 20) + 16)) == ALIGN
+    bad = _p(D=80)
+    assert lib.bsa_select_workspace_bytes(ctypes.byref(bad)) == 0
+
+
+def test_workspace_sizes_follow_the_shapes(lib):
+    # prefill: float32 selector vectors + lower-triangular float32 score rows
+    p = _p(B=2, Hq=8, Hkv=2, seq_q=64 * 10, seq_k=64 * 10)
+    qbar = 2 * 2 * 10 * 128 * 4
+    scores = 2 * 2 * (10 * 11 // 2) * 4
+    rnd = lambda x: (x + 255) // 256 * 256
+    assert lib.bsa_select_workspace_bytes(ctypes.byref(p)) == rnd(qbar) + rnd(scores)
+    d = _p(B=3, Hq=16, Hkv=2, seq_q=1, seq_k=64 * 9 + 5, topk=4)
+    assert lib.bsa_select_workspace_bytes(ctypes.byref(d)) == rnd(3 * 2 * 128 * 4) + rnd(3 * 2 * 10 * 4)
+    assert lib.bsa_decode_workspace_bytes(ctypes.byref(d)) > 0
+    f = _p(B=3, Hq=16, Hkv=2, seq_q=1, seq_k=640, dtype=bsa.torch.float32)
+    assert lib.bsa_decode_workspace_bytes(ctypes.byref(f)) == 0
+
+
+def test_attend_validation(lib):
+    def pre(p, **kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, lm=None, idx=FAKE, sc=None, out=FAKE, lse=None)
+        a.update(kw)
+        return lib.bsa_attend_prefill(ctypes.byref(p), a["q"], a["k"], a["v"], a["lm"], a["idx"],
+                                      a["sc"], a["out"], a["lse"], None)
+
+    assert pre(_p(mode="sas")) == NULL           # SAS needs sc
+    assert pre(_p(mode="hils")) == NULL          # HILS needs lm
+    assert pre(_p(mode="hils"), lm=FAKE, lse=FAKE) == UNSUP
+    assert pre(_p(mode="hils", topk=62), lm=FAKE) == UNSUP   # NA > 64 for bf16 HILS prefill
+    assert pre(_p(seq_q=1)) == SHAPE
+    assert pre(_p(), out=MIS) == ALIGN
+    p = _p()
+    p.mode = 5
+    assert pre(p) == UNSUP
+    p = _p()
+    p.scale = float("nan")
+    assert pre(p) == SHAPE
+
+    def dec(p, ws=FAKE, nbytes=1 << 40, **kw):
+        a = dict(q=FAKE, kc=FAKE, vc=FAKE, lm=None, idx=FAKE, sc=None, out=FAKE, lse=None)
+        a.update(kw)
+        return lib.bsa_attend_decode(ctypes.byref(p), a["q"], a["kc"], a["vc"], a["lm"], a["idx"],
+                                     a["sc"], a["out"], a["lse"], ws, nbytes, None)
+
+    d = _p(seq_q=1, seq_k=4096)
+    assert dec(_p()) == SHAPE                    # decode needs seq_q == 1
+    assert dec(d, ws=None) == WS
+    assert dec(d, nbytes=10) == WS
+    assert dec(_p(seq_q=1, seq_k=4096, Hq=64, Hkv=1)) == UNSUP   # G > 32 on the bf16 path
+    assert dec(d, vc=None) == NULL
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        bsa.pool_landmarks(torch.zeros(1, 1, 64, 64))

@@ -1,0 +1,293 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Small shapes are compared element by element (several tiles, ragged tails, edge cases: one
+token, exactly one block, K = 0, K >= all candidates, other sink/local sizes, G = 1..32).
+The five workload shapes are run in the launch configuration the benchmark times; their
+outputs are compared on seeded samples of query blocks (sequences for decode) that the
+oracle computes one by one.  Bars are defined in tests/parity_util.py.
+"""
+
+import gc
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import block_sparse_attention_landmark_amd as bsa
+from block_sparse_attention_landmark_amd import synth
+
+from parity_util import (check_landmarks, check_lse, check_out, check_selection, host64)
+
+pytestmark = pytest.mark.gpu
+
+DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib(gpu):
+    bsa.load_library()   # raises if the HIP library is missing: no fallback exists
+    yield
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+# ---------------------------------------------------------------------------------------------
+# per-row oracle checks (shared by the small and the sampled tests)
+# ---------------------------------------------------------------------------------------------
+
+def _check_prefill_rows(q, k, v, res, rows, *, mode, dtype, topk, n_sink, n_local, tag):
+    B, Hq, T, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(D)
+    idx = res["idx"].cpu().numpy()
+    sc = res["sc"].cpu().numpy()
+    worst = [0.0, 0.0]
+    by_group = {}
+    for (b, g, c) in rows:
+        by_group.setdefault((b, g), []).append(c)
+    for (b, g), cs in sorted(by_group.items()):
+        K64, V64 = host64(k[b, g]), host64(v[b, g])
+        lm_ref = O.landmarks(K64[None, None], dtype)[0, 0]
+        check_landmarks(host64(res["lm"][b, g]), lm_ref, dtype, f"{tag} lm b{b} g{g}")
+        for c in cs:
+            lo, hi = c * 64, min(c * 64 + 64, T)
+            qs = host64(q[b, g * G:(g + 1) * G, lo:hi])                     # [G, n, D]
+            qbar = O.selector_vectors(qs[None], 1)[0, 0, 0]
+            s_row = O.block_scores(qbar[None], lm_ref)[0]
+            where = f"{tag} b{b} g{g} c{c}"
+            A = check_selection(idx[b, g, c], s_row, c, topk, n_sink, n_local, where)
+            # the scores listed beside the attended set are the selector scores, to float32
+            # summation accuracy relative to sum_i |qbar_i L_i| (the dot product's scale)
+            cond = np.abs(qbar)[None, :] @ np.abs(lm_ref[A]).T
+            np.testing.assert_array_less(np.abs(sc[b, g, c, : A.size] - s_row[A]),
+                                         2e-6 * cond[0] + 1e-30, err_msg=where)
+            tpos = np.arange(lo, hi)
+            dev = host64(res["out"][b, g * G:(g + 1) * G, lo:hi])
+            for hh in range(G):
+                if mode == "hils":
+                    ref = O.attend_hils_rows(qs[hh], tpos, K64, V64, lm_ref[A], A, scale)
+                else:
+                    gates = O.sas_gates(A, s_row[A], c) if mode == "sas" else np.zeros(A.size)
+                    ref, lse_ref = O.attend_rows(qs[hh], tpos, K64, V64, A, gates, scale)
+                    if res.get("lse") is not None:
+                        check_lse(host64(res["lse"][b, g * G + hh, lo:hi]), lse_ref, dtype, where)
+                mx, rel = check_out(dev[hh], ref, dtype, f"{where} h{hh}")
+                worst = [max(worst[0], mx), max(worst[1], rel)]
+    return worst
+
+
+def _check_decode_pairs(q, kc, vc, res, lm_dev, pairs, *, mode, dtype, topk, n_sink, n_local, tag):
+    B, Hq, _, D = q.shape
+    Hkv, Tk = kc.shape[1], kc.shape[2]
+    G = Hq // Hkv
+    c = (Tk - 1) // 64
+    scale = 1.0 / math.sqrt(D)
+    idx = res["idx"].cpu().numpy()
+    worst = [0.0, 0.0]
+    for (b, g) in pairs:
+        K64, V64 = host64(kc[b, g]), host64(vc[b, g])
+        lm_ref = O.landmarks(K64[None, None], dtype)[0, 0]
+        check_landmarks(host64(lm_dev[b, g]), lm_ref, dtype, f"{tag} lm b{b} g{g}")
+        qs = host64(q[b, g * G:(g + 1) * G, 0])                               # [G, D]
+        qbar = O.decode_selector_vectors(qs[None], 1)[0, 0]
+        s_row = O.block_scores(qbar[None], lm_ref)[0]
+        where = f"{tag} b{b} g{g}"
+        A = check_selection(idx[b, g, 0], s_row, c, topk, n_sink, n_local, where)
+        dev = host64(res["out"][b, g * G:(g + 1) * G, 0])
+        tpos = np.array([Tk - 1])
+        for hh in range(G):
+            if mode == "hils":
+                ref = O.attend_hils_rows(qs[hh][None], tpos, K64, V64, lm_ref[A], A, scale)
+            else:
+                gates = O.sas_gates(A, s_row[A], c) if mode == "sas" else np.zeros(A.size)
+                ref, lse_ref = O.attend_rows(qs[hh][None], tpos, K64, V64, A, gates, scale)
+                if res.get("lse") is not None:
+                    check_lse(host64(res["lse"][b, g * G + hh][None]), lse_ref, dtype, where)
+            mx, rel = check_out(dev[hh][None], ref, dtype, f"{where} h{hh}")
+            worst = [max(worst[0], mx), max(worst[1], rel)]
+    return worst
+
+
+# ---------------------------------------------------------------------------------------------
+# small shapes, every element
+# ---------------------------------------------------------------------------------------------
+
+SMALL_PREFILL = [
+    # id,            B, Hq, Hkv, T,          D,   dtype,  topk, sink, local, data
+    ("g4_tail",      1, 4,  1,   64 * 6 + 17, 128, "bf16", 2,   1, 2, "iid"),
+    ("g2_b2_d64",    2, 4,  2,   64 * 9,      64,  "bf16", 3,   1, 2, "clustered"),
+    ("g1_clustered", 1, 1,  1,   64 * 12 + 1, 128, "bf16", 4,   1, 2, "clustered"),
+    ("g8",           1, 8,  1,   64 * 7 + 40, 128, "bf16", 1,   1, 2, "iid"),
+    ("g4_many",      1, 4,  1,   64 * 40 + 3, 128, "bf16", 8,   1, 2, "clustered"),
+    ("k0",           1, 4,  1,   64 * 5 + 3,  128, "bf16", 0,   1, 2, "iid"),
+    ("kall",         1, 4,  1,   64 * 6,      128, "bf16", 50,  1, 2, "iid"),
+    ("sink0_local1", 1, 4,  1,   64 * 7,      128, "bf16", 2,   0, 1, "iid"),
+    ("sink2_local3", 1, 4,  2,   64 * 8 + 9,  64,  "bf16", 2,   2, 3, "clustered"),
+    ("t1",           1, 4,  1,   1,           128, "bf16", 2,   1, 2, "iid"),
+    ("t64",          1, 4,  1,   64,          64,  "bf16", 2,   1, 2, "iid"),
+    ("f32_g2",       1, 2,  1,   64 * 8 + 5,  64,  "f32",  2,   1, 2, "iid"),
+    ("f32_d128",     1, 1,  1,   64 * 5,      128, "f32",  1,   1, 2, "iid"),
+    ("f32_t65",      1, 4,  1,   65,          64,  "f32",  2,   1, 2, "iid"),
+]
+
+
+@pytest.mark.parametrize("mode", ["plain", "sas", "hils"])
+@pytest.mark.parametrize("case", SMALL_PREFILL, ids=[c[0] for c in SMALL_PREFILL])
+def test_prefill_small(case, mode):
+    name, B, Hq, Hkv, T, D, dtype, topk, ns, nl, data = case
+    if mode == "hils" and dtype == "bf16" and ns + nl + topk > 64:
+        pytest.skip("bf16 HILS prefill holds at most 64 attended chunks per row")
+    _print(f"prefill {name} {mode}")
+    q, k, v = synth.make_prefill(B, Hq, Hkv, T, D, dtype, data, seed=3, device="cuda", n_centres=16,
+                                 n_aim=4)
+    res = bsa.prefill(q, k, v, topk=topk, mode=mode, n_sink=ns, n_local=nl,
+                      want_lse=(mode != "hils"))
+    torch.cuda.synchronize()
+    rows = [(b, g, c) for b in range(B) for g in range(Hkv) for c in range((T + 63) // 64)]
+    _check_prefill_rows(q, k, v, res, rows, mode=mode, dtype=dtype, topk=topk, n_sink=ns,
+                        n_local=nl, tag=f"{name}/{mode}")
+
+
+SMALL_DECODE = [
+    # id,        B, Hq, Hkv, Tk,          D,   dtype,  topk, data
+    ("g8",       3, 8,  1,   64 * 20 + 7, 128, "bf16", 4,    "clustered"),
+    ("g4_d64",   2, 8,  2,   64 * 33,     64,  "bf16", 8,    "iid"),
+    ("g32",      1, 32, 1,   64 * 10,     128, "bf16", 3,    "iid"),
+    ("g1",       2, 2,  2,   64 * 9 + 1,  128, "bf16", 2,    "clustered"),
+    ("tk1",      2, 4,  1,   1,           128, "bf16", 2,    "iid"),
+    ("tk64",     1, 8,  1,   64,          128, "bf16", 2,    "iid"),
+    ("kall",     1, 8,  1,   64 * 5,      128, "bf16", 50,   "iid"),
+    ("f32",      2, 4,  2,   64 * 6 + 9,  64,  "f32",  2,    "iid"),
+    ("f32_d128", 1, 8,  1,   64 * 4,      128, "f32",  1,    "iid"),
+]
+
+
+@pytest.mark.parametrize("mode", ["plain", "sas", "hils"])
+@pytest.mark.parametrize("case", SMALL_DECODE, ids=[c[0] for c in SMALL_DECODE])
+def test_decode_small(case, mode):
+    name, B, Hq, Hkv, Tk, D, dtype, topk, data = case
+    _print(f"decode {name} {mode}")
+    q, kc, vc = synth.make_decode(B, Hq, Hkv, Tk, D, dtype, data, seed=5, device="cuda",
+                                  n_centres=16, n_aim=4)
+    lm = bsa.pool_landmarks(kc)
+    res = bsa.decode(q[:, :, None, :].contiguous(), kc, vc, lm, topk=topk, mode=mode,
+                     want_lse=(mode != "hils"))
+    torch.cuda.synchronize()
+    q4 = q[:, :, None, :]
+    pairs = [(b, g) for b in range(B) for g in range(Hkv)]
+    _check_decode_pairs(q4, kc, vc, res, lm, pairs, mode=mode, dtype=dtype, topk=topk, n_sink=1,
+                        n_local=2, tag=f"{name}/{mode}")
+
+
+def test_output_buffers_fully_written_and_deterministic():
+    """Outputs pre-filled with NaN come back finite everywhere; two runs agree bit for bit."""
+    q, k, v = synth.make_prefill(1, 4, 1, 64 * 9 + 11, 128, "bf16", "clustered", seed=9,
+                                 device="cuda", n_centres=8, n_aim=4)
+    for mode in ["plain", "sas", "hils"]:
+        lm = bsa.pool_landmarks(k)
+        idx, sc = bsa.select_topk(q, lm, topk=3)
+        out = torch.full_like(q, float("nan"))
+        lse = None if mode == "hils" else torch.full(q.shape[:3], float("nan"), device="cuda")
+        bsa.attend_prefill(q, k, v, idx, sc, lm, mode=mode, topk=3, out=out, lse=lse)
+        idx2, sc2 = bsa.select_topk(q, lm, topk=3)
+        out2, _ = bsa.attend_prefill(q, k, v, idx2, sc2, lm, mode=mode, topk=3)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out).all()
+        assert lse is None or torch.isfinite(lse).all()
+        assert torch.equal(idx, idx2) and torch.equal(sc, sc2)
+        assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+def test_invalid_call_launches_nothing():
+    """A rejected call leaves its output untouched (no launch happens)."""
+    q, k, v = synth.make_prefill(1, 4, 1, 256, 128, "bf16", "iid", seed=1, device="cuda")
+    lm = bsa.pool_landmarks(k)
+    idx, sc = bsa.select_topk(q, lm, topk=1)
+    out = torch.full_like(q, 7.0)
+    with pytest.raises(bsa.BsaError):
+        bsa.attend_prefill(q, k, v, idx, None, None, mode="sas", topk=1, out=out)   # sc missing
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
+
+
+# ---------------------------------------------------------------------------------------------
+# the workload shapes (launch configuration of the benchmark), sampled rows
+# ---------------------------------------------------------------------------------------------
+
+def _sample_rows(rng, B, Hkv, NQB, n):
+    rows = {(0, 0, 0), (0, 0, 1), (0, 0, 2), (0, Hkv - 1, NQB - 1)}
+    while len(rows) < n:
+        rows.add((int(rng.integers(B)), int(rng.integers(Hkv)), int(rng.integers(NQB))))
+    return sorted(rows)
+
+
+def _workload_prefill(name, n_rows, max_groups=None):
+    w = synth.WORKLOADS[name]
+    B, Hq, Hkv, T, D = w["B"], w["Hq"], w["Hkv"], w["T"], w["D"]
+    _print(f"workload {name}: generating")
+    q, k, v = synth.make_prefill(B, Hq, Hkv, T, D, w["dtype"], w["data"], seed=0, device="cuda",
+                                 n_centres=w.get("n_centres", 256), n_aim=w.get("n_aim", 16))
+    _print(f"workload {name}: running")
+    res = bsa.prefill(q, k, v, topk=w["topk"], mode=w["mode"], want_lse=(w["mode"] != "hils"))
+    torch.cuda.synchronize()
+    NQB = (T + 63) // 64
+    rng = np.random.default_rng(1234)
+    if n_rows is None:
+        rows = [(b, g, c) for b in range(B) for g in range(Hkv) for c in range(NQB)]
+    else:
+        rows = _sample_rows(rng, B, Hkv, NQB, n_rows)
+        if max_groups is not None:
+            keep = sorted({(b, g) for b, g, _ in rows})[:max_groups]
+            rows = [r for r in rows if (r[0], r[1]) in keep]
+    _print(f"workload {name}: checking {len(rows)} rows")
+    worst = _check_prefill_rows(q, k, v, res, rows, mode=w["mode"], dtype=w["dtype"],
+                                topk=w["topk"], n_sink=1, n_local=2, tag=name)
+    _print(f"workload {name}: worst max-abs {worst[0]:.3e} mean-rel {worst[1]:.3e}")
+    del q, k, v, res
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def test_workload_tiny_f32_4k_full():
+    _workload_prefill("tiny_f32_4k", None)
+
+
+def test_workload_gqa_bf16_32k_sampled():
+    _workload_prefill("gqa_bf16_32k", 40)
+
+
+def test_workload_sas_bf16_128k_sampled():
+    _workload_prefill("sas_bf16_128k", 24, max_groups=4)
+
+
+def test_workload_hils_bf16_1m_sampled():
+    _workload_prefill("hils_bf16_1m", 10, max_groups=2)
+
+
+def test_workload_decode_bf16_32x128k_sampled():
+    w = synth.WORKLOADS["decode_bf16_32x128k"]
+    B, Hq, Hkv, Tk, D = w["B"], w["Hq"], w["Hkv"], w["T"], w["D"]
+    _print("workload decode: generating")
+    q, kc, vc = synth.make_decode(B, Hq, Hkv, Tk, D, w["dtype"], w["data"], seed=0, device="cuda",
+                                  n_centres=w["n_centres"], n_aim=w["n_aim"])
+    lm = bsa.pool_landmarks(kc)
+    q4 = q[:, :, None, :].contiguous()
+    res = bsa.decode(q4, kc, vc, lm, topk=w["topk"], mode=w["mode"], want_lse=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(99)
+    pairs = sorted({(0, 0), (B - 1, Hkv - 1)} |
+                   {(int(rng.integers(B)), int(rng.integers(Hkv))) for _ in range(4)})
+    _print(f"workload decode: checking {pairs}")
+    worst = _check_decode_pairs(q4, kc, vc, res, lm, pairs, mode=w["mode"], dtype=w["dtype"],
+                                topk=w["topk"], n_sink=1, n_local=2, tag="decode")
+    _print(f"workload decode: worst max-abs {worst[0]:.3e} mean-rel {worst[1]:.3e}")
+    del q, kc, vc, lm, res
+    gc.collect()
+    torch.cuda.empty_cache()
