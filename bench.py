@@ -1,0 +1,331 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-sparse landmark attention path on one MI355X.
+
+One step = one pass of the whole prefill path over the SAS workload at 128K tokens
+(B=1, 32 query / 8 kv heads, D=128, bf16, top-K=32 plus sink and two local blocks):
+landmark pooling, selector vectors, MFMA block scoring, top-K selection and the gated
+block-sparse attention.  Inputs are synthetic (clustered keys, aimed queries), generated on
+the device before the timed region.  `value` is prefill tokens/s over the timed steps.
+
+Reported beside it, measured in the same run:
+* the attention kernel's attended TFLOP/s and its fraction of the bf16 MFMA peak (HIP events
+  around that kernel on the stream it is launched on);
+* the decode path (32 sequences x 128K cached tokens, 64 query / 8 kv heads, top-K=64):
+  selection + split-K attention, algorithmic HBM GB/s and fraction of the HBM peak, with the
+  caches flushed (a 1 GiB write) between timed steps;
+* optionally the HiLS workload at 1M tokens (--hils);
+* the float64 oracle timed on the host cores on a bounded sample of the prefill workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--hils]
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill tok/s + attended TFLOP/s at 128K; decode HBM GB/s (top-K block attn)"
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+
+
+def attended_flops(B, Hq, D, T, K, n_sink=1, n_local=2):
+    """4*D flops (QK^T and PV) per visible (query, key) pair per query head."""
+    total = 0
+    nqb = (T + 63) // 64
+    for c in range(nqb):
+        n_att = min(c + 1, K + n_sink + n_local)
+        diag = 64 * 65 // 2 if (c + 1) * 64 <= T else (T - 64 * c) * (T - 64 * c + 1) // 2
+        total += 64 * min(64, T - 64 * c) * (n_att - 1) + diag
+    return 4 * D * Hq * B * total
+
+
+def decode_bytes(B, Hq, Hkv, Tk, D, K, elem=2, n_sink=1, n_local=2):
+    """Bytes a decode step must move: candidate landmarks, the attended K and V blocks, q, o."""
+    c = (Tk - 1) // 64
+    n_cand = max(0, c - n_local - n_sink + 1)
+    n_att = min(c + 1, K + n_sink + n_local)
+    G = Hq // Hkv
+    per = n_cand * D * elem + n_att * 64 * D * elem * 2 + 2 * G * D * elem
+    return per * B * Hkv
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--hils", action="store_true", help="also time the HiLS workload at 1M tokens")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration under rocprofv3)")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Events:
+    """Pairs of HIP events on the current stream (where libbsa launches its kernels)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def start(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.append([e, None])
+
+    def stop(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs[-1][1] = e
+
+    def ms(self):
+        return [a.elapsed_time(b) for a, b in self.pairs]
+
+
+def bench_prefill(torch, bsa, synth, name, steps, warmup):
+    w = synth.WORKLOADS[name]
+    B, Hq, Hkv, T, D, K, mode = w["B"], w["Hq"], w["Hkv"], w["T"], w["D"], w["topk"], w["mode"]
+    log(f"[bench] {name}: generating inputs")
+    q, k, v = synth.make_prefill(B, Hq, Hkv, T, D, w["dtype"], w["data"], seed=0, device="cuda",
+                                 n_centres=w["n_centres"], n_aim=w["n_aim"])
+    NB = (T + 63) // 64
+    NA = K + 3
+    lm = torch.empty((B, Hkv, NB, D), dtype=q.dtype, device="cuda")
+    idx = torch.empty((B, Hkv, NB, NA), dtype=torch.int32, device="cuda")
+    sc = torch.empty((B, Hkv, NB, NA), dtype=torch.float32, device="cuda")
+    out = torch.empty_like(q)
+    p = bsa.make_params(B=B, Hq=Hq, Hkv=Hkv, D=D, seq_q=T, seq_k=T, dtype=q.dtype, topk=K)
+    ws = torch.empty(bsa.select_workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    ev_attn, ev_sel, ev_pool = Events(torch), Events(torch), Events(torch)
+
+    def step(record):
+        if record:
+            ev_pool.start()
+        bsa.pool_landmarks(k, out=lm)
+        if record:
+            ev_pool.stop()
+            ev_sel.start()
+        bsa.select_topk(q, lm, topk=K, ws=ws, idx=idx, sc=sc)
+        if record:
+            ev_sel.stop()
+            ev_attn.start()
+        bsa.attend_prefill(q, k, v, idx, sc, lm if mode == "hils" else None, mode=mode, topk=K,
+                           out=out)
+        if record:
+            ev_attn.stop()
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log(f"[bench] {name}: timing {steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    flops = attended_flops(B, Hq, D, T, K)
+    attn_ms = sum(ev_attn.ms()) / steps
+    res = {
+        "ms_per_step": wall * 1e3 / steps,
+        "tok_per_s": B * T * steps / wall,
+        "attn_ms": attn_ms,
+        "select_ms": sum(ev_sel.ms()) / steps,
+        "pool_ms": sum(ev_pool.ms()) / steps,
+        "attended_flops": flops,
+        "attended_tflops_kernel": flops / (attn_ms * 1e-3) / 1e12,
+        "attended_tflops_e2e": flops * steps / wall / 1e12,
+    }
+    log(f"[bench] {name}: {json.dumps(res)}")
+    tensors = (q, k, v, lm, idx, sc, out, ws)
+    return res, tensors
+
+
+def bench_decode(torch, bsa, synth, steps, warmup):
+    w = synth.WORKLOADS["decode_bf16_32x128k"]
+    B, Hq, Hkv, Tk, D, K = w["B"], w["Hq"], w["Hkv"], w["T"], w["D"], w["topk"]
+    log("[bench] decode: generating inputs")
+    q, kc, vc = synth.make_decode(B, Hq, Hkv, Tk, D, w["dtype"], w["data"], seed=0, device="cuda",
+                                  n_centres=w["n_centres"], n_aim=w["n_aim"])
+    q = q[:, :, None, :].contiguous()
+    lm = bsa.pool_landmarks(kc)                  # cache-fill time, not timed
+    NA = K + 3
+    idx = torch.empty((B, Hkv, 1, NA), dtype=torch.int32, device="cuda")
+    sc = torch.empty((B, Hkv, 1, NA), dtype=torch.float32, device="cuda")
+    out = torch.empty_like(q)
+    p = bsa.make_params(B=B, Hq=Hq, Hkv=Hkv, D=D, seq_q=1, seq_k=Tk, dtype=q.dtype, topk=K)
+    ws_sel = torch.empty(bsa.select_workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    ws_dec = torch.empty(bsa.decode_workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    ev_step, ev_attn = Events(torch), Events(torch)
+
+    def step(record):
+        if record:
+            ev_step.start()
+        bsa.select_topk(q, lm, topk=K, seq_k=Tk, ws=ws_sel, idx=idx, sc=sc)
+        if record:
+            ev_attn.start()
+        bsa.attend_decode(q, kc, vc, idx, sc, None, mode="plain", topk=K, out=out, ws=ws_dec)
+        if record:
+            ev_attn.stop()
+            ev_step.pairs[-1][1] = ev_attn.pairs[-1][1]
+
+    for _ in range(warmup):
+        step(False)
+    for _ in range(steps):
+        flush.fill_(1)                           # evict L2 and the MALL between steps
+        step(True)
+    torch.cuda.synchronize()
+    nbytes = decode_bytes(B, Hq, Hkv, Tk, D, K)
+    step_us = 1e3 * sum(ev_step.ms()) / steps
+    attn_us = 1e3 * sum(ev_attn.ms()) / steps
+    res = {"us_per_step": step_us, "attn_us": attn_us, "select_us": step_us - attn_us,
+           "algorithmic_bytes": nbytes, "hbm_gbps": nbytes / (step_us * 1e-6) / 1e9}
+    res["hbm_frac"] = res["hbm_gbps"] / PEAK_HBM_GBPS
+    log(f"[bench] decode: {json.dumps(res)}")
+    del q, kc, vc, lm, flush
+    return res
+
+
+def cpu_baseline(torch, tensors, name, synth, budget_s=12.0):
+    """The float64 oracle on a sample of the prefill workload, extrapolated to tok/s."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    w = synth.WORKLOADS[name]
+    q, k, v = tensors[:3]
+    B, Hq, Hkv, T, D, K = w["B"], w["Hq"], w["Hkv"], w["T"], w["D"], w["topk"]
+    G = Hq // Hkv
+    NQB = (T + 63) // 64
+    h = lambda t: t.float().cpu().numpy().astype(np.float64)
+    K64, V64 = h(k[0, 0]), h(v[0, 0])
+    rng = np.random.default_rng(7)
+    t0 = time.perf_counter()
+    lm = O.landmarks(K64[None, None], w["dtype"])[0, 0]
+    t_lm = time.perf_counter() - t0
+    n_rows, t_rows = 0, 0.0
+    scale = 1 / math.sqrt(D)
+    while t_rows < budget_s and n_rows < 4096:
+        c = int(rng.integers(NQB))
+        qs = h(q[0, 0:G, c * 64:(c + 1) * 64])
+        t1 = time.perf_counter()
+        qbar = O.selector_vectors(qs[None], 1)[0, 0, 0]
+        s_row = O.block_scores(qbar[None], lm)[0]
+        A, sA = O.select_row(s_row, c, K)
+        gates = O.sas_gates(A, sA, c) if w["mode"] == "sas" else np.zeros(A.size)
+        tpos = np.arange(c * 64, c * 64 + 64)
+        for hh in range(G):
+            O.attend_rows(qs[hh], tpos, K64, V64, A, gates, scale)
+        t_rows += time.perf_counter() - t1
+        n_rows += 1
+    per_step = B * Hkv * (t_lm + t_rows / n_rows * NQB)
+    return {"value": B * T / per_step, "unit": "tok/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"kv group 0 of {name}: its landmarks plus {n_rows} random query blocks "
+                       f"(all {G} heads x 64 tokens: scores, top-K, gates, attention) in "
+                       f"{t_lm + t_rows:.1f} s; extrapolated linearly to {B * Hkv} groups x "
+                       f"{NQB} query blocks"),
+            "seconds_per_step_extrapolated": per_step}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU path is "
+              "not built.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import block_sparse_attention_landmark_amd as bsa
+    from block_sparse_attention_landmark_amd import synth
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    bsa.load_library()
+
+    name = "sas_bf16_128k"
+    pre, tensors = bench_prefill(torch, bsa, synth, name, args.steps, args.warmup)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host cores")
+        cpu = cpu_baseline(torch, tensors, name, synth)
+        log(f"[bench] cpu baseline: {cpu['value']:.1f} tok/s")
+    del tensors
+    torch.cuda.empty_cache()
+    dec = None
+    if not args.no_decode:
+        dec = bench_decode(torch, bsa, synth, args.steps, args.warmup)
+        torch.cuda.empty_cache()
+    hils = None
+    if args.hils:
+        hils, t = bench_prefill(torch, bsa, synth, "hils_bf16_1m", max(2, args.steps // 4), 1)
+        del t
+        torch.cuda.empty_cache()
+    if args.copy_probe:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    w = synth.WORKLOADS[name]
+    line = {
+        "metric": METRIC,
+        "value": pre["tok_per_s"],
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pre["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (clustered keys, aimed queries; seeded)",
+        "config": {"workload": f"{name}: SAS-gated block-sparse prefill, B={w['B']}, "
+                               f"Hq={w['Hq']}, Hkv={w['Hkv']}, D={w['D']}, T={w['T']}, block=64, "
+                               f"top-K={w['topk']} + sink + 2 local",
+                   "step": "pool + select (selector, scores, top-K) + attend"},
+        "attended_tflops": pre["attended_tflops_e2e"],
+        "attended_tflops_attention_kernel": pre["attended_tflops_kernel"],
+        "breakdown_ms": {"pool": pre["pool_ms"], "select": pre["select_ms"],
+                         "attend": pre["attn_ms"]},
+        "roofline": {"bound": "mfma", "achieved": pre["attended_tflops_kernel"],
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": pre["attended_tflops_kernel"] / PEAK_BF16_TFLOPS, "traffic": None,
+                     "kernel": "attend_prefill_bf16_kernel<128, SAS, 4>"},
+    }
+    if dec is not None:
+        line["decode"] = {
+            "workload": "decode_bf16_32x128k: 32 seqs x 131072 cached tokens, Hq=64, Hkv=8, "
+                        "D=128, top-K=64 + sink + 2 local, bf16",
+            "hbm_gbps": dec["hbm_gbps"], "us_per_step": dec["us_per_step"],
+            "breakdown_us": {"select": dec["select_us"], "attend": dec["attn_us"]},
+            "roofline": {"bound": "hbm", "achieved": dec["hbm_gbps"], "peak": PEAK_HBM_GBPS,
+                         "unit": "GB/s", "frac": dec["hbm_frac"],
+                         "algorithmic_bytes": dec["algorithmic_bytes"]}}
+    if hils is not None:
+        line["hils_1m"] = {"tok_per_s": hils["tok_per_s"], "ms_per_step": hils["ms_per_step"],
+                           "attended_tflops_attention_kernel": hils["attended_tflops_kernel"],
+                           "frac_of_bf16_peak": hils["attended_tflops_kernel"] / PEAK_BF16_TFLOPS}
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
