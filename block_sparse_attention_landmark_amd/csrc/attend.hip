@@ -37,6 +37,18 @@ __device__ __forceinline__ int count_valid(const int32_t* row, int NA) {
 // =============================================================================================
 // bf16 prefill
 // =============================================================================================
+// Pipeline per workgroup: the K and V blocks of attended entry a+1 are written from registers
+// into the second LDS buffer and the global loads of entry a+2 are issued while the waves finish
+// entry a, so each block costs one barrier and its HBM/L2 latency hides behind a block of math.
+// V stays row-major in LDS and reaches the P V MFMA through transposed LDS reads.
+//
+// Softmax (PLAIN/SAS), per query row, in log2 units: the block's max comes from the raw scores
+// (the scale is positive and the gate constant per block), every probability is one FMA and
+// one exp2, and the running max is only raised -- rescaling O and the sum -- when the block's
+// max exceeds it by more than 8 (probabilities then stay below 2^8, far inside float32 and bf16
+// range); the final O / sum is unchanged by the choice of reference max.
+constexpr float kLazyRescale = 8.0f;
+
 template <int D, int MODE, int HPW>
 __global__ __launch_bounds__(HPW * 128) void attend_prefill_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
@@ -46,16 +58,27 @@ __global__ __launch_bounds__(HPW * 128) void attend_prefill_bf16_kernel(
   constexpr int NWAVE = HPW * 2;
   constexpr int NT = NWAVE * kWave;
   constexpr int KP = D + 8;        // K tile row pitch (elements)
-  constexpr int VP = kBlock + 8;   // V^T tile row pitch (elements)
+  constexpr int VP = D + 16;       // V tile row pitch (elements): conflict-free transposed reads
   constexpr int C8 = D / 8;        // 16-byte chunks per row
-  __shared__ __attribute__((aligned(16))) bf16 Ks[kBlock * KP];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[D * VP];
+  constexpr int CPT = kBlock * C8 / NT;   // chunks of each tile staged per thread
+  __shared__ __attribute__((aligned(16))) bf16 Ks[2][kBlock * KP];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[2][kBlock * VP];
   __shared__ float wbuf[MODE == 2 ? NWAVE * 64 * 32 : 1];
 
-  const int c = NQB - 1 - (int)blockIdx.x;   // heavy (late) query blocks first
-  const int g = blockIdx.y / n_hc;
-  const int hc = blockIdx.y % n_hc;
-  const int b = blockIdx.z;
+  // XCD-aware order: workgroups are dispatched round-robin over the 8 XCDs, so give each XCD a
+  // contiguous range of (batch, head chunk, query block) -- neighbouring query blocks share
+  // their local window and sink in that XCD's L2.
+  const int nh = Hkv * n_hc;
+  const int total = NQB * nh * (int)gridDim.z;
+  int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  if (total % 8 == 0) lin = (lin % 8) * (total / 8) + lin / 8;
+  const int b = lin / (NQB * nh);
+  const int rem = lin % (NQB * nh);
+  const int gh = rem / NQB;
+  const int c = NQB - 1 - rem % NQB;          // heavy (late) query blocks first
+  const int g = gh / n_hc;
+  const int hc = gh % n_hc;
+
   const int tid = threadIdx.x;
   const int w = tid / kWave;
   const int lane = tid % kWave;
@@ -83,6 +106,34 @@ __global__ __launch_bounds__(HPW * 128) void attend_prefill_bf16_kernel(
   float s_ref = 0.0f;
   if (MODE == 1 && nval > 0) s_ref = srow[nval - 1];
 
+  // ---- staging helpers ----
+  u32x4 kreg[CPT], vreg[CPT];
+  auto load_tile = [&](int a) {
+    const int j = irow[a];
+    const bool ok = j >= 0 && j <= c;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int ci = tid + i * NT;
+      const int row = ci / C8, c8 = ci % C8;
+      const int tok = j * kBlock + row;
+      kreg[i] = u32x4{0u, 0u, 0u, 0u};
+      vreg[i] = u32x4{0u, 0u, 0u, 0u};
+      if (ok && tok < T) {
+        kreg[i] = *reinterpret_cast<const u32x4*>(k + kvbase + (size_t)tok * D + c8 * 8);
+        vreg[i] = *reinterpret_cast<const u32x4*>(v + kvbase + (size_t)tok * D + c8 * 8);
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int ci = tid + i * NT;
+      const int row = ci / C8, c8 = ci % C8;
+      *reinterpret_cast<u32x4*>(&Ks[buf][row * KP + c8 * 8]) = kreg[i];
+      *reinterpret_cast<u32x4*>(&Vs[buf][row * VP + c8 * 8]) = vreg[i];
+    }
+  };
+
   f32x16 o[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
@@ -90,15 +141,18 @@ __global__ __launch_bounds__(HPW * 128) void attend_prefill_bf16_kernel(
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
 
+  if (nval > 0) load_tile(0);
+
   if constexpr (MODE == 2) {
-    // retrieval weights of every attended chunk for this wave's 32 query rows
+    // retrieval weights of every attended chunk for this wave's 32 query rows (landmark rows
+    // staged in the second K buffer, which the pipeline first writes after the next barrier)
     for (int ci = tid; ci < kBlock * C8; ci += NT) {
       const int row = ci / C8, c8 = ci % C8;
       u32x4 val = u32x4{0u, 0u, 0u, 0u};
       const int jr = row < nval ? irow[row] : -1;
       if (jr >= 0 && jr <= c)
         val = *reinterpret_cast<const u32x4*>(lm + ((size_t)(b * Hkv + g) * NQB + jr) * D + c8 * 8);
-      *reinterpret_cast<u32x4*>(&Ks[row * KP + c8 * 8]) = val;
+      *reinterpret_cast<u32x4*>(&Ks[1][row * KP + c8 * 8]) = val;
     }
     __syncthreads();
     f32x16 rt[2];
@@ -108,7 +162,7 @@ __global__ __launch_bounds__(HPW * 128) void attend_prefill_bf16_kernel(
       for (int i = 0; i < 16; ++i) rt[kt][i] = 0.0f;
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
-        bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[(kt * 32 + l32) * KP + 16 * s + 8 * half]);
+        bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[1][(kt * 32 + l32) * KP + 16 * s + 8 * half]);
         rt[kt] = mfma32(a, qf[s], rt[kt]);
       }
     }
@@ -143,107 +197,111 @@ __global__ __launch_bounds__(HPW * 128) void attend_prefill_bf16_kernel(
       }
   }
 
-  for (int a = 0; a < nval; ++a) {
-    const int j = irow[a];
-    if (j < 0 || j > c) continue;
-    __syncthreads();
-    // stage K (row-major) and V (transposed) of block j
-    for (int ci = tid; ci < kBlock * C8; ci += NT) {
-      const int row = ci / C8, c8 = ci % C8;
-      const int tok = j * kBlock + row;
-      u32x4 val = u32x4{0u, 0u, 0u, 0u};
-      if (tok < T) val = *reinterpret_cast<const u32x4*>(k + kvbase + (size_t)tok * D + c8 * 8);
-      *reinterpret_cast<u32x4*>(&Ks[row * KP + c8 * 8]) = val;
-    }
-    for (int ci = tid; ci < kBlock * C8; ci += NT) {
-      const int row = ci % kBlock, c8 = ci / kBlock;
-      const int tok = j * kBlock + row;
-      u32x4 val = u32x4{0u, 0u, 0u, 0u};
-      if (tok < T) val = *reinterpret_cast<const u32x4*>(v + kvbase + (size_t)tok * D + c8 * 8);
-      const bf16x8 vv = __builtin_bit_cast(bf16x8, val);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) Vt[(c8 * 8 + e) * VP + row] = vv[e];
-    }
-    __syncthreads();
+  if (nval > 0) store_tile(0);
+  if (nval > 1) load_tile(1);
+  __syncthreads();
 
-    // S^T = K Q^T: st[kt][i] = score of key kt*32 + 8*(i/4) + 4*half + i%4 for query row l32
-    f32x16 st[2];
+  for (int a = 0; a < nval; ++a) {
+    const int buf = a & 1;
+    const int j = irow[a];
+    if (j >= 0 && j <= c) {
+      const bf16* Kb = Ks[buf];
+      const bf16* Vb = Vs[buf];
+      // S^T = K Q^T: st[kt][i] = score of key kt*32 + 8*(i/4) + 4*half + i%4 for query row l32
+      f32x16 st[2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+      for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) st[kt][i] = 0.0f;
+        for (int i = 0; i < 16; ++i) st[kt][i] = 0.0f;
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[(kt * 32 + l32) * KP + 16 * s + 8 * half]);
-        st[kt] = mfma32(a, qf[s], st[kt]);
-      }
-    }
-    const bool diag = (j == c);
-    float gate2 = 0.0f;
-    if (MODE == 1 && !diag) gate2 = log_sigmoid(srow[a] - s_ref) * kLog2e;
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = kt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-        float x = st[kt][i] * scale_log2 + gate2;
-        if (diag && j * kBlock + key > tq) x = -INFINITY;
-        st[kt][i] = x;
-        mloc = fmaxf(mloc, x);
-      }
-    if constexpr (MODE == 2) {
-      const float mj = wave_max_xor32(mloc);
-      float lsum = 0.0f;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float e = fast_exp2(st[kt][i] - mj);
-          st[kt][i] = e;
-          lsum += e;
+        for (int s = 0; s < D / 16; ++s) {
+          bf16x8 av = *reinterpret_cast<const bf16x8*>(&Kb[(kt * 32 + l32) * KP + 16 * s + 8 * half]);
+          st[kt] = mfma32(av, qf[s], st[kt]);
         }
-      const float lj = wave_sum_xor32(lsum);
-      const float coef = wbuf[(w * 64 + a) * 32 + l32] / lj;
+      }
+      float mx = -INFINITY;
+      if (j == c) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) st[kt][i] *= coef;
-    } else {
-      const float m_new = fmaxf(m_run, wave_max_xor32(mloc));
-      const float alpha = fast_exp2(m_run - m_new);
-      float lsum = 0.0f;
+          for (int i = 0; i < 16; ++i) {
+            const int key = kt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+            if (j * kBlock + key > tq) st[kt][i] = -INFINITY;
+            mx = fmaxf(mx, st[kt][i]);
+          }
+      } else {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = fast_exp2(st[kt][i] - m_new);
-          st[kt][i] = p;
-          lsum += p;
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[kt][i]);
+      }
+      mx = wave_max_xor32(mx);
+      if constexpr (MODE == 2) {
+        const float mj = mx * scale_log2;
+        float lsum = 0.0f;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float e = fast_exp2(fmaf(st[kt][i], scale_log2, -mj));
+            st[kt][i] = e;
+            lsum += e;
+          }
+        const float lj = wave_sum_xor32(lsum);
+        const float coef = wbuf[(w * 64 + a) * 32 + l32] / lj;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) st[kt][i] *= coef;
+      } else {
+        float gate2 = 0.0f;
+        if (MODE == 1 && j != c) gate2 = log_sigmoid(srow[a] - s_ref) * kLog2e;
+        const float m_blk = fmaf(mx, scale_log2, gate2);
+        const bool need = m_blk > m_run + kLazyRescale;
+        if (__any(need)) {
+          const float m_new = need ? m_blk : m_run;
+          const float alpha = fast_exp2(m_run - m_new);
+          m_run = m_new;
+          l_run *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
         }
-      l_run = l_run * alpha + lsum;
-      m_run = m_new;
+        const float bias = gate2 - m_run;
+        float lsum = 0.0f;
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
-    }
-    // O^T += V^T P^T over 4 k-steps of 16 keys; lane half h supplies keys
-    // 16ks + 4h + {0..3} and 16ks + 8 + 4h + {0..3}
+          for (int i = 0; i < 16; ++i) {
+            const float p = fast_exp2(fmaf(st[kt][i], scale_log2, bias));
+            st[kt][i] = p;
+            lsum += p;
+          }
+        l_run += lsum;
+      }
+      // O^T += V^T P^T over 4 k-steps of 16 keys; lane half h supplies keys
+      // 16ks + 4h + {0..3} and 16ks + 8 + 4h + {0..3} (same order in both operands)
+      const int vrow = (lane % 16) / 4;
+      const int vcol = 16 * ((lane / 16) % 2) + 4 * (lane % 4);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 pb;
+      for (int ks = 0; ks < 4; ++ks) {
+        bf16x8 pb;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pb[e] = f2bf(st[ks / 2][8 * (ks % 2) + e]);
+        for (int e = 0; e < 8; ++e) pb[e] = f2bf(st[ks / 2][8 * (ks % 2) + e]);
+        const bf16* v0 = Vb + (16 * ks + 4 * half + vrow) * VP + vcol;
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        const bf16* vp = &Vt[(dt * 32 + l32) * VP + 16 * ks + 4 * half];
-        const u32x2 x0 = *reinterpret_cast<const u32x2*>(vp);
-        const u32x2 x1 = *reinterpret_cast<const u32x2*>(vp + 8);
-        const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{x0[0], x0[1], x1[0], x1[1]});
-        o[dt] = mfma32(av, pb, o[dt]);
+        for (int dt = 0; dt < D / 32; ++dt) {
+          const i16x4 x0 = lds_read_tr16(v0 + dt * 32);
+          const i16x4 x1 = lds_read_tr16(v0 + 8 * VP + dt * 32);
+          const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[dt] = mfma32(av, pb, o[dt]);
+        }
       }
     }
+    if (a + 1 < nval) store_tile(buf ^ 1);
+    if (a + 2 < nval) load_tile(a + 2);
+    __syncthreads();
   }
 
   float inv = 1.0f;
@@ -267,7 +325,6 @@ __global__ __launch_bounds__(HPW * 128) void attend_prefill_bf16_kernel(
     if (MODE != 2 && lse != nullptr && half == 0) lse[(size_t)(b * Hq + h) * T + tq] = lse_val;
   }
 }
-
 // =============================================================================================
 // bf16 decode: split-K over the attended blocks, one wave per (sequence, kv group, split)
 // =============================================================================================

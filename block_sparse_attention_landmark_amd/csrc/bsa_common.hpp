@@ -50,6 +50,18 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 acc) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
 }
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Transposed 8-byte LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16 lanes, lane l
+// receives element l%4 of the four-element chunks addressed by lanes 4e + (l%16)/4 of its group,
+// for e = 0..3.  With lane s of a group pointing at row (base + (s%16)/4), columns 4*(s%4)..+3 of
+// a row-major tile, lane l therefore gets column (l%16) of rows base..base+3: a column read.
+__device__ __forceinline__ i16x4 lds_read_tr16(const bf16* p) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  typedef __attribute__((address_space(3))) bf16 lds_bf16;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_bf16*)p);
+}
+
 __device__ __forceinline__ float wave_max_xor32(float x) {
   return fmaxf(x, __shfl_xor(x, 32, kWave));
 }
