@@ -58,7 +58,8 @@ __global__ __launch_bounds__(HPW * 128) void attend_prefill_bf16_kernel(
   constexpr int NWAVE = HPW * 2;
   constexpr int NT = NWAVE * kWave;
   constexpr int KP = D + 8;        // K tile row pitch (elements)
-  constexpr int VP = D + 16;       // V tile row pitch (elements): conflict-free transposed reads
+  constexpr int VP = D + 32;       // V tile row pitch (elements): rows 16 banks apart, so the
+                                   // transposed reads of 32 lanes cover all 64 banks once
   constexpr int C8 = D / 8;        // 16-byte chunks per row
   constexpr int CPT = kBlock * C8 / NT;   // chunks of each tile staged per thread
   __shared__ __attribute__((aligned(16))) bf16 Ks[2][kBlock * KP];
@@ -200,6 +201,8 @@ __global__ __launch_bounds__(HPW * 128) void attend_prefill_bf16_kernel(
   if (nval > 0) store_tile(0);
   if (nval > 1) load_tile(1);
   __syncthreads();
+  float gvec = 0.0f;        // SAS gates (log2 units) of entries gbase .. gbase + 63, one per lane
+  int gbase = -kWave;
 
   for (int a = 0; a < nval; ++a) {
     const int buf = a & 1;
@@ -208,17 +211,25 @@ __global__ __launch_bounds__(HPW * 128) void attend_prefill_bf16_kernel(
       const bf16* Kb = Ks[buf];
       const bf16* Vb = Vs[buf];
       // S^T = K Q^T: st[kt][i] = score of key kt*32 + 8*(i/4) + 4*half + i%4 for query row l32
+      // all K fragments first, so the MFMAs do not each wait on their own LDS read
+      bf16x8 kf[2][D / 16];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s)
+          kf[kt][s] = *reinterpret_cast<const bf16x8*>(&Kb[(kt * 32 + l32) * KP + 16 * s + 8 * half]);
       f32x16 st[2];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) st[kt][i] = 0.0f;
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-          bf16x8 av = *reinterpret_cast<const bf16x8*>(&Kb[(kt * 32 + l32) * KP + 16 * s + 8 * half]);
-          st[kt] = mfma32(av, qf[s], st[kt]);
-        }
+        for (int s = 0; s < D / 16; ++s) st[kt] = mfma32(kf[kt][s], qf[s], st[kt]);
       }
+      // schedule: every K-fragment read, then the MFMAs (the reads of the second key tile land
+      // while the first tile's MFMAs run)
+      __builtin_amdgcn_sched_group_barrier(0x100, D / 8, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, D / 8, 0);
       float mx = -INFINITY;
       if (j == c) {
 #pragma unroll
@@ -255,7 +266,16 @@ __global__ __launch_bounds__(HPW * 128) void attend_prefill_bf16_kernel(
           for (int i = 0; i < 16; ++i) st[kt][i] *= coef;
       } else {
         float gate2 = 0.0f;
-        if (MODE == 1 && j != c) gate2 = log_sigmoid(srow[a] - s_ref) * kLog2e;
+        if constexpr (MODE == 1) {
+          // gates of 64 entries at a time, one per lane; this entry's is read from its lane
+          if (a >= gbase + kWave) {
+            gbase = a;
+            const int e = gbase + lane;
+            gvec = 0.0f;
+            if (e < nval && irow[e] != c) gvec = log_sigmoid(srow[e] - s_ref) * kLog2e;
+          }
+          gate2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gvec), a - gbase));
+        }
         const float m_blk = fmaf(mx, scale_log2, gate2);
         const bool need = m_blk > m_run + kLazyRescale;
         if (__any(need)) {

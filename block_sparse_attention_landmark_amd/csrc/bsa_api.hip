@@ -4,7 +4,7 @@
 #include <stdio.h>
 #include <string.h>
 
-#include "../../include/bsa.h"
+#include "bsa.h"
 #include "bsa_internal.hpp"
 
 namespace {

@@ -62,10 +62,17 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const bf16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_bf16*)p);
 }
 
+// Combine a value with the one held 32 lanes away (lanes l and l^32 hold the same query row in
+// the MFMA layouts used here).  v_permlane32_swap exchanges the upper half of its first operand
+// with the lower half of its second; given x twice, the two results hold x of both halves.
 __device__ __forceinline__ float wave_max_xor32(float x) {
-  return fmaxf(x, __shfl_xor(x, 32, kWave));
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float wave_sum_xor32(float x) { return x + __shfl_xor(x, 32, kWave); }
+__device__ __forceinline__ float wave_sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
