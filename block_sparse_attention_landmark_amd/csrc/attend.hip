@@ -27,10 +27,19 @@ namespace bsa {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// number of valid entries in an attended-set row (stops at the first -1)
+// Number of valid entries in an attended-set row (the valid entries form a prefix; -1 pads).
+// Each lane of the wave reads one entry, so a row costs one load per 64 entries instead of a
+// chain of dependent loads.
 __device__ __forceinline__ int count_valid(const int32_t* row, int NA) {
+  const int lane = threadIdx.x % kWave;
   int n = 0;
-  while (n < NA && row[n] >= 0) ++n;
+  for (int i0 = 0; i0 < NA; i0 += kWave) {
+    const int i = i0 + lane;
+    const bool ok = i < NA && row[i] >= 0;
+    const int cnt = __popcll(__ballot(ok));
+    n += cnt;
+    if (cnt < kWave) break;
+  }
   return n;
 }
 
@@ -346,29 +355,50 @@ __global__ __launch_bounds__(HPW * 128) void attend_prefill_bf16_kernel(
   }
 }
 // =============================================================================================
-// bf16 decode: split-K over the attended blocks, one wave per (sequence, kv group, split)
+// bf16 decode: split-K over the attended blocks, one block per wave
 // =============================================================================================
-constexpr int kDecodeBlocksPerSplit = 4;
+constexpr int kDecodeWaves = 4;          // waves per workgroup
+constexpr int kMergeMaxSplits = 64;      // partial states merged per (sequence, kv group)
 
+// Blocks each wave handles so that a row of NA attended entries needs at most
+// kMergeMaxSplits splits of kDecodeWaves waves.
+inline int decode_blocks_per_wave(int NA) {
+  const int per_split = kDecodeWaves * kMergeMaxSplits;
+  return (NA + per_split - 1) / per_split;
+}
+
+// One workgroup per (sequence, kv group, split); wave w of split s takes the attended entries
+// (s * waves * bpw) + w + waves * i, i < bpw.  K and V blocks are copied straight from memory
+// into the wave's LDS tiles (no register round trip, 1 KB per instruction), with 16-byte chunks
+// XOR-swizzled so the fragment and transposed reads are free of bank conflicts.  Each wave keeps
+// an online softmax state; the four states are combined in LDS and written as the split's
+// partial state.
 template <int D, int MODE>
-__global__ __launch_bounds__(64) void attend_decode_bf16_kernel(
+__global__ __launch_bounds__(kDecodeWaves * 64) void attend_decode_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
     const bf16* __restrict__ lm, const int32_t* __restrict__ idx, const float* __restrict__ sc,
     float* __restrict__ part_o, float* __restrict__ part_ml, int Hq, int Hkv, int G, int Tk,
-    int NB, int NA, int nsplit, float scale_log2) {
-  constexpr int VP = kBlock + 8;
-  constexpr int C8 = D / 8;
-  __shared__ __attribute__((aligned(16))) bf16 Vt[D * VP];
+    int NB, int NA, int nsplit, int bpw, float scale_log2) {
+  constexpr int C16 = D / 8;                 // 16-byte chunks per row
+  constexpr int RPI = 64 / C16;              // rows covered by one 64-lane 16-byte copy
+  __shared__ __attribute__((aligned(16))) bf16 Ks[kDecodeWaves][kBlock * D];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[kDecodeWaves][kBlock * D];
+  __shared__ float comb_ml[kDecodeWaves][32][2];
 
   const int split = blockIdx.x;
   const int g = blockIdx.y;
   const int b = blockIdx.z;
-  const int lane = threadIdx.x;
+  const int w = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
   const int half = lane / 32;
   const int l32 = lane % 32;
   const bool row_ok = l32 < G;
   const int h = g * G + min(l32, G - 1);
   const int c = (Tk - 1) / kBlock;
+  // chunk swizzles (physical 16-byte chunk = logical ^ swz(row)): for the V tile, the four rows of
+  // a transposed read land on distinct banks; for the K tile, the 16 rows of a fragment read do
+  auto swz = [](int row) { return D == 128 ? 4 * (row % 4) : 0; };
+  auto swzk = [](int row) { return D == 128 ? row % 16 : (row / 2) % 8; };
 
   bf16x8 qf[D / 16];
   {
@@ -384,8 +414,10 @@ __global__ __launch_bounds__(64) void attend_decode_bf16_kernel(
   const int32_t* irow = idx + (size_t)(b * Hkv + g) * NA;
   const float* srow = sc + (size_t)(b * Hkv + g) * NA;
   const int nval = count_valid(irow, NA);
-  float s_ref = 0.0f;
-  if (MODE == 1 && nval > 0) s_ref = srow[nval - 1];
+  bf16* kt_ = Ks[w];
+  bf16* vt = Vs[w];
+  const int vrow = (lane % 16) / 4;
+  const int vcol = 16 * ((lane / 16) % 2) + 4 * (lane % 4);
 
   f32x16 o[D / 32];
 #pragma unroll
@@ -394,70 +426,61 @@ __global__ __launch_bounds__(64) void attend_decode_bf16_kernel(
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
 
-  const int a_beg = split * kDecodeBlocksPerSplit;
-  const int a_end = min(nval, a_beg + kDecodeBlocksPerSplit);
-  for (int a = a_beg; a < a_end; ++a) {
-    const int j = irow[a];
+  for (int it = 0; it < bpw; ++it) {
+    const int a = split * kDecodeWaves * bpw + w + kDecodeWaves * it;
+    const int j = a < nval ? irow[a] : -1;
     if (j < 0 || j > c) continue;
-    // V block: lane = token row, 16-byte chunks along D
-    u32x4 vraw[C8];
-    {
-      const int tok = j * kBlock + lane;
+    // K and V rows j*64 .. j*64+63 into this wave's LDS tiles (rows past the cache end read
+    // its last row; their probabilities are zero)
 #pragma unroll
-      for (int c8 = 0; c8 < C8; ++c8) {
-        vraw[c8] = u32x4{0u, 0u, 0u, 0u};
-        if (tok < Tk) vraw[c8] = *reinterpret_cast<const u32x4*>(vc + kvbase + (size_t)tok * D + c8 * 8);
-      }
+    for (int n = 0; n < kBlock / RPI; ++n) {
+      const int row = n * RPI + lane / C16;
+      const int tok = min(j * kBlock + row, Tk - 1);
+      const size_t rbase = kvbase + (size_t)tok * D;
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(kc + rbase + ((lane % C16) ^ swzk(row)) * 8),
+          (__attribute__((address_space(3))) void*)(kt_ + n * RPI * D), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(vc + rbase + ((lane % C16) ^ swz(row)) * 8),
+          (__attribute__((address_space(3))) void*)(vt + n * RPI * D), 16, 0, 0);
     }
-    // K fragments straight from memory in MFMA A layout
+    __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): both tiles have landed
+    // S^T = K Q^T with K fragments (key kt*32 + l32, dims 16s + 8*half .. +8) read from LDS
     f32x16 st[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const int tok = j * kBlock + kt * 32 + l32;
-      const bf16* krow = kc + kvbase + (size_t)min(tok, Tk - 1) * D;
+      const int row = kt * 32 + l32;
+      bf16x8 kf[D / 16];
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s)
+        kf[s] = *reinterpret_cast<const bf16x8*>(kt_ + row * D + (((2 * s + half) ^ swzk(row)) * 8));
 #pragma unroll
       for (int i = 0; i < 16; ++i) st[kt][i] = 0.0f;
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        u32x4 raw = *reinterpret_cast<const u32x4*>(krow + 16 * s + 8 * half);
-        if (tok >= Tk) raw = u32x4{0u, 0u, 0u, 0u};
-        st[kt] = mfma32(__builtin_bit_cast(bf16x8, raw), qf[s], st[kt]);
-      }
+      for (int s = 0; s < D / 16; ++s) st[kt] = mfma32(kf[s], qf[s], st[kt]);
     }
-    __syncthreads();
-#pragma unroll
-    for (int c8 = 0; c8 < C8; ++c8) {
-      const bf16x8 vv = __builtin_bit_cast(bf16x8, vraw[c8]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) Vt[(c8 * 8 + e) * VP + lane] = vv[e];
-    }
-    float gate2 = 0.0f;
-    if (MODE == 1 && j != c) gate2 = log_sigmoid(srow[a] - s_ref) * kLog2e;
-    float mloc = -INFINITY;
+    float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = kt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-        float x = st[kt][i] * scale_log2 + gate2;
-        if (j * kBlock + key >= Tk) x = -INFINITY;
-        st[kt][i] = x;
-        mloc = fmaxf(mloc, x);
+        if (j * kBlock + key >= Tk) st[kt][i] = -INFINITY;
+        mx = fmaxf(mx, st[kt][i]);
       }
+    mx = wave_max_xor32(mx);
     float alpha, coef = 1.0f;
     if constexpr (MODE == 2) {
       // per-chunk softmax, then an online softmax over the chunks' retrieval scores
-      const float mj = wave_max_xor32(mloc);
       float lsum = 0.0f;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float e = fast_exp2(st[kt][i] - mj);
+          const float e = fast_exp2(fmaf(st[kt][i], scale_log2, -mx * scale_log2));
           st[kt][i] = e;
           lsum += e;
         }
-      const float lj = wave_sum_xor32(lsum);
       const bf16* lrow = lm + ((size_t)(b * Hkv + g) * NB + j) * D;
       float part = 0.0f;
 #pragma unroll
@@ -466,33 +489,38 @@ __global__ __launch_bounds__(64) void attend_decode_bf16_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) part += bf2f(qf[s][e]) * bf2f(lv[e]);
       }
-      const float r2 = wave_sum_xor32(part) * scale_log2;
+      const float r2 = wave_sum_xor32(part) * scale_log2;     // retrieval score, log2 units
       const float m_new = fmaxf(m_run, r2);
       alpha = fast_exp2(m_run - m_new);
       const float wr = fast_exp2(r2 - m_new);
       l_run = l_run * alpha + wr;
       m_run = m_new;
-      coef = wr / lj;
+      coef = wr / wave_sum_xor32(lsum);
     } else {
-      const float m_new = fmaxf(m_run, wave_max_xor32(mloc));
+      float gate2 = 0.0f;
+      if (MODE == 1 && j != c) gate2 = log_sigmoid(srow[a] - srow[nval - 1]) * kLog2e;
+      const float m_new = fmaxf(m_run, fmaf(mx, scale_log2, gate2));
       alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      const float bias = gate2 - m_run;
       float lsum = 0.0f;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = fast_exp2(st[kt][i] - m_new);
+          const float p = fast_exp2(fmaf(st[kt][i], scale_log2, bias));
           st[kt][i] = p;
           lsum += p;
         }
-      l_run = l_run * alpha + lsum;
-      m_run = m_new;
+      l_run = l_run * alpha + wave_sum_xor32(lsum);
     }
+    if (alpha != 1.0f) {
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+      for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
-    __syncthreads();
+        for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+    }
+    // O^T += V^T P^T; transposed reads of the swizzled V tile
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       bf16x8 pb;
@@ -500,19 +528,22 @@ __global__ __launch_bounds__(64) void attend_decode_bf16_kernel(
       for (int e = 0; e < 8; ++e) pb[e] = f2bf(st[ks / 2][8 * (ks % 2) + e] * coef);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const bf16* vp = &Vt[(dt * 32 + l32) * VP + 16 * ks + 4 * half];
-        const u32x2 x0 = *reinterpret_cast<const u32x2*>(vp);
-        const u32x2 x1 = *reinterpret_cast<const u32x2*>(vp + 8);
-        const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{x0[0], x0[1], x1[0], x1[1]});
+        const int r0 = 16 * ks + 4 * half + vrow;
+        const int col = dt * 32 + vcol;               // element column (multiple of 4)
+        const bf16* p0 = vt + r0 * D + (((col / 8) ^ swz(r0)) * 8) + col % 8;
+        const bf16* p1 = vt + (r0 + 8) * D + (((col / 8) ^ swz(r0 + 8)) * 8) + col % 8;
+        const i16x4 x0 = lds_read_tr16(p0);
+        const i16x4 x1 = lds_read_tr16(p1);
+        const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
         o[dt] = mfma32(av, pb, o[dt]);
       }
     }
   }
-  // partial state: O (unnormalised), m (log2 units) and l; PLAIN/SAS sum l over both halves
-  if constexpr (MODE != 2) l_run = wave_sum_xor32(l_run);
-  const size_t pbase = ((size_t)(b * Hkv + g) * nsplit + split) * G;
+
+  // combine the four waves' states (rows < G) through LDS (the K tiles are reused)
+  __syncthreads();
+  float* comb_o = reinterpret_cast<float*>(&Ks[0][0]);        // [wave][row][D]
   if (row_ok) {
-    float* po = part_o + (pbase + l32) * D;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -520,15 +551,40 @@ __global__ __launch_bounds__(64) void attend_decode_bf16_kernel(
         f32x4 ov;
 #pragma unroll
         for (int e = 0; e < 4; ++e) ov[e] = o[dt][4 * i4 + e];
-        *reinterpret_cast<f32x4*>(po + dt * 32 + 8 * i4 + 4 * half) = ov;
+        *reinterpret_cast<f32x4*>(&comb_o[(w * 32 + l32) * D + dt * 32 + 8 * i4 + 4 * half]) = ov;
       }
     if (half == 0) {
-      part_ml[(pbase + l32) * 2 + 0] = m_run;
-      part_ml[(pbase + l32) * 2 + 1] = l_run;
+      comb_ml[w][l32][0] = m_run;
+      comb_ml[w][l32][1] = l_run;
+    }
+  }
+  __syncthreads();
+  const size_t pbase = ((size_t)(b * Hkv + g) * nsplit + split) * G;
+  for (int e = threadIdx.x; e < G * D; e += kDecodeWaves * 64) {
+    const int row = e / D, d = e % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < kDecodeWaves; ++v) M = fmaxf(M, comb_ml[v][row][0]);
+    float L = 0.0f, acc = 0.0f;
+#pragma unroll
+    for (int v = 0; v < kDecodeWaves; ++v) {
+      const float m = comb_ml[v][row][0];
+      if (m == -INFINITY) continue;
+      const float f = fast_exp2(m - M);
+      L += comb_ml[v][row][1] * f;
+      acc += comb_o[(v * 32 + row) * D + d] * f;
+    }
+    part_o[(pbase + row) * D + d] = acc;
+    if (d == 0) {
+      part_ml[(pbase + row) * 2 + 0] = M;
+      part_ml[(pbase + row) * 2 + 1] = L;
     }
   }
 }
 
+// Merge of the split partial states of one (sequence, kv group): every (row, split) pair loads
+// its (m, l) at once, the per-split weights exp2(m_s - M) / L are formed in LDS, then each output
+// element sums its column of partial outputs with independent loads.
 template <typename OUT>
 __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_ml,
@@ -536,26 +592,39 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
                                                            float* __restrict__ lse, int Hkv,
                                                            int G, int D, int nsplit,
                                                            int write_lse) {
+  __shared__ float sm[32][kMergeMaxSplits];
+  __shared__ float sl[32][kMergeMaxSplits];
   const int bg = blockIdx.x;
   const int b = bg / Hkv, g = bg % Hkv;
+  const size_t pb = (size_t)bg * nsplit;
+  for (int t = threadIdx.x; t < G * nsplit; t += blockDim.x) {
+    const int row = t / nsplit, s = t % nsplit;
+    sm[row][s] = part_ml[((pb + s) * G + row) * 2];
+    sl[row][s] = part_ml[((pb + s) * G + row) * 2 + 1];
+  }
+  __syncthreads();
+  if (threadIdx.x < G) {
+    const int row = threadIdx.x;
+    float M = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, sm[row][s]);
+    float L = 0.0f;
+    for (int s = 0; s < nsplit; ++s) {
+      const float f = (sm[row][s] == -INFINITY) ? 0.0f : fast_exp2(sm[row][s] - M);
+      sm[row][s] = f;
+      L += sl[row][s] * f;
+    }
+    const float inv = 1.0f / L;
+    for (int s = 0; s < nsplit; ++s) sm[row][s] *= inv;
+    if (write_lse && lse != nullptr) lse[(size_t)b * Hkv * G + g * G + row] = (M + log2f(L)) * kLn2;
+  }
+  __syncthreads();
   for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
     const int row = e / D, d = e % D;
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s)
-      M = fmaxf(M, part_ml[(((size_t)bg * nsplit + s) * G + row) * 2]);
-    float L = 0.0f, acc = 0.0f;
-    for (int s = 0; s < nsplit; ++s) {
-      const size_t pr = ((size_t)bg * nsplit + s) * G + row;
-      const float m = part_ml[pr * 2];
-      if (m == -INFINITY) continue;
-      const float f = fast_exp2(m - M);
-      L += part_ml[pr * 2 + 1] * f;
-      acc += part_o[pr * D + d] * f;
-    }
-    const int hq = g * G + row;
-    const size_t orow = (size_t)(b * Hkv * G + hq);
-    out[orow * D + d] = (OUT)(acc / L);
-    if (write_lse && d == 0 && lse != nullptr) lse[orow] = (M + log2f(L)) * kLn2;
+    const float* col = part_o + (pb * G + row) * D + d;
+    float acc = 0.0f;
+#pragma unroll 8
+    for (int s = 0; s < nsplit; ++s) acc += col[(size_t)s * G * D] * sm[row][s];
+    out[((size_t)b * Hkv * G + g * G + row) * D + d] = (OUT)acc;
   }
 }
 
@@ -674,7 +743,8 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(
 // launchers
 // =============================================================================================
 int decode_splits(const Shape& s) {
-  return (s.NA + kDecodeBlocksPerSplit - 1) / kDecodeBlocksPerSplit;
+  const int per_split = kDecodeWaves * decode_blocks_per_wave(s.NA);
+  return (s.NA + per_split - 1) / per_split;
 }
 
 size_t decode_ws_bytes(const Shape& s) {
@@ -751,9 +821,10 @@ static void launch_decode_bf16_d(const Shape& s, const void* q, const void* kc, 
   dim3 grid(nsplit, s.Hkv, s.B);
   const float sl2 = s.scale * kLog2e;
 #define BSA_DEC(MODE)                                                                          \
-  hipLaunchKernelGGL((attend_decode_bf16_kernel<D, MODE>), grid, dim3(64), 0, st,              \
+  hipLaunchKernelGGL((attend_decode_bf16_kernel<D, MODE>), grid, dim3(kDecodeWaves * 64), 0, st, \
                      (const bf16*)q, (const bf16*)kc, (const bf16*)vc, (const bf16*)lm, idx,   \
-                     sc, part_o, part_ml, s.Hq, s.Hkv, s.G, s.Tk, s.NB, s.NA, nsplit, sl2)
+                     sc, part_o, part_ml, s.Hq, s.Hkv, s.G, s.Tk, s.NB, s.NA, nsplit,          \
+                     decode_blocks_per_wave(s.NA), sl2)
   if (s.mode == 0) BSA_DEC(0);
   else if (s.mode == 1) BSA_DEC(1);
   else BSA_DEC(2);

@@ -162,6 +162,8 @@ bsa_status_t bsa_select_topk(const bsa_params_t* params, const void* q, const vo
                 ws == nullptr ? ", NULL pointer" : "");
   if (((uintptr_t)ws & 255u) != 0) return fail(BSA_ERR_ALIGN, "ws is not 256-byte aligned");
   hipStream_t st = (hipStream_t)stream;
+  if (bsa::decode_select_fused(s))
+    return hip_result(bsa::launch_decode_select(s, q, lm, idx, sc, st), "select_topk");
   float* qbar = (float*)ws;
   float* scores = (float*)((char*)ws + bsa::select_ws_qbar_bytes(s));
   hipError_t e = bsa::launch_selector_vectors(s, q, qbar, st);

@@ -37,6 +37,10 @@ hipError_t launch_block_scores(const Shape& s, const float* qbar, const void* lm
                                hipStream_t st);
 hipError_t launch_topk(const Shape& s, const float* scores, int32_t* idx, float* sc,
                        hipStream_t st);
+// decode with bf16 landmarks: selector vector, scores and top-K in one kernel
+bool decode_select_fused(const Shape& s);
+hipError_t launch_decode_select(const Shape& s, const void* q, const void* lm, int32_t* idx,
+                                float* sc, hipStream_t st);
 hipError_t launch_attend_prefill(const Shape& s, const void* q, const void* k, const void* v,
                                  const void* lm, const int32_t* idx, const float* sc, void* out,
                                  float* lse, hipStream_t st);

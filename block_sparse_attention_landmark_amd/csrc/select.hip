@@ -161,14 +161,15 @@ hipError_t launch_block_scores(const Shape& s, const float* qbar, const void* lm
 }
 
 // ---------------------------------------------------------------------------------------------
-// top-K: one workgroup of 256 threads per selection row
+// top-K of one selection row, executed by a whole workgroup of NT threads
 // ---------------------------------------------------------------------------------------------
 constexpr int kTopkThreads = 256;
-constexpr int kTopkWaves = kTopkThreads / kWave;
 constexpr int kKeyCache = 12288;   // candidate keys held in LDS; longer rows re-read L2
 
 // exclusive prefix sum over the workgroup; *total receives the sum of all x
+template <int NT>
 __device__ __forceinline__ int block_exclusive_scan(int x, int* sbuf, int* total) {
+  constexpr int NW = NT / kWave;
   const int lane = threadIdx.x % kWave;
   const int w = threadIdx.x / kWave;
   int incl = x;
@@ -181,7 +182,7 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int* sbuf, int* total
   __syncthreads();
   int base = 0, tot = 0;
 #pragma unroll
-  for (int i = 0; i < kTopkWaves; ++i) {
+  for (int i = 0; i < NW; ++i) {
     const int v = sbuf[i];
     base += (i < w) ? v : 0;
     tot += v;
@@ -191,24 +192,15 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int* sbuf, int* total
   return base + incl - x;
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ scores,
-                                                            int32_t* __restrict__ idx,
-                                                            float* __restrict__ sc, int R,
-                                                            int NB, int c_dec, int topk,
-                                                            int n_sink, int n_local, int NA) {
-  __shared__ uint32_t skeys[kKeyCache];
-  __shared__ int hist[256];
-  __shared__ int sbuf[kTopkWaves];
-  __shared__ int sh_digit, sh_krem;
-
-  const int r = blockIdx.x;
-  const int bg = blockIdx.y;
+// Writes the attended set of query block c: forced sink entries, the K chosen candidates in
+// ascending block order, the local window, -1 padding; osc gets the aligned scores.
+// score_at(j) gives the score of block j <= c; key_at(i) the order-preserving key of candidate
+// n_sink + i.  Every thread of the workgroup must call it.
+template <int NT, typename ScoreAt, typename KeyAt>
+__device__ void topk_select(ScoreAt score_at, KeyAt key_at, int c, int topk, int n_sink,
+                            int n_local, int NA, int32_t* __restrict__ oidx,
+                            float* __restrict__ osc, int* hist, int* sbuf, int* sh) {
   const int tid = threadIdx.x;
-  const int c = (c_dec >= 0) ? c_dec : r;
-  const float* srow = scores + ((c_dec >= 0) ? (size_t)bg * NB : (size_t)bg * tri(R) + tri(c));
-  int32_t* oidx = idx + ((size_t)bg * R + r) * NA;
-  float* osc = sc + ((size_t)bg * R + r) * NA;
-
   const int n_sink_eff = min(n_sink, c + 1);
   const int lo = n_sink;                       // first candidate
   const int hi = c - n_local;                  // last candidate
@@ -218,66 +210,56 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   const int n_loc = max(0, c - loc_beg + 1);
 
   // forced entries and padding
-  for (int i = tid; i < NA; i += kTopkThreads) {
-    int32_t jj = -1;
-    float ss = 0.0f;
+  for (int i = tid; i < NA; i += NT) {
     if (i < n_sink_eff) {
-      jj = i;
-    } else if (i >= n_sink_eff + K && i < n_sink_eff + K + n_loc) {
-      jj = loc_beg + (i - n_sink_eff - K);
-    }
-    if (jj >= 0) ss = srow[jj];
-    if (i < n_sink_eff || i >= n_sink_eff + K) {
-      oidx[i] = jj;
-      osc[i] = ss;
+      oidx[i] = i;
+      osc[i] = score_at(i);
+    } else if (i >= n_sink_eff + K) {
+      const bool loc = i < n_sink_eff + K + n_loc;
+      const int jj = loc_beg + (i - n_sink_eff - K);
+      oidx[i] = loc ? jj : -1;
+      osc[i] = loc ? score_at(jj) : 0.0f;
     }
   }
   if (K == 0) return;
   if (K == n) {
-    for (int i = tid; i < n; i += kTopkThreads) {
+    for (int i = tid; i < n; i += NT) {
       oidx[n_sink_eff + i] = lo + i;
-      osc[n_sink_eff + i] = srow[lo + i];
+      osc[n_sink_eff + i] = score_at(lo + i);
     }
     return;
   }
 
-  const bool cached = n <= kKeyCache;
-  if (cached) {
-    for (int i = tid; i < n; i += kTopkThreads) skeys[i] = float_key(srow[lo + i]);
-  }
-  __syncthreads();
-  auto key_at = [&](int i) -> uint32_t { return cached ? skeys[i] : float_key(srow[lo + i]); };
-
-  // radix select of the K-th largest key
+  // radix select of the K-th largest key, 8 bits at a time
   uint32_t prefix = 0u, mask = 0u;
   int krem = K;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    hist[tid] = 0;
+    for (int i = tid; i < 256; i += NT) hist[i] = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += kTopkThreads) {
+    for (int i = tid; i < n; i += NT) {
       const uint32_t key = key_at(i);
       if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
     }
     __syncthreads();
-    const int cnt = hist[255 - tid];         // thread t holds digit 255 - t
+    const int cnt = tid < 256 ? hist[255 - tid] : 0;   // thread t holds digit 255 - t
     int tot;
-    const int above = block_exclusive_scan(cnt, sbuf, &tot);   // keys with a larger digit
-    if (above < krem && krem <= above + cnt) {
-      sh_digit = 255 - tid;
-      sh_krem = krem - above;
+    const int above = block_exclusive_scan<NT>(cnt, sbuf, &tot);   // keys with larger digits
+    if (tid < 256 && above < krem && krem <= above + cnt) {
+      sh[0] = 255 - tid;
+      sh[1] = krem - above;
     }
     __syncthreads();
-    prefix |= (uint32_t)sh_digit << shift;
+    prefix |= (uint32_t)sh[0] << shift;
     mask |= 255u << shift;
-    krem = sh_krem;
+    krem = sh[1];
     __syncthreads();
   }
   const uint32_t tau = prefix;
   const int need_eq = krem;                  // keys equal to tau to take, lowest index first
 
   // index-ordered compaction: each thread owns a contiguous slice
-  const int per = (n + kTopkThreads - 1) / kTopkThreads;
+  const int per = (n + NT - 1) / NT;
   const int beg = min(n, tid * per);
   const int end = min(n, beg + per);
   int gt = 0, eq = 0;
@@ -287,9 +269,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
     eq += key == tau;
   }
   int tot;
-  const int eq_before = block_exclusive_scan(eq, sbuf, &tot);
+  const int eq_before = block_exclusive_scan<NT>(eq, sbuf, &tot);
   const int take_eq = min(eq, max(0, need_eq - eq_before));
-  int pos = block_exclusive_scan(gt + take_eq, sbuf, &tot);
+  int pos = block_exclusive_scan<NT>(gt + take_eq, sbuf, &tot);
   int eq_seen = 0;
   for (int i = beg; i < end; ++i) {
     const uint32_t key = key_at(i);
@@ -300,10 +282,120 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
     }
     if (take) {
       oidx[n_sink_eff + pos] = lo + i;
-      osc[n_sink_eff + pos] = srow[lo + i];
+      osc[n_sink_eff + pos] = score_at(lo + i);
       ++pos;
     }
   }
+}
+
+// one workgroup of 256 threads per selection row, scores from the score workspace
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ scores,
+                                                            int32_t* __restrict__ idx,
+                                                            float* __restrict__ sc, int R,
+                                                            int NB, int c_dec, int topk,
+                                                            int n_sink, int n_local, int NA) {
+  __shared__ uint32_t skeys[kKeyCache];
+  __shared__ int hist[256];
+  __shared__ int sbuf[kTopkThreads / kWave];
+  __shared__ int sh[2];
+  const int r = blockIdx.x;
+  const int bg = blockIdx.y;
+  const int c = (c_dec >= 0) ? c_dec : r;
+  const float* srow = scores + ((c_dec >= 0) ? (size_t)bg * NB : (size_t)bg * tri(R) + tri(c));
+  const int n = max(0, c - n_local - n_sink + 1);
+  const bool cached = n <= kKeyCache;
+  if (cached) {
+    for (int i = threadIdx.x; i < n; i += kTopkThreads) skeys[i] = float_key(srow[n_sink + i]);
+  }
+  __syncthreads();
+  topk_select<kTopkThreads>(
+      [&](int j) { return srow[j]; },
+      [&](int i) { return cached ? skeys[i] : float_key(srow[n_sink + i]); }, c, topk, n_sink,
+      n_local, NA, idx + ((size_t)bg * R + r) * NA, sc + ((size_t)bg * R + r) * NA, hist, sbuf,
+      sh);
+}
+
+// ---------------------------------------------------------------------------------------------
+// decode: selector vector, scores of every block and top-K in one workgroup per (sequence, kv
+// group); the landmark rows are read with 16 lanes per row (coalesced 1 KB per instruction)
+// ---------------------------------------------------------------------------------------------
+constexpr int kDecodeSelThreads = 1024;
+constexpr int kDecodeSelMaxBlocks = 16384;    // scores kept in LDS (64 KB)
+
+template <int D>
+__global__ __launch_bounds__(kDecodeSelThreads) void decode_select_bf16_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ lm, int32_t* __restrict__ idx,
+    float* __restrict__ sc, int Hq, int Hkv, int G, int NB, int c, int topk, int n_sink,
+    int n_local, int NA) {
+  constexpr int LPR = D / 8;                  // lanes per landmark row (8 elements each)
+  constexpr int RPI = kWave / LPR;            // rows per wave instruction
+  constexpr int NW = kDecodeSelThreads / kWave;
+  __shared__ float qb[D];
+  __shared__ float ssc[kDecodeSelMaxBlocks];
+  __shared__ int hist[256];
+  __shared__ int sbuf[NW];
+  __shared__ int sh[2];
+  const int bg = blockIdx.x;
+  const int b = bg / Hkv, g = bg % Hkv;
+  const int tid = threadIdx.x;
+  if (tid < D) {
+    double acc = 0.0;
+    for (int hh = 0; hh < G; ++hh) acc += (double)bf2f(q[(size_t)(b * Hq + g * G + hh) * D + tid]);
+    qb[tid] = (float)acc;
+  }
+  __syncthreads();
+  const int w = tid / kWave, lane = tid % kWave;
+  const int part = lane % LPR, sub = lane / LPR;
+  float qv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) qv[e] = qb[part * 8 + e];
+  const bf16* lbase = lm + (size_t)bg * NB * D;
+  for (int j0 = w * RPI; j0 <= c; j0 += NW * RPI * 4) {
+    float acc[4];
+    u32x4 raw[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = min(j0 + u * NW * RPI + sub, c);
+      raw[u] = *reinterpret_cast<const u32x4*>(lbase + (size_t)j * D + part * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bf16x8 lv = __builtin_bit_cast(bf16x8, raw[u]);
+      float s = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s = fmaf(qv[e], bf2f(lv[e]), s);
+#pragma unroll
+      for (int o = LPR / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, kWave);
+      acc[u] = s;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = j0 + u * NW * RPI + sub;
+      if (part == 0 && j <= c) ssc[j] = acc[u];
+    }
+  }
+  __syncthreads();
+  topk_select<kDecodeSelThreads>(
+      [&](int j) { return ssc[j]; }, [&](int i) { return float_key(ssc[n_sink + i]); }, c, topk,
+      n_sink, n_local, NA, idx + (size_t)bg * NA, sc + (size_t)bg * NA, hist, sbuf, sh);
+}
+
+bool decode_select_fused(const Shape& s) {
+  return s.decode && s.bf16 && s.c_dec + 1 <= kDecodeSelMaxBlocks;
+}
+
+hipError_t launch_decode_select(const Shape& s, const void* q, const void* lm, int32_t* idx,
+                                float* sc, hipStream_t st) {
+  dim3 grid(s.B * s.Hkv);
+  if (s.D == 128)
+    hipLaunchKernelGGL(decode_select_bf16_kernel<128>, grid, dim3(kDecodeSelThreads), 0, st,
+                       (const bf16*)q, (const bf16*)lm, idx, sc, s.Hq, s.Hkv, s.G, s.NB, s.c_dec,
+                       s.topk, s.n_sink, s.n_local, s.NA);
+  else
+    hipLaunchKernelGGL(decode_select_bf16_kernel<64>, grid, dim3(kDecodeSelThreads), 0, st,
+                       (const bf16*)q, (const bf16*)lm, idx, sc, s.Hq, s.Hkv, s.G, s.NB, s.c_dec,
+                       s.topk, s.n_sink, s.n_local, s.NA);
+  return hipGetLastError();
 }
 
 hipError_t launch_topk(const Shape& s, const float* scores, int32_t* idx, float* sc,
