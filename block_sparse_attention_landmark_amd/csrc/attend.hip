@@ -19,6 +19,8 @@
 // keys is permuted identically on both operands), V transposed into LDS when staged.
 #include <math.h>
 
+#include <algorithm>
+
 #include "bsa_common.hpp"
 #include "bsa_internal.hpp"
 
@@ -360,25 +362,33 @@ __global__ __launch_bounds__(HPW * 128) void attend_prefill_bf16_kernel(
 constexpr int kDecodeWaves = 4;          // waves per workgroup
 constexpr int kMergeMaxSplits = 64;      // partial states merged per (sequence, kv group)
 
-// Blocks each wave handles so that a row of NA attended entries needs at most
-// kMergeMaxSplits splits of kDecodeWaves waves.
-inline int decode_blocks_per_wave(int NA) {
-  const int per_split = kDecodeWaves * kMergeMaxSplits;
-  return (NA + per_split - 1) / per_split;
+constexpr int kDecodeTargetWorkgroups = 256;   // one per CU is enough to stream the cache
+
+// Splits of the attended blocks of one (sequence, kv group): as few as keep the GPU busy (each
+// split's partial state costs a write and a read), at most kMergeMaxSplits.
+inline int decode_nsplit(int NA, int pairs) {
+  const int max_useful = (NA + kDecodeWaves - 1) / kDecodeWaves;
+  const int want = (kDecodeTargetWorkgroups + pairs - 1) / pairs;
+  return std::max(1, std::min(std::min(want, max_useful), kMergeMaxSplits));
+}
+inline int decode_blocks_per_wave(int NA, int nsplit) {
+  const int per_split = (NA + nsplit - 1) / nsplit;
+  return (per_split + kDecodeWaves - 1) / kDecodeWaves;
 }
 
 // One workgroup per (sequence, kv group, split); wave w of split s takes the attended entries
 // (s * waves * bpw) + w + waves * i, i < bpw.  K and V blocks are copied straight from memory
 // into the wave's LDS tiles (no register round trip, 1 KB per instruction), with 16-byte chunks
 // XOR-swizzled so the fragment and transposed reads are free of bank conflicts.  Each wave keeps
-// an online softmax state; the four states are combined in LDS and written as the split's
+// an online softmax state; the waves' states are combined in LDS and written as the split's
 // partial state.
 template <int D, int MODE>
 __global__ __launch_bounds__(kDecodeWaves * 64) void attend_decode_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
     const bf16* __restrict__ lm, const int32_t* __restrict__ idx, const float* __restrict__ sc,
-    float* __restrict__ part_o, float* __restrict__ part_ml, int Hq, int Hkv, int G, int Tk,
-    int NB, int NA, int nsplit, int bpw, float scale_log2) {
+    float* __restrict__ part_o, float* __restrict__ part_ml, bf16* __restrict__ out,
+    float* __restrict__ lse, int Hq, int Hkv, int G, int Tk, int NB, int NA, int nsplit, int bpw,
+    float scale_log2) {
   constexpr int C16 = D / 8;                 // 16-byte chunks per row
   constexpr int RPI = 64 / C16;              // rows covered by one 64-lane 16-byte copy
   __shared__ __attribute__((aligned(16))) bf16 Ks[kDecodeWaves][kBlock * D];
@@ -426,38 +436,70 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void attend_decode_bf16_kernel(
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
 
-  for (int it = 0; it < bpw; ++it) {
+  // entry of iteration it, or -1
+  auto entry = [&](int it) {
     const int a = split * kDecodeWaves * bpw + w + kDecodeWaves * it;
-    const int j = a < nval ? irow[a] : -1;
-    if (j < 0 || j > c) continue;
-    // K and V rows j*64 .. j*64+63 into this wave's LDS tiles (rows past the cache end read
-    // its last row; their probabilities are zero)
+    const int j = (it < bpw && a < nval) ? irow[a] : -1;
+    return (j >= 0 && j <= c) ? j : -1;
+  };
+  // copy the K (or V) rows of block j into this wave's tile, 1 KB per instruction (rows past
+  // the cache end read its last row; their probabilities are zero)
+  auto copy_k = [&](int j) {
 #pragma unroll
     for (int n = 0; n < kBlock / RPI; ++n) {
       const int row = n * RPI + lane / C16;
       const int tok = min(j * kBlock + row, Tk - 1);
-      const size_t rbase = kvbase + (size_t)tok * D;
       __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(kc + rbase + ((lane % C16) ^ swzk(row)) * 8),
+          (const __attribute__((address_space(1))) void*)(kc + kvbase + (size_t)tok * D +
+                                                          ((lane % C16) ^ swzk(row)) * 8),
           (__attribute__((address_space(3))) void*)(kt_ + n * RPI * D), 16, 0, 0);
+    }
+  };
+  auto copy_v = [&](int j) {
+#pragma unroll
+    for (int n = 0; n < kBlock / RPI; ++n) {
+      const int row = n * RPI + lane / C16;
+      const int tok = min(j * kBlock + row, Tk - 1);
       __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(vc + rbase + ((lane % C16) ^ swz(row)) * 8),
+          (const __attribute__((address_space(1))) void*)(vc + kvbase + (size_t)tok * D +
+                                                          ((lane % C16) ^ swz(row)) * 8),
           (__attribute__((address_space(3))) void*)(vt + n * RPI * D), 16, 0, 0);
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): both tiles have landed
+  };
+
+  // find the first valid entry and start its copies
+  int it0 = 0;
+  int j = entry(0);
+  while (j < 0 && it0 + 1 < bpw) j = entry(++it0);
+  if (j >= 0) {
+    copy_k(j);
+    copy_v(j);
+  }
+  for (int it = it0; it < bpw && j >= 0; ) {
+    const int a = split * kDecodeWaves * bpw + w + kDecodeWaves * it;
+    // next valid entry: its copies start as soon as this block's tiles are read
+    int it_next = it + 1;
+    int jn = entry(it_next);
+    while (jn < 0 && it_next + 1 < bpw) jn = entry(++it_next);
+    __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): both tiles of block j have landed
     // S^T = K Q^T with K fragments (key kt*32 + l32, dims 16s + 8*half .. +8) read from LDS
-    f32x16 st[2];
+    bf16x8 kf[2][D / 16];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       const int row = kt * 32 + l32;
-      bf16x8 kf[D / 16];
 #pragma unroll
       for (int s = 0; s < D / 16; ++s)
-        kf[s] = *reinterpret_cast<const bf16x8*>(kt_ + row * D + (((2 * s + half) ^ swzk(row)) * 8));
+        kf[kt][s] = *reinterpret_cast<const bf16x8*>(kt_ + row * D + (((2 * s + half) ^ swzk(row)) * 8));
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): the K tile may be overwritten
+    if (jn >= 0) copy_k(jn);
+    f32x16 st[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) st[kt][i] = 0.0f;
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) st[kt] = mfma32(kf[s], qf[s], st[kt]);
+      for (int s = 0; s < D / 16; ++s) st[kt] = mfma32(kf[kt][s], qf[s], st[kt]);
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -520,12 +562,10 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void attend_decode_bf16_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
     }
-    // O^T += V^T P^T; transposed reads of the swizzled V tile
+    // O^T += V^T P^T; transposed reads of the swizzled V tile, all issued before the MFMAs
+    bf16x8 vf[4][D / 32];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 pb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pb[e] = f2bf(st[ks / 2][8 * (ks % 2) + e] * coef);
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
         const int r0 = 16 * ks + 4 * half + vrow;
@@ -534,13 +574,23 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void attend_decode_bf16_kernel(
         const bf16* p1 = vt + (r0 + 8) * D + (((col / 8) ^ swz(r0 + 8)) * 8) + col % 8;
         const i16x4 x0 = lds_read_tr16(p0);
         const i16x4 x1 = lds_read_tr16(p1);
-        const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[dt] = mfma32(av, pb, o[dt]);
+        vf[ks][dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
       }
+    __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): the V tile may be overwritten
+    if (jn >= 0) copy_v(jn);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 pb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[e] = f2bf(st[ks / 2][8 * (ks % 2) + e] * coef);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) o[dt] = mfma32(vf[ks][dt], pb, o[dt]);
     }
+    it = it_next;
+    j = jn;
   }
 
-  // combine the four waves' states (rows < G) through LDS (the K tiles are reused)
+  // combine the waves' states (rows < G) through LDS (the K tiles are reused)
   __syncthreads();
   float* comb_o = reinterpret_cast<float*>(&Ks[0][0]);        // [wave][row][D]
   if (row_ok) {
@@ -574,10 +624,17 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void attend_decode_bf16_kernel(
       L += comb_ml[v][row][1] * f;
       acc += comb_o[(v * 32 + row) * D + d] * f;
     }
-    part_o[(pbase + row) * D + d] = acc;
-    if (d == 0) {
-      part_ml[(pbase + row) * 2 + 0] = M;
-      part_ml[(pbase + row) * 2 + 1] = L;
+    if (nsplit == 1) {
+      // a single split is the whole row: normalise and write the output directly
+      const size_t orow = (size_t)b * Hq + g * G + row;
+      out[orow * D + d] = f2bf(acc / L);
+      if (MODE != 2 && lse != nullptr && d == 0) lse[orow] = (M + log2f(L)) * kLn2;
+    } else {
+      part_o[(pbase + row) * D + d] = acc;
+      if (d == 0) {
+        part_ml[(pbase + row) * 2 + 0] = M;
+        part_ml[(pbase + row) * 2 + 1] = L;
+      }
     }
   }
 }
@@ -742,13 +799,10 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(
 // =============================================================================================
 // launchers
 // =============================================================================================
-int decode_splits(const Shape& s) {
-  const int per_split = kDecodeWaves * decode_blocks_per_wave(s.NA);
-  return (s.NA + per_split - 1) / per_split;
-}
+int decode_splits(const Shape& s) { return decode_nsplit(s.NA, s.B * s.Hkv); }
 
 size_t decode_ws_bytes(const Shape& s) {
-  if (!s.bf16) return 0;
+  if (!s.bf16 || decode_splits(s) == 1) return 0;
   const size_t rows = (size_t)s.B * s.Hkv * decode_splits(s) * s.G;
   const size_t o = (rows * s.D * sizeof(float) + 255) & ~(size_t)255;
   return o + rows * 2 * sizeof(float);
@@ -823,14 +877,15 @@ static void launch_decode_bf16_d(const Shape& s, const void* q, const void* kc, 
 #define BSA_DEC(MODE)                                                                          \
   hipLaunchKernelGGL((attend_decode_bf16_kernel<D, MODE>), grid, dim3(kDecodeWaves * 64), 0, st, \
                      (const bf16*)q, (const bf16*)kc, (const bf16*)vc, (const bf16*)lm, idx,   \
-                     sc, part_o, part_ml, s.Hq, s.Hkv, s.G, s.Tk, s.NB, s.NA, nsplit,          \
-                     decode_blocks_per_wave(s.NA), sl2)
+                     sc, part_o, part_ml, (bf16*)out, lse, s.Hq, s.Hkv, s.G, s.Tk, s.NB, s.NA,  \
+                     nsplit, decode_blocks_per_wave(s.NA, nsplit), sl2)
   if (s.mode == 0) BSA_DEC(0);
   else if (s.mode == 1) BSA_DEC(1);
   else BSA_DEC(2);
 #undef BSA_DEC
-  hipLaunchKernelGGL(decode_merge_kernel<bf16>, dim3(s.B * s.Hkv), dim3(256), 0, st, part_o,
-                     part_ml, (bf16*)out, lse, s.Hkv, s.G, s.D, nsplit, s.mode != 2 ? 1 : 0);
+  if (nsplit > 1)
+    hipLaunchKernelGGL(decode_merge_kernel<bf16>, dim3(s.B * s.Hkv), dim3(256), 0, st, part_o,
+                       part_ml, (bf16*)out, lse, s.Hkv, s.G, s.D, nsplit, s.mode != 2 ? 1 : 0);
 }
 
 hipError_t launch_attend_decode(const Shape& s, const void* q, const void* kc, const void* vc,
