@@ -20,9 +20,11 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [
 """
 
 import argparse
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -53,6 +55,22 @@ def decode_bytes(B, Hq, Hkv, Tk, D, K, elem=2, n_sink=1, n_local=2):
     G = Hq // Hkv
     per = n_cand * D * elem + n_att * 64 * D * elem * 2 + 2 * G * D * elem
     return per * B * Hkv
+
+
+def profiled_traffic(summary, key):
+    """HBM bytes per launch from a committed rocprofv3 counter summary under profiles/, or None
+    if there is none or the kernel sources changed since the counters were taken."""
+    try:
+        text = open(os.path.join(ROOT, "profiles", summary)).read()
+        val = int(re.search(key + r": (\d+)", text).group(1))
+        for src, sha in re.findall(r"kernel_source(?:_\d+)?: (\S+)\s+kernel_source(?:_\d+)?_sha256_16: (\w+)",
+                                   text):
+            cur = hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest()[:16]
+            if cur != sha:
+                return None
+        return val
+    except (OSError, AttributeError, ValueError):
+        return None
 
 
 def parse():
@@ -308,7 +326,10 @@ def main():
                          "attend": pre["attn_ms"]},
         "roofline": {"bound": "mfma", "achieved": pre["attended_tflops_kernel"],
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": pre["attended_tflops_kernel"] / PEAK_BF16_TFLOPS, "traffic": None,
+                     "frac": pre["attended_tflops_kernel"] / PEAK_BF16_TFLOPS,
+                     "traffic": profiled_traffic("attend_prefill_sas_bf16_128k.md",
+                                                 "traffic_bytes_per_launch"),
+                     "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE)",
                      "kernel": "attend_prefill_bf16_kernel<128, SAS, 4>"},
     }
     if dec is not None:
@@ -319,7 +340,9 @@ def main():
             "breakdown_us": {"select": dec["select_us"], "attend": dec["attn_us"]},
             "roofline": {"bound": "hbm", "achieved": dec["hbm_gbps"], "peak": PEAK_HBM_GBPS,
                          "unit": "GB/s", "frac": dec["hbm_frac"],
-                         "algorithmic_bytes": dec["algorithmic_bytes"]}}
+                         "algorithmic_bytes": dec["algorithmic_bytes"],
+                         "traffic": profiled_traffic("decode_bf16_32x128k.md",
+                                                     "traffic_bytes_per_step")}}
     if hils is not None:
         line["hils_1m"] = {"tok_per_s": hils["tok_per_s"], "ms_per_step": hils["ms_per_step"],
                            "attended_tflops_attention_kernel": hils["attended_tflops_kernel"],
