@@ -77,13 +77,11 @@ __global__ __launch_bounds__(HPW * 128) void attend_prefill_bf16_kernel(
   __shared__ __attribute__((aligned(16))) bf16 Vs[2][kBlock * VP];
   __shared__ float wbuf[MODE == 2 ? NWAVE * 64 * 32 : 1];
 
-  // XCD-aware order: workgroups are dispatched round-robin over the 8 XCDs, so give each XCD a
-  // contiguous range of (batch, head chunk, query block) -- neighbouring query blocks share
-  // their local window and sink in that XCD's L2.
+  // Order: kv group major, query blocks (heavy, late ones first) minor.  Workgroups are dealt
+  // round-robin over the 8 XCDs, so all XCDs work on the same kv group at a time and share its
+  // K/V blocks through the memory-side cache instead of each streaming a different group.
   const int nh = Hkv * n_hc;
-  const int total = NQB * nh * (int)gridDim.z;
-  int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
-  if (total % 8 == 0) lin = (lin % 8) * (total / 8) + lin / 8;
+  const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
   const int b = lin / (NQB * nh);
   const int rem = lin % (NQB * nh);
   const int gh = rem / NQB;
