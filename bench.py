@@ -330,7 +330,7 @@ def main():
                      "traffic": profiled_traffic("attend_prefill_sas_bf16_128k.md",
                                                  "traffic_bytes_per_launch"),
                      "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE)",
-                     "kernel": "attend_prefill_bf16_kernel<128, SAS, 4>"},
+                     "kernel": "attend_prefill_pp_kernel<128, SAS>"},
     }
     if dec is not None:
         line["decode"] = {

@@ -20,6 +20,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "bsa_common.hpp"
 #include "bsa_internal.hpp"
@@ -59,6 +60,8 @@ __device__ __forceinline__ int count_valid(const int32_t* row, int NA) {
 // max exceeds it by more than 8 (probabilities then stay below 2^8, far inside float32 and bf16
 // range); the final O / sum is unchanged by the choice of reference max.
 constexpr float kLazyRescale = 8.0f;
+constexpr int kPpUnits = 4;       // staging units in LDS for the ping-pong prefill kernel (a power
+                                   // of two keeps the unit addressing cheap)
 
 template <int D, int MODE, int HPW>
 __global__ __launch_bounds__(HPW * 128) void attend_prefill_bf16_kernel(
@@ -354,6 +357,387 @@ __global__ __launch_bounds__(HPW * 128) void attend_prefill_bf16_kernel(
     if (MODE != 2 && lse != nullptr && half == 0) lse[(size_t)(b * Hq + h) * T + tq] = lse_val;
   }
 }
+// One 16-byte-per-lane copy from global memory straight into LDS: lane l's 16 bytes at
+// gbase + voff land at LDS byte address lds_addr + 16 l (gbase and lds_addr wave-uniform).  Issued as inline assembly so the
+// compiler does not treat the copy as an LDS write of unknown extent: its own tracking would
+// otherwise wait for every copy in flight before each LDS read and at each barrier, which
+// defeats copying several blocks ahead.  Completion is the caller's business (vmcnt); M0 is
+// saved and restored around the copy.
+__device__ __forceinline__ void dma_row16(const char* gbase, uint32_t voff, uint32_t lds_addr) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  // both addresses are wave-uniform; make that explicit so they live in scalar registers
+  // (readfirstlane returns int: widen through uint32_t so the low half is not sign-extended)
+  const uint32_t la = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr);
+  const uint64_t ga = (uint64_t)(uintptr_t)gbase;
+  const uint32_t g_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(ga >> 32));
+  const uint32_t g_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)ga);
+  const uint64_t gs = ((uint64_t)g_hi << 32) | (uint64_t)g_lo;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(la), "v"(voff), "s"(gs)
+      : "memory");
+#endif
+}
+
+// ---------------------------------------------------------------------------------------------
+// bf16 prefill, PLAIN / SAS, four query heads per workgroup: ping-pong schedule
+// ---------------------------------------------------------------------------------------------
+// The eight waves form two groups of four (waves 0-3 and 4-7; each SIMD holds one wave of each).
+// A wave's work per attended entry a alternates a matrix phase M(a) -- O^T += V(a-1)^T P(a-1)^T
+// and S^T(a) = K(a) Q^T, all MFMA and LDS reads -- and a vector phase V(a) -- the online softmax
+// of S(a) into P(a), all VALU.  The second group runs one phase behind the first, so in every
+// phase one wave of each SIMD multiplies while the other exponentiates, and the SIMD overlaps the
+// two instead of alternating between them.  A barrier separates phases.
+//
+// LDS holds two staging units; unit a = {K of entry a, V of entry a-1} is read in phases 2a and
+// 2a+1 and copied straight from memory into LDS (global_load_lds, 1 KB per instruction, no
+// register round trip) during phases 2a-2 and 2a-1, the copies of all eight waves sharing the
+// 32 KB.  16-byte chunks are XOR-swizzled per row so the K fragment reads and the transposed V
+// reads are free of bank conflicts.
+template <int D, int MODE, bool PRIO>
+__global__ __launch_bounds__(512) void attend_prefill_pp_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const int32_t* __restrict__ idx, const float* __restrict__ sc, bf16* __restrict__ out,
+    float* __restrict__ lse, int Hq, int Hkv, int G, int T, int NQB, int NA, int n_hc,
+    float scale_log2) {
+  constexpr int C16 = D / 8;                  // 16-byte chunks per row
+  constexpr int RPI = kWave / C16;            // rows per 1 KB copy instruction
+  constexpr int TILE = kBlock * D;            // elements of one K or V tile
+  constexpr int HSL = kBlock / RPI;           // copy instructions per tile
+  constexpr int SPW = 2 * HSL / 8;            // copy instructions per wave per unit
+  static_assert(SPW % 2 == 0, "each wave copies as many K as V slabs");
+  __shared__ __attribute__((aligned(16))) bf16 U[kPpUnits][2 * TILE];
+
+  // Order: (batch, kv group) pairs one after another, so that all XCDs share one group's K/V
+  // blocks through the memory-side cache; within a pair, workgroups are dealt round-robin over
+  // the 8 XCDs and each XCD takes a contiguous run of query blocks, so the blocks that
+  // neighbouring query blocks share (local window, sink, overlapping top-K choices) are reused
+  // from that XCD's L2.
+  const int nh = Hkv * n_hc;
+  const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  int pair, qb;
+  if (NQB % 8 == 0) {
+    const int per = NQB / 8, xcd = lin % 8, kk = lin / 8;
+    pair = kk / per;
+    qb = xcd * per + kk % per;
+  } else {
+    pair = lin / NQB;
+    qb = lin % NQB;
+  }
+  const int b = pair / nh;
+  const int gh = pair % nh;
+  const int c = NQB - 1 - qb;                 // heavy (late) query blocks first
+  const int g = gh / n_hc;
+  const int hc = gh % n_hc;
+
+  const int tid = threadIdx.x;
+  const int w = tid / kWave;
+  const int lane = tid % kWave;
+  const int half = lane / 32;
+  const int l32 = lane % 32;
+  const bool lead = w < 4;                    // the leading group
+  const int h = g * G + hc * 4 + w / 2;
+  const int tq = c * kBlock + (w % 2) * 32 + l32;
+  const bool row_ok = tq < T;
+  auto swzk = [](int row) { return D == 128 ? row % 16 : (row / 2) % 8; };
+  auto swzv = [](int row) { return D == 128 ? 4 * (row % 4) : 0; };
+
+  bf16x8 qf[D / 16];
+  {
+    const bf16* qrow = q + ((size_t)(b * Hq + h) * T + min(tq, T - 1)) * D;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      u32x4 raw = *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * half);
+      if (!row_ok) raw = u32x4{0u, 0u, 0u, 0u};
+      qf[s] = __builtin_bit_cast(bf16x8, raw);
+    }
+  }
+  const size_t kvbase = (size_t)(b * Hkv + g) * T * D;
+  const size_t rowsel = ((size_t)(b * Hkv + g) * NQB + c) * NA;
+  const int32_t* irow = idx + rowsel;
+  const float* srow = sc + rowsel;
+  const int nval = count_valid(irow, NA);
+
+  // entries 0..63 one per lane (block index, SAS gate in log2 units); later ones re-read
+  int jvec = lane < nval ? irow[lane] : -1;
+  float gvec = 0.0f;
+  float s_ref = 0.0f;
+  if constexpr (MODE == 1) {
+    if (nval > 0) s_ref = srow[nval - 1];
+    if (lane < nval && jvec != c) gvec = log_sigmoid(srow[lane] - s_ref) * kLog2e;
+  }
+  auto entry = [&](int a) {          // block of entry a (a < nval), wave-uniform
+    const int j = a < kWave ? __builtin_amdgcn_readlane(jvec, a) : irow[a];
+    return (j >= 0 && j <= c) ? j : -1;
+  };
+  auto gate = [&](int a, int j) {
+    if constexpr (MODE != 1) return 0.0f;
+    if (j == c) return 0.0f;
+    if (a < kWave) return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gvec), a));
+    return log_sigmoid(srow[a] - s_ref) * kLog2e;
+  };
+
+  // ---- staging: wave w copies K slabs w, w+8, .. and V slabs w, w+8, .. of a unit ----
+  // Unit a = {K(entry a), V(entry a-1)}, 0 <= a <= nval; the halves that do not exist (V of
+  // unit 0, K of unit nval) copy a neighbouring entry instead so that every unit costs each wave
+  // exactly SPW copy instructions (the waits count them).
+  // Source of lane `lane` of copy instruction i within a block: row crow[i] (a block row past the
+  // end of the sequence reads the last row instead; its probability is zero), logical chunk
+  // (physical ^ swizzle); the block's base address is wave-uniform.
+  int crow[SPW / 2], kcol[SPW / 2], vcol_[SPW / 2];
+#pragma unroll
+  for (int i = 0; i < SPW / 2; ++i) {
+    crow[i] = (w + 8 * i) * RPI + lane / C16;
+    kcol[i] = ((lane % C16) ^ swzk(crow[i])) * 16;
+    vcol_[i] = ((lane % C16) ^ swzv(crow[i])) * 16;
+  }
+  const char* kb = reinterpret_cast<const char*>(k + kvbase);
+  const char* vb = reinterpret_cast<const char*>(v + kvbase);
+  // This wave's part of unit a: SPW copies of 1 KB (K slab, V slab, K slab, ...), issued in two
+  // halves: copies x with x % 2 == h for half h (K slabs, then V slabs).
+  const uint32_t u_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16*)&U[0][0];
+  auto copy_half = [&](int a, int hv) {
+    const uint32_t dst = u_lds + (uint32_t)(a % kPpUnits) * (2 * TILE * 2);
+    int j = hv == 0 ? entry(min(a, nval - 1)) : entry(max(a - 1, 0));
+    j = j < 0 ? c : j;
+    const int lim = T - 1 - j * kBlock;
+    const char* blk = (hv == 0 ? kb : vb) + (size_t)j * (kBlock * D * 2);
+#pragma unroll
+    for (int i = 0; i < SPW / 2; ++i) {
+      const int sl = w + 8 * i;
+      dma_row16(blk, (uint32_t)(min(crow[i], lim) * (D * 2) + (hv == 0 ? kcol[i] : vcol_[i])),
+                dst + (hv * TILE + sl * RPI * D) * 2);
+    }
+  };
+  auto copy_unit = [&](int a) {
+    copy_half(a, 0);
+    copy_half(a, 1);
+  };
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[dt][i] = 0.0f;
+  f32x16 st[2];
+  bf16x8 pf[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pf[ks][e] = f2bf(0.0f);
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  const int vrow = (lane % 16) / 4;
+  const int vcol = 16 * ((lane / 16) % 2) + 4 * (lane % 4);
+
+  // matrix phase of entry a: O^T += V^T P^T for entry a-1 (PV) and S^T = K Q^T for entry a
+  // (QK).  LDS reads run one MFMA group ahead of the MFMAs that consume them: the V fragments
+  // of k-step ks+1 (or the first K fragments) load during the MFMAs of k-step ks, the second
+  // key tile's K fragments during the first tile's MFMAs.
+  auto mphase = [&](int a, auto pv_tag, auto qk_tag) {
+    constexpr bool PV = decltype(pv_tag)::value;
+    constexpr bool QK = decltype(qk_tag)::value;
+    if (PRIO) __builtin_amdgcn_s_setprio(1);
+    const bf16* Ku = U[a % kPpUnits];
+    const bf16* Vu = U[a % kPpUnits] + TILE;
+    auto read_v = [&](int ks, bf16x8* vf) {
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const int r0 = 16 * ks + 4 * half + vrow;
+        const int col = dt * 32 + vcol;
+        const bf16* p0 = Vu + r0 * D + (((col / 8) ^ swzv(r0)) * 8) + col % 8;
+        const bf16* p1 = Vu + (r0 + 8) * D + (((col / 8) ^ swzv(r0 + 8)) * 8) + col % 8;
+        const i16x4 x0 = lds_read_tr16(p0);
+        const i16x4 x1 = lds_read_tr16(p1);
+        vf[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    };
+    auto read_k = [&](int kt, bf16x8* kf) {
+      const int row = kt * 32 + l32;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s)
+        kf[s] = *reinterpret_cast<const bf16x8*>(Ku + row * D + (((2 * s + half) ^ swzk(row)) * 8));
+    };
+    bf16x8 kf[2][D / 16];
+    if constexpr (PV) {
+      bf16x8 vf[4][D / 32];
+      read_v(0, vf[0]);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (D / 32), 0);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        if (ks < 3) read_v(ks + 1, vf[ks + 1]);
+        else if (QK) read_k(0, kf[0]);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) o[dt] = mfma32(vf[ks][dt], pf[ks], o[dt]);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (ks < 3 || QK) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+      }
+    } else {
+      read_k(0, kf[0]);
+      __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 0);
+    }
+    if constexpr (QK) {
+      read_k(1, kf[1]);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st[kt][i] = 0.0f;
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) st[kt] = mfma32(kf[kt][s], qf[s], st[kt]);
+      }
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, D / 16, 0);
+    }
+    if (PRIO) __builtin_amdgcn_s_setprio(0);
+  };
+
+  // vector phase of entry a: online softmax of its scores into pf
+  auto vphase = [&](int a) {
+    const int j = entry(a);
+    float mx = -INFINITY;
+    if (j < 0) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st[kt][i] = -INFINITY;
+    } else if (j == c) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+          if (j * kBlock + key > tq) st[kt][i] = -INFINITY;
+          mx = fmaxf(mx, st[kt][i]);
+        }
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[kt][i]);
+    }
+    mx = wave_max_xor32(mx);
+    const float gate2 = gate(a, j);
+    const float m_blk = fmaf(mx, scale_log2, gate2);
+    const bool need = m_blk > m_run + kLazyRescale;
+    if (__any(need)) {
+      const float m_new = need ? m_blk : m_run;
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+    }
+    const float bias = gate2 - m_run;
+    float lsum = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = fast_exp2(fmaf(st[ks / 2][8 * (ks % 2) + e], scale_log2, bias));
+        lsum += p;
+        pf[ks][e] = f2bf(p);
+      }
+    l_run += lsum;
+  };
+
+  // Phases (lead = waves 0-3, trail = waves 4-7; M = matrix phase, V = vector phase):
+  //   0: lead M(0) QK only        1: lead V(0),   trail M(0) QK only
+  //   2a: lead M(a), trail V(a-1)  2a+1: lead V(a), trail M(a)      (1 <= a < n)
+  //   2n: lead M(n) PV only, trail V(n-1)      2n+1: trail M(n) PV only
+  // Unit a+3 is copied during phases 2a and 2a+1 into the buffer of unit a-1 (read for the last
+  // time in phase 2a-1): each wave issues half of its share after the MFMAs of its matrix phase
+  // and half at the start of its vector phase, which spreads the copies over both phases.  Unit
+  // a+1 is waited for at the end of phase 2a+1, so a copy has four to five phases to land.
+  using T_ = std::integral_constant<bool, true>;
+  using F_ = std::integral_constant<bool, false>;
+  constexpr int AHEAD = kPpUnits - 1;
+  static_assert(AHEAD == 3, "the waits below count up to two units in flight");
+  const int n = nval;
+  // wait until at most `left` (0..2) units of copies are still in flight
+  auto wait_units = [&](int left) {
+    if (left >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * SPW));
+    else if (left == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | SPW);
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
+  };
+  if (n > 0) {
+    for (int u = 0; u < AHEAD && u <= n; ++u) copy_unit(u);
+    wait_units(min(AHEAD - 1, n));              // unit 0 has landed
+    __syncthreads();
+    if (lead) {
+      mphase(0, F_{}, T_{});
+      if (AHEAD <= n) copy_half(AHEAD, 0);
+    } else if (AHEAD <= n) {
+      copy_half(AHEAD, 0);
+    }
+    __syncthreads();
+    if (lead) {
+      if (AHEAD <= n) copy_half(AHEAD, 1);
+      vphase(0);
+    } else {
+      mphase(0, F_{}, T_{});
+      if (AHEAD <= n) copy_half(AHEAD, 1);
+    }
+    wait_units(min(AHEAD, n) - 1);              // unit 1 has landed
+    __syncthreads();
+    for (int a = 1; a < n; ++a) {
+      const bool cp = a + AHEAD <= n;
+      if (lead) {
+        mphase(a, T_{}, T_{});
+        if (cp) copy_half(a + AHEAD, 0);
+      } else {
+        if (cp) copy_half(a + AHEAD, 0);
+        vphase(a - 1);
+      }
+      __syncthreads();
+      if (lead) {
+        if (cp) copy_half(a + AHEAD, 1);
+        vphase(a);
+      } else {
+        mphase(a, T_{}, T_{});
+        if (cp) copy_half(a + AHEAD, 1);
+      }
+      wait_units(min(a + AHEAD, n) - (a + 1));  // unit a+1 has landed
+      __syncthreads();
+    }
+    if (lead) mphase(n, T_{}, F_{});
+    else vphase(n - 1);
+    __syncthreads();
+    if (!lead) mphase(n, T_{}, F_{});
+  }
+
+  const float l_tot = wave_sum_xor32(l_run);
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  const float lse_val = (m_run + log2f(l_tot)) * kLn2;
+  if (row_ok) {
+    bf16* orow = out + ((size_t)(b * Hq + h) * T + tq) * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        bf16x4 ov;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ov[e] = f2bf(o[dt][4 * i4 + e] * inv);
+        *reinterpret_cast<bf16x4*>(orow + dt * 32 + 8 * i4 + 4 * half) = ov;
+      }
+    if (lse != nullptr && half == 0) lse[(size_t)(b * Hq + h) * T + tq] = lse_val;
+  }
+}
+
 // =============================================================================================
 // bf16 decode: split-K over the attended blocks, one block per wave
 // =============================================================================================
@@ -822,7 +1206,15 @@ static void launch_prefill_bf16_d(const Shape& s, const void* q, const void* k, 
   if (s.mode == 0) BSA_PF(0, HPW);    \
   else if (s.mode == 1) BSA_PF(1, HPW); \
   else BSA_PF(2, HPW);
-  if (hpw == 4) {
+#define BSA_PP(MODE)                                                                           \
+  hipLaunchKernelGGL((attend_prefill_pp_kernel<D, MODE, true>), grid, dim3(512), 0, st,         \
+                     (const bf16*)q, (const bf16*)k, (const bf16*)v, idx, sc, (bf16*)out, lse, \
+                     s.Hq, s.Hkv, s.G, s.Tq, s.R, s.NA, n_hc, sl2)
+  if (hpw == 4 && s.mode == 0) {
+    BSA_PP(0);
+  } else if (hpw == 4 && s.mode == 1) {
+    BSA_PP(1);
+  } else if (hpw == 4) {
     BSA_PF_MODE(4)
   } else if (hpw == 2) {
     BSA_PF_MODE(2)
@@ -831,6 +1223,7 @@ static void launch_prefill_bf16_d(const Shape& s, const void* q, const void* k, 
   }
 #undef BSA_PF_MODE
 #undef BSA_PF
+#undef BSA_PP
 }
 
 template <int D>

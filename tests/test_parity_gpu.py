@@ -130,6 +130,8 @@ SMALL_PREFILL = [
     ("kall",         1, 4,  1,   64 * 6,      128, "bf16", 50,  1, 2, "iid"),
     ("sink0_local1", 1, 4,  1,   64 * 7,      128, "bf16", 2,   0, 1, "iid"),
     ("sink2_local3", 1, 4,  2,   64 * 8 + 9,  64,  "bf16", 2,   2, 3, "clustered"),
+    ("g4_nqb16_tail", 2, 8, 2,   64 * 15 + 5, 128, "bf16", 3,   1, 2, "clustered"),
+    ("g4_nqb8_d64",  1, 4,  1,   64 * 8,      64,  "bf16", 2,   1, 2, "clustered"),
     ("t1",           1, 4,  1,   1,           128, "bf16", 2,   1, 2, "iid"),
     ("t64",          1, 4,  1,   64,          64,  "bf16", 2,   1, 2, "iid"),
     ("f32_g2",       1, 2,  1,   64 * 8 + 5,  64,  "f32",  2,   1, 2, "iid"),
