@@ -60,6 +60,7 @@ __device__ __forceinline__ int count_valid(const int32_t* row, int NA) {
 // max exceeds it by more than 8 (probabilities then stay below 2^8, far inside float32 and bf16
 // range); the final O / sum is unchanged by the choice of reference max.
 constexpr float kLazyRescale = 8.0f;
+constexpr float kPpSumLimit = 65536.0f;   // see the vector phase of the ping-pong kernel
 constexpr int kPpUnits = 4;       // staging units in LDS for the ping-pong prefill kernel (a power
                                    // of two keeps the unit addressing cheap)
 
@@ -604,10 +605,14 @@ __global__ __launch_bounds__(512) void attend_prefill_pp_kernel(
     if (PRIO) __builtin_amdgcn_s_setprio(0);
   };
 
-  // vector phase of entry a: online softmax of its scores into pf
+  // vector phase of entry a: online softmax of its scores into pf.  The probabilities are first
+  // taken against the running reference max; only if some row's sum then exceeds kPpSumLimit
+  // (the block holds scores far above the reference, or this is the row's first block, whose
+  // reference is -inf) is the block max formed, O and the sum rescaled and the probabilities
+  // recomputed.  Below the limit every probability is at most kPpSumLimit, far inside float32
+  // and bf16 range, and the final O / sum does not depend on the reference.
   auto vphase = [&](int a) {
     const int j = entry(a);
-    float mx = -INFINITY;
     if (j < 0) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -620,20 +625,30 @@ __global__ __launch_bounds__(512) void attend_prefill_pp_kernel(
         for (int i = 0; i < 16; ++i) {
           const int key = kt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
           if (j * kBlock + key > tq) st[kt][i] = -INFINITY;
-          mx = fmaxf(mx, st[kt][i]);
         }
-    } else {
+    }
+    const float gate2 = gate(a, j);
+    auto probs = [&](float bias) {
+      float lsum = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = fast_exp2(fmaf(st[ks / 2][8 * (ks % 2) + e], scale_log2, bias));
+          lsum += p;
+          pf[ks][e] = f2bf(p);
+        }
+      return lsum;
+    };
+    float lsum = probs(gate2 - m_run);
+    if (__any(!(lsum <= kPpSumLimit))) {        // also true for inf / NaN sums
+      float mx = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[kt][i]);
-    }
-    mx = wave_max_xor32(mx);
-    const float gate2 = gate(a, j);
-    const float m_blk = fmaf(mx, scale_log2, gate2);
-    const bool need = m_blk > m_run + kLazyRescale;
-    if (__any(need)) {
-      const float m_new = need ? m_blk : m_run;
+      mx = wave_max_xor32(mx);
+      const float m_new = fmaxf(m_run, fmaf(mx, scale_log2, gate2));
       const float alpha = fast_exp2(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
@@ -641,17 +656,8 @@ __global__ __launch_bounds__(512) void attend_prefill_pp_kernel(
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+      lsum = probs(gate2 - m_run);
     }
-    const float bias = gate2 - m_run;
-    float lsum = 0.0f;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = fast_exp2(fmaf(st[ks / 2][8 * (ks % 2) + e], scale_log2, bias));
-        lsum += p;
-        pf[ks][e] = f2bf(p);
-      }
     l_run += lsum;
   };
 
@@ -675,15 +681,14 @@ __global__ __launch_bounds__(512) void attend_prefill_pp_kernel(
     else __builtin_amdgcn_s_waitcnt(0x0F70);
   };
   if (n > 0) {
-    for (int u = 0; u < AHEAD && u <= n; ++u) copy_unit(u);
-    wait_units(min(AHEAD - 1, n));              // unit 0 has landed
+    // only unit 0 before the first phase: the copies of units 1..AHEAD-1 go out after the lead
+    // group's first matrix phase (and while the trail group waits for it)
+    copy_unit(0);
+    wait_units(0);                              // unit 0 has landed
     __syncthreads();
-    if (lead) {
-      mphase(0, F_{}, T_{});
-      if (AHEAD <= n) copy_half(AHEAD, 0);
-    } else if (AHEAD <= n) {
-      copy_half(AHEAD, 0);
-    }
+    if (lead) mphase(0, F_{}, T_{});
+    for (int u = 1; u < AHEAD && u <= n; ++u) copy_unit(u);
+    if (AHEAD <= n) copy_half(AHEAD, 0);
     __syncthreads();
     if (lead) {
       if (AHEAD <= n) copy_half(AHEAD, 1);
