@@ -12,7 +12,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libbsa.so")
-SOURCES = ["bsa_api.hip", "pool.hip", "select.hip", "attend.hip"]
+SOURCES = ["bsa_api.hip", "pool.hip", "select.hip", "attend_prefill.hip", "attend_decode.hip",
+           "attend_f32.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

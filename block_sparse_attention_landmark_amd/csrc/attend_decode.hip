@@ -1,0 +1,391 @@
+// Block-sparse attention over the attended block lists: bf16 decode kernels (one query token
+// per sequence; the attended blocks of each (sequence, kv group) are streamed by one or more
+// workgroups and the partial softmax states merged through their log-sum-exp).  Same PLAIN /
+// SAS / HiLS rules as the prefill kernels.
+#include <math.h>
+
+#include <algorithm>
+
+#include "attend_common.hpp"
+#include "bsa_internal.hpp"
+
+namespace bsa {
+
+// =============================================================================================
+// bf16 decode: split-K over the attended blocks, one block per wave
+// =============================================================================================
+constexpr int kDecodeWaves = 4;          // waves per workgroup
+constexpr int kMergeMaxSplits = 64;      // partial states merged per (sequence, kv group)
+
+constexpr int kDecodeTargetWorkgroups = 256;   // one per CU is enough to stream the cache
+
+// Splits of the attended blocks of one (sequence, kv group): as few as keep the GPU busy (each
+// split's partial state costs a write and a read), at most kMergeMaxSplits.
+inline int decode_nsplit(int NA, int pairs) {
+  const int max_useful = (NA + kDecodeWaves - 1) / kDecodeWaves;
+  const int want = (kDecodeTargetWorkgroups + pairs - 1) / pairs;
+  return std::max(1, std::min(std::min(want, max_useful), kMergeMaxSplits));
+}
+inline int decode_blocks_per_wave(int NA, int nsplit) {
+  const int per_split = (NA + nsplit - 1) / nsplit;
+  return (per_split + kDecodeWaves - 1) / kDecodeWaves;
+}
+
+// One workgroup per (sequence, kv group, split); wave w of split s takes the attended entries
+// (s * waves * bpw) + w + waves * i, i < bpw.  K and V blocks are copied straight from memory
+// into the wave's LDS tiles (no register round trip, 1 KB per instruction), with 16-byte chunks
+// XOR-swizzled so the fragment and transposed reads are free of bank conflicts.  Each wave keeps
+// an online softmax state; the waves' states are combined in LDS and written as the split's
+// partial state.
+template <int D, int MODE>
+__global__ __launch_bounds__(kDecodeWaves * 64) void attend_decode_bf16_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
+    const bf16* __restrict__ lm, const int32_t* __restrict__ idx, const float* __restrict__ sc,
+    float* __restrict__ part_o, float* __restrict__ part_ml, bf16* __restrict__ out,
+    float* __restrict__ lse, int Hq, int Hkv, int G, int Tk, int NB, int NA, int nsplit, int bpw,
+    float scale_log2) {
+  constexpr int C16 = D / 8;                 // 16-byte chunks per row
+  constexpr int RPI = 64 / C16;              // rows covered by one 64-lane 16-byte copy
+  __shared__ __attribute__((aligned(16))) bf16 Ks[kDecodeWaves][kBlock * D];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[kDecodeWaves][kBlock * D];
+  __shared__ float comb_ml[kDecodeWaves][32][2];
+
+  const int split = blockIdx.x;
+  const int g = blockIdx.y;
+  const int b = blockIdx.z;
+  const int w = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int half = lane / 32;
+  const int l32 = lane % 32;
+  const bool row_ok = l32 < G;
+  const int h = g * G + min(l32, G - 1);
+  const int c = (Tk - 1) / kBlock;
+  // chunk swizzles (physical 16-byte chunk = logical ^ swz(row)): for the V tile, the four rows of
+  // a transposed read land on distinct banks; for the K tile, the 16 rows of a fragment read do
+  auto swz = [](int row) { return D == 128 ? 4 * (row % 4) : 0; };
+  auto swzk = [](int row) { return D == 128 ? row % 16 : (row / 2) % 8; };
+
+  bf16x8 qf[D / 16];
+  {
+    const bf16* qrow = q + (size_t)(b * Hq + h) * D;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      u32x4 raw = *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * half);
+      if (!row_ok) raw = u32x4{0u, 0u, 0u, 0u};
+      qf[s] = __builtin_bit_cast(bf16x8, raw);
+    }
+  }
+  const size_t kvbase = (size_t)(b * Hkv + g) * Tk * D;
+  const int32_t* irow = idx + (size_t)(b * Hkv + g) * NA;
+  const float* srow = sc + (size_t)(b * Hkv + g) * NA;
+  const int nval = count_valid(irow, NA);
+  bf16* kt_ = Ks[w];
+  bf16* vt = Vs[w];
+  const int vrow = (lane % 16) / 4;
+  const int vcol = 16 * ((lane / 16) % 2) + 4 * (lane % 4);
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[dt][i] = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  // entry of iteration it, or -1
+  auto entry = [&](int it) {
+    const int a = split * kDecodeWaves * bpw + w + kDecodeWaves * it;
+    const int j = (it < bpw && a < nval) ? irow[a] : -1;
+    return (j >= 0 && j <= c) ? j : -1;
+  };
+  // copy the K (or V) rows of block j into this wave's tile, 1 KB per instruction (rows past
+  // the cache end read its last row; their probabilities are zero)
+  auto copy_k = [&](int j) {
+#pragma unroll
+    for (int n = 0; n < kBlock / RPI; ++n) {
+      const int row = n * RPI + lane / C16;
+      const int tok = min(j * kBlock + row, Tk - 1);
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(kc + kvbase + (size_t)tok * D +
+                                                          ((lane % C16) ^ swzk(row)) * 8),
+          (__attribute__((address_space(3))) void*)(kt_ + n * RPI * D), 16, 0, 0);
+    }
+  };
+  auto copy_v = [&](int j) {
+#pragma unroll
+    for (int n = 0; n < kBlock / RPI; ++n) {
+      const int row = n * RPI + lane / C16;
+      const int tok = min(j * kBlock + row, Tk - 1);
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(vc + kvbase + (size_t)tok * D +
+                                                          ((lane % C16) ^ swz(row)) * 8),
+          (__attribute__((address_space(3))) void*)(vt + n * RPI * D), 16, 0, 0);
+    }
+  };
+
+  // find the first valid entry and start its copies
+  int it0 = 0;
+  int j = entry(0);
+  while (j < 0 && it0 + 1 < bpw) j = entry(++it0);
+  if (j >= 0) {
+    copy_k(j);
+    copy_v(j);
+  }
+  for (int it = it0; it < bpw && j >= 0; ) {
+    const int a = split * kDecodeWaves * bpw + w + kDecodeWaves * it;
+    // next valid entry: its copies start as soon as this block's tiles are read
+    int it_next = it + 1;
+    int jn = entry(it_next);
+    while (jn < 0 && it_next + 1 < bpw) jn = entry(++it_next);
+    __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): both tiles of block j have landed
+    // S^T = K Q^T with K fragments (key kt*32 + l32, dims 16s + 8*half .. +8) read from LDS
+    bf16x8 kf[2][D / 16];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int row = kt * 32 + l32;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s)
+        kf[kt][s] = *reinterpret_cast<const bf16x8*>(kt_ + row * D + (((2 * s + half) ^ swzk(row)) * 8));
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): the K tile may be overwritten
+    if (jn >= 0) copy_k(jn);
+    f32x16 st[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st[kt][i] = 0.0f;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) st[kt] = mfma32(kf[kt][s], qf[s], st[kt]);
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+        if (j * kBlock + key >= Tk) st[kt][i] = -INFINITY;
+        mx = fmaxf(mx, st[kt][i]);
+      }
+    mx = wave_max_xor32(mx);
+    float alpha, coef = 1.0f;
+    if constexpr (MODE == 2) {
+      // per-chunk softmax, then an online softmax over the chunks' retrieval scores
+      float lsum = 0.0f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float e = fast_exp2(fmaf(st[kt][i], scale_log2, -mx * scale_log2));
+          st[kt][i] = e;
+          lsum += e;
+        }
+      const bf16* lrow = lm + ((size_t)(b * Hkv + g) * NB + j) * D;
+      float part = 0.0f;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        const bf16x8 lv = *reinterpret_cast<const bf16x8*>(lrow + 16 * s + 8 * half);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part += bf2f(qf[s][e]) * bf2f(lv[e]);
+      }
+      const float r2 = wave_sum_xor32(part) * scale_log2;     // retrieval score, log2 units
+      const float m_new = fmaxf(m_run, r2);
+      alpha = fast_exp2(m_run - m_new);
+      const float wr = fast_exp2(r2 - m_new);
+      l_run = l_run * alpha + wr;
+      m_run = m_new;
+      coef = wr / wave_sum_xor32(lsum);
+    } else {
+      float gate2 = 0.0f;
+      if (MODE == 1 && j != c) gate2 = log_sigmoid(srow[a] - srow[nval - 1]) * kLog2e;
+      const float m_new = fmaxf(m_run, fmaf(mx, scale_log2, gate2));
+      alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      const float bias = gate2 - m_run;
+      float lsum = 0.0f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = fast_exp2(fmaf(st[kt][i], scale_log2, bias));
+          st[kt][i] = p;
+          lsum += p;
+        }
+      l_run = l_run * alpha + wave_sum_xor32(lsum);
+    }
+    if (alpha != 1.0f) {
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+    }
+    // O^T += V^T P^T; transposed reads of the swizzled V tile, all issued before the MFMAs
+    bf16x8 vf[4][D / 32];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const int r0 = 16 * ks + 4 * half + vrow;
+        const int col = dt * 32 + vcol;               // element column (multiple of 4)
+        const bf16* p0 = vt + r0 * D + (((col / 8) ^ swz(r0)) * 8) + col % 8;
+        const bf16* p1 = vt + (r0 + 8) * D + (((col / 8) ^ swz(r0 + 8)) * 8) + col % 8;
+        const i16x4 x0 = lds_read_tr16(p0);
+        const i16x4 x1 = lds_read_tr16(p1);
+        vf[ks][dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): the V tile may be overwritten
+    if (jn >= 0) copy_v(jn);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 pb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[e] = f2bf(st[ks / 2][8 * (ks % 2) + e] * coef);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) o[dt] = mfma32(vf[ks][dt], pb, o[dt]);
+    }
+    it = it_next;
+    j = jn;
+  }
+
+  // combine the waves' states (rows < G) through LDS (the K tiles are reused)
+  __syncthreads();
+  float* comb_o = reinterpret_cast<float*>(&Ks[0][0]);        // [wave][row][D]
+  if (row_ok) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        f32x4 ov;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ov[e] = o[dt][4 * i4 + e];
+        *reinterpret_cast<f32x4*>(&comb_o[(w * 32 + l32) * D + dt * 32 + 8 * i4 + 4 * half]) = ov;
+      }
+    if (half == 0) {
+      comb_ml[w][l32][0] = m_run;
+      comb_ml[w][l32][1] = l_run;
+    }
+  }
+  __syncthreads();
+  const size_t pbase = ((size_t)(b * Hkv + g) * nsplit + split) * G;
+  for (int e = threadIdx.x; e < G * D; e += kDecodeWaves * 64) {
+    const int row = e / D, d = e % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < kDecodeWaves; ++v) M = fmaxf(M, comb_ml[v][row][0]);
+    float L = 0.0f, acc = 0.0f;
+#pragma unroll
+    for (int v = 0; v < kDecodeWaves; ++v) {
+      const float m = comb_ml[v][row][0];
+      if (m == -INFINITY) continue;
+      const float f = fast_exp2(m - M);
+      L += comb_ml[v][row][1] * f;
+      acc += comb_o[(v * 32 + row) * D + d] * f;
+    }
+    if (nsplit == 1) {
+      // a single split is the whole row: normalise and write the output directly
+      const size_t orow = (size_t)b * Hq + g * G + row;
+      out[orow * D + d] = f2bf(acc / L);
+      if (MODE != 2 && lse != nullptr && d == 0) lse[orow] = (M + log2f(L)) * kLn2;
+    } else {
+      part_o[(pbase + row) * D + d] = acc;
+      if (d == 0) {
+        part_ml[(pbase + row) * 2 + 0] = M;
+        part_ml[(pbase + row) * 2 + 1] = L;
+      }
+    }
+  }
+}
+
+// Merge of the split partial states of one (sequence, kv group): every (row, split) pair loads
+// its (m, l) at once, the per-split weights exp2(m_s - M) / L are formed in LDS, then each output
+// element sums its column of partial outputs with independent loads.
+template <typename OUT>
+__global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restrict__ part_o,
+                                                           const float* __restrict__ part_ml,
+                                                           OUT* __restrict__ out,
+                                                           float* __restrict__ lse, int Hkv,
+                                                           int G, int D, int nsplit,
+                                                           int write_lse) {
+  __shared__ float sm[32][kMergeMaxSplits];
+  __shared__ float sl[32][kMergeMaxSplits];
+  const int bg = blockIdx.x;
+  const int b = bg / Hkv, g = bg % Hkv;
+  const size_t pb = (size_t)bg * nsplit;
+  for (int t = threadIdx.x; t < G * nsplit; t += blockDim.x) {
+    const int row = t / nsplit, s = t % nsplit;
+    sm[row][s] = part_ml[((pb + s) * G + row) * 2];
+    sl[row][s] = part_ml[((pb + s) * G + row) * 2 + 1];
+  }
+  __syncthreads();
+  if (threadIdx.x < G) {
+    const int row = threadIdx.x;
+    float M = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, sm[row][s]);
+    float L = 0.0f;
+    for (int s = 0; s < nsplit; ++s) {
+      const float f = (sm[row][s] == -INFINITY) ? 0.0f : fast_exp2(sm[row][s] - M);
+      sm[row][s] = f;
+      L += sl[row][s] * f;
+    }
+    const float inv = 1.0f / L;
+    for (int s = 0; s < nsplit; ++s) sm[row][s] *= inv;
+    if (write_lse && lse != nullptr) lse[(size_t)b * Hkv * G + g * G + row] = (M + log2f(L)) * kLn2;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
+    const int row = e / D, d = e % D;
+    const float* col = part_o + (pb * G + row) * D + d;
+    float acc = 0.0f;
+#pragma unroll 8
+    for (int s = 0; s < nsplit; ++s) acc += col[(size_t)s * G * D] * sm[row][s];
+    out[((size_t)b * Hkv * G + g * G + row) * D + d] = (OUT)acc;
+  }
+}
+
+// =============================================================================================
+// launchers
+// =============================================================================================
+int decode_splits(const Shape& s) { return decode_nsplit(s.NA, s.B * s.Hkv); }
+
+size_t decode_ws_bytes(const Shape& s) {
+  if (!s.bf16 || decode_splits(s) == 1) return 0;
+  const size_t rows = (size_t)s.B * s.Hkv * decode_splits(s) * s.G;
+  const size_t o = (rows * s.D * sizeof(float) + 255) & ~(size_t)255;
+  return o + rows * 2 * sizeof(float);
+}
+
+template <int D>
+static void launch_decode_bf16_d(const Shape& s, const void* q, const void* kc, const void* vc,
+                                 const void* lm, const int32_t* idx, const float* sc, void* out,
+                                 float* lse, void* ws, hipStream_t st) {
+  const int nsplit = decode_splits(s);
+  const size_t rows = (size_t)s.B * s.Hkv * nsplit * s.G;
+  float* part_o = (float*)ws;
+  float* part_ml = (float*)((char*)ws + ((rows * s.D * sizeof(float) + 255) & ~(size_t)255));
+  dim3 grid(nsplit, s.Hkv, s.B);
+  const float sl2 = s.scale * kLog2e;
+#define BSA_DEC(MODE)                                                                          \
+  hipLaunchKernelGGL((attend_decode_bf16_kernel<D, MODE>), grid, dim3(kDecodeWaves * 64), 0, st, \
+                     (const bf16*)q, (const bf16*)kc, (const bf16*)vc, (const bf16*)lm, idx,   \
+                     sc, part_o, part_ml, (bf16*)out, lse, s.Hq, s.Hkv, s.G, s.Tk, s.NB, s.NA,  \
+                     nsplit, decode_blocks_per_wave(s.NA, nsplit), sl2)
+  if (s.mode == 0) BSA_DEC(0);
+  else if (s.mode == 1) BSA_DEC(1);
+  else BSA_DEC(2);
+#undef BSA_DEC
+  if (nsplit > 1)
+    hipLaunchKernelGGL(decode_merge_kernel<bf16>, dim3(s.B * s.Hkv), dim3(256), 0, st, part_o,
+                       part_ml, (bf16*)out, lse, s.Hkv, s.G, s.D, nsplit, s.mode != 2 ? 1 : 0);
+}
+
+hipError_t launch_attend_decode(const Shape& s, const void* q, const void* kc, const void* vc,
+                                const void* lm, const int32_t* idx, const float* sc, void* out,
+                                float* lse, void* ws, hipStream_t st) {
+  if (s.bf16) {
+    if (s.D == 128) launch_decode_bf16_d<128>(s, q, kc, vc, lm, idx, sc, out, lse, ws, st);
+    else launch_decode_bf16_d<64>(s, q, kc, vc, lm, idx, sc, out, lse, ws, st);
+  } else {
+    return launch_attend_f32(s, q, kc, vc, lm, idx, sc, out, lse, st);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace bsa

@@ -44,6 +44,10 @@ hipError_t launch_decode_select(const Shape& s, const void* q, const void* lm, i
 hipError_t launch_attend_prefill(const Shape& s, const void* q, const void* k, const void* v,
                                  const void* lm, const int32_t* idx, const float* sc, void* out,
                                  float* lse, hipStream_t st);
+// float32 path of both attend calls
+hipError_t launch_attend_f32(const Shape& s, const void* q, const void* k, const void* v,
+                             const void* lm, const int32_t* idx, const float* sc, void* out,
+                             float* lse, hipStream_t st);
 hipError_t launch_attend_decode(const Shape& s, const void* q, const void* kc, const void* vc,
                                 const void* lm, const int32_t* idx, const float* sc, void* out,
                                 float* lse, void* ws, hipStream_t st);
