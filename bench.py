@@ -13,6 +13,8 @@ Reported beside it, measured in the same run:
 * the decode path (32 sequences x 128K cached tokens, 64 query / 8 kv heads, top-K=64):
   selection + split-K attention, algorithmic HBM GB/s and fraction of the HBM peak, with the
   caches flushed (a 1 GiB read) between timed steps;
+* the same decode step over a ragged batch held in a paged cache (32 sequences of 16K..128K
+  tokens in shuffled 64-token pages);
 * optionally the HiLS workload at 1M tokens (--hils);
 * the float64 oracle timed on the host cores on a bounded sample of the prefill workload.
 
@@ -217,6 +219,63 @@ def bench_decode(torch, bsa, synth, steps, warmup):
     return res
 
 
+def bench_decode_paged(torch, bsa, synth, steps, warmup):
+    """Ragged batch in a paged cache: paged selection + paged split-K attention per step."""
+    import numpy as np
+    name = "decode_paged_bf16_32x16k_128k"
+    w = synth.WORKLOADS[name]
+    B, Hq, Hkv, D, K = w["B"], w["Hq"], w["Hkv"], w["D"], w["topk"]
+    lens = np.random.default_rng(11).integers(w["T_min"], w["T"] + 1, size=B).tolist()
+    log(f"[bench] decode paged: generating inputs ({sum(lens)} cached tokens)")
+    q, k_pool, v_pool, table, seq_lens = synth.make_paged_decode(
+        lens, Hq, Hkv, D, w["dtype"], w["data"], seed=0, device="cuda",
+        n_centres=w["n_centres"], n_aim=w["n_aim"])
+    q = q[:, :, None, :].contiguous()
+    lm = bsa.pool_landmarks_paged(k_pool, table, seq_lens)     # cache-fill time, not timed
+    NB = table.shape[1]
+    NA = K + 3
+    idx = torch.empty((B, Hkv, 1, NA), dtype=torch.int32, device="cuda")
+    sc = torch.empty((B, Hkv, 1, NA), dtype=torch.float32, device="cuda")
+    out = torch.empty_like(q)
+    p = bsa.make_params(B=B, Hq=Hq, Hkv=Hkv, D=D, seq_q=1, seq_k=NB * 64, dtype=q.dtype, topk=K)
+    ws_dec = torch.empty(max(256, bsa.decode_workspace_bytes(p)), dtype=torch.uint8, device="cuda")
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    ev_step, ev_attn = Events(torch), Events(torch)
+
+    def step(record):
+        if record:
+            ev_step.start()
+        bsa.select_topk_paged(q, lm, seq_lens, topk=K, idx=idx, sc=sc)
+        if record:
+            ev_attn.start()
+        bsa.attend_decode_paged(q, k_pool, v_pool, table, seq_lens, idx, sc, None, mode="plain",
+                                topk=K, out=out, ws=ws_dec)
+        if record:
+            ev_attn.stop()
+            ev_step.pairs[-1][1] = ev_attn.pairs[-1][1]
+
+    for _ in range(warmup):
+        step(False)
+    for _ in range(steps):
+        flush.sum()
+        step(True)
+    torch.cuda.synchronize()
+    nbytes = sum(decode_bytes(1, Hq, Hkv, L, D, K) for L in lens)
+    step_us = 1e3 * sum(ev_step.ms()) / steps
+    attn_us = 1e3 * sum(ev_attn.ms()) / steps
+    res = {"workload": f"{name}: {B} seqs of {min(lens)}..{max(lens)} cached tokens (seeded "
+                       f"uniform), shuffled 64-token pages, Hq={Hq}, Hkv={Hkv}, D={D}, "
+                       f"top-K={K} + sink + 2 local, bf16",
+           "us_per_step": step_us, "breakdown_us": {"select": step_us - attn_us, "attend": attn_us},
+           "hbm_gbps": nbytes / (step_us * 1e-6) / 1e9}
+    res["roofline"] = {"bound": "hbm", "achieved": res["hbm_gbps"], "peak": PEAK_HBM_GBPS,
+                       "unit": "GB/s", "frac": res["hbm_gbps"] / PEAK_HBM_GBPS,
+                       "algorithmic_bytes": nbytes, "traffic": None}
+    log(f"[bench] decode paged: {json.dumps(res)}")
+    del q, k_pool, v_pool, table, seq_lens, lm, flush
+    return res
+
+
 def cpu_baseline(torch, tensors, name, synth, budget_s=12.0):
     """The float64 oracle on a sample of the prefill workload, extrapolated to tok/s."""
     import numpy as np
@@ -289,6 +348,10 @@ def main():
     if not args.no_decode:
         dec = bench_decode(torch, bsa, synth, args.steps, args.warmup)
         torch.cuda.empty_cache()
+    dec_paged = None
+    if not args.no_decode:
+        dec_paged = bench_decode_paged(torch, bsa, synth, args.steps, args.warmup)
+        torch.cuda.empty_cache()
     hils = None
     if args.hils:
         hils, t = bench_prefill(torch, bsa, synth, "hils_bf16_1m", max(2, args.steps // 4), 1)
@@ -343,6 +406,8 @@ def main():
                          "algorithmic_bytes": dec["algorithmic_bytes"],
                          "traffic": profiled_traffic("decode_bf16_32x128k.md",
                                                      "traffic_bytes_per_step")}}
+    if dec_paged is not None:
+        line["decode_paged"] = dec_paged
     if hils is not None:
         line["hils_1m"] = {"tok_per_s": hils["tok_per_s"], "ms_per_step": hils["ms_per_step"],
                            "attended_tflops_attention_kernel": hils["attended_tflops_kernel"],

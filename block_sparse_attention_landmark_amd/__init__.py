@@ -80,6 +80,14 @@ def load_library():
     lib.bsa_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.bsa_attend_decode.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.bsa_attend_decode.restype = st
+    i32 = ctypes.c_int32
+    lib.bsa_pool_landmarks_paged.argtypes = [P, vp, i32, vp, vp, vp, vp]
+    lib.bsa_pool_landmarks_paged.restype = st
+    lib.bsa_select_topk_paged.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    lib.bsa_select_topk_paged.restype = st
+    lib.bsa_attend_decode_paged.argtypes = [P, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                            ctypes.c_size_t, vp]
+    lib.bsa_attend_decode_paged.restype = st
     lib.bsa_status_string.argtypes = [ctypes.c_int]
     lib.bsa_status_string.restype = ctypes.c_char_p
     lib.bsa_last_error.argtypes = []
@@ -287,3 +295,111 @@ def decode(q, kc, vc, lm, *, topk: int, mode: str = "plain", n_sink: int = 1, n_
                              topk=topk, n_sink=n_sink, n_local=n_local, scale=scale,
                              want_lse=want_lse and mode != "hils")
     return {"out": out, "lse": lse, "idx": idx, "sc": sc}
+
+
+# ---------------------------------------------------------------------------------------------
+# paged (ragged) decode: 64-token pages [n_pages,Hkv,64,D], page_table [B,NB], seq_lens [B]
+# ---------------------------------------------------------------------------------------------
+
+def _paged_shapes(k_pool, page_table, seq_lens):
+    _need(k_pool, "k_pool", ndim=4)
+    _need(page_table, "page_table", dtype=torch.int32, ndim=2)
+    _need(seq_lens, "seq_lens", dtype=torch.int32, ndim=1)
+    n_pages, Hkv, blk, D = k_pool.shape
+    if blk != 64:
+        raise ValueError("k_pool must be [n_pages,Hkv,64,D]")
+    B, NB = page_table.shape
+    if seq_lens.shape != (B,):
+        raise ValueError("seq_lens must be [B] matching page_table [B,NB]")
+    return n_pages, Hkv, D, B, NB
+
+
+def pool_landmarks_paged(k_pool, page_table, seq_lens, out=None):
+    """Landmarks [B,Hkv,NB,D] of a paged cache (blocks past a sequence's end are zero)."""
+    lib = load_library()
+    n_pages, Hkv, D, B, NB = _paged_shapes(k_pool, page_table, seq_lens)
+    if out is None:
+        out = torch.empty((B, Hkv, NB, D), dtype=k_pool.dtype, device=k_pool.device)
+    _need(out, "lm", dtype=k_pool.dtype, ndim=4)
+    p = make_params(B=B, Hq=Hkv, Hkv=Hkv, D=D, seq_q=NB * 64, seq_k=NB * 64, dtype=k_pool.dtype)
+    _check("bsa_pool_landmarks_paged",
+           lib.bsa_pool_landmarks_paged(ctypes.byref(p), _ptr(k_pool), int(n_pages),
+                                        _ptr(page_table), _ptr(seq_lens), _ptr(out),
+                                        _stream(k_pool.device)))
+    return out
+
+
+def select_topk_paged(q, lm, seq_lens, *, topk: int, n_sink: int = 1, n_local: int = 2,
+                      idx=None, sc=None):
+    """Attended sets of a paged decode batch: q [B,Hq,1,D], lm [B,Hkv,NB,D] -> idx, sc [B,Hkv,1,NA]."""
+    lib = load_library()
+    _need(q, "q", ndim=4)
+    _need(lm, "lm", dtype=q.dtype, ndim=4)
+    _need(seq_lens, "seq_lens", dtype=torch.int32, ndim=1)
+    B, Hq, one, D = q.shape
+    Hkv, NB = lm.shape[1], lm.shape[2]
+    if one != 1 or lm.shape != (B, Hkv, NB, D):
+        raise ValueError("q must be [B,Hq,1,D] and lm [B,Hkv,NB,D]")
+    NA = n_sink + n_local + topk
+    if idx is None:
+        idx = torch.empty((B, Hkv, 1, NA), dtype=torch.int32, device=q.device)
+    if sc is None:
+        sc = torch.empty((B, Hkv, 1, NA), dtype=torch.float32, device=q.device)
+    p = make_params(B=B, Hq=Hq, Hkv=Hkv, D=D, seq_q=1, seq_k=NB * 64, dtype=q.dtype, topk=topk,
+                    n_sink=n_sink, n_local=n_local)
+    _check("bsa_select_topk_paged",
+           lib.bsa_select_topk_paged(ctypes.byref(p), _ptr(q), _ptr(lm), _ptr(seq_lens),
+                                     _ptr(idx), _ptr(sc), _stream(q.device)))
+    return idx, sc
+
+
+def attend_decode_paged(q, k_pool, v_pool, page_table, seq_lens, idx, sc=None, lm=None, *,
+                        mode="plain", topk=None, n_sink=1, n_local=2, scale=0.0, want_lse=False,
+                        out=None, lse=None, ws=None):
+    """Decode attention over a paged batch; q [B,Hq,1,D]; returns (out, lse or None)."""
+    lib = load_library()
+    _need(q, "q", ndim=4)
+    n_pages, Hkv, D, B, NB = _paged_shapes(k_pool, page_table, seq_lens)
+    _need(v_pool, "v_pool", dtype=k_pool.dtype, ndim=4)
+    if v_pool.shape != k_pool.shape or k_pool.dtype != q.dtype:
+        raise ValueError("v_pool must match k_pool, and both q's dtype")
+    _need(idx, "idx", dtype=torch.int32, ndim=4)
+    Hq = q.shape[1]
+    NA = idx.shape[-1]
+    if topk is None:
+        topk = NA - n_sink - n_local
+    if q.shape != (B, Hq, 1, D) or idx.shape != (B, Hkv, 1, NA) or NA != n_sink + n_local + topk:
+        raise ValueError("q must be [B,Hq,1,D] and idx [B,Hkv,1,NA] matching the call")
+    if sc is not None:
+        _need(sc, "sc", dtype=torch.float32, ndim=4)
+    if lm is not None:
+        _need(lm, "lm", dtype=q.dtype, ndim=4)
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    p = make_params(B=B, Hq=Hq, Hkv=Hkv, D=D, seq_q=1, seq_k=NB * 64, dtype=q.dtype, topk=topk,
+                    n_sink=n_sink, n_local=n_local, scale=scale, mode=mode)
+    need = decode_workspace_bytes(p)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check("bsa_attend_decode_paged",
+           lib.bsa_attend_decode_paged(ctypes.byref(p), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                       int(n_pages), _ptr(page_table), _ptr(seq_lens), _ptr(lm),
+                                       _ptr(idx), _ptr(sc), _ptr(out), _ptr(lse), _ptr(ws),
+                                       0 if ws is None else ws.numel(), _stream(q.device)))
+    return out, lse
+
+
+def decode_paged(q, k_pool, v_pool, page_table, seq_lens, *, topk: int, mode: str = "plain",
+                 n_sink: int = 1, n_local: int = 2, scale: float = 0.0, want_lse: bool = False,
+                 lm=None):
+    """Pool (unless lm is given), select and attend for one paged decode step."""
+    if lm is None:
+        lm = pool_landmarks_paged(k_pool, page_table, seq_lens)
+    idx, sc = select_topk_paged(q, lm, seq_lens, topk=topk, n_sink=n_sink, n_local=n_local)
+    out, lse = attend_decode_paged(q, k_pool, v_pool, page_table, seq_lens, idx, sc,
+                                   lm if mode == "hils" else None, mode=mode, topk=topk,
+                                   n_sink=n_sink, n_local=n_local, scale=scale,
+                                   want_lse=want_lse and mode != "hils")
+    return {"out": out, "lse": lse, "idx": idx, "sc": sc, "lm": lm}

@@ -37,13 +37,18 @@ inline int decode_blocks_per_wave(int NA, int nsplit) {
 // XOR-swizzled so the fragment and transposed reads are free of bank conflicts.  Each wave keeps
 // an online softmax state; the waves' states are combined in LDS and written as the split's
 // partial state.
-template <int D, int MODE>
+//
+// PAGED: the cache is a pool of 64-token pages [n_pages, Hkv, 64, D]; block j of sequence b is
+// page page_table[b * NB + j] (clamped into the pool) and the sequence holds seq_lens[b] tokens
+// (clamped to 1 .. NB * 64); otherwise kc / vc are [B, Hkv, Tk, D] and every sequence holds Tk.
+template <int D, int MODE, bool PAGED>
 __global__ __launch_bounds__(kDecodeWaves * 64) void attend_decode_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
     const bf16* __restrict__ lm, const int32_t* __restrict__ idx, const float* __restrict__ sc,
     float* __restrict__ part_o, float* __restrict__ part_ml, bf16* __restrict__ out,
-    float* __restrict__ lse, int Hq, int Hkv, int G, int Tk, int NB, int NA, int nsplit, int bpw,
-    float scale_log2) {
+    float* __restrict__ lse, int Hq, int Hkv, int G, int Tk_all, int NB, int NA, int nsplit, int bpw,
+    float scale_log2, const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens,
+    int n_pages) {
   constexpr int C16 = D / 8;                 // 16-byte chunks per row
   constexpr int RPI = 64 / C16;              // rows covered by one 64-lane 16-byte copy
   __shared__ __attribute__((aligned(16))) bf16 Ks[kDecodeWaves][kBlock * D];
@@ -59,6 +64,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void attend_decode_bf16_kernel(
   const int l32 = lane % 32;
   const bool row_ok = l32 < G;
   const int h = g * G + min(l32, G - 1);
+  const int Tk = PAGED ? min(max(seq_lens[b], 1), NB * kBlock) : Tk_all;   // this sequence
   const int c = (Tk - 1) / kBlock;
   // chunk swizzles (physical 16-byte chunk = logical ^ swz(row)): for the V tile, the four rows of
   // a transposed read land on distinct banks; for the K tile, the 16 rows of a fragment read do
@@ -75,7 +81,16 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void attend_decode_bf16_kernel(
       qf[s] = __builtin_bit_cast(bf16x8, raw);
     }
   }
-  const size_t kvbase = (size_t)(b * Hkv + g) * Tk * D;
+  const size_t kvbase = (size_t)(b * Hkv + g) * Tk_all * D;
+  // first element of block j of this (sequence, kv group) in kc / vc
+  auto block_at = [&](int j) -> size_t {
+    if constexpr (PAGED) {
+      const int pg = min(max(page_table[(size_t)b * NB + j], 0), n_pages - 1);
+      return ((size_t)pg * Hkv + g) * kBlock * D;
+    } else {
+      return kvbase + (size_t)j * kBlock * D;
+    }
+  };
   const int32_t* irow = idx + (size_t)(b * Hkv + g) * NA;
   const float* srow = sc + (size_t)(b * Hkv + g) * NA;
   const int nval = count_valid(irow, NA);
@@ -100,23 +115,25 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void attend_decode_bf16_kernel(
   // copy the K (or V) rows of block j into this wave's tile, 1 KB per instruction (rows past
   // the cache end read its last row; their probabilities are zero)
   auto copy_k = [&](int j) {
+    const size_t base = block_at(j);
 #pragma unroll
     for (int n = 0; n < kBlock / RPI; ++n) {
       const int row = n * RPI + lane / C16;
-      const int tok = min(j * kBlock + row, Tk - 1);
+      const int r = min(row, Tk - 1 - j * kBlock);
       __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(kc + kvbase + (size_t)tok * D +
+          (const __attribute__((address_space(1))) void*)(kc + base + (size_t)r * D +
                                                           ((lane % C16) ^ swzk(row)) * 8),
           (__attribute__((address_space(3))) void*)(kt_ + n * RPI * D), 16, 0, 0);
     }
   };
   auto copy_v = [&](int j) {
+    const size_t base = block_at(j);
 #pragma unroll
     for (int n = 0; n < kBlock / RPI; ++n) {
       const int row = n * RPI + lane / C16;
-      const int tok = min(j * kBlock + row, Tk - 1);
+      const int r = min(row, Tk - 1 - j * kBlock);
       __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(vc + kvbase + (size_t)tok * D +
+          (const __attribute__((address_space(1))) void*)(vc + base + (size_t)r * D +
                                                           ((lane % C16) ^ swz(row)) * 8),
           (__attribute__((address_space(3))) void*)(vt + n * RPI * D), 16, 0, 0);
     }
@@ -352,21 +369,22 @@ size_t decode_ws_bytes(const Shape& s) {
   return o + rows * 2 * sizeof(float);
 }
 
-template <int D>
+template <int D, bool PAGED>
 static void launch_decode_bf16_d(const Shape& s, const void* q, const void* kc, const void* vc,
                                  const void* lm, const int32_t* idx, const float* sc, void* out,
-                                 float* lse, void* ws, hipStream_t st) {
+                                 float* lse, void* ws, const Pages* pg, hipStream_t st) {
   const int nsplit = decode_splits(s);
   const size_t rows = (size_t)s.B * s.Hkv * nsplit * s.G;
   float* part_o = (float*)ws;
   float* part_ml = (float*)((char*)ws + ((rows * s.D * sizeof(float) + 255) & ~(size_t)255));
   dim3 grid(nsplit, s.Hkv, s.B);
   const float sl2 = s.scale * kLog2e;
-#define BSA_DEC(MODE)                                                                          \
-  hipLaunchKernelGGL((attend_decode_bf16_kernel<D, MODE>), grid, dim3(kDecodeWaves * 64), 0, st, \
-                     (const bf16*)q, (const bf16*)kc, (const bf16*)vc, (const bf16*)lm, idx,   \
-                     sc, part_o, part_ml, (bf16*)out, lse, s.Hq, s.Hkv, s.G, s.Tk, s.NB, s.NA,  \
-                     nsplit, decode_blocks_per_wave(s.NA, nsplit), sl2)
+#define BSA_DEC(MODE)                                                                           \
+  hipLaunchKernelGGL((attend_decode_bf16_kernel<D, MODE, PAGED>), grid, dim3(kDecodeWaves * 64), \
+                     0, st, (const bf16*)q, (const bf16*)kc, (const bf16*)vc, (const bf16*)lm,  \
+                     idx, sc, part_o, part_ml, (bf16*)out, lse, s.Hq, s.Hkv, s.G, s.Tk, s.NB,   \
+                     s.NA, nsplit, decode_blocks_per_wave(s.NA, nsplit), sl2,                  \
+                     pg ? pg->table : nullptr, pg ? pg->lens : nullptr, pg ? pg->n_pages : 1)
   if (s.mode == 0) BSA_DEC(0);
   else if (s.mode == 1) BSA_DEC(1);
   else BSA_DEC(2);
@@ -378,10 +396,15 @@ static void launch_decode_bf16_d(const Shape& s, const void* q, const void* kc, 
 
 hipError_t launch_attend_decode(const Shape& s, const void* q, const void* kc, const void* vc,
                                 const void* lm, const int32_t* idx, const float* sc, void* out,
-                                float* lse, void* ws, hipStream_t st) {
+                                float* lse, void* ws, hipStream_t st, const Pages* pg) {
   if (s.bf16) {
-    if (s.D == 128) launch_decode_bf16_d<128>(s, q, kc, vc, lm, idx, sc, out, lse, ws, st);
-    else launch_decode_bf16_d<64>(s, q, kc, vc, lm, idx, sc, out, lse, ws, st);
+    if (pg != nullptr) {
+      if (s.D == 128) launch_decode_bf16_d<128, true>(s, q, kc, vc, lm, idx, sc, out, lse, ws, pg, st);
+      else launch_decode_bf16_d<64, true>(s, q, kc, vc, lm, idx, sc, out, lse, ws, pg, st);
+    } else {
+      if (s.D == 128) launch_decode_bf16_d<128, false>(s, q, kc, vc, lm, idx, sc, out, lse, ws, nullptr, st);
+      else launch_decode_bf16_d<64, false>(s, q, kc, vc, lm, idx, sc, out, lse, ws, nullptr, st);
+    }
   } else {
     return launch_attend_f32(s, q, kc, vc, lm, idx, sc, out, lse, st);
   }

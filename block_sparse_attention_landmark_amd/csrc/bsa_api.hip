@@ -112,6 +112,21 @@ bsa_status_t hip_result(hipError_t e, const char* what) {
     if (st_ != BSA_OK) return st_;     \
   } while (0)
 
+// checks shared by the paged (ragged) decode calls
+bsa_status_t check_paged(const bsa_params_t* params, const bsa::Shape& s, int32_t n_pages,
+                         const int32_t* page_table, const int32_t* seq_lens, bool need_table) {
+  if (params->seq_k % 64 != 0)
+    return fail(BSA_ERR_SHAPE, "paged calls need seq_k (the capacity) to be a multiple of 64 (got %d)",
+                params->seq_k);
+  if (need_table) {
+    if (n_pages < 1) return fail(BSA_ERR_SHAPE, "n_pages must be >= 1 (got %d)", n_pages);
+    BSA_TRY(check_ptr(page_table, "page_table"));
+  }
+  BSA_TRY(check_ptr(seq_lens, "seq_lens"));
+  (void)s;
+  return BSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -226,6 +241,73 @@ bsa_status_t bsa_attend_decode(const bsa_params_t* params, const void* q, const 
   return hip_result(bsa::launch_attend_decode(s, q, kc, vc, lm, idx, sc, out, lse, ws,
                                               (hipStream_t)stream),
                     "attend_decode");
+}
+
+// ---- paged (ragged) decode ----
+
+bsa_status_t bsa_pool_landmarks_paged(const bsa_params_t* params, const void* k_pool,
+                                      int32_t n_pages, const int32_t* page_table,
+                                      const int32_t* seq_lens, void* lm, void* stream) {
+  bsa::Shape s;
+  BSA_TRY(make_shape(params, kPool, &s));
+  BSA_TRY(check_paged(params, s, n_pages, page_table, seq_lens, true));
+  BSA_TRY(check_ptr(k_pool, "k_pool"));
+  BSA_TRY(check_ptr(lm, "lm"));
+  const bsa::Pages pg{page_table, seq_lens, n_pages};
+  return hip_result(bsa::launch_pool_landmarks_paged(s, k_pool, pg, lm, (hipStream_t)stream),
+                    "pool_landmarks_paged");
+}
+
+bsa_status_t bsa_select_topk_paged(const bsa_params_t* params, const void* q, const void* lm,
+                                   const int32_t* seq_lens, int32_t* idx, float* sc,
+                                   void* stream) {
+  bsa::Shape s;
+  BSA_TRY(make_shape(params, kDecode, &s));
+  BSA_TRY(check_paged(params, s, 1, nullptr, seq_lens, false));
+  if (!s.bf16) return fail(BSA_ERR_UNSUPPORTED, "paged selection is implemented for bf16 only");
+  if (!bsa::decode_select_fused(s))
+    return fail(BSA_ERR_UNSUPPORTED, "paged selection supports at most 16384 blocks per sequence");
+  BSA_TRY(check_ptr(q, "q"));
+  BSA_TRY(check_ptr(lm, "lm"));
+  BSA_TRY(check_ptr(idx, "idx"));
+  BSA_TRY(check_ptr(sc, "sc"));
+  const bsa::Pages pg{nullptr, seq_lens, 1};
+  return hip_result(bsa::launch_decode_select(s, q, lm, idx, sc, (hipStream_t)stream, &pg),
+                    "select_topk_paged");
+}
+
+bsa_status_t bsa_attend_decode_paged(const bsa_params_t* params, const void* q,
+                                     const void* k_pool, const void* v_pool, int32_t n_pages,
+                                     const int32_t* page_table, const int32_t* seq_lens,
+                                     const void* lm, const int32_t* idx, const float* sc,
+                                     void* out, float* lse, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  bsa::Shape s;
+  BSA_TRY(make_shape(params, kDecode, &s));
+  BSA_TRY(check_paged(params, s, n_pages, page_table, seq_lens, true));
+  if (!s.bf16) return fail(BSA_ERR_UNSUPPORTED, "paged decode is implemented for bf16 only");
+  BSA_TRY(check_ptr(q, "q"));
+  BSA_TRY(check_ptr(k_pool, "k_pool"));
+  BSA_TRY(check_ptr(v_pool, "v_pool"));
+  BSA_TRY(check_ptr(idx, "idx"));
+  BSA_TRY(check_ptr(out, "out"));
+  if (s.mode == BSA_MODE_SAS) BSA_TRY(check_ptr(sc, "sc"));
+  if (s.mode == BSA_MODE_HILS) {
+    BSA_TRY(check_ptr(lm, "lm"));
+    if (lse != nullptr) return fail(BSA_ERR_UNSUPPORTED, "lse is not defined for HILS; pass NULL");
+  }
+  if (lse != nullptr) BSA_TRY(check_ptr(lse, "lse"));
+  const size_t need = bsa::decode_ws_bytes(s);
+  if (need > 0) {
+    if (ws == nullptr || ws_bytes < need)
+      return fail(BSA_ERR_WORKSPACE, "decode workspace needs %zu bytes (got %zu%s)", need,
+                  ws_bytes, ws == nullptr ? ", NULL pointer" : "");
+    if (((uintptr_t)ws & 255u) != 0) return fail(BSA_ERR_ALIGN, "ws is not 256-byte aligned");
+  }
+  const bsa::Pages pg{page_table, seq_lens, n_pages};
+  return hip_result(bsa::launch_attend_decode(s, q, k_pool, v_pool, lm, idx, sc, out, lse, ws,
+                                              (hipStream_t)stream, &pg),
+                    "attend_decode_paged");
 }
 
 }  // extern "C"

@@ -20,6 +20,14 @@ struct Shape {
   float scale;      // softmax scale (already defaulted to 1/sqrt(D))
 };
 
+// Paged decode cache: block j of sequence b is page table[b * NB + j] of a pool of n_pages
+// 64-token pages [n_pages, Hkv, 64, D]; sequence b holds lens[b] tokens (device pointers).
+struct Pages {
+  const int32_t* table;
+  const int32_t* lens;
+  int n_pages;
+};
+
 // Block index of selection row r (prefill: r; decode: the query token's block).
 inline int row_block(const Shape& s, int r) { return s.decode ? s.c_dec : r; }
 
@@ -40,7 +48,9 @@ hipError_t launch_topk(const Shape& s, const float* scores, int32_t* idx, float*
 // decode with bf16 landmarks: selector vector, scores and top-K in one kernel
 bool decode_select_fused(const Shape& s);
 hipError_t launch_decode_select(const Shape& s, const void* q, const void* lm, int32_t* idx,
-                                float* sc, hipStream_t st);
+                                float* sc, hipStream_t st, const Pages* pg = nullptr);
+hipError_t launch_pool_landmarks_paged(const Shape& s, const void* k_pool, const Pages& pg,
+                                       void* lm, hipStream_t st);
 hipError_t launch_attend_prefill(const Shape& s, const void* q, const void* k, const void* v,
                                  const void* lm, const int32_t* idx, const float* sc, void* out,
                                  float* lse, hipStream_t st);
@@ -50,6 +60,6 @@ hipError_t launch_attend_f32(const Shape& s, const void* q, const void* k, const
                              float* lse, hipStream_t st);
 hipError_t launch_attend_decode(const Shape& s, const void* q, const void* kc, const void* vc,
                                 const void* lm, const int32_t* idx, const float* sc, void* out,
-                                float* lse, void* ws, hipStream_t st);
+                                float* lse, void* ws, hipStream_t st, const Pages* pg = nullptr);
 
 }  // namespace bsa

@@ -67,6 +67,70 @@ __global__ __launch_bounds__(256) void pool_rows_kernel(const T* __restrict__ sr
   }
 }
 
+// Landmarks of a paged cache: block j of sequence b (page table[b * NB + j] of the pool
+// [n_pages, Hkv, 64, D]) averages its first min(64, len_b - 64 j) tokens, len_b = lens[b]
+// clamped to 1 .. NB * 64; blocks past the end of a sequence are written as zeros.  Same float64
+// accumulation and single rounding as above.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void pool_paged_kernel(const T* __restrict__ pool,
+                                                         T* __restrict__ dst,
+                                                         const int32_t* __restrict__ table,
+                                                         const int32_t* __restrict__ lens, int Hkv,
+                                                         int NB, int n_pages) {
+  constexpr int EPC = 16 / sizeof(T);
+  constexpr int NC = D / EPC;
+  constexpr int RG = 256 / NC;
+  __shared__ double red[RG][D];
+  const int j = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int chunk = tid % NC, rg = tid / NC;
+  const int len = min(max(lens[b], 1), NB * kBlock);
+  const int ntok = min(kBlock, len - j * kBlock);      // <= 0: block past the end
+  T* o = dst + ((size_t)(b * Hkv + g) * NB + j) * D;
+  if (ntok <= 0) {
+    for (int d = tid; d < D; d += 256) o[d] = (T)0.0f;
+    return;
+  }
+  const int pg = min(max(table[(size_t)b * NB + j], 0), n_pages - 1);
+  const T* blk = pool + ((size_t)pg * Hkv + g) * kBlock * D;
+  double acc[EPC];
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) acc[e] = 0.0;
+  for (int r = rg; r < ntok; r += RG) {
+    u32x4 raw = *reinterpret_cast<const u32x4*>(blk + (size_t)r * D + chunk * EPC);
+    const T* vals = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[e] += (double)(float)vals[e];
+  }
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) red[rg][chunk * EPC + e] = acc[e];
+  __syncthreads();
+  if (tid < D) {
+    double sum = 0.0;
+    for (int i = 0; i < RG; ++i) sum += red[i][tid];
+    const double mean = sum / (double)ntok;
+    if constexpr (sizeof(T) == 2) o[tid] = f64_to_bf16_rne(mean);
+    else o[tid] = (float)mean;
+  }
+}
+
+hipError_t launch_pool_landmarks_paged(const Shape& s, const void* k_pool, const Pages& pg,
+                                       void* lm, hipStream_t st) {
+  dim3 grid(s.NB, s.Hkv, s.B);
+#define BSA_PPOOL(T_, D_)                                                                   \
+  hipLaunchKernelGGL((pool_paged_kernel<T_, D_>), grid, dim3(256), 0, st, (const T_*)k_pool, \
+                     (T_*)lm, pg.table, pg.lens, s.Hkv, s.NB, pg.n_pages)
+  if (s.bf16) {
+    if (s.D == 128) BSA_PPOOL(bf16, 128);
+    else BSA_PPOOL(bf16, 64);
+  } else {
+    if (s.D == 128) BSA_PPOOL(float, 128);
+    else BSA_PPOOL(float, 64);
+  }
+#undef BSA_PPOOL
+  return hipGetLastError();
+}
+
 template <typename T, typename OUT>
 static hipError_t launch_pool_t(const void* src, void* dst, int B, int heads_src, int groups,
                                 int heads_per_group, int T_len, int D, hipStream_t st) {

@@ -322,11 +322,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
 constexpr int kDecodeSelThreads = 1024;
 constexpr int kDecodeSelMaxBlocks = 16384;    // scores kept in LDS (64 KB)
 
-template <int D>
+// (PAGED: sequence b holds seq_lens[b] tokens, clamped to 1 .. NB * 64, and its query is the
+// last of them; otherwise every sequence's query block is c_all.)
+template <int D, bool PAGED>
 __global__ __launch_bounds__(kDecodeSelThreads) void decode_select_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ lm, int32_t* __restrict__ idx,
-    float* __restrict__ sc, int Hq, int Hkv, int G, int NB, int c, int topk, int n_sink,
-    int n_local, int NA) {
+    float* __restrict__ sc, int Hq, int Hkv, int G, int NB, int c_all, int topk, int n_sink,
+    int n_local, int NA, const int32_t* __restrict__ seq_lens) {
   constexpr int LPR = D / 8;                  // lanes per landmark row (8 elements each)
   constexpr int RPI = kWave / LPR;            // rows per wave instruction
   constexpr int NW = kDecodeSelThreads / kWave;
@@ -337,6 +339,7 @@ __global__ __launch_bounds__(kDecodeSelThreads) void decode_select_bf16_kernel(
   __shared__ int sh[2];
   const int bg = blockIdx.x;
   const int b = bg / Hkv, g = bg % Hkv;
+  const int c = PAGED ? (min(max(seq_lens[b], 1), NB * kBlock) - 1) / kBlock : c_all;
   const int tid = threadIdx.x;
   if (tid < D) {
     double acc = 0.0;
@@ -385,16 +388,20 @@ bool decode_select_fused(const Shape& s) {
 }
 
 hipError_t launch_decode_select(const Shape& s, const void* q, const void* lm, int32_t* idx,
-                                float* sc, hipStream_t st) {
+                                float* sc, hipStream_t st, const Pages* pg) {
   dim3 grid(s.B * s.Hkv);
-  if (s.D == 128)
-    hipLaunchKernelGGL(decode_select_bf16_kernel<128>, grid, dim3(kDecodeSelThreads), 0, st,
-                       (const bf16*)q, (const bf16*)lm, idx, sc, s.Hq, s.Hkv, s.G, s.NB, s.c_dec,
-                       s.topk, s.n_sink, s.n_local, s.NA);
-  else
-    hipLaunchKernelGGL(decode_select_bf16_kernel<64>, grid, dim3(kDecodeSelThreads), 0, st,
-                       (const bf16*)q, (const bf16*)lm, idx, sc, s.Hq, s.Hkv, s.G, s.NB, s.c_dec,
-                       s.topk, s.n_sink, s.n_local, s.NA);
+#define BSA_DSEL(D_, P_)                                                                        \
+  hipLaunchKernelGGL((decode_select_bf16_kernel<D_, P_>), grid, dim3(kDecodeSelThreads), 0, st, \
+                     (const bf16*)q, (const bf16*)lm, idx, sc, s.Hq, s.Hkv, s.G, s.NB, s.c_dec, \
+                     s.topk, s.n_sink, s.n_local, s.NA, pg ? pg->lens : nullptr)
+  if (s.D == 128) {
+    if (pg) BSA_DSEL(128, true);
+    else BSA_DSEL(128, false);
+  } else {
+    if (pg) BSA_DSEL(64, true);
+    else BSA_DSEL(64, false);
+  }
+#undef BSA_DSEL
   return hipGetLastError();
 }
 

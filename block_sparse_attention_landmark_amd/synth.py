@@ -41,6 +41,11 @@ WORKLOADS = {
                                 n_centres=256, n_aim=16),
     "hils_bf16_1m": dict(kind="prefill", B=1, Hq=32, Hkv=8, D=128, T=1048576, dtype="bf16",
                          topk=32, mode="hils", data="clustered", n_centres=4096, n_aim=16),
+    # ragged serving batch: 32 sequences of 16K..128K tokens in shuffled 64-token pages
+    "decode_paged_bf16_32x16k_128k": dict(kind="decode_paged", B=32, Hq=64, Hkv=8, D=128,
+                                          T_min=16384, T=131072, dtype="bf16", topk=64,
+                                          mode="plain", data="clustered", n_centres=256,
+                                          n_aim=16),
 }
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -142,3 +147,41 @@ def make_decode(B, Hq, Hkv, Tk, D, dtype="bf16", data="clustered", seed=0, devic
     cent = C[bidx, gidx, z[bidx, gidx, target]]                                # [B,Hq,D]
     q = (3.0 * cent + _randn((B, Hq, D), gq, device)).to(tdt)
     return q, kc, vc
+
+
+def make_paged_decode(lens, Hq, Hkv, D, dtype="bf16", data="clustered", seed=0, device="cpu",
+                      n_centres=256, n_aim=16, spare_pages=16, block=BLOCK):
+    """A ragged decode batch in a paged cache.
+
+    Sequence b (len lens[b]) is make_decode's cache for one sequence (seed + b); its blocks are
+    scattered over a pool of 64-token pages [n_pages,Hkv,64,D] in a seeded random order, with
+    `spare_pages` unused pages.  Returns q [B,Hq,D], k_pool, v_pool, page_table [B,NB] int32
+    (NB = the longest sequence's blocks; unused entries point at page 0) and seq_lens [B] int32.
+    """
+    B = len(lens)
+    nblk = [(int(L) + block - 1) // block for L in lens]
+    NB = max(nblk)
+    n_pages = sum(nblk) + spare_pages
+    tdt = TORCH_DTYPE[dtype]
+    k_pool = torch.zeros((n_pages, Hkv, block, D), dtype=tdt, device=device)
+    v_pool = torch.zeros((n_pages, Hkv, block, D), dtype=tdt, device=device)
+    order = torch.randperm(n_pages, generator=_gen("cpu", seed, 9)).to(device)
+    table = torch.zeros((B, NB), dtype=torch.int32, device=device)
+    qs = []
+    nxt = 0
+    for b, L in enumerate(lens):
+        L = int(L)
+        q, kc, vc = make_decode(1, Hq, Hkv, L, D, dtype, data, seed=seed + b, device=device,
+                                n_centres=n_centres, n_aim=n_aim, block=block)
+        qs.append(q)
+        pages = order[nxt:nxt + nblk[b]]
+        nxt += nblk[b]
+        pad = nblk[b] * block - L
+        for src, pool in ((kc, k_pool), (vc, v_pool)):
+            t = torch.nn.functional.pad(src[0], (0, 0, 0, pad))            # [Hkv, nblk*64, D]
+            pool[pages] = t.view(Hkv, nblk[b], block, D).permute(1, 0, 2, 3)
+        table[b, : nblk[b]] = pages.to(torch.int32)
+        del kc, vc
+    seq_lens = torch.tensor([int(L) for L in lens], dtype=torch.int32, device=device)
+    return torch.cat(qs, 0), k_pool, v_pool, table, seq_lens
+

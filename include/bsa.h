@@ -142,6 +142,49 @@ bsa_status_t bsa_attend_decode(const bsa_params_t* params, const void* q, const 
                                const float* sc, void* out, float* lse, void* ws,
                                size_t ws_bytes, void* stream);
 
+/*
+ * Paged, ragged decode: the serving layout, where sequences of different lengths share one pool
+ * of 64-token pages (one page = one block, so a block never straddles two pages).
+ *   k_pool, v_pool [n_pages, Hkv, 64, D]: page p of kv head g is the contiguous 64 x D tile at
+ *       (p * Hkv + g) * 64 * D;
+ *   page_table [B, NB] int32 (NB = params->seq_k / 64, seq_k a multiple of 64: the capacity of
+ *       a sequence): logical block j of sequence b is page page_table[b * NB + j];
+ *   seq_lens [B] int32: sequence b holds seq_lens[b] tokens (1 <= seq_lens[b] <= seq_k), its
+ *       query is the token seq_lens[b] - 1, and its K / V include that token.
+ * Per sequence, every rule of the contiguous calls holds with Tk = seq_lens[b] (landmark means,
+ * candidates, sink / local window, gates, HiLS merge).  Page indices and lengths are device
+ * data and are not checked by the host: out-of-range values are clamped into range (results
+ * then unspecified, but nothing outside the pools, the table or the outputs is accessed).
+ * params: batch = B, seq_q = 1, seq_k = NB * 64; the other fields as for the contiguous calls.
+ *
+ * Landmarks of the paged cache: lm [B, Hkv, NB, D], block j of sequence b the mean of its
+ * min(64, seq_lens[b] - 64 j) tokens (float64 accumulation, one rounding); blocks past the end
+ * of a sequence are written as zeros.  float32 and bf16.
+ */
+bsa_status_t bsa_pool_landmarks_paged(const bsa_params_t* params, const void* k_pool,
+                                      int32_t n_pages, const int32_t* page_table,
+                                      const int32_t* seq_lens, void* lm, void* stream);
+
+/*
+ * Selection for a paged batch: as bsa_select_topk for a decode step, sequence b's query block
+ * being (seq_lens[b] - 1) / 64.  q [B,Hq,1,D], lm from bsa_pool_landmarks_paged, idx / sc
+ * [B,Hkv,1,NA] outputs.  bf16 only, NB <= 16384; needs no workspace.
+ */
+bsa_status_t bsa_select_topk_paged(const bsa_params_t* params, const void* q, const void* lm,
+                                   const int32_t* seq_lens, int32_t* idx, float* sc,
+                                   void* stream);
+
+/*
+ * Decode attention over a paged batch: as bsa_attend_decode with the cache read through the
+ * page table; ws of bsa_decode_workspace_bytes(params) bytes.  bf16 only.
+ */
+bsa_status_t bsa_attend_decode_paged(const bsa_params_t* params, const void* q,
+                                     const void* k_pool, const void* v_pool, int32_t n_pages,
+                                     const int32_t* page_table, const int32_t* seq_lens,
+                                     const void* lm, const int32_t* idx, const float* sc,
+                                     void* out, float* lse, void* ws, size_t ws_bytes,
+                                     void* stream);
+
 /* Static description of a status code. */
 const char* bsa_status_string(int status);
 /* Detail of the last failed call on this thread ("" if none). */

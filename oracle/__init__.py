@@ -37,4 +37,7 @@ from .bsa_oracle import (  # noqa: F401
     prefill,
     prefill_rows,
     decode,
+    n_blocks,
+    gather_pages,
+    decode_paged,
 )

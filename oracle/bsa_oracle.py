@@ -28,6 +28,10 @@ What is computed, step by step, in the pages' order:
 7. HiLS        -- each query attends to each selected chunk on its own, then the chunk outputs
                   are merged with weights equal to the chunks' retrieval scores (HiLS page,
                   summary paragraph 2); the retrieval score is softmax_j(q . L_j / sqrt(D)).
+8. paged decode -- the decode step of a ragged batch whose cache lives in 64-token pages: each
+                  sequence is the contiguous decode step of its own tokens, read through its
+                  page table (the serving layout; the pages say nothing of storage, so the
+                  method is unchanged by it).
 
 Readings taken where the pages are silent (each is listed in the design notes):
 * the selector vector is kept in float64 here (float32 on the device), never rounded to bf16;
@@ -38,7 +42,8 @@ Readings taken where the pages are silent (each is listed in the design notes):
   is 0; every other attended block (sink, local, top-K) is gated;
 * HiLS retrieval scores use each token's own query of its own head, scaled by 1/sqrt(D),
   softmax-normalised over all attended chunks, with the current chunk's full-block landmark;
-* a partial last block (T not a multiple of 64) pools over the tokens present.
+* a partial last block (T not a multiple of 64) pools over the tokens present;
+* paged decode: a page holds one 64-token block of every kv head, [n_pages, Hkv, 64, D].
 """
 
 from __future__ import annotations
@@ -413,3 +418,48 @@ def decode(q, kc, vc, lm, *, topk: int, mode: str, block: int = BLOCK, n_sink: i
                     o, l_ = attend_rows(qr, tpos, kc[b, g], vc[b, g], A, gates, sc_, block)
                     out[b, h], lse[b, h] = o[0], l_[0]
     return {"idx": out_idx, "sc": out_sc, "out": out, "lse": lse, "qbar": qbar}
+
+
+# ---------------------------------------------------------------------------------------------
+# paged, ragged decode (the serving layout of the decode step)
+# ---------------------------------------------------------------------------------------------
+# Readings: a page holds one 64-token block of every kv head, pool [n_pages, Hkv, 64, D]; block j
+# of sequence b is page page_table[b, j]; sequence b holds seq_lens[b] tokens.  The method is
+# unchanged by the storage: each sequence is the contiguous decode step of its own first
+# seq_lens[b] tokens (LSA page, first section, paragraph 4 and "The index stops scanning the
+# whole context", paragraph 3: the cache is pooled and scanned per sequence; the pages only say
+# where its blocks live).
+
+def gather_pages(pool: np.ndarray, table_row, n_tokens: int, block: int = BLOCK) -> np.ndarray:
+    """The first n_tokens of one sequence's cache read through its page table: [Hkv, n_tokens, D]."""
+    tiles = [pool[int(table_row[j])] for j in range(n_blocks(n_tokens, block))]
+    return np.concatenate(tiles, axis=1)[:, :n_tokens]
+
+
+def decode_paged(q, k_pool, v_pool, page_table, seq_lens, *, topk: int, mode: str, dtype: str,
+                 block: int = BLOCK, n_sink: int = 1, n_local: int = 2, scale=None):
+    """Paged decode step: sequence b is `decode` on its gathered cache of seq_lens[b] tokens.
+
+    q [B,Hq,D]; k_pool/v_pool [n_pages,Hkv,64,D]; page_table [B,NB]; seq_lens [B].
+    Returns out [B,Hq,D], lse [B,Hq], idx/sc [B,Hkv,NA] and lm [B,Hkv,NB,D] (the landmarks of
+    each sequence's blocks, zeros past its end).
+    """
+    B, Hq, D = q.shape
+    Hkv = k_pool.shape[1]
+    NB = page_table.shape[1]
+    NA = n_sink + n_local + topk
+    out = np.full((B, Hq, D), np.nan)
+    lse = np.full((B, Hq), np.nan)
+    idx = np.full((B, Hkv, NA), -1, dtype=np.int64)
+    sc = np.full((B, Hkv, NA), np.nan)
+    lm = np.zeros((B, Hkv, NB, D))
+    for b in range(B):
+        n = int(seq_lens[b])
+        kc = gather_pages(k_pool, page_table[b], n, block)[None]
+        vc = gather_pages(v_pool, page_table[b], n, block)[None]
+        lm_b = landmarks(kc, dtype, block)
+        r = decode(q[b:b + 1], kc, vc, lm_b, topk=topk, mode=mode, block=block, n_sink=n_sink,
+                   n_local=n_local, scale=scale)
+        out[b], lse[b], idx[b], sc[b] = r["out"][0], r["lse"][0], r["idx"][0], r["sc"][0]
+        lm[b, :, : lm_b.shape[2]] = lm_b[0]
+    return {"out": out, "lse": lse, "idx": idx, "sc": sc, "lm": lm}

@@ -486,3 +486,74 @@ def test_decode_equals_prefill_rows_when_query_is_last(mode):
     qbar[0, 0, 5] = d["qbar"][0, 0]
     p = O.prefill_rows(q, k, v, [(0, 0, 5)], topk=2, mode=mode, dtype="bf16", idx=idx, lm=lm, qbar=qbar)
     np.testing.assert_allclose(p[(0, 0, 5)]["out"][:, -1], d["out"][0], atol=1e-13)
+
+
+# ---------------------------------------------------------------------------------------
+# paged, ragged decode
+# ---------------------------------------------------------------------------------------
+
+def _paged_layout(r, caches, extra_pages=3, extra_blocks=1):
+    """Scatter per-sequence caches [Hkv, L_b, D] into a shuffled page pool padded with garbage;
+    returns pool [n_pages, Hkv, 64, D] and page_table [B, NB]."""
+    Hkv, D = caches[0].shape[0], caches[0].shape[2]
+    nblk = [O.n_blocks(c.shape[1]) for c in caches]
+    NB = max(nblk) + extra_blocks
+    n_pages = sum(nblk) + extra_pages
+    pool = 1e3 * r.standard_normal((n_pages, Hkv, 64, D))     # garbage everywhere first
+    perm = r.permutation(n_pages)
+    table = np.array(r.integers(0, n_pages, size=(len(caches), NB)))
+    nxt = 0
+    for b, c in enumerate(caches):
+        for j in range(nblk[b]):
+            pg = int(perm[nxt]); nxt += 1
+            tok = c[:, 64 * j: 64 * (j + 1)]
+            pool[pg, :, : tok.shape[1]] = tok
+            table[b, j] = pg
+    return pool, table
+
+
+def test_paged_decode_dense_limit_is_sdpa():
+    """With K >= every candidate, each sequence of a paged ragged batch attends to all of its
+    own tokens and nothing else: torch SDPA (float64) over the contiguous cache cut at its
+    length, whatever the page order and whatever sits in the unused pages and page tails."""
+    r = _rng(30)
+    Hq, Hkv, D = 4, 2, 8
+    lens = [1, 63, 64, 65, 64 * 5 + 9]
+    ks = [O.round_to_dtype(r.standard_normal((Hkv, L, D)), "bf16") for L in lens]
+    vs = [r.standard_normal((Hkv, L, D)) for L in lens]
+    q = r.standard_normal((len(lens), Hq, D))
+    k_pool, table = _paged_layout(r, ks)
+    v_pool = np.zeros_like(k_pool)
+    for b, v in enumerate(vs):
+        for j in range(O.n_blocks(v.shape[1])):
+            tok = v[:, 64 * j: 64 * (j + 1)]
+            v_pool[table[b, j], :, : tok.shape[1]] = tok
+    d = O.decode_paged(q, k_pool, v_pool, table, np.array(lens), topk=100, mode="plain", dtype="bf16")
+    for b, L in enumerate(lens):
+        ref = _sdpa(q[b][:, None, :], np.repeat(ks[b], 2, axis=0), np.repeat(vs[b], 2, axis=0))[:, 0]
+        np.testing.assert_allclose(d["out"][b], ref, atol=1e-12)
+
+
+def test_paged_landmarks_and_selection_per_sequence():
+    """Landmarks of a paged sequence are the means of its own tokens (a partial last block
+    averages the tokens present, blocks past the end are zero), and its attended set is the
+    brute-force selection over those landmarks with its own current block."""
+    r = _rng(31)
+    Hq, Hkv, D = 2, 1, 6
+    lens = [64 * 7 + 20, 130]
+    ks = [O.round_to_dtype(r.standard_normal((Hkv, L, D)), "bf16") for L in lens]
+    q = r.standard_normal((len(lens), Hq, D))
+    k_pool, table = _paged_layout(r, ks, extra_blocks=2)
+    d = O.decode_paged(q, k_pool, k_pool, table, np.array(lens), topk=2, mode="plain", dtype="bf16")
+    for b, L in enumerate(lens):
+        nb = O.n_blocks(L)
+        for j in range(table.shape[1]):
+            if j < nb:
+                mean = ks[b][0, 64 * j: min(64 * (j + 1), L)].mean(axis=0)
+                want = torch.from_numpy(mean).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+                np.testing.assert_array_equal(d["lm"][b, 0, j], want)
+            else:
+                assert not d["lm"][b, 0, j].any()
+        qs = q[b, 0] + q[b, 1]
+        s = [float(qs @ d["lm"][b, 0, j]) for j in range(nb)]
+        assert [j for j in d["idx"][b, 0] if j >= 0] == _brute_select(s, nb - 1, 2, 1, 2)

@@ -188,6 +188,94 @@ def test_decode_small(case, mode):
                         n_local=2, tag=f"{name}/{mode}")
 
 
+# ---------------------------------------------------------------------------------------------
+# paged, ragged decode: each sequence against the oracle on its own contiguous cache
+# ---------------------------------------------------------------------------------------------
+
+PAGED_DECODE = [
+    # id,           Hq, Hkv, D,   lens,                              topk, data
+    ("ragged_g4",   8,  2,   128, [1, 63, 64, 65, 64 * 20 + 7],      4,    "clustered"),
+    ("ragged_d64",  16, 2,   64,  [640, 130, 64 * 33],               8,    "iid"),
+    ("ragged_g32",  32, 1,   128, [5, 64 * 10 + 3],                  3,    "clustered"),
+]
+
+
+def _paged_batch(Hq, Hkv, D, lens, data, seed):
+    """Per-sequence caches (synthetic recipe) scattered into a shuffled page pool whose unused
+    pages and page tails hold large values; returns q, pool, table, lens and the caches."""
+    rng = np.random.default_rng(seed)
+    qs, kcs, vcs = [], [], []
+    for b, L in enumerate(lens):
+        q, kc, vc = synth.make_decode(1, Hq, Hkv, L, D, "bf16", data, seed=seed + 17 * b,
+                                      device="cuda", n_centres=16, n_aim=4)
+        qs.append(q), kcs.append(kc[0]), vcs.append(vc[0])
+    nblk = [(L + 63) // 64 for L in lens]
+    NB = max(nblk) + 2
+    n_pages = sum(nblk) + 5
+    k_pool = (30.0 * torch.randn((n_pages, Hkv, 64, D), device="cuda")).to(torch.bfloat16)
+    v_pool = (30.0 * torch.randn((n_pages, Hkv, 64, D), device="cuda")).to(torch.bfloat16)
+    perm = rng.permutation(n_pages)
+    table = torch.from_numpy(rng.integers(0, n_pages, size=(len(lens), NB)).astype(np.int32))
+    nxt = 0
+    for b, L in enumerate(lens):
+        for j in range(nblk[b]):
+            pg = int(perm[nxt]); nxt += 1
+            n = min(64, L - 64 * j)
+            k_pool[pg, :, :n] = kcs[b][:, 64 * j: 64 * j + n]
+            v_pool[pg, :, :n] = vcs[b][:, 64 * j: 64 * j + n]
+            table[b, j] = pg
+    q = torch.cat(qs, 0)[:, :, None, :].contiguous()
+    seq_lens = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    return q, k_pool, v_pool, table.cuda(), seq_lens, kcs, vcs
+
+
+@pytest.mark.parametrize("mode", ["plain", "sas", "hils"])
+@pytest.mark.parametrize("case", PAGED_DECODE, ids=[c[0] for c in PAGED_DECODE])
+def test_decode_paged(case, mode):
+    name, Hq, Hkv, D, lens, topk, data = case
+    _print(f"decode paged {name} {mode}")
+    q, k_pool, v_pool, table, seq_lens, kcs, vcs = _paged_batch(Hq, Hkv, D, lens, data, seed=7)
+    res = bsa.decode_paged(q, k_pool, v_pool, table, seq_lens, topk=topk, mode=mode,
+                           want_lse=(mode != "hils"))
+    torch.cuda.synchronize()
+    NB = table.shape[1]
+    for b, L in enumerate(lens):
+        nb = (L + 63) // 64
+        assert not res["lm"][b, :, nb:].float().abs().sum().item(), "landmarks past the end"
+        one = {"idx": res["idx"][b:b + 1], "out": res["out"][b:b + 1],
+               "lse": None if res["lse"] is None else res["lse"][b:b + 1]}
+        _check_decode_pairs(q[b:b + 1], kcs[b][None], vcs[b][None], one,
+                            res["lm"][b:b + 1, :, :nb], [(0, g) for g in range(Hkv)], mode=mode,
+                            dtype="bf16", topk=topk, n_sink=1, n_local=2,
+                            tag=f"paged {name}/{mode} seq{b} (len {L}, NB {NB})")
+
+
+def test_decode_paged_identity_pages_match_contiguous():
+    """Identity page tables and equal lengths: the paged calls give the contiguous calls'
+    results bit for bit (same kernels, same arithmetic)."""
+    B, Hq, Hkv, Tk, D = 3, 8, 2, 64 * 12, 128
+    q, kc, vc = synth.make_decode(B, Hq, Hkv, Tk, D, "bf16", "clustered", seed=4, device="cuda",
+                                  n_centres=16, n_aim=4)
+    q4 = q[:, :, None, :].contiguous()
+    nb = Tk // 64
+    # pool page b*nb + j holds block j of sequence b for every kv head
+    k_pool = kc.view(B, Hkv, nb, 64, D).permute(0, 2, 1, 3, 4).reshape(B * nb, Hkv, 64, D).contiguous()
+    v_pool = vc.view(B, Hkv, nb, 64, D).permute(0, 2, 1, 3, 4).reshape(B * nb, Hkv, 64, D).contiguous()
+    table = torch.arange(B * nb, dtype=torch.int32, device="cuda").view(B, nb)
+    seq_lens = torch.full((B,), Tk, dtype=torch.int32, device="cuda")
+    for mode in ["plain", "sas", "hils"]:
+        lm = bsa.pool_landmarks(kc)
+        ref = bsa.decode(q4, kc, vc, lm, topk=5, mode=mode, want_lse=(mode != "hils"))
+        got = bsa.decode_paged(q4, k_pool, v_pool, table, seq_lens, topk=5, mode=mode,
+                               want_lse=(mode != "hils"))
+        torch.cuda.synchronize()
+        assert torch.equal(got["lm"].view(torch.int16), lm.view(torch.int16))
+        assert torch.equal(got["idx"], ref["idx"]) and torch.equal(got["sc"], ref["sc"])
+        assert torch.equal(got["out"].view(torch.int16), ref["out"].view(torch.int16))
+        if mode != "hils":
+            assert torch.equal(got["lse"], ref["lse"])
+
+
 def test_output_buffers_fully_written_and_deterministic():
     """Outputs pre-filled with NaN come back finite everywhere; two runs agree bit for bit."""
     q, k, v = synth.make_prefill(1, 4, 1, 64 * 9 + 11, 128, "bf16", "clustered", seed=9,
