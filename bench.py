@@ -270,7 +270,9 @@ def bench_decode_paged(torch, bsa, synth, steps, warmup):
            "hbm_gbps": nbytes / (step_us * 1e-6) / 1e9}
     res["roofline"] = {"bound": "hbm", "achieved": res["hbm_gbps"], "peak": PEAK_HBM_GBPS,
                        "unit": "GB/s", "frac": res["hbm_gbps"] / PEAK_HBM_GBPS,
-                       "algorithmic_bytes": nbytes, "traffic": None}
+                       "algorithmic_bytes": nbytes,
+                       "traffic": profiled_traffic("decode_paged_bf16_32x16k_128k.md",
+                                                   "traffic_bytes_per_step")}
     log(f"[bench] decode paged: {json.dumps(res)}")
     del q, k_pool, v_pool, table, seq_lens, lm, flush
     return res
