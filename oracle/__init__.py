@@ -40,4 +40,7 @@ from .bsa_oracle import (  # noqa: F401
     n_blocks,
     gather_pages,
     decode_paged,
+    attend_rows_grad,
+    sas_gates_grad,
+    prefill_backward,
 )

@@ -32,6 +32,9 @@ What is computed, step by step, in the pages' order:
                   sequence is the contiguous decode step of its own tokens, read through its
                   page table (the serving layout; the pages say nothing of storage, so the
                   method is unchanged by it).
+9. backward    -- gradients of the PLAIN / SAS attention step for given attended sets: into q,
+                  k, v and into the selector scores through the SAS gates (the pages train the
+                  selector end to end through these gates).
 
 Readings taken where the pages are silent (each is listed in the design notes):
 * the selector vector is kept in float64 here (float32 on the device), never rounded to bf16;
@@ -463,3 +466,102 @@ def decode_paged(q, k_pool, v_pool, page_table, seq_lens, *, topk: int, mode: st
         out[b], lse[b], idx[b], sc[b] = r["out"][0], r["lse"][0], r["idx"][0], r["sc"][0]
         lm[b, :, : lm_b.shape[2]] = lm_b[0]
     return {"out": out, "lse": lse, "idx": idx, "sc": sc, "lm": lm}
+
+
+# ---------------------------------------------------------------------------------------------
+# backward pass of PLAIN / SAS prefill attention
+# ---------------------------------------------------------------------------------------------
+# The gradients of the attention step (steps 5-6) with respect to q, k, v and to the selector
+# scores that feed the SAS gates, for given attended sets: the pages train the selector end to
+# end through these gates (SAS page, summary paragraphs 2-3: the continuous score enters the
+# softmax as a log gate so the selector is trained by the task loss).  Standard softmax calculus,
+# written out per query row:
+#   x_u = scale q.k_u + g_{j(u)},  P_u = exp(x_u - lse),  o = sum_u P_u v_u
+#   dv_u += P_u do,  dP_u = do.v_u,  dx_u = P_u (dP_u - do.o),
+#   dq = scale sum_u dx_u k_u,  dk_u += scale dx_u q,  dg_j += sum_{u in block j} dx_u,
+#   g_j = log sigmoid(S_j - S_c):  dS_j += dg_j sigmoid(S_c - S_j),  dS_c -= the same  (j != c).
+
+def attend_rows_grad(qrows, tpos, K, V, A, gates, scale: float, dout, block: int = BLOCK):
+    """Gradients of attend_rows for one head's rows.
+
+    Returns dq [m,D], dK [T,D], dV [T,D] (nonzero only on the attended keys) and dgates aligned
+    with A (the summed logit gradient of each attended block).
+    """
+    T = K.shape[0]
+    pos, blk = _block_keys(A, T, block)
+    gate_of = dict(zip([int(a) for a in A], np.asarray(gates, dtype=np.float64)))
+    gvec = np.array([gate_of[int(j)] for j in blk], dtype=np.float64)
+    logits = scale * (qrows @ K[pos].T) + gvec[None, :]
+    visible = pos[None, :] <= np.asarray(tpos)[:, None]
+    logits = np.where(visible, logits, -np.inf)
+    mx = logits.max(axis=1, keepdims=True)
+    e = np.exp(logits - mx)
+    P = e / e.sum(axis=1, keepdims=True)                              # [m, |U|]
+    out = P @ V[pos]
+    dP = dout @ V[pos].T                                              # [m, |U|]
+    dx = P * (dP - np.sum(dout * out, axis=1, keepdims=True))
+    dq = scale * (dx @ K[pos])
+    dK = np.zeros_like(K)
+    dV = np.zeros_like(V)
+    np.add.at(dK, pos, scale * (dx.T @ qrows))
+    np.add.at(dV, pos, P.T @ dout)
+    col = dx.sum(axis=0)
+    dg = np.array([col[blk == int(j)].sum() for j in A])
+    return dq, dK, dV, dg
+
+
+def sas_gates_grad(A, sA, c: int, dg) -> np.ndarray:
+    """Gradient with respect to the scores sA listed beside A, given dg = d loss / d gate."""
+    A = np.asarray(A)
+    sA = np.asarray(sA, dtype=np.float64)
+    d = np.zeros(len(A))
+    ic = int(np.nonzero(A == c)[0][0])
+    for i, j in enumerate(A):
+        if int(j) == c:
+            continue
+        w = dg[i] / (1.0 + np.exp(sA[i] - sA[ic]))        # dg * sigmoid(S_c - S_j)
+        d[i] += w
+        d[ic] -= w
+    return d
+
+
+def prefill_backward(q, k, v, idx, sc, dout, *, mode: str, block: int = BLOCK, scale=None):
+    """Backward of PLAIN / SAS prefill attention for the attended sets idx [B,Hkv,NQB,NA] and,
+    for SAS, the scores sc aligned with them (the gates are formed from sc).
+
+    Returns dq [B,Hq,T,D], dk, dv [B,Hkv,T,D] and dsc [B,Hkv,NQB,NA] (zero for PLAIN and in the
+    padding).
+    """
+    if mode not in ("plain", "sas"):
+        raise ValueError("backward is defined here for PLAIN and SAS")
+    B, Hq, T, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    sc_ = _default_scale(D, scale)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dsc = np.zeros(idx.shape)
+    for b in range(B):
+        for g in range(Hkv):
+            for c in range(idx.shape[2]):
+                valid = [i for i, j in enumerate(idx[b, g, c]) if j >= 0]
+                if not valid:
+                    continue
+                A = np.array([idx[b, g, c, i] for i in valid], dtype=np.int64)
+                sA = np.array([sc[b, g, c, i] for i in valid], dtype=np.float64)
+                gates = sas_gates(A, sA, c) if mode == "sas" else np.zeros(len(A))
+                lo, hi = c * block, min((c + 1) * block, T)
+                tpos = np.arange(lo, hi)
+                dg = np.zeros(len(A))
+                for hh in range(G):
+                    h = g * G + hh
+                    dq_h, dK, dV, dg_h = attend_rows_grad(q[b, h, lo:hi], tpos, k[b, g], v[b, g], A,
+                                                          gates, sc_, dout[b, h, lo:hi], block)
+                    dq[b, h, lo:hi] += dq_h
+                    dk[b, g] += dK
+                    dv[b, g] += dV
+                    dg += dg_h
+                if mode == "sas":
+                    dsc[b, g, c, valid] = sas_gates_grad(A, sA, c, dg)
+    return {"dq": dq, "dk": dk, "dv": dv, "dsc": dsc}

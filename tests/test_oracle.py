@@ -557,3 +557,109 @@ def test_paged_landmarks_and_selection_per_sequence():
         qs = q[b, 0] + q[b, 1]
         s = [float(qs @ d["lm"][b, 0, j]) for j in range(nb)]
         assert [j for j in d["idx"][b, 0] if j >= 0] == _brute_select(s, nb - 1, 2, 1, 2)
+
+
+# ---------------------------------------------------------------------------------------
+# backward (PLAIN / SAS)
+# ---------------------------------------------------------------------------------------
+
+def _torch_dense_loss(q, k, v, idx, sc, dout, mode, scale, block=64):
+    """The same attention written as dense masked softmax in torch (float64), gates built from
+    sc with torch ops so autograd reaches sc; returns sum(O * dout)."""
+    B, Hq, T, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    NQB = idx.shape[2]
+    loss = 0.0
+    for b in range(B):
+        for g in range(Hkv):
+            bias = torch.full((T, T), float("-inf"), dtype=torch.float64)
+            rows = []
+            for c in range(NQB):
+                ents = [(i, int(j)) for i, j in enumerate(idx[b, g, c]) if j >= 0]
+                ic = [i for i, j in ents if j == c][0]
+                for i, j in ents:
+                    if mode == "sas" and j != c:
+                        gate = torch.nn.functional.logsigmoid(sc[b, g, c, i] - sc[b, g, c, ic])
+                    else:
+                        gate = torch.zeros((), dtype=torch.float64)
+                    lo, hi = c * block, min((c + 1) * block, T)
+                    klo, khi = j * block, min((j + 1) * block, T)
+                    blockmask = torch.zeros((T, T), dtype=torch.float64)
+                    blockmask[lo:hi, klo:khi] = 1.0
+                    rows.append((blockmask, gate))
+            gate_mat = sum(m * gt for m, gt in rows)
+            attended = sum(m for m, _ in rows) > 0
+            causal = torch.tril(torch.ones((T, T), dtype=torch.bool))
+            allowed = attended & causal
+            for hh in range(G):
+                h = g * G + hh
+                logits = scale * (q[b, h] @ k[b, g].T) + gate_mat
+                logits = torch.where(allowed, logits, torch.full_like(logits, float("-inf")))
+                o = torch.softmax(logits, dim=-1) @ v[b, g]
+                loss = loss + (o * dout[b, h]).sum()
+    return loss
+
+
+@pytest.mark.parametrize("mode", ["plain", "sas"])
+def test_backward_matches_torch_autograd(mode):
+    """Oracle gradients (dq, dk, dv, d sc) = torch autograd of the dense masked formulation in
+    float64, with a non-trivial selection (top-K smaller than the candidates, partial block)."""
+    r = _rng(40)
+    B, Hq, Hkv, T, D = 1, 4, 2, 64 * 5 + 23, 8
+    q = r.standard_normal((B, Hq, T, D))
+    k = O.round_to_dtype(r.standard_normal((B, Hkv, T, D)), "bf16")
+    v = r.standard_normal((B, Hkv, T, D))
+    dout = r.standard_normal((B, Hq, T, D))
+    fwd = O.prefill(q, k, v, topk=1, mode=mode, dtype="bf16")
+    idx, sc = fwd["idx"], fwd["sc"] + r.standard_normal(fwd["sc"].shape)   # varied gates
+    scale = 1.0 / math.sqrt(D)
+    got = O.prefill_backward(q, k, v, idx, sc, dout, mode=mode, scale=scale)
+    t = lambda a: torch.tensor(a, dtype=torch.float64, requires_grad=True)
+    tq, tk, tv, tsc = t(q), t(k), t(v), t(np.nan_to_num(sc))
+    loss = _torch_dense_loss(tq, tk, tv, idx, tsc, torch.tensor(dout), mode, scale)
+    loss.backward()
+    np.testing.assert_allclose(got["dq"], tq.grad.numpy(), atol=1e-11)
+    np.testing.assert_allclose(got["dk"], tk.grad.numpy(), atol=1e-11)
+    np.testing.assert_allclose(got["dv"], tv.grad.numpy(), atol=1e-11)
+    gsc = np.zeros(sc.shape) if tsc.grad is None else tsc.grad.numpy()     # PLAIN: sc unused
+    want_dsc = np.where(idx >= 0, gsc, 0.0)
+    np.testing.assert_allclose(got["dsc"], want_dsc, atol=1e-11)
+    if mode == "plain":
+        assert not got["dsc"].any()
+
+
+def test_backward_directional_finite_difference():
+    """Second pin, independent of torch: the directional derivative of sum(O * dout) along a
+    random direction matches a central finite difference of the oracle's forward (SAS)."""
+    r = _rng(41)
+    B, Hq, Hkv, T, D = 1, 2, 1, 64 * 3 + 7, 4
+    q = r.standard_normal((B, Hq, T, D))
+    k = r.standard_normal((B, Hkv, T, D))
+    v = r.standard_normal((B, Hkv, T, D))
+    dout = r.standard_normal((B, Hq, T, D))
+    fwd = O.prefill(q, k, v, topk=1, mode="sas", dtype="f32")
+    idx, sc = fwd["idx"], np.nan_to_num(fwd["sc"])
+    g = O.prefill_backward(q, k, v, idx, sc, dout, mode="sas")
+    dirs = {n: r.standard_normal(a.shape) for n, a in (("q", q), ("k", k), ("v", v), ("sc", sc))}
+
+    def f(e):
+        qq, kk, vv = q + e * dirs["q"], k + e * dirs["k"], v + e * dirs["v"]
+        ss = sc + e * dirs["sc"]
+        out = np.zeros_like(q)
+        for c in range(idx.shape[2]):
+            A = np.array([j for j in idx[0, 0, c] if j >= 0])
+            sA = np.array([ss[0, 0, c, i] for i, j in enumerate(idx[0, 0, c]) if j >= 0])
+            gates = O.sas_gates(A, sA, c)
+            lo, hi = 64 * c, min(64 * c + 64, T)
+            for h in range(Hq):
+                o, _ = O.attend_rows(qq[0, h, lo:hi], np.arange(lo, hi), kk[0, 0], vv[0, 0], A,
+                                     gates, 1 / math.sqrt(D))
+                out[0, h, lo:hi] = o
+        return float(np.sum(out * dout))
+
+    eps = 1e-5
+    fd = (f(eps) - f(-eps)) / (2 * eps)
+    an = sum(float(np.sum(g[n2] * dirs[n1])) for n1, n2 in (("q", "dq"), ("k", "dk"), ("v", "dv"),
+                                                            ("sc", "dsc")))
+    assert abs(fd - an) < 1e-6 * max(1.0, abs(an))
