@@ -27,4 +27,51 @@ __device__ __forceinline__ int count_valid(const int32_t* row, int NA) {
   return n;
 }
 
+// One copy from global memory straight into LDS, BYTES (4 or 16) per lane: lane l's bytes at
+// gbase + voff land at LDS byte address lds_addr + BYTES * l (gbase and lds_addr wave-uniform;
+// lanes outside the exec mask copy nothing).  Issued as inline assembly so the compiler does not
+// treat the copy as an LDS write of unknown extent: its own tracking would otherwise wait for
+// every copy in flight before each LDS read and at each barrier, which defeats copying several
+// blocks ahead.  Completion is the caller's business (vmcnt); M0 is saved and restored around
+// the copy.
+template <int BYTES>
+__device__ __forceinline__ void dma_lds(const char* gbase, uint32_t voff, uint32_t lds_addr) {
+  static_assert(BYTES == 4 || BYTES == 16, "global_load_lds moves 4 or 16 bytes per lane here");
+#if defined(__HIP_DEVICE_COMPILE__)
+  // both addresses are wave-uniform; make that explicit so they live in scalar registers
+  // (readfirstlane returns int: widen through uint32_t so the low half is not sign-extended)
+  const uint32_t la = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr);
+  const uint64_t ga = (uint64_t)(uintptr_t)gbase;
+  const uint32_t g_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(ga >> 32));
+  const uint32_t g_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)ga);
+  const uint64_t gs = ((uint64_t)g_hi << 32) | (uint64_t)g_lo;
+  uint32_t saved;
+  if constexpr (BYTES == 16)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %3\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(la), "v"(voff), "s"(gs)
+        : "memory");
+  else
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %2, %3\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(la), "v"(voff), "s"(gs)
+        : "memory");
+#endif
+}
+
+// LDS byte address of a shared-memory pointer
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
 }  // namespace bsa

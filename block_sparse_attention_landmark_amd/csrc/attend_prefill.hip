@@ -339,34 +339,6 @@ __global__ __launch_bounds__(HPW * 128) void attend_prefill_bf16_kernel(
     if (MODE != 2 && lse != nullptr && half == 0) lse[(size_t)(b * Hq + h) * T + tq] = lse_val;
   }
 }
-// One 16-byte-per-lane copy from global memory straight into LDS: lane l's 16 bytes at
-// gbase + voff land at LDS byte address lds_addr + 16 l (gbase and lds_addr wave-uniform).  Issued as inline assembly so the
-// compiler does not treat the copy as an LDS write of unknown extent: its own tracking would
-// otherwise wait for every copy in flight before each LDS read and at each barrier, which
-// defeats copying several blocks ahead.  Completion is the caller's business (vmcnt); M0 is
-// saved and restored around the copy.
-__device__ __forceinline__ void dma_row16(const char* gbase, uint32_t voff, uint32_t lds_addr) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  // both addresses are wave-uniform; make that explicit so they live in scalar registers
-  // (readfirstlane returns int: widen through uint32_t so the low half is not sign-extended)
-  const uint32_t la = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr);
-  const uint64_t ga = (uint64_t)(uintptr_t)gbase;
-  const uint32_t g_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(ga >> 32));
-  const uint32_t g_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)ga);
-  const uint64_t gs = ((uint64_t)g_hi << 32) | (uint64_t)g_lo;
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %2, %3\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(la), "v"(voff), "s"(gs)
-      : "memory");
-#endif
-}
-
 // ---------------------------------------------------------------------------------------------
 // bf16 prefill, PLAIN / SAS, four query heads per workgroup: ping-pong schedule
 // ---------------------------------------------------------------------------------------------
@@ -493,7 +465,7 @@ __global__ __launch_bounds__(512) void attend_prefill_pp_kernel(
 #pragma unroll
     for (int i = 0; i < SPW / 2; ++i) {
       const int sl = w + 8 * i;
-      dma_row16(blk, (uint32_t)(min(crow[i], lim) * (D * 2) + (hv == 0 ? kcol[i] : vcol_[i])),
+      dma_lds<16>(blk, (uint32_t)(min(crow[i], lim) * (D * 2) + (hv == 0 ? kcol[i] : vcol_[i])),
                 dst + (hv * TILE + sl * RPI * D) * 2);
     }
   };
