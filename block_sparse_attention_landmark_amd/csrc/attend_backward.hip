@@ -1,0 +1,721 @@
+// Backward pass of PLAIN / SAS block-sparse prefill attention (bf16 inputs, float32 arithmetic).
+//
+// For the attended sets of a forward pass (SAS page, summary paragraphs 2-3: the selector is
+// trained end to end through the gates inside the softmax), per query row t and attended key u:
+//   x = scale q.k_u + g_j(u),  P = exp(x - lse),  dP = do.v_u,  dx = P (dP - do.o),
+//   dq = scale sum_u dx k_u,  dk_u = scale sum_t dx q_t,  dv_u = sum_t P do_t,
+//   dg_j = sum over the rows of query block c (all heads of the group) and keys of block j of dx,
+//   g_j = log sigmoid(S_j - S_c): d S_j = dg_j sigmoid(S_c - S_j), d S_c -= the same (j != c).
+//
+// Kernels, in launch order:
+//   bwd_delta_kernel        Delta = do . o per query row (float32);
+//   bwd_count/scan/fill     the inverse of the attended sets: for every key block j of every
+//                           (sequence, kv group) the entries (c, pos) that attend it, grouped by
+//                           j, sorted (bwd_sort_kernel) so sums are deterministic, and cut into
+//                           work items of kBwdChunk entries;
+//   bwd_dq_kernel           one workgroup per (query block, kv group, head chunk): for each
+//                           attended block, S^T = K Q^T, dP^T = V dO^T (MFMA), dx, then
+//                           dQ^T += K^T dx^T (MFMA, K read transposed); sums dx per block into dg
+//                           and stores each entry's gate;
+//   bwd_dkdv_kernel         one workgroup per work item (key block j, chunk of entries): K_j and
+//                           V_j stay in registers; for each entry and head it stages Q and dO of
+//                           the query block, forms S = Q K^T, dP = dO V^T, dx, and accumulates
+//                           dV^T += dO^T P and dK^T += Q^T dx (MFMA) for its keys;
+//   bwd_reduce_kernel       sums a key block's work-item partials in order, scales, writes dk, dv;
+//   bwd_dsc_kernel          the selector-score gradient of each attended-set row (SAS).
+// The MFMA layouts are those of the forward kernels (32x32x16 bf16; see attend_prefill.hip).
+#include <math.h>
+
+#include <algorithm>
+
+#include "attend_common.hpp"
+#include "bsa_internal.hpp"
+
+namespace bsa {
+
+constexpr int kBwdChunk = 32;        // attended entries per dK/dV work item
+constexpr int kBwdSortCap = 4096;    // longer entry lists of one key block are left unsorted
+
+static inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// ---------------------------------------------------------------------------------------------
+// workspace
+// ---------------------------------------------------------------------------------------------
+struct BwdWs {
+  float* delta;   // [B, Hq, T]
+  float* dg;      // [B, Hkv, R, NA]
+  float* gates;   // [B, Hkv, R, NA] gate of each entry, log2 units
+  int* cnt_off;   // [B*Hkv, NB + 1]: counts, then exclusive offsets
+  int* cursor;    // [B*Hkv, NB]
+  int* chunk_off; // [B*Hkv, NB + 1]
+  int* work;      // [B*Hkv, max_work]: j | chunk << 16
+  int* n_work;    // [B*Hkv]
+  int* list;      // [B*Hkv, R * NA]: c * NA + pos, grouped by key block
+  float* part;    // [B*Hkv, max_work, 2, 64 * D]: dK^T then dV^T partial tiles
+};
+
+static int bwd_max_work(const Shape& s) {
+  return (int)(((int64_t)s.R * s.NA + kBwdChunk - 1) / kBwdChunk) + s.NB;
+}
+
+static size_t bwd_layout(const Shape& s, char* base, BwdWs* w) {
+  const size_t BG = (size_t)s.B * s.Hkv;
+  const size_t rowsel = BG * s.R * s.NA;
+  const size_t mw = (size_t)bwd_max_work(s);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += al256(bytes);
+    return p;
+  };
+  BwdWs x;
+  x.delta = (float*)take((size_t)s.B * s.Hq * s.Tq * 4);
+  x.dg = (float*)take(rowsel * 4);
+  x.gates = (float*)take(rowsel * 4);
+  x.cnt_off = (int*)take(BG * (s.NB + 1) * 4);
+  x.cursor = (int*)take(BG * s.NB * 4);
+  x.chunk_off = (int*)take(BG * (s.NB + 1) * 4);
+  x.work = (int*)take(BG * mw * 4);
+  x.n_work = (int*)take(BG * 4);
+  x.list = (int*)take(rowsel * 4);
+  x.part = (float*)take(BG * mw * 2 * kBlock * s.D * 4);
+  if (w) *w = x;
+  return off;
+}
+
+size_t backward_ws_bytes(const Shape& s) { return bwd_layout(s, nullptr, nullptr); }
+
+// ---------------------------------------------------------------------------------------------
+// Delta = do . o, D / 8 lanes per row
+// ---------------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(const bf16* __restrict__ out,
+                                                        const bf16* __restrict__ dout,
+                                                        float* __restrict__ delta, int64_t rows) {
+  constexpr int LPR = D / 8;
+  constexpr int RPW = kWave / LPR;
+  const int64_t r = ((int64_t)blockIdx.x * 4 + threadIdx.x / kWave) * RPW + (threadIdx.x % kWave) / LPR;
+  const int part = threadIdx.x % LPR;
+  float s = 0.0f;
+  if (r < rows) {
+    const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(out + r * D + part * 8));
+    const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(dout + r * D + part * 8));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s = fmaf(bf2f(a[e]), bf2f(b[e]), s);
+  }
+#pragma unroll
+  for (int o = LPR / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, kWave);
+  if (r < rows && part == 0) delta[r] = s;
+}
+
+// ---------------------------------------------------------------------------------------------
+// inverse of the attended sets
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_fill_zero_kernel(int* __restrict__ p, int64_t n,
+                                                            float* __restrict__ f, int64_t nf) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nf; i += (int64_t)gridDim.x * 256) f[i] = 0.0f;
+}
+
+__global__ __launch_bounds__(256) void bwd_count_kernel(const int32_t* __restrict__ idx,
+                                                        int* __restrict__ cnt, int R, int NA,
+                                                        int NB, int64_t n_entries) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= n_entries) return;
+  const int64_t row = e / NA;
+  const int bg = (int)(row / R), c = (int)(row % R);
+  const int j = idx[e];
+  if (j >= 0 && j <= c && j < NB) atomicAdd(&cnt[(int64_t)bg * (NB + 1) + j], 1);
+}
+
+// exclusive scan over a 1024-thread workgroup
+__device__ __forceinline__ int bwd_block_scan(int x, int* sbuf, int* total) {
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  int incl = x;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += y;
+  }
+  if (lane == kWave - 1) sbuf[w] = incl;
+  __syncthreads();
+  int base = 0, tot = 0;
+  for (int i = 0; i < 16; ++i) {
+    const int v = sbuf[i];
+    base += (i < w) ? v : 0;
+    tot += v;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + incl - x;
+}
+
+// one workgroup of 1024 threads per (sequence, kv group)
+__global__ __launch_bounds__(1024) void bwd_scan_kernel(int* __restrict__ cnt_off,
+                                                        int* __restrict__ cursor,
+                                                        int* __restrict__ chunk_off,
+                                                        int* __restrict__ work,
+                                                        int* __restrict__ n_work, int NB,
+                                                        int max_work) {
+  __shared__ int sbuf[16];
+  const int bg = blockIdx.x;
+  int* cnt = cnt_off + (int64_t)bg * (NB + 1);
+  int* cur = cursor + (int64_t)bg * NB;
+  int* coff = chunk_off + (int64_t)bg * (NB + 1);
+  int* wl = work + (int64_t)bg * max_work;
+  const int per = (NB + 1023) / 1024;
+  const int beg = min(NB, (int)threadIdx.x * per), end = min(NB, beg + per);
+  int s_cnt = 0, s_ch = 0;
+  for (int j = beg; j < end; ++j) {
+    s_cnt += cnt[j];
+    s_ch += (cnt[j] + kBwdChunk - 1) / kBwdChunk;
+  }
+  int tot_cnt, tot_ch;
+  int o_cnt = bwd_block_scan(s_cnt, sbuf, &tot_cnt);
+  int o_ch = bwd_block_scan(s_ch, sbuf, &tot_ch);
+  for (int j = beg; j < end; ++j) {
+    const int n = cnt[j];
+    const int nch = (n + kBwdChunk - 1) / kBwdChunk;
+    cnt[j] = o_cnt;
+    cur[j] = o_cnt;
+    coff[j] = o_ch;
+    for (int ch = 0; ch < nch; ++ch) wl[o_ch + ch] = j | (ch << 16);
+    o_cnt += n;
+    o_ch += nch;
+  }
+  if (threadIdx.x == 0) {
+    cnt[NB] = tot_cnt;
+    coff[NB] = tot_ch;
+    n_work[bg] = tot_ch;
+  }
+}
+
+__global__ __launch_bounds__(256) void bwd_fill_kernel(const int32_t* __restrict__ idx,
+                                                       int* __restrict__ cursor,
+                                                       int* __restrict__ list, int R, int NA,
+                                                       int NB, int64_t n_entries) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= n_entries) return;
+  const int64_t row = e / NA;
+  const int bg = (int)(row / R), c = (int)(row % R), pos = (int)(e % NA);
+  const int j = idx[e];
+  if (j >= 0 && j <= c && j < NB) {
+    const int slot = atomicAdd(&cursor[(int64_t)bg * NB + j], 1);
+    list[(int64_t)bg * R * NA + slot] = c * NA + pos;
+  }
+}
+
+// one workgroup per (key block, sequence x kv group): bitonic sort of the block's entries
+__global__ __launch_bounds__(256) void bwd_sort_kernel(const int* __restrict__ cnt_off,
+                                                       int* __restrict__ list, int R, int NA,
+                                                       int NB) {
+  __shared__ int buf[kBwdSortCap];
+  const int j = blockIdx.x, bg = blockIdx.y;
+  const int off = cnt_off[(int64_t)bg * (NB + 1) + j];
+  const int n = cnt_off[(int64_t)bg * (NB + 1) + j + 1] - off;
+  if (n <= 1 || n > kBwdSortCap) return;
+  int* seg = list + (int64_t)bg * R * NA + off;
+  int m = 1;
+  while (m < n) m <<= 1;
+  for (int i = threadIdx.x; i < m; i += 256) buf[i] = i < n ? seg[i] : 0x7fffffff;
+  __syncthreads();
+  for (int k = 2; k <= m; k <<= 1)
+    for (int s = k >> 1; s > 0; s >>= 1) {
+      for (int i = threadIdx.x; i < m; i += 256) {
+        const int p = i ^ s;
+        if (p > i) {
+          const bool up = (i & k) == 0;
+          const int a = buf[i], b2 = buf[p];
+          if ((a > b2) == up) {
+            buf[i] = b2;
+            buf[p] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  for (int i = threadIdx.x; i < n; i += 256) seg[i] = buf[i];
+}
+
+// ---------------------------------------------------------------------------------------------
+// dQ (and the per-entry gate gradient sums)
+// ---------------------------------------------------------------------------------------------
+template <int D, int MODE, int HPW>
+__global__ __launch_bounds__(HPW * 128) void bwd_dq_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    const int32_t* __restrict__ idx, const float* __restrict__ sc, bf16* __restrict__ dq,
+    float* __restrict__ dg, float* __restrict__ gates_out, int Hq, int Hkv, int G, int T,
+    int NQB, int NA, int n_hc, float scale_log2, float scale) {
+  constexpr int NT = HPW * 128;
+  constexpr int KP = D + 8;            // tile row pitch (elements)
+  constexpr int C8 = D / 8;
+  constexpr int CPT = kBlock * C8 / NT;
+  __shared__ __attribute__((aligned(16))) bf16 Ks[2][kBlock * KP];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[2][kBlock * KP];
+
+  const int c = NQB - 1 - (int)blockIdx.x;   // heavy (late) query blocks first
+  const int g = blockIdx.y / n_hc, hc = blockIdx.y % n_hc;
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
+  const int half = lane / 32, l32 = lane % 32;
+  const int h = g * G + hc * HPW + w / 2;
+  const int tq = c * kBlock + (w % 2) * 32 + l32;
+  const bool row_ok = tq < T;
+  const size_t qrow_off = ((size_t)(b * Hq + h) * T + min(tq, T - 1)) * D;
+
+  bf16x8 qf[D / 16], df[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    u32x4 a = *reinterpret_cast<const u32x4*>(q + qrow_off + 16 * s + 8 * half);
+    u32x4 bb = *reinterpret_cast<const u32x4*>(dout + qrow_off + 16 * s + 8 * half);
+    if (!row_ok) a = bb = u32x4{0u, 0u, 0u, 0u};
+    qf[s] = __builtin_bit_cast(bf16x8, a);
+    df[s] = __builtin_bit_cast(bf16x8, bb);
+  }
+  const size_t rrow = (size_t)(b * Hq + h) * T + min(tq, T - 1);
+  const float lse2 = row_ok ? lse[rrow] * kLog2e : 0.0f;
+  const float dlt = row_ok ? delta[rrow] : 0.0f;
+
+  const size_t kvbase = (size_t)(b * Hkv + g) * T * D;
+  const size_t rowsel = ((size_t)(b * Hkv + g) * NQB + c) * NA;
+  const int32_t* irow = idx + rowsel;
+  const int nval = count_valid(irow, NA);
+  float s_ref = 0.0f;
+  if (MODE == 1 && nval > 0) s_ref = sc[rowsel + nval - 1];
+  auto gate_of = [&](int a, int j) {
+    if (MODE != 1 || j == c) return 0.0f;
+    return log_sigmoid(sc[rowsel + a] - s_ref) * kLog2e;
+  };
+  if (hc == 0 && w == 0)
+    for (int a = lane; a < nval; a += kWave) {
+      const int j = irow[a];
+      gates_out[rowsel + a] = gate_of(a, j);
+    }
+
+  u32x4 kreg[CPT], vreg[CPT];
+  auto load_tile = [&](int a) {
+    const int j = irow[a];
+    const bool ok = j >= 0 && j <= c;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int ci = tid + i * NT;
+      const int row = ci / C8, c8 = ci % C8;
+      const int tok = j * kBlock + row;
+      kreg[i] = vreg[i] = u32x4{0u, 0u, 0u, 0u};
+      if (ok && tok < T) {
+        kreg[i] = *reinterpret_cast<const u32x4*>(k + kvbase + (size_t)tok * D + c8 * 8);
+        vreg[i] = *reinterpret_cast<const u32x4*>(v + kvbase + (size_t)tok * D + c8 * 8);
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int ci = tid + i * NT;
+      const int row = ci / C8, c8 = ci % C8;
+      *reinterpret_cast<u32x4*>(&Ks[buf][row * KP + c8 * 8]) = kreg[i];
+      *reinterpret_cast<u32x4*>(&Vs[buf][row * KP + c8 * 8]) = vreg[i];
+    }
+  };
+
+  f32x16 dqa[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dqa[dt][i] = 0.0f;
+  const int vrow = (lane % 16) / 4;
+  const int vcol = 16 * ((lane / 16) % 2) + 4 * (lane % 4);
+
+  if (nval > 0) load_tile(0);
+  if (nval > 0) store_tile(0);
+  if (nval > 1) load_tile(1);
+  __syncthreads();
+  for (int a = 0; a < nval; ++a) {
+    const int buf = a & 1;
+    const int j = irow[a];
+    if (j >= 0 && j <= c) {
+      const bf16* Kb = Ks[buf];
+      const bf16* Vb = Vs[buf];
+      f32x16 st[2], dp[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st[kt][i] = dp[kt][i] = 0.0f;
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+          const int off = (kt * 32 + l32) * KP + 16 * s + 8 * half;
+          const bf16x8 kfr = *reinterpret_cast<const bf16x8*>(&Kb[off]);
+          const bf16x8 vfr = *reinterpret_cast<const bf16x8*>(&Vb[off]);
+          st[kt] = mfma32(kfr, qf[s], st[kt]);
+          dp[kt] = mfma32(vfr, df[s], dp[kt]);
+        }
+      }
+      const float gb = gate_of(a, j) - lse2;
+      float dgs = 0.0f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = j * kBlock + kt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+          const bool vis = row_ok && key <= tq;
+          const float p = vis ? fast_exp2(fmaf(st[kt][i], scale_log2, gb)) : 0.0f;
+          const float x = p * (dp[kt][i] - dlt);
+          st[kt][i] = x;
+          dgs += x;
+        }
+      // gate gradient of this entry: the sum over the wave's rows and keys
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) dgs += __shfl_xor(dgs, o, kWave);
+      if (lane == 0 && MODE == 1) atomicAdd(&dg[rowsel + a], dgs);
+      // dQ^T += K^T dx^T: the K tile read transposed, dx^T from the score registers
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        bf16x8 xb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xb[e] = f2bf(st[ks / 2][8 * (ks % 2) + e]);
+        const bf16* k0 = Kb + (16 * ks + 4 * half + vrow) * KP + vcol;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          const i16x4 x0 = lds_read_tr16(k0 + dt * 32);
+          const i16x4 x1 = lds_read_tr16(k0 + 8 * KP + dt * 32);
+          const bf16x8 ak = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+          dqa[dt] = mfma32(ak, xb, dqa[dt]);
+        }
+      }
+    }
+    if (a + 1 < nval) store_tile(buf ^ 1);
+    if (a + 2 < nval) load_tile(a + 2);
+    __syncthreads();
+  }
+  if (row_ok) {
+    bf16* orow = dq + ((size_t)(b * Hq + h) * T + tq) * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        bf16x4 ov;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ov[e] = f2bf(dqa[dt][4 * i4 + e] * scale);
+        *reinterpret_cast<bf16x4*>(orow + dt * 32 + 8 * i4 + 4 * half) = ov;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// dK, dV partials of one work item: key block j, entries [e0, e1) of its list, all heads
+// ---------------------------------------------------------------------------------------------
+// Wave w owns keys kh*32..+32 (kh = w % 2) of the block and d columns dh*D/2..+D/2 (dh = w / 2)
+// of the accumulators; S and dP are formed for its 32 keys by both of its d halves.
+template <int D, int MODE>
+__global__ __launch_bounds__(256) void bwd_dkdv_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    const float* __restrict__ gates, const int* __restrict__ cnt_off,
+    const int* __restrict__ list, const int* __restrict__ work, const int* __restrict__ n_work,
+    float* __restrict__ part, int Hq, int Hkv, int G, int T, int NQB, int NB, int NA,
+    int max_work, float scale_log2) {
+  constexpr int KP = D + 8;
+  constexpr int C8 = D / 8;
+  constexpr int CPT = kBlock * C8 / 256;      // 16-byte chunks of one 64 x D tile per thread
+  constexpr int DT = D / 64;                  // 32-column d tiles per wave
+  __shared__ __attribute__((aligned(16))) bf16 Qs[2][kBlock * KP];
+  __shared__ __attribute__((aligned(16))) bf16 Os[2][kBlock * KP];
+  __shared__ __attribute__((aligned(16))) float Ls[2][kBlock];
+  __shared__ __attribute__((aligned(16))) float Ds[2][kBlock];
+
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int bg = b * Hkv + g;
+  const int wi = blockIdx.x;
+  if (wi >= n_work[bg]) return;                 // whole workgroup, before any barrier
+  const int item = work[(size_t)bg * max_work + wi];
+  const int j = item & 0xffff, ch = item >> 16;
+  const int* co = cnt_off + (size_t)bg * (NB + 1);
+  const int e0 = co[j] + ch * kBwdChunk;
+  const int e1 = min(co[j + 1], e0 + kBwdChunk);
+  const int* lst = list + (size_t)bg * NQB * NA;
+
+  const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
+  const int half = lane / 32, l32 = lane % 32;
+  const int kh = w % 2, dh = w / 2;
+  const int ku = j * kBlock + kh * 32 + l32;   // this lane's key (the n index of S)
+  const size_t kvbase = (size_t)bg * T * D;
+
+  // K_j and V_j rows of this wave's keys as B fragments: B[k = d][n = key]
+  bf16x8 kb[D / 16], vb[D / 16];
+  {
+    const int tok = min(ku, T - 1);
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      kb[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(k + kvbase + (size_t)tok * D + 16 * s + 8 * half));
+      vb[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(v + kvbase + (size_t)tok * D + 16 * s + 8 * half));
+    }
+  }
+  f32x16 dka[DT], dva[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dka[dt][i] = dva[dt][i] = 0.0f;
+
+  // step s = (entry e0 + s / G, head s % G)
+  const int nsteps = (e1 - e0) * G;
+  u32x4 qreg[CPT], oreg[CPT];
+  float lreg = 0.0f, dreg = 0.0f;
+  auto step_c = [&](int st) { return lst[e0 + st / G] / NA; };
+  auto load_step = [&](int st) {
+    const int c = step_c(st);
+    const int h = g * G + st % G;
+    const size_t base = (size_t)(b * Hq + h) * T;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int ci = tid + i * 256;
+      const int row = ci / C8, c8 = ci % C8;
+      const int tok = min(c * kBlock + row, T - 1);
+      qreg[i] = *reinterpret_cast<const u32x4*>(q + (base + tok) * D + c8 * 8);
+      oreg[i] = *reinterpret_cast<const u32x4*>(dout + (base + tok) * D + c8 * 8);
+    }
+    if (tid < kBlock) {
+      const int tok = min(c * kBlock + tid, T - 1);
+      lreg = lse[base + tok] * kLog2e;
+      dreg = delta[base + tok];
+    }
+  };
+  auto store_step = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int ci = tid + i * 256;
+      const int row = ci / C8, c8 = ci % C8;
+      *reinterpret_cast<u32x4*>(&Qs[buf][row * KP + c8 * 8]) = qreg[i];
+      *reinterpret_cast<u32x4*>(&Os[buf][row * KP + c8 * 8]) = oreg[i];
+    }
+    if (tid < kBlock) {
+      Ls[buf][tid] = lreg;
+      Ds[buf][tid] = dreg;
+    }
+  };
+
+  const int vrow = (lane % 16) / 4;
+  const int vcol = 16 * ((lane / 16) % 2) + 4 * (lane % 4);
+  if (nsteps > 0) {
+    load_step(0);
+    store_step(0);
+    if (nsteps > 1) load_step(1);
+  }
+  __syncthreads();
+  for (int st = 0; st < nsteps; ++st) {
+    const int buf = st & 1;
+    const int ent = lst[e0 + st / G];
+    const int c = ent / NA;
+    const float gb = MODE == 1 ? gates[((size_t)bg * NQB + c) * NA + ent % NA] : 0.0f;
+    const bf16* Qb = Qs[buf];
+    const bf16* Ob = Os[buf];
+    // S = Q K^T and dP = dO V^T for the 64 rows of query block c and this wave's 32 keys
+    f32x16 s2[2], p2[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s2[tt][i] = p2[tt][i] = 0.0f;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        const int off = (tt * 32 + l32) * KP + 16 * s + 8 * half;
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&Qb[off]);
+        const bf16x8 oa = *reinterpret_cast<const bf16x8*>(&Ob[off]);
+        s2[tt] = mfma32(qa, kb[s], s2[tt]);
+        p2[tt] = mfma32(oa, vb[s], p2[tt]);
+      }
+    }
+    // P and dx; register i of t-tile tt holds row t = 32 tt + 8 (i / 4) + 4 half + i % 4
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int t0 = tt * 32 + 8 * i4 + 4 * half;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&Ls[buf][t0]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Ds[buf][t0]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int tq = c * kBlock + t0 + e;
+          const bool vis = tq < T && ku <= tq;
+          const float p = vis ? fast_exp2(fmaf(s2[tt][4 * i4 + e], scale_log2, gb - l4[e])) : 0.0f;
+          s2[tt][4 * i4 + e] = p;
+          p2[tt][4 * i4 + e] = p * (p2[tt][4 * i4 + e] - d4[e]);
+        }
+      }
+    // dV^T += dO^T P and dK^T += Q^T dx over the 64 rows (4 k-steps of 16), this wave's d tiles
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 pb, xb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pb[e] = f2bf(s2[ks / 2][8 * (ks % 2) + e]);
+        xb[e] = f2bf(p2[ks / 2][8 * (ks % 2) + e]);
+      }
+      const int r0 = 16 * ks + 4 * half + vrow;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int col = (dh * DT + dt) * 32 + vcol;
+        const i16x4 o0 = lds_read_tr16(Ob + r0 * KP + col);
+        const i16x4 o1 = lds_read_tr16(Ob + (r0 + 8) * KP + col);
+        const i16x4 q0 = lds_read_tr16(Qb + r0 * KP + col);
+        const i16x4 q1 = lds_read_tr16(Qb + (r0 + 8) * KP + col);
+        const bf16x8 ao = __builtin_bit_cast(bf16x8, __builtin_shufflevector(o0, o1, 0, 1, 2, 3, 4, 5, 6, 7));
+        const bf16x8 aq = __builtin_bit_cast(bf16x8, __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7));
+        dva[dt] = mfma32(ao, pb, dva[dt]);
+        dka[dt] = mfma32(aq, xb, dka[dt]);
+      }
+    }
+    if (st + 1 < nsteps) store_step(buf ^ 1);
+    if (st + 2 < nsteps) load_step(st + 2);
+    __syncthreads();
+  }
+  // partial tiles, layout [d][key]: dK^T then dV^T
+  float* pt = part + ((size_t)bg * max_work + wi) * 2 * kBlock * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int d = (dh * DT + dt) * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+      const int u = kh * 32 + l32;
+      pt[d * kBlock + u] = dka[dt][i];
+      pt[kBlock * D + d * kBlock + u] = dva[dt][i];
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// dk, dv of one key block: its work items' partials summed in order
+// ---------------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict__ part,
+                                                         const int* __restrict__ chunk_off,
+                                                         bf16* __restrict__ dk,
+                                                         bf16* __restrict__ dv, int Hkv, int T,
+                                                         int NB, int max_work, float scale) {
+  __shared__ float tile[kBlock * (D + 1)];
+  const int j = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int bg = b * Hkv + g;
+  const int c0 = chunk_off[(size_t)bg * (NB + 1) + j];
+  const int c1 = chunk_off[(size_t)bg * (NB + 1) + j + 1];
+  for (int which = 0; which < 2; ++which) {
+    for (int e = threadIdx.x; e < kBlock * D; e += 256) {   // e = d * 64 + key
+      float s = 0.0f;
+      for (int ch = c0; ch < c1; ++ch) s += part[((size_t)bg * max_work + ch) * 2 * kBlock * D + which * kBlock * D + e];
+      const int d = e / kBlock, u = e % kBlock;
+      tile[u * (D + 1) + d] = which == 0 ? s * scale : s;
+    }
+    __syncthreads();
+    bf16* dst = which == 0 ? dk : dv;
+    for (int e = threadIdx.x; e < kBlock * D; e += 256) {   // e = key * D + d
+      const int u = e / D, d = e % D;
+      const int tok = j * kBlock + u;
+      if (tok < T) dst[((size_t)bg * T + tok) * D + d] = f2bf(tile[u * (D + 1) + d]);
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// selector-score gradient of each attended-set row (SAS)
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_dsc_kernel(const int32_t* __restrict__ idx,
+                                                      const float* __restrict__ sc,
+                                                      const float* __restrict__ dg,
+                                                      float* __restrict__ dsc, int R, int NA,
+                                                      int64_t nrows, int mode) {
+  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (row >= nrows) return;
+  const int c = (int)(row % R);
+  const int32_t* ir = idx + row * NA;
+  const float* sr = sc ? sc + row * NA : nullptr;
+  float* out = dsc + row * NA;
+  int nval = 0;
+  while (nval < NA && ir[nval] >= 0) ++nval;
+  int ic = -1;
+  for (int a = 0; a < nval; ++a)
+    if (ir[a] == c) ic = a;
+  float acc_c = 0.0f;
+  for (int a = 0; a < NA; ++a) {
+    float d = 0.0f;
+    if (mode == 1 && a < nval && a != ic && ic >= 0) {
+      const float sg = 1.0f / (1.0f + expf(sr[a] - sr[ic]));   // sigmoid(S_c - S_j)
+      d = dg[row * NA + a] * sg;
+      acc_c -= d;
+    }
+    out[a] = d;
+  }
+  if (ic >= 0 && mode == 1) out[ic] = acc_c;
+}
+
+// ---------------------------------------------------------------------------------------------
+// launcher
+// ---------------------------------------------------------------------------------------------
+template <int D>
+static hipError_t launch_backward_d(const Shape& s, const void* q, const void* k, const void* v,
+                                    const int32_t* idx, const float* sc, const void* out,
+                                    const float* lse, const void* dout, void* dq, void* dk,
+                                    void* dv, float* dsc, void* ws, hipStream_t st) {
+  BwdWs W;
+  bwd_layout(s, (char*)ws, &W);
+  const int BG = s.B * s.Hkv;
+  const int64_t rows = (int64_t)s.B * s.Hq * s.Tq;
+  const int64_t n_entries = (int64_t)BG * s.R * s.NA;
+  const int mw = bwd_max_work(s);
+  const float sl2 = s.scale * kLog2e;
+  {
+    constexpr int RPB = 4 * (kWave / (D / 8));
+    hipLaunchKernelGGL(bwd_delta_kernel<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
+                       st, (const bf16*)out, (const bf16*)dout, W.delta, rows);
+  }
+  hipLaunchKernelGGL(bwd_fill_zero_kernel, dim3(1024), dim3(256), 0, st, W.cnt_off,
+                     (int64_t)BG * (s.NB + 1), W.dg, n_entries);
+  const unsigned eg = (unsigned)((n_entries + 255) / 256);
+  hipLaunchKernelGGL(bwd_count_kernel, dim3(eg), dim3(256), 0, st, idx, W.cnt_off, s.R, s.NA,
+                     s.NB, n_entries);
+  hipLaunchKernelGGL(bwd_scan_kernel, dim3(BG), dim3(1024), 0, st, W.cnt_off, W.cursor,
+                     W.chunk_off, W.work, W.n_work, s.NB, mw);
+  hipLaunchKernelGGL(bwd_fill_kernel, dim3(eg), dim3(256), 0, st, idx, W.cursor, W.list, s.R,
+                     s.NA, s.NB, n_entries);
+  hipLaunchKernelGGL(bwd_sort_kernel, dim3(s.NB, BG), dim3(256), 0, st, W.cnt_off, W.list, s.R,
+                     s.NA, s.NB);
+  const int hpw = (s.G % 4 == 0) ? 4 : (s.G % 2 == 0) ? 2 : 1;
+  const int n_hc = s.G / hpw;
+#define BSA_DQ(MODE, HPW)                                                                        \
+  hipLaunchKernelGGL((bwd_dq_kernel<D, MODE, HPW>), dim3(s.R, s.Hkv * n_hc, s.B), dim3(HPW * 128),\
+                     0, st, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout,     \
+                     lse, W.delta, idx, sc, (bf16*)dq, W.dg, W.gates, s.Hq, s.Hkv, s.G, s.Tq,      \
+                     s.R, s.NA, n_hc, sl2, s.scale)
+#define BSA_DQ_H(MODE)                                           \
+  if (hpw == 4) BSA_DQ(MODE, 4);                                  \
+  else if (hpw == 2) BSA_DQ(MODE, 2);                             \
+  else BSA_DQ(MODE, 1);
+  if (s.mode == 1) {
+    BSA_DQ_H(1)
+  } else {
+    BSA_DQ_H(0)
+  }
+#undef BSA_DQ_H
+#undef BSA_DQ
+#define BSA_KV(MODE)                                                                            \
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, MODE>), dim3(mw, s.Hkv, s.B), dim3(256), 0, st,        \
+                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, lse,     \
+                     W.delta, W.gates, W.cnt_off, W.list, W.work, W.n_work, W.part, s.Hq, s.Hkv, \
+                     s.G, s.Tq, s.R, s.NB, s.NA, mw, sl2)
+  if (s.mode == 1) BSA_KV(1);
+  else BSA_KV(0);
+#undef BSA_KV
+  hipLaunchKernelGGL(bwd_reduce_kernel<D>, dim3(s.NB, s.Hkv, s.B), dim3(256), 0, st, W.part,
+                     W.chunk_off, (bf16*)dk, (bf16*)dv, s.Hkv, s.Tq, s.NB, mw, s.scale);
+  if (dsc != nullptr)
+    hipLaunchKernelGGL(bwd_dsc_kernel, dim3((unsigned)((BG * (int64_t)s.R + 255) / 256)), dim3(256),
+                       0, st, idx, sc, W.dg, dsc, s.R, s.NA, (int64_t)BG * s.R, s.mode);
+  return hipGetLastError();
+}
+
+hipError_t launch_attend_backward(const Shape& s, const void* q, const void* k, const void* v,
+                                  const int32_t* idx, const float* sc, const void* out,
+                                  const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                                  float* dsc, void* ws, hipStream_t st) {
+  if (s.D == 128) return launch_backward_d<128>(s, q, k, v, idx, sc, out, lse, dout, dq, dk, dv, dsc, ws, st);
+  return launch_backward_d<64>(s, q, k, v, idx, sc, out, lse, dout, dq, dk, dv, dsc, ws, st);
+}
+
+}  // namespace bsa

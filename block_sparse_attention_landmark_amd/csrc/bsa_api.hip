@@ -208,6 +208,62 @@ bsa_status_t bsa_attend_prefill(const bsa_params_t* params, const void* q, const
                     "attend_prefill");
 }
 
+// ---- backward of PLAIN / SAS prefill ----
+
+namespace {
+bsa_status_t backward_shape(const bsa_params_t* params, bsa::Shape* s) {
+  BSA_TRY(make_shape(params, kPrefill, s));
+  if (!s->bf16) return fail(BSA_ERR_UNSUPPORTED, "the backward pass is implemented for bf16 only");
+  if (s->mode == BSA_MODE_HILS)
+    return fail(BSA_ERR_UNSUPPORTED, "the backward pass is implemented for PLAIN and SAS only");
+  if (s->NB > 65535)
+    return fail(BSA_ERR_UNSUPPORTED, "the backward pass supports at most 65535 key blocks (got %d)",
+                s->NB);
+  if ((int64_t)s->R * s->NA >= ((int64_t)1 << 31))
+    return fail(BSA_ERR_SHAPE, "query blocks x attended entries exceeds 2^31 - 1");
+  return BSA_OK;
+}
+}  // namespace
+
+size_t bsa_backward_workspace_bytes(const bsa_params_t* params) {
+  bsa::Shape s;
+  if (backward_shape(params, &s) != BSA_OK) return 0;
+  return bsa::backward_ws_bytes(s);
+}
+
+bsa_status_t bsa_attend_prefill_backward(const bsa_params_t* params, const void* q,
+                                         const void* k, const void* v, const int32_t* idx,
+                                         const float* sc, const void* out, const float* lse,
+                                         const void* dout, void* dq, void* dk, void* dv,
+                                         float* dsc, void* ws, size_t ws_bytes, void* stream) {
+  bsa::Shape s;
+  BSA_TRY(backward_shape(params, &s));
+  BSA_TRY(check_ptr(q, "q"));
+  BSA_TRY(check_ptr(k, "k"));
+  BSA_TRY(check_ptr(v, "v"));
+  BSA_TRY(check_ptr(idx, "idx"));
+  BSA_TRY(check_ptr(out, "out"));
+  BSA_TRY(check_ptr(lse, "lse"));
+  BSA_TRY(check_ptr(dout, "dout"));
+  BSA_TRY(check_ptr(dq, "dq"));
+  BSA_TRY(check_ptr(dk, "dk"));
+  BSA_TRY(check_ptr(dv, "dv"));
+  if (s.mode == BSA_MODE_SAS) {
+    BSA_TRY(check_ptr(sc, "sc"));
+    BSA_TRY(check_ptr(dsc, "dsc"));
+  } else if (dsc != nullptr) {
+    BSA_TRY(check_ptr(dsc, "dsc"));
+  }
+  const size_t need = bsa::backward_ws_bytes(s);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(BSA_ERR_WORKSPACE, "backward workspace needs %zu bytes (got %zu%s)", need,
+                ws_bytes, ws == nullptr ? ", NULL pointer" : "");
+  if (((uintptr_t)ws & 255u) != 0) return fail(BSA_ERR_ALIGN, "ws is not 256-byte aligned");
+  return hip_result(bsa::launch_attend_backward(s, q, k, v, idx, sc, out, lse, dout, dq, dk, dv,
+                                                dsc, ws, (hipStream_t)stream),
+                    "attend_prefill_backward");
+}
+
 size_t bsa_decode_workspace_bytes(const bsa_params_t* params) {
   bsa::Shape s;
   if (make_shape(params, kDecode, &s) != BSA_OK) return 0;

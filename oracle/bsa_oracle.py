@@ -484,8 +484,9 @@ def decode_paged(q, k_pool, v_pool, page_table, seq_lens, *, topk: int, mode: st
 def attend_rows_grad(qrows, tpos, K, V, A, gates, scale: float, dout, block: int = BLOCK):
     """Gradients of attend_rows for one head's rows.
 
-    Returns dq [m,D], dK [T,D], dV [T,D] (nonzero only on the attended keys) and dgates aligned
-    with A (the summed logit gradient of each attended block).
+    Returns dq [m,D], pos (the attended key positions, ascending, each once), dK and dV [|pos|,D]
+    (the gradients of the keys and values at pos) and dgates aligned with A (the summed logit
+    gradient of each attended block).
     """
     T = K.shape[0]
     pos, blk = _block_keys(A, T, block)
@@ -501,13 +502,11 @@ def attend_rows_grad(qrows, tpos, K, V, A, gates, scale: float, dout, block: int
     dP = dout @ V[pos].T                                              # [m, |U|]
     dx = P * (dP - np.sum(dout * out, axis=1, keepdims=True))
     dq = scale * (dx @ K[pos])
-    dK = np.zeros_like(K)
-    dV = np.zeros_like(V)
-    np.add.at(dK, pos, scale * (dx.T @ qrows))
-    np.add.at(dV, pos, P.T @ dout)
+    dK = scale * (dx.T @ qrows)
+    dV = P.T @ dout
     col = dx.sum(axis=0)
     dg = np.array([col[blk == int(j)].sum() for j in A])
-    return dq, dK, dV, dg
+    return dq, pos, dK, dV, dg
 
 
 def sas_gates_grad(A, sA, c: int, dg) -> np.ndarray:
@@ -556,11 +555,12 @@ def prefill_backward(q, k, v, idx, sc, dout, *, mode: str, block: int = BLOCK, s
                 dg = np.zeros(len(A))
                 for hh in range(G):
                     h = g * G + hh
-                    dq_h, dK, dV, dg_h = attend_rows_grad(q[b, h, lo:hi], tpos, k[b, g], v[b, g], A,
-                                                          gates, sc_, dout[b, h, lo:hi], block)
+                    dq_h, pos, dK, dV, dg_h = attend_rows_grad(q[b, h, lo:hi], tpos, k[b, g],
+                                                               v[b, g], A, gates, sc_,
+                                                               dout[b, h, lo:hi], block)
                     dq[b, h, lo:hi] += dq_h
-                    dk[b, g] += dK
-                    dv[b, g] += dV
+                    dk[b, g, pos] += dK          # pos holds each key once
+                    dv[b, g, pos] += dV
                     dg += dg_h
                 if mode == "sas":
                     dsc[b, g, c, valid] = sas_gates_grad(A, sA, c, dg)

@@ -8,6 +8,12 @@ Bars (written here once, used by every parity test):
 * float32 outputs: max-abs error <= 1e-4;
 * log-sum-exp: abs error <= 1e-3 (bf16 inputs) or 1e-4 (float32);
 * landmarks: bit-exact (bf16); float32 within one float32 ulp of the oracle's rounding.
+* gradients of the backward pass (dq, dk, dv bf16; dsc float32), per head or group slice:
+  mean |error| / mean |reference| <= 1e-2 and max |error| <= 5e-2 * max |reference|.  The
+  kernels round P and dx = P (dP - Delta) to bf16 (relative 2^-9) before the dV, dK and dQ
+  products, store bf16 (2^-9) and form Delta = dout . out from the bf16 forward output, whose
+  2^-9 relative error is amplified where dP and Delta nearly cancel; 1e-2 is about five such
+  roundings on the mean, and the max bound leaves room for the cancelling entries.
 """
 
 import numpy as np
@@ -19,6 +25,8 @@ TIE_BAND = 1e-3
 BF16_MAX_ABS = 2e-2
 BF16_MEAN_REL = 5e-3
 F32_MAX_ABS = 1e-4
+GRAD_MEAN_REL = 1e-2
+GRAD_MAX_REL = 5e-2
 
 
 def host64(t: torch.Tensor) -> np.ndarray:
@@ -79,3 +87,21 @@ def check_landmarks(dev: np.ndarray, ref: np.ndarray, dtype: str, where=""):
     else:
         ulp = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
         assert np.all(np.abs(dev - ref) <= ulp), f"{where}: float32 landmarks off by more than 1 ulp"
+
+
+def check_grad(dev: np.ndarray, ref: np.ndarray, where=""):
+    """Backward-pass bar: relative to the reference's own mean and max magnitude."""
+    err = np.abs(dev - ref)
+    if err.size == 0:
+        return 0.0, 0.0
+    ref_max = float(np.abs(ref).max())
+    ref_mean = float(np.abs(ref).mean())
+    mx = float(err.max())
+    if ref_max == 0.0:
+        assert mx == 0.0, f"{where}: reference is zero but the device gives max {mx:.3e}"
+        return 0.0, 0.0
+    rel = float(err.mean()) / ref_mean
+    assert rel <= GRAD_MEAN_REL, f"{where}: mean-rel {rel:.3e} > {GRAD_MEAN_REL}"
+    assert mx <= GRAD_MAX_REL * ref_max, (f"{where}: max-abs {mx:.3e} > {GRAD_MAX_REL} * "
+                                          f"max|ref| {ref_max:.3e}")
+    return mx, rel
