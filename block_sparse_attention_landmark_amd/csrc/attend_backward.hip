@@ -17,11 +17,12 @@
 //                           attended block, S^T = K Q^T, dP^T = V dO^T (MFMA), dx, then
 //                           dQ^T += K^T dx^T (MFMA, K read transposed); sums dx per block into dg
 //                           and stores each entry's gate;
-//   bwd_dkdv_kernel         one workgroup per work item (key block j, chunk of entries): K_j and
-//                           V_j stay in registers; for each entry and head it stages Q and dO of
-//                           the query block, forms S = Q K^T, dP = dO V^T, dx, and accumulates
-//                           dV^T += dO^T P and dK^T += Q^T dx (MFMA) for its keys;
-//   bwd_reduce_kernel       sums a key block's work-item partials in order, scales, writes dk, dv;
+//   bwd_dkdv_kernel         one workgroup per work item (key block j, up to kBwdChunk entries):
+//                           K_j and V_j stay in registers; for each entry and head it copies Q and
+//                           dO of the query block into LDS a few steps ahead, forms S = Q K^T,
+//                           dP = dO V^T, dx, and accumulates dV^T += dO^T P and dK^T += Q^T dx
+//                           (MFMA) for its keys; a key block's only work item writes dk, dv;
+//   bwd_reduce_kernel       otherwise sums the block's work-item partials in order and writes;
 //   bwd_dsc_kernel          the selector-score gradient of each attended-set row (SAS).
 // The MFMA layouts are those of the forward kernels (32x32x16 bf16; see attend_prefill.hip).
 #include <math.h>
@@ -33,7 +34,7 @@
 
 namespace bsa {
 
-constexpr int kBwdChunk = 32;        // attended entries per dK/dV work item
+constexpr int kBwdChunk = 64;        // attended entries per dK/dV work item
 constexpr int kBwdSortCap = 4096;    // longer entry lists of one key block are left unsorted
 
 static inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -51,7 +52,7 @@ struct BwdWs {
   int* work;      // [B*Hkv, max_work]: j | chunk << 16
   int* n_work;    // [B*Hkv]
   int* list;      // [B*Hkv, R * NA]: c * NA + pos, grouped by key block
-  float* part;    // [B*Hkv, max_work, 2, 64 * D]: dK^T then dV^T partial tiles
+  float* part;    // [B*Hkv, max_work, 2, 64, D]: dK then dV partial tiles (unscaled)
 };
 
 static int bwd_max_work(const Shape& s) {
@@ -403,44 +404,89 @@ __global__ __launch_bounds__(HPW * 128) void bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
-// dK, dV partials of one work item: key block j, entries [e0, e1) of its list, all heads
+// dK, dV of one work item: key block j, entries [e0, e1) of its list, all heads of the group
 // ---------------------------------------------------------------------------------------------
-// Wave w owns keys kh*32..+32 (kh = w % 2) of the block and d columns dh*D/2..+D/2 (dh = w / 2)
-// of the accumulators; S and dP are formed for its 32 keys by both of its d halves.
+// Four waves; wave w owns keys kh*32..+32 (kh = w % 2) and query rows th*32..+32 (th = w / 2) of
+// every step, so S and dP are formed once.  K_j and V_j stay in registers as MFMA B fragments for
+// the whole item.  Step s = (entry s / G, head s % G) needs Q and dO of that query block and head
+// (64 x D each) plus lse and Delta of its 64 rows; they are copied from global memory straight
+// into LDS (dma_lds) kBwdAhead steps ahead, in kBwdStages rotating stages, one barrier per step.
+// No other vector memory instruction is issued inside the step loop (the per-entry block and gate
+// are staged in LDS first), so the copy counter waits below count exactly those copies.
+// Tiles are stored with the 16-byte chunks of row r XOR-swizzled by bwd_swz(r): conflict-free
+// both for row reads (the A operands of S and dP) and for transposed reads (dO^T, Q^T).
+constexpr int kBwdStages = 4;
+constexpr int kBwdAhead = kBwdStages - 1;
+
+template <int D>
+__device__ __forceinline__ int bwd_swz(int r) {
+  if constexpr (D == 128) return (4 * (r % 4)) ^ ((r / 4) % 4);
+  return 4 * ((r / 2) % 2) + ((r / 4) % 4);
+}
+// element offset of (row, col) in a swizzled 64 x D tile
+template <int D>
+__device__ __forceinline__ int bwd_tile_off(int row, int col) {
+  return row * D + 8 * ((col >> 3) ^ bwd_swz<D>(row)) + (col & 7);
+}
+
+__device__ __forceinline__ void bwd_wait_copies(int left) {
+  // s_waitcnt with expcnt and lgkmcnt at their maxima and vmcnt = left (split over two fields)
+#define BSA_VM(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
+  switch (left) {
+    case 0: BSA_VM(0); break;
+    case 5: BSA_VM(5); break;
+    case 9: BSA_VM(9); break;
+    case 10: BSA_VM(10); break;
+    case 18: BSA_VM(18); break;
+    default: BSA_VM(0); break;
+  }
+#undef BSA_VM
+}
+
 template <int D, int MODE>
 __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     const float* __restrict__ gates, const int* __restrict__ cnt_off,
-    const int* __restrict__ list, const int* __restrict__ work, const int* __restrict__ n_work,
-    float* __restrict__ part, int Hq, int Hkv, int G, int T, int NQB, int NB, int NA,
-    int max_work, float scale_log2) {
-  constexpr int KP = D + 8;
-  constexpr int C8 = D / 8;
-  constexpr int CPT = kBlock * C8 / 256;      // 16-byte chunks of one 64 x D tile per thread
-  constexpr int DT = D / 64;                  // 32-column d tiles per wave
-  __shared__ __attribute__((aligned(16))) bf16 Qs[2][kBlock * KP];
-  __shared__ __attribute__((aligned(16))) bf16 Os[2][kBlock * KP];
-  __shared__ __attribute__((aligned(16))) float Ls[2][kBlock];
-  __shared__ __attribute__((aligned(16))) float Ds[2][kBlock];
+    const int* __restrict__ chunk_off, const int* __restrict__ list, const int* __restrict__ work,
+    const int* __restrict__ n_work, float* __restrict__ part, bf16* __restrict__ dk,
+    bf16* __restrict__ dv, int Hq, int Hkv, int G, int T, int NQB, int NB, int NA, int max_work,
+    float scale_log2, float scale) {
+  constexpr int C = D / 8;                       // 16-byte chunks per row
+  constexpr int TILE_B = kBlock * D * 2;         // bytes of one 64 x D bf16 tile
+  constexpr int CPW = TILE_B / 16 / 256;         // copies of one tile per wave and step
+  constexpr int NPS = 2 * CPW + 1;               // copy instructions per wave and step
+  constexpr int STAGE_B = 2 * TILE_B + 4 * kBlock * 4;
+  constexpr int DT = D / 32;                     // 32-column d tiles
+  static_assert(NPS == 5 || NPS == 9, "copy counts must match bwd_wait_copies");
+  __shared__ __attribute__((aligned(16))) char smem[kBwdStages * STAGE_B];
+  __shared__ int Ec[kBwdChunk];
+  __shared__ float Eg[kBwdChunk];
 
   const int g = blockIdx.y, b = blockIdx.z;
   const int bg = b * Hkv + g;
   const int wi = blockIdx.x;
-  if (wi >= n_work[bg]) return;                 // whole workgroup, before any barrier
+  if (wi >= n_work[bg]) return;                  // whole workgroup, before any barrier
   const int item = work[(size_t)bg * max_work + wi];
   const int j = item & 0xffff, ch = item >> 16;
   const int* co = cnt_off + (size_t)bg * (NB + 1);
   const int e0 = co[j] + ch * kBwdChunk;
-  const int e1 = min(co[j + 1], e0 + kBwdChunk);
+  const int ne = min(co[j + 1] - e0, kBwdChunk);
+  const int nch = chunk_off[(size_t)bg * (NB + 1) + j + 1] - chunk_off[(size_t)bg * (NB + 1) + j];
   const int* lst = list + (size_t)bg * NQB * NA;
 
   const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
   const int half = lane / 32, l32 = lane % 32;
-  const int kh = w % 2, dh = w / 2;
-  const int ku = j * kBlock + kh * 32 + l32;   // this lane's key (the n index of S)
+  const int kh = w % 2, th = w / 2;
+  const int ku = j * kBlock + kh * 32 + l32;     // this lane's key (the n index of S)
   const size_t kvbase = (size_t)bg * T * D;
 
+  if (tid < ne) {
+    const int ent = lst[e0 + tid];
+    const int c = ent / NA;
+    Ec[tid] = c;
+    Eg[tid] = MODE == 1 ? gates[((size_t)bg * NQB + c) * NA + ent % NA] : 0.0f;
+  }
   // K_j and V_j rows of this wave's keys as B fragments: B[k = d][n = key]
   bf16x8 kb[D / 16], vb[D / 16];
   {
@@ -450,139 +496,172 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
       kb[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(k + kvbase + (size_t)tok * D + 16 * s + 8 * half));
       vb[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(v + kvbase + (size_t)tok * D + 16 * s + 8 * half));
     }
+    // keep these loads ahead of the first copy: the copy waits below count copies only
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) asm volatile("" : "+v"(kb[s]), "+v"(vb[s]));
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0)
+  __syncthreads();
+
+  const int nsteps = ne * G;
+  const uint32_t smem_lds = lds_addr_of(smem);
+  auto issue = [&](int st) {
+    const int c = Ec[st / G];
+    const int h = g * G + st % G;
+    const int rmax = T - 1 - c * kBlock;         // last valid row of this query block
+    const size_t row0 = (size_t)(b * Hq + h) * T + (size_t)c * kBlock;
+    const char* qg = reinterpret_cast<const char*>(q + row0 * D);
+    const char* og = reinterpret_cast<const char*>(dout + row0 * D);
+    const uint32_t st_lds = smem_lds + (uint32_t)((st % kBwdStages) * STAGE_B);
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      const int slot = (i * 4 + w) * kWave + lane;
+      const int row = slot / C, pc = slot % C;
+      const uint32_t voff = (uint32_t)(min(row, rmax) * (D * 2) + ((pc ^ bwd_swz<D>(row)) * 16));
+      const uint32_t la = st_lds + (uint32_t)((i * 4 + w) * kWave * 16);
+      dma_lds<16>(qg, voff, la);
+      dma_lds<16>(og, voff, la + TILE_B);
+    }
+    // lse (waves 0, 2) and Delta (waves 1, 3); waves 2 and 3 fill a second, unused copy so that
+    // every wave issues the same number of copies per step
+    const float* src = (w % 2 == 0) ? lse : delta;
+    dma_lds<4>(reinterpret_cast<const char*>(src + row0), (uint32_t)(min(lane, rmax) * 4),
+               st_lds + 2 * TILE_B + (uint32_t)(w * kBlock * 4));
+  };
+
   f32x16 dka[DT], dva[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) dka[dt][i] = dva[dt][i] = 0.0f;
 
-  // step s = (entry e0 + s / G, head s % G)
-  const int nsteps = (e1 - e0) * G;
-  u32x4 qreg[CPT], oreg[CPT];
-  float lreg = 0.0f, dreg = 0.0f;
-  auto step_c = [&](int st) { return lst[e0 + st / G] / NA; };
-  auto load_step = [&](int st) {
-    const int c = step_c(st);
-    const int h = g * G + st % G;
-    const size_t base = (size_t)(b * Hq + h) * T;
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int ci = tid + i * 256;
-      const int row = ci / C8, c8 = ci % C8;
-      const int tok = min(c * kBlock + row, T - 1);
-      qreg[i] = *reinterpret_cast<const u32x4*>(q + (base + tok) * D + c8 * 8);
-      oreg[i] = *reinterpret_cast<const u32x4*>(dout + (base + tok) * D + c8 * 8);
-    }
-    if (tid < kBlock) {
-      const int tok = min(c * kBlock + tid, T - 1);
-      lreg = lse[base + tok] * kLog2e;
-      dreg = delta[base + tok];
-    }
-  };
-  auto store_step = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int ci = tid + i * 256;
-      const int row = ci / C8, c8 = ci % C8;
-      *reinterpret_cast<u32x4*>(&Qs[buf][row * KP + c8 * 8]) = qreg[i];
-      *reinterpret_cast<u32x4*>(&Os[buf][row * KP + c8 * 8]) = oreg[i];
-    }
-    if (tid < kBlock) {
-      Ls[buf][tid] = lreg;
-      Ds[buf][tid] = dreg;
-    }
-  };
-
   const int vrow = (lane % 16) / 4;
   const int vcol = 16 * ((lane / 16) % 2) + 4 * (lane % 4);
-  if (nsteps > 0) {
-    load_step(0);
-    store_step(0);
-    if (nsteps > 1) load_step(1);
-  }
-  __syncthreads();
+  for (int s = 0; s < kBwdAhead; ++s)
+    if (s < nsteps) issue(s);
   for (int st = 0; st < nsteps; ++st) {
-    const int buf = st & 1;
-    const int ent = lst[e0 + st / G];
-    const int c = ent / NA;
-    const float gb = MODE == 1 ? gates[((size_t)bg * NQB + c) * NA + ent % NA] : 0.0f;
-    const bf16* Qb = Qs[buf];
-    const bf16* Ob = Os[buf];
-    // S = Q K^T and dP = dO V^T for the 64 rows of query block c and this wave's 32 keys
-    f32x16 s2[2], p2[2];
+    bwd_wait_copies(NPS * (min(nsteps - 1, st + kBwdAhead - 1) - st));
+    __syncthreads();
+    if (st + kBwdAhead < nsteps) issue(st + kBwdAhead);
+    const char* stg = smem + (st % kBwdStages) * STAGE_B;
+    const bf16* Qb = reinterpret_cast<const bf16*>(stg);
+    const bf16* Ob = reinterpret_cast<const bf16*>(stg + TILE_B);
+    const float* Lb = reinterpret_cast<const float*>(stg + 2 * TILE_B);
+    const float* Db = Lb + kBlock;
+    const int c = Ec[st / G];
+    const float gb = Eg[st / G];
+    // S = Q K^T and dP = dO V^T for rows th*32..+32 and this wave's 32 keys
+    f32x16 sa, pa;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+    for (int i = 0; i < 16; ++i) sa[i] = pa[i] = 0.0f;
+    const int arow = th * 32 + l32;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s2[tt][i] = p2[tt][i] = 0.0f;
+    for (int s = 0; s < D / 16; ++s) {
+      const int off = bwd_tile_off<D>(arow, 16 * s + 8 * half);
+      const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&Qb[off]);
+      const bf16x8 oa = *reinterpret_cast<const bf16x8*>(&Ob[off]);
+      sa = mfma32(qa, kb[s], sa);
+      pa = mfma32(oa, vb[s], pa);
+    }
+    // P and dx; register i holds row t = th*32 + 8 (i / 4) + 4 half + i % 4
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        const int off = (tt * 32 + l32) * KP + 16 * s + 8 * half;
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&Qb[off]);
-        const bf16x8 oa = *reinterpret_cast<const bf16x8*>(&Ob[off]);
-        s2[tt] = mfma32(qa, kb[s], s2[tt]);
-        p2[tt] = mfma32(oa, vb[s], p2[tt]);
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int t0 = th * 32 + 8 * i4 + 4 * half;
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&Lb[t0]);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Db[t0]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int tq = c * kBlock + t0 + e;
+        const bool vis = tq < T && ku <= tq;
+        const float p = vis ? fast_exp2(fmaf(sa[4 * i4 + e], scale_log2, gb - l4[e] * kLog2e)) : 0.0f;
+        sa[4 * i4 + e] = p;
+        pa[4 * i4 + e] = p * (pa[4 * i4 + e] - d4[e]);
       }
     }
-    // P and dx; register i of t-tile tt holds row t = 32 tt + 8 (i / 4) + 4 half + i % 4
+    // dV^T += dO^T P and dK^T += Q^T dx over this wave's 32 rows (2 k-steps of 16)
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int t0 = tt * 32 + 8 * i4 + 4 * half;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&Ls[buf][t0]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Ds[buf][t0]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int tq = c * kBlock + t0 + e;
-          const bool vis = tq < T && ku <= tq;
-          const float p = vis ? fast_exp2(fmaf(s2[tt][4 * i4 + e], scale_log2, gb - l4[e])) : 0.0f;
-          s2[tt][4 * i4 + e] = p;
-          p2[tt][4 * i4 + e] = p * (p2[tt][4 * i4 + e] - d4[e]);
-        }
-      }
-    // dV^T += dO^T P and dK^T += Q^T dx over the 64 rows (4 k-steps of 16), this wave's d tiles
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < 2; ++ks) {
       bf16x8 pb, xb;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        pb[e] = f2bf(s2[ks / 2][8 * (ks % 2) + e]);
-        xb[e] = f2bf(p2[ks / 2][8 * (ks % 2) + e]);
+        pb[e] = f2bf(sa[8 * ks + e]);
+        xb[e] = f2bf(pa[8 * ks + e]);
       }
-      const int r0 = 16 * ks + 4 * half + vrow;
+      const int r0 = th * 32 + 16 * ks + 4 * half + vrow;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const int col = (dh * DT + dt) * 32 + vcol;
-        const i16x4 o0 = lds_read_tr16(Ob + r0 * KP + col);
-        const i16x4 o1 = lds_read_tr16(Ob + (r0 + 8) * KP + col);
-        const i16x4 q0 = lds_read_tr16(Qb + r0 * KP + col);
-        const i16x4 q1 = lds_read_tr16(Qb + (r0 + 8) * KP + col);
+        const int col = dt * 32 + vcol;
+        const i16x4 o0 = lds_read_tr16(Ob + bwd_tile_off<D>(r0, col));
+        const i16x4 o1 = lds_read_tr16(Ob + bwd_tile_off<D>(r0 + 8, col));
+        const i16x4 q0 = lds_read_tr16(Qb + bwd_tile_off<D>(r0, col));
+        const i16x4 q1 = lds_read_tr16(Qb + bwd_tile_off<D>(r0 + 8, col));
         const bf16x8 ao = __builtin_bit_cast(bf16x8, __builtin_shufflevector(o0, o1, 0, 1, 2, 3, 4, 5, 6, 7));
         const bf16x8 aq = __builtin_bit_cast(bf16x8, __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7));
         dva[dt] = mfma32(ao, pb, dva[dt]);
         dka[dt] = mfma32(aq, xb, dka[dt]);
       }
     }
-    if (st + 1 < nsteps) store_step(buf ^ 1);
-    if (st + 2 < nsteps) load_step(st + 2);
-    __syncthreads();
   }
-  // partial tiles, layout [d][key]: dK^T then dV^T
-  float* pt = part + ((size_t)bg * max_work + wi) * 2 * kBlock * D;
+  __syncthreads();   // stages free (the last wait was vmcnt(0))
+
+  // sum the two row halves: waves th = 1 hand their accumulators to waves th = 0
+  float* red = reinterpret_cast<float*>(smem);
+  constexpr int RED = 2 * DT * 16 * kWave;       // floats per key half
+  if (th == 1) {
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int d = (dh * DT + dt) * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-      const int u = kh * 32 + l32;
-      pt[d * kBlock + u] = dka[dt][i];
-      pt[kBlock * D + d * kBlock + u] = dva[dt][i];
+      for (int i = 0; i < 16; ++i) {
+        red[kh * RED + (dt * 16 + i) * kWave + lane] = dka[dt][i];
+        red[kh * RED + ((DT + dt) * 16 + i) * kWave + lane] = dva[dt][i];
+      }
+  }
+  __syncthreads();
+  constexpr int FP = D + 4;                      // row pitch (floats) of the [key][d] tiles
+  float* F = red + 2 * RED;                      // [2][64][FP]: dK then dV
+  if (th == 0) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int d = dt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+        const int u = kh * 32 + l32;
+        F[u * FP + d] = dka[dt][i] + red[kh * RED + (dt * 16 + i) * kWave + lane];
+        F[kBlock * FP + u * FP + d] = dva[dt][i] + red[kh * RED + ((DT + dt) * 16 + i) * kWave + lane];
+      }
+  }
+  __syncthreads();
+  // write: bf16 dk, dv when this is the key block's only work item, else a float32 partial
+  constexpr int ITEMS = 2 * kBlock * C;          // (which, key, 8 columns)
+  for (int it = tid; it < ITEMS; it += 256) {
+    const int which = it / (kBlock * C);
+    const int u = (it / C) % kBlock, c8 = it % C;
+    const float* src = F + which * kBlock * FP + u * FP + c8 * 8;
+    const f32x4 a0 = *reinterpret_cast<const f32x4*>(src);
+    const f32x4 a1 = *reinterpret_cast<const f32x4*>(src + 4);
+    if (nch == 1) {
+      const int tok = j * kBlock + u;
+      if (tok < T) {
+        const float sc = which == 0 ? scale : 1.0f;
+        bf16x8 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o[e] = f2bf(a0[e] * sc);
+          o[4 + e] = f2bf(a1[e] * sc);
+        }
+        bf16* dst = which == 0 ? dk : dv;
+        *reinterpret_cast<bf16x8*>(dst + kvbase + (size_t)tok * D + c8 * 8) = o;
+      }
+    } else {
+      float* pt = part + (((size_t)bg * max_work + wi) * 2 + which) * kBlock * D + u * D + c8 * 8;
+      *reinterpret_cast<f32x4*>(pt) = a0;
+      *reinterpret_cast<f32x4*>(pt + 4) = a1;
     }
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
-// dk, dv of one key block: its work items' partials summed in order
+// dk, dv of a key block with several work items (or none): partials summed in order
 // ---------------------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict__ part,
@@ -590,26 +669,32 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict
                                                          bf16* __restrict__ dk,
                                                          bf16* __restrict__ dv, int Hkv, int T,
                                                          int NB, int max_work, float scale) {
-  __shared__ float tile[kBlock * (D + 1)];
+  constexpr int C = D / 8;
   const int j = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int bg = b * Hkv + g;
   const int c0 = chunk_off[(size_t)bg * (NB + 1) + j];
   const int c1 = chunk_off[(size_t)bg * (NB + 1) + j + 1];
-  for (int which = 0; which < 2; ++which) {
-    for (int e = threadIdx.x; e < kBlock * D; e += 256) {   // e = d * 64 + key
-      float s = 0.0f;
-      for (int ch = c0; ch < c1; ++ch) s += part[((size_t)bg * max_work + ch) * 2 * kBlock * D + which * kBlock * D + e];
-      const int d = e / kBlock, u = e % kBlock;
-      tile[u * (D + 1) + d] = which == 0 ? s * scale : s;
+  if (c1 - c0 == 1) return;                      // written by its only work item
+  for (int it = threadIdx.x; it < 2 * kBlock * C; it += 256) {
+    const int which = it / (kBlock * C);
+    const int u = (it / C) % kBlock, c8 = it % C;
+    const int tok = j * kBlock + u;
+    if (tok >= T) continue;
+    f32x4 a0 = {0.0f, 0.0f, 0.0f, 0.0f}, a1 = a0;
+    for (int chn = c0; chn < c1; ++chn) {
+      const float* pt = part + (((size_t)bg * max_work + chn) * 2 + which) * kBlock * D + u * D + c8 * 8;
+      a0 += *reinterpret_cast<const f32x4*>(pt);
+      a1 += *reinterpret_cast<const f32x4*>(pt + 4);
     }
-    __syncthreads();
+    const float sc = which == 0 ? scale : 1.0f;
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      o[e] = f2bf(a0[e] * sc);
+      o[4 + e] = f2bf(a1[e] * sc);
+    }
     bf16* dst = which == 0 ? dk : dv;
-    for (int e = threadIdx.x; e < kBlock * D; e += 256) {   // e = key * D + d
-      const int u = e / D, d = e % D;
-      const int tok = j * kBlock + u;
-      if (tok < T) dst[((size_t)bg * T + tok) * D + d] = f2bf(tile[u * (D + 1) + d]);
-    }
-    __syncthreads();
+    *reinterpret_cast<bf16x8*>(dst + ((size_t)bg * T + tok) * D + c8 * 8) = o;
   }
 }
 
@@ -697,8 +782,9 @@ static hipError_t launch_backward_d(const Shape& s, const void* q, const void* k
 #define BSA_KV(MODE)                                                                            \
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, MODE>), dim3(mw, s.Hkv, s.B), dim3(256), 0, st,        \
                      (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, lse,     \
-                     W.delta, W.gates, W.cnt_off, W.list, W.work, W.n_work, W.part, s.Hq, s.Hkv, \
-                     s.G, s.Tq, s.R, s.NB, s.NA, mw, sl2)
+                     W.delta, W.gates, W.cnt_off, W.chunk_off, W.list, W.work, W.n_work, W.part, \
+                     (bf16*)dk, (bf16*)dv, s.Hq, s.Hkv, s.G, s.Tq, s.R, s.NB, s.NA, mw, sl2,     \
+                     s.scale)
   if (s.mode == 1) BSA_KV(1);
   else BSA_KV(0);
 #undef BSA_KV
