@@ -550,32 +550,62 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     const float* Db = Lb + kBlock;
     const int c = Ec[st / G];
     const float gb = Eg[st / G];
+    // LDS fragments of the step, ordered for a single wave per SIMD: the A operands of S and dP
+    // and the row statistics first, then the transposed operands of dV and dK interleaved with
+    // the S and dP products so that their latency hides behind the matrix work
+    const int arow = th * 32 + l32;
+    bf16x8 qa[D / 16], oa[D / 16];
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      const int off = bwd_tile_off<D>(arow, 16 * s + 8 * half);
+      qa[s] = *reinterpret_cast<const bf16x8*>(&Qb[off]);
+      oa[s] = *reinterpret_cast<const bf16x8*>(&Ob[off]);
+    }
+    const int tb = th * 32 + 4 * half;
+    f32x4 l4[4], d4[4];
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      l4[i4] = *reinterpret_cast<const f32x4*>(&Lb[tb + 8 * i4]);
+      d4[i4] = *reinterpret_cast<const f32x4*>(&Db[tb + 8 * i4]);
+    }
     // S = Q K^T and dP = dO V^T for rows th*32..+32 and this wave's 32 keys
     f32x16 sa, pa;
 #pragma unroll
     for (int i = 0; i < 16; ++i) sa[i] = pa[i] = 0.0f;
-    const int arow = th * 32 + l32;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
-      const int off = bwd_tile_off<D>(arow, 16 * s + 8 * half);
-      const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&Qb[off]);
-      const bf16x8 oa = *reinterpret_cast<const bf16x8*>(&Ob[off]);
-      sa = mfma32(qa, kb[s], sa);
-      pa = mfma32(oa, vb[s], pa);
+      sa = mfma32(qa[s], kb[s], sa);
+      pa = mfma32(oa[s], vb[s], pa);
+    }
+    i16x4 tr[2][DT][4];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int r0 = th * 32 + 16 * ks + 4 * half + vrow;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int col = dt * 32 + vcol;
+        tr[ks][dt][0] = lds_read_tr16(Ob + bwd_tile_off<D>(r0, col));
+        tr[ks][dt][1] = lds_read_tr16(Ob + bwd_tile_off<D>(r0 + 8, col));
+        tr[ks][dt][2] = lds_read_tr16(Qb + bwd_tile_off<D>(r0, col));
+        tr[ks][dt][3] = lds_read_tr16(Qb + bwd_tile_off<D>(r0 + 8, col));
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, D / 8 + 8, 0);     // A operands, lse, Delta
+#pragma unroll
+    for (int s = 0; s < D / 8; ++s) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // one S or dP product
+      __builtin_amdgcn_sched_group_barrier(0x100, DT, 0);          // DT transposed reads
     }
     // P and dx; register i holds row t = th*32 + 8 (i / 4) + 4 half + i % 4
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
-      const int t0 = th * 32 + 8 * i4 + 4 * half;
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&Lb[t0]);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Db[t0]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int tq = c * kBlock + t0 + e;
+        const int tq = c * kBlock + tb + 8 * i4 + e;
         const bool vis = tq < T && ku <= tq;
-        const float p = vis ? fast_exp2(fmaf(sa[4 * i4 + e], scale_log2, gb - l4[e] * kLog2e)) : 0.0f;
+        const float p = vis ? fast_exp2(fmaf(sa[4 * i4 + e], scale_log2, gb - l4[i4][e] * kLog2e)) : 0.0f;
         sa[4 * i4 + e] = p;
-        pa[4 * i4 + e] = p * (pa[4 * i4 + e] - d4[e]);
+        pa[4 * i4 + e] = p * (pa[4 * i4 + e] - d4[i4][e]);
       }
     }
     // dV^T += dO^T P and dK^T += Q^T dx over this wave's 32 rows (2 k-steps of 16)
@@ -587,16 +617,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
         pb[e] = f2bf(sa[8 * ks + e]);
         xb[e] = f2bf(pa[8 * ks + e]);
       }
-      const int r0 = th * 32 + 16 * ks + 4 * half + vrow;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const int col = dt * 32 + vcol;
-        const i16x4 o0 = lds_read_tr16(Ob + bwd_tile_off<D>(r0, col));
-        const i16x4 o1 = lds_read_tr16(Ob + bwd_tile_off<D>(r0 + 8, col));
-        const i16x4 q0 = lds_read_tr16(Qb + bwd_tile_off<D>(r0, col));
-        const i16x4 q1 = lds_read_tr16(Qb + bwd_tile_off<D>(r0 + 8, col));
-        const bf16x8 ao = __builtin_bit_cast(bf16x8, __builtin_shufflevector(o0, o1, 0, 1, 2, 3, 4, 5, 6, 7));
-        const bf16x8 aq = __builtin_bit_cast(bf16x8, __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7));
+        const bf16x8 ao = __builtin_bit_cast(bf16x8, __builtin_shufflevector(tr[ks][dt][0], tr[ks][dt][1], 0, 1, 2, 3, 4, 5, 6, 7));
+        const bf16x8 aq = __builtin_bit_cast(bf16x8, __builtin_shufflevector(tr[ks][dt][2], tr[ks][dt][3], 0, 1, 2, 3, 4, 5, 6, 7));
         dva[dt] = mfma32(ao, pb, dva[dt]);
         dka[dt] = mfma32(aq, xb, dka[dt]);
       }
