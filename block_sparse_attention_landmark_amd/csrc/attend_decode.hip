@@ -54,6 +54,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void attend_decode_bf16_kernel(
   __shared__ __attribute__((aligned(16))) bf16 Ks[kDecodeWaves][kBlock * D];
   __shared__ __attribute__((aligned(16))) bf16 Vs[kDecodeWaves][kBlock * D];
   __shared__ float comb_ml[kDecodeWaves][32][2];
+  __shared__ __attribute__((aligned(16))) bf16 Ls[kDecodeWaves][128];   // HiLS: landmark row
 
   const int split = blockIdx.x;
   const int g = blockIdx.y;
@@ -96,6 +97,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void attend_decode_bf16_kernel(
   const int nval = count_valid(irow, NA);
   bf16* kt_ = Ks[w];
   bf16* vt = Vs[w];
+  const uint32_t k_lds = lds_addr_of(kt_), v_lds = lds_addr_of(vt), l_lds = lds_addr_of(Ls[w]);
   const int vrow = (lane % 16) / 4;
   const int vcol = 16 * ((lane / 16) % 2) + 4 * (lane % 4);
 
@@ -106,54 +108,85 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void attend_decode_bf16_kernel(
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
 
-  // entry of iteration it, or -1
-  auto entry = [&](int it) {
-    const int a = split * kDecodeWaves * bpw + w + kDecodeWaves * it;
-    const int j = (it < bpw && a < nval) ? irow[a] : -1;
-    return (j >= 0 && j <= c) ? j : -1;
+  // This wave's entries: a = a0 + waves * it for it < n_it.  They are held one per lane, 64 at a
+  // time (block index and SAS gate), and read with readlane, so the loop below issues no memory
+  // loads besides the tile copies: the only copy wait is the full one at the top of an iteration.
+  const int a0 = split * kDecodeWaves * bpw + w;
+  const int n_it = a0 < nval ? min(bpw, (nval - a0 + kDecodeWaves - 1) / kDecodeWaves) : 0;
+  const float s_ref = (MODE == 1 && nval > 0) ? srow[nval - 1] : 0.0f;
+  int ej = -1;
+  float eg = 0.0f;
+  auto load_batch = [&](int base) {
+    const int it = base + lane;
+    int jv = -1;
+    float gv = 0.0f;
+    if (it < n_it) {
+      const int a = a0 + kDecodeWaves * it;
+      jv = irow[a];
+      if (jv < 0 || jv > c) jv = -1;
+      else if (MODE == 1 && jv != c) gv = log_sigmoid(srow[a] - s_ref) * kLog2e;
+    }
+    ej = jv;
+    eg = gv;
   };
   // copy the K (or V) rows of block j into this wave's tile, 1 KB per instruction (rows past
-  // the cache end read its last row; their probabilities are zero)
+  // the cache end read its last row; their probabilities are zero); HiLS also copies the
+  // block's landmark row beside the K tile
   auto copy_k = [&](int j) {
-    const size_t base = block_at(j);
+    const char* base = reinterpret_cast<const char*>(kc + block_at(j));
 #pragma unroll
     for (int n = 0; n < kBlock / RPI; ++n) {
       const int row = n * RPI + lane / C16;
       const int r = min(row, Tk - 1 - j * kBlock);
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(kc + base + (size_t)r * D +
-                                                          ((lane % C16) ^ swzk(row)) * 8),
-          (__attribute__((address_space(3))) void*)(kt_ + n * RPI * D), 16, 0, 0);
+      dma_lds<16>(base, (uint32_t)((r * D + ((lane % C16) ^ swzk(row)) * 8) * 2),
+                  k_lds + (uint32_t)(n * RPI * D * 2));
+    }
+    if constexpr (MODE == 2) {
+      const char* lrow = reinterpret_cast<const char*>(lm + ((size_t)(b * Hkv + g) * NB + j) * D);
+      dma_lds<4>(lrow, (uint32_t)((lane % (D / 2)) * 4), l_lds);
     }
   };
   auto copy_v = [&](int j) {
-    const size_t base = block_at(j);
+    const char* base = reinterpret_cast<const char*>(vc + block_at(j));
 #pragma unroll
     for (int n = 0; n < kBlock / RPI; ++n) {
       const int row = n * RPI + lane / C16;
       const int r = min(row, Tk - 1 - j * kBlock);
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(vc + base + (size_t)r * D +
-                                                          ((lane % C16) ^ swz(row)) * 8),
-          (__attribute__((address_space(3))) void*)(vt + n * RPI * D), 16, 0, 0);
+      dma_lds<16>(base, (uint32_t)((r * D + ((lane % C16) ^ swz(row)) * 8) * 2),
+                  v_lds + (uint32_t)(n * RPI * D * 2));
     }
   };
 
-  // find the first valid entry and start its copies
-  int it0 = 0;
-  int j = entry(0);
-  while (j < 0 && it0 + 1 < bpw) j = entry(++it0);
+  load_batch(0);
+  int j = n_it > 0 ? __builtin_amdgcn_readlane(ej, 0) : -1;
+  float gate2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(eg), 0));
   if (j >= 0) {
     copy_k(j);
     copy_v(j);
   }
-  for (int it = it0; it < bpw && j >= 0; ) {
-    const int a = split * kDecodeWaves * bpw + w + kDecodeWaves * it;
-    // next valid entry: its copies start as soon as this block's tiles are read
-    int it_next = it + 1;
-    int jn = entry(it_next);
-    while (jn < 0 && it_next + 1 < bpw) jn = entry(++it_next);
-    __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): both tiles of block j have landed
+  for (int it = 0; it < n_it; ++it) {
+    // the next entry (the held batch is reloaded at a 64-entry boundary: a full wait, rare)
+    int jn = -1;
+    float gn = 0.0f;
+    if (it + 1 < n_it) {
+      if (((it + 1) & 63) == 0) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        load_batch(it + 1);
+      }
+      jn = __builtin_amdgcn_readlane(ej, (it + 1) & 63);
+      gn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(eg), (it + 1) & 63));
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): the tiles of block j have landed
+    if (j < 0) {
+      // an entry outside the causal range: nothing to attend; keep the copy stream going
+      if (jn >= 0) {
+        copy_k(jn);
+        copy_v(jn);
+      }
+      j = jn;
+      gate2 = gn;
+      continue;
+    }
     // S^T = K Q^T with K fragments (key kt*32 + l32, dims 16s + 8*half .. +8) read from LDS
     bf16x8 kf[2][D / 16];
 #pragma unroll
@@ -162,6 +195,18 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void attend_decode_bf16_kernel(
 #pragma unroll
       for (int s = 0; s < D / 16; ++s)
         kf[kt][s] = *reinterpret_cast<const bf16x8*>(kt_ + row * D + (((2 * s + half) ^ swzk(row)) * 8));
+    }
+    float r2 = 0.0f;
+    if constexpr (MODE == 2) {
+      // retrieval score q . L_j of this lane's row, log2 units
+      float part = 0.0f;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        const bf16x8 lv = *reinterpret_cast<const bf16x8*>(&Ls[w][16 * s + 8 * half]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part += bf2f(qf[s][e]) * bf2f(lv[e]);
+      }
+      r2 = wave_sum_xor32(part) * scale_log2;
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): the K tile may be overwritten
     if (jn >= 0) copy_k(jn);
@@ -195,15 +240,6 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void attend_decode_bf16_kernel(
           st[kt][i] = e;
           lsum += e;
         }
-      const bf16* lrow = lm + ((size_t)(b * Hkv + g) * NB + j) * D;
-      float part = 0.0f;
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        const bf16x8 lv = *reinterpret_cast<const bf16x8*>(lrow + 16 * s + 8 * half);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) part += bf2f(qf[s][e]) * bf2f(lv[e]);
-      }
-      const float r2 = wave_sum_xor32(part) * scale_log2;     // retrieval score, log2 units
       const float m_new = fmaxf(m_run, r2);
       alpha = fast_exp2(m_run - m_new);
       const float wr = fast_exp2(r2 - m_new);
@@ -211,8 +247,6 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void attend_decode_bf16_kernel(
       m_run = m_new;
       coef = wr / wave_sum_xor32(lsum);
     } else {
-      float gate2 = 0.0f;
-      if (MODE == 1 && j != c) gate2 = log_sigmoid(srow[a] - srow[nval - 1]) * kLog2e;
       const float m_new = fmaxf(m_run, fmaf(mx, scale_log2, gate2));
       alpha = fast_exp2(m_run - m_new);
       m_run = m_new;
@@ -258,8 +292,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void attend_decode_bf16_kernel(
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) o[dt] = mfma32(vf[ks][dt], pb, o[dt]);
     }
-    it = it_next;
     j = jn;
+    gate2 = gn;
   }
 
   // combine the waves' states (rows < G) through LDS (the K tiles are reused)

@@ -166,6 +166,8 @@ SMALL_DECODE = [
     ("tk1",      2, 4,  1,   1,           128, "bf16", 2,    "iid"),
     ("tk64",     1, 8,  1,   64,          128, "bf16", 2,    "iid"),
     ("kall",     1, 8,  1,   64 * 5,      128, "bf16", 50,   "iid"),
+    # 256 (sequence, kv head) pairs: one workgroup per pair walks all 73 attended blocks
+    ("many_blocks", 16, 16, 16, 64 * 80 + 5, 64, "bf16", 70,   "iid"),
     ("f32",      2, 4,  2,   64 * 6 + 9,  64,  "f32",  2,    "iid"),
     ("f32_d128", 1, 8,  1,   64 * 4,      128, "f32",  1,    "iid"),
 ]
@@ -197,6 +199,8 @@ PAGED_DECODE = [
     ("ragged_g4",   8,  2,   128, [1, 63, 64, 65, 64 * 20 + 7],      4,    "clustered"),
     ("ragged_d64",  16, 2,   64,  [640, 130, 64 * 33],               8,    "iid"),
     ("ragged_g32",  32, 1,   128, [5, 64 * 10 + 3],                  3,    "clustered"),
+    # 256 (sequence, kv head) pairs, up to 143 attended blocks per sequence
+    ("ragged_many", 16, 16,  64,  [64 * 150 - 577 * i for i in range(16)], 140, "iid"),
 ]
 
 
