@@ -42,5 +42,6 @@ from .bsa_oracle import (  # noqa: F401
     decode_paged,
     attend_rows_grad,
     sas_gates_grad,
+    hils_rows_grad,
     prefill_backward,
 )

@@ -32,9 +32,10 @@ What is computed, step by step, in the pages' order:
                   sequence is the contiguous decode step of its own tokens, read through its
                   page table (the serving layout; the pages say nothing of storage, so the
                   method is unchanged by it).
-9. backward    -- gradients of the PLAIN / SAS attention step for given attended sets: into q,
-                  k, v and into the selector scores through the SAS gates (the pages train the
-                  selector end to end through these gates).
+9. backward    -- gradients of the attention step for given attended sets: into q, k, v; for
+                  SAS into the selector scores through the gates (the pages train the selector
+                  end to end through these gates); for HiLS into the landmarks through the
+                  retrieval scores.
 
 Readings taken where the pages are silent (each is listed in the design notes):
 * the selector vector is kept in float64 here (float32 on the device), never rounded to bf16;
@@ -524,15 +525,67 @@ def sas_gates_grad(A, sA, c: int, dg) -> np.ndarray:
     return d
 
 
-def prefill_backward(q, k, v, idx, sc, dout, *, mode: str, block: int = BLOCK, scale=None):
-    """Backward of PLAIN / SAS prefill attention for the attended sets idx [B,Hkv,NQB,NA] and,
-    for SAS, the scores sc aligned with them (the gates are formed from sc).
+def hils_rows_grad(qrows, tpos, K, V, Lrows, A, scale: float, dout, block: int = BLOCK):
+    """Gradients of attend_hils_rows for one head's rows.
 
-    Returns dq [B,Hq,T,D], dk, dv [B,Hkv,T,D] and dsc [B,Hkv,NQB,NA] (zero for PLAIN and in the
-    padding).
+    With o_j the softmax attention of a row over the visible keys of chunk j alone,
+    w = softmax_j(scale * q . L_j) and o = sum_j w_j o_j (HiLS page, summary paragraph 2):
+      dw_j = dout . o_j,  dr_j = w_j (dw_j - sum_i w_i dw_i)  (softmax backward),
+      each chunk is a softmax attention with output gradient w_j dout,
+      dq = sum over chunks of the attention gradient + scale * sum_j dr_j L_j,
+      dL_j = scale * sum_rows dr_j q.
+    Returns dq [m,D], pos (attended key positions, ascending, each once), dK, dV [|pos|,D] and
+    dL [|A|,D] aligned with A.
     """
+    T, D = K.shape
+    m = qrows.shape[0]
+    tpos = np.asarray(tpos)
+    r = scale * (qrows @ Lrows.T)
+    w = np.exp(r - r.max(axis=1, keepdims=True))
+    w = w / w.sum(axis=1, keepdims=True)                               # [m, |A|]
+    pos, blk = _block_keys(A, T, block)
+    dq = np.zeros((m, D))
+    dK = np.zeros((pos.size, D))
+    dV = np.zeros((pos.size, D))
+    dw = np.zeros((m, len(A)))
+    chunks = []
+    for i, j in enumerate(A):
+        sel = np.nonzero(blk == int(j))[0]
+        keys = pos[sel]
+        logits = scale * (qrows @ K[keys].T)
+        logits = np.where(keys[None, :] <= tpos[:, None], logits, -np.inf)
+        e = np.exp(logits - logits.max(axis=1, keepdims=True))
+        P = e / e.sum(axis=1, keepdims=True)
+        o_j = P @ V[keys]
+        dw[:, i] = np.sum(dout * o_j, axis=1)
+        chunks.append((sel, keys, P, o_j))
+    dr = w * (dw - np.sum(w * dw, axis=1, keepdims=True))
+    dq += scale * (dr @ Lrows)
+    dL = scale * (dr.T @ qrows)
+    for i, (sel, keys, P, o_j) in enumerate(chunks):
+        dOj = w[:, i:i + 1] * dout
+        dP = dOj @ V[keys].T
+        dx = P * (dP - np.sum(dOj * o_j, axis=1, keepdims=True))
+        dq += scale * (dx @ K[keys])
+        dK[sel] += scale * (dx.T @ qrows)
+        dV[sel] += P.T @ dOj
+    return dq, pos, dK, dV, dL
+
+
+def prefill_backward(q, k, v, idx, sc, dout, *, mode: str, block: int = BLOCK, scale=None,
+                     lm=None):
+    """Backward of prefill attention for the attended sets idx [B,Hkv,NQB,NA]: for SAS the
+    scores sc aligned with them form the gates; for HiLS lm [B,Hkv,NB,D] are the landmarks the
+    forward used (its retrieval scores).
+
+    Returns dq [B,Hq,T,D], dk, dv [B,Hkv,T,D], dsc [B,Hkv,NQB,NA] (zero for PLAIN and HiLS and
+    in the padding) and, for HiLS, dlm [B,Hkv,NB,D] (the gradient of the landmark values; dk
+    does not include the pooling that produced them).
+    """
+    if mode == "hils":
+        return _hils_backward(q, k, v, idx, lm, dout, block=block, scale=scale)
     if mode not in ("plain", "sas"):
-        raise ValueError("backward is defined here for PLAIN and SAS")
+        raise ValueError("mode must be plain, sas or hils")
     B, Hq, T, D = q.shape
     Hkv = k.shape[1]
     G = Hq // Hkv
@@ -565,3 +618,32 @@ def prefill_backward(q, k, v, idx, sc, dout, *, mode: str, block: int = BLOCK, s
                 if mode == "sas":
                     dsc[b, g, c, valid] = sas_gates_grad(A, sA, c, dg)
     return {"dq": dq, "dk": dk, "dv": dv, "dsc": dsc}
+
+
+def _hils_backward(q, k, v, idx, lm, dout, *, block: int = BLOCK, scale=None):
+    B, Hq, T, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    sc_ = _default_scale(D, scale)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dlm = np.zeros(lm.shape)
+    for b in range(B):
+        for g in range(Hkv):
+            for c in range(idx.shape[2]):
+                A = np.array([int(j) for j in idx[b, g, c] if j >= 0], dtype=np.int64)
+                if A.size == 0:
+                    continue
+                lo, hi = c * block, min((c + 1) * block, T)
+                tpos = np.arange(lo, hi)
+                for hh in range(G):
+                    h = g * G + hh
+                    dq_h, pos, dK, dV, dL = hils_rows_grad(q[b, h, lo:hi], tpos, k[b, g], v[b, g],
+                                                          lm[b, g, A], A, sc_, dout[b, h, lo:hi],
+                                                          block)
+                    dq[b, h, lo:hi] += dq_h
+                    dk[b, g, pos] += dK
+                    dv[b, g, pos] += dV
+                    dlm[b, g, A] += dL
+    return {"dq": dq, "dk": dk, "dv": dv, "dsc": np.zeros(idx.shape), "dlm": dlm}

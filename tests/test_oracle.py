@@ -663,3 +663,93 @@ def test_backward_directional_finite_difference():
     an = sum(float(np.sum(g[n2] * dirs[n1])) for n1, n2 in (("q", "dq"), ("k", "dk"), ("v", "dv"),
                                                             ("sc", "dsc")))
     assert abs(fd - an) < 1e-6 * max(1.0, abs(an))
+
+
+def _torch_hils_loss(q, k, v, lm, idx, dout, scale, block=64):
+    """HiLS written densely in torch (float64): for each query block and head, one masked
+    softmax per attended chunk over the full key axis, merged with softmax(scale * q . L_j);
+    lm is a leaf so autograd reaches the landmarks.  Returns sum(O * dout)."""
+    B, Hq, T, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    loss = 0.0
+    keypos = torch.arange(T)
+    for b in range(B):
+        for g in range(Hkv):
+            for c in range(idx.shape[2]):
+                A = [int(j) for j in idx[b, g, c] if j >= 0]
+                lo, hi = c * block, min((c + 1) * block, T)
+                tpos = torch.arange(lo, hi)
+                for hh in range(G):
+                    h = g * G + hh
+                    qr = q[b, h, lo:hi]
+                    logits = scale * (qr @ k[b, g].T)                       # [m, T]
+                    r = scale * (qr @ lm[b, g, A].T)                        # [m, |A|]
+                    wts = torch.softmax(r, dim=-1)
+                    o = 0.0
+                    for i, j in enumerate(A):
+                        allowed = (keypos[None, :] // block == j) & (keypos[None, :] <= tpos[:, None])
+                        lj = torch.where(allowed, logits, torch.full_like(logits, float("-inf")))
+                        o = o + wts[:, i:i + 1] * (torch.softmax(lj, dim=-1) @ v[b, g])
+                    loss = loss + (o * dout[b, h, lo:hi]).sum()
+    return loss
+
+
+def test_hils_backward_matches_torch_autograd():
+    """HiLS oracle gradients (dq, dk, dv, d landmarks) = torch autograd of the dense per-chunk
+    formulation in float64 (partial last block, top-K smaller than the candidates)."""
+    r = _rng(43)
+    B, Hq, Hkv, T, D = 1, 4, 2, 64 * 5 + 23, 8
+    q = r.standard_normal((B, Hq, T, D))
+    k = O.round_to_dtype(r.standard_normal((B, Hkv, T, D)), "bf16")
+    v = r.standard_normal((B, Hkv, T, D))
+    dout = r.standard_normal((B, Hq, T, D))
+    fwd = O.prefill(q, k, v, topk=1, mode="hils", dtype="bf16")
+    idx = fwd["idx"]
+    lm = O.landmarks(k, "bf16") + 0.3 * r.standard_normal((B, Hkv, (T + 63) // 64, D))
+    scale = 1.0 / math.sqrt(D)
+    got = O.prefill_backward(q, k, v, idx, None, dout, mode="hils", scale=scale, lm=lm)
+    t = lambda a: torch.tensor(a, dtype=torch.float64, requires_grad=True)
+    tq, tk, tv, tl = t(q), t(k), t(v), t(lm)
+    loss = _torch_hils_loss(tq, tk, tv, tl, idx, torch.tensor(dout), scale)
+    loss.backward()
+    np.testing.assert_allclose(got["dq"], tq.grad.numpy(), atol=1e-11)
+    np.testing.assert_allclose(got["dk"], tk.grad.numpy(), atol=1e-11)
+    np.testing.assert_allclose(got["dv"], tv.grad.numpy(), atol=1e-11)
+    np.testing.assert_allclose(got["dlm"], tl.grad.numpy(), atol=1e-11)
+    assert not got["dsc"].any()
+
+
+def test_hils_backward_directional_finite_difference():
+    """Second HiLS pin, independent of torch: the directional derivative of sum(O * dout) along
+    a random direction in (q, k, v, landmarks) matches a central finite difference of the
+    oracle's HiLS forward."""
+    r = _rng(44)
+    B, Hq, Hkv, T, D = 1, 2, 1, 64 * 3 + 7, 4
+    q = r.standard_normal((B, Hq, T, D))
+    k = r.standard_normal((B, Hkv, T, D))
+    v = r.standard_normal((B, Hkv, T, D))
+    dout = r.standard_normal((B, Hq, T, D))
+    idx = O.prefill(q, k, v, topk=1, mode="hils", dtype="f32")["idx"]
+    lm = O.landmarks(k, "f32")
+    g = O.prefill_backward(q, k, v, idx, None, dout, mode="hils", lm=lm)
+    dirs = {n: r.standard_normal(a.shape) for n, a in (("q", q), ("k", k), ("v", v), ("lm", lm))}
+
+    def f(e):
+        qq, kk, vv, ll = (q + e * dirs["q"], k + e * dirs["k"], v + e * dirs["v"],
+                          lm + e * dirs["lm"])
+        total = 0.0
+        for c in range(idx.shape[2]):
+            A = np.array([j for j in idx[0, 0, c] if j >= 0])
+            lo, hi = 64 * c, min(64 * c + 64, T)
+            for h in range(Hq):
+                o = O.attend_hils_rows(qq[0, h, lo:hi], np.arange(lo, hi), kk[0, 0], vv[0, 0],
+                                       ll[0, 0, A], A, 1 / math.sqrt(D))
+                total += float(np.sum(o * dout[0, h, lo:hi]))
+        return total
+
+    eps = 1e-5
+    fd = (f(eps) - f(-eps)) / (2 * eps)
+    an = sum(float(np.sum(g[n2] * dirs[n1])) for n1, n2 in (("q", "dq"), ("k", "dk"), ("v", "dv"),
+                                                            ("lm", "dlm")))
+    assert abs(fd - an) < 1e-6 * max(1.0, abs(an))
