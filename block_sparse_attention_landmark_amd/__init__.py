@@ -11,7 +11,7 @@ Entry points mirror the C ABI in include/bsa.h:
 * ``select_topk(q, lm, topk=..., seq_k=...)``      -> (idx, sc)
 * ``attend_prefill(q, k, v, idx, sc, lm, mode)``  -> (out, lse)
 * ``attend_decode(q, kc, vc, idx, sc, lm, mode)`` -> (out, lse)
-* ``attend_prefill_backward(q, k, v, idx, sc, out, lse, dout, mode)`` -> (dq, dk, dv, dsc)
+* ``attend_prefill_backward(q, k, v, idx, sc, out, lse, dout, mode, lm)`` -> (dq, dk, dv, dsc, dlm)
 
 and ``prefill(q, k, v, ...)`` / ``decode(q, kc, vc, lm, ...)`` chain them.
 """
@@ -91,7 +91,7 @@ def load_library():
     lib.bsa_attend_decode_paged.restype = st
     lib.bsa_backward_workspace_bytes.argtypes = [P]
     lib.bsa_backward_workspace_bytes.restype = ctypes.c_size_t
-    lib.bsa_attend_prefill_backward.argtypes = [P] + [vp] * 13 + [ctypes.c_size_t, vp]
+    lib.bsa_attend_prefill_backward.argtypes = [P] + [vp] * 15 + [ctypes.c_size_t, vp]
     lib.bsa_attend_prefill_backward.restype = st
     lib.bsa_status_string.argtypes = [ctypes.c_int]
     lib.bsa_status_string.restype = ctypes.c_char_p
@@ -281,26 +281,31 @@ def backward_workspace_bytes(p: Params) -> int:
     return int(load_library().bsa_backward_workspace_bytes(ctypes.byref(p)))
 
 
-def attend_prefill_backward(q, k, v, idx, sc, out, lse, dout, *, mode="plain", topk=None,
+def attend_prefill_backward(q, k, v, idx, sc, out, lse, dout, *, mode="plain", lm=None, topk=None,
                             n_sink=1, n_local=2, scale=0.0, ws=None, dq=None, dk=None, dv=None,
-                            dsc=None):
-    """Gradients of PLAIN / SAS bf16 prefill attention given the forward's out and lse.
+                            dsc=None, dlm=None):
+    """Gradients of bf16 prefill attention given the forward's out (and lse for PLAIN / SAS).
 
-    Returns (dq [B,Hq,T,D], dk, dv [B,Hkv,T,D], dsc [B,Hkv,ceil(T/64),NA] float32); dsc is the
-    gradient with respect to the selector scores sc through the SAS gates (zeros for PLAIN).
+    Returns (dq [B,Hq,T,D], dk, dv [B,Hkv,T,D], dsc [B,Hkv,ceil(T/64),NA] float32, dlm): dsc is
+    the gradient with respect to the selector scores through the SAS gates (zeros otherwise);
+    dlm [B,Hkv,ceil(T/64),D] float32 is, for HiLS (which needs lm, the forward's landmarks), the
+    gradient with respect to the landmarks through the retrieval scores, else None.
     """
     lib = load_library()
     _need(q, "q", dtype=torch.bfloat16, ndim=4)
     for t, n in ((k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
         _need(t, n, dtype=q.dtype, ndim=4)
     _need(idx, "idx", dtype=torch.int32, ndim=4)
-    _need(lse, "lse", dtype=torch.float32, ndim=3)
     B, Hq, T, D = q.shape
     Hkv = k.shape[1]
     if k.shape != (B, Hkv, T, D) or v.shape != k.shape:
         raise ValueError("k and v must be [B,Hkv,T,D] matching q")
-    if out.shape != q.shape or dout.shape != q.shape or lse.shape != (B, Hq, T):
-        raise ValueError("out and dout must have q's shape and lse must be [B,Hq,T]")
+    if out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("out and dout must have q's shape")
+    if lse is not None:
+        _need(lse, "lse", dtype=torch.float32, ndim=3)
+        if lse.shape != (B, Hq, T):
+            raise ValueError("lse must be [B,Hq,T]")
     NA = idx.shape[-1]
     if topk is None:
         topk = NA - n_sink - n_local
@@ -310,6 +315,10 @@ def attend_prefill_backward(q, k, v, idx, sc, out, lse, dout, *, mode="plain", t
         _need(sc, "sc", dtype=torch.float32, ndim=4)
         if sc.shape != idx.shape:
             raise ValueError("sc must have idx's shape")
+    if lm is not None:
+        _need(lm, "lm", dtype=q.dtype, ndim=4)
+        if lm.shape != (B, Hkv, _nblocks(T), D):
+            raise ValueError("lm must be [B,Hkv,ceil(T/64),D]")
     p = make_params(B=B, Hq=Hq, Hkv=Hkv, D=D, seq_q=T, seq_k=T, dtype=q.dtype, topk=topk,
                     n_sink=n_sink, n_local=n_local, scale=scale, mode=mode)
     if dq is None:
@@ -320,21 +329,25 @@ def attend_prefill_backward(q, k, v, idx, sc, out, lse, dout, *, mode="plain", t
         dv = torch.empty_like(v)
     if dsc is None:
         dsc = torch.empty(idx.shape, dtype=torch.float32, device=q.device)
+    if mode == "hils" and dlm is None:
+        dlm = torch.empty((B, Hkv, _nblocks(T), D), dtype=torch.float32, device=q.device)
     _need(dq, "dq", dtype=q.dtype, ndim=4)
     _need(dk, "dk", dtype=q.dtype, ndim=4)
     _need(dv, "dv", dtype=q.dtype, ndim=4)
     _need(dsc, "dsc", dtype=torch.float32, ndim=4)
+    if dlm is not None:
+        _need(dlm, "dlm", dtype=torch.float32, ndim=4)
     need = backward_workspace_bytes(p)
     if need == 0:
         need = 256    # the call itself reports why the shape is rejected
     if ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     _check("bsa_attend_prefill_backward",
-           lib.bsa_attend_prefill_backward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(idx),
-                                           _ptr(sc), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq),
-                                           _ptr(dk), _ptr(dv), _ptr(dsc), _ptr(ws), ws.numel(),
-                                           _stream(q.device)))
-    return dq, dk, dv, dsc
+           lib.bsa_attend_prefill_backward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(lm),
+                                           _ptr(idx), _ptr(sc), _ptr(out), _ptr(lse), _ptr(dout),
+                                           _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dsc), _ptr(dlm),
+                                           _ptr(ws), ws.numel(), _stream(q.device)))
+    return dq, dk, dv, dsc, (dlm if mode == "hils" else None)
 
 
 # ---------------------------------------------------------------------------------------------

@@ -53,6 +53,9 @@ struct BwdWs {
   int* n_work;    // [B*Hkv]
   int* list;      // [B*Hkv, R * NA]: c * NA + pos, grouped by key block
   float* part;    // [B*Hkv, max_work, 2, 64, D]: dK then dV partial tiles (unscaled)
+  float* hstat;   // HiLS: 3 x [B, Hq, R, NA, 64] row statistics (softmax bias, dw, dr)
+  size_t hs_n;    // elements of one of them
+  float* partL;   // HiLS: [B*Hkv, max_work, D] landmark-gradient partials (unscaled)
 };
 
 static int bwd_max_work(const Shape& s) {
@@ -80,6 +83,9 @@ static size_t bwd_layout(const Shape& s, char* base, BwdWs* w) {
   x.n_work = (int*)take(BG * 4);
   x.list = (int*)take(rowsel * 4);
   x.part = (float*)take(BG * mw * 2 * kBlock * s.D * 4);
+  x.hs_n = s.mode == 2 ? (size_t)s.B * s.Hq * s.R * s.NA * kBlock : 0;
+  x.hstat = (float*)take(3 * x.hs_n * 4);
+  x.partL = (float*)take(s.mode == 2 ? BG * mw * s.D * 4 : 0);
   if (w) *w = x;
   return off;
 }
@@ -245,15 +251,24 @@ template <int D, int MODE, int HPW>
 __global__ __launch_bounds__(HPW * 128) void bwd_dq_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
-    const int32_t* __restrict__ idx, const float* __restrict__ sc, bf16* __restrict__ dq,
-    float* __restrict__ dg, float* __restrict__ gates_out, int Hq, int Hkv, int G, int T,
-    int NQB, int NA, int n_hc, float scale_log2, float scale) {
+    const int32_t* __restrict__ idx, const float* __restrict__ sc, const bf16* __restrict__ lm,
+    bf16* __restrict__ dq, float* __restrict__ dg, float* __restrict__ gates_out,
+    float* __restrict__ hstat, size_t hs_n, int Hq, int Hkv, int G, int T, int NQB, int NA,
+    int n_hc, float scale_log2, float scale) {
   constexpr int NT = HPW * 128;
+  constexpr int NWAVE = HPW * 2;
   constexpr int KP = D + 8;            // tile row pitch (elements)
   constexpr int C8 = D / 8;
   constexpr int CPT = kBlock * C8 / NT;
   __shared__ __attribute__((aligned(16))) bf16 Ks[2][kBlock * KP];
   __shared__ __attribute__((aligned(16))) bf16 Vs[2][kBlock * KP];
+  // HiLS: landmark rows of the attended chunks, and per (wave, entry, row) the retrieval weight
+  // (overwritten by the retrieval-score gradient after the entry loop) and dw = dout . o_j
+  static_assert(MODE != 2 || HPW <= 2, "the HiLS tables fit LDS for at most two heads");
+  __shared__ __attribute__((aligned(16))) bf16 Lb[MODE == 2 ? kBlock * KP : 8];
+  __shared__ float wbuf[MODE == 2 ? NWAVE * 64 * 32 : 1];
+  __shared__ float dwbuf[MODE == 2 ? NWAVE * 64 * 32 : 1];
+  float g_acc = 0.0f;                  // HiLS: sum_j w_j dw_j = dout . o, accumulated exactly
 
   const int c = NQB - 1 - (int)blockIdx.x;   // heavy (late) query blocks first
   const int g = blockIdx.y / n_hc, hc = blockIdx.y % n_hc;
@@ -275,7 +290,7 @@ __global__ __launch_bounds__(HPW * 128) void bwd_dq_kernel(
     df[s] = __builtin_bit_cast(bf16x8, bb);
   }
   const size_t rrow = (size_t)(b * Hq + h) * T + min(tq, T - 1);
-  const float lse2 = row_ok ? lse[rrow] * kLog2e : 0.0f;
+  const float lse2 = (MODE != 2 && row_ok) ? lse[rrow] * kLog2e : 0.0f;
   const float dlt = row_ok ? delta[rrow] : 0.0f;
 
   const size_t kvbase = (size_t)(b * Hkv + g) * T * D;
@@ -288,11 +303,63 @@ __global__ __launch_bounds__(HPW * 128) void bwd_dq_kernel(
     if (MODE != 1 || j == c) return 0.0f;
     return log_sigmoid(sc[rowsel + a] - s_ref) * kLog2e;
   };
-  if (hc == 0 && w == 0)
+  if (MODE != 2 && hc == 0 && w == 0)
     for (int a = lane; a < nval; a += kWave) {
       const int j = irow[a];
       gates_out[rowsel + a] = gate_of(a, j);
     }
+  if constexpr (MODE == 2) {
+    // retrieval weights softmax_j(scale q . L_j) of this wave's 32 rows over the attended
+    // chunks (at most 64), as in the forward: R^T = L Q^T on MFMA with the landmark rows in LDS
+    for (int ci = tid; ci < kBlock * C8; ci += NT) {
+      const int row = ci / C8, c8 = ci % C8;
+      u32x4 val = u32x4{0u, 0u, 0u, 0u};
+      const int jr = row < nval ? irow[row] : -1;
+      if (jr >= 0 && jr <= c)
+        val = *reinterpret_cast<const u32x4*>(lm + ((size_t)(b * Hkv + g) * NQB + jr) * D + c8 * 8);
+      *reinterpret_cast<u32x4*>(&Lb[row * KP + c8 * 8]) = val;
+    }
+    __syncthreads();
+    f32x16 rt[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) rt[kt][i] = 0.0f;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Lb[(kt * 32 + l32) * KP + 16 * s + 8 * half]);
+        rt[kt] = mfma32(a, qf[s], rt[kt]);
+      }
+    }
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int slot = kt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+        const float x = slot < nval ? rt[kt][i] * scale_log2 : -INFINITY;
+        rt[kt][i] = x;
+        mloc = fmaxf(mloc, x);
+      }
+    const float M = wave_max_xor32(mloc);
+    float den = 0.0f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float e = fast_exp2(rt[kt][i] - M);
+        rt[kt][i] = e;
+        den += e;
+      }
+    const float inv = 1.0f / wave_sum_xor32(den);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int slot = kt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+        wbuf[(w * 64 + slot) * 32 + l32] = rt[kt][i] * inv;
+      }
+  }
 
   u32x4 kreg[CPT], vreg[CPT];
   auto load_tile = [&](int a) {
@@ -352,23 +419,68 @@ __global__ __launch_bounds__(HPW * 128) void bwd_dq_kernel(
           dp[kt] = mfma32(vfr, df[s], dp[kt]);
         }
       }
-      const float gb = gate_of(a, j) - lse2;
-      float dgs = 0.0f;
+      if constexpr (MODE == 2) {
+        // HiLS: softmax of the row over this chunk's visible keys alone (P), dw = dout . o_j,
+        // dx = w_j P (dP - dw); dr_j = w_j (dw_j - sum_i w_i dw_i) is formed after the loop
+        float mx = -INFINITY;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = j * kBlock + kt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-          const bool vis = row_ok && key <= tq;
-          const float p = vis ? fast_exp2(fmaf(st[kt][i], scale_log2, gb)) : 0.0f;
-          const float x = p * (dp[kt][i] - dlt);
-          st[kt][i] = x;
-          dgs += x;
+          for (int i = 0; i < 16; ++i) {
+            const int key = j * kBlock + kt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+            if (!(row_ok && key <= tq)) st[kt][i] = -INFINITY;
+            mx = fmaxf(mx, st[kt][i]);
+          }
+        mx = wave_max_xor32(mx);
+        const float mxs = mx == -INFINITY ? 0.0f : mx * scale_log2;
+        float l = 0.0f, dwp = 0.0f;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float p = st[kt][i] == -INFINITY ? 0.0f : fast_exp2(fmaf(st[kt][i], scale_log2, -mxs));
+            st[kt][i] = p;
+            l += p;
+            dwp = fmaf(p, dp[kt][i], dwp);
+          }
+        l = wave_sum_xor32(l);
+        dwp = wave_sum_xor32(dwp);
+        const float inv_l = l > 0.0f ? 1.0f / l : 0.0f;
+        const float dwv = dwp * inv_l;
+        const float wj = wbuf[(w * 64 + a) * 32 + l32];
+        g_acc = fmaf(wj, dwv, g_acc);
+        const float coef = wj * inv_l;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) st[kt][i] = coef * st[kt][i] * (dp[kt][i] - dwv);
+        if (half == 0) {
+          // row statistics for the key side: w_j P = exp2(scale_log2 s - bias)
+          const size_t hi = (((size_t)(b * Hq + h) * NQB + c) * NA + a) * kBlock + (w % 2) * 32 + l32;
+          const bool live = row_ok && l > 0.0f && wj > 0.0f;
+          hstat[hi] = live ? mxs + log2f(l) - log2f(wj) : 0.0f;
+          hstat[hs_n + hi] = live ? dwv : 0.0f;
+          dwbuf[(w * 64 + a) * 32 + l32] = dwv;
         }
-      // gate gradient of this entry: the sum over the wave's rows and keys
+      } else {
+        const float gb = gate_of(a, j) - lse2;
+        float dgs = 0.0f;
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) dgs += __shfl_xor(dgs, o, kWave);
-      if (lane == 0 && MODE == 1) atomicAdd(&dg[rowsel + a], dgs);
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = j * kBlock + kt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+            const bool vis = row_ok && key <= tq;
+            const float p = vis ? fast_exp2(fmaf(st[kt][i], scale_log2, gb)) : 0.0f;
+            const float x = p * (dp[kt][i] - dlt);
+            st[kt][i] = x;
+            dgs += x;
+          }
+        // gate gradient of this entry: the sum over the wave's rows and keys
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) dgs += __shfl_xor(dgs, o, kWave);
+        if (lane == 0 && MODE == 1) atomicAdd(&dg[rowsel + a], dgs);
+      }
       // dQ^T += K^T dx^T: the K tile read transposed, dx^T from the score registers
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
@@ -388,6 +500,34 @@ __global__ __launch_bounds__(HPW * 128) void bwd_dq_kernel(
     if (a + 1 < nval) store_tile(buf ^ 1);
     if (a + 2 < nval) load_tile(a + 2);
     __syncthreads();
+  }
+  if constexpr (MODE == 2) {
+    // retrieval-score gradients dr_j = w_j (dw_j - sum_i w_i dw_i), kept for the key side
+    if (half == 0)
+      for (int a = 0; a < nval; ++a) {
+        const float wj = wbuf[(w * 64 + a) * 32 + l32];
+        const float drv = row_ok ? wj * (dwbuf[(w * 64 + a) * 32 + l32] - g_acc) : 0.0f;
+        hstat[2 * hs_n + (((size_t)(b * Hq + h) * NQB + c) * NA + a) * kBlock + (w % 2) * 32 + l32] = drv;
+        wbuf[(w * 64 + a) * 32 + l32] = drv;
+      }
+    // dQ^T += L^T dR^T over the attended chunks, 16 per k-step; the transposed landmark reads
+    // put chunks 16ks + 4half + {0..3} and 16ks + 8 + 4half + {0..3} in a lane's k slots, and the
+    // retrieval-score gradients are taken in the same order
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 rb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        rb[e] = f2bf(wbuf[(w * 64 + 16 * ks + 4 * half + (e % 4) + 8 * (e / 4)) * 32 + l32]);
+      const bf16* l0 = Lb + (16 * ks + 4 * half + vrow) * KP + vcol;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const i16x4 x0 = lds_read_tr16(l0 + dt * 32);
+        const i16x4 x1 = lds_read_tr16(l0 + 8 * KP + dt * 32);
+        const bf16x8 al = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+        dqa[dt] = mfma32(al, rb, dqa[dt]);
+      }
+    }
   }
   if (row_ok) {
     bf16* orow = dq + ((size_t)(b * Hq + h) * T + tq) * D;
@@ -450,7 +590,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     const float* __restrict__ gates, const int* __restrict__ cnt_off,
     const int* __restrict__ chunk_off, const int* __restrict__ list, const int* __restrict__ work,
     const int* __restrict__ n_work, float* __restrict__ part, bf16* __restrict__ dk,
-    bf16* __restrict__ dv, int Hq, int Hkv, int G, int T, int NQB, int NB, int NA, int max_work,
+    bf16* __restrict__ dv, const float* __restrict__ hstat, size_t hs_n, float* __restrict__ partL,
+    float* __restrict__ dlm, int Hq, int Hkv, int G, int T, int NQB, int NB, int NA, int max_work,
     float scale_log2, float scale) {
   constexpr int C = D / 8;                       // 16-byte chunks per row
   constexpr int TILE_B = kBlock * D * 2;         // bytes of one 64 x D bf16 tile
@@ -462,6 +603,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(16))) char smem[kBwdStages * STAGE_B];
   __shared__ int Ec[kBwdChunk];
   __shared__ float Eg[kBwdChunk];
+  __shared__ int Ep[kBwdChunk];                  // HiLS: the entry's position in its row
+  __shared__ float Lred[MODE == 2 ? 2 * D : 1];
 
   const int g = blockIdx.y, b = blockIdx.z;
   const int bg = b * Hkv + g;
@@ -485,6 +628,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     const int ent = lst[e0 + tid];
     const int c = ent / NA;
     Ec[tid] = c;
+    Ep[tid] = ent % NA;
     Eg[tid] = MODE == 1 ? gates[((size_t)bg * NQB + c) * NA + ent % NA] : 0.0f;
   }
   // K_j and V_j rows of this wave's keys as B fragments: B[k = d][n = key]
@@ -522,11 +666,21 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
       dma_lds<16>(qg, voff, la);
       dma_lds<16>(og, voff, la + TILE_B);
     }
-    // lse (waves 0, 2) and Delta (waves 1, 3); waves 2 and 3 fill a second, unused copy so that
-    // every wave issues the same number of copies per step
-    const float* src = (w % 2 == 0) ? lse : delta;
-    dma_lds<4>(reinterpret_cast<const char*>(src + row0), (uint32_t)(min(lane, rmax) * 4),
-               st_lds + 2 * TILE_B + (uint32_t)(w * kBlock * 4));
+    if constexpr (MODE == 2) {
+      // HiLS row statistics of this (query block, entry, head): softmax bias (wave 0), dw
+      // (wave 1), retrieval-score gradient (wave 2); wave 3 fills an unused copy so that every
+      // wave issues the same number of copies per step
+      const size_t hrow = (((size_t)(b * Hq + h) * NQB + c) * NA + Ep[st / G]) * kBlock;
+      const float* src = hstat + (size_t)(w % 3) * hs_n + hrow;
+      dma_lds<4>(reinterpret_cast<const char*>(src), (uint32_t)(lane * 4),
+                 st_lds + 2 * TILE_B + (uint32_t)(w * kBlock * 4));
+    } else {
+      // lse (waves 0, 2) and Delta (waves 1, 3); waves 2 and 3 fill a second, unused copy so
+      // that every wave issues the same number of copies per step
+      const float* src = (w % 2 == 0) ? lse : delta;
+      dma_lds<4>(reinterpret_cast<const char*>(src + row0), (uint32_t)(min(lane, rmax) * 4),
+                 st_lds + 2 * TILE_B + (uint32_t)(w * kBlock * 4));
+    }
   };
 
   f32x16 dka[DT], dva[DT];
@@ -534,6 +688,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) dka[dt][i] = dva[dt][i] = 0.0f;
+  float dla[DT];                                 // HiLS: dL for column dt*32 + l32, this lane's rows
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dla[dt] = 0.0f;
 
   const int vrow = (lane % 16) / 4;
   const int vcol = 16 * ((lane / 16) % 2) + 4 * (lane % 4);
@@ -603,7 +760,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
       for (int e = 0; e < 4; ++e) {
         const int tq = c * kBlock + tb + 8 * i4 + e;
         const bool vis = tq < T && ku <= tq;
-        const float p = vis ? fast_exp2(fmaf(sa[4 * i4 + e], scale_log2, gb - l4[i4][e] * kLog2e)) : 0.0f;
+        const float bias = MODE == 2 ? -l4[i4][e] : gb - l4[i4][e] * kLog2e;
+        const float p = vis ? fast_exp2(fmaf(sa[4 * i4 + e], scale_log2, bias)) : 0.0f;
         sa[4 * i4 + e] = p;
         pa[4 * i4 + e] = p * (pa[4 * i4 + e] - d4[i4][e]);
       }
@@ -625,12 +783,40 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
         dka[dt] = mfma32(aq, xb, dka[dt]);
       }
     }
+    if constexpr (MODE == 2) {
+      // dL_j += sum over this wave's rows of dr_t q_t, from the transposed Q fragments (rows in
+      // the same permuted order as the P registers); one key tile's waves suffice
+      if (kh == 0) {
+        const float* Rb = Lb + 2 * kBlock;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const f32x4 r0 = *reinterpret_cast<const f32x4*>(&Rb[tb + 16 * ks]);
+          const f32x4 r1 = *reinterpret_cast<const f32x4*>(&Rb[tb + 16 * ks + 8]);
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            const bf16x4 q0 = __builtin_bit_cast(bf16x4, tr[ks][dt][2]);
+            const bf16x4 q1 = __builtin_bit_cast(bf16x4, tr[ks][dt][3]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              dla[dt] = fmaf(bf2f(q0[e]), r0[e], dla[dt]);
+              dla[dt] = fmaf(bf2f(q1[e]), r1[e], dla[dt]);
+            }
+          }
+        }
+      }
+    }
   }
   __syncthreads();   // stages free (the last wait was vmcnt(0))
 
   // sum the two row halves: waves th = 1 hand their accumulators to waves th = 0
   float* red = reinterpret_cast<float*>(smem);
   constexpr int RED = 2 * DT * 16 * kWave;       // floats per key half
+  float dlv[DT];
+  if constexpr (MODE == 2) {
+    // dL: lanes l and l^32 hold the same columns for different rows
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) dlv[dt] = wave_sum_xor32(dla[dt]);
+  }
   if (th == 1) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -639,8 +825,24 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
         red[kh * RED + (dt * 16 + i) * kWave + lane] = dka[dt][i];
         red[kh * RED + ((DT + dt) * 16 + i) * kWave + lane] = dva[dt][i];
       }
+    if constexpr (MODE == 2) {
+      if (kh == 0 && half == 0)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) Lred[dt * 32 + l32] = dlv[dt];
+    }
   }
   __syncthreads();
+  if constexpr (MODE == 2) {
+    // the two row halves of dL_j: written directly for a single work item, else as a partial
+    if (kh == 0 && th == 0 && half == 0)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int d = dt * 32 + l32;
+        const float val = dlv[dt] + Lred[d];
+        if (nch == 1) dlm[((size_t)bg * NB + j) * D + d] = val * scale;
+        else partL[((size_t)bg * max_work + wi) * D + d] = val;
+      }
+  }
   constexpr int FP = D + 4;                      // row pitch (floats) of the [key][d] tiles
   float* F = red + 2 * RED;                      // [2][64][FP]: dK then dV
   if (th == 0) {
@@ -691,7 +893,9 @@ template <int D>
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict__ part,
                                                          const int* __restrict__ chunk_off,
                                                          bf16* __restrict__ dk,
-                                                         bf16* __restrict__ dv, int Hkv, int T,
+                                                         bf16* __restrict__ dv,
+                                                         const float* __restrict__ partL,
+                                                         float* __restrict__ dlm, int Hkv, int T,
                                                          int NB, int max_work, float scale) {
   constexpr int C = D / 8;
   const int j = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -699,6 +903,11 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict
   const int c0 = chunk_off[(size_t)bg * (NB + 1) + j];
   const int c1 = chunk_off[(size_t)bg * (NB + 1) + j + 1];
   if (c1 - c0 == 1) return;                      // written by its only work item
+  if (dlm != nullptr && threadIdx.x < D) {
+    float acc = 0.0f;
+    for (int chn = c0; chn < c1; ++chn) acc += partL[((size_t)bg * max_work + chn) * D + threadIdx.x];
+    dlm[((size_t)bg * NB + j) * D + threadIdx.x] = acc * scale;
+  }
   for (int it = threadIdx.x; it < 2 * kBlock * C; it += 256) {
     const int which = it / (kBlock * C);
     const int u = (it / C) % kBlock, c8 = it % C;
@@ -759,9 +968,10 @@ __global__ __launch_bounds__(256) void bwd_dsc_kernel(const int32_t* __restrict_
 // ---------------------------------------------------------------------------------------------
 template <int D>
 static hipError_t launch_backward_d(const Shape& s, const void* q, const void* k, const void* v,
-                                    const int32_t* idx, const float* sc, const void* out,
-                                    const float* lse, const void* dout, void* dq, void* dk,
-                                    void* dv, float* dsc, void* ws, hipStream_t st) {
+                                    const void* lm, const int32_t* idx, const float* sc,
+                                    const void* out, const float* lse, const void* dout, void* dq,
+                                    void* dk, void* dv, float* dsc, float* dlm, void* ws,
+                                    hipStream_t st) {
   BwdWs W;
   bwd_layout(s, (char*)ws, &W);
   const int BG = s.B * s.Hkv;
@@ -769,7 +979,7 @@ static hipError_t launch_backward_d(const Shape& s, const void* q, const void* k
   const int64_t n_entries = (int64_t)BG * s.R * s.NA;
   const int mw = bwd_max_work(s);
   const float sl2 = s.scale * kLog2e;
-  {
+  if (s.mode != 2) {
     constexpr int RPB = 4 * (kWave / (D / 8));
     hipLaunchKernelGGL(bwd_delta_kernel<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
                        st, (const bf16*)out, (const bf16*)dout, W.delta, rows);
@@ -785,19 +995,22 @@ static hipError_t launch_backward_d(const Shape& s, const void* q, const void* k
                      s.NA, s.NB, n_entries);
   hipLaunchKernelGGL(bwd_sort_kernel, dim3(s.NB, BG), dim3(256), 0, st, W.cnt_off, W.list, s.R,
                      s.NA, s.NB);
-  const int hpw = (s.G % 4 == 0) ? 4 : (s.G % 2 == 0) ? 2 : 1;
+  const int hpw = (s.G % 4 == 0 && s.mode != 2) ? 4 : (s.G % 2 == 0) ? 2 : 1;
   const int n_hc = s.G / hpw;
 #define BSA_DQ(MODE, HPW)                                                                        \
   hipLaunchKernelGGL((bwd_dq_kernel<D, MODE, HPW>), dim3(s.R, s.Hkv * n_hc, s.B), dim3(HPW * 128),\
                      0, st, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout,     \
-                     lse, W.delta, idx, sc, (bf16*)dq, W.dg, W.gates, s.Hq, s.Hkv, s.G, s.Tq,      \
-                     s.R, s.NA, n_hc, sl2, s.scale)
+                     lse, W.delta, idx, sc, (const bf16*)lm, (bf16*)dq, W.dg, W.gates, W.hstat,    \
+                     W.hs_n, s.Hq, s.Hkv, s.G, s.Tq, s.R, s.NA, n_hc, sl2, s.scale)
 #define BSA_DQ_H(MODE)                                           \
   if (hpw == 4) BSA_DQ(MODE, 4);                                  \
   else if (hpw == 2) BSA_DQ(MODE, 2);                             \
   else BSA_DQ(MODE, 1);
   if (s.mode == 1) {
     BSA_DQ_H(1)
+  } else if (s.mode == 2) {
+    if (hpw >= 2) BSA_DQ(2, 2);
+    else BSA_DQ(2, 1);
   } else {
     BSA_DQ_H(0)
   }
@@ -807,13 +1020,15 @@ static hipError_t launch_backward_d(const Shape& s, const void* q, const void* k
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, MODE>), dim3(mw, s.Hkv, s.B), dim3(256), 0, st,        \
                      (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, lse,     \
                      W.delta, W.gates, W.cnt_off, W.chunk_off, W.list, W.work, W.n_work, W.part, \
-                     (bf16*)dk, (bf16*)dv, s.Hq, s.Hkv, s.G, s.Tq, s.R, s.NB, s.NA, mw, sl2,     \
-                     s.scale)
+                     (bf16*)dk, (bf16*)dv, W.hstat, W.hs_n, W.partL, dlm, s.Hq, s.Hkv, s.G,      \
+                     s.Tq, s.R, s.NB, s.NA, mw, sl2, s.scale)
   if (s.mode == 1) BSA_KV(1);
+  else if (s.mode == 2) BSA_KV(2);
   else BSA_KV(0);
 #undef BSA_KV
   hipLaunchKernelGGL(bwd_reduce_kernel<D>, dim3(s.NB, s.Hkv, s.B), dim3(256), 0, st, W.part,
-                     W.chunk_off, (bf16*)dk, (bf16*)dv, s.Hkv, s.Tq, s.NB, mw, s.scale);
+                     W.chunk_off, (bf16*)dk, (bf16*)dv, W.partL, s.mode == 2 ? dlm : nullptr,
+                     s.Hkv, s.Tq, s.NB, mw, s.scale);
   if (dsc != nullptr)
     hipLaunchKernelGGL(bwd_dsc_kernel, dim3((unsigned)((BG * (int64_t)s.R + 255) / 256)), dim3(256),
                        0, st, idx, sc, W.dg, dsc, s.R, s.NA, (int64_t)BG * s.R, s.mode);
@@ -821,11 +1036,13 @@ static hipError_t launch_backward_d(const Shape& s, const void* q, const void* k
 }
 
 hipError_t launch_attend_backward(const Shape& s, const void* q, const void* k, const void* v,
-                                  const int32_t* idx, const float* sc, const void* out,
-                                  const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                                  float* dsc, void* ws, hipStream_t st) {
-  if (s.D == 128) return launch_backward_d<128>(s, q, k, v, idx, sc, out, lse, dout, dq, dk, dv, dsc, ws, st);
-  return launch_backward_d<64>(s, q, k, v, idx, sc, out, lse, dout, dq, dk, dv, dsc, ws, st);
+                                  const void* lm, const int32_t* idx, const float* sc,
+                                  const void* out, const float* lse, const void* dout, void* dq,
+                                  void* dk, void* dv, float* dsc, float* dlm, void* ws,
+                                  hipStream_t st) {
+  if (s.D == 128)
+    return launch_backward_d<128>(s, q, k, v, lm, idx, sc, out, lse, dout, dq, dk, dv, dsc, dlm, ws, st);
+  return launch_backward_d<64>(s, q, k, v, lm, idx, sc, out, lse, dout, dq, dk, dv, dsc, dlm, ws, st);
 }
 
 }  // namespace bsa

@@ -214,8 +214,9 @@ namespace {
 bsa_status_t backward_shape(const bsa_params_t* params, bsa::Shape* s) {
   BSA_TRY(make_shape(params, kPrefill, s));
   if (!s->bf16) return fail(BSA_ERR_UNSUPPORTED, "the backward pass is implemented for bf16 only");
-  if (s->mode == BSA_MODE_HILS)
-    return fail(BSA_ERR_UNSUPPORTED, "the backward pass is implemented for PLAIN and SAS only");
+  if (s->mode == BSA_MODE_HILS && s->NA > 64)
+    return fail(BSA_ERR_UNSUPPORTED, "the HILS backward supports n_sink + n_local + topk <= 64 (got %d)",
+                s->NA);
   if (s->NB > 65535)
     return fail(BSA_ERR_UNSUPPORTED, "the backward pass supports at most 65535 key blocks (got %d)",
                 s->NB);
@@ -232,18 +233,24 @@ size_t bsa_backward_workspace_bytes(const bsa_params_t* params) {
 }
 
 bsa_status_t bsa_attend_prefill_backward(const bsa_params_t* params, const void* q,
-                                         const void* k, const void* v, const int32_t* idx,
-                                         const float* sc, const void* out, const float* lse,
-                                         const void* dout, void* dq, void* dk, void* dv,
-                                         float* dsc, void* ws, size_t ws_bytes, void* stream) {
+                                         const void* k, const void* v, const void* lm,
+                                         const int32_t* idx, const float* sc, const void* out,
+                                         const float* lse, const void* dout, void* dq, void* dk,
+                                         void* dv, float* dsc, float* dlm, void* ws,
+                                         size_t ws_bytes, void* stream) {
   bsa::Shape s;
   BSA_TRY(backward_shape(params, &s));
   BSA_TRY(check_ptr(q, "q"));
   BSA_TRY(check_ptr(k, "k"));
   BSA_TRY(check_ptr(v, "v"));
   BSA_TRY(check_ptr(idx, "idx"));
-  BSA_TRY(check_ptr(out, "out"));
-  BSA_TRY(check_ptr(lse, "lse"));
+  if (s.mode == BSA_MODE_HILS) {
+    BSA_TRY(check_ptr(lm, "lm"));
+    BSA_TRY(check_ptr(dlm, "dlm"));
+  } else {
+    BSA_TRY(check_ptr(out, "out"));
+    BSA_TRY(check_ptr(lse, "lse"));
+  }
   BSA_TRY(check_ptr(dout, "dout"));
   BSA_TRY(check_ptr(dq, "dq"));
   BSA_TRY(check_ptr(dk, "dk"));
@@ -259,8 +266,9 @@ bsa_status_t bsa_attend_prefill_backward(const bsa_params_t* params, const void*
     return fail(BSA_ERR_WORKSPACE, "backward workspace needs %zu bytes (got %zu%s)", need,
                 ws_bytes, ws == nullptr ? ", NULL pointer" : "");
   if (((uintptr_t)ws & 255u) != 0) return fail(BSA_ERR_ALIGN, "ws is not 256-byte aligned");
-  return hip_result(bsa::launch_attend_backward(s, q, k, v, idx, sc, out, lse, dout, dq, dk, dv,
-                                                dsc, ws, (hipStream_t)stream),
+  return hip_result(bsa::launch_attend_backward(s, q, k, v, lm, idx, sc, out, lse, dout, dq, dk,
+                                                dv, dsc, s.mode == BSA_MODE_HILS ? dlm : nullptr,
+                                                ws, (hipStream_t)stream),
                     "attend_prefill_backward");
 }
 

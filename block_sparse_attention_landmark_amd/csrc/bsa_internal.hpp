@@ -62,11 +62,12 @@ hipError_t launch_attend_decode(const Shape& s, const void* q, const void* kc, c
                                 const void* lm, const int32_t* idx, const float* sc, void* out,
                                 float* lse, void* ws, hipStream_t st, const Pages* pg = nullptr);
 
-// Backward of PLAIN / SAS bf16 prefill attention: workspace size and launcher.
+// Backward of bf16 prefill attention (PLAIN / SAS / HiLS): workspace size and launcher.
 size_t backward_ws_bytes(const Shape& s);
 hipError_t launch_attend_backward(const Shape& s, const void* q, const void* k, const void* v,
-                                  const int32_t* idx, const float* sc, const void* out,
-                                  const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                                  float* dsc, void* ws, hipStream_t st);
+                                  const void* lm, const int32_t* idx, const float* sc,
+                                  const void* out, const float* lse, const void* dout, void* dq,
+                                  void* dk, void* dv, float* dsc, float* dlm, void* ws,
+                                  hipStream_t st);
 
 }  // namespace bsa

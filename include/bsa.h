@@ -192,32 +192,46 @@ bsa_status_t bsa_attend_decode_paged(const bsa_params_t* params, const void* q,
 size_t bsa_backward_workspace_bytes(const bsa_params_t* params);
 
 /*
- * Backward of PLAIN / SAS prefill attention (bf16 only), so that the selector is trained end
- * to end through the SAS gates (SAS page, summary paragraphs 2-3: the top-K choice itself is
- * hard, but the continuous scores enter the softmax through the gates and carry gradient).
- * With the forward's logits x_tu = scale * q_t.k_u + g_j(u) over the keys u of A_c (u <= t),
- * P = exp(x - lse), dP_tu = dout_t.v_u and dx = P * (dP - dout_t.out_t):
+ * Backward of prefill attention (bf16 only).  PLAIN / SAS: the selector is trained end to end
+ * through the SAS gates (SAS page, summary paragraphs 2-3: the top-K choice itself is hard, but
+ * the continuous scores enter the softmax through the gates and carry gradient).  HILS: the
+ * chunk results are merged by the chunks' retrieval scores (HiLS page, summary paragraph 2), so
+ * the gradient also reaches the landmarks through those scores.
+ * PLAIN / SAS, with the forward's logits x_tu = scale * q_t.k_u + g_j(u) over the keys u of A_c
+ * (u <= t), P = exp(x - lse), dP_tu = dout_t.v_u and dx = P * (dP - dout_t.out_t):
  *   dq_t = scale * sum_u dx_tu k_u;  dk_u = scale * sum_t dx_tu q_t;  dv_u = sum_t P_tu dout_t
  *   (sums over every query head of the kv group and every query block that attends u);
  *   SAS: dg_j = sum of dx over the rows of block c (all heads of the group) and the keys of
  *   block j; d sc_j = dg_j * sigmoid(sc_c - sc_j) for j != c and d sc_c = -(sum of those).
- *   q, k, v, idx, sc: the forward's inputs (sc required for SAS, ignored for PLAIN);
- *   out [B,Hq,T,D] bf16 and lse [B,Hq,T] float32: the forward's outputs;
+ * HILS, with P_j the softmax of row t over the visible keys of chunk j alone, o_j = P_j V,
+ * w = softmax_j(scale * q_t.L_j), dw_j = dout_t.o_j and dr_j = w_j (dw_j - sum_i w_i dw_i):
+ *   chunk j is a softmax attention with output gradient w_j dout (giving dq, dk, dv as above
+ *   with dx = w_j P_j (dP - dw_j)); dq_t += scale * sum_j dr_j L_j; dlm_j = scale * sum of
+ *   dr_j q_t over every row and query head that attends chunk j.  dk does not include the
+ *   pooling that produced the landmarks (a caller training through it adds dlm_j / n_j to
+ *   each of the n_j keys of block j).
+ *   q, k, v, idx: the forward's inputs; sc (SAS: required; else ignored); lm [B,Hkv,NB,D] bf16
+ *   (HILS: the landmarks the forward used, required; else ignored);
+ *   out [B,Hq,T,D] bf16 and lse [B,Hq,T] float32: the forward's output and lse (PLAIN / SAS:
+ *   required; HILS: ignored, may be NULL -- the sum over chunks is formed exactly instead);
  *   dout [B,Hq,T,D] bf16: gradient of the loss with respect to out;
  *   dq [B,Hq,T,D], dk, dv [B,Hkv,T,D] bf16 outputs (every element written);
- *   dsc [B,Hkv,R,NA] float32 output, zero in the padding and for PLAIN (may be NULL for PLAIN);
+ *   dsc [B,Hkv,R,NA] float32 output, zero in the padding and for PLAIN / HILS (may be NULL
+ *   unless SAS); dlm [B,Hkv,NB,D] float32 output (HILS: required, every element written; else
+ *   ignored);
  *   ws: device workspace of bsa_backward_workspace_bytes(params) bytes, 256-byte aligned;
  *       contents on entry are ignored.
- * Limits: at most 65535 key blocks; R * NA < 2^31.  Sums over many query blocks (dk, dv)
- * are taken in a fixed order when a key block is attended by at most 4096 query blocks;
- * beyond that their float32 rounding may differ between runs.  dsc accumulates with float32
- * atomics and its rounding may differ between runs.
+ * Limits: at most 65535 key blocks; R * NA < 2^31; HILS: NA <= 64.  Sums over many query
+ * blocks (dk, dv, dlm) are taken in a fixed order when a key block is attended by at most
+ * 4096 query blocks; beyond that their float32 rounding may differ between runs.  dsc
+ * accumulates with float32 atomics and its rounding may differ between runs.
  */
 bsa_status_t bsa_attend_prefill_backward(const bsa_params_t* params, const void* q,
-                                         const void* k, const void* v, const int32_t* idx,
-                                         const float* sc, const void* out, const float* lse,
-                                         const void* dout, void* dq, void* dk, void* dv,
-                                         float* dsc, void* ws, size_t ws_bytes, void* stream);
+                                         const void* k, const void* v, const void* lm,
+                                         const int32_t* idx, const float* sc, const void* out,
+                                         const float* lse, const void* dout, void* dq, void* dk,
+                                         void* dv, float* dsc, float* dlm, void* ws,
+                                         size_t ws_bytes, void* stream);
 
 /* Static description of a status code. */
 const char* bsa_status_string(int status);

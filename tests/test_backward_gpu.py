@@ -1,4 +1,4 @@
-"""GPU parity of the backward pass (PLAIN / SAS, bf16) against the float64 oracle.
+"""GPU parity of the backward pass (PLAIN / SAS / HiLS, bf16) against the float64 oracle.
 
 The device's forward supplies the attended sets, scores, out and lse; the oracle recomputes
 the gradients from the same q, k, v, attended sets, scores and dout in float64.  Small shapes
@@ -41,13 +41,14 @@ def _dout(shape, seed):
 
 
 def _run(q, k, v, *, topk, mode, ns, nl, seed):
-    res = bsa.prefill(q, k, v, topk=topk, mode=mode, n_sink=ns, n_local=nl, want_lse=True)
+    res = bsa.prefill(q, k, v, topk=topk, mode=mode, n_sink=ns, n_local=nl,
+                      want_lse=(mode != "hils"))
     dout = _dout(q.shape, seed)
-    dq, dk, dv, dsc = bsa.attend_prefill_backward(q, k, v, res["idx"], res["sc"], res["out"],
-                                                  res["lse"], dout, mode=mode, topk=topk,
-                                                  n_sink=ns, n_local=nl)
+    dq, dk, dv, dsc, dlm = bsa.attend_prefill_backward(
+        q, k, v, res["idx"], res["sc"], res["out"], res["lse"], dout, mode=mode,
+        lm=res["lm"] if mode == "hils" else None, topk=topk, n_sink=ns, n_local=nl)
     torch.cuda.synchronize()
-    return res, dout, dq, dk, dv, dsc
+    return res, dout, dq, dk, dv, dsc, dlm
 
 
 BWD_SMALL = [
@@ -67,16 +68,19 @@ BWD_SMALL = [
 ]
 
 
-@pytest.mark.parametrize("mode", ["plain", "sas"])
+@pytest.mark.parametrize("mode", ["plain", "sas", "hils"])
 @pytest.mark.parametrize("case", BWD_SMALL, ids=[c[0] for c in BWD_SMALL])
 def test_backward_small(case, mode):
     name, B, Hq, Hkv, T, D, topk, ns, nl, data = case
+    if mode == "hils" and ns + nl + topk > 64:
+        pytest.skip("the HiLS backward holds at most 64 attended chunks per row")
     _print(f"backward {name} {mode}")
     q, k, v = synth.make_prefill(B, Hq, Hkv, T, D, "bf16", data, seed=5, device="cuda",
                                  n_centres=16, n_aim=4)
-    res, dout, dq, dk, dv, dsc = _run(q, k, v, topk=topk, mode=mode, ns=ns, nl=nl, seed=11)
+    res, dout, dq, dk, dv, dsc, dlm = _run(q, k, v, topk=topk, mode=mode, ns=ns, nl=nl, seed=11)
     ref = O.prefill_backward(host64(q), host64(k), host64(v), res["idx"].cpu().numpy(),
-                             res["sc"].cpu().numpy().astype(np.float64), host64(dout), mode=mode)
+                             res["sc"].cpu().numpy().astype(np.float64), host64(dout), mode=mode,
+                             lm=host64(res["lm"]))
     tag = f"{name}/{mode}"
     for b in range(B):
         for h in range(Hq):
@@ -85,25 +89,29 @@ def test_backward_small(case, mode):
             check_grad(host64(dk[b, g]), ref["dk"][b, g], f"{tag} dk b{b} g{g}")
             check_grad(host64(dv[b, g]), ref["dv"][b, g], f"{tag} dv b{b} g{g}")
             check_grad(host64(dsc[b, g]), ref["dsc"][b, g], f"{tag} dsc b{b} g{g}")
-    if mode == "plain":
-        assert torch.count_nonzero(dsc).item() == 0, f"{tag}: dsc must be zero for PLAIN"
+            if mode == "hils":
+                check_grad(host64(dlm[b, g]), ref["dlm"][b, g], f"{tag} dlm b{b} g{g}")
+    if mode != "sas":
+        assert torch.count_nonzero(dsc).item() == 0, f"{tag}: dsc must be zero for {mode}"
 
 
 def test_backward_deterministic_dq_dk_dv():
     """dq, dk and dv are summed in a fixed order: two calls give identical bits."""
     q, k, v = synth.make_prefill(1, 8, 2, 64 * 21 + 7, 128, "bf16", "clustered", seed=8,
                                  device="cuda", n_centres=16, n_aim=4)
-    a = _run(q, k, v, topk=4, mode="sas", ns=1, nl=2, seed=3)
-    b = _run(q, k, v, topk=4, mode="sas", ns=1, nl=2, seed=3)
-    for i, name in ((2, "dq"), (3, "dk"), (4, "dv")):
-        assert torch.equal(a[i], b[i]), f"{name} differs between identical calls"
+    for mode in ("sas", "hils"):
+        a = _run(q, k, v, topk=4, mode=mode, ns=1, nl=2, seed=3)
+        b = _run(q, k, v, topk=4, mode=mode, ns=1, nl=2, seed=3)
+        for i, name in ((2, "dq"), (3, "dk"), (4, "dv"), (6, "dlm")):
+            if a[i] is not None:
+                assert torch.equal(a[i], b[i]), f"{mode}: {name} differs between identical calls"
 
 
 def test_backward_invalid_calls_rejected():
     q, k, v = synth.make_prefill(1, 4, 1, 128, 64, "bf16", "iid", seed=1, device="cuda")
     res = bsa.prefill(q, k, v, topk=1, mode="sas", want_lse=True)
     dout = torch.zeros_like(q)
-    with pytest.raises(bsa.BsaError):   # HiLS has no backward here
+    with pytest.raises(bsa.BsaError):   # HiLS needs the forward's landmarks
         bsa.attend_prefill_backward(q, k, v, res["idx"], res["sc"], res["out"], res["lse"], dout,
                                     mode="hils", topk=1)
     with pytest.raises(bsa.BsaError):   # workspace too small
@@ -112,16 +120,19 @@ def test_backward_invalid_calls_rejected():
                                     ws=torch.empty(256, dtype=torch.uint8, device="cuda"))
 
 
-def test_workload_backward_sas_bf16_128k_sampled():
-    """The 128K SAS workload's backward in one call; sampled query blocks and key blocks."""
+@pytest.mark.parametrize("mode", ["sas", "hils"])
+def test_workload_backward_bf16_128k_sampled(mode):
+    """The 128K workload's backward (SAS, and HiLS on the same shape) in one call; sampled
+    query blocks and key blocks."""
     w = synth.WORKLOADS["sas_bf16_128k"]
     B, Hq, Hkv, T, D = w["B"], w["Hq"], w["Hkv"], w["T"], w["D"]
     G = Hq // Hkv
-    _print("backward workload: generating")
+    _print(f"backward workload {mode}: generating")
     q, k, v = synth.make_prefill(B, Hq, Hkv, T, D, w["dtype"], w["data"], seed=0, device="cuda",
                                  n_centres=w.get("n_centres", 256), n_aim=w.get("n_aim", 16))
-    _print("backward workload: running")
-    res, dout, dq, dk, dv, dsc = _run(q, k, v, topk=w["topk"], mode="sas", ns=1, nl=2, seed=21)
+    _print(f"backward workload {mode}: running")
+    res, dout, dq, dk, dv, dsc, dlm = _run(q, k, v, topk=w["topk"], mode=mode, ns=1, nl=2,
+                                           seed=21)
     idx = res["idx"].cpu().numpy()
     sc = res["sc"].cpu().numpy().astype(np.float64)
     NQB = (T + 63) // 64
@@ -133,17 +144,23 @@ def test_workload_backward_sas_bf16_128k_sampled():
         K64, V64 = host64(k[b, g]), host64(v[b, g])
         Q64 = host64(q[b, g * G:(g + 1) * G])
         dO64 = host64(dout[b, g * G:(g + 1) * G])
+        L64 = host64(res["lm"][b, g])
 
         def grads_of_row(c):
             A = idx[b, g, c][idx[b, g, c] >= 0].astype(np.int64)
             sA = sc[b, g, c, :A.size]
-            gates = O.sas_gates(A, sA, c)
             lo, hi = c * 64, min(c * 64 + 64, T)
             tpos = np.arange(lo, hi)
             out = []
             for hh in range(G):
-                out.append(O.attend_rows_grad(Q64[hh, lo:hi], tpos, K64, V64, A, gates, scale,
-                                              dO64[hh, lo:hi]))
+                if mode == "hils":
+                    dq_h, pos, dK, dV, dL = O.hils_rows_grad(Q64[hh, lo:hi], tpos, K64, V64,
+                                                             L64[A], A, scale, dO64[hh, lo:hi])
+                    out.append((dq_h, pos, dK, dV, np.zeros(A.size), dL))
+                else:
+                    gates = O.sas_gates(A, sA, c)
+                    out.append(O.attend_rows_grad(Q64[hh, lo:hi], tpos, K64, V64, A, gates,
+                                                  scale, dO64[hh, lo:hi]))
             return A, sA, out
 
         # query blocks: dq rows and dsc rows
@@ -161,7 +178,8 @@ def test_workload_backward_sas_bf16_128k_sampled():
                 check_grad(host64(dq[b, g * G + hh, lo:hi]), out[hh][0], f"dq g{g} c{c} h{hh}")
                 dg += out[hh][4]
             ref_dsc = np.zeros(idx.shape[-1])
-            ref_dsc[:A.size] = O.sas_gates_grad(A, sA, c, dg)
+            if mode == "sas":
+                ref_dsc[:A.size] = O.sas_gates_grad(A, sA, c, dg)
             dsc_dev.append(host64(dsc[b, g, c]))
             dsc_ref.append(ref_dsc)
         check_grad(np.concatenate(dsc_dev), np.concatenate(dsc_ref), f"dsc g{g} rows {cs}")
@@ -172,16 +190,21 @@ def test_workload_backward_sas_bf16_128k_sampled():
             _print(f"backward workload: g{g} key block {j}, {len(users)} query blocks")
             dK = np.zeros((64, D))
             dV = np.zeros((64, D))
+            dLj = np.zeros(D)
             lo, hi = j * 64, min(j * 64 + 64, T)
             for c in users:
-                _, _, out = grads_of_row(c)
+                A, _, out = grads_of_row(c)
                 for hh in range(G):
                     pos = out[hh][1]
                     sel = (pos >= lo) & (pos < hi)
                     dK[pos[sel] - lo] += out[hh][2][sel]
                     dV[pos[sel] - lo] += out[hh][3][sel]
+                    if mode == "hils":
+                        dLj += out[hh][5][int(np.nonzero(A == j)[0][0])]
             check_grad(host64(dk[b, g, lo:hi]), dK[: hi - lo], f"dk g{g} j{j}")
             check_grad(host64(dv[b, g, lo:hi]), dV[: hi - lo], f"dv g{g} j{j}")
-    del q, k, v, res, dout, dq, dk, dv, dsc
+            if mode == "hils":
+                check_grad(host64(dlm[b, g, j]), dLj, f"dlm g{g} j{j}")
+    del q, k, v, res, dout, dq, dk, dv, dsc, dlm
     gc.collect()
     torch.cuda.empty_cache()
