@@ -16,7 +16,8 @@ Reported beside it, measured in the same run:
 * the same decode step over a ragged batch held in a paged cache (32 sequences of 16K..128K
   tokens in shuffled 64-token pages);
 * the backward of the SAS prefill (dq, dk, dv and the selector-score gradient) on the same
-  workload, timed per call (--no-backward skips it);
+  workload, and the HiLS backward (dq, dk, dv and the landmark gradient) on the same shape and
+  attended sets, each timed per call (--no-backward skips both);
 * optionally the HiLS workload at 1M tokens (--hils);
 * the float64 oracle timed on the host cores on a bounded sample of the prefill workload.
 
@@ -174,12 +175,15 @@ def bench_prefill(torch, bsa, synth, name, steps, warmup):
     return res, tensors
 
 
-def bench_backward(torch, bsa, synth, name, tensors, steps, warmup):
-    """The backward of the SAS prefill (dq, dk, dv, d scores) on the forward's own outputs."""
+def bench_backward(torch, bsa, synth, name, tensors, steps, warmup, mode=None):
+    """The backward of the prefill (dq, dk, dv, and the score or landmark gradient) on the
+    forward's own outputs; mode defaults to the workload's."""
     w = synth.WORKLOADS[name]
-    B, Hq, Hkv, T, D, K, mode = w["B"], w["Hq"], w["Hkv"], w["T"], w["D"], w["topk"], w["mode"]
+    B, Hq, Hkv, T, D, K = w["B"], w["Hq"], w["Hkv"], w["T"], w["D"], w["topk"]
+    mode = mode or w["mode"]
     q, k, v, lm, idx, sc = tensors[:6]
-    out, lse = bsa.attend_prefill(q, k, v, idx, sc, None, mode=mode, topk=K, want_lse=True)
+    out, lse = bsa.attend_prefill(q, k, v, idx, sc, lm if mode == "hils" else None, mode=mode,
+                                  topk=K, want_lse=(mode != "hils"))
     g = torch.Generator(device="cuda").manual_seed(5)
     dout = torch.randn(q.shape, generator=g, device="cuda", dtype=torch.float32).to(q.dtype)
     p = bsa.make_params(B=B, Hq=Hq, Hkv=Hkv, D=D, seq_q=T, seq_k=T, dtype=q.dtype, topk=K,
@@ -187,13 +191,15 @@ def bench_backward(torch, bsa, synth, name, tensors, steps, warmup):
     ws = torch.empty(bsa.backward_workspace_bytes(p), dtype=torch.uint8, device="cuda")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dsc = torch.empty(idx.shape, dtype=torch.float32, device="cuda")
+    dlm = torch.empty(lm.shape, dtype=torch.float32, device="cuda") if mode == "hils" else None
     ev = Events(torch)
 
     def step(record):
         if record:
             ev.start()
-        bsa.attend_prefill_backward(q, k, v, idx, sc, out, lse, dout, mode=mode, topk=K, ws=ws,
-                                    dq=dq, dk=dk, dv=dv, dsc=dsc)
+        bsa.attend_prefill_backward(q, k, v, idx, sc, out, lse, dout, mode=mode,
+                                    lm=lm if mode == "hils" else None, topk=K, ws=ws, dq=dq,
+                                    dk=dk, dv=dv, dsc=dsc, dlm=dlm)
         if record:
             ev.stop()
 
@@ -207,20 +213,23 @@ def bench_backward(torch, bsa, synth, name, tensors, steps, warmup):
     ms = sum(ev.ms()) / steps
     flops = attended_flops(B, Hq, D, T, K) // 4 * 10
     tf = flops / (ms * 1e-3) / 1e12
-    res = {"workload": f"{name}: backward of the SAS prefill (dq, dk, dv, selector-score "
-                       f"gradient) given the forward's out and lse",
+    what = ("HiLS prefill on the same shape and attended sets (dq, dk, dv, landmark gradient)"
+            if mode == "hils" else "SAS prefill (dq, dk, dv, selector-score gradient) given the "
+            "forward's out and lse")
+    res = {"workload": f"{name}: backward of the {what}",
            "ms_per_call": ms, "tok_per_s": B * T / (ms * 1e-3),
            "algorithmic_flops": flops,
            "flops_definition": "10*D per visible (query, key) pair per query head: "
                                "recomputed S, dP, dQ, dK, dV (2*D each)",
            "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
                         "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
-                        "traffic": profiled_traffic("attend_backward_sas_bf16_128k.md",
-                                                    "traffic_bytes_per_call"),
+                        "traffic": (profiled_traffic("attend_backward_sas_bf16_128k.md",
+                                                     "traffic_bytes_per_call")
+                                    if mode == "sas" else None),
                         "traffic_unit": "bytes per call (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE)",
                         "scope": "whole backward call (all its kernels)"}}
     log(f"[bench] backward: {json.dumps(res)}")
-    del ws, dq, dk, dv, dsc, dout, out, lse
+    del ws, dq, dk, dv, dsc, dlm, dout, out, lse
     return res
 
 
@@ -397,9 +406,12 @@ def main():
         log("[bench] timing the oracle on the host cores")
         cpu = cpu_baseline(torch, tensors, name, synth)
         log(f"[bench] cpu baseline: {cpu['value']:.1f} tok/s")
-    bwd = None
+    bwd = bwd_hils = None
     if not args.no_backward:
         bwd = bench_backward(torch, bsa, synth, name, tensors, max(3, args.steps // 4), 1)
+        torch.cuda.empty_cache()
+        bwd_hils = bench_backward(torch, bsa, synth, name, tensors, max(3, args.steps // 4), 1,
+                                  mode="hils")
     del tensors
     torch.cuda.empty_cache()
     dec = None
@@ -468,6 +480,8 @@ def main():
         line["decode_paged"] = dec_paged
     if bwd is not None:
         line["backward"] = bwd
+    if bwd_hils is not None:
+        line["backward_hils"] = bwd_hils
     if hils is not None:
         line["hils_1m"] = {"tok_per_s": hils["tok_per_s"], "ms_per_step": hils["ms_per_step"],
                            "attended_tflops_attention_kernel": hils["attended_tflops_kernel"],
