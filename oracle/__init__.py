@@ -44,4 +44,7 @@ from .bsa_oracle import (  # noqa: F401
     sas_gates_grad,
     hils_rows_grad,
     prefill_backward,
+    ward_clusters,
+    lsa_index,
+    lsa_select_row,
 )

@@ -36,6 +36,10 @@ What is computed, step by step, in the pages' order:
                   SAS into the selector scores through the gates (the pages train the selector
                   end to end through these gates); for HiLS into the landmarks through the
                   retrieval scores.
+10. LSA index   -- the flat clustered indexer: Ward clusters of the landmarks of each completed
+                  segment, kept as centres plus member tables; a query scores the centres and
+                  the best clusters are expanded back to blocks (LSA page, "The index stops
+                  scanning the whole context", paragraphs 3-5).
 
 Readings taken where the pages are silent (each is listed in the design notes):
 * the selector vector is kept in float64 here (float32 on the device), never rounded to bf16;
@@ -647,3 +651,117 @@ def _hils_backward(q, k, v, idx, lm, dout, *, block: int = BLOCK, scale=None):
                     dv[b, g, pos] += dV
                     dlm[b, g, A] += dL
     return {"dq": dq, "dk": dk, "dv": dv, "dsc": np.zeros(idx.shape), "dlm": dlm}
+
+
+# --------------------------------------------------------------------------------------
+# 10. LSA flat clustered index (Ward clustering of the landmarks of completed segments)
+# --------------------------------------------------------------------------------------
+#
+# LSA page, "The index stops scanning the whole context", paragraphs 3-5: neighbouring keys are
+# merged first (the landmarks), Ward's algorithm groups similar ones into clusters, a completed
+# block's clustering is then fixed and kept as each cluster's centre plus the table of its
+# positions; a query is compared with the centres only, the best clusters are expanded back to
+# positions, and the start of the context and the recent window are added.  The flat variant
+# scans every centre.  Readings (the page gives no constants): a "completed block" is a segment
+# of seg_blocks consecutive landmarks (64 = 4096 tokens), clustered into n_clusters clusters; a
+# cluster's id is its lowest member block; the candidate blocks that are not inside a completed
+# segment lying wholly at or before the last candidate block are scored one by one against their
+# own landmark; units are expanded in score order until K blocks are chosen.
+
+def ward_clusters(X: np.ndarray, n_clusters: int):
+    """Ward agglomerative clustering of the rows of X [n, D] into n_clusters clusters.
+
+    Starting from singletons, the two clusters A, B whose merge increases the total
+    within-cluster sum of squares the least, |A||B| / (|A|+|B|) * ||mean_A - mean_B||^2, are
+    merged, until n_clusters remain.  Among equal increases the pair with the lexicographically
+    smallest (id_A, id_B) is merged, a cluster's id being its lowest member row.
+    Returns (members, merges): the ascending member rows of each cluster in id order, and the
+    (id_A, id_B) pairs merged, in order (id_A < id_B; the merged cluster keeps id_A).
+    """
+    X = np.asarray(X, dtype=np.float64)
+    n = X.shape[0]
+    size = np.ones(n)
+    mean = X.copy()
+    alive = np.ones(n, dtype=bool)
+    cost = np.full((n, n), np.inf)
+    iu = np.triu_indices(n, 1)
+    diff = X[iu[0]] - X[iu[1]]
+    cost[iu] = 0.5 * np.sum(diff * diff, axis=1)
+    merges = []
+    members = {i: [i] for i in range(n)}
+    for _ in range(n - n_clusters):
+        flat = int(np.argmin(cost))              # row-major: the first minimum is the smallest pair
+        a, b = divmod(flat, n)
+        mean[a] = (size[a] * mean[a] + size[b] * mean[b]) / (size[a] + size[b])
+        size[a] += size[b]
+        alive[b] = False
+        members[a] = sorted(members[a] + members.pop(b))
+        cost[b, :] = np.inf
+        cost[:, b] = np.inf
+        for k in np.nonzero(alive)[0]:
+            if k == a:
+                continue
+            d = mean[a] - mean[k]
+            cost[min(a, k), max(a, k)] = size[a] * size[k] / (size[a] + size[k]) * float(d @ d)
+        merges.append((a, b))
+    return [np.array(members[i], dtype=np.int64) for i in sorted(members)], merges
+
+
+def lsa_index(L: np.ndarray, seg_blocks: int = 64, n_clusters: int = 16):
+    """Flat LSA index of one (sequence, kv head): L [NB, D] landmarks (the rounded values).
+
+    For every completed segment s (blocks s*seg_blocks .. +seg_blocks, s < NB // seg_blocks):
+    Ward clusters of its landmarks; each cluster's member blocks (ascending, absolute block
+    indices) and centre (the mean of its members' landmarks).  Returns a list of
+    (members, centres [n_clusters, D], merges) per segment, merges in absolute block indices.
+    """
+    L = np.asarray(L, dtype=np.float64)
+    out = []
+    for s in range(L.shape[0] // seg_blocks):
+        lo = s * seg_blocks
+        mem, merges = ward_clusters(L[lo:lo + seg_blocks], n_clusters)
+        members = [m + lo for m in mem]
+        centres = np.stack([L[m].mean(axis=0) for m in members])
+        out.append((members, centres, [(a + lo, b + lo) for a, b in merges]))
+    return out
+
+
+def lsa_select_row(qbar_c: np.ndarray, L: np.ndarray, index, c: int, topk: int, n_sink: int = 1,
+                   n_local: int = 2, seg_blocks: int = 64):
+    """Attended set of query block c (ascending) and the scores aligned with it, flat LSA index.
+
+    Units: the clusters of completed segments whose blocks all lie at or before the last
+    candidate block c - n_local, scored qbar . centre; and every other candidate block
+    (n_sink <= j <= c - n_local) on its own, scored qbar . L_j.  Units are taken by score,
+    descending (equal scores: lower id first), and expanded into their candidate blocks
+    (ascending; sink blocks are attended anyway) until K blocks are chosen, the last unit cut
+    short if needed.  The sink and the local window are added as in select_row.  A chosen
+    block's score is its unit's score; a sink or local block's is qbar . L_j.
+    """
+    qbar_c = np.asarray(qbar_c, dtype=np.float64)
+    L = np.asarray(L, dtype=np.float64)
+    last = c - n_local
+    n_elig = min(len(index), max(0, (last + 1) // seg_blocks))
+    units = []
+    for s in range(n_elig):
+        members, centres, _ = index[s]
+        for m, centre in zip(members, centres):
+            blocks = [int(j) for j in m if j >= n_sink]
+            if blocks:
+                units.append((float(qbar_c @ centre), int(m[0]), blocks))
+    for j in range(max(n_sink, n_elig * seg_blocks), last + 1):
+        units.append((float(qbar_c @ L[j]), j, [j]))
+    units.sort(key=lambda u: (-u[0], u[1]))
+    chosen = {}
+    for score, _, blocks in units:
+        for j in blocks:
+            if len(chosen) >= topk:
+                break
+            chosen[j] = score
+        if len(chosen) >= topk:
+            break
+    sink = set(range(0, min(n_sink, c + 1)))
+    local = set(range(max(0, c - n_local + 1), c + 1))
+    A = np.array(sorted(sink | local | set(chosen)), dtype=np.int64)
+    sA = np.array([chosen[j] if j in chosen else float(qbar_c @ L[j]) for j in A])
+    return A, sA

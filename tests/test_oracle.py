@@ -753,3 +753,115 @@ def test_hils_backward_directional_finite_difference():
     an = sum(float(np.sum(g[n2] * dirs[n1])) for n1, n2 in (("q", "dq"), ("k", "dk"), ("v", "dv"),
                                                             ("lm", "dlm")))
     assert abs(fd - an) < 1e-6 * max(1.0, abs(an))
+
+
+# ---------------------------------------------------------------------------------------------
+# LSA flat clustered index
+# ---------------------------------------------------------------------------------------------
+
+def _partition(labels):
+    groups = {}
+    for i, lab in enumerate(labels):
+        groups.setdefault(int(lab), []).append(i)
+    return sorted(tuple(g) for g in groups.values())
+
+
+@pytest.mark.parametrize("n,D,k", [(24, 8, 4), (40, 16, 8), (64, 8, 16)])
+def test_ward_matches_scipy(n, D, k):
+    """Ward clusters = scipy's Ward linkage cut into k clusters (continuous random data, so no
+    equal merge costs)."""
+    from scipy.cluster.hierarchy import fcluster, linkage
+    X = _rng(50 + n).standard_normal((n, D))
+    members, merges = O.ward_clusters(X, k)
+    ref = _partition(fcluster(linkage(X, method="ward"), t=k, criterion="maxclust"))
+    assert sorted(tuple(m.tolist()) for m in members) == ref
+    assert len(merges) == n - k
+
+
+def test_ward_merges_are_greedy_minimal_sse_increases():
+    """Each merge raises the total within-cluster sum of squares by exactly the Ward cost, and
+    by no more than any other pair would (brute force over the points themselves)."""
+    X = _rng(53).standard_normal((14, 5))
+    _, merges = O.ward_clusters(X, 3)
+    clusters = {i: [i] for i in range(14)}
+
+    def sse(groups):
+        return sum(float(np.sum((X[g] - X[g].mean(axis=0)) ** 2)) for g in groups)
+
+    for a, b in merges:
+        before = sse(clusters.values())
+        incs = {}
+        ids = sorted(clusters)
+        for i, x in enumerate(ids):
+            for y in ids[i + 1:]:
+                trial = [g for kk, g in clusters.items() if kk not in (x, y)] + [clusters[x] + clusters[y]]
+                incs[(x, y)] = sse(trial) - before
+        assert (a, b) in incs and a < b
+        assert incs[(a, b)] <= min(incs.values()) + 1e-12
+        clusters[a] = clusters[a] + clusters.pop(b)
+
+
+def test_lsa_index_partitions_segments_and_centres_are_means():
+    r = _rng(54)
+    L = r.standard_normal((64 * 3 + 10, 6))
+    idx = O.lsa_index(L, seg_blocks=64, n_clusters=16)
+    assert len(idx) == 3
+    for s, (members, centres, merges) in enumerate(idx):
+        allb = np.sort(np.concatenate(members))
+        assert np.array_equal(allb, np.arange(64 * s, 64 * s + 64))
+        assert len(members) == 16 and len(merges) == 48
+        for m, ctr in zip(members, centres):
+            np.testing.assert_allclose(ctr, L[m].mean(axis=0), atol=1e-14)
+        assert [int(m[0]) for m in members] == sorted(int(m[0]) for m in members)
+
+
+@pytest.mark.parametrize("n_sink,n_local", [(1, 2), (0, 1), (2, 3)])
+def test_lsa_singleton_clusters_reduce_to_block_topk(n_sink, n_local):
+    """With one block per cluster every unit is a block scored by its own landmark (a cluster
+    of one has its landmark as centre), so the flat index selects exactly the blocks of the
+    plain top-K selection."""
+    r = _rng(55)
+    seg = 8
+    L = r.standard_normal((seg * 5 + 3, 6))
+    idx = O.lsa_index(L, seg_blocks=seg, n_clusters=seg)
+    for c in range(L.shape[0]):
+        qb = r.standard_normal(6)
+        for K in (0, 1, 3, 7, 50):
+            A, _ = O.lsa_select_row(qb, L, idx, c, K, n_sink, n_local, seg_blocks=seg)
+            B, _ = O.select_row(L @ qb, c, K, n_sink, n_local)
+            assert np.array_equal(A, B), (c, K)
+
+
+def test_lsa_selection_invariants():
+    """Chosen units outrank unchosen ones, at most one unit is cut short, the set size is
+    min(K, candidates) + sink + local, and K >= candidates attends every block up to c."""
+    r = _rng(56)
+    seg, ncl = 16, 4
+    L = r.standard_normal((seg * 6 + 5, 8))
+    idx = O.lsa_index(L, seg_blocks=seg, n_clusters=ncl)
+    for c in (0, 3, 17, 40, 70, L.shape[0] - 1):
+        qb = r.standard_normal(8)
+        for K in (2, 9, 25):
+            A, sA = O.lsa_select_row(qb, L, idx, c, K, 1, 2, seg_blocks=seg)
+            last = c - 2
+            n_cand = max(0, last - 1 + 1)
+            forced = set(range(min(1, c + 1))) | set(range(max(0, c - 1), c + 1))
+            assert A.size == min(K, n_cand) + len(forced)
+            chosen = [j for j in A if j not in forced]
+            n_elig = min(len(idx), max(0, (last + 1) // seg))
+            units = []
+            for s in range(n_elig):
+                for m, ctr in zip(idx[s][0], idx[s][1]):
+                    bl = [int(j) for j in m if j >= 1]
+                    if bl:
+                        units.append((float(qb @ ctr), bl))
+            for j in range(max(1, n_elig * seg), last + 1):
+                units.append((float(qb @ L[j]), [j]))
+            full = [u for u in units if set(u[1]) <= set(chosen)]
+            part = [u for u in units if set(u[1]) & set(chosen) and not set(u[1]) <= set(chosen)]
+            none = [u for u in units if not set(u[1]) & set(chosen)]
+            assert len(part) <= 1
+            if none and (full or part):
+                assert min(u[0] for u in full + part) >= max(u[0] for u in none)
+            if K >= n_cand:
+                assert np.array_equal(A, np.arange(0, c + 1))
