@@ -13,7 +13,11 @@ Entry points mirror the C ABI in include/bsa.h:
 * ``attend_decode(q, kc, vc, idx, sc, lm, mode)`` -> (out, lse)
 * ``attend_prefill_backward(q, k, v, idx, sc, out, lse, dout, mode, lm)`` -> (dq, dk, dv, dsc, dlm)
 
-and ``prefill(q, k, v, ...)`` / ``decode(q, kc, vc, lm, ...)`` chain them.
+* ``lsa_build_index(lm, seg_blocks, n_clusters)``  -> flat clustered index (dict of tensors)
+* ``lsa_select(q, lm, index, topk=...)``          -> (idx, sc) from the clustered index
+
+and ``prefill(q, k, v, ...)`` / ``decode(q, kc, vc, lm, ...)`` chain them (``prefill_lsa`` /
+``decode_lsa`` with the clustered index in place of the per-block top-K).
 """
 
 from __future__ import annotations
@@ -27,6 +31,7 @@ __all__ = [
     "MODES", "Params", "library_path", "load_library", "pool_landmarks", "select_topk",
     "attend_prefill", "attend_decode", "select_workspace_bytes", "decode_workspace_bytes",
     "prefill", "decode", "BsaError", "attend_prefill_backward", "backward_workspace_bytes",
+    "lsa_build_index", "lsa_select", "prefill_lsa", "decode_lsa",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -93,6 +98,12 @@ def load_library():
     lib.bsa_backward_workspace_bytes.restype = ctypes.c_size_t
     lib.bsa_attend_prefill_backward.argtypes = [P] + [vp] * 15 + [ctypes.c_size_t, vp]
     lib.bsa_attend_prefill_backward.restype = st
+    lib.bsa_lsa_build_index.argtypes = [P, vp, i32, i32, vp, vp, vp, vp, vp]
+    lib.bsa_lsa_build_index.restype = st
+    lib.bsa_lsa_select_workspace_bytes.argtypes = [P]
+    lib.bsa_lsa_select_workspace_bytes.restype = ctypes.c_size_t
+    lib.bsa_lsa_select.argtypes = [P, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.bsa_lsa_select.restype = st
     lib.bsa_status_string.argtypes = [ctypes.c_int]
     lib.bsa_status_string.restype = ctypes.c_char_p
     lib.bsa_last_error.argtypes = []
@@ -350,6 +361,64 @@ def attend_prefill_backward(q, k, v, idx, sc, out, lse, dout, *, mode="plain", l
     return dq, dk, dv, dsc, (dlm if mode == "hils" else None)
 
 
+def lsa_build_index(lm: torch.Tensor, *, seg_blocks: int = 64, n_clusters: int = 16) -> dict:
+    """Flat clustered index of landmarks lm [B,Hkv,NB,D]: Ward clusters of every completed
+    segment of seg_blocks landmarks.  Returns dict(centres [B,Hkv,NS*n_clusters,D] float32,
+    members [B,Hkv,NS,seg_blocks] int32, offsets [B,Hkv,NS,n_clusters+1] int32,
+    merges [B,Hkv,NS,seg_blocks-n_clusters,2] int32, seg_blocks, n_clusters), NS = NB // seg_blocks."""
+    lib = load_library()
+    _need(lm, "lm", ndim=4)
+    B, Hkv, NB, D = lm.shape
+    NS = NB // seg_blocks if seg_blocks > 0 else 0
+    dev = lm.device
+    centres = torch.empty((B, Hkv, NS * n_clusters, D), dtype=torch.float32, device=dev)
+    members = torch.empty((B, Hkv, NS, seg_blocks), dtype=torch.int32, device=dev)
+    offsets = torch.empty((B, Hkv, NS, n_clusters + 1), dtype=torch.int32, device=dev)
+    merges = torch.empty((B, Hkv, NS, max(seg_blocks - n_clusters, 0), 2), dtype=torch.int32,
+                         device=dev)
+    p = make_params(B=B, Hq=Hkv, Hkv=Hkv, D=D, seq_q=NB * 64, seq_k=NB * 64, dtype=lm.dtype)
+    _check("bsa_lsa_build_index",
+           lib.bsa_lsa_build_index(ctypes.byref(p), _ptr(lm), seg_blocks, n_clusters,
+                                   _ptr(centres), _ptr(members), _ptr(offsets), _ptr(merges),
+                                   _stream(dev)))
+    return {"centres": centres, "members": members, "offsets": offsets, "merges": merges,
+            "seg_blocks": seg_blocks, "n_clusters": n_clusters}
+
+
+def lsa_select(q: torch.Tensor, lm: torch.Tensor, index: dict, *, topk: int,
+               seq_k: int | None = None, n_sink: int = 1, n_local: int = 2, ws=None, idx=None,
+               sc=None):
+    """Attended block sets from the flat clustered index (prefill: q [B,Hq,T,D]; decode:
+    q [B,Hq,1,D] with seq_k cached tokens).  Same layout as select_topk's output."""
+    lib = load_library()
+    _need(q, "q", ndim=4)
+    _need(lm, "lm", dtype=q.dtype, ndim=4)
+    B, Hq, Tq, D = q.shape
+    Hkv = lm.shape[1]
+    Tk = Tq if seq_k is None else int(seq_k)
+    if lm.shape != (B, Hkv, _nblocks(Tk), D):
+        raise ValueError(f"lm shape {tuple(lm.shape)} does not match {(B, Hkv, _nblocks(Tk), D)}")
+    p = make_params(B=B, Hq=Hq, Hkv=Hkv, D=D, seq_q=Tq, seq_k=Tk, dtype=q.dtype, topk=topk,
+                    n_sink=n_sink, n_local=n_local)
+    R = 1 if (Tq == 1 and Tk != 1) else _nblocks(Tq)
+    NA = n_sink + n_local + topk
+    if idx is None:
+        idx = torch.empty((B, Hkv, R, NA), dtype=torch.int32, device=q.device)
+    if sc is None:
+        sc = torch.empty((B, Hkv, R, NA), dtype=torch.float32, device=q.device)
+    need = int(lib.bsa_lsa_select_workspace_bytes(ctypes.byref(p)))
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    NS = index["members"].shape[2]
+    cen, mem, off = (index["centres"], index["members"], index["offsets"]) if NS else (None,) * 3
+    _check("bsa_lsa_select",
+           lib.bsa_lsa_select(ctypes.byref(p), _ptr(q), _ptr(lm), index["seg_blocks"],
+                              index["n_clusters"], _ptr(cen), _ptr(mem), _ptr(off), _ptr(idx),
+                              _ptr(sc), _ptr(ws), 0 if ws is None else ws.numel(),
+                              _stream(q.device)))
+    return idx, sc
+
+
 # ---------------------------------------------------------------------------------------------
 # whole path
 # ---------------------------------------------------------------------------------------------
@@ -481,3 +550,28 @@ def decode_paged(q, k_pool, v_pool, page_table, seq_lens, *, topk: int, mode: st
                                    n_sink=n_sink, n_local=n_local, scale=scale,
                                    want_lse=want_lse and mode != "hils")
     return {"out": out, "lse": lse, "idx": idx, "sc": sc, "lm": lm}
+
+
+def prefill_lsa(q, k, v, *, topk: int, mode: str = "plain", seg_blocks: int = 64,
+                n_clusters: int = 16, n_sink: int = 1, n_local: int = 2, scale: float = 0.0,
+                want_lse: bool = False):
+    """Pool, build the flat clustered index, select from it and attend, for a prefill; returns
+    dict(out, lse, idx, sc, lm, index)."""
+    lm = pool_landmarks(k)
+    index = lsa_build_index(lm, seg_blocks=seg_blocks, n_clusters=n_clusters)
+    idx, sc = lsa_select(q, lm, index, topk=topk, n_sink=n_sink, n_local=n_local)
+    out, lse = attend_prefill(q, k, v, idx, sc, lm if mode == "hils" else None, mode=mode,
+                              topk=topk, n_sink=n_sink, n_local=n_local, scale=scale,
+                              want_lse=want_lse and mode != "hils")
+    return {"out": out, "lse": lse, "idx": idx, "sc": sc, "lm": lm, "index": index}
+
+
+def decode_lsa(q, kc, vc, lm, index, *, topk: int, mode: str = "plain", n_sink: int = 1,
+               n_local: int = 2, scale: float = 0.0, want_lse: bool = False):
+    """Select from the flat clustered index and attend, for one decode step (q [B,Hq,1,D])."""
+    idx, sc = lsa_select(q, lm, index, topk=topk, seq_k=kc.shape[2], n_sink=n_sink,
+                         n_local=n_local)
+    out, lse = attend_decode(q, kc, vc, idx, sc, lm if mode == "hils" else None, mode=mode,
+                             topk=topk, n_sink=n_sink, n_local=n_local, scale=scale,
+                             want_lse=want_lse and mode != "hils")
+    return {"out": out, "lse": lse, "idx": idx, "sc": sc}

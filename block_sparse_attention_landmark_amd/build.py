@@ -13,7 +13,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libbsa.so")
 SOURCES = ["bsa_api.hip", "pool.hip", "select.hip", "attend_prefill.hip", "attend_decode.hip",
-           "attend_f32.hip", "attend_backward.hip"]
+           "attend_f32.hip", "attend_backward.hip", "lsa.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

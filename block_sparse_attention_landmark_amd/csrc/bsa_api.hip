@@ -208,6 +208,72 @@ bsa_status_t bsa_attend_prefill(const bsa_params_t* params, const void* q, const
                     "attend_prefill");
 }
 
+// ---- flat clustered (LSA) index ----
+
+namespace {
+bsa_status_t check_lsa(const bsa::Shape& s, int32_t seg_blocks, int32_t n_clusters) {
+  if (seg_blocks < 1 || seg_blocks > 64 || n_clusters < 1 || n_clusters > seg_blocks)
+    return fail(BSA_ERR_UNSUPPORTED, "need 1 <= n_clusters <= seg_blocks <= 64 (got %d, %d)",
+                n_clusters, seg_blocks);
+  if (!bsa::lsa_shape_ok(s, seg_blocks, n_clusters))
+    return fail(BSA_ERR_UNSUPPORTED,
+                "the LSA selection sorts at most 8192 units per row (segments x n_clusters + "
+                "seg_blocks) and chooses at most 2048 blocks (topk)");
+  return BSA_OK;
+}
+}  // namespace
+
+bsa_status_t bsa_lsa_build_index(const bsa_params_t* params, const void* lm, int32_t seg_blocks,
+                                 int32_t n_clusters, float* centres, int32_t* members,
+                                 int32_t* offsets, int32_t* merges, void* stream) {
+  bsa::Shape s;
+  BSA_TRY(make_shape(params, kPool, &s));
+  BSA_TRY(check_lsa(s, seg_blocks, n_clusters));
+  if (s.NB / seg_blocks == 0) return ok();       // no completed segment: nothing to build
+  BSA_TRY(check_ptr(lm, "lm"));
+  BSA_TRY(check_ptr(centres, "centres"));
+  BSA_TRY(check_ptr(members, "members"));
+  BSA_TRY(check_ptr(offsets, "offsets"));
+  if (seg_blocks > n_clusters) BSA_TRY(check_ptr(merges, "merges"));
+  return hip_result(bsa::launch_lsa_build(s, lm, seg_blocks, n_clusters, centres, members, offsets,
+                                          merges, (hipStream_t)stream),
+                    "lsa_build_index");
+}
+
+size_t bsa_lsa_select_workspace_bytes(const bsa_params_t* params) {
+  bsa::Shape s;
+  if (make_shape(params, kSelect, &s) != BSA_OK) return 0;
+  return s.decode ? 0 : bsa::select_ws_qbar_bytes(s);
+}
+
+bsa_status_t bsa_lsa_select(const bsa_params_t* params, const void* q, const void* lm,
+                            int32_t seg_blocks, int32_t n_clusters, const float* centres,
+                            const int32_t* members, const int32_t* offsets, int32_t* idx,
+                            float* sc, void* ws, size_t ws_bytes, void* stream) {
+  bsa::Shape s;
+  BSA_TRY(make_shape(params, kSelect, &s));
+  BSA_TRY(check_lsa(s, seg_blocks, n_clusters));
+  BSA_TRY(check_ptr(q, "q"));
+  BSA_TRY(check_ptr(lm, "lm"));
+  BSA_TRY(check_ptr(idx, "idx"));
+  BSA_TRY(check_ptr(sc, "sc"));
+  if (s.NB / seg_blocks > 0) {
+    BSA_TRY(check_ptr(centres, "centres"));
+    BSA_TRY(check_ptr(members, "members"));
+    BSA_TRY(check_ptr(offsets, "offsets"));
+  }
+  const size_t need = s.decode ? 0 : bsa::select_ws_qbar_bytes(s);
+  if (need > 0) {
+    if (ws == nullptr || ws_bytes < need)
+      return fail(BSA_ERR_WORKSPACE, "LSA selection workspace needs %zu bytes (got %zu%s)", need,
+                  ws_bytes, ws == nullptr ? ", NULL pointer" : "");
+    if (((uintptr_t)ws & 255u) != 0) return fail(BSA_ERR_ALIGN, "ws is not 256-byte aligned");
+  }
+  return hip_result(bsa::launch_lsa_select(s, q, lm, seg_blocks, n_clusters, centres, members,
+                                           offsets, idx, sc, (float*)ws, (hipStream_t)stream),
+                    "lsa_select");
+}
+
 // ---- backward of PLAIN / SAS prefill ----
 
 namespace {

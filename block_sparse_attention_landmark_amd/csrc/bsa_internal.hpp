@@ -70,4 +70,13 @@ hipError_t launch_attend_backward(const Shape& s, const void* q, const void* k, 
                                   void* dk, void* dv, float* dsc, float* dlm, void* ws,
                                   hipStream_t st);
 
+// Flat clustered (LSA) index: shape limits, index build, selection over it.
+bool lsa_shape_ok(const Shape& s, int seg, int nc);
+hipError_t launch_lsa_build(const Shape& s, const void* lm, int seg, int nc, float* centres,
+                            int32_t* members, int32_t* offsets, int32_t* merges, hipStream_t st);
+hipError_t launch_lsa_select(const Shape& s, const void* q, const void* lm, int seg, int nc,
+                             const float* centres, const int32_t* members,
+                             const int32_t* offsets, int32_t* idx, float* sc, float* qbar,
+                             hipStream_t st);
+
 }  // namespace bsa

@@ -186,6 +186,52 @@ bsa_status_t bsa_attend_decode_paged(const bsa_params_t* params, const void* q,
                                      void* stream);
 
 /*
+ * Flat clustered index over the landmarks (LSA page, "The index stops scanning the whole
+ * context", paragraphs 3-5: similar pooled keys are grouped by Ward's algorithm once a block of
+ * the context is complete, and kept as each cluster's centre plus the table of its positions).
+ * Every completed segment s of seg_blocks landmarks (blocks s*seg_blocks .. +seg_blocks, for
+ * s < NS = floor(NB / seg_blocks); NB = ceil(seq_k / 64)) is clustered into n_clusters clusters:
+ * starting from single landmarks, the two clusters A, B with the smallest
+ * |A||B| / (|A|+|B|) * ||mean_A - mean_B||^2 are merged (equal costs: the smallest pair of ids,
+ * a cluster's id being its lowest block; float32 arithmetic) until n_clusters remain.
+ *   lm       [B,Hkv,NB,D] landmarks (params->dtype) from bsa_pool_landmarks
+ *   centres  [B,Hkv,NS*n_clusters,D] float32 output: the mean of each cluster's landmarks
+ *   members  [B,Hkv,NS,seg_blocks] int32 output: each segment's blocks grouped by cluster
+ *            (clusters in id order, blocks ascending), absolute block indices
+ *   offsets  [B,Hkv,NS,n_clusters+1] int32 output: cluster r of a segment is members[o_r .. o_r+1)
+ *   merges   [B,Hkv,NS,seg_blocks-n_clusters,2] int32 output: the merged pairs of ids, in order
+ *            (may be NULL when seg_blocks == n_clusters)
+ * Limits: 1 <= n_clusters <= seg_blocks <= 64.  With NS = 0 nothing is launched.
+ */
+bsa_status_t bsa_lsa_build_index(const bsa_params_t* params, const void* lm, int32_t seg_blocks,
+                                 int32_t n_clusters, float* centres, int32_t* members,
+                                 int32_t* offsets, int32_t* merges, void* stream);
+
+/* Workspace bytes of bsa_lsa_select (prefill: the selector vectors; decode: 0). */
+size_t bsa_lsa_select_workspace_bytes(const bsa_params_t* params);
+
+/*
+ * Attended block sets from the flat clustered index (prefill: one row per 64-token query
+ * block; decode: seq_q == 1, one row for the query at position seq_k - 1), same layout as
+ * bsa_select_topk's.  The selector vector qbar is that of bsa_select_topk.  With
+ * last = c - n_local the last candidate block, the units are: the clusters of the completed
+ * segments lying wholly at or before block last (first NE = min(NS, (last+1)/seg_blocks)
+ * segments), scored qbar . centre, and every other candidate block j (max(n_sink, NE*seg_blocks)
+ * <= j <= last) on its own, scored qbar . L_j (float32).  Units are taken by score, descending
+ * (equal scores: the lower id first), and expanded into their candidate blocks (blocks >= n_sink,
+ * ascending) until min(topk, candidates) blocks are chosen, the last unit cut short if needed.
+ * Row c lists the sink blocks, the chosen blocks ascending, the local window, then -1; sc holds
+ * a chosen block's unit score and qbar . L_j for sink and local blocks (0 in the padding).
+ *   q, lm: as for bsa_select_topk; centres, members, offsets: from bsa_lsa_build_index with the
+ *   same seg_blocks and n_clusters (may be NULL when NS = 0); ws: bsa_lsa_select_workspace_bytes.
+ * Limits: as bsa_lsa_build_index, plus NS * n_clusters + seg_blocks <= 8192 and topk <= 2048.
+ */
+bsa_status_t bsa_lsa_select(const bsa_params_t* params, const void* q, const void* lm,
+                            int32_t seg_blocks, int32_t n_clusters, const float* centres,
+                            const int32_t* members, const int32_t* offsets, int32_t* idx,
+                            float* sc, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Workspace bytes of bsa_attend_prefill_backward for these params (0 if the params are
  * rejected by that call).
  */
