@@ -18,6 +18,8 @@ Reported beside it, measured in the same run:
 * the backward of the SAS prefill (dq, dk, dv and the selector-score gradient) on the same
   workload, and the HiLS backward (dq, dk, dv and the landmark gradient) on the same shape and
   attended sets, each timed per call (--no-backward skips both);
+* the same prefill step with the flat clustered (LSA) index -- pool, Ward index build,
+  selection over the index, attention -- each part timed (--no-lsa skips it);
 * optionally the HiLS workload at 1M tokens (--hils);
 * the float64 oracle timed on the host cores on a bounded sample of the prefill workload.
 
@@ -86,6 +88,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-lsa", action="store_true")
     ap.add_argument("--hils", action="store_true", help="also time the HiLS workload at 1M tokens")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3)")
@@ -230,6 +233,53 @@ def bench_backward(torch, bsa, synth, name, tensors, steps, warmup, mode=None):
                         "scope": "whole backward call (all its kernels)"}}
     log(f"[bench] backward: {json.dumps(res)}")
     del ws, dq, dk, dv, dsc, dlm, dout, out, lse
+    return res
+
+
+def bench_lsa(torch, bsa, synth, name, tensors, steps, warmup, seg_blocks=64, n_clusters=16):
+    """The prefill step with the flat clustered index in place of the per-block top-K: pool,
+    Ward index build, selection over the index, attention; each part timed with HIP events."""
+    w = synth.WORKLOADS[name]
+    B, Hq, Hkv, T, D, K, mode = w["B"], w["Hq"], w["Hkv"], w["T"], w["D"], w["topk"], w["mode"]
+    q, k, v, lm, idx, sc, out = tensors[:7]
+    index = bsa.lsa_build_index(lm, seg_blocks=seg_blocks, n_clusters=n_clusters)
+    p = bsa.make_params(B=B, Hq=Hq, Hkv=Hkv, D=D, seq_q=T, seq_k=T, dtype=q.dtype, topk=K)
+    ws = torch.empty(max(bsa.select_workspace_bytes(p), 256), dtype=torch.uint8, device="cuda")
+    ev = {n: Events(torch) for n in ("pool", "build", "select", "attend")}
+
+    def step(record):
+        def timed(n, fn):
+            if record:
+                ev[n].start()
+            fn()
+            if record:
+                ev[n].stop()
+        timed("pool", lambda: bsa.pool_landmarks(k, out=lm))
+        timed("build", lambda: bsa.lsa_build_index(lm, seg_blocks=seg_blocks,
+                                                   n_clusters=n_clusters))
+        timed("select", lambda: bsa.lsa_select(q, lm, index, topk=K, ws=ws, idx=idx, sc=sc))
+        timed("attend", lambda: bsa.attend_prefill(q, k, v, idx, sc, None, mode=mode, topk=K,
+                                                   out=out))
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log(f"[bench] lsa {name}: timing {steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = {n: sum(e.ms()) / steps for n, e in ev.items()}
+    NB = (T + 63) // 64
+    NS = NB // seg_blocks
+    res = {"workload": f"{name} with the flat clustered index: {NS} segments of {seg_blocks} "
+                       f"landmarks x {n_clusters} Ward clusters per kv group; a query block "
+                       f"scores at most {NS * n_clusters + seg_blocks} units instead of {NB} "
+                       f"landmarks",
+           "tok_per_s": B * T * steps / wall, "ms_per_step": wall * 1e3 / steps,
+           "breakdown_ms": ms}
+    log(f"[bench] lsa: {json.dumps(res)}")
     return res
 
 
@@ -406,6 +456,10 @@ def main():
         log("[bench] timing the oracle on the host cores")
         cpu = cpu_baseline(torch, tensors, name, synth)
         log(f"[bench] cpu baseline: {cpu['value']:.1f} tok/s")
+    lsa = None
+    if not args.no_lsa:
+        lsa = bench_lsa(torch, bsa, synth, name, tensors, max(3, args.steps // 2), 1)
+        torch.cuda.empty_cache()
     bwd = bwd_hils = None
     if not args.no_backward:
         bwd = bench_backward(torch, bsa, synth, name, tensors, max(3, args.steps // 4), 1)
@@ -478,6 +532,8 @@ def main():
                                                      "traffic_bytes_per_step")}}
     if dec_paged is not None:
         line["decode_paged"] = dec_paged
+    if lsa is not None:
+        line["lsa_prefill"] = lsa
     if bwd is not None:
         line["backward"] = bwd
     if bwd_hils is not None:

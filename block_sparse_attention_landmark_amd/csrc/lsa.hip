@@ -220,7 +220,9 @@ __device__ __forceinline__ void lsa_bitonic(uint64_t* key, int* pay, int m) {
     }
 }
 
-template <int D, typename TIN>
+// UCAP / KCAP: the units and chosen blocks one row can hold (LDS is sized by them, so a small
+// variant lets several rows share a CU)
+template <int D, typename TIN, int UCAP, int KCAP>
 __global__ __launch_bounds__(256) void lsa_select_kernel(
     const float* __restrict__ qbar, const TIN* __restrict__ q, const TIN* __restrict__ lm,
     const float* __restrict__ centres, const int32_t* __restrict__ members,
@@ -230,10 +232,10 @@ __global__ __launch_bounds__(256) void lsa_select_kernel(
   __shared__ float qv[D];
   // sort key: (order-preserving key of the score, inverted) << 32 | unit id; payload: unit index
   // | candidate blocks << 16 (a unit's score is recovered from its key)
-  __shared__ uint64_t skey[kLsaMaxUnits];
-  __shared__ int spay[kLsaMaxUnits];
-  __shared__ int ch_blk[kLsaMaxK];
-  __shared__ float ch_sc[kLsaMaxK];
+  __shared__ uint64_t skey[UCAP];
+  __shared__ int spay[UCAP];
+  __shared__ int ch_blk[KCAP];
+  __shared__ float ch_sc[KCAP];
   __shared__ int wsum[4];
   const int row = blockIdx.x, bg = blockIdx.y;
   const int b = bg / Hkv, g = bg % Hkv;
@@ -254,6 +256,7 @@ __global__ __launch_bounds__(256) void lsa_select_kernel(
   __syncthreads();
   auto dot_lm = [&](int j) {
     float acc = 0.0f;
+#pragma unroll 8
     for (int d = 0; d < D; ++d) acc = fmaf(qv[d], (float)Lg[(size_t)j * D + d], acc);
     return acc;
   };
@@ -265,30 +268,46 @@ __global__ __launch_bounds__(256) void lsa_select_kernel(
   const int n_units = n_elig * NC + n_single;
   int m = 1;
   while (m < n_units) m <<= 1;
-  // unit u: a cluster (u < n_elig * NC) or the single block single_lo + u - n_elig * NC
-  for (int u = tid; u < m; u += 256) {
-    uint64_t key = ~(uint64_t)0;
-    float s = -INFINITY;
+  // unit u: a cluster (u < n_elig * NC) or the single block single_lo + u - n_elig * NC; its
+  // score is a dot product over D spread on LPU lanes (8 elements each), UPW units per wave
+  constexpr int LPU = D / 8;
+  constexpr int UPW = kWave / LPU;
+  const int sub = lane % LPU, uw = lane / LPU;
+  float qf[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) qf[e] = qv[sub * 8 + e];
+  for (int u0 = w * UPW; u0 < m; u0 += 4 * UPW) {
+    const int u = u0 + uw;
+    float part = 0.0f;
     int size = 0;
+    uint32_t id = 0;
     if (u < n_elig * NC) {
       const int sg = u / NC, r = u % NC;
       const size_t sb = (size_t)bg * NS + sg;
       const int o0 = offsets[sb * (NC + 1) + r], o1 = offsets[sb * (NC + 1) + r + 1];
       const int32_t* mem = members + sb * SEG;
       for (int i = o0; i < o1; ++i) size += mem[i] >= n_sink;
-      const float* ctr = centres + (sb * NC + r) * D;
-      float acc = 0.0f;
-      for (int d = 0; d < D; ++d) acc = fmaf(qv[d], ctr[d], acc);
-      s = acc;
-      if (size > 0) key = ((uint64_t)(~float_key(s)) << 32) | (uint32_t)mem[o0];
+      id = (uint32_t)mem[o0];
+      const f32x4* ctr = reinterpret_cast<const f32x4*>(centres + (sb * NC + r) * D + sub * 8);
+      const f32x4 c0 = ctr[0], c1 = ctr[1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) part = fmaf(qf[e], c0[e], fmaf(qf[4 + e], c1[e], part));
     } else if (u < n_units) {
       const int j = single_lo + (u - n_elig * NC);
-      s = dot_lm(j);
+      const TIN* lrow = Lg + (size_t)j * D + sub * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part = fmaf(qf[e], (float)lrow[e], part);
       size = 1;
-      key = ((uint64_t)(~float_key(s)) << 32) | (uint32_t)j;
+      id = (uint32_t)j;
     }
-    skey[u] = key;
-    spay[u] = u | (size << 16);
+#pragma unroll
+    for (int o = LPU / 2; o > 0; o >>= 1) part += __shfl_xor(part, o, kWave);
+    if (sub == 0 && u < m) {
+      uint64_t key = ~(uint64_t)0;
+      if (u < n_units && size > 0) key = ((uint64_t)(~float_key(part)) << 32) | id;
+      skey[u] = key;
+      spay[u] = u | (size << 16);
+    }
   }
   __syncthreads();
   lsa_bitonic(skey, spay, m);
@@ -409,17 +428,29 @@ hipError_t launch_lsa_select(const Shape& s, const void* q, const void* lm, int 
   }
   const int ns = s.NB / seg;
   dim3 grid(s.R, s.B * s.Hkv);
-#define BSA_LSEL(D_, T_)                                                                        \
-  hipLaunchKernelGGL((lsa_select_kernel<D_, T_>), grid, dim3(256), 0, st, qbar, (const T_*)q,   \
-                     (const T_*)lm, centres, members, offsets, idx, sc, s.Hq, s.Hkv, s.G, s.NB,  \
-                     ns, seg, nc, s.R, s.decode ? s.c_dec : -1, s.topk, s.n_sink, s.n_local, s.NA)
+  const bool small = ns * nc + seg <= 1024 && s.topk <= 256;
+#define BSA_LSEL(D_, T_, U_, K_)                                                                 \
+  hipLaunchKernelGGL((lsa_select_kernel<D_, T_, U_, K_>), grid, dim3(256), 0, st, qbar,           \
+                     (const T_*)q, (const T_*)lm, centres, members, offsets, idx, sc, s.Hq, s.Hkv, \
+                     s.G, s.NB, ns, seg, nc, s.R, s.decode ? s.c_dec : -1, s.topk, s.n_sink,       \
+                     s.n_local, s.NA)
+#define BSA_LSEL_CAP(D_, T_)                          \
+  if (small) BSA_LSEL(D_, T_, 1024, 256);             \
+  else BSA_LSEL(D_, T_, kLsaMaxUnits, kLsaMaxK);
   if (s.D == 128) {
-    if (s.bf16) BSA_LSEL(128, bf16);
-    else BSA_LSEL(128, float);
+    if (s.bf16) {
+      BSA_LSEL_CAP(128, bf16)
+    } else {
+      BSA_LSEL_CAP(128, float)
+    }
   } else {
-    if (s.bf16) BSA_LSEL(64, bf16);
-    else BSA_LSEL(64, float);
+    if (s.bf16) {
+      BSA_LSEL_CAP(64, bf16)
+    } else {
+      BSA_LSEL_CAP(64, float)
+    }
   }
+#undef BSA_LSEL_CAP
 #undef BSA_LSEL
   return hipGetLastError();
 }
