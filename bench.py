@@ -226,9 +226,9 @@ def bench_backward(torch, bsa, synth, name, tensors, steps, warmup, mode=None):
                                "recomputed S, dP, dQ, dK, dV (2*D each)",
            "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
                         "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
-                        "traffic": (profiled_traffic("attend_backward_sas_bf16_128k.md",
-                                                     "traffic_bytes_per_call")
-                                    if mode == "sas" else None),
+                        "traffic": profiled_traffic("attend_backward_sas_bf16_128k.md",
+                                                    "traffic_bytes_per_call" if mode == "sas"
+                                                    else "traffic_bytes_per_call_hils"),
                         "traffic_unit": "bytes per call (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE)",
                         "scope": "whole backward call (all its kernels)"}}
     log(f"[bench] backward: {json.dumps(res)}")
