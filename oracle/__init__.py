@@ -47,4 +47,6 @@ from .bsa_oracle import (  # noqa: F401
     ward_clusters,
     lsa_index,
     lsa_select_row,
+    lsa_tree_centres,
+    lsa_tree_select_row,
 )

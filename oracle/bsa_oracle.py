@@ -40,6 +40,8 @@ What is computed, step by step, in the pages' order:
                   segment, kept as centres plus member tables; a query scores the centres and
                   the best clusters are expanded back to blocks (LSA page, "The index stops
                   scanning the whole context", paragraphs 3-5).
+11. LSA tree    -- the same clusters under segments and groups of segments, walked by beam
+                  search (the same page, paragraph 5).
 
 Readings taken where the pages are silent (each is listed in the design notes):
 * the selector vector is kept in float64 here (float32 on the device), never rounded to bf16;
@@ -749,6 +751,82 @@ def lsa_select_row(qbar_c: np.ndarray, L: np.ndarray, index, c: int, topk: int, 
             blocks = [int(j) for j in m if j >= n_sink]
             if blocks:
                 units.append((float(qbar_c @ centre), int(m[0]), blocks))
+    for j in range(max(n_sink, n_elig * seg_blocks), last + 1):
+        units.append((float(qbar_c @ L[j]), j, [j]))
+    units.sort(key=lambda u: (-u[0], u[1]))
+    chosen = {}
+    for score, _, blocks in units:
+        for j in blocks:
+            if len(chosen) >= topk:
+                break
+            chosen[j] = score
+        if len(chosen) >= topk:
+            break
+    sink = set(range(0, min(n_sink, c + 1)))
+    local = set(range(max(0, c - n_local + 1), c + 1))
+    A = np.array(sorted(sink | local | set(chosen)), dtype=np.int64)
+    sA = np.array([chosen[j] if j in chosen else float(qbar_c @ L[j]) for j in A])
+    return A, sA
+
+
+# --------------------------------------------------------------------------------------
+# 11. LSA tree index: beam search over groups of segments, segments, clusters
+# --------------------------------------------------------------------------------------
+#
+# LSA page, "The index stops scanning the whole context", paragraph 5: the tree variant joins
+# the clusters into a hierarchy and walks it with beam search, keeping a few branches per level,
+# so a query makes a logarithmic number of comparisons.  Readings: above the Ward clusters of a
+# segment sits the segment; above segments, groups of `fanout` consecutive segments; a node's
+# centre is the mean of the landmarks under it.  A query uses only nodes lying wholly within its
+# eligible prefix (the completed segments at or before its last candidate block); eligible
+# segments not filling a whole group stand at the top level themselves.  At each level the
+# `beam` best children of the kept nodes survive (equal scores: lower id first); the kept
+# clusters, with the not yet clustered candidate blocks, are then expanded as in the flat index.
+
+def lsa_tree_centres(L: np.ndarray, seg_blocks: int = 64, fanout: int = 8):
+    """Centres of the segments [NS, D] and of the whole groups of `fanout` segments [NG, D]."""
+    L = np.asarray(L, dtype=np.float64)
+    NS = L.shape[0] // seg_blocks
+    seg = np.stack([L[s * seg_blocks:(s + 1) * seg_blocks].mean(axis=0) for s in range(NS)]) \
+        if NS else np.zeros((0, L.shape[1]))
+    NG = NS // fanout
+    grp = np.stack([seg[gi * fanout:(gi + 1) * fanout].mean(axis=0) for gi in range(NG)]) \
+        if NG else np.zeros((0, L.shape[1]))
+    return seg, grp
+
+
+def lsa_tree_select_row(qbar_c, L, index, c: int, topk: int, n_sink: int = 1, n_local: int = 2,
+                        seg_blocks: int = 64, fanout: int = 8, beam: int = 8):
+    """Attended set of query block c and its scores, beam search over the tree (see above)."""
+    qbar_c = np.asarray(qbar_c, dtype=np.float64)
+    L = np.asarray(L, dtype=np.float64)
+    seg_c, grp_c = lsa_tree_centres(L, seg_blocks, fanout)
+    last = c - n_local
+    n_elig = min(len(index), max(0, (last + 1) // seg_blocks))
+
+    def best(cands):                      # cands: (score, id, payload); keep the beam best
+        cands = sorted(cands, key=lambda x: (-x[0], x[1]))
+        return cands[:beam]
+
+    n_grp = n_elig // fanout
+    top = [(float(qbar_c @ grp_c[gi]), gi * fanout * seg_blocks, ("g", gi)) for gi in range(n_grp)]
+    top += [(float(qbar_c @ seg_c[s]), s * seg_blocks, ("s", s)) for s in range(n_grp * fanout, n_elig)]
+    segs = []
+    for _, _, (kind, i) in best(top):
+        if kind == "g":
+            segs += list(range(i * fanout, (i + 1) * fanout))
+        else:
+            segs.append(i)
+    kept_segs = [p[1] for _, _, p in best([(float(qbar_c @ seg_c[s]), s * seg_blocks, ("s", s))
+                                          for s in segs])]
+    clusters = []
+    for s in kept_segs:
+        members, centres, _ = index[s]
+        for m, ctr in zip(members, centres):
+            blocks = [int(j) for j in m if j >= n_sink]
+            if blocks:
+                clusters.append((float(qbar_c @ ctr), int(m[0]), blocks))
+    units = best(clusters)
     for j in range(max(n_sink, n_elig * seg_blocks), last + 1):
         units.append((float(qbar_c @ L[j]), j, [j]))
     units.sort(key=lambda u: (-u[0], u[1]))

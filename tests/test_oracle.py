@@ -865,3 +865,52 @@ def test_lsa_selection_invariants():
                 assert min(u[0] for u in full + part) >= max(u[0] for u in none)
             if K >= n_cand:
                 assert np.array_equal(A, np.arange(0, c + 1))
+
+
+def test_lsa_tree_centres_are_means():
+    L = _rng(57).standard_normal((64 * 20 + 9, 5))
+    seg, grp = O.lsa_tree_centres(L, 64, 8)
+    assert seg.shape == (20, 5) and grp.shape == (2, 5)
+    np.testing.assert_allclose(seg[3], L[192:256].mean(axis=0), atol=1e-14)
+    np.testing.assert_allclose(grp[1], L[512:1024].mean(axis=0), atol=1e-14)
+
+
+def test_lsa_tree_with_a_wide_beam_is_the_flat_index():
+    """A beam wider than every level keeps every node, so the tree selects exactly what the
+    flat index selects."""
+    r = _rng(58)
+    seg, ncl = 8, 3
+    L = r.standard_normal((seg * 23 + 5, 6))
+    idx = O.lsa_index(L, seg_blocks=seg, n_clusters=ncl)
+    for c in range(0, L.shape[0], 7):
+        qb = r.standard_normal(6)
+        for K in (1, 5, 12):
+            A, sA = O.lsa_tree_select_row(qb, L, idx, c, K, 1, 2, seg_blocks=seg, fanout=4,
+                                          beam=1000)
+            B, sB = O.lsa_select_row(qb, L, idx, c, K, 1, 2, seg_blocks=seg)
+            assert np.array_equal(A, B)
+            np.testing.assert_allclose(sA, sB, atol=1e-12)
+
+
+def test_lsa_tree_beam_keeps_the_best_nodes():
+    """Brute force: with beam 2 the chosen clusters all lie in the 2 best segments among the 2
+    best top-level nodes, and among the clusters of those segments the chosen ones are the best
+    2 (when K exceeds what they hold, every block of both is chosen)."""
+    r = _rng(59)
+    seg, ncl, fan, beam = 8, 4, 2, 2
+    L = r.standard_normal((seg * 12, 6))
+    idx = O.lsa_index(L, seg_blocks=seg, n_clusters=ncl)
+    segc, grpc = O.lsa_tree_centres(L, seg, fan)
+    c = L.shape[0] - 1
+    qb = r.standard_normal(6)
+    A, _ = O.lsa_tree_select_row(qb, L, idx, c, 50, 1, 2, seg_blocks=seg, fanout=fan, beam=beam)
+    n_elig = (c - 2 + 1) // seg
+    tops = sorted([(-(qb @ grpc[g]), g) for g in range(n_elig // fan)])[:beam]
+    segs = [s for _, g in tops for s in range(g * fan, (g + 1) * fan)]
+    best_segs = [s for _, s in sorted([(-(qb @ segc[s]), s) for s in segs])[:beam]]
+    cl = sorted([(-(qb @ ctr), int(m[0]), m) for s in best_segs for m, ctr in zip(idx[s][0], idx[s][1])],
+                key=lambda x: (x[0], x[1]))[:beam]
+    want = set(j for _, _, m in cl for j in m.tolist() if j >= 1)
+    tail = set(range(n_elig * seg, c - 2 + 1))
+    chosen = set(A.tolist()) - {0, c - 1, c}
+    assert chosen == want | tail
