@@ -31,7 +31,8 @@ __all__ = [
     "MODES", "Params", "library_path", "load_library", "pool_landmarks", "select_topk",
     "attend_prefill", "attend_decode", "select_workspace_bytes", "decode_workspace_bytes",
     "prefill", "decode", "BsaError", "attend_prefill_backward", "backward_workspace_bytes",
-    "lsa_build_index", "lsa_select", "prefill_lsa", "decode_lsa",
+    "lsa_build_index", "lsa_select", "prefill_lsa", "decode_lsa", "lsa_build_tree",
+    "lsa_tree_select",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -104,6 +105,10 @@ def load_library():
     lib.bsa_lsa_select_workspace_bytes.restype = ctypes.c_size_t
     lib.bsa_lsa_select.argtypes = [P, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.bsa_lsa_select.restype = st
+    lib.bsa_lsa_tree_centres.argtypes = [P, vp, i32, i32, vp, vp, vp]
+    lib.bsa_lsa_tree_centres.restype = st
+    lib.bsa_lsa_tree_select.argtypes = [P, vp, vp, i32, i32, i32, i32] + [vp] * 7 + [vp, ctypes.c_size_t, vp]
+    lib.bsa_lsa_tree_select.restype = st
     lib.bsa_status_string.argtypes = [ctypes.c_int]
     lib.bsa_status_string.restype = ctypes.c_char_p
     lib.bsa_last_error.argtypes = []
@@ -419,6 +424,59 @@ def lsa_select(q: torch.Tensor, lm: torch.Tensor, index: dict, *, topk: int,
     return idx, sc
 
 
+def lsa_build_tree(lm: torch.Tensor, index: dict, *, fanout: int = 8) -> dict:
+    """Adds the tree's node centres to an index from lsa_build_index: seg_centres
+    [B,Hkv,NS,D] and grp_centres [B,Hkv,NS // fanout,D] (float32); returns the index."""
+    lib = load_library()
+    _need(lm, "lm", ndim=4)
+    B, Hkv, NB, D = lm.shape
+    seg = index["seg_blocks"]
+    NS = NB // seg
+    seg_c = torch.empty((B, Hkv, NS, D), dtype=torch.float32, device=lm.device)
+    grp_c = torch.empty((B, Hkv, NS // fanout, D), dtype=torch.float32, device=lm.device)
+    p = make_params(B=B, Hq=Hkv, Hkv=Hkv, D=D, seq_q=NB * 64, seq_k=NB * 64, dtype=lm.dtype)
+    _check("bsa_lsa_tree_centres",
+           lib.bsa_lsa_tree_centres(ctypes.byref(p), _ptr(lm), seg, fanout, _ptr(seg_c),
+                                    _ptr(grp_c), _stream(lm.device)))
+    index.update(seg_centres=seg_c, grp_centres=grp_c, fanout=fanout)
+    return index
+
+
+def lsa_tree_select(q: torch.Tensor, lm: torch.Tensor, index: dict, *, topk: int, beam: int = 8,
+                    seq_k: int | None = None, n_sink: int = 1, n_local: int = 2, ws=None,
+                    idx=None, sc=None):
+    """Attended block sets by beam search over the tree (index from lsa_build_index and
+    lsa_build_tree); same layout as select_topk's output."""
+    lib = load_library()
+    _need(q, "q", ndim=4)
+    _need(lm, "lm", dtype=q.dtype, ndim=4)
+    B, Hq, Tq, D = q.shape
+    Hkv = lm.shape[1]
+    Tk = Tq if seq_k is None else int(seq_k)
+    if lm.shape != (B, Hkv, _nblocks(Tk), D):
+        raise ValueError(f"lm shape {tuple(lm.shape)} does not match {(B, Hkv, _nblocks(Tk), D)}")
+    p = make_params(B=B, Hq=Hq, Hkv=Hkv, D=D, seq_q=Tq, seq_k=Tk, dtype=q.dtype, topk=topk,
+                    n_sink=n_sink, n_local=n_local)
+    R = 1 if (Tq == 1 and Tk != 1) else _nblocks(Tq)
+    NA = n_sink + n_local + topk
+    if idx is None:
+        idx = torch.empty((B, Hkv, R, NA), dtype=torch.int32, device=q.device)
+    if sc is None:
+        sc = torch.empty((B, Hkv, R, NA), dtype=torch.float32, device=q.device)
+    need = int(lib.bsa_lsa_select_workspace_bytes(ctypes.byref(p)))
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    NS = index["members"].shape[2]
+    tens = [index[k] if NS else None for k in ("centres", "members", "offsets", "seg_centres")]
+    grp = index["grp_centres"] if index["grp_centres"].shape[2] else None
+    _check("bsa_lsa_tree_select",
+           lib.bsa_lsa_tree_select(ctypes.byref(p), _ptr(q), _ptr(lm), index["seg_blocks"],
+                                   index["n_clusters"], index["fanout"], beam,
+                                   *[_ptr(t) for t in tens], _ptr(grp), _ptr(idx), _ptr(sc),
+                                   _ptr(ws), 0 if ws is None else ws.numel(), _stream(q.device)))
+    return idx, sc
+
+
 # ---------------------------------------------------------------------------------------------
 # whole path
 # ---------------------------------------------------------------------------------------------
@@ -554,12 +612,17 @@ def decode_paged(q, k_pool, v_pool, page_table, seq_lens, *, topk: int, mode: st
 
 def prefill_lsa(q, k, v, *, topk: int, mode: str = "plain", seg_blocks: int = 64,
                 n_clusters: int = 16, n_sink: int = 1, n_local: int = 2, scale: float = 0.0,
-                want_lse: bool = False):
-    """Pool, build the flat clustered index, select from it and attend, for a prefill; returns
-    dict(out, lse, idx, sc, lm, index)."""
+                want_lse: bool = False, tree: bool = False, fanout: int = 8, beam: int = 8):
+    """Pool, build the clustered index, select from it (flat, or by beam search over the tree
+    when tree=True) and attend, for a prefill; returns dict(out, lse, idx, sc, lm, index)."""
     lm = pool_landmarks(k)
     index = lsa_build_index(lm, seg_blocks=seg_blocks, n_clusters=n_clusters)
-    idx, sc = lsa_select(q, lm, index, topk=topk, n_sink=n_sink, n_local=n_local)
+    if tree:
+        lsa_build_tree(lm, index, fanout=fanout)
+        idx, sc = lsa_tree_select(q, lm, index, topk=topk, beam=beam, n_sink=n_sink,
+                                  n_local=n_local)
+    else:
+        idx, sc = lsa_select(q, lm, index, topk=topk, n_sink=n_sink, n_local=n_local)
     out, lse = attend_prefill(q, k, v, idx, sc, lm if mode == "hils" else None, mode=mode,
                               topk=topk, n_sink=n_sink, n_local=n_local, scale=scale,
                               want_lse=want_lse and mode != "hils")

@@ -274,6 +274,63 @@ bsa_status_t bsa_lsa_select(const bsa_params_t* params, const void* q, const voi
                     "lsa_select");
 }
 
+bsa_status_t bsa_lsa_tree_centres(const bsa_params_t* params, const void* lm,
+                                  int32_t seg_blocks, int32_t fanout, float* seg_centres,
+                                  float* grp_centres, void* stream) {
+  bsa::Shape s;
+  BSA_TRY(make_shape(params, kPool, &s));
+  if (seg_blocks < 1 || seg_blocks > 64 || fanout < 1)
+    return fail(BSA_ERR_UNSUPPORTED, "need 1 <= seg_blocks <= 64 and fanout >= 1 (got %d, %d)",
+                seg_blocks, fanout);
+  const int ns = s.NB / seg_blocks;
+  if (ns == 0) return ok();
+  BSA_TRY(check_ptr(lm, "lm"));
+  BSA_TRY(check_ptr(seg_centres, "seg_centres"));
+  if (ns / fanout > 0) BSA_TRY(check_ptr(grp_centres, "grp_centres"));
+  return hip_result(bsa::launch_lsa_tree_centres(s, lm, seg_blocks, fanout, seg_centres,
+                                                 grp_centres, (hipStream_t)stream),
+                    "lsa_tree_centres");
+}
+
+bsa_status_t bsa_lsa_tree_select(const bsa_params_t* params, const void* q, const void* lm,
+                                 int32_t seg_blocks, int32_t n_clusters, int32_t fanout,
+                                 int32_t beam, const float* centres, const int32_t* members,
+                                 const int32_t* offsets, const float* seg_centres,
+                                 const float* grp_centres, int32_t* idx, float* sc, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  bsa::Shape s;
+  BSA_TRY(make_shape(params, kSelect, &s));
+  BSA_TRY(check_lsa(s, seg_blocks, n_clusters));
+  if (!bsa::lsa_tree_shape_ok(s, seg_blocks, n_clusters, fanout, beam))
+    return fail(BSA_ERR_UNSUPPORTED,
+                "the LSA tree needs 1 <= beam <= 64, fanout >= 1, segments / fanout + fanout, "
+                "beam * fanout and beam * n_clusters at most 1024");
+  BSA_TRY(check_ptr(q, "q"));
+  BSA_TRY(check_ptr(lm, "lm"));
+  BSA_TRY(check_ptr(idx, "idx"));
+  BSA_TRY(check_ptr(sc, "sc"));
+  const int ns = s.NB / seg_blocks;
+  if (ns > 0) {
+    BSA_TRY(check_ptr(centres, "centres"));
+    BSA_TRY(check_ptr(members, "members"));
+    BSA_TRY(check_ptr(offsets, "offsets"));
+    BSA_TRY(check_ptr(seg_centres, "seg_centres"));
+    if (ns / fanout > 0) BSA_TRY(check_ptr(grp_centres, "grp_centres"));
+  }
+  const size_t need = s.decode ? 0 : bsa::select_ws_qbar_bytes(s);
+  if (need > 0) {
+    if (ws == nullptr || ws_bytes < need)
+      return fail(BSA_ERR_WORKSPACE, "LSA selection workspace needs %zu bytes (got %zu%s)", need,
+                  ws_bytes, ws == nullptr ? ", NULL pointer" : "");
+    if (((uintptr_t)ws & 255u) != 0) return fail(BSA_ERR_ALIGN, "ws is not 256-byte aligned");
+  }
+  return hip_result(bsa::launch_lsa_tree_select(s, q, lm, seg_blocks, n_clusters, fanout, beam,
+                                                centres, members, offsets, seg_centres,
+                                                grp_centres, idx, sc, (float*)ws,
+                                                (hipStream_t)stream),
+                    "lsa_tree_select");
+}
+
 // ---- backward of PLAIN / SAS prefill ----
 
 namespace {

@@ -79,4 +79,13 @@ hipError_t launch_lsa_select(const Shape& s, const void* q, const void* lm, int 
                              const int32_t* offsets, int32_t* idx, float* sc, float* qbar,
                              hipStream_t st);
 
+// LSA tree index: shape limits, node centres, beam-search selection.
+bool lsa_tree_shape_ok(const Shape& s, int seg, int nc, int fan, int beam);
+hipError_t launch_lsa_tree_centres(const Shape& s, const void* lm, int seg, int fan, float* seg_c,
+                                   float* grp_c, hipStream_t st);
+hipError_t launch_lsa_tree_select(const Shape& s, const void* q, const void* lm, int seg, int nc,
+                                  int fan, int beam, const float* centres, const int32_t* members,
+                                  const int32_t* offsets, const float* seg_c, const float* grp_c,
+                                  int32_t* idx, float* sc, float* qbar, hipStream_t st);
+
 }  // namespace bsa

@@ -389,6 +389,366 @@ __global__ __launch_bounds__(256) void lsa_select_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
+// tree index: node centres, beam-search selection
+// ---------------------------------------------------------------------------------------------
+// Above the Ward clusters of a segment sits the segment, above segments groups of FAN
+// consecutive segments; a node's centre is the mean of the landmarks under it (LSA page, the
+// same section, paragraph 5: the tree variant joins clusters into a hierarchy and walks it by
+// beam search, keeping a few branches per level).
+
+// one workgroup per (segment, sequence x kv group): the segment's centre; segments that close a
+// group of FAN also write the group's centre (the mean of its segments' centres)
+template <int D, typename TIN>
+__global__ __launch_bounds__(128) void lsa_tree_centres_kernel(const TIN* __restrict__ lm,
+                                                               float* __restrict__ seg_c,
+                                                               float* __restrict__ grp_c, int NB,
+                                                               int NS, int NG, int SEG, int FAN) {
+  const int s = blockIdx.x, bg = blockIdx.y;
+  for (int d = threadIdx.x; d < D; d += 128) {
+    const TIN* L = lm + ((size_t)bg * NB + (size_t)s * SEG) * D + d;
+    float acc = 0.0f;
+    for (int p = 0; p < SEG; ++p) acc += (float)L[(size_t)p * D];
+    seg_c[((size_t)bg * NS + s) * D + d] = acc / (float)SEG;
+  }
+  if ((s + 1) % FAN != 0 || (s + 1) / FAN > NG) return;
+  const int gi = s / FAN;
+  // the group's centre is formed by the segment that closes it from the landmarks directly (the
+  // other segments' centres may not be written yet): mean over FAN * SEG landmarks
+  for (int d = threadIdx.x; d < D; d += 128) {
+    float acc = 0.0f;
+    for (int t = 0; t < FAN; ++t) {
+      const TIN* L = lm + ((size_t)bg * NB + (size_t)(gi * FAN + t) * SEG) * D + d;
+      float a2 = 0.0f;
+      for (int p = 0; p < SEG; ++p) a2 += (float)L[(size_t)p * D];
+      acc += a2 / (float)SEG;
+    }
+    grp_c[((size_t)bg * NG + gi) * D + d] = acc / (float)FAN;
+  }
+}
+
+template <int D, typename TIN, int KCAP>
+__global__ __launch_bounds__(256) void lsa_tree_select_kernel(
+    const float* __restrict__ qbar, const TIN* __restrict__ q, const TIN* __restrict__ lm,
+    const float* __restrict__ centres, const int32_t* __restrict__ members,
+    const int32_t* __restrict__ offsets, const float* __restrict__ seg_c,
+    const float* __restrict__ grp_c, int32_t* __restrict__ idx, float* __restrict__ sc, int Hq,
+    int Hkv, int G, int NB, int NS, int NG, int SEG, int NC, int FAN, int BEAM, int R, int c_dec,
+    int topk, int n_sink, int n_local, int NA) {
+  constexpr int CAP = 1024;
+  __shared__ float qv[D];
+  __shared__ uint64_t skey[CAP];
+  __shared__ int spay[CAP];
+  __shared__ int cand[CAP];                      // candidate node ids of the next level
+  __shared__ int kept[64];
+  __shared__ int ch_blk[KCAP];
+  __shared__ float ch_sc[KCAP];
+  __shared__ int wsum[4];
+  __shared__ int ncand_s;
+  const int row = blockIdx.x, bg = blockIdx.y;
+  const int b = bg / Hkv, g = bg % Hkv;
+  const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
+  const int c = c_dec >= 0 ? c_dec : row;
+  const TIN* Lg = lm + (size_t)bg * NB * D;
+  if (tid < D) {
+    if (c_dec >= 0) {
+      double acc = 0.0;
+      for (int hh = 0; hh < G; ++hh) acc += (double)(float)q[(size_t)(b * Hq + g * G + hh) * D + tid];
+      qv[tid] = (float)acc;
+    } else {
+      qv[tid] = qbar[((size_t)bg * R + row) * D + tid];
+    }
+  }
+  __syncthreads();
+  constexpr int LPU = D / 8;
+  constexpr int UPW = kWave / LPU;
+  const int sub = lane % LPU, uw = lane / LPU;
+  float qf[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) qf[e] = qv[sub * 8 + e];
+  // Score n nodes: node u's centre row is ctr(u) (float32), its id (first block) id(u), its
+  // candidate size size(u) (0: not a unit); sort them by (score desc, id asc).  Returns the
+  // sort length.
+  auto score_sort = [&](int n, auto ctr, auto id_of, auto size_of) {
+    int m = 1;
+    while (m < n) m <<= 1;
+    for (int u0 = w * UPW; u0 < m; u0 += 4 * UPW) {
+      const int u = u0 + uw;
+      float part = 0.0f;
+      if (u < n) {
+        const f32x4* cp = reinterpret_cast<const f32x4*>(ctr(u) + sub * 8);
+        const f32x4 c0 = cp[0], c1 = cp[1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) part = fmaf(qf[e], c0[e], fmaf(qf[4 + e], c1[e], part));
+      }
+#pragma unroll
+      for (int o = LPU / 2; o > 0; o >>= 1) part += __shfl_xor(part, o, kWave);
+      if (sub == 0 && u < m) {
+        uint64_t key = ~(uint64_t)0;
+        int size = 0;
+        if (u < n) {
+          size = size_of(u);
+          if (size > 0) key = ((uint64_t)(~float_key(part)) << 32) | (uint32_t)id_of(u);
+        }
+        skey[u] = key;
+        spay[u] = u | (size << 16);
+      }
+    }
+    __syncthreads();
+    lsa_bitonic(skey, spay, m);
+    return m;
+  };
+
+  const int last = c - n_local;
+  const int n_elig = min(NS, max(0, (last + 1) / SEG));
+  const int n_grp = min(NG, n_elig / FAN);
+  const int n_left = n_elig - n_grp * FAN;
+  // level 1: whole groups, and the eligible segments not in a whole group
+  {
+    const int n = n_grp + n_left;
+    score_sort(n,
+               [&](int u) { return u < n_grp ? grp_c + ((size_t)bg * NG + u) * D
+                                             : seg_c + ((size_t)bg * NS + n_grp * FAN + (u - n_grp)) * D; },
+               [&](int u) { return u < n_grp ? u * FAN * SEG : (n_grp * FAN + (u - n_grp)) * SEG; },
+               [&](int) { return 1; });
+    // candidate segments of the kept nodes
+    if (tid == 0) {
+      int nc = 0;
+      for (int i = 0; i < min(BEAM, n); ++i) {
+        const int u = spay[i] & 0xffff;
+        if (u < n_grp)
+          for (int t = 0; t < FAN; ++t) cand[nc++] = u * FAN + t;
+        else
+          cand[nc++] = n_grp * FAN + (u - n_grp);
+      }
+      ncand_s = nc;
+    }
+    __syncthreads();
+  }
+  // level 2: segments
+  {
+    const int n = ncand_s;
+    score_sort(n, [&](int u) { return seg_c + ((size_t)bg * NS + cand[u]) * D; },
+               [&](int u) { return cand[u] * SEG; }, [&](int) { return 1; });
+    if (tid < min(BEAM, n)) kept[tid] = cand[spay[tid] & 0xffff];
+    if (tid == 0) ncand_s = min(BEAM, n);
+    __syncthreads();
+  }
+  // level 3: the clusters of the kept segments
+  const int nseg = ncand_s;
+  {
+    const int n = nseg * NC;
+    auto cl_off = [&](int u, int k) {
+      const size_t sb = (size_t)bg * NS + kept[u / NC];
+      return offsets[sb * (NC + 1) + u % NC + k];
+    };
+    score_sort(n, [&](int u) { return centres + (((size_t)bg * NS + kept[u / NC]) * NC + u % NC) * D; },
+               [&](int u) { return members[((size_t)bg * NS + kept[u / NC]) * SEG + cl_off(u, 0)]; },
+               [&](int u) {
+                 const int32_t* mem = members + ((size_t)bg * NS + kept[u / NC]) * SEG;
+                 int sz = 0;
+                 for (int i = cl_off(u, 0); i < cl_off(u, 1); ++i) sz += mem[i] >= n_sink;
+                 return sz;
+               });
+    // kept clusters become units: cand[i] = cluster u (segment slot u / NC, cluster u % NC)
+    if (tid == 0) {
+      int nc = 0;
+      for (int i = 0; i < min(BEAM, n); ++i)
+        if (skey[i] != ~(uint64_t)0) cand[nc++] = spay[i] & 0xffff;
+      ncand_s = nc;
+    }
+    __syncthreads();
+  }
+  // units: the kept clusters and the not yet clustered candidate blocks, expanded to K blocks
+  const int n_cl = ncand_s;
+  const int single_lo = max(n_sink, n_elig * SEG);
+  const int n_single = max(0, last - single_lo + 1);
+  const int n_units = n_cl + n_single;
+  auto unit_members = [&](int u, int& o0, int& o1) -> const int32_t* {
+    const int cu = cand[u];
+    const size_t sb = (size_t)bg * NS + kept[cu / NC];
+    o0 = offsets[sb * (NC + 1) + cu % NC];
+    o1 = offsets[sb * (NC + 1) + cu % NC + 1];
+    return members + sb * SEG;
+  };
+  int m = 1;
+  while (m < n_units) m <<= 1;
+  for (int u0 = w * UPW; u0 < m; u0 += 4 * UPW) {
+    const int u = u0 + uw;
+    float part = 0.0f;
+    int size = 0;
+    uint32_t id = 0;
+    if (u < n_cl) {
+      int o0, o1;
+      const int32_t* mem = unit_members(u, o0, o1);
+      for (int i = o0; i < o1; ++i) size += mem[i] >= n_sink;
+      id = (uint32_t)mem[o0];
+      const int cu = cand[u];
+      const f32x4* cp = reinterpret_cast<const f32x4*>(
+          centres + (((size_t)bg * NS + kept[cu / NC]) * NC + cu % NC) * D + sub * 8);
+      const f32x4 c0 = cp[0], c1 = cp[1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) part = fmaf(qf[e], c0[e], fmaf(qf[4 + e], c1[e], part));
+    } else if (u < n_units) {
+      const int j = single_lo + (u - n_cl);
+      const TIN* lrow = Lg + (size_t)j * D + sub * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part = fmaf(qf[e], (float)lrow[e], part);
+      size = 1;
+      id = (uint32_t)j;
+    }
+#pragma unroll
+    for (int o = LPU / 2; o > 0; o >>= 1) part += __shfl_xor(part, o, kWave);
+    if (sub == 0 && u < m) {
+      uint64_t key = ~(uint64_t)0;
+      if (u < n_units && size > 0) key = ((uint64_t)(~float_key(part)) << 32) | id;
+      skey[u] = key;
+      spay[u] = u | (size << 16);
+    }
+  }
+  __syncthreads();
+  lsa_bitonic(skey, spay, m);
+  const int per = (m + 255) / 256;
+  int local_sum = 0;
+  for (int i = tid * per; i < min(m, (tid + 1) * per); ++i)
+    if (skey[i] != ~(uint64_t)0) local_sum += spay[i] >> 16;
+  int incl = local_sum;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += y;
+  }
+  if (lane == kWave - 1) wsum[w] = incl;
+  __syncthreads();
+  int base = incl - local_sum;
+  for (int v = 0; v < w; ++v) base += wsum[v];
+  const int total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  const int K = min(topk, total);
+  for (int i = tid * per; i < min(m, (tid + 1) * per); ++i) {
+    if (skey[i] == ~(uint64_t)0) continue;
+    const int u = spay[i] & 0xffff;
+    const int size = spay[i] >> 16;
+    const float uscore = key_float(~(uint32_t)(skey[i] >> 32));
+    if (base < K) {
+      const int take = min(size, K - base);
+      if (u < n_cl) {
+        int o0, o1;
+        const int32_t* mem = unit_members(u, o0, o1);
+        int n = 0;
+        for (int x = o0; x < o1 && n < take; ++x)
+          if (mem[x] >= n_sink) {
+            ch_blk[base + n] = mem[x];
+            ch_sc[base + n] = uscore;
+            ++n;
+          }
+      } else {
+        ch_blk[base] = single_lo + (u - n_cl);
+        ch_sc[base] = uscore;
+      }
+    }
+    base += size;
+  }
+  __syncthreads();
+  int mk = 1;
+  while (mk < K) mk <<= 1;
+  for (int i = tid; i < mk; i += 256) {
+    skey[i] = i < K ? (uint64_t)(uint32_t)ch_blk[i] : ~(uint64_t)0;
+    spay[i] = i;
+  }
+  __syncthreads();
+  if (K > 1) lsa_bitonic(skey, spay, mk);
+  const int n_s = min(n_sink, c + 1);
+  const int l0 = max(n_s, c - n_local + 1);
+  const int n_l = max(0, c - l0 + 1);
+  const size_t rb = ((size_t)bg * R + row) * NA;
+  auto dot_lm = [&](int j) {
+    float acc = 0.0f;
+#pragma unroll 8
+    for (int d = 0; d < D; ++d) acc = fmaf(qv[d], (float)Lg[(size_t)j * D + d], acc);
+    return acc;
+  };
+  for (int i = tid; i < NA; i += 256) {
+    int j = -1;
+    float s = 0.0f;
+    if (i < n_s) {
+      j = i;
+      s = dot_lm(j);
+    } else if (i < n_s + K) {
+      const int slot = spay[i - n_s];
+      j = ch_blk[slot];
+      s = ch_sc[slot];
+    } else if (i < n_s + K + n_l) {
+      j = l0 + (i - n_s - K);
+      s = dot_lm(j);
+    }
+    idx[rb + i] = j;
+    sc[rb + i] = s;
+  }
+}
+
+bool lsa_tree_shape_ok(const Shape& s, int seg, int nc, int fan, int beam) {
+  if (!lsa_shape_ok(s, seg, nc) || fan < 1 || beam < 1 || beam > 64) return false;
+  const int ns = s.NB / seg;
+  return ns / fan + fan <= 1024 && beam * fan <= 1024 && beam * nc <= 1024 &&
+         beam + seg <= 1024;
+}
+
+hipError_t launch_lsa_tree_centres(const Shape& s, const void* lm, int seg, int fan,
+                                   float* seg_c, float* grp_c, hipStream_t st) {
+  const int ns = s.NB / seg;
+  if (ns == 0) return hipSuccess;
+  const int ng = ns / fan;
+  dim3 grid(ns, s.B * s.Hkv);
+#define BSA_TC(D_, T_)                                                                           \
+  hipLaunchKernelGGL((lsa_tree_centres_kernel<D_, T_>), grid, dim3(128), 0, st, (const T_*)lm,    \
+                     seg_c, grp_c, s.NB, ns, ng, seg, fan)
+  if (s.D == 128) {
+    if (s.bf16) BSA_TC(128, bf16);
+    else BSA_TC(128, float);
+  } else {
+    if (s.bf16) BSA_TC(64, bf16);
+    else BSA_TC(64, float);
+  }
+#undef BSA_TC
+  return hipGetLastError();
+}
+
+hipError_t launch_lsa_tree_select(const Shape& s, const void* q, const void* lm, int seg, int nc,
+                                  int fan, int beam, const float* centres, const int32_t* members,
+                                  const int32_t* offsets, const float* seg_c, const float* grp_c,
+                                  int32_t* idx, float* sc, float* qbar, hipStream_t st) {
+  if (!s.decode) {
+    const hipError_t e = launch_selector_vectors(s, q, qbar, st);
+    if (e != hipSuccess) return e;
+  }
+  const int ns = s.NB / seg;
+  dim3 grid(s.R, s.B * s.Hkv);
+#define BSA_TS(D_, T_, K_)                                                                       \
+  hipLaunchKernelGGL((lsa_tree_select_kernel<D_, T_, K_>), grid, dim3(256), 0, st, qbar,          \
+                     (const T_*)q, (const T_*)lm, centres, members, offsets, seg_c, grp_c, idx, sc, \
+                     s.Hq, s.Hkv, s.G, s.NB, ns, ns / fan, seg, nc, fan, beam, s.R,               \
+                     s.decode ? s.c_dec : -1, s.topk, s.n_sink, s.n_local, s.NA)
+#define BSA_TS_K(D_, T_)                  \
+  if (s.topk <= 256) BSA_TS(D_, T_, 256); \
+  else BSA_TS(D_, T_, kLsaMaxK);
+  if (s.D == 128) {
+    if (s.bf16) {
+      BSA_TS_K(128, bf16)
+    } else {
+      BSA_TS_K(128, float)
+    }
+  } else {
+    if (s.bf16) {
+      BSA_TS_K(64, bf16)
+    } else {
+      BSA_TS_K(64, float)
+    }
+  }
+#undef BSA_TS_K
+#undef BSA_TS
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------------------------
 bool lsa_shape_ok(const Shape& s, int seg, int nc) {

@@ -232,6 +232,38 @@ bsa_status_t bsa_lsa_select(const bsa_params_t* params, const void* q, const voi
                             float* sc, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Tree over the flat index (LSA page, the same section, paragraph 5: the tree variant joins the
+ * clusters into a hierarchy and walks it by beam search, keeping a few branches per level, so a
+ * query makes a logarithmic number of comparisons).  Above the clusters of a segment sits the
+ * segment, above segments groups of `fanout` consecutive segments; a node's centre is the mean
+ * of the landmarks under it.
+ *   seg_centres [B,Hkv,NS,D] float32 output; grp_centres [B,Hkv,NG,D] float32 output,
+ *   NG = floor(NS / fanout) (may be NULL when NG = 0).  lm as for bsa_lsa_build_index.
+ */
+bsa_status_t bsa_lsa_tree_centres(const bsa_params_t* params, const void* lm,
+                                  int32_t seg_blocks, int32_t fanout, float* seg_centres,
+                                  float* grp_centres, void* stream);
+
+/*
+ * Attended block sets by beam search over the tree.  For query block c (decode: the query at
+ * seq_k - 1), with NE the eligible segments of bsa_lsa_select: the top level holds the whole
+ * groups among them and the eligible segments left over; at each level the `beam` best nodes
+ * (by qbar . centre, descending; equal scores: the node whose first block is lower) pass their
+ * children on -- groups their segments, segments their clusters -- and the `beam` best clusters
+ * become units, expanded with the not yet clustered candidate blocks exactly as in
+ * bsa_lsa_select (same row layout and scores).  Arguments as bsa_lsa_select plus the tree
+ * centres; ws: bsa_lsa_select_workspace_bytes.
+ * Limits: those of bsa_lsa_select, 1 <= beam <= 64, fanout >= 1, and NS / fanout + fanout,
+ * beam * fanout, beam * n_clusters each at most 1024.
+ */
+bsa_status_t bsa_lsa_tree_select(const bsa_params_t* params, const void* q, const void* lm,
+                                 int32_t seg_blocks, int32_t n_clusters, int32_t fanout,
+                                 int32_t beam, const float* centres, const int32_t* members,
+                                 const int32_t* offsets, const float* seg_centres,
+                                 const float* grp_centres, int32_t* idx, float* sc, void* ws,
+                                 size_t ws_bytes, void* stream);
+
+/*
  * Workspace bytes of bsa_attend_prefill_backward for these params (0 if the params are
  * rejected by that call).
  */

@@ -279,3 +279,171 @@ def test_workload_lsa_sas_bf16_128k_sampled():
     del q, k, v, res
     gc.collect()
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------------------------
+# tree index (beam search)
+# ---------------------------------------------------------------------------------------------
+
+def _tree_min_gap(qbar, L64, ref_index, c, K, ns, nl, seg, fan, beam):
+    """Smallest relative score gap at any cut the beam search makes for this row (the beam cut
+    at each level and the unit boundary at K blocks): below TIE_BAND the row is ambiguous."""
+    segc, grpc = O.lsa_tree_centres(L64, seg, fan)
+    last = c - nl
+    n_elig = min(len(ref_index), max(0, (last + 1) // seg))
+    n_grp = n_elig // fan
+    gaps = []
+
+    def keep(cands):
+        cands = sorted(cands, key=lambda x: (-x[0], x[1]))
+        if len(cands) > beam:
+            a, b = cands[beam - 1][0], cands[beam][0]
+            gaps.append(abs(a - b) / max(abs(a), abs(b), 1e-30))
+        return cands[:beam]
+
+    top = [(float(qbar @ grpc[g]), g * fan * seg, ("g", g)) for g in range(n_grp)]
+    top += [(float(qbar @ segc[s]), s * seg, ("s", s)) for s in range(n_grp * fan, n_elig)]
+    segs = []
+    for _, _, (kind, i) in keep(top):
+        segs += list(range(i * fan, (i + 1) * fan)) if kind == "g" else [i]
+    kept = [p[1] for _, _, p in keep([(float(qbar @ segc[s]), s * seg, ("s", s)) for s in segs])]
+    cl = []
+    for s in kept:
+        for m, ctr in zip(ref_index[s][0], ref_index[s][1]):
+            bl = [int(j) for j in m if j >= ns]
+            if bl:
+                cl.append((float(qbar @ ctr), int(m[0]), bl))
+    units = keep(cl)
+    for j in range(max(ns, n_elig * seg), last + 1):
+        units.append((float(qbar @ L64[j]), j, [j]))
+    units.sort(key=lambda u: (-u[0], u[1]))
+    taken = 0
+    for i, u in enumerate(units):
+        taken += len(u[2])
+        if taken >= K and i + 1 < len(units):
+            a, b = u[0], units[i + 1][0]
+            gaps.append(abs(a - b) / max(abs(a), abs(b), 1e-30))
+            break
+    return min(gaps) if gaps else math.inf
+
+
+def _check_tree(res, q, lm, topk, seg, fan, beam, tag):
+    B, Hkv = lm.shape[0], lm.shape[1]
+    index = res["index"]
+    idx = res["idx"].cpu().numpy()
+    qbar = O.selector_vectors(host64(q), Hkv)
+    ambiguous = 0
+    for b in range(B):
+        for g in range(Hkv):
+            L64 = host64(lm[b, g])
+            segc, grpc = O.lsa_tree_centres(L64, seg, fan)
+            np.testing.assert_allclose(host64(index["seg_centres"][b, g]), segc, atol=1e-5,
+                                       err_msg=f"{tag} segment centres")
+            np.testing.assert_allclose(host64(index["grp_centres"][b, g]), grpc, atol=1e-5,
+                                       err_msg=f"{tag} group centres")
+            ref_index = _dev_index(index, L64, b, g)
+            for c in range(idx.shape[2]):
+                A = idx[b, g, c][idx[b, g, c] >= 0].astype(np.int64)
+                A_ref, _ = O.lsa_tree_select_row(qbar[b, g, c], L64, ref_index, c, topk, 1, 2,
+                                                 seg_blocks=seg, fanout=fan, beam=beam)
+                if not np.array_equal(A, A_ref):
+                    gap = _tree_min_gap(qbar[b, g, c], L64, ref_index, c, topk, 1, 2, seg, fan, beam)
+                    assert gap < TIE_BAND, f"{tag} b{b} g{g} c{c}: tree selection differs " \
+                                           f"(no near tie: smallest gap {gap:.2e})"
+                    ambiguous += 1
+    _print(f"{tag}: {ambiguous} rows differ at a near tie")
+
+
+LSA_TREE = [
+    # id,        B, Hq, Hkv, T,            D,   topk, seg, nc, fan, beam
+    ("t_seg8",   1, 4,  1,   64 * 120 + 7, 128, 6,    8,   3,  4,   3),
+    ("t_b2",     2, 4,  2,   64 * 90,      64,  9,    8,   4,  3,   2),
+    ("t_seg16",  1, 8,  2,   64 * 300,     128, 20,   16,  4,  4,   4),
+    ("t_wide",   1, 4,  1,   64 * 100,     128, 8,    8,   2,  2,   64),
+]
+
+
+@pytest.mark.parametrize("mode", ["plain", "sas"])
+@pytest.mark.parametrize("case", LSA_TREE, ids=[c[0] for c in LSA_TREE])
+def test_lsa_tree_prefill_small(case, mode):
+    name, B, Hq, Hkv, T, D, topk, seg, nc, fan, beam = case
+    _print(f"lsa tree {name} {mode}")
+    q, k, v = synth.make_prefill(B, Hq, Hkv, T, D, "bf16", "clustered", seed=12, device="cuda",
+                                 n_centres=16, n_aim=4)
+    res = bsa.prefill_lsa(q, k, v, topk=topk, mode=mode, seg_blocks=seg, n_clusters=nc,
+                          want_lse=True, tree=True, fanout=fan, beam=beam)
+    torch.cuda.synchronize()
+    tag = f"{name}/{mode}"
+    _check_tree(res, q, res["lm"], topk, seg, fan, beam, tag)
+    # attention over the device's sets
+    idx = res["idx"].cpu().numpy()
+    sc = res["sc"].cpu().numpy().astype(np.float64)
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(D)
+    for b in range(B):
+        for g in range(Hkv):
+            K64, V64 = host64(k[b, g]), host64(v[b, g])
+            for c in range(0, idx.shape[2], 5):
+                A = idx[b, g, c][idx[b, g, c] >= 0].astype(np.int64)
+                lo, hi = c * 64, min(c * 64 + 64, T)
+                gates = O.sas_gates(A, sc[b, g, c, :A.size], c) if mode == "sas" else np.zeros(A.size)
+                for hh in range(G):
+                    ref, _ = O.attend_rows(host64(q[b, g * G + hh, lo:hi]), np.arange(lo, hi),
+                                           K64, V64, A, gates, scale)
+                    check_out(host64(res["out"][b, g * G + hh, lo:hi]), ref, "bf16",
+                              f"{tag} b{b} g{g} c{c} h{hh}")
+
+
+def test_lsa_tree_wide_beam_equals_flat_on_device():
+    """A beam wider than every level gives the flat index's sets, bit for bit, on the device."""
+    q, k, v = synth.make_prefill(1, 4, 1, 64 * 100, 128, "bf16", "clustered", seed=13,
+                                 device="cuda", n_centres=16, n_aim=4)
+    flat = bsa.prefill_lsa(q, k, v, topk=8, seg_blocks=8, n_clusters=2)
+    tree = bsa.prefill_lsa(q, k, v, topk=8, seg_blocks=8, n_clusters=2, tree=True, fanout=2,
+                           beam=64)
+    torch.cuda.synchronize()
+    assert torch.equal(flat["idx"], tree["idx"])
+
+
+def test_workload_lsa_tree_sas_bf16_128k_sampled():
+    """The 128K SAS workload, tree index (fanout 8, beam 8): node centres of two groups and
+    sampled rows' selections and attention."""
+    w = synth.WORKLOADS["sas_bf16_128k"]
+    B, Hq, Hkv, T, D, K = w["B"], w["Hq"], w["Hkv"], w["T"], w["D"], w["topk"]
+    G = Hq // Hkv
+    q, k, v = synth.make_prefill(B, Hq, Hkv, T, D, w["dtype"], w["data"], seed=0, device="cuda",
+                                 n_centres=w["n_centres"], n_aim=w["n_aim"])
+    res = bsa.prefill_lsa(q, k, v, topk=K, mode="sas", want_lse=True, tree=True)
+    torch.cuda.synchronize()
+    idx = res["idx"].cpu().numpy()
+    sc = res["sc"].cpu().numpy().astype(np.float64)
+    NQB = (T + 63) // 64
+    rng = np.random.default_rng(8)
+    scale = 1.0 / math.sqrt(D)
+    ambiguous = 0
+    for g in (0, Hkv - 1):
+        L64 = host64(res["lm"][0, g])
+        segc, grpc = O.lsa_tree_centres(L64, 64, 8)
+        np.testing.assert_allclose(host64(res["index"]["seg_centres"][0, g]), segc, atol=1e-5)
+        np.testing.assert_allclose(host64(res["index"]["grp_centres"][0, g]), grpc, atol=1e-5)
+        ref_index = _dev_index(res["index"], L64, 0, g)
+        K64, V64 = host64(k[0, g]), host64(v[0, g])
+        for c in sorted({0, 64, 65, 600, NQB - 1} | {int(x) for x in rng.integers(0, NQB, 6)}):
+            lo, hi = c * 64, min(c * 64 + 64, T)
+            qs = host64(q[0, g * G:(g + 1) * G, lo:hi])
+            qbar = O.selector_vectors(qs[None], 1)[0, 0, 0]
+            A = idx[0, g, c][idx[0, g, c] >= 0].astype(np.int64)
+            A_ref, _ = O.lsa_tree_select_row(qbar, L64, ref_index, c, K, 1, 2)
+            if not np.array_equal(A, A_ref):
+                gap = _tree_min_gap(qbar, L64, ref_index, c, K, 1, 2, 64, 8, 8)
+                assert gap < TIE_BAND, f"tree 128k g{g} c{c}: differs without a near tie ({gap:.2e})"
+                ambiguous += 1
+            gates = O.sas_gates(A, sc[0, g, c, :A.size], c)
+            for hh in range(G):
+                ref, _ = O.attend_rows(qs[hh], np.arange(lo, hi), K64, V64, A, gates, scale)
+                check_out(host64(res["out"][0, g * G + hh, lo:hi]), ref, "bf16",
+                          f"tree 128k g{g} c{c} h{hh}")
+    _print(f"tree 128k: {ambiguous} sampled rows differ at a near tie")
+    del q, k, v, res
+    gc.collect()
+    torch.cuda.empty_cache()
