@@ -19,7 +19,8 @@ Reported beside it, measured in the same run:
   workload, and the HiLS backward (dq, dk, dv and the landmark gradient) on the same shape and
   attended sets, each timed per call (--no-backward skips both);
 * the same prefill step with the flat clustered (LSA) index -- pool, Ward index build,
-  selection over the index, attention -- each part timed (--no-lsa skips it);
+  selection over the index, attention -- each part timed, and again with the tree index (beam
+  search over groups of segments, segments and clusters) (--no-lsa skips both);
 * optionally the HiLS workload at 1M tokens (--hils);
 * the float64 oracle timed on the host cores on a bounded sample of the prefill workload.
 
@@ -236,13 +237,17 @@ def bench_backward(torch, bsa, synth, name, tensors, steps, warmup, mode=None):
     return res
 
 
-def bench_lsa(torch, bsa, synth, name, tensors, steps, warmup, seg_blocks=64, n_clusters=16):
-    """The prefill step with the flat clustered index in place of the per-block top-K: pool,
-    Ward index build, selection over the index, attention; each part timed with HIP events."""
+def bench_lsa(torch, bsa, synth, name, tensors, steps, warmup, seg_blocks=64, n_clusters=16,
+              tree=False, fanout=8, beam=8):
+    """The prefill step with the clustered index in place of the per-block top-K: pool, Ward
+    index build (and, for the tree, its node centres), selection over the index (flat, or beam
+    search over the tree), attention; each part timed with HIP events."""
     w = synth.WORKLOADS[name]
     B, Hq, Hkv, T, D, K, mode = w["B"], w["Hq"], w["Hkv"], w["T"], w["D"], w["topk"], w["mode"]
     q, k, v, lm, idx, sc, out = tensors[:7]
     index = bsa.lsa_build_index(lm, seg_blocks=seg_blocks, n_clusters=n_clusters)
+    if tree:
+        bsa.lsa_build_tree(lm, index, fanout=fanout)
     p = bsa.make_params(B=B, Hq=Hq, Hkv=Hkv, D=D, seq_q=T, seq_k=T, dtype=q.dtype, topk=K)
     ws = torch.empty(max(bsa.select_workspace_bytes(p), 256), dtype=torch.uint8, device="cuda")
     ev = {n: Events(torch) for n in ("pool", "build", "select", "attend")}
@@ -255,9 +260,18 @@ def bench_lsa(torch, bsa, synth, name, tensors, steps, warmup, seg_blocks=64, n_
             if record:
                 ev[n].stop()
         timed("pool", lambda: bsa.pool_landmarks(k, out=lm))
-        timed("build", lambda: bsa.lsa_build_index(lm, seg_blocks=seg_blocks,
-                                                   n_clusters=n_clusters))
-        timed("select", lambda: bsa.lsa_select(q, lm, index, topk=K, ws=ws, idx=idx, sc=sc))
+        def build():
+            bsa.lsa_build_index(lm, seg_blocks=seg_blocks, n_clusters=n_clusters)
+            if tree:
+                bsa.lsa_build_tree(lm, index, fanout=fanout)
+
+        def select():
+            if tree:
+                bsa.lsa_tree_select(q, lm, index, topk=K, beam=beam, ws=ws, idx=idx, sc=sc)
+            else:
+                bsa.lsa_select(q, lm, index, topk=K, ws=ws, idx=idx, sc=sc)
+        timed("build", build)
+        timed("select", select)
         timed("attend", lambda: bsa.attend_prefill(q, k, v, idx, sc, None, mode=mode, topk=K,
                                                    out=out))
 
@@ -273,10 +287,16 @@ def bench_lsa(torch, bsa, synth, name, tensors, steps, warmup, seg_blocks=64, n_
     ms = {n: sum(e.ms()) / steps for n, e in ev.items()}
     NB = (T + 63) // 64
     NS = NB // seg_blocks
-    res = {"workload": f"{name} with the flat clustered index: {NS} segments of {seg_blocks} "
-                       f"landmarks x {n_clusters} Ward clusters per kv group; a query block "
-                       f"scores at most {NS * n_clusters + seg_blocks} units instead of {NB} "
-                       f"landmarks",
+    if tree:
+        scored = (NS // fanout + fanout) + beam * fanout + beam * n_clusters + beam + seg_blocks
+        what = (f"the tree index (groups of {fanout} segments, beam {beam}) over {NS} segments of "
+                f"{seg_blocks} landmarks x {n_clusters} Ward clusters per kv group; a query block "
+                f"scores at most {scored} nodes and units instead of {NB} landmarks")
+    else:
+        what = (f"the flat clustered index: {NS} segments of {seg_blocks} landmarks x "
+                f"{n_clusters} Ward clusters per kv group; a query block scores at most "
+                f"{NS * n_clusters + seg_blocks} units instead of {NB} landmarks")
+    res = {"workload": f"{name} with {what}",
            "tok_per_s": B * T * steps / wall, "ms_per_step": wall * 1e3 / steps,
            "breakdown_ms": ms}
     log(f"[bench] lsa: {json.dumps(res)}")
@@ -456,9 +476,11 @@ def main():
         log("[bench] timing the oracle on the host cores")
         cpu = cpu_baseline(torch, tensors, name, synth)
         log(f"[bench] cpu baseline: {cpu['value']:.1f} tok/s")
-    lsa = None
+    lsa = lsa_tree = None
     if not args.no_lsa:
         lsa = bench_lsa(torch, bsa, synth, name, tensors, max(3, args.steps // 2), 1)
+        lsa_tree = bench_lsa(torch, bsa, synth, name, tensors, max(3, args.steps // 2), 1,
+                             tree=True)
         torch.cuda.empty_cache()
     bwd = bwd_hils = None
     if not args.no_backward:
@@ -534,6 +556,8 @@ def main():
         line["decode_paged"] = dec_paged
     if lsa is not None:
         line["lsa_prefill"] = lsa
+    if lsa_tree is not None:
+        line["lsa_tree_prefill"] = lsa_tree
     if bwd is not None:
         line["backward"] = bwd
     if bwd_hils is not None:
