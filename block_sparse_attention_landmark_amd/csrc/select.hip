@@ -164,7 +164,7 @@ hipError_t launch_block_scores(const Shape& s, const float* qbar, const void* lm
 // top-K of one selection row, executed by a whole workgroup of NT threads
 // ---------------------------------------------------------------------------------------------
 constexpr int kTopkThreads = 256;
-constexpr int kKeyCache = 12288;   // candidate keys held in LDS; longer rows re-read L2
+constexpr int kKeyCache = 16384;   // candidate keys held in LDS; longer rows re-read L2
 
 // exclusive prefix sum over the workgroup; *total receives the sum of all x
 template <int NT>
@@ -288,13 +288,15 @@ __device__ void topk_select(ScoreAt score_at, KeyAt key_at, int c, int topk, int
   }
 }
 
-// one workgroup of 256 threads per selection row, scores from the score workspace
+// one workgroup of 256 threads per selection row, scores from the score workspace; CACHE keys
+// of the row are held in LDS (a smaller cache lets more rows share a CU)
+template <int CACHE>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ scores,
                                                             int32_t* __restrict__ idx,
                                                             float* __restrict__ sc, int R,
                                                             int NB, int c_dec, int topk,
                                                             int n_sink, int n_local, int NA) {
-  __shared__ uint32_t skeys[kKeyCache];
+  __shared__ uint32_t skeys[CACHE];
   __shared__ int hist[256];
   __shared__ int sbuf[kTopkThreads / kWave];
   __shared__ int sh[2];
@@ -303,9 +305,23 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   const int c = (c_dec >= 0) ? c_dec : r;
   const float* srow = scores + ((c_dec >= 0) ? (size_t)bg * NB : (size_t)bg * tri(R) + tri(c));
   const int n = max(0, c - n_local - n_sink + 1);
-  const bool cached = n <= kKeyCache;
+  const bool cached = n <= CACHE;
   if (cached) {
-    for (int i = threadIdx.x; i < n; i += kTopkThreads) skeys[i] = float_key(srow[n_sink + i]);
+    // 16 loads in flight per thread (a row of 16K scores is 4 rounds, not 64 round trips)
+    constexpr int U = 16;
+    for (int i0 = 0; i0 < n; i0 += kTopkThreads * U) {
+      float v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * kTopkThreads + threadIdx.x;
+        v[u] = i < n ? srow[n_sink + i] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * kTopkThreads + threadIdx.x;
+        if (i < n) skeys[i] = float_key(v[u]);
+      }
+    }
   }
   __syncthreads();
   topk_select<kTopkThreads>(
@@ -408,8 +424,12 @@ hipError_t launch_decode_select(const Shape& s, const void* q, const void* lm, i
 hipError_t launch_topk(const Shape& s, const float* scores, int32_t* idx, float* sc,
                        hipStream_t st) {
   dim3 grid(s.R, s.B * s.Hkv);
-  hipLaunchKernelGGL(topk_kernel, grid, dim3(kTopkThreads), 0, st, scores, idx, sc, s.R, s.NB,
-                     s.decode ? s.c_dec : -1, s.topk, s.n_sink, s.n_local, s.NA);
+  if (s.NB <= 4096)
+    hipLaunchKernelGGL(topk_kernel<4096>, grid, dim3(kTopkThreads), 0, st, scores, idx, sc, s.R,
+                       s.NB, s.decode ? s.c_dec : -1, s.topk, s.n_sink, s.n_local, s.NA);
+  else
+    hipLaunchKernelGGL(topk_kernel<kKeyCache>, grid, dim3(kTopkThreads), 0, st, scores, idx, sc,
+                       s.R, s.NB, s.decode ? s.c_dec : -1, s.topk, s.n_sink, s.n_local, s.NA);
   return hipGetLastError();
 }
 

@@ -385,3 +385,33 @@ def test_workload_decode_bf16_32x128k_sampled():
     del q, kc, vc, lm, res
     gc.collect()
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("n_patterns", [5, 1])
+def test_selection_exact_ties(n_patterns):
+    """Blocks repeat n_patterns key patterns, so most selector scores tie exactly (n_patterns=1:
+    every candidate ties).  The attended sets must equal the oracle's bit for bit: among equal
+    scores the lower block index wins, for prefill rows and for decode."""
+    B, Hq, Hkv, T, D, topk = 1, 4, 1, 64 * 300, 64, 20
+    g = torch.Generator().manual_seed(17)
+    pats = torch.randn((n_patterns, 64, D), generator=g)
+    nb = T // 64
+    k = pats[torch.arange(nb) % n_patterns].reshape(1, 1, T, D).to(torch.bfloat16).cuda()
+    q = torch.randn((B, Hq, T, D), generator=g).to(torch.bfloat16).cuda()
+    v = torch.randn((B, Hkv, T, D), generator=g).to(torch.bfloat16).cuda()
+    res = bsa.prefill(q, k, v, topk=topk)
+    torch.cuda.synchronize()
+    L64 = host64(res["lm"][0, 0])
+    qbar = O.selector_vectors(host64(q), Hkv)[0, 0]
+    idx = res["idx"][0, 0].cpu().numpy()
+    for c in range(nb):
+        A_ref, _ = O.select_row(O.block_scores(qbar[c][None], L64)[0], c, topk)
+        A = idx[c][idx[c] >= 0]
+        assert np.array_equal(A, A_ref), f"prefill c{c}: {A.tolist()} != {A_ref.tolist()}"
+    qd = q[:, :, -1:, :].contiguous()
+    dres = bsa.decode(qd, k, v, res["lm"], topk=topk)
+    torch.cuda.synchronize()
+    qb = O.decode_selector_vectors(host64(q[:, :, -1]), Hkv)[0, 0]
+    A_ref, _ = O.select_row(O.block_scores(qb[None], L64)[0], nb - 1, topk)
+    A = dres["idx"][0, 0, 0].cpu().numpy()
+    assert np.array_equal(A[A >= 0], A_ref)
