@@ -318,32 +318,44 @@ def bench_decode(torch, bsa, synth, steps, warmup):
     p = bsa.make_params(B=B, Hq=Hq, Hkv=Hkv, D=D, seq_q=1, seq_k=Tk, dtype=q.dtype, topk=K)
     ws_sel = torch.empty(bsa.select_workspace_bytes(p), dtype=torch.uint8, device="cuda")
     ws_dec = torch.empty(bsa.decode_workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    ws_step = torch.empty(max(256, bsa.decode_step_workspace_bytes(p)), dtype=torch.uint8,
+                          device="cuda")
     # evicting the caches with a read leaves them full of clean lines; a write would leave dirty
     # lines whose write-back the timed step would then pay for
     flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-    ev_step, ev_attn = Events(torch), Events(torch)
+    ev_step, ev_two, ev_attn = Events(torch), Events(torch), Events(torch)
 
-    def step(record):
+    def step(record):                            # one call: selection + attention fused
         if record:
             ev_step.start()
+        bsa.decode_step(q, kc, vc, lm, topk=K, idx=idx, sc=sc, out=out, ws=ws_step)
+        if record:
+            ev_step.stop()
+
+    def two_calls(record):                       # the selection call, then the attention call
+        if record:
+            ev_two.start()
         bsa.select_topk(q, lm, topk=K, seq_k=Tk, ws=ws_sel, idx=idx, sc=sc)
         if record:
             ev_attn.start()
         bsa.attend_decode(q, kc, vc, idx, sc, None, mode="plain", topk=K, out=out, ws=ws_dec)
         if record:
             ev_attn.stop()
-            ev_step.pairs[-1][1] = ev_attn.pairs[-1][1]
+            ev_two.pairs[-1][1] = ev_attn.pairs[-1][1]
 
-    for _ in range(warmup):
-        step(False)
-    for _ in range(steps):
-        flush.sum()                              # evict L2 and the MALL between steps
-        step(True)
+    for fn in (step, two_calls):
+        for _ in range(warmup):
+            fn(False)
+        for _ in range(steps):
+            flush.sum()                          # evict L2 and the MALL between steps
+            fn(True)
     torch.cuda.synchronize()
     nbytes = decode_bytes(B, Hq, Hkv, Tk, D, K)
     step_us = 1e3 * sum(ev_step.ms()) / steps
+    two_us = 1e3 * sum(ev_two.ms()) / steps
     attn_us = 1e3 * sum(ev_attn.ms()) / steps
-    res = {"us_per_step": step_us, "attn_us": attn_us, "select_us": step_us - attn_us,
+    res = {"us_per_step": step_us, "two_call_us_per_step": two_us,
+           "two_call_breakdown_us": {"select": two_us - attn_us, "attend": attn_us},
            "algorithmic_bytes": nbytes, "hbm_gbps": nbytes / (step_us * 1e-6) / 1e9}
     res["hbm_frac"] = res["hbm_gbps"] / PEAK_HBM_GBPS
     log(f"[bench] decode: {json.dumps(res)}")
@@ -352,7 +364,8 @@ def bench_decode(torch, bsa, synth, steps, warmup):
 
 
 def bench_decode_paged(torch, bsa, synth, steps, warmup):
-    """Ragged batch in a paged cache: paged selection + paged split-K attention per step."""
+    """Ragged batch in a paged cache: one paged decode step call (fused selection + attention)
+    per step; the paged selection and attention calls one after the other for comparison."""
     import numpy as np
     name = "decode_paged_bf16_32x16k_128k"
     w = synth.WORKLOADS[name]
@@ -371,12 +384,22 @@ def bench_decode_paged(torch, bsa, synth, steps, warmup):
     out = torch.empty_like(q)
     p = bsa.make_params(B=B, Hq=Hq, Hkv=Hkv, D=D, seq_q=1, seq_k=NB * 64, dtype=q.dtype, topk=K)
     ws_dec = torch.empty(max(256, bsa.decode_workspace_bytes(p)), dtype=torch.uint8, device="cuda")
+    ws_step = torch.empty(max(256, bsa.decode_step_workspace_bytes(p)), dtype=torch.uint8,
+                          device="cuda")
     flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-    ev_step, ev_attn = Events(torch), Events(torch)
+    ev_step, ev_two, ev_attn = Events(torch), Events(torch), Events(torch)
 
     def step(record):
         if record:
             ev_step.start()
+        bsa.decode_step_paged(q, k_pool, v_pool, table, seq_lens, lm, topk=K, idx=idx, sc=sc,
+                              out=out, ws=ws_step)
+        if record:
+            ev_step.stop()
+
+    def two_calls(record):
+        if record:
+            ev_two.start()
         bsa.select_topk_paged(q, lm, seq_lens, topk=K, idx=idx, sc=sc)
         if record:
             ev_attn.start()
@@ -384,21 +407,24 @@ def bench_decode_paged(torch, bsa, synth, steps, warmup):
                                 topk=K, out=out, ws=ws_dec)
         if record:
             ev_attn.stop()
-            ev_step.pairs[-1][1] = ev_attn.pairs[-1][1]
+            ev_two.pairs[-1][1] = ev_attn.pairs[-1][1]
 
-    for _ in range(warmup):
-        step(False)
-    for _ in range(steps):
-        flush.sum()
-        step(True)
+    for fn in (step, two_calls):
+        for _ in range(warmup):
+            fn(False)
+        for _ in range(steps):
+            flush.sum()
+            fn(True)
     torch.cuda.synchronize()
     nbytes = sum(decode_bytes(1, Hq, Hkv, L, D, K) for L in lens)
     step_us = 1e3 * sum(ev_step.ms()) / steps
+    two_us = 1e3 * sum(ev_two.ms()) / steps
     attn_us = 1e3 * sum(ev_attn.ms()) / steps
     res = {"workload": f"{name}: {B} seqs of {min(lens)}..{max(lens)} cached tokens (seeded "
                        f"uniform), shuffled 64-token pages, Hq={Hq}, Hkv={Hkv}, D={D}, "
                        f"top-K={K} + sink + 2 local, bf16",
-           "us_per_step": step_us, "breakdown_us": {"select": step_us - attn_us, "attend": attn_us},
+           "us_per_step": step_us, "two_call_us_per_step": two_us,
+           "two_call_breakdown_us": {"select": two_us - attn_us, "attend": attn_us},
            "hbm_gbps": nbytes / (step_us * 1e-6) / 1e9}
     res["roofline"] = {"bound": "hbm", "achieved": res["hbm_gbps"], "peak": PEAK_HBM_GBPS,
                        "unit": "GB/s", "frac": res["hbm_gbps"] / PEAK_HBM_GBPS,
@@ -545,8 +571,10 @@ def main():
         line["decode"] = {
             "workload": "decode_bf16_32x128k: 32 seqs x 131072 cached tokens, Hq=64, Hkv=8, "
                         "D=128, top-K=64 + sink + 2 local, bf16",
+            "step": "one decode step call: selection and attention in one fused kernel",
             "hbm_gbps": dec["hbm_gbps"], "us_per_step": dec["us_per_step"],
-            "breakdown_us": {"select": dec["select_us"], "attend": dec["attn_us"]},
+            "two_call_us_per_step": dec["two_call_us_per_step"],
+            "two_call_breakdown_us": dec["two_call_breakdown_us"],
             "roofline": {"bound": "hbm", "achieved": dec["hbm_gbps"], "peak": PEAK_HBM_GBPS,
                          "unit": "GB/s", "frac": dec["hbm_frac"],
                          "algorithmic_bytes": dec["algorithmic_bytes"],

@@ -32,7 +32,7 @@ __all__ = [
     "attend_prefill", "attend_decode", "select_workspace_bytes", "decode_workspace_bytes",
     "prefill", "decode", "BsaError", "attend_prefill_backward", "backward_workspace_bytes",
     "lsa_build_index", "lsa_select", "prefill_lsa", "decode_lsa", "lsa_build_tree",
-    "lsa_tree_select",
+    "lsa_tree_select", "decode_step", "decode_step_paged", "decode_step_workspace_bytes",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -95,6 +95,13 @@ def load_library():
     lib.bsa_attend_decode_paged.argtypes = [P, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp,
                                             ctypes.c_size_t, vp]
     lib.bsa_attend_decode_paged.restype = st
+    lib.bsa_decode_step_workspace_bytes.argtypes = [P]
+    lib.bsa_decode_step_workspace_bytes.restype = ctypes.c_size_t
+    lib.bsa_decode_step.argtypes = [P] + [vp] * 9 + [ctypes.c_size_t, vp]
+    lib.bsa_decode_step.restype = st
+    lib.bsa_decode_step_paged.argtypes = [P, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                          ctypes.c_size_t, vp]
+    lib.bsa_decode_step_paged.restype = st
     lib.bsa_backward_workspace_bytes.argtypes = [P]
     lib.bsa_backward_workspace_bytes.restype = ctypes.c_size_t
     lib.bsa_attend_prefill_backward.argtypes = [P] + [vp] * 15 + [ctypes.c_size_t, vp]
@@ -502,6 +509,52 @@ def decode(q, kc, vc, lm, *, topk: int, mode: str = "plain", n_sink: int = 1, n_
     return {"out": out, "lse": lse, "idx": idx, "sc": sc}
 
 
+def decode_step_workspace_bytes(p: Params) -> int:
+    return int(load_library().bsa_decode_step_workspace_bytes(ctypes.byref(p)))
+
+
+def _step_outputs(q, B, Hkv, Hq, NA, idx, sc, out, lse, want_lse, mode):
+    if idx is None:
+        idx = torch.empty((B, Hkv, 1, NA), dtype=torch.int32, device=q.device)
+    if sc is None:
+        sc = torch.empty((B, Hkv, 1, NA), dtype=torch.float32, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and mode != "hils" and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    return idx, sc, out, lse
+
+
+def decode_step(q, kc, vc, lm, *, topk: int, mode: str = "plain", n_sink: int = 1,
+                n_local: int = 2, scale: float = 0.0, want_lse: bool = False, idx=None, sc=None,
+                out=None, lse=None, ws=None):
+    """One decode step (selection + attention) in one library call: q [B,Hq,1,D], kc/vc
+    [B,Hkv,Tk,D], lm [B,Hkv,NB,D]; returns dict(out, lse, idx, sc) as decode() does."""
+    lib = load_library()
+    _need(q, "q", ndim=4)
+    _need(kc, "kc", dtype=q.dtype, ndim=4)
+    _need(vc, "vc", dtype=q.dtype, ndim=4)
+    _need(lm, "lm", dtype=q.dtype, ndim=4)
+    B, Hq, one, D = q.shape
+    Hkv, Tk = kc.shape[1], kc.shape[2]
+    if one != 1 or kc.shape != (B, Hkv, Tk, D) or vc.shape != kc.shape:
+        raise ValueError("q must be [B,Hq,1,D] and kc/vc [B,Hkv,Tk,D]")
+    if lm.shape != (B, Hkv, _nblocks(Tk), D):
+        raise ValueError(f"lm shape {tuple(lm.shape)} does not match the cache")
+    NA = n_sink + n_local + topk
+    idx, sc, out, lse = _step_outputs(q, B, Hkv, Hq, NA, idx, sc, out, lse, want_lse, mode)
+    p = make_params(B=B, Hq=Hq, Hkv=Hkv, D=D, seq_q=1, seq_k=Tk, dtype=q.dtype, topk=topk,
+                    n_sink=n_sink, n_local=n_local, scale=scale, mode=mode)
+    need = decode_step_workspace_bytes(p)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check("bsa_decode_step",
+           lib.bsa_decode_step(ctypes.byref(p), _ptr(q), _ptr(kc), _ptr(vc), _ptr(lm), _ptr(idx),
+                               _ptr(sc), _ptr(out), _ptr(lse), _ptr(ws),
+                               0 if ws is None else ws.numel(), _stream(q.device)))
+    return {"out": out, "lse": lse, "idx": idx, "sc": sc}
+
+
 # ---------------------------------------------------------------------------------------------
 # paged (ragged) decode: 64-token pages [n_pages,Hkv,64,D], page_table [B,NB], seq_lens [B]
 # ---------------------------------------------------------------------------------------------
@@ -594,6 +647,36 @@ def attend_decode_paged(q, k_pool, v_pool, page_table, seq_lens, idx, sc=None, l
                                        _ptr(idx), _ptr(sc), _ptr(out), _ptr(lse), _ptr(ws),
                                        0 if ws is None else ws.numel(), _stream(q.device)))
     return out, lse
+
+
+def decode_step_paged(q, k_pool, v_pool, page_table, seq_lens, lm, *, topk: int,
+                      mode: str = "plain", n_sink: int = 1, n_local: int = 2, scale: float = 0.0,
+                      want_lse: bool = False, idx=None, sc=None, out=None, lse=None, ws=None):
+    """One paged decode step (selection + attention) in one library call; lm from
+    pool_landmarks_paged; returns dict(out, lse, idx, sc)."""
+    lib = load_library()
+    _need(q, "q", ndim=4)
+    n_pages, Hkv, D, B, NB = _paged_shapes(k_pool, page_table, seq_lens)
+    _need(v_pool, "v_pool", dtype=k_pool.dtype, ndim=4)
+    if v_pool.shape != k_pool.shape or k_pool.dtype != q.dtype:
+        raise ValueError("v_pool must match k_pool, and both q's dtype")
+    _need(lm, "lm", dtype=q.dtype, ndim=4)
+    Hq = q.shape[1]
+    if q.shape != (B, Hq, 1, D) or lm.shape != (B, Hkv, NB, D):
+        raise ValueError("q must be [B,Hq,1,D] and lm [B,Hkv,NB,D]")
+    NA = n_sink + n_local + topk
+    idx, sc, out, lse = _step_outputs(q, B, Hkv, Hq, NA, idx, sc, out, lse, want_lse, mode)
+    p = make_params(B=B, Hq=Hq, Hkv=Hkv, D=D, seq_q=1, seq_k=NB * 64, dtype=q.dtype, topk=topk,
+                    n_sink=n_sink, n_local=n_local, scale=scale, mode=mode)
+    need = decode_step_workspace_bytes(p)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check("bsa_decode_step_paged",
+           lib.bsa_decode_step_paged(ctypes.byref(p), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                     int(n_pages), _ptr(page_table), _ptr(seq_lens), _ptr(lm),
+                                     _ptr(idx), _ptr(sc), _ptr(out), _ptr(lse), _ptr(ws),
+                                     0 if ws is None else ws.numel(), _stream(q.device)))
+    return {"out": out, "lse": lse, "idx": idx, "sc": sc}
 
 
 def decode_paged(q, k_pool, v_pool, page_table, seq_lens, *, topk: int, mode: str = "plain",

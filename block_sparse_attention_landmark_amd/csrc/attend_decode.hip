@@ -8,6 +8,7 @@
 
 #include "attend_common.hpp"
 #include "bsa_internal.hpp"
+#include "select_common.hpp"
 
 namespace bsa {
 
@@ -18,6 +19,10 @@ constexpr int kDecodeWaves = 4;          // waves per workgroup
 constexpr int kMergeMaxSplits = 64;      // partial states merged per (sequence, kv group)
 
 constexpr int kDecodeTargetWorkgroups = 256;   // one per CU is enough to stream the cache
+
+// fused selection + attention: limits of the LDS-held score row and attended set
+constexpr int kFusedMaxBlocks = 4096;
+constexpr int kFusedMaxNA = 256;
 
 // Splits of the attended blocks of one (sequence, kv group): as few as keep the GPU busy (each
 // split's partial state costs a write and a read), at most kMergeMaxSplits.
@@ -41,14 +46,22 @@ inline int decode_blocks_per_wave(int NA, int nsplit) {
 // PAGED: the cache is a pool of 64-token pages [n_pages, Hkv, 64, D]; block j of sequence b is
 // page page_table[b * NB + j] (clamped into the pool) and the sequence holds seq_lens[b] tokens
 // (clamped to 1 .. NB * 64); otherwise kc / vc are [B, Hkv, Tk, D] and every sequence holds Tk.
-template <int D, int MODE, bool PAGED>
+//
+// FUSED (nsplit == 1): the workgroup first selects its own attended set -- the selector vector
+// (sum of the group's query heads), the scores of blocks 0..c against the landmarks, the top-K
+// with the forced sink and local blocks (the same arithmetic, bit for bit, as the decode
+// selection kernel) -- writes it to sel_idx / sel_sc and attends it from LDS.  The sink and local
+// blocks are processed first, and their copies are issued before the top-K runs, so the cache
+// stream starts while the selection is still being decided.
+template <int D, int MODE, bool PAGED, bool FUSED>
 __global__ __launch_bounds__(kDecodeWaves * 64) void attend_decode_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
     const bf16* __restrict__ lm, const int32_t* __restrict__ idx, const float* __restrict__ sc,
     float* __restrict__ part_o, float* __restrict__ part_ml, bf16* __restrict__ out,
     float* __restrict__ lse, int Hq, int Hkv, int G, int Tk_all, int NB, int NA, int nsplit, int bpw,
     float scale_log2, const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens,
-    int n_pages) {
+    int n_pages, int32_t* __restrict__ sel_idx, float* __restrict__ sel_sc, int topk, int n_sink,
+    int n_local) {
   constexpr int C16 = D / 8;                 // 16-byte chunks per row
   constexpr int RPI = 64 / C16;              // rows covered by one 64-lane 16-byte copy
   __shared__ __attribute__((aligned(16))) bf16 Ks[kDecodeWaves][kBlock * D];
@@ -92,9 +105,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void attend_decode_bf16_kernel(
       return kvbase + (size_t)j * kBlock * D;
     }
   };
-  const int32_t* irow = idx + (size_t)(b * Hkv + g) * NA;
-  const float* srow = sc + (size_t)(b * Hkv + g) * NA;
-  const int nval = count_valid(irow, NA);
+  const int32_t* irow = FUSED ? nullptr : idx + (size_t)(b * Hkv + g) * NA;
+  const float* srow = FUSED ? nullptr : sc + (size_t)(b * Hkv + g) * NA;
+  int nval = FUSED ? 0 : count_valid(irow, NA);
   bf16* kt_ = Ks[w];
   bf16* vt = Vs[w];
   const uint32_t k_lds = lds_addr_of(kt_), v_lds = lds_addr_of(vt), l_lds = lds_addr_of(Ls[w]);
@@ -108,27 +121,6 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void attend_decode_bf16_kernel(
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
 
-  // This wave's entries: a = a0 + waves * it for it < n_it.  They are held one per lane, 64 at a
-  // time (block index and SAS gate), and read with readlane, so the loop below issues no memory
-  // loads besides the tile copies: the only copy wait is the full one at the top of an iteration.
-  const int a0 = split * kDecodeWaves * bpw + w;
-  const int n_it = a0 < nval ? min(bpw, (nval - a0 + kDecodeWaves - 1) / kDecodeWaves) : 0;
-  const float s_ref = (MODE == 1 && nval > 0) ? srow[nval - 1] : 0.0f;
-  int ej = -1;
-  float eg = 0.0f;
-  auto load_batch = [&](int base) {
-    const int it = base + lane;
-    int jv = -1;
-    float gv = 0.0f;
-    if (it < n_it) {
-      const int a = a0 + kDecodeWaves * it;
-      jv = irow[a];
-      if (jv < 0 || jv > c) jv = -1;
-      else if (MODE == 1 && jv != c) gv = log_sigmoid(srow[a] - s_ref) * kLog2e;
-    }
-    ej = jv;
-    eg = gv;
-  };
   // copy the K (or V) rows of block j into this wave's tile, 1 KB per instruction (rows past
   // the cache end read its last row; their probabilities are zero); HiLS also copies the
   // block's landmark row beside the K tile
@@ -157,10 +149,134 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void attend_decode_bf16_kernel(
     }
   };
 
+  // ---- FUSED: select the attended set of this (sequence, kv group) into LDS ----
+  int32_t* fidx = nullptr;      // the attended set in LDS (FUSED)
+  float* fsc = nullptr;
+  int n_forced = 0, n_sink_eff = 0;
+  if constexpr (FUSED) {
+    __shared__ float s_qb[D];
+    __shared__ float s_score[kFusedMaxBlocks];
+    __shared__ int s_hist[kTopkHistWords];
+    __shared__ int s_sbuf[kDecodeWaves];
+    __shared__ int s_sh[2];
+    __shared__ int32_t s_idx[kFusedMaxNA];
+    __shared__ float s_sel[kFusedMaxNA];
+    fidx = s_idx;
+    fsc = s_sel;
+    const int tid = threadIdx.x;
+    // selector vector: sum of the group's query heads (float64, then float32)
+    if (tid < D) {
+      double acc = 0.0;
+      for (int hh = 0; hh < G; ++hh) acc += (double)bf2f(q[(size_t)(b * Hq + g * G + hh) * D + tid]);
+      s_qb[tid] = (float)acc;
+    }
+    __syncthreads();
+    // scores of blocks 0..c, one landmark row per lane: wave w streams rows
+    // (4 r + w) * 64 .. +64 of round r straight into its own two tiles (rounds alternate between
+    // them, two rounds in flight), 16-byte chunks XOR-swizzled by row so that the lanes' row
+    // reads hit distinct banks; each lane then sums q . L over the row in dimension order
+    {
+      constexpr int C16 = D / 8;                // 16-byte chunks per row
+      constexpr int RPI = kWave / C16;          // rows per copy instruction
+      constexpr int NI = kBlock / RPI;          // copy instructions per 64-row round
+      auto swzl = [](int row) { return D == 128 ? row % 16 : (row / 2) % 8; };
+      const char* lrows = reinterpret_cast<const char*>(lm + (size_t)(b * Hkv + g) * NB * D);
+      auto issue = [&](int r) {
+        const int row0 = (r * kDecodeWaves + w) * kBlock;
+        if (row0 > c) return;
+        const uint32_t dst = (r & 1) ? v_lds : k_lds;
+#pragma unroll
+        for (int n = 0; n < NI; ++n) {
+          const int row = n * RPI + lane / C16;
+          const int rr = min(row0 + row, c);
+          dma_lds<16>(lrows, (uint32_t)((rr * D + ((lane % C16) ^ swzl(row)) * 8) * 2),
+                      dst + (uint32_t)(n * RPI * D * 2));
+        }
+      };
+      issue(0);
+      issue(1);
+      for (int r = 0;; ++r) {
+        const int row0 = (r * kDecodeWaves + w) * kBlock;
+        if (row0 > c) break;
+        if (row0 + kDecodeWaves * kBlock <= c)   // round r + 1 is in flight behind round r
+          __builtin_amdgcn_s_waitcnt(0x0F70 | (NI & 15) | ((NI >> 4) << 14));
+        else
+          __builtin_amdgcn_s_waitcnt(0x0F70);
+        const bf16* tile = (r & 1) ? vt : kt_;
+        const int row = row0 + lane;
+        float sdot = 0.0f;
+#pragma unroll
+        for (int k = 0; k < C16; ++k) {
+          const bf16x8 x = *reinterpret_cast<const bf16x8*>(tile + lane * D + ((k ^ swzl(lane)) * 8));
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sdot = fmaf(s_qb[8 * k + e], bf2f(x[e]), sdot);
+        }
+        if (row <= c) s_score[row] = sdot;
+        __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): this tile may be overwritten
+        issue(r + 2);
+      }
+    }
+    __syncthreads();
+    // the forced blocks (sink, then the local window) are this set's first entries in the order
+    // processed below; wave w < n_forced starts copying forced block w now
+    n_sink_eff = min(n_sink, c + 1);
+    const int loc_beg = max(n_sink, c - n_local + 1);
+    n_forced = n_sink_eff + max(0, c - loc_beg + 1);
+    if (w < n_forced) {
+      const int jf = w < n_sink_eff ? w : loc_beg + (w - n_sink_eff);
+      copy_k(jf);
+      copy_v(jf);
+    }
+    topk_select<kDecodeWaves * 64>(
+        [&](int jj) { return s_score[jj]; }, [&](int i) { return float_key(s_score[n_sink + i]); },
+        c, topk, n_sink, n_local, NA, s_idx, s_sel, s_hist, s_sbuf, s_sh);
+    __syncthreads();
+    int32_t* gi = sel_idx + (size_t)(b * Hkv + g) * NA;
+    float* gs = sel_sc + (size_t)(b * Hkv + g) * NA;
+    for (int i = tid; i < NA; i += kDecodeWaves * 64) {
+      gi[i] = s_idx[i];
+      gs[i] = s_sel[i];
+    }
+    nval = n_forced + min(topk, max(0, c - n_local - n_sink + 1));
+  }
+  // position, in the attended-set row, of the entry processed p-th: the stored order unless
+  // FUSED, where the forced blocks come first (sink entries, local entries, then the chosen)
+  auto pos_of = [&](int p) {
+    if constexpr (!FUSED) return p;
+    const int kc_ = nval - n_forced;
+    if (p < n_sink_eff) return p;
+    if (p < n_forced) return kc_ + p;
+    return p - (n_forced - n_sink_eff);
+  };
+
+  // This wave's entries: the p-th processed with p = a0 + waves * it for it < n_it.  They are
+  // held one per lane, 64 at a time (block index and SAS gate), and read with readlane, so the
+  // loop below issues no memory loads besides the tile copies: the only copy wait is the full
+  // one at the top of an iteration.
+  const int a0 = split * kDecodeWaves * bpw + w;
+  const int n_it = a0 < nval ? min(bpw, (nval - a0 + kDecodeWaves - 1) / kDecodeWaves) : 0;
+  float s_ref = 0.0f;
+  if (MODE == 1 && nval > 0) s_ref = FUSED ? fsc[nval - 1] : srow[nval - 1];
+  int ej = -1;
+  float eg = 0.0f;
+  auto load_batch = [&](int base) {
+    const int it = base + lane;
+    int jv = -1;
+    float gv = 0.0f;
+    if (it < n_it) {
+      const int a = pos_of(a0 + kDecodeWaves * it);
+      jv = FUSED ? fidx[a] : irow[a];
+      if (jv < 0 || jv > c) jv = -1;
+      else if (MODE == 1 && jv != c) gv = log_sigmoid((FUSED ? fsc[a] : srow[a]) - s_ref) * kLog2e;
+    }
+    ej = jv;
+    eg = gv;
+  };
+
   load_batch(0);
   int j = n_it > 0 ? __builtin_amdgcn_readlane(ej, 0) : -1;
   float gate2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(eg), 0));
-  if (j >= 0) {
+  if (j >= 0 && !(FUSED && w < n_forced)) {    // (FUSED: forced blocks are already in flight)
     copy_k(j);
     copy_v(j);
   }
@@ -403,27 +519,32 @@ size_t decode_ws_bytes(const Shape& s) {
   return o + rows * 2 * sizeof(float);
 }
 
-template <int D, bool PAGED>
+// FUSED: idx / sc are the outputs of the selection (sel_idx / sel_sc); nsplit is 1
+template <int D, bool PAGED, bool FUSED>
 static void launch_decode_bf16_d(const Shape& s, const void* q, const void* kc, const void* vc,
                                  const void* lm, const int32_t* idx, const float* sc, void* out,
                                  float* lse, void* ws, const Pages* pg, hipStream_t st) {
-  const int nsplit = decode_splits(s);
+  const int nsplit = FUSED ? 1 : decode_splits(s);
   const size_t rows = (size_t)s.B * s.Hkv * nsplit * s.G;
   float* part_o = (float*)ws;
-  float* part_ml = (float*)((char*)ws + ((rows * s.D * sizeof(float) + 255) & ~(size_t)255));
+  float* part_ml =
+      ws ? (float*)((char*)ws + ((rows * s.D * sizeof(float) + 255) & ~(size_t)255)) : nullptr;
   dim3 grid(nsplit, s.Hkv, s.B);
   const float sl2 = s.scale * kLog2e;
 #define BSA_DEC(MODE)                                                                           \
-  hipLaunchKernelGGL((attend_decode_bf16_kernel<D, MODE, PAGED>), grid, dim3(kDecodeWaves * 64), \
-                     0, st, (const bf16*)q, (const bf16*)kc, (const bf16*)vc, (const bf16*)lm,  \
-                     idx, sc, part_o, part_ml, (bf16*)out, lse, s.Hq, s.Hkv, s.G, s.Tk, s.NB,   \
-                     s.NA, nsplit, decode_blocks_per_wave(s.NA, nsplit), sl2,                  \
-                     pg ? pg->table : nullptr, pg ? pg->lens : nullptr, pg ? pg->n_pages : 1)
+  hipLaunchKernelGGL((attend_decode_bf16_kernel<D, MODE, PAGED, FUSED>), grid,                  \
+                     dim3(kDecodeWaves * 64), 0, st, (const bf16*)q, (const bf16*)kc,           \
+                     (const bf16*)vc, (const bf16*)lm, FUSED ? nullptr : idx,                   \
+                     FUSED ? nullptr : sc, part_o, part_ml, (bf16*)out, lse, s.Hq, s.Hkv, s.G,  \
+                     s.Tk, s.NB, s.NA, nsplit, decode_blocks_per_wave(s.NA, nsplit), sl2,       \
+                     pg ? pg->table : nullptr, pg ? pg->lens : nullptr, pg ? pg->n_pages : 1,   \
+                     FUSED ? const_cast<int32_t*>(idx) : nullptr,                              \
+                     FUSED ? const_cast<float*>(sc) : nullptr, s.topk, s.n_sink, s.n_local)
   if (s.mode == 0) BSA_DEC(0);
   else if (s.mode == 1) BSA_DEC(1);
   else BSA_DEC(2);
 #undef BSA_DEC
-  if (nsplit > 1)
+  if (!FUSED && nsplit > 1)
     hipLaunchKernelGGL(decode_merge_kernel<bf16>, dim3(s.B * s.Hkv), dim3(256), 0, st, part_o,
                        part_ml, (bf16*)out, lse, s.Hkv, s.G, s.D, nsplit, s.mode != 2 ? 1 : 0);
 }
@@ -433,14 +554,32 @@ hipError_t launch_attend_decode(const Shape& s, const void* q, const void* kc, c
                                 float* lse, void* ws, hipStream_t st, const Pages* pg) {
   if (s.bf16) {
     if (pg != nullptr) {
-      if (s.D == 128) launch_decode_bf16_d<128, true>(s, q, kc, vc, lm, idx, sc, out, lse, ws, pg, st);
-      else launch_decode_bf16_d<64, true>(s, q, kc, vc, lm, idx, sc, out, lse, ws, pg, st);
+      if (s.D == 128) launch_decode_bf16_d<128, true, false>(s, q, kc, vc, lm, idx, sc, out, lse, ws, pg, st);
+      else launch_decode_bf16_d<64, true, false>(s, q, kc, vc, lm, idx, sc, out, lse, ws, pg, st);
     } else {
-      if (s.D == 128) launch_decode_bf16_d<128, false>(s, q, kc, vc, lm, idx, sc, out, lse, ws, nullptr, st);
-      else launch_decode_bf16_d<64, false>(s, q, kc, vc, lm, idx, sc, out, lse, ws, nullptr, st);
+      if (s.D == 128) launch_decode_bf16_d<128, false, false>(s, q, kc, vc, lm, idx, sc, out, lse, ws, nullptr, st);
+      else launch_decode_bf16_d<64, false, false>(s, q, kc, vc, lm, idx, sc, out, lse, ws, nullptr, st);
     }
   } else {
     return launch_attend_f32(s, q, kc, vc, lm, idx, sc, out, lse, st);
+  }
+  return hipGetLastError();
+}
+
+bool decode_step_fused(const Shape& s) {
+  return s.bf16 && s.decode && decode_splits(s) == 1 && s.NB <= kFusedMaxBlocks &&
+         s.NA <= kFusedMaxNA && s.G <= 32;
+}
+
+hipError_t launch_decode_step_fused(const Shape& s, const void* q, const void* kc, const void* vc,
+                                    const void* lm, int32_t* idx, float* sc, void* out,
+                                    float* lse, hipStream_t st, const Pages* pg) {
+  if (pg != nullptr) {
+    if (s.D == 128) launch_decode_bf16_d<128, true, true>(s, q, kc, vc, lm, idx, sc, out, lse, nullptr, pg, st);
+    else launch_decode_bf16_d<64, true, true>(s, q, kc, vc, lm, idx, sc, out, lse, nullptr, pg, st);
+  } else {
+    if (s.D == 128) launch_decode_bf16_d<128, false, true>(s, q, kc, vc, lm, idx, sc, out, lse, nullptr, nullptr, st);
+    else launch_decode_bf16_d<64, false, true>(s, q, kc, vc, lm, idx, sc, out, lse, nullptr, nullptr, st);
   }
   return hipGetLastError();
 }

@@ -497,4 +497,99 @@ bsa_status_t bsa_attend_decode_paged(const bsa_params_t* params, const void* q,
                     "attend_decode_paged");
 }
 
+// ---- one decode step (selection + attention) ----
+
+size_t bsa_decode_step_workspace_bytes(const bsa_params_t* params) {
+  bsa::Shape s;
+  if (make_shape(params, kDecode, &s) != BSA_OK) return 0;
+  if (bsa::decode_step_fused(s)) return 0;
+  const size_t sel = bsa::decode_select_fused(s) ? 0 : bsa::select_ws_bytes(s);
+  return ((sel + 255) & ~(size_t)255) + bsa::decode_ws_bytes(s);
+}
+
+static bsa_status_t check_decode_step(const bsa::Shape& s, const void* q, const void* kc,
+                                      const void* vc, const void* lm, const int32_t* idx,
+                                      const float* sc, const void* out, const float* lse,
+                                      const void* ws, size_t ws_bytes, size_t need) {
+  BSA_TRY(check_ptr(q, "q"));
+  BSA_TRY(check_ptr(kc, "k cache"));
+  BSA_TRY(check_ptr(vc, "v cache"));
+  BSA_TRY(check_ptr(lm, "lm"));
+  BSA_TRY(check_ptr(idx, "idx"));
+  BSA_TRY(check_ptr(sc, "sc"));
+  BSA_TRY(check_ptr(out, "out"));
+  if (s.mode == BSA_MODE_HILS && lse != nullptr)
+    return fail(BSA_ERR_UNSUPPORTED, "lse is not defined for HILS; pass NULL");
+  if (lse != nullptr) BSA_TRY(check_ptr(lse, "lse"));
+  if (need > 0) {
+    if (ws == nullptr || ws_bytes < need)
+      return fail(BSA_ERR_WORKSPACE, "decode step workspace needs %zu bytes (got %zu%s)", need,
+                  ws_bytes, ws == nullptr ? ", NULL pointer" : "");
+    if (((uintptr_t)ws & 255u) != 0) return fail(BSA_ERR_ALIGN, "ws is not 256-byte aligned");
+  }
+  return BSA_OK;
+}
+
+// the selection and the attention as two launches (shapes the fused kernel does not take)
+static hipError_t decode_step_unfused(const bsa::Shape& s, const void* q, const void* kc,
+                                      const void* vc, const void* lm, int32_t* idx, float* sc,
+                                      void* out, float* lse, void* ws, hipStream_t st,
+                                      const bsa::Pages* pg) {
+  hipError_t e;
+  size_t sel = 0;
+  if (bsa::decode_select_fused(s)) {
+    const bsa::Pages lens{nullptr, pg ? pg->lens : nullptr, 1};
+    e = bsa::launch_decode_select(s, q, lm, idx, sc, st, pg ? &lens : nullptr);
+  } else {
+    sel = (bsa::select_ws_bytes(s) + 255) & ~(size_t)255;
+    float* qbar = (float*)ws;
+    float* scores = (float*)((char*)ws + bsa::select_ws_qbar_bytes(s));
+    e = bsa::launch_selector_vectors(s, q, qbar, st);
+    if (e == hipSuccess) e = bsa::launch_block_scores(s, qbar, lm, scores, st);
+    if (e == hipSuccess) e = bsa::launch_topk(s, scores, idx, sc, st);
+  }
+  if (e != hipSuccess) return e;
+  void* dws = bsa::decode_ws_bytes(s) > 0 ? (void*)((char*)ws + sel) : nullptr;
+  return bsa::launch_attend_decode(s, q, kc, vc, lm, idx, sc, out, lse, dws, st, pg);
+}
+
+bsa_status_t bsa_decode_step(const bsa_params_t* params, const void* q, const void* kc,
+                             const void* vc, const void* lm, int32_t* idx, float* sc, void* out,
+                             float* lse, void* ws, size_t ws_bytes, void* stream) {
+  bsa::Shape s;
+  BSA_TRY(make_shape(params, kDecode, &s));
+  BSA_TRY(check_decode_step(s, q, kc, vc, lm, idx, sc, out, lse, ws, ws_bytes,
+                            bsa_decode_step_workspace_bytes(params)));
+  hipStream_t st = (hipStream_t)stream;
+  if (bsa::decode_step_fused(s))
+    return hip_result(
+        bsa::launch_decode_step_fused(s, q, kc, vc, lm, idx, sc, out, lse, st, nullptr),
+        "decode_step");
+  return hip_result(decode_step_unfused(s, q, kc, vc, lm, idx, sc, out, lse, ws, st, nullptr),
+                    "decode_step");
+}
+
+bsa_status_t bsa_decode_step_paged(const bsa_params_t* params, const void* q,
+                                   const void* k_pool, const void* v_pool, int32_t n_pages,
+                                   const int32_t* page_table, const int32_t* seq_lens,
+                                   const void* lm, int32_t* idx, float* sc, void* out,
+                                   float* lse, void* ws, size_t ws_bytes, void* stream) {
+  bsa::Shape s;
+  BSA_TRY(make_shape(params, kDecode, &s));
+  BSA_TRY(check_paged(params, s, n_pages, page_table, seq_lens, true));
+  if (!s.bf16) return fail(BSA_ERR_UNSUPPORTED, "paged decode is implemented for bf16 only");
+  if (!bsa::decode_select_fused(s))
+    return fail(BSA_ERR_UNSUPPORTED, "paged selection supports at most 16384 blocks per sequence");
+  BSA_TRY(check_decode_step(s, q, k_pool, v_pool, lm, idx, sc, out, lse, ws, ws_bytes,
+                            bsa_decode_step_workspace_bytes(params)));
+  hipStream_t st = (hipStream_t)stream;
+  const bsa::Pages pg{page_table, seq_lens, n_pages};
+  if (bsa::decode_step_fused(s))
+    return hip_result(
+        bsa::launch_decode_step_fused(s, q, k_pool, v_pool, lm, idx, sc, out, lse, st, &pg),
+        "decode_step_paged");
+  return hip_result(decode_step_unfused(s, q, k_pool, v_pool, lm, idx, sc, out, lse, ws, st, &pg),
+                    "decode_step_paged");
+}
+
 }  // extern "C"

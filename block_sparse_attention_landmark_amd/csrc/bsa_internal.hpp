@@ -58,6 +58,11 @@ hipError_t launch_attend_prefill(const Shape& s, const void* q, const void* k, c
 hipError_t launch_attend_f32(const Shape& s, const void* q, const void* k, const void* v,
                              const void* lm, const int32_t* idx, const float* sc, void* out,
                              float* lse, hipStream_t st);
+// one decode step in one kernel per (sequence, kv group): selection, then attention
+bool decode_step_fused(const Shape& s);
+hipError_t launch_decode_step_fused(const Shape& s, const void* q, const void* kc, const void* vc,
+                                    const void* lm, int32_t* idx, float* sc, void* out,
+                                    float* lse, hipStream_t st, const Pages* pg);
 hipError_t launch_attend_decode(const Shape& s, const void* q, const void* kc, const void* vc,
                                 const void* lm, const int32_t* idx, const float* sc, void* out,
                                 float* lse, void* ws, hipStream_t st, const Pages* pg = nullptr);

@@ -16,6 +16,7 @@
 // candidates, then the local window ending at c; padding is -1.
 #include "bsa_common.hpp"
 #include "bsa_internal.hpp"
+#include "select_common.hpp"
 
 namespace bsa {
 
@@ -161,132 +162,10 @@ hipError_t launch_block_scores(const Shape& s, const float* qbar, const void* lm
 }
 
 // ---------------------------------------------------------------------------------------------
-// top-K of one selection row, executed by a whole workgroup of NT threads
+// top-K rows from the score workspace (the row select itself: topk_select in select_common.hpp)
 // ---------------------------------------------------------------------------------------------
 constexpr int kTopkThreads = 256;
 constexpr int kKeyCache = 16384;   // candidate keys held in LDS; longer rows re-read L2
-
-// exclusive prefix sum over the workgroup; *total receives the sum of all x
-template <int NT>
-__device__ __forceinline__ int block_exclusive_scan(int x, int* sbuf, int* total) {
-  constexpr int NW = NT / kWave;
-  const int lane = threadIdx.x % kWave;
-  const int w = threadIdx.x / kWave;
-  int incl = x;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += y;
-  }
-  if (lane == kWave - 1) sbuf[w] = incl;
-  __syncthreads();
-  int base = 0, tot = 0;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    const int v = sbuf[i];
-    base += (i < w) ? v : 0;
-    tot += v;
-  }
-  __syncthreads();
-  *total = tot;
-  return base + incl - x;
-}
-
-// Writes the attended set of query block c: forced sink entries, the K chosen candidates in
-// ascending block order, the local window, -1 padding; osc gets the aligned scores.
-// score_at(j) gives the score of block j <= c; key_at(i) the order-preserving key of candidate
-// n_sink + i.  Every thread of the workgroup must call it.
-template <int NT, typename ScoreAt, typename KeyAt>
-__device__ void topk_select(ScoreAt score_at, KeyAt key_at, int c, int topk, int n_sink,
-                            int n_local, int NA, int32_t* __restrict__ oidx,
-                            float* __restrict__ osc, int* hist, int* sbuf, int* sh) {
-  const int tid = threadIdx.x;
-  const int n_sink_eff = min(n_sink, c + 1);
-  const int lo = n_sink;                       // first candidate
-  const int hi = c - n_local;                  // last candidate
-  const int n = max(0, hi - lo + 1);
-  const int K = min(topk, n);
-  const int loc_beg = max(n_sink, c - n_local + 1);
-  const int n_loc = max(0, c - loc_beg + 1);
-
-  // forced entries and padding
-  for (int i = tid; i < NA; i += NT) {
-    if (i < n_sink_eff) {
-      oidx[i] = i;
-      osc[i] = score_at(i);
-    } else if (i >= n_sink_eff + K) {
-      const bool loc = i < n_sink_eff + K + n_loc;
-      const int jj = loc_beg + (i - n_sink_eff - K);
-      oidx[i] = loc ? jj : -1;
-      osc[i] = loc ? score_at(jj) : 0.0f;
-    }
-  }
-  if (K == 0) return;
-  if (K == n) {
-    for (int i = tid; i < n; i += NT) {
-      oidx[n_sink_eff + i] = lo + i;
-      osc[n_sink_eff + i] = score_at(lo + i);
-    }
-    return;
-  }
-
-  // radix select of the K-th largest key, 8 bits at a time
-  uint32_t prefix = 0u, mask = 0u;
-  int krem = K;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = tid; i < 256; i += NT) hist[i] = 0;
-    __syncthreads();
-    for (int i = tid; i < n; i += NT) {
-      const uint32_t key = key_at(i);
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
-    }
-    __syncthreads();
-    const int cnt = tid < 256 ? hist[255 - tid] : 0;   // thread t holds digit 255 - t
-    int tot;
-    const int above = block_exclusive_scan<NT>(cnt, sbuf, &tot);   // keys with larger digits
-    if (tid < 256 && above < krem && krem <= above + cnt) {
-      sh[0] = 255 - tid;
-      sh[1] = krem - above;
-    }
-    __syncthreads();
-    prefix |= (uint32_t)sh[0] << shift;
-    mask |= 255u << shift;
-    krem = sh[1];
-    __syncthreads();
-  }
-  const uint32_t tau = prefix;
-  const int need_eq = krem;                  // keys equal to tau to take, lowest index first
-
-  // index-ordered compaction: each thread owns a contiguous slice
-  const int per = (n + NT - 1) / NT;
-  const int beg = min(n, tid * per);
-  const int end = min(n, beg + per);
-  int gt = 0, eq = 0;
-  for (int i = beg; i < end; ++i) {
-    const uint32_t key = key_at(i);
-    gt += key > tau;
-    eq += key == tau;
-  }
-  int tot;
-  const int eq_before = block_exclusive_scan<NT>(eq, sbuf, &tot);
-  const int take_eq = min(eq, max(0, need_eq - eq_before));
-  int pos = block_exclusive_scan<NT>(gt + take_eq, sbuf, &tot);
-  int eq_seen = 0;
-  for (int i = beg; i < end; ++i) {
-    const uint32_t key = key_at(i);
-    bool take = key > tau;
-    if (key == tau) {
-      take = eq_seen < take_eq;
-      ++eq_seen;
-    }
-    if (take) {
-      oidx[n_sink_eff + pos] = lo + i;
-      osc[n_sink_eff + pos] = score_at(lo + i);
-      ++pos;
-    }
-  }
-}
 
 // one workgroup of 256 threads per selection row, scores from the score workspace; CACHE keys
 // of the row are held in LDS (a smaller cache lets more rows share a CU)
@@ -297,7 +176,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
                                                             int NB, int c_dec, int topk,
                                                             int n_sink, int n_local, int NA) {
   __shared__ uint32_t skeys[CACHE];
-  __shared__ int hist[256];
+  __shared__ int hist[kTopkHistWords];
   __shared__ int sbuf[kTopkThreads / kWave];
   __shared__ int sh[2];
   const int r = blockIdx.x;
@@ -350,7 +229,7 @@ __global__ __launch_bounds__(kDecodeSelThreads) void decode_select_bf16_kernel(
   constexpr int NW = kDecodeSelThreads / kWave;
   __shared__ float qb[D];
   __shared__ float ssc[kDecodeSelMaxBlocks];
-  __shared__ int hist[256];
+  __shared__ int hist[kTopkHistWords];
   __shared__ int sbuf[NW];
   __shared__ int sh[2];
   const int bg = blockIdx.x;

@@ -186,6 +186,37 @@ bsa_status_t bsa_attend_decode_paged(const bsa_params_t* params, const void* q,
                                      void* stream);
 
 /*
+ * One decode step: the selection of bsa_select_topk followed by the attention of
+ * bsa_attend_decode (method steps 2-4 for the query token of each sequence), in one call.
+ * For bf16 with at least one workgroup's worth of (sequence, kv head) pairs per compute unit
+ * (B * Hkv >= 256), NB <= 4096 and NA <= 256, both run in a single kernel: each (sequence, kv
+ * head) workgroup scores its landmarks, takes its top-K and streams the attended blocks, the
+ * sink and local blocks' copies starting while the top-K is decided.  Otherwise the two are
+ * launched one after the other.  idx and sc follow bsa_select_topk's rule and layout; the fused
+ * kernel sums each score in another float32 order, so sc may differ from that call's in the last
+ * bits and the chosen set only where two scores agree to that precision.  out and lse are those
+ * of bsa_attend_decode on the written idx / sc, up to float32 summation order.
+ *   q [B,Hq,1,D], kc/vc [B,Hkv,Tk,D], lm [B,Hkv,NB,D] (inputs); idx/sc [B,Hkv,1,NA],
+ *   out [B,Hq,1,D], lse [B,Hq] (outputs; lse may be NULL and must be NULL for HILS);
+ *   ws of bsa_decode_step_workspace_bytes(params) bytes, 256-byte aligned (NULL if that is 0).
+ */
+size_t bsa_decode_step_workspace_bytes(const bsa_params_t* params);
+bsa_status_t bsa_decode_step(const bsa_params_t* params, const void* q, const void* kc,
+                             const void* vc, const void* lm, int32_t* idx, float* sc, void* out,
+                             float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The same step over a paged, ragged batch (k_pool, v_pool, n_pages, page_table, seq_lens as
+ * for bsa_attend_decode_paged; lm from bsa_pool_landmarks_paged).  bf16 only, NB <= 16384;
+ * ws of bsa_decode_step_workspace_bytes(params) bytes.
+ */
+bsa_status_t bsa_decode_step_paged(const bsa_params_t* params, const void* q,
+                                   const void* k_pool, const void* v_pool, int32_t n_pages,
+                                   const int32_t* page_table, const int32_t* seq_lens,
+                                   const void* lm, int32_t* idx, float* sc, void* out,
+                                   float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Flat clustered index over the landmarks (LSA page, "The index stops scanning the whole
  * context", paragraphs 3-5: similar pooled keys are grouped by Ward's algorithm once a block of
  * the context is complete, and kept as each cluster's centre plus the table of its positions).

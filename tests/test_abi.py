@@ -162,6 +162,49 @@ def test_attend_validation(lib):
     assert dec(d, vc=None) == NULL
 
 
+def test_decode_step_workspace_and_validation(lib):
+    rnd = lambda x: (x + 255) // 256 * 256
+    ws = lambda p: lib.bsa_decode_step_workspace_bytes(ctypes.byref(p))
+    # 256 (sequence, kv head) pairs at 128K: one fused kernel, no workspace
+    big = _p(B=32, Hq=64, Hkv=8, seq_q=1, seq_k=131072, topk=64)
+    assert ws(big) == 0
+    # few pairs: selection kernel + split attention, whose partials need the workspace
+    few = _p(B=3, Hq=16, Hkv=2, seq_q=1, seq_k=64 * 9 + 5, topk=4)
+    assert ws(few) == lib.bsa_decode_workspace_bytes(ctypes.byref(few)) > 0
+    # float32: the generic selection's selector vectors and score rows, no split partials
+    f = _p(B=3, Hq=16, Hkv=2, seq_q=1, seq_k=640, topk=4, dtype=bsa.torch.float32)
+    assert ws(f) == rnd(lib.bsa_select_workspace_bytes(ctypes.byref(f)))
+
+    def step(p, ws=None, nbytes=0, **kw):
+        a = dict(q=FAKE, kc=FAKE, vc=FAKE, lm=FAKE, idx=FAKE, sc=FAKE, out=FAKE, lse=None)
+        a.update(kw)
+        return lib.bsa_decode_step(ctypes.byref(p), a["q"], a["kc"], a["vc"], a["lm"], a["idx"],
+                                   a["sc"], a["out"], a["lse"], ws, nbytes, None)
+
+    assert step(_p()) == SHAPE                   # seq_q must be 1
+    assert step(big, lm=None) == NULL            # the selection needs the landmarks
+    assert step(big, sc=None) == NULL
+    assert step(big, out=MIS) == ALIGN
+    hils = _p(B=32, Hq=64, Hkv=8, seq_q=1, seq_k=131072, topk=64, mode="hils")
+    assert step(hils, lse=FAKE) == UNSUP
+    assert step(few) == WS                       # workspace needed, none given
+    assert step(few, ws=FAKE, nbytes=16) == WS
+    assert step(few, ws=ctypes.c_void_p((1 << 20) + 16), nbytes=1 << 30) == ALIGN
+
+    def paged(p, n_pages=10, **kw):
+        a = dict(q=FAKE, kp=FAKE, vp=FAKE, table=FAKE, lens=FAKE, lm=FAKE, idx=FAKE, sc=FAKE,
+                 out=FAKE, lse=None)
+        a.update(kw)
+        return lib.bsa_decode_step_paged(ctypes.byref(p), a["q"], a["kp"], a["vp"], n_pages,
+                                         a["table"], a["lens"], a["lm"], a["idx"], a["sc"],
+                                         a["out"], a["lse"], None, 0, None)
+
+    assert paged(big, table=None) == NULL
+    assert paged(big, n_pages=0) == SHAPE
+    assert paged(_p(B=32, Hq=64, Hkv=8, seq_q=1, seq_k=131072, topk=64,
+                    dtype=bsa.torch.float32)) == UNSUP
+
+
 def test_python_binding_rejects_cpu_tensors():
     import torch
     with pytest.raises(ValueError):

@@ -191,6 +191,79 @@ def test_decode_small(case, mode):
 
 
 # ---------------------------------------------------------------------------------------------
+# one decode step in one call.  With >= 256 (sequence, kv head) pairs, NB <= 4096 and NA <= 256
+# (every case below) the selection and the attention run in one fused kernel, whose scores are
+# summed in another order than the selection kernel's: its sets must equal that kernel's except
+# at near ties, and its outputs must match the oracle's.
+# ---------------------------------------------------------------------------------------------
+
+STEP_DECODE = [
+    # id,             B,   Hq, Hkv, Tk,          D,   topk, data,        sink, local
+    ("g8_t20",        32,  64, 8,   64 * 20 + 7, 128, 4,    "clustered", 1, 2),
+    ("tk1",           32,  32, 8,   1,           128, 2,    "iid",       1, 2),
+    ("tk64",          64,  16, 4,   64,          128, 2,    "iid",       1, 2),
+    ("kall",          32,  64, 8,   64 * 5,      128, 50,   "iid",       1, 2),
+    ("d64",           16,  32, 16,  64 * 33,     64,  8,    "iid",       1, 2),
+    ("g32",           256, 32, 1,   64 * 10,     128, 3,    "iid",       1, 2),
+    ("many",          32,  64, 8,   64 * 80 + 5, 128, 70,   "clustered", 1, 2),
+    ("sink2_local3",  32,  32, 8,   64 * 12 + 9, 128, 5,    "clustered", 2, 3),
+    ("sink0_local1",  32,  32, 8,   64 * 9,      64,  3,    "iid",       0, 1),
+]
+
+
+@pytest.mark.parametrize("mode", ["plain", "sas", "hils"])
+@pytest.mark.parametrize("case", STEP_DECODE, ids=[c[0] for c in STEP_DECODE])
+def test_decode_step_fused(case, mode):
+    name, B, Hq, Hkv, Tk, D, topk, data, ns, nl = case
+    _print(f"decode step {name} {mode}")
+    q, kc, vc = synth.make_decode(B, Hq, Hkv, Tk, D, "bf16", data, seed=6, device="cuda",
+                                  n_centres=16, n_aim=4)
+    q4 = q[:, :, None, :].contiguous()
+    lm = bsa.pool_landmarks(kc)
+    want_lse = mode != "hils"
+    got = bsa.decode_step(q4, kc, vc, lm, topk=topk, mode=mode, n_sink=ns, n_local=nl,
+                          want_lse=want_lse)
+    two = bsa.decode(q4, kc, vc, lm, topk=topk, mode=mode, n_sink=ns, n_local=nl,
+                     want_lse=want_lse)
+    torch.cuda.synchronize()
+    same = (got["idx"] == two["idx"]).all(dim=-1).squeeze(-1)            # [B, Hkv]
+    differ = [(int(b), int(g)) for b, g in (~same).nonzero().tolist()]
+    assert len(differ) <= max(2, B * Hkv // 50), f"{name}/{mode}: {len(differ)} sets differ"
+    # float32 scores of the same blocks, summed in another order
+    sg, st = got["sc"][same], two["sc"][same]
+    assert torch.allclose(sg, st, rtol=1e-5, atol=1e-5), f"{name}/{mode}: scores differ"
+    # the same sets attended in another order: the float32 sums differ only in rounding, so
+    # the bf16 outputs differ by at most one bf16 step (2^-7 relative)
+    G = Hq // Hkv
+    rows = same.repeat_interleave(G, dim=1)                              # [B, Hq]
+    a, r = got["out"][rows].float(), two["out"][rows].float()
+    bad = ((a - r).abs() > 1e-2 * r.abs().clamp_min(1.0)).sum().item()
+    assert bad == 0, f"{name}/{mode}: {bad} outputs differ from the two-call step by > 1 bf16 step"
+    rng = np.random.default_rng(1)
+    pairs = sorted({(0, 0), (B - 1, Hkv - 1)} | set(differ) |
+                   {(int(rng.integers(B)), int(rng.integers(Hkv))) for _ in range(4)})
+    _check_decode_pairs(q4, kc, vc, got, lm, pairs, mode=mode, dtype="bf16", topk=topk,
+                        n_sink=ns, n_local=nl, tag=f"step {name}/{mode}")
+
+
+def test_decode_step_unfused_equals_two_calls():
+    """Few (sequence, kv head) pairs: the step call launches the selection and the split
+    attention, exactly the kernels of the two separate calls."""
+    q, kc, vc = synth.make_decode(3, 16, 2, 64 * 21 + 3, 128, "bf16", "clustered", seed=2,
+                                  device="cuda", n_centres=16, n_aim=4)
+    q4 = q[:, :, None, :].contiguous()
+    lm = bsa.pool_landmarks(kc)
+    for mode in ["plain", "sas", "hils"]:
+        got = bsa.decode_step(q4, kc, vc, lm, topk=6, mode=mode, want_lse=(mode != "hils"))
+        two = bsa.decode(q4, kc, vc, lm, topk=6, mode=mode, want_lse=(mode != "hils"))
+        torch.cuda.synchronize()
+        assert torch.equal(got["idx"], two["idx"]) and torch.equal(got["sc"], two["sc"])
+        assert torch.equal(got["out"].view(torch.int16), two["out"].view(torch.int16))
+        if mode != "hils":
+            assert torch.equal(got["lse"], two["lse"])
+
+
+# ---------------------------------------------------------------------------------------------
 # paged, ragged decode: each sequence against the oracle on its own contiguous cache
 # ---------------------------------------------------------------------------------------------
 
@@ -252,6 +325,34 @@ def test_decode_paged(case, mode):
                             res["lm"][b:b + 1, :, :nb], [(0, g) for g in range(Hkv)], mode=mode,
                             dtype="bf16", topk=topk, n_sink=1, n_local=2,
                             tag=f"paged {name}/{mode} seq{b} (len {L}, NB {NB})")
+
+
+@pytest.mark.parametrize("mode", ["plain", "sas", "hils"])
+def test_decode_step_paged_fused(mode):
+    """The ragged 256-pair batch through the one-call paged step (fused kernel): attended sets
+    equal the paged selection call's except at near ties, outputs match the oracle per
+    sequence."""
+    name, Hq, Hkv, D, lens, topk, data = PAGED_DECODE[-1]
+    _print(f"decode step paged {name} {mode}")
+    q, k_pool, v_pool, table, seq_lens, kcs, vcs = _paged_batch(Hq, Hkv, D, lens, data, seed=9)
+    lm = bsa.pool_landmarks_paged(k_pool, table, seq_lens)
+    got = bsa.decode_step_paged(q, k_pool, v_pool, table, seq_lens, lm, topk=topk, mode=mode,
+                                want_lse=(mode != "hils"))
+    two = bsa.decode_paged(q, k_pool, v_pool, table, seq_lens, topk=topk, mode=mode,
+                           want_lse=(mode != "hils"), lm=lm)
+    torch.cuda.synchronize()
+    same = (got["idx"] == two["idx"]).all(dim=-1).squeeze(-1)
+    assert (~same).sum().item() <= 4, "paged step: too many sets differ from the selection call"
+    assert torch.allclose(got["sc"][same], two["sc"][same], rtol=1e-5, atol=1e-5)
+    for b in sorted({0, 7, len(lens) - 1} | {int(x) for x in (~same).nonzero()[:, 0].tolist()}):
+        L = lens[b]
+        nb = (L + 63) // 64
+        one = {"idx": got["idx"][b:b + 1], "out": got["out"][b:b + 1],
+               "lse": None if got["lse"] is None else got["lse"][b:b + 1]}
+        _check_decode_pairs(q[b:b + 1], kcs[b][None], vcs[b][None], one, lm[b:b + 1, :, :nb],
+                            [(0, g) for g in (0, 5, Hkv - 1)], mode=mode, dtype="bf16",
+                            topk=topk, n_sink=1, n_local=2,
+                            tag=f"step paged {name}/{mode} seq{b} (len {L})")
 
 
 def test_decode_paged_identity_pages_match_contiguous():
