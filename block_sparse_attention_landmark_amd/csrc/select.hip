@@ -164,20 +164,22 @@ hipError_t launch_block_scores(const Shape& s, const float* qbar, const void* lm
 // ---------------------------------------------------------------------------------------------
 // top-K rows from the score workspace (the row select itself: topk_select in select_common.hpp)
 // ---------------------------------------------------------------------------------------------
-constexpr int kTopkThreads = 256;
-constexpr int kKeyCache = 16384;   // candidate keys held in LDS; longer rows re-read L2
+constexpr int kTopkKeysPerThread = 16;   // keys a thread holds in registers
 
-// one workgroup of 256 threads per selection row, scores from the score workspace; CACHE keys
-// of the row are held in LDS (a smaller cache lets more rows share a CU)
-template <int CACHE>
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ scores,
-                                                            int32_t* __restrict__ idx,
-                                                            float* __restrict__ sc, int R,
-                                                            int NB, int c_dec, int topk,
-                                                            int n_sink, int n_local, int NA) {
+// one workgroup of NT threads per selection row, scores from the score workspace: the row is
+// read with 16 loads in flight per thread into an LDS cache of CACHE keys (longer rows re-read
+// L2), from which each thread takes its contiguous slice of keys into registers.  Rows of up to
+// 4096 candidates take 256 threads (more rows share a CU), longer ones 1024, so that every key
+// of a row up to 16384 candidates stays in a register through the radix passes.
+template <int CACHE, int NT>
+__global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scores,
+                                                  int32_t* __restrict__ idx,
+                                                  float* __restrict__ sc, int R, int NB,
+                                                  int c_dec, int topk, int n_sink, int n_local,
+                                                  int NA) {
   __shared__ uint32_t skeys[CACHE];
   __shared__ int hist[kTopkHistWords];
-  __shared__ int sbuf[kTopkThreads / kWave];
+  __shared__ int sbuf[NT / kWave];
   __shared__ int sh[2];
   const int r = blockIdx.x;
   const int bg = blockIdx.y;
@@ -186,24 +188,23 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   const int n = max(0, c - n_local - n_sink + 1);
   const bool cached = n <= CACHE;
   if (cached) {
-    // 16 loads in flight per thread (a row of 16K scores is 4 rounds, not 64 round trips)
     constexpr int U = 16;
-    for (int i0 = 0; i0 < n; i0 += kTopkThreads * U) {
+    for (int i0 = 0; i0 < n; i0 += NT * U) {
       float v[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int i = i0 + u * kTopkThreads + threadIdx.x;
+        const int i = i0 + u * NT + threadIdx.x;
         v[u] = i < n ? srow[n_sink + i] : 0.0f;
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int i = i0 + u * kTopkThreads + threadIdx.x;
+        const int i = i0 + u * NT + threadIdx.x;
         if (i < n) skeys[i] = float_key(v[u]);
       }
     }
   }
   __syncthreads();
-  topk_select<kTopkThreads>(
+  topk_select<NT, kTopkKeysPerThread>(
       [&](int j) { return srow[j]; },
       [&](int i) { return cached ? skeys[i] : float_key(srow[n_sink + i]); }, c, topk, n_sink,
       n_local, NA, idx + ((size_t)bg * R + r) * NA, sc + ((size_t)bg * R + r) * NA, hist, sbuf,
@@ -304,10 +305,10 @@ hipError_t launch_topk(const Shape& s, const float* scores, int32_t* idx, float*
                        hipStream_t st) {
   dim3 grid(s.R, s.B * s.Hkv);
   if (s.NB <= 4096)
-    hipLaunchKernelGGL(topk_kernel<4096>, grid, dim3(kTopkThreads), 0, st, scores, idx, sc, s.R,
+    hipLaunchKernelGGL((topk_kernel<4096, 256>), grid, dim3(256), 0, st, scores, idx, sc, s.R,
                        s.NB, s.decode ? s.c_dec : -1, s.topk, s.n_sink, s.n_local, s.NA);
   else
-    hipLaunchKernelGGL(topk_kernel<kKeyCache>, grid, dim3(kTopkThreads), 0, st, scores, idx, sc,
+    hipLaunchKernelGGL((topk_kernel<16384, 1024>), grid, dim3(1024), 0, st, scores, idx, sc,
                        s.R, s.NB, s.decode ? s.c_dec : -1, s.topk, s.n_sink, s.n_local, s.NA);
   return hipGetLastError();
 }

@@ -56,8 +56,8 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int* sbuf, int* total
 // Writes the attended set of query block c: forced sink entries, the K chosen candidates in
 // ascending block order, the local window, -1 padding; osc gets the aligned scores.
 // score_at(j) gives the score of block j <= c; key_at(i) the order-preserving key of candidate
-// n_sink + i.  hist holds kTopkHistWords ints, sbuf NT / 64 and sh 2.  Every thread of the
-// workgroup must call it.
+// n_sink + i.  hist holds kTopkHistWords ints, sbuf NT / 64 and sh 2.  Rows of at most NT * KPT
+// candidates keep every key in registers.  Every thread of the workgroup must call it.
 //
 // The select is latency-bound (a few thousand keys per workgroup), so each radix pass costs two
 // barriers: the digit counts go into one of two histograms while the other is cleared for the
@@ -66,7 +66,7 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int* sbuf, int* total
 // word when the row has fewer than 2^15 candidates.
 constexpr int kTopkHistWords = 2 * 256;
 
-template <int NT, typename ScoreAt, typename KeyAt>
+template <int NT, int KPT = 8, typename ScoreAt, typename KeyAt>
 __device__ void topk_select(ScoreAt score_at, KeyAt key_at, int c, int topk, int n_sink,
                             int n_local, int NA, int32_t* __restrict__ oidx,
                             float* __restrict__ osc, int* hist, int* sbuf, int* sh) {
@@ -104,7 +104,6 @@ __device__ void topk_select(ScoreAt score_at, KeyAt key_at, int c, int topk, int
 
   // each thread owns the contiguous slice beg..end of the candidates (index order for the
   // compaction); slices of at most KPT keys are held in registers for every pass
-  constexpr int KPT = 8;
   const int per = (n + NT - 1) / NT;
   const int beg = min(n, tid * per);
   const int end = min(n, beg + per);
