@@ -33,7 +33,9 @@ size_t select_ws_scores_bytes(const Shape& s) {
 size_t select_ws_bytes(const Shape& s) { return select_ws_qbar_bytes(s) + select_ws_scores_bytes(s); }
 
 // ---------------------------------------------------------------------------------------------
-// scores, bf16 landmarks: 64x64 tiles per workgroup, one 32x32 MFMA sub-tile per wave
+// scores, bf16 landmarks: 64x64 tiles per workgroup, one 32x32 MFMA sub-tile per wave.  Used
+// for decode rows (one row per (sequence, kv group), tile tj = blockIdx.x) when the fused decode
+// selection does not apply; prefill rows use score_strip_kernel below.
 // ---------------------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void score_mfma_kernel(const float* __restrict__ qbar,
@@ -41,19 +43,8 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(const float* __restrict
                                                          float* __restrict__ scores, int R,
                                                          int NB, int c_dec) {
   const int bg = blockIdx.y;
-  int ti, tj;
-  if (c_dec >= 0) {
-    ti = 0;
-    tj = blockIdx.x;
-  } else {
-    // linear index p over the lower-triangular tile pairs (ti >= tj)
-    const long p = blockIdx.x;
-    long t = (long)((sqrt(8.0 * (double)p + 1.0) - 1.0) * 0.5);
-    while (tri(t + 1) <= (size_t)p) ++t;
-    while (tri(t) > (size_t)p) --t;
-    ti = (int)t;
-    tj = (int)(p - (long)tri(t));
-  }
+  const int ti = 0;
+  const int tj = blockIdx.x;
   const int w = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   const int half = lane / 32;
@@ -111,6 +102,99 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(const float* __restrict
   }
 }
 
+// scores of a prefill, bf16 landmarks: one workgroup per strip of up to kScoreStrip column
+// tiles (64 x 64) of one tile row of the lower triangle.  Each wave splits the selector vectors
+// of its 32 rows into their three bf16 terms once and reuses them for every tile of the strip
+// (same products and summation order as score_mfma_kernel, so the scores are identical).
+// Strip index p: the tile rows form bands of kScoreStrip rows; the rows of band k hold k + 1
+// strips each, so band k starts at strip kScoreStrip * k (k + 1) / 2.
+constexpr int kScoreStrip = 8;
+
+template <int D>
+__global__ __launch_bounds__(256) void score_strip_kernel(const float* __restrict__ qbar,
+                                                          const bf16* __restrict__ lm,
+                                                          float* __restrict__ scores, int R,
+                                                          int NB) {
+  constexpr int S = kScoreStrip;
+  const int bg = blockIdx.y;
+  const long p = blockIdx.x;
+  long k = (long)((sqrt(8.0 * (double)(p / S) + 1.0) - 1.0) * 0.5);
+  while ((long)S * (long)tri(k + 1) <= p) ++k;
+  while ((long)S * (long)tri(k) > p) --k;
+  const long rem = p - (long)S * (long)tri(k);
+  const int ti = (int)(k * S + rem / (k + 1));
+  const int strip = (int)(rem % (k + 1));
+  const int w = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int half = lane / 32;
+  const int l32 = lane % 32;
+  const int row0 = ti * 64 + (w / 2) * 32;
+  if (row0 >= R) return;
+  const int last_row = min(row0 + 31, R - 1);
+  const int r = row0 + l32;
+  const float* qrow = qbar + ((size_t)bg * R + min(r, R - 1)) * D;
+  bf16x8 hi[D / 16], mid[D / 16], lo[D / 16];
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) {
+    const int d0 = 16 * st + 8 * half;
+    f32x4 x0 = *reinterpret_cast<const f32x4*>(qrow + d0);
+    f32x4 x1 = *reinterpret_cast<const f32x4*>(qrow + d0 + 4);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = (e < 4) ? x0[e] : x1[e - 4];
+      if (r >= R) x = 0.0f;
+      const bf16 h = f2bf(x);
+      const float r1 = x - bf2f(h);          // exact in float32
+      const bf16 m = f2bf(r1);
+      hi[st][e] = h;
+      mid[st][e] = m;
+      lo[st][e] = f2bf(r1 - bf2f(m));        // the remaining <= 8 significant bits
+    }
+  }
+  const size_t obase = (size_t)bg * tri(R);
+  // landmark fragments of column tile tj (rows past NB read as zeros); the next tile's are
+  // loaded while the current one is multiplied
+  auto load_l = [&](int tj, bf16x8* bl) {
+    const int j = tj * 64 + (w % 2) * 32 + l32;
+    const bf16* lrow = lm + ((size_t)bg * NB + min(j, NB - 1)) * D;
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+      bl[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(lrow + 16 * st + 8 * half));
+      if (j >= NB) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bl[st][e] = f2bf(0.0f);
+      }
+    }
+  };
+  const int tj_end = min(strip * S + S, ti + 1);
+  bf16x8 bl[D / 16], bn[D / 16];
+  load_l(strip * S, bl);
+  for (int tj = strip * S; tj < tj_end; ++tj) {
+    const int col0 = tj * 64 + (w % 2) * 32;
+    if (col0 > last_row || col0 >= NB) break;
+    const int j = col0 + l32;
+    if (tj + 1 < tj_end) load_l(tj + 1, bn);
+    f32x16 acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+      acc = mfma32(hi[st], bl[st], acc);
+      acc = mfma32(mid[st], bl[st], acc);
+      acc = mfma32(lo[st], bl[st], acc);
+    }
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) bl[st] = bn[st];
+    if (j >= NB) continue;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int rr = row0 + 8 * (i / 4) + 4 * half + (i % 4);
+      if (rr >= R || j > rr) continue;
+      scores[obase + tri(rr) + j] = acc[i];
+    }
+  }
+}
+
 // scores, float32 landmarks: one thread per (row, block), float64 accumulation
 template <int D>
 __global__ __launch_bounds__(256) void score_f32_kernel(const float* __restrict__ qbar,
@@ -135,13 +219,18 @@ hipError_t launch_block_scores(const Shape& s, const float* qbar, const void* lm
                                hipStream_t st) {
   const int c_dec = s.decode ? s.c_dec : -1;
   if (s.bf16) {
-    dim3 grid;
-    if (s.decode) {
-      grid = dim3((s.c_dec + 1 + 63) / 64, s.B * s.Hkv);
-    } else {
-      const size_t nt = (s.R + 63) / 64;
-      grid = dim3((unsigned)tri(nt), s.B * s.Hkv);
+    if (!s.decode) {
+      const size_t bands = ((s.R + 63) / 64 + kScoreStrip - 1) / kScoreStrip;
+      const dim3 grid((unsigned)(kScoreStrip * tri(bands)), s.B * s.Hkv);
+      if (s.D == 128)
+        hipLaunchKernelGGL(score_strip_kernel<128>, grid, dim3(256), 0, st, qbar,
+                           (const bf16*)lm, scores, s.R, s.NB);
+      else
+        hipLaunchKernelGGL(score_strip_kernel<64>, grid, dim3(256), 0, st, qbar,
+                           (const bf16*)lm, scores, s.R, s.NB);
+      return hipGetLastError();
     }
+    const dim3 grid((s.c_dec + 1 + 63) / 64, s.B * s.Hkv);
     if (s.D == 128)
       hipLaunchKernelGGL(score_mfma_kernel<128>, grid, dim3(256), 0, st, qbar, (const bf16*)lm,
                          scores, s.R, s.NB, c_dec);

@@ -488,6 +488,28 @@ def test_workload_decode_bf16_32x128k_sampled():
     torch.cuda.empty_cache()
 
 
+def test_decode_beyond_fused_selection():
+    """A cache of 16 500 blocks (1.06 M tokens): past the one-kernel decode selection, so the
+    selector vector, the decode score kernel and the long-row top-K run (the row's 16 497
+    candidates exceed the top-K's LDS key cache and its registers, so keys are re-read)."""
+    B, Hq, Hkv, D, topk = 1, 4, 1, 64, 40
+    Tk = 64 * 16500 - 5
+    q, kc, vc = synth.make_decode(B, Hq, Hkv, Tk, D, "bf16", "clustered", seed=12, device="cuda",
+                                  n_centres=64, n_aim=4)
+    lm = bsa.pool_landmarks(kc)
+    q4 = q[:, :, None, :].contiguous()
+    for mode in ("sas", "plain"):
+        res = bsa.decode_step(q4, kc, vc, lm, topk=topk, mode=mode, want_lse=True)
+        two = bsa.decode(q4, kc, vc, lm, topk=topk, mode=mode, want_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(res["idx"], two["idx"]) and torch.equal(res["sc"], two["sc"])
+        _check_decode_pairs(q4, kc, vc, res, lm, [(0, 0)], mode=mode, dtype="bf16", topk=topk,
+                            n_sink=1, n_local=2, tag=f"decode 16500 blocks {mode}")
+    del q, kc, vc, lm
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("n_patterns", [5, 1])
 def test_selection_exact_ties(n_patterns):
     """Blocks repeat n_patterns key patterns, so most selector scores tie exactly (n_patterns=1:
