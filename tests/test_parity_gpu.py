@@ -474,15 +474,18 @@ def test_workload_decode_bf16_32x128k_sampled():
                                   n_centres=w["n_centres"], n_aim=w["n_aim"])
     lm = bsa.pool_landmarks(kc)
     q4 = q[:, :, None, :].contiguous()
-    res = bsa.decode(q4, kc, vc, lm, topk=w["topk"], mode=w["mode"], want_lse=True)
-    torch.cuda.synchronize()
     rng = np.random.default_rng(99)
     pairs = sorted({(0, 0), (B - 1, Hkv - 1)} |
                    {(int(rng.integers(B)), int(rng.integers(Hkv))) for _ in range(4)})
-    _print(f"workload decode: checking {pairs}")
-    worst = _check_decode_pairs(q4, kc, vc, res, lm, pairs, mode=w["mode"], dtype=w["dtype"],
-                                topk=w["topk"], n_sink=1, n_local=2, tag="decode")
-    _print(f"workload decode: worst max-abs {worst[0]:.3e} mean-rel {worst[1]:.3e}")
+    # the two calls (selection kernel, attention kernel) and the one-launch step that bench.py
+    # times (selection and attention fused in one kernel per (sequence, kv head))
+    for name, run in (("two calls", bsa.decode), ("one-launch step", bsa.decode_step)):
+        res = run(q4, kc, vc, lm, topk=w["topk"], mode=w["mode"], want_lse=True)
+        torch.cuda.synchronize()
+        _print(f"workload decode ({name}): checking {pairs}")
+        worst = _check_decode_pairs(q4, kc, vc, res, lm, pairs, mode=w["mode"], dtype=w["dtype"],
+                                    topk=w["topk"], n_sink=1, n_local=2, tag=f"decode {name}")
+        _print(f"workload decode ({name}): worst max-abs {worst[0]:.3e} mean-rel {worst[1]:.3e}")
     del q, kc, vc, lm, res
     gc.collect()
     torch.cuda.empty_cache()
@@ -506,6 +509,40 @@ def test_decode_beyond_fused_selection():
         _check_decode_pairs(q4, kc, vc, res, lm, [(0, 0)], mode=mode, dtype="bf16", topk=topk,
                             n_sink=1, n_local=2, tag=f"decode 16500 blocks {mode}")
     del q, kc, vc, lm
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def test_workload_decode_paged_32x16k_128k_sampled():
+    """The paged workload bench.py times (32 sequences of 16K..128K tokens in shuffled pages),
+    through the one-launch paged step; sampled sequences and kv heads against the oracle on each
+    sequence's own contiguous cache (gathered back from its pages)."""
+    w = synth.WORKLOADS["decode_paged_bf16_32x16k_128k"]
+    B, Hq, Hkv, D, K = w["B"], w["Hq"], w["Hkv"], w["D"], w["topk"]
+    lens = np.random.default_rng(11).integers(w["T_min"], w["T"] + 1, size=B).tolist()
+    _print(f"workload decode paged: generating ({sum(lens)} tokens)")
+    q, k_pool, v_pool, table, seq_lens = synth.make_paged_decode(
+        lens, Hq, Hkv, D, w["dtype"], w["data"], seed=0, device="cuda",
+        n_centres=w["n_centres"], n_aim=w["n_aim"])
+    q4 = q[:, :, None, :].contiguous()
+    lm = bsa.pool_landmarks_paged(k_pool, table, seq_lens)
+    res = bsa.decode_step_paged(q4, k_pool, v_pool, table, seq_lens, lm, topk=K, mode=w["mode"],
+                                want_lse=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    for b in sorted({0, B - 1} | {int(x) for x in rng.integers(0, B, 2)}):
+        L = lens[b]
+        nb = (L + 63) // 64
+        pages = table[b, :nb].long()
+        kc = k_pool[pages].permute(1, 0, 2, 3).reshape(1, Hkv, nb * 64, D)[:, :, :L].contiguous()
+        vc = v_pool[pages].permute(1, 0, 2, 3).reshape(1, Hkv, nb * 64, D)[:, :, :L].contiguous()
+        one = {"idx": res["idx"][b:b + 1], "out": res["out"][b:b + 1], "lse": res["lse"][b:b + 1]}
+        gs = sorted({0, Hkv - 1, int(rng.integers(Hkv))})
+        _print(f"workload decode paged: sequence {b} (len {L}), kv heads {gs}")
+        _check_decode_pairs(q4[b:b + 1], kc, vc, one, lm[b:b + 1, :, :nb], [(0, g) for g in gs],
+                            mode=w["mode"], dtype="bf16", topk=K, n_sink=1, n_local=2,
+                            tag=f"paged workload seq{b}")
+    del q, k_pool, v_pool, lm, res
     gc.collect()
     torch.cuda.empty_cache()
 
