@@ -253,14 +253,13 @@ hipError_t launch_block_scores(const Shape& s, const float* qbar, const void* lm
 // ---------------------------------------------------------------------------------------------
 // top-K rows from the score workspace (the row select itself: topk_select in select_common.hpp)
 // ---------------------------------------------------------------------------------------------
-constexpr int kTopkKeysPerThread = 16;   // keys a thread holds in registers
-
 // one workgroup of NT threads per selection row, scores from the score workspace: the row is
 // read with 16 loads in flight per thread into an LDS cache of CACHE keys (longer rows re-read
-// L2), from which each thread takes its contiguous slice of keys into registers.  Rows of up to
-// 4096 candidates take 256 threads (more rows share a CU), longer ones 1024, so that every key
+// L2), from which each thread takes its contiguous slice of up to KPT keys into registers.  Rows
+// of up to 4096 candidates take 256 threads holding 8 keys each (more rows share a CU; rows of
+// 2049..4096 candidates count from LDS), longer ones 1024 threads holding 16, so that every key
 // of a row up to 16384 candidates stays in a register through the radix passes.
-template <int CACHE, int NT>
+template <int CACHE, int NT, int KPT>
 __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scores,
                                                   int32_t* __restrict__ idx,
                                                   float* __restrict__ sc, int R, int NB,
@@ -293,7 +292,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
     }
   }
   __syncthreads();
-  topk_select<NT, kTopkKeysPerThread>(
+  topk_select<NT, KPT>(
       [&](int j) { return srow[j]; },
       [&](int i) { return cached ? skeys[i] : float_key(srow[n_sink + i]); }, c, topk, n_sink,
       n_local, NA, idx + ((size_t)bg * R + r) * NA, sc + ((size_t)bg * R + r) * NA, hist, sbuf,
@@ -394,10 +393,10 @@ hipError_t launch_topk(const Shape& s, const float* scores, int32_t* idx, float*
                        hipStream_t st) {
   dim3 grid(s.R, s.B * s.Hkv);
   if (s.NB <= 4096)
-    hipLaunchKernelGGL((topk_kernel<4096, 256>), grid, dim3(256), 0, st, scores, idx, sc, s.R,
+    hipLaunchKernelGGL((topk_kernel<4096, 256, 8>), grid, dim3(256), 0, st, scores, idx, sc, s.R,
                        s.NB, s.decode ? s.c_dec : -1, s.topk, s.n_sink, s.n_local, s.NA);
   else
-    hipLaunchKernelGGL((topk_kernel<16384, 1024>), grid, dim3(1024), 0, st, scores, idx, sc,
+    hipLaunchKernelGGL((topk_kernel<16384, 1024, 16>), grid, dim3(1024), 0, st, scores, idx, sc,
                        s.R, s.NB, s.decode ? s.c_dec : -1, s.topk, s.n_sink, s.n_local, s.NA);
   return hipGetLastError();
 }
