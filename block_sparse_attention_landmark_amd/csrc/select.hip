@@ -258,15 +258,16 @@ hipError_t launch_block_scores(const Shape& s, const float* qbar, const void* lm
 // L2), from which each thread takes its contiguous slice of up to KPT keys into registers.  Rows
 // of up to 4096 candidates take 256 threads holding 8 keys each (more rows share a CU; rows of
 // 2049..4096 candidates count from LDS), longer ones 1024 threads holding 16, so that every key
-// of a row up to 16384 candidates stays in a register through the radix passes.
-template <int CACHE, int NT, int KPT>
+// of a row up to 16384 candidates stays in a register through the radix passes; their digit
+// counts are spread over 4 words per digit.
+template <int CACHE, int NT, int KPT, int REP>
 __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scores,
                                                   int32_t* __restrict__ idx,
                                                   float* __restrict__ sc, int R, int NB,
                                                   int c_dec, int topk, int n_sink, int n_local,
                                                   int NA) {
   __shared__ uint32_t skeys[CACHE];
-  __shared__ int hist[kTopkHistWords];
+  __shared__ int hist[kTopkHistWords * REP];
   __shared__ int sbuf[NT / kWave];
   __shared__ int sh[2];
   const int r = blockIdx.x;
@@ -292,7 +293,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
     }
   }
   __syncthreads();
-  topk_select<NT, KPT>(
+  topk_select<NT, KPT, REP>(
       [&](int j) { return srow[j]; },
       [&](int i) { return cached ? skeys[i] : float_key(srow[n_sink + i]); }, c, topk, n_sink,
       n_local, NA, idx + ((size_t)bg * R + r) * NA, sc + ((size_t)bg * R + r) * NA, hist, sbuf,
@@ -393,10 +394,10 @@ hipError_t launch_topk(const Shape& s, const float* scores, int32_t* idx, float*
                        hipStream_t st) {
   dim3 grid(s.R, s.B * s.Hkv);
   if (s.NB <= 4096)
-    hipLaunchKernelGGL((topk_kernel<4096, 256, 8>), grid, dim3(256), 0, st, scores, idx, sc, s.R,
+    hipLaunchKernelGGL((topk_kernel<4096, 256, 8, 1>), grid, dim3(256), 0, st, scores, idx, sc, s.R,
                        s.NB, s.decode ? s.c_dec : -1, s.topk, s.n_sink, s.n_local, s.NA);
   else
-    hipLaunchKernelGGL((topk_kernel<16384, 1024, 16>), grid, dim3(1024), 0, st, scores, idx, sc,
+    hipLaunchKernelGGL((topk_kernel<16384, 1024, 16, 4>), grid, dim3(1024), 0, st, scores, idx, sc,
                        s.R, s.NB, s.decode ? s.c_dec : -1, s.topk, s.n_sink, s.n_local, s.NA);
   return hipGetLastError();
 }

@@ -56,8 +56,11 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int* sbuf, int* total
 // Writes the attended set of query block c: forced sink entries, the K chosen candidates in
 // ascending block order, the local window, -1 padding; osc gets the aligned scores.
 // score_at(j) gives the score of block j <= c; key_at(i) the order-preserving key of candidate
-// n_sink + i.  hist holds kTopkHistWords ints, sbuf NT / 64 and sh 2.  Rows of at most NT * KPT
-// candidates keep every key in registers.  Every thread of the workgroup must call it.
+// n_sink + i.  hist holds kTopkHistWords * R ints, sbuf NT / 64 and sh 2.  Rows of at most
+// NT * KPT candidates keep every key in registers.  With R > 1 each digit is counted in R words
+// (lane % R picks one; consecutive words, so distinct banks): the leading digits of a long row's
+// keys are mostly equal, and a single word would serialise its thousands of increments.  Every
+// thread of the workgroup must call it.
 //
 // The select is latency-bound (a few thousand keys per workgroup), so each radix pass costs two
 // barriers: the digit counts go into one of two histograms while the other is cleared for the
@@ -66,7 +69,7 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int* sbuf, int* total
 // word when the row has fewer than 2^15 candidates.
 constexpr int kTopkHistWords = 2 * 256;
 
-template <int NT, int KPT = 8, typename ScoreAt, typename KeyAt>
+template <int NT, int KPT = 8, int R = 1, typename ScoreAt, typename KeyAt>
 __device__ void topk_select(ScoreAt score_at, KeyAt key_at, int c, int topk, int n_sink,
                             int n_local, int NA, int32_t* __restrict__ oidx,
                             float* __restrict__ osc, int* hist, int* sbuf, int* sh) {
@@ -115,29 +118,34 @@ __device__ void topk_select(ScoreAt score_at, KeyAt key_at, int c, int topk, int
   // radix select of the K-th largest key, 8 bits at a time
   uint32_t prefix = 0u, mask = 0u;
   int krem = K;
-  if (tid < 256) hist[tid] = 0;
+  constexpr int HW = 256 * R;                  // words of one histogram
+  for (int i = tid; i < HW; i += NT) hist[i] = 0;
   __syncthreads();
+  const int rep = tid % R;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    int* h = hist + (pass & 1) * 256;
+    int* h = hist + (pass & 1) * HW;
     if (in_regs) {
 #pragma unroll
       for (int j = 0; j < KPT; ++j)
-        if (beg + j < end && (kr[j] & mask) == prefix) atomicAdd(&h[(kr[j] >> shift) & 255u], 1);
+        if (beg + j < end && (kr[j] & mask) == prefix)
+          atomicAdd(&h[((kr[j] >> shift) & 255u) * R + rep], 1);
     } else {
       for (int i = tid; i < n; i += NT) {     // strided: consecutive lanes, consecutive keys
         const uint32_t key = key_at(i);
-        if ((key & mask) == prefix) atomicAdd(&h[(key >> shift) & 255u], 1);
+        if ((key & mask) == prefix) atomicAdd(&h[((key >> shift) & 255u) * R + rep], 1);
       }
     }
-    if (tid < 256) hist[((pass + 1) & 1) * 256 + tid] = 0;   // the next pass's histogram
+    for (int i = tid; i < HW; i += NT) hist[((pass + 1) & 1) * HW + i] = 0;   // the next pass's
     __syncthreads();
     if (tid < kWave) {
       // lane l holds digits 255 - 4l .. 252 - 4l (descending)
       int c4[4], t4 = 0;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        c4[k] = h[255 - 4 * lane - k];
+        c4[k] = 0;
+#pragma unroll
+        for (int r = 0; r < R; ++r) c4[k] += h[(255 - 4 * lane - k) * R + r];
         t4 += c4[k];
       }
       const int incl = wave_inclusive_scan(t4);
