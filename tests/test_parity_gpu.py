@@ -192,9 +192,9 @@ def test_decode_small(case, mode):
 
 # ---------------------------------------------------------------------------------------------
 # one decode step in one call.  With >= 256 (sequence, kv head) pairs, NB <= 4096 and NA <= 256
-# (every case below) the selection and the attention run in one fused kernel, whose scores are
-# summed in another order than the selection kernel's: its sets must equal that kernel's except
-# at near ties, and its outputs must match the oracle's.
+# (every case below but the last) the selection and the attention run in one fused kernel, whose
+# scores are summed in another order than the selection kernel's: its sets must equal that
+# kernel's except at near ties, and its outputs must match the oracle's.
 # ---------------------------------------------------------------------------------------------
 
 STEP_DECODE = [
@@ -208,6 +208,8 @@ STEP_DECODE = [
     ("many",          32,  64, 8,   64 * 80 + 5, 128, 70,   "clustered", 1, 2),
     ("sink2_local3",  32,  32, 8,   64 * 12 + 9, 128, 5,    "clustered", 2, 3),
     ("sink0_local1",  32,  32, 8,   64 * 9,      64,  3,    "iid",       0, 1),
+    # NA = 303 > 256: the step launches the selection and the attention separately
+    ("na303",         32,  32, 8,   64 * 400,    64,  300,  "iid",       1, 2),
 ]
 
 
