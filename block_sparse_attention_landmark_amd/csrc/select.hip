@@ -33,9 +33,10 @@ size_t select_ws_scores_bytes(const Shape& s) {
 size_t select_ws_bytes(const Shape& s) { return select_ws_qbar_bytes(s) + select_ws_scores_bytes(s); }
 
 // ---------------------------------------------------------------------------------------------
-// scores, bf16 landmarks: 64x64 tiles per workgroup, one 32x32 MFMA sub-tile per wave.  Used
-// for decode rows (one row per (sequence, kv group), tile tj = blockIdx.x) when the fused decode
-// selection does not apply; prefill rows use score_strip_kernel below.
+// decode scores, bf16 landmarks: the one selection row of each (sequence, kv group) against
+// blocks 0..c_dec, 64 blocks per workgroup (tile tj = blockIdx.x), one 32x32 MFMA sub-tile per
+// wave (waves 2, 3 hold only padding rows and leave).  Used when the fused decode selection does
+// not apply (more than 16384 blocks); prefill rows use score_strip_kernel below.
 // ---------------------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void score_mfma_kernel(const float* __restrict__ qbar,
@@ -43,18 +44,15 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(const float* __restrict
                                                          float* __restrict__ scores, int R,
                                                          int NB, int c_dec) {
   const int bg = blockIdx.y;
-  const int ti = 0;
   const int tj = blockIdx.x;
   const int w = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   const int half = lane / 32;
   const int l32 = lane % 32;
-  const int row0 = ti * 64 + (w / 2) * 32;
+  const int row0 = (w / 2) * 32;              // R == 1: rows past it are padding
   const int col0 = tj * 64 + (w % 2) * 32;
-  const int last_row = min(row0 + 31, R - 1);
   if (row0 >= R) return;
-  const int max_c = (c_dec >= 0) ? c_dec : last_row;
-  if (col0 > max_c || col0 >= NB) return;
+  if (col0 > c_dec || col0 >= NB) return;
 
   const int r = row0 + l32;
   const int j = col0 + l32;
@@ -90,15 +88,11 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(const float* __restrict
     acc = mfma32(mid, bl, acc);
     acc = mfma32(lo, bl, acc);
   }
-  if (j >= NB) return;
+  if (j >= NB || j > c_dec) return;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int rr = row0 + 8 * (i / 4) + 4 * half + (i % 4);
-    if (rr >= R) continue;
-    const int cc = (c_dec >= 0) ? c_dec : rr;
-    if (j > cc) continue;
-    const size_t off = (c_dec >= 0) ? (size_t)bg * NB : (size_t)bg * tri(R) + tri(rr);
-    scores[off + j] = acc[i];
+    if (rr < R) scores[(size_t)bg * NB + j] = acc[i];
   }
 }
 
