@@ -134,6 +134,8 @@ SMALL_PREFILL = [
     ("g4_nqb8_d64",  1, 4,  1,   64 * 8,      64,  "bf16", 2,   1, 2, "clustered"),
     ("t1",           1, 4,  1,   1,           128, "bf16", 2,   1, 2, "iid"),
     ("t64",          1, 4,  1,   64,          64,  "bf16", 2,   1, 2, "iid"),
+    # rows of up to 73 attended entries: entries past the 64th are read from memory in the loop
+    ("g4_na73",      1, 4,  1,   64 * 90 + 7, 64,  "bf16", 70,  1, 2, "iid"),
     ("f32_g2",       1, 2,  1,   64 * 8 + 5,  64,  "f32",  2,   1, 2, "iid"),
     ("f32_d128",     1, 1,  1,   64 * 5,      128, "f32",  1,   1, 2, "iid"),
     ("f32_t65",      1, 4,  1,   65,          64,  "f32",  2,   1, 2, "iid"),
