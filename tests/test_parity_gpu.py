@@ -41,11 +41,12 @@ def _print(*a):
 # per-row oracle checks (shared by the small and the sampled tests)
 # ---------------------------------------------------------------------------------------------
 
-def _check_prefill_rows(q, k, v, res, rows, *, mode, dtype, topk, n_sink, n_local, tag):
+def _check_prefill_rows(q, k, v, res, rows, *, mode, dtype, topk, n_sink, n_local, tag,
+                        scale=None):
     B, Hq, T, D = q.shape
     Hkv = k.shape[1]
     G = Hq // Hkv
-    scale = 1.0 / math.sqrt(D)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
     idx = res["idx"].cpu().numpy()
     sc = res["sc"].cpu().numpy()
     worst = [0.0, 0.0]
@@ -83,12 +84,13 @@ def _check_prefill_rows(q, k, v, res, rows, *, mode, dtype, topk, n_sink, n_loca
     return worst
 
 
-def _check_decode_pairs(q, kc, vc, res, lm_dev, pairs, *, mode, dtype, topk, n_sink, n_local, tag):
+def _check_decode_pairs(q, kc, vc, res, lm_dev, pairs, *, mode, dtype, topk, n_sink, n_local, tag,
+                        scale=None):
     B, Hq, _, D = q.shape
     Hkv, Tk = kc.shape[1], kc.shape[2]
     G = Hq // Hkv
     c = (Tk - 1) // 64
-    scale = 1.0 / math.sqrt(D)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
     idx = res["idx"].cpu().numpy()
     worst = [0.0, 0.0]
     for (b, g) in pairs:
@@ -157,6 +159,49 @@ def test_prefill_small(case, mode):
     rows = [(b, g, c) for b in range(B) for g in range(Hkv) for c in range((T + 63) // 64)]
     _check_prefill_rows(q, k, v, res, rows, mode=mode, dtype=dtype, topk=topk, n_sink=ns,
                         n_local=nl, tag=f"{name}/{mode}")
+
+
+# a softmax scale other than 1/sqrt(D) (the C ABI's scale field): the ping-pong kernel (G = 4),
+# the generic kernel (G = 2) and the float32 kernel for prefill; both decode paths
+CUSTOM_SCALE = [
+    # id,     B, Hq, Hkv, T,           D,   dtype,  scale
+    ("g4",    1, 4,  1,   64 * 9 + 11, 128, "bf16", 0.021),
+    ("g2",    1, 4,  2,   64 * 7,      64,  "bf16", 0.3),
+    ("f32",   1, 2,  1,   64 * 5 + 3,  64,  "f32",  0.25),
+]
+
+
+@pytest.mark.parametrize("mode", ["plain", "sas", "hils"])
+@pytest.mark.parametrize("case", CUSTOM_SCALE, ids=[c[0] for c in CUSTOM_SCALE])
+def test_prefill_custom_scale(case, mode):
+    name, B, Hq, Hkv, T, D, dtype, scale = case
+    _print(f"prefill scale {name} {mode}")
+    q, k, v = synth.make_prefill(B, Hq, Hkv, T, D, dtype, "clustered", seed=13, device="cuda",
+                                 n_centres=16, n_aim=4)
+    res = bsa.prefill(q, k, v, topk=3, mode=mode, scale=scale, want_lse=(mode != "hils"))
+    torch.cuda.synchronize()
+    rows = [(b, g, c) for b in range(B) for g in range(Hkv) for c in range((T + 63) // 64)]
+    _check_prefill_rows(q, k, v, res, rows, mode=mode, dtype=dtype, topk=3, n_sink=1, n_local=2,
+                        tag=f"scale {name}/{mode}", scale=scale)
+
+
+@pytest.mark.parametrize("mode", ["plain", "sas", "hils"])
+def test_decode_custom_scale(mode):
+    # 256 (sequence, kv head) pairs, so the one-launch step takes its fused path
+    B, Hq, Hkv, Tk, D, topk, scale = 32, 64, 8, 64 * 40 + 21, 128, 6, 0.05
+    _print(f"decode scale {mode}")
+    q, kc, vc = synth.make_decode(B, Hq, Hkv, Tk, D, "bf16", "clustered", seed=17, device="cuda",
+                                  n_centres=16, n_aim=4)
+    lm = bsa.pool_landmarks(kc)
+    q4 = q[:, :, None, :].contiguous()
+    want = mode != "hils"
+    two = bsa.decode(q4, kc, vc, lm, topk=topk, mode=mode, scale=scale, want_lse=want)
+    one = bsa.decode_step(q4, kc, vc, lm, topk=topk, mode=mode, scale=scale, want_lse=want)
+    torch.cuda.synchronize()
+    pairs = [(b, g) for b in range(0, B, 5) for g in range(0, Hkv, 3)]
+    for tag, res in (("two-call", two), ("step", one)):
+        _check_decode_pairs(q4, kc, vc, res, lm, pairs, mode=mode, dtype="bf16", topk=topk,
+                            n_sink=1, n_local=2, tag=f"scale {tag}/{mode}", scale=scale)
 
 
 SMALL_DECODE = [
