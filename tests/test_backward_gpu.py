@@ -40,13 +40,13 @@ def _dout(shape, seed):
     return torch.randn(shape, generator=g, dtype=torch.float32).to(torch.bfloat16).cuda()
 
 
-def _run(q, k, v, *, topk, mode, ns, nl, seed):
-    res = bsa.prefill(q, k, v, topk=topk, mode=mode, n_sink=ns, n_local=nl,
+def _run(q, k, v, *, topk, mode, ns, nl, seed, scale=0.0):
+    res = bsa.prefill(q, k, v, topk=topk, mode=mode, n_sink=ns, n_local=nl, scale=scale,
                       want_lse=(mode != "hils"))
     dout = _dout(q.shape, seed)
     dq, dk, dv, dsc, dlm = bsa.attend_prefill_backward(
         q, k, v, res["idx"], res["sc"], res["out"], res["lse"], dout, mode=mode,
-        lm=res["lm"] if mode == "hils" else None, topk=topk, n_sink=ns, n_local=nl)
+        lm=res["lm"] if mode == "hils" else None, topk=topk, n_sink=ns, n_local=nl, scale=scale)
     torch.cuda.synchronize()
     return res, dout, dq, dk, dv, dsc, dlm
 
@@ -93,6 +93,31 @@ def test_backward_small(case, mode):
                 check_grad(host64(dlm[b, g]), ref["dlm"][b, g], f"{tag} dlm b{b} g{g}")
     if mode != "sas":
         assert torch.count_nonzero(dsc).item() == 0, f"{tag}: dsc must be zero for {mode}"
+
+
+@pytest.mark.parametrize("mode", ["plain", "sas", "hils"])
+def test_backward_custom_scale(mode):
+    """A softmax scale other than 1/sqrt(D) enters the forward, the recomputed logits, dq, dk
+    and (HiLS) the retrieval weights and dlm."""
+    B, Hq, Hkv, T, D, topk, scale = 1, 8, 2, 64 * 11 + 5, 128, 3, 0.03
+    _print(f"backward scale {mode}")
+    q, k, v = synth.make_prefill(B, Hq, Hkv, T, D, "bf16", "clustered", seed=21, device="cuda",
+                                 n_centres=16, n_aim=4)
+    res, dout, dq, dk, dv, dsc, dlm = _run(q, k, v, topk=topk, mode=mode, ns=1, nl=2, seed=23,
+                                           scale=scale)
+    ref = O.prefill_backward(host64(q), host64(k), host64(v), res["idx"].cpu().numpy(),
+                             res["sc"].cpu().numpy().astype(np.float64), host64(dout), mode=mode,
+                             lm=host64(res["lm"]), scale=scale)
+    tag = f"scale/{mode}"
+    for b in range(B):
+        for h in range(Hq):
+            check_grad(host64(dq[b, h]), ref["dq"][b, h], f"{tag} dq b{b} h{h}")
+        for g in range(Hkv):
+            check_grad(host64(dk[b, g]), ref["dk"][b, g], f"{tag} dk b{b} g{g}")
+            check_grad(host64(dv[b, g]), ref["dv"][b, g], f"{tag} dv b{b} g{g}")
+            check_grad(host64(dsc[b, g]), ref["dsc"][b, g], f"{tag} dsc b{b} g{g}")
+            if mode == "hils":
+                check_grad(host64(dlm[b, g]), ref["dlm"][b, g], f"{tag} dlm b{b} g{g}")
 
 
 def test_backward_deterministic_dq_dk_dv():
