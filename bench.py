@@ -93,6 +93,8 @@ def parse():
     ap.add_argument("--no-hils", action="store_true", help="skip the HiLS workload at 1M tokens")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3)")
+    ap.add_argument("--no-peak-probe", action="store_true",
+                    help="skip measuring the bf16 MFMA and 16 KB gather ceilings")
     return ap.parse_args()
 
 
@@ -480,6 +482,64 @@ def cpu_baseline(torch, tensors, name, synth, budget_s=12.0):
             "seconds_per_step_extrapolated": per_step}
 
 
+def measured_peaks(torch):
+    """Ceilings of this GPU measured with the probes of libbsa_peak.so: back-to-back 32x32x16 bf16
+    MFMAs on every SIMD (TFLOP/s), and random 16 KB blocks of a 4 GiB buffer gathered straight
+    into LDS (GB/s, read bytes).  Best of 3 timed launches each, HIP events on the launch stream."""
+    import ctypes
+    from block_sparse_attention_landmark_amd import build as B
+    if not os.path.exists(B.PEAK_LIB):
+        raise RuntimeError(f"{B.PEAK_LIB} is missing; build the package first")
+    lib = ctypes.CDLL(B.PEAK_LIB)
+    lib.bsa_peak_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.bsa_peak_mfma.restype = ctypes.c_int
+    lib.bsa_peak_gather.argtypes = [ctypes.c_void_p, ctypes.c_uint32, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_void_p, ctypes.c_void_p]
+    lib.bsa_peak_gather.restype = ctypes.c_int
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def best_ms(launch, reps=3):
+        launch()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            launch()
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        return best
+
+    n_wg, iters = 1024, 4000                      # 4 workgroups of 4 waves per CU
+    out = torch.empty(n_wg * 256, dtype=torch.float32, device="cuda")
+
+    def mfma():
+        if lib.bsa_peak_mfma(ctypes.c_void_p(out.data_ptr()), n_wg, iters, stream) != 0:
+            raise RuntimeError("bsa_peak_mfma failed")
+    ms = best_ms(mfma)
+    mfma_tflops = n_wg * 4 * iters * 16 * 32768 / (ms * 1e-3) / 1e12
+    src = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    n_blocks = src.numel() // 16384
+    g_wg, bpw = 256, 512                          # 256 x 4 waves x 512 blocks x 16 KB = 8 GiB
+    outg = torch.empty(g_wg * 256, dtype=torch.int32, device="cuda")
+
+    def gather():
+        if lib.bsa_peak_gather(ctypes.c_void_p(src.data_ptr()), n_blocks, g_wg, bpw,
+                               ctypes.c_void_p(outg.data_ptr()), stream) != 0:
+            raise RuntimeError("bsa_peak_gather failed")
+    ms_g = best_ms(gather)
+    gather_gbps = g_wg * 4 * bpw * 16384 / (ms_g * 1e-3) / 1e9
+    del src, out, outg
+    torch.cuda.empty_cache()
+    return {"mfma_bf16_tflops": mfma_tflops, "gather_16k_gbps": gather_gbps,
+            "how": "libbsa_peak.so: 1024 workgroups x 4 waves of back-to-back 32x32x16 bf16 MFMAs; "
+                   "256 workgroups x 4 waves gathering random 16 KB blocks of a 4 GiB buffer "
+                   "into LDS (8 GiB read); best of 3 launches"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -529,6 +589,11 @@ def main():
         hils, t = bench_prefill(torch, bsa, synth, "hils_bf16_1m", max(2, args.steps // 4), 1)
         del t
         torch.cuda.empty_cache()
+    peaks = None
+    if not args.no_peak_probe:
+        peaks = measured_peaks(torch)
+        log(f"[bench] measured ceilings: {peaks['mfma_bf16_tflops']:.0f} TFLOP/s bf16 MFMA, "
+            f"{peaks['gather_16k_gbps']:.0f} GB/s 16 KB gathers")
     if args.copy_probe:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
@@ -599,6 +664,19 @@ def main():
                                             "attend": hils["attn_ms"]},
                            "attended_tflops_attention_kernel": hils["attended_tflops_kernel"],
                            "frac_of_bf16_peak": hils["attended_tflops_kernel"] / PEAK_BF16_TFLOPS}
+    if peaks is not None:
+        # the same achieved rates against the ceilings measured on this GPU in this run
+        line["measured_peaks"] = peaks
+        line["roofline"]["frac_of_measured"] = \
+            line["roofline"]["achieved"] / peaks["mfma_bf16_tflops"]
+        for key in ("decode", "decode_paged"):
+            if key in line:
+                r = line[key]["roofline"]
+                r["frac_of_measured"] = r["achieved"] / peaks["gather_16k_gbps"]
+        for key in ("backward", "backward_hils"):
+            if key in line and "roofline" in line[key]:
+                r = line[key]["roofline"]
+                r["frac_of_measured"] = r["achieved"] / peaks["mfma_bf16_tflops"]
     if cpu is not None:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)

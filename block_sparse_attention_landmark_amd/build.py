@@ -1,4 +1,5 @@
-"""Build libbsa.so (the HIP kernels and the C-ABI) in-tree for gfx950 with hipcc.
+"""Build libbsa.so (the HIP kernels and the C-ABI) in-tree for gfx950 with hipcc, and beside it
+libbsa_peak.so (the benchmark's measured-ceiling probes, not part of the attention path).
 
     python -m block_sparse_attention_landmark_amd.build
 """
@@ -12,6 +13,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libbsa.so")
+PEAK_LIB = os.path.join(PKG, "libbsa_peak.so")
+PEAK_SOURCES = ["peak_probe.hip"]
 SOURCES = ["bsa_api.hip", "pool.hip", "select.hip", "attend_prefill.hip", "attend_decode.hip",
            "attend_f32.hip", "attend_backward.hip", "lsa.hip"]
 
@@ -36,10 +39,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found; the ROCm toolchain is required to build libbsa.so")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into libbsa.so next to this file; returns the library path."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+def _compile(sources, out: str, verbose: bool) -> None:
+    tmp = out + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, *[os.path.join(CSRC, s) for s in sources], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -49,7 +51,14 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(errs))
     if verbose and errs:
         print("\n".join(errs), file=sys.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source into libbsa.so next to this file, and the probes into
+    libbsa_peak.so; returns the path of libbsa.so."""
+    _compile(SOURCES, LIB, verbose)
+    _compile(PEAK_SOURCES, PEAK_LIB, verbose)
     return LIB
 
 
