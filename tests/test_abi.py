@@ -51,6 +51,20 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, n)
 
 
+def test_peak_probe_library_exports_its_probes():
+    """The benchmark's ceiling probes live in their own library, outside the attention ABI."""
+    from block_sparse_attention_landmark_amd import build as B
+    if not os.path.exists(B.PEAK_LIB):
+        pytest.fail("libbsa_peak.so is not built; run `python -m block_sparse_attention_landmark_amd.build`")
+    out = subprocess.run(["nm", "-D", "--defined-only", B.PEAK_LIB], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (bsa_\w+)", out))
+    assert exported == {"bsa_peak_mfma", "bsa_peak_gather"}, exported
+    main = subprocess.run(["nm", "-D", "--defined-only", bsa.library_path()], capture_output=True,
+                          text=True, check=True).stdout
+    assert "bsa_peak_" not in main
+
+
 def test_params_struct_matches_header_layout():
     # 12 int32 fields + 1 float, no padding
     assert ctypes.sizeof(bsa.Params) == 13 * 4
