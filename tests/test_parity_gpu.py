@@ -376,19 +376,20 @@ def test_decode_paged(case, mode):
                             tag=f"paged {name}/{mode} seq{b} (len {L}, NB {NB})")
 
 
+@pytest.mark.parametrize("scale", [0.0, 0.07], ids=["default_scale", "scale0.07"])
 @pytest.mark.parametrize("mode", ["plain", "sas", "hils"])
-def test_decode_step_paged_fused(mode):
+def test_decode_step_paged_fused(mode, scale):
     """The ragged 256-pair batch through the one-call paged step (fused kernel): attended sets
     equal the paged selection call's except at near ties, outputs match the oracle per
-    sequence."""
+    sequence (default softmax scale and another one)."""
     name, Hq, Hkv, D, lens, topk, data = PAGED_DECODE[-1]
-    _print(f"decode step paged {name} {mode}")
+    _print(f"decode step paged {name} {mode} scale {scale}")
     q, k_pool, v_pool, table, seq_lens, kcs, vcs = _paged_batch(Hq, Hkv, D, lens, data, seed=9)
     lm = bsa.pool_landmarks_paged(k_pool, table, seq_lens)
     got = bsa.decode_step_paged(q, k_pool, v_pool, table, seq_lens, lm, topk=topk, mode=mode,
-                                want_lse=(mode != "hils"))
+                                scale=scale, want_lse=(mode != "hils"))
     two = bsa.decode_paged(q, k_pool, v_pool, table, seq_lens, topk=topk, mode=mode,
-                           want_lse=(mode != "hils"), lm=lm)
+                           scale=scale, want_lse=(mode != "hils"), lm=lm)
     torch.cuda.synchronize()
     same = (got["idx"] == two["idx"]).all(dim=-1).squeeze(-1)
     assert (~same).sum().item() <= 4, "paged step: too many sets differ from the selection call"
@@ -401,7 +402,8 @@ def test_decode_step_paged_fused(mode):
         _check_decode_pairs(q[b:b + 1], kcs[b][None], vcs[b][None], one, lm[b:b + 1, :, :nb],
                             [(0, g) for g in (0, 5, Hkv - 1)], mode=mode, dtype="bf16",
                             topk=topk, n_sink=1, n_local=2,
-                            tag=f"step paged {name}/{mode} seq{b} (len {L})")
+                            tag=f"step paged {name}/{mode} seq{b} (len {L})",
+                            scale=scale if scale else None)
 
 
 def test_decode_paged_identity_pages_match_contiguous():
