@@ -456,12 +456,26 @@ __global__ __launch_bounds__(512) void attend_prefill_pp_kernel(
   // This wave's part of unit a: SPW copies of 1 KB (K slab, V slab, K slab, ...), issued in two
   // halves: copies x with x % 2 == h for half h (K slabs, then V slabs).
   const uint32_t u_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16*)&U[0][0];
+  // entries 0..63, one per lane: byte offset of the block a copy reads (the entry's block, or
+  // the current block for an invalid entry) and that block's last row inside the sequence
+  const int jcp = (jvec >= 0 && jvec <= c) ? jvec : c;
+  const uint32_t cp_off = (uint32_t)jcp * (uint32_t)(kBlock * D * 2);
+  const int cp_lim = T - 1 - jcp * kBlock;
   auto copy_half = [&](int a, int hv) {
     const uint32_t dst = u_lds + (uint32_t)(a % kPpUnits) * (2 * TILE * 2);
-    int j = hv == 0 ? entry(min(a, nval - 1)) : entry(max(a - 1, 0));
-    j = j < 0 ? c : j;
-    const int lim = T - 1 - j * kBlock;
-    const char* blk = (hv == 0 ? kb : vb) + (size_t)j * (kBlock * D * 2);
+    const int ae = hv == 0 ? min(a, nval - 1) : max(a - 1, 0);
+    uint32_t off;
+    int lim;
+    if (ae < kWave) {
+      off = (uint32_t)__builtin_amdgcn_readlane((int)cp_off, ae);
+      lim = __builtin_amdgcn_readlane(cp_lim, ae);
+    } else {
+      int j = entry(ae);
+      j = j < 0 ? c : j;
+      off = (uint32_t)j * (uint32_t)(kBlock * D * 2);
+      lim = T - 1 - j * kBlock;
+    }
+    const char* blk = (hv == 0 ? kb : vb) + off;
 #pragma unroll
     for (int i = 0; i < SPW / 2; ++i) {
       const int sl = w + 8 * i;
