@@ -354,7 +354,7 @@ __global__ __launch_bounds__(HPW * 128) void attend_prefill_bf16_kernel(
 // register round trip) during phases 2a-2 and 2a-1, the copies of all eight waves sharing the
 // 32 KB.  16-byte chunks are XOR-swizzled per row so the K fragment reads and the transposed V
 // reads are free of bank conflicts.
-template <int D, int MODE, bool PRIO>
+template <int D, int MODE>
 __global__ __launch_bounds__(512) void attend_prefill_pp_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const int32_t* __restrict__ idx, const float* __restrict__ sc, bf16* __restrict__ out,
@@ -511,7 +511,6 @@ __global__ __launch_bounds__(512) void attend_prefill_pp_kernel(
   auto mphase = [&](int a, auto pv_tag, auto qk_tag) {
     constexpr bool PV = decltype(pv_tag)::value;
     constexpr bool QK = decltype(qk_tag)::value;
-    if (PRIO) __builtin_amdgcn_s_setprio(1);
     const bf16* Ku = U[a % kPpUnits];
     const bf16* Vu = U[a % kPpUnits] + TILE;
     auto read_v = [&](int ks, bf16x8* vf) {
@@ -569,7 +568,6 @@ __global__ __launch_bounds__(512) void attend_prefill_pp_kernel(
       }
       __builtin_amdgcn_sched_group_barrier(0x008, D / 16, 0);
     }
-    if (PRIO) __builtin_amdgcn_s_setprio(0);
   };
 
   // vector phase of entry a: online softmax of its scores into pf.  The probabilities are first
@@ -730,7 +728,7 @@ static void launch_prefill_bf16_d(const Shape& s, const void* q, const void* k, 
   else if (s.mode == 1) BSA_PF(1, HPW); \
   else BSA_PF(2, HPW);
 #define BSA_PP(MODE)                                                                           \
-  hipLaunchKernelGGL((attend_prefill_pp_kernel<D, MODE, true>), grid, dim3(512), 0, st,         \
+  hipLaunchKernelGGL((attend_prefill_pp_kernel<D, MODE>), grid, dim3(512), 0, st,         \
                      (const bf16*)q, (const bf16*)k, (const bf16*)v, idx, sc, (bf16*)out, lse, \
                      s.Hq, s.Hkv, s.G, s.Tq, s.R, s.NA, n_hc, sl2)
   if (hpw == 4 && s.mode == 0) {
