@@ -102,6 +102,24 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def stat(xs, kind):
+    xs = sorted(xs)
+    if kind == "median":
+        n = len(xs)
+        return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+    raise ValueError(kind)
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 class Events:
     """Pairs of HIP events on the current stream (where libbsa launches its kernels)."""
 
@@ -165,16 +183,34 @@ def bench_prefill(torch, bsa, synth, name, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     flops = attended_flops(B, Hq, D, T, K)
-    attn_ms = sum(ev_attn.ms()) / steps
+    attn = ev_attn.ms()
+    attn_ms = sum(attn) / steps
+    # the same steps once more, each after a 1 GiB read that evicts L2 and the memory-side
+    # cache (outside the timed region above), timed step by step with HIP events
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    ev_attn.pairs, ev_sel.pairs, ev_pool.pairs = [], [], []
+    for _ in range(steps):
+        flush.sum()
+        step(True)
+    torch.cuda.synchronize()
+    del flush
+    f_attn = ev_attn.ms()
+    f_step = [a + b + c for a, b, c in zip(ev_pool.ms(), ev_sel.ms(), f_attn)]
     res = {
         "ms_per_step": wall * 1e3 / steps,
         "tok_per_s": B * T * steps / wall,
         "attn_ms": attn_ms,
+        "attn_ms_median": stat(attn, "median"),
+        "attn_ms_min": min(attn),
         "select_ms": sum(ev_sel.ms()) / steps,
         "pool_ms": sum(ev_pool.ms()) / steps,
         "attended_flops": flops,
         "attended_tflops_kernel": flops / (attn_ms * 1e-3) / 1e12,
         "attended_tflops_e2e": flops * steps / wall / 1e12,
+        "flushed": {"step_ms_median": stat(f_step, "median"), "step_ms_min": min(f_step),
+                    "attend_ms_median": stat(f_attn, "median"), "attend_ms_min": min(f_attn),
+                    "how": "each step after a 1 GiB read that evicts L2 and the memory-side "
+                           "cache; pool + select + attend summed from HIP events"},
     }
     log(f"[bench] {name}: {json.dumps(res)}")
     tensors = (q, k, v, lm, idx, sc, out, ws)
@@ -356,7 +392,8 @@ def bench_decode(torch, bsa, synth, steps, warmup):
     step_us = 1e3 * sum(ev_step.ms()) / steps
     two_us = 1e3 * sum(ev_two.ms()) / steps
     attn_us = 1e3 * sum(ev_attn.ms()) / steps
-    res = {"us_per_step": step_us, "two_call_us_per_step": two_us,
+    res = {"us_per_step": step_us, "us_per_step_median": 1e3 * stat(ev_step.ms(), "median"),
+           "us_per_step_min": 1e3 * min(ev_step.ms()), "two_call_us_per_step": two_us,
            "two_call_breakdown_us": {"select": two_us - attn_us, "attend": attn_us},
            "algorithmic_bytes": nbytes, "hbm_gbps": nbytes / (step_us * 1e-6) / 1e9}
     res["hbm_frac"] = res["hbm_gbps"] / PEAK_HBM_GBPS
@@ -425,7 +462,8 @@ def bench_decode_paged(torch, bsa, synth, steps, warmup):
     res = {"workload": f"{name}: {B} seqs of {min(lens)}..{max(lens)} cached tokens (seeded "
                        f"uniform), shuffled 64-token pages, Hq={Hq}, Hkv={Hkv}, D={D}, "
                        f"top-K={K} + sink + 2 local, bf16",
-           "us_per_step": step_us, "two_call_us_per_step": two_us,
+           "us_per_step": step_us, "us_per_step_median": 1e3 * stat(ev_step.ms(), "median"),
+           "us_per_step_min": 1e3 * min(ev_step.ms()), "two_call_us_per_step": two_us,
            "two_call_breakdown_us": {"select": two_us - attn_us, "attend": attn_us},
            "hbm_gbps": nbytes / (step_us * 1e-6) / 1e9}
     res["roofline"] = {"bound": "hbm", "achieved": res["hbm_gbps"], "peak": PEAK_HBM_GBPS,
@@ -442,11 +480,20 @@ def cpu_baseline(torch, tensors, name, synth, budget_s=12.0):
     """The float64 oracle on a sample of the prefill workload, extrapolated to tok/s."""
     import numpy as np
     import oracle as O
+    cores = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=cores)     # BLAS threads = every core of this process
     except Exception:  # noqa: BLE001
-        threads = 1
+        limiter = None
+    try:
+        return _cpu_baseline(torch, tensors, name, synth, budget_s, cores, np, O)
+    finally:
+        if limiter is not None:
+            limiter.restore_original_limits()
+
+
+def _cpu_baseline(torch, tensors, name, synth, budget_s, cores, np, O):
     w = synth.WORKLOADS[name]
     q, k, v = tensors[:3]
     B, Hq, Hkv, T, D, K = w["B"], w["Hq"], w["Hkv"], w["T"], w["D"], w["topk"]
@@ -474,7 +521,8 @@ def cpu_baseline(torch, tensors, name, synth, budget_s=12.0):
         t_rows += time.perf_counter() - t1
         n_rows += 1
     per_step = B * Hkv * (t_lm + t_rows / n_rows * NQB)
-    return {"value": B * T / per_step, "unit": "tok/s", "cores": int(threads), "kind": "oracle",
+    return {"value": B * T / per_step, "unit": "tok/s", "cores": cores, "cpu_model": cpu_model(),
+            "kind": "oracle",
             "sample": (f"kv group 0 of {name}: its landmarks plus {n_rows} random query blocks "
                        f"(all {G} heads x 64 tokens: scores, top-K, gates, attention) in "
                        f"{t_lm + t_rows:.1f} s; extrapolated linearly to {B * Hkv} groups x "
@@ -624,6 +672,9 @@ def main():
         "attended_tflops_attention_kernel": pre["attended_tflops_kernel"],
         "breakdown_ms": {"pool": pre["pool_ms"], "select": pre["select_ms"],
                          "attend": pre["attn_ms"]},
+        "attend_ms_median": pre["attn_ms_median"],
+        "attend_ms_min": pre["attn_ms_min"],
+        "flushed": pre["flushed"],
         "roofline": {"bound": "mfma", "achieved": pre["attended_tflops_kernel"],
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": pre["attended_tflops_kernel"] / PEAK_BF16_TFLOPS,
@@ -638,6 +689,8 @@ def main():
                         "D=128, top-K=64 + sink + 2 local, bf16",
             "step": "one decode step call: selection and attention in one fused kernel",
             "hbm_gbps": dec["hbm_gbps"], "us_per_step": dec["us_per_step"],
+            "us_per_step_median": dec["us_per_step_median"],
+            "us_per_step_min": dec["us_per_step_min"],
             "two_call_us_per_step": dec["two_call_us_per_step"],
             "two_call_breakdown_us": dec["two_call_breakdown_us"],
             "roofline": {"bound": "hbm", "achieved": dec["hbm_gbps"], "peak": PEAK_HBM_GBPS,

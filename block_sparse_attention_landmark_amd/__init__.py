@@ -116,6 +116,8 @@ def load_library():
     lib.bsa_lsa_tree_centres.restype = st
     lib.bsa_lsa_tree_select.argtypes = [P, vp, vp, i32, i32, i32, i32] + [vp] * 7 + [vp, ctypes.c_size_t, vp]
     lib.bsa_lsa_tree_select.restype = st
+    lib.bsa_workspace_bytes.argtypes = [P, ctypes.c_int]
+    lib.bsa_workspace_bytes.restype = ctypes.c_size_t
     lib.bsa_status_string.argtypes = [ctypes.c_int]
     lib.bsa_status_string.restype = ctypes.c_char_p
     lib.bsa_last_error.argtypes = []
@@ -141,17 +143,30 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _need(t: torch.Tensor, name: str, dtype=None, ndim=None):
+def _need(t: torch.Tensor, name: str, dtype=None, ndim=None, shape=None):
+    """Type, dtype, rank, exact shape and contiguity of a tensor handed to the library.  The
+    C ABI receives bare pointers, so this is the only place where a buffer that is too small
+    or of the wrong type can be caught.  The device is checked separately (_on_device), after
+    every tensor of the call has passed this check."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
-        raise ValueError(f"{name} must be on a HIP device (got {t.device})")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dimensions (got {t.dim()})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _on_device(ref: torch.Tensor, **tensors):
+    """Every tensor of a call lives on the same HIP device as `ref` (None entries skipped)."""
+    if ref.device.type != "cuda":
+        raise ValueError(f"tensors must be on a HIP device (got {ref.device})")
+    for name, t in tensors.items():
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, expected {ref.device}")
 
 
 def make_params(*, B, Hq, Hkv, D, seq_q, seq_k, dtype, topk=0, n_sink=1, n_local=2, scale=0.0,
@@ -175,7 +190,8 @@ def pool_landmarks(k: torch.Tensor, out: torch.Tensor | None = None) -> torch.Te
     B, Hkv, T, D = k.shape
     if out is None:
         out = torch.empty((B, Hkv, _nblocks(T), D), dtype=k.dtype, device=k.device)
-    _need(out, "lm", dtype=k.dtype, ndim=4)
+    _need(out, "lm", dtype=k.dtype, shape=(B, Hkv, _nblocks(T), D))
+    _on_device(k, lm=out)
     p = make_params(B=B, Hq=Hkv, Hkv=Hkv, D=D, seq_q=T, seq_k=T, dtype=k.dtype)
     _check("bsa_pool_landmarks", lib.bsa_pool_landmarks(ctypes.byref(p), _ptr(k), _ptr(out),
                                                         _stream(k.device)))
@@ -204,8 +220,7 @@ def select_topk(q: torch.Tensor, lm: torch.Tensor, *, topk: int, seq_k: int | No
     B, Hq, Tq, D = q.shape
     Hkv = lm.shape[1]
     Tk = Tq if seq_k is None else int(seq_k)
-    if lm.shape != (B, Hkv, _nblocks(Tk), D):
-        raise ValueError(f"lm shape {tuple(lm.shape)} does not match {(B, Hkv, _nblocks(Tk), D)}")
+    _need(lm, "lm", shape=(B, Hkv, _nblocks(Tk), D))
     p = make_params(B=B, Hq=Hq, Hkv=Hkv, D=D, seq_q=Tq, seq_k=Tk, dtype=q.dtype, topk=topk,
                     n_sink=n_sink, n_local=n_local)
     R = 1 if (Tq == 1 and Tk != 1) else _nblocks(Tq)
@@ -214,11 +229,13 @@ def select_topk(q: torch.Tensor, lm: torch.Tensor, *, topk: int, seq_k: int | No
         idx = torch.empty((B, Hkv, R, NA), dtype=torch.int32, device=q.device)
     if sc is None:
         sc = torch.empty((B, Hkv, R, NA), dtype=torch.float32, device=q.device)
-    _need(idx, "idx", dtype=torch.int32, ndim=4)
-    _need(sc, "sc", dtype=torch.float32, ndim=4)
+    _need(idx, "idx", dtype=torch.int32, shape=(B, Hkv, R, NA))
+    _need(sc, "sc", dtype=torch.float32, shape=(B, Hkv, R, NA))
     need = select_workspace_bytes(p)
     if ws is None:
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _need(ws, "ws", dtype=torch.uint8, ndim=1)
+    _on_device(q, lm=lm, idx=idx, sc=sc, ws=ws)
     _check("bsa_select_topk", lib.bsa_select_topk(ctypes.byref(p), _ptr(q), _ptr(lm), _ptr(idx),
                                                   _ptr(sc), _ptr(ws), ws.numel(),
                                                   _stream(q.device)))
@@ -230,31 +247,30 @@ def attend_prefill(q, k, v, idx, sc=None, lm=None, *, mode="plain", topk=None, n
     """Block-sparse prefill attention; returns (out [B,Hq,T,D], lse [B,Hq,T] or None)."""
     lib = load_library()
     _need(q, "q", ndim=4)
-    _need(k, "k", dtype=q.dtype, ndim=4)
-    _need(v, "v", dtype=q.dtype, ndim=4)
-    _need(idx, "idx", dtype=torch.int32, ndim=4)
     B, Hq, T, D = q.shape
+    _need(k, "k", dtype=q.dtype, ndim=4)
     Hkv = k.shape[1]
-    if k.shape != (B, Hkv, T, D) or v.shape != k.shape:
-        raise ValueError("k and v must be [B,Hkv,T,D] matching q")
+    _need(k, "k", shape=(B, Hkv, T, D))
+    _need(v, "v", dtype=q.dtype, shape=(B, Hkv, T, D))
+    _need(idx, "idx", dtype=torch.int32, ndim=4)
     NA = idx.shape[-1]
     if topk is None:
         topk = NA - n_sink - n_local
-    if idx.shape != (B, Hkv, _nblocks(T), NA) or NA != n_sink + n_local + topk:
-        raise ValueError(f"idx shape {tuple(idx.shape)} does not match the call")
+    if NA != n_sink + n_local + topk:
+        raise ValueError(f"idx has {NA} entries per row, the call needs n_sink + n_local + topk")
+    _need(idx, "idx", shape=(B, Hkv, _nblocks(T), NA))
     if sc is not None:
-        _need(sc, "sc", dtype=torch.float32, ndim=4)
-        if sc.shape != idx.shape:
-            raise ValueError("sc must have idx's shape")
+        _need(sc, "sc", dtype=torch.float32, shape=idx.shape)
     if lm is not None:
-        _need(lm, "lm", dtype=q.dtype, ndim=4)
-        if lm.shape != (B, Hkv, _nblocks(T), D):
-            raise ValueError("lm must be [B,Hkv,ceil(T/64),D]")
+        _need(lm, "lm", dtype=q.dtype, shape=(B, Hkv, _nblocks(T), D))
     if out is None:
         out = torch.empty_like(q)
-    _need(out, "out", dtype=q.dtype, ndim=4)
+    _need(out, "out", dtype=q.dtype, shape=q.shape)
     if want_lse and lse is None:
         lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", dtype=torch.float32, shape=(B, Hq, T))
+    _on_device(q, k=k, v=v, idx=idx, sc=sc, lm=lm, out=out, lse=lse)
     p = make_params(B=B, Hq=Hq, Hkv=Hkv, D=D, seq_q=T, seq_k=T, dtype=q.dtype, topk=topk,
                     n_sink=n_sink, n_local=n_local, scale=scale, mode=mode)
     _check("bsa_attend_prefill",
@@ -268,31 +284,39 @@ def attend_decode(q, kc, vc, idx, sc=None, lm=None, *, mode="plain", topk=None, 
     """Block-sparse decode attention of the token at position Tk-1; q [B,Hq,1,D]."""
     lib = load_library()
     _need(q, "q", ndim=4)
-    _need(kc, "kc", dtype=q.dtype, ndim=4)
-    _need(vc, "vc", dtype=q.dtype, ndim=4)
-    _need(idx, "idx", dtype=torch.int32, ndim=4)
     B, Hq, one, D = q.shape
+    if one != 1:
+        raise ValueError("q must be [B,Hq,1,D]")
+    _need(kc, "kc", dtype=q.dtype, ndim=4)
     Hkv, Tk = kc.shape[1], kc.shape[2]
-    if one != 1 or kc.shape != (B, Hkv, Tk, D) or vc.shape != kc.shape:
-        raise ValueError("q must be [B,Hq,1,D] and kc/vc [B,Hkv,Tk,D]")
+    _need(kc, "kc", shape=(B, Hkv, Tk, D))
+    _need(vc, "vc", dtype=q.dtype, shape=(B, Hkv, Tk, D))
+    _need(idx, "idx", dtype=torch.int32, ndim=4)
     NA = idx.shape[-1]
     if topk is None:
         topk = NA - n_sink - n_local
-    if idx.shape != (B, Hkv, 1, NA) or NA != n_sink + n_local + topk:
-        raise ValueError(f"idx shape {tuple(idx.shape)} does not match the call")
+    if NA != n_sink + n_local + topk:
+        raise ValueError(f"idx has {NA} entries per row, the call needs n_sink + n_local + topk")
+    _need(idx, "idx", shape=(B, Hkv, 1, NA))
     if sc is not None:
-        _need(sc, "sc", dtype=torch.float32, ndim=4)
+        _need(sc, "sc", dtype=torch.float32, shape=(B, Hkv, 1, NA))
     if lm is not None:
-        _need(lm, "lm", dtype=q.dtype, ndim=4)
+        _need(lm, "lm", dtype=q.dtype, shape=(B, Hkv, _nblocks(Tk), D))
     if out is None:
         out = torch.empty_like(q)
+    _need(out, "out", dtype=q.dtype, shape=q.shape)
     if want_lse and lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", dtype=torch.float32, shape=(B, Hq))
     p = make_params(B=B, Hq=Hq, Hkv=Hkv, D=D, seq_q=1, seq_k=Tk, dtype=q.dtype, topk=topk,
                     n_sink=n_sink, n_local=n_local, scale=scale, mode=mode)
     need = decode_workspace_bytes(p)
     if ws is None and need > 0:
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if ws is not None:
+        _need(ws, "ws", dtype=torch.uint8, ndim=1)
+    _on_device(q, kc=kc, vc=vc, idx=idx, sc=sc, lm=lm, out=out, lse=lse, ws=ws)
     _check("bsa_attend_decode",
            lib.bsa_attend_decode(ctypes.byref(p), _ptr(q), _ptr(kc), _ptr(vc), _ptr(lm), _ptr(idx),
                                  _ptr(sc), _ptr(out), _ptr(lse), _ptr(ws),
@@ -316,32 +340,27 @@ def attend_prefill_backward(q, k, v, idx, sc, out, lse, dout, *, mode="plain", l
     """
     lib = load_library()
     _need(q, "q", dtype=torch.bfloat16, ndim=4)
-    for t, n in ((k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
-        _need(t, n, dtype=q.dtype, ndim=4)
-    _need(idx, "idx", dtype=torch.int32, ndim=4)
     B, Hq, T, D = q.shape
+    _need(k, "k", dtype=q.dtype, ndim=4)
     Hkv = k.shape[1]
-    if k.shape != (B, Hkv, T, D) or v.shape != k.shape:
-        raise ValueError("k and v must be [B,Hkv,T,D] matching q")
-    if out.shape != q.shape or dout.shape != q.shape:
-        raise ValueError("out and dout must have q's shape")
+    _need(k, "k", shape=(B, Hkv, T, D))
+    _need(v, "v", dtype=q.dtype, shape=(B, Hkv, T, D))
+    if out is not None:
+        _need(out, "out", dtype=q.dtype, shape=q.shape)
+    _need(dout, "dout", dtype=q.dtype, shape=q.shape)
     if lse is not None:
-        _need(lse, "lse", dtype=torch.float32, ndim=3)
-        if lse.shape != (B, Hq, T):
-            raise ValueError("lse must be [B,Hq,T]")
+        _need(lse, "lse", dtype=torch.float32, shape=(B, Hq, T))
+    _need(idx, "idx", dtype=torch.int32, ndim=4)
     NA = idx.shape[-1]
     if topk is None:
         topk = NA - n_sink - n_local
-    if idx.shape != (B, Hkv, _nblocks(T), NA) or NA != n_sink + n_local + topk:
-        raise ValueError(f"idx shape {tuple(idx.shape)} does not match the call")
+    if NA != n_sink + n_local + topk:
+        raise ValueError(f"idx has {NA} entries per row, the call needs n_sink + n_local + topk")
+    _need(idx, "idx", shape=(B, Hkv, _nblocks(T), NA))
     if sc is not None:
-        _need(sc, "sc", dtype=torch.float32, ndim=4)
-        if sc.shape != idx.shape:
-            raise ValueError("sc must have idx's shape")
+        _need(sc, "sc", dtype=torch.float32, shape=idx.shape)
     if lm is not None:
-        _need(lm, "lm", dtype=q.dtype, ndim=4)
-        if lm.shape != (B, Hkv, _nblocks(T), D):
-            raise ValueError("lm must be [B,Hkv,ceil(T/64),D]")
+        _need(lm, "lm", dtype=q.dtype, shape=(B, Hkv, _nblocks(T), D))
     p = make_params(B=B, Hq=Hq, Hkv=Hkv, D=D, seq_q=T, seq_k=T, dtype=q.dtype, topk=topk,
                     n_sink=n_sink, n_local=n_local, scale=scale, mode=mode)
     if dq is None:
@@ -354,17 +373,20 @@ def attend_prefill_backward(q, k, v, idx, sc, out, lse, dout, *, mode="plain", l
         dsc = torch.empty(idx.shape, dtype=torch.float32, device=q.device)
     if mode == "hils" and dlm is None:
         dlm = torch.empty((B, Hkv, _nblocks(T), D), dtype=torch.float32, device=q.device)
-    _need(dq, "dq", dtype=q.dtype, ndim=4)
-    _need(dk, "dk", dtype=q.dtype, ndim=4)
-    _need(dv, "dv", dtype=q.dtype, ndim=4)
-    _need(dsc, "dsc", dtype=torch.float32, ndim=4)
+    _need(dq, "dq", dtype=q.dtype, shape=q.shape)
+    _need(dk, "dk", dtype=q.dtype, shape=k.shape)
+    _need(dv, "dv", dtype=q.dtype, shape=k.shape)
+    _need(dsc, "dsc", dtype=torch.float32, shape=idx.shape)
     if dlm is not None:
-        _need(dlm, "dlm", dtype=torch.float32, ndim=4)
+        _need(dlm, "dlm", dtype=torch.float32, shape=(B, Hkv, _nblocks(T), D))
     need = backward_workspace_bytes(p)
     if need == 0:
         need = 256    # the call itself reports why the shape is rejected
     if ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _need(ws, "ws", dtype=torch.uint8, ndim=1)
+    _on_device(q, k=k, v=v, idx=idx, sc=sc, out=out, lse=lse, dout=dout, lm=lm, dq=dq, dk=dk,
+               dv=dv, dsc=dsc, dlm=dlm, ws=ws)
     _check("bsa_attend_prefill_backward",
            lib.bsa_attend_prefill_backward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(lm),
                                            _ptr(idx), _ptr(sc), _ptr(out), _ptr(lse), _ptr(dout),
@@ -388,6 +410,7 @@ def lsa_build_index(lm: torch.Tensor, *, seg_blocks: int = 64, n_clusters: int =
     offsets = torch.empty((B, Hkv, NS, n_clusters + 1), dtype=torch.int32, device=dev)
     merges = torch.empty((B, Hkv, NS, max(seg_blocks - n_clusters, 0), 2), dtype=torch.int32,
                          device=dev)
+    _on_device(lm)
     p = make_params(B=B, Hq=Hkv, Hkv=Hkv, D=D, seq_q=NB * 64, seq_k=NB * 64, dtype=lm.dtype)
     _check("bsa_lsa_build_index",
            lib.bsa_lsa_build_index(ctypes.byref(p), _ptr(lm), seg_blocks, n_clusters,
@@ -395,6 +418,35 @@ def lsa_build_index(lm: torch.Tensor, *, seg_blocks: int = 64, n_clusters: int =
                                    _stream(dev)))
     return {"centres": centres, "members": members, "offsets": offsets, "merges": merges,
             "seg_blocks": seg_blocks, "n_clusters": n_clusters}
+
+
+def _check_index(index: dict, B: int, Hkv: int, NB: int, D: int, tree: bool = False):
+    """Shapes and dtypes of an index from lsa_build_index (and lsa_build_tree)."""
+    seg, nc = int(index["seg_blocks"]), int(index["n_clusters"])
+    if seg < 1:
+        raise ValueError("index seg_blocks must be >= 1")
+    NS = NB // seg
+    _need(index["centres"], "centres", dtype=torch.float32, shape=(B, Hkv, NS * nc, D))
+    _need(index["members"], "members", dtype=torch.int32, shape=(B, Hkv, NS, seg))
+    _need(index["offsets"], "offsets", dtype=torch.int32, shape=(B, Hkv, NS, nc + 1))
+    if tree:
+        fan = int(index["fanout"])
+        if fan < 1:
+            raise ValueError("index fanout must be >= 1")
+        _need(index["seg_centres"], "seg_centres", dtype=torch.float32, shape=(B, Hkv, NS, D))
+        _need(index["grp_centres"], "grp_centres", dtype=torch.float32,
+              shape=(B, Hkv, NS // fan, D))
+    return NS
+
+
+def _select_outputs(q, B, Hkv, R, NA, idx, sc):
+    if idx is None:
+        idx = torch.empty((B, Hkv, R, NA), dtype=torch.int32, device=q.device)
+    if sc is None:
+        sc = torch.empty((B, Hkv, R, NA), dtype=torch.float32, device=q.device)
+    _need(idx, "idx", dtype=torch.int32, shape=(B, Hkv, R, NA))
+    _need(sc, "sc", dtype=torch.float32, shape=(B, Hkv, R, NA))
+    return idx, sc
 
 
 def lsa_select(q: torch.Tensor, lm: torch.Tensor, index: dict, *, topk: int,
@@ -408,21 +460,19 @@ def lsa_select(q: torch.Tensor, lm: torch.Tensor, index: dict, *, topk: int,
     B, Hq, Tq, D = q.shape
     Hkv = lm.shape[1]
     Tk = Tq if seq_k is None else int(seq_k)
-    if lm.shape != (B, Hkv, _nblocks(Tk), D):
-        raise ValueError(f"lm shape {tuple(lm.shape)} does not match {(B, Hkv, _nblocks(Tk), D)}")
+    _need(lm, "lm", shape=(B, Hkv, _nblocks(Tk), D))
+    NS = _check_index(index, B, Hkv, _nblocks(Tk), D)
     p = make_params(B=B, Hq=Hq, Hkv=Hkv, D=D, seq_q=Tq, seq_k=Tk, dtype=q.dtype, topk=topk,
                     n_sink=n_sink, n_local=n_local)
     R = 1 if (Tq == 1 and Tk != 1) else _nblocks(Tq)
-    NA = n_sink + n_local + topk
-    if idx is None:
-        idx = torch.empty((B, Hkv, R, NA), dtype=torch.int32, device=q.device)
-    if sc is None:
-        sc = torch.empty((B, Hkv, R, NA), dtype=torch.float32, device=q.device)
+    idx, sc = _select_outputs(q, B, Hkv, R, n_sink + n_local + topk, idx, sc)
     need = int(lib.bsa_lsa_select_workspace_bytes(ctypes.byref(p)))
     if ws is None and need > 0:
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
-    NS = index["members"].shape[2]
+    if ws is not None:
+        _need(ws, "ws", dtype=torch.uint8, ndim=1)
     cen, mem, off = (index["centres"], index["members"], index["offsets"]) if NS else (None,) * 3
+    _on_device(q, lm=lm, centres=cen, members=mem, offsets=off, idx=idx, sc=sc, ws=ws)
     _check("bsa_lsa_select",
            lib.bsa_lsa_select(ctypes.byref(p), _ptr(q), _ptr(lm), index["seg_blocks"],
                               index["n_clusters"], _ptr(cen), _ptr(mem), _ptr(off), _ptr(idx),
@@ -438,9 +488,13 @@ def lsa_build_tree(lm: torch.Tensor, index: dict, *, fanout: int = 8) -> dict:
     _need(lm, "lm", ndim=4)
     B, Hkv, NB, D = lm.shape
     seg = index["seg_blocks"]
+    if fanout < 1:
+        raise ValueError("fanout must be >= 1")
+    _check_index(index, B, Hkv, NB, D)
     NS = NB // seg
     seg_c = torch.empty((B, Hkv, NS, D), dtype=torch.float32, device=lm.device)
     grp_c = torch.empty((B, Hkv, NS // fanout, D), dtype=torch.float32, device=lm.device)
+    _on_device(lm)
     p = make_params(B=B, Hq=Hkv, Hkv=Hkv, D=D, seq_q=NB * 64, seq_k=NB * 64, dtype=lm.dtype)
     _check("bsa_lsa_tree_centres",
            lib.bsa_lsa_tree_centres(ctypes.byref(p), _ptr(lm), seg, fanout, _ptr(seg_c),
@@ -460,22 +514,21 @@ def lsa_tree_select(q: torch.Tensor, lm: torch.Tensor, index: dict, *, topk: int
     B, Hq, Tq, D = q.shape
     Hkv = lm.shape[1]
     Tk = Tq if seq_k is None else int(seq_k)
-    if lm.shape != (B, Hkv, _nblocks(Tk), D):
-        raise ValueError(f"lm shape {tuple(lm.shape)} does not match {(B, Hkv, _nblocks(Tk), D)}")
+    _need(lm, "lm", shape=(B, Hkv, _nblocks(Tk), D))
+    NS = _check_index(index, B, Hkv, _nblocks(Tk), D, tree=True)
     p = make_params(B=B, Hq=Hq, Hkv=Hkv, D=D, seq_q=Tq, seq_k=Tk, dtype=q.dtype, topk=topk,
                     n_sink=n_sink, n_local=n_local)
     R = 1 if (Tq == 1 and Tk != 1) else _nblocks(Tq)
-    NA = n_sink + n_local + topk
-    if idx is None:
-        idx = torch.empty((B, Hkv, R, NA), dtype=torch.int32, device=q.device)
-    if sc is None:
-        sc = torch.empty((B, Hkv, R, NA), dtype=torch.float32, device=q.device)
+    idx, sc = _select_outputs(q, B, Hkv, R, n_sink + n_local + topk, idx, sc)
     need = int(lib.bsa_lsa_select_workspace_bytes(ctypes.byref(p)))
     if ws is None and need > 0:
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
-    NS = index["members"].shape[2]
+    if ws is not None:
+        _need(ws, "ws", dtype=torch.uint8, ndim=1)
     tens = [index[k] if NS else None for k in ("centres", "members", "offsets", "seg_centres")]
     grp = index["grp_centres"] if index["grp_centres"].shape[2] else None
+    _on_device(q, lm=lm, centres=tens[0], members=tens[1], offsets=tens[2], seg_centres=tens[3],
+               grp_centres=grp, idx=idx, sc=sc, ws=ws)
     _check("bsa_lsa_tree_select",
            lib.bsa_lsa_tree_select(ctypes.byref(p), _ptr(q), _ptr(lm), index["seg_blocks"],
                                    index["n_clusters"], index["fanout"], beam,
@@ -522,6 +575,11 @@ def _step_outputs(q, B, Hkv, Hq, NA, idx, sc, out, lse, want_lse, mode):
         out = torch.empty_like(q)
     if want_lse and mode != "hils" and lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _need(idx, "idx", dtype=torch.int32, shape=(B, Hkv, 1, NA))
+    _need(sc, "sc", dtype=torch.float32, shape=(B, Hkv, 1, NA))
+    _need(out, "out", dtype=q.dtype, shape=q.shape)
+    if lse is not None:
+        _need(lse, "lse", dtype=torch.float32, shape=(B, Hq))
     return idx, sc, out, lse
 
 
@@ -532,15 +590,14 @@ def decode_step(q, kc, vc, lm, *, topk: int, mode: str = "plain", n_sink: int = 
     [B,Hkv,Tk,D], lm [B,Hkv,NB,D]; returns dict(out, lse, idx, sc) as decode() does."""
     lib = load_library()
     _need(q, "q", ndim=4)
-    _need(kc, "kc", dtype=q.dtype, ndim=4)
-    _need(vc, "vc", dtype=q.dtype, ndim=4)
-    _need(lm, "lm", dtype=q.dtype, ndim=4)
     B, Hq, one, D = q.shape
+    if one != 1:
+        raise ValueError("q must be [B,Hq,1,D]")
+    _need(kc, "kc", dtype=q.dtype, ndim=4)
     Hkv, Tk = kc.shape[1], kc.shape[2]
-    if one != 1 or kc.shape != (B, Hkv, Tk, D) or vc.shape != kc.shape:
-        raise ValueError("q must be [B,Hq,1,D] and kc/vc [B,Hkv,Tk,D]")
-    if lm.shape != (B, Hkv, _nblocks(Tk), D):
-        raise ValueError(f"lm shape {tuple(lm.shape)} does not match the cache")
+    _need(kc, "kc", shape=(B, Hkv, Tk, D))
+    _need(vc, "vc", dtype=q.dtype, shape=(B, Hkv, Tk, D))
+    _need(lm, "lm", dtype=q.dtype, shape=(B, Hkv, _nblocks(Tk), D))
     NA = n_sink + n_local + topk
     idx, sc, out, lse = _step_outputs(q, B, Hkv, Hq, NA, idx, sc, out, lse, want_lse, mode)
     p = make_params(B=B, Hq=Hq, Hkv=Hkv, D=D, seq_q=1, seq_k=Tk, dtype=q.dtype, topk=topk,
@@ -548,6 +605,9 @@ def decode_step(q, kc, vc, lm, *, topk: int, mode: str = "plain", n_sink: int = 
     need = decode_step_workspace_bytes(p)
     if ws is None and need > 0:
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if ws is not None:
+        _need(ws, "ws", dtype=torch.uint8, ndim=1)
+    _on_device(q, kc=kc, vc=vc, lm=lm, idx=idx, sc=sc, out=out, lse=lse, ws=ws)
     _check("bsa_decode_step",
            lib.bsa_decode_step(ctypes.byref(p), _ptr(q), _ptr(kc), _ptr(vc), _ptr(lm), _ptr(idx),
                                _ptr(sc), _ptr(out), _ptr(lse), _ptr(ws),
@@ -562,13 +622,11 @@ def decode_step(q, kc, vc, lm, *, topk: int, mode: str = "plain", n_sink: int = 
 def _paged_shapes(k_pool, page_table, seq_lens):
     _need(k_pool, "k_pool", ndim=4)
     _need(page_table, "page_table", dtype=torch.int32, ndim=2)
-    _need(seq_lens, "seq_lens", dtype=torch.int32, ndim=1)
     n_pages, Hkv, blk, D = k_pool.shape
     if blk != 64:
         raise ValueError("k_pool must be [n_pages,Hkv,64,D]")
     B, NB = page_table.shape
-    if seq_lens.shape != (B,):
-        raise ValueError("seq_lens must be [B] matching page_table [B,NB]")
+    _need(seq_lens, "seq_lens", dtype=torch.int32, shape=(B,))
     return n_pages, Hkv, D, B, NB
 
 
@@ -578,7 +636,8 @@ def pool_landmarks_paged(k_pool, page_table, seq_lens, out=None):
     n_pages, Hkv, D, B, NB = _paged_shapes(k_pool, page_table, seq_lens)
     if out is None:
         out = torch.empty((B, Hkv, NB, D), dtype=k_pool.dtype, device=k_pool.device)
-    _need(out, "lm", dtype=k_pool.dtype, ndim=4)
+    _need(out, "lm", dtype=k_pool.dtype, shape=(B, Hkv, NB, D))
+    _on_device(k_pool, page_table=page_table, seq_lens=seq_lens, lm=out)
     p = make_params(B=B, Hq=Hkv, Hkv=Hkv, D=D, seq_q=NB * 64, seq_k=NB * 64, dtype=k_pool.dtype)
     _check("bsa_pool_landmarks_paged",
            lib.bsa_pool_landmarks_paged(ctypes.byref(p), _ptr(k_pool), int(n_pages),
@@ -593,16 +652,14 @@ def select_topk_paged(q, lm, seq_lens, *, topk: int, n_sink: int = 1, n_local: i
     lib = load_library()
     _need(q, "q", ndim=4)
     _need(lm, "lm", dtype=q.dtype, ndim=4)
-    _need(seq_lens, "seq_lens", dtype=torch.int32, ndim=1)
     B, Hq, one, D = q.shape
     Hkv, NB = lm.shape[1], lm.shape[2]
-    if one != 1 or lm.shape != (B, Hkv, NB, D):
-        raise ValueError("q must be [B,Hq,1,D] and lm [B,Hkv,NB,D]")
-    NA = n_sink + n_local + topk
-    if idx is None:
-        idx = torch.empty((B, Hkv, 1, NA), dtype=torch.int32, device=q.device)
-    if sc is None:
-        sc = torch.empty((B, Hkv, 1, NA), dtype=torch.float32, device=q.device)
+    if one != 1:
+        raise ValueError("q must be [B,Hq,1,D]")
+    _need(lm, "lm", shape=(B, Hkv, NB, D))
+    _need(seq_lens, "seq_lens", dtype=torch.int32, shape=(B,))
+    idx, sc = _select_outputs(q, B, Hkv, 1, n_sink + n_local + topk, idx, sc)
+    _on_device(q, lm=lm, seq_lens=seq_lens, idx=idx, sc=sc)
     p = make_params(B=B, Hq=Hq, Hkv=Hkv, D=D, seq_q=1, seq_k=NB * 64, dtype=q.dtype, topk=topk,
                     n_sink=n_sink, n_local=n_local)
     _check("bsa_select_topk_paged",
@@ -623,24 +680,33 @@ def attend_decode_paged(q, k_pool, v_pool, page_table, seq_lens, idx, sc=None, l
         raise ValueError("v_pool must match k_pool, and both q's dtype")
     _need(idx, "idx", dtype=torch.int32, ndim=4)
     Hq = q.shape[1]
+    _need(q, "q", shape=(B, Hq, 1, D))
     NA = idx.shape[-1]
     if topk is None:
         topk = NA - n_sink - n_local
-    if q.shape != (B, Hq, 1, D) or idx.shape != (B, Hkv, 1, NA) or NA != n_sink + n_local + topk:
-        raise ValueError("q must be [B,Hq,1,D] and idx [B,Hkv,1,NA] matching the call")
+    if NA != n_sink + n_local + topk:
+        raise ValueError(f"idx has {NA} entries per row, the call needs n_sink + n_local + topk")
+    _need(idx, "idx", shape=(B, Hkv, 1, NA))
     if sc is not None:
-        _need(sc, "sc", dtype=torch.float32, ndim=4)
+        _need(sc, "sc", dtype=torch.float32, shape=(B, Hkv, 1, NA))
     if lm is not None:
-        _need(lm, "lm", dtype=q.dtype, ndim=4)
+        _need(lm, "lm", dtype=q.dtype, shape=(B, Hkv, NB, D))
     if out is None:
         out = torch.empty_like(q)
+    _need(out, "out", dtype=q.dtype, shape=q.shape)
     if want_lse and lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", dtype=torch.float32, shape=(B, Hq))
     p = make_params(B=B, Hq=Hq, Hkv=Hkv, D=D, seq_q=1, seq_k=NB * 64, dtype=q.dtype, topk=topk,
                     n_sink=n_sink, n_local=n_local, scale=scale, mode=mode)
     need = decode_workspace_bytes(p)
     if ws is None and need > 0:
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if ws is not None:
+        _need(ws, "ws", dtype=torch.uint8, ndim=1)
+    _on_device(q, k_pool=k_pool, v_pool=v_pool, page_table=page_table, seq_lens=seq_lens,
+               idx=idx, sc=sc, lm=lm, out=out, lse=lse, ws=ws)
     _check("bsa_attend_decode_paged",
            lib.bsa_attend_decode_paged(ctypes.byref(p), _ptr(q), _ptr(k_pool), _ptr(v_pool),
                                        int(n_pages), _ptr(page_table), _ptr(seq_lens), _ptr(lm),
@@ -660,10 +726,9 @@ def decode_step_paged(q, k_pool, v_pool, page_table, seq_lens, lm, *, topk: int,
     _need(v_pool, "v_pool", dtype=k_pool.dtype, ndim=4)
     if v_pool.shape != k_pool.shape or k_pool.dtype != q.dtype:
         raise ValueError("v_pool must match k_pool, and both q's dtype")
-    _need(lm, "lm", dtype=q.dtype, ndim=4)
     Hq = q.shape[1]
-    if q.shape != (B, Hq, 1, D) or lm.shape != (B, Hkv, NB, D):
-        raise ValueError("q must be [B,Hq,1,D] and lm [B,Hkv,NB,D]")
+    _need(q, "q", shape=(B, Hq, 1, D))
+    _need(lm, "lm", dtype=q.dtype, shape=(B, Hkv, NB, D))
     NA = n_sink + n_local + topk
     idx, sc, out, lse = _step_outputs(q, B, Hkv, Hq, NA, idx, sc, out, lse, want_lse, mode)
     p = make_params(B=B, Hq=Hq, Hkv=Hkv, D=D, seq_q=1, seq_k=NB * 64, dtype=q.dtype, topk=topk,
@@ -671,6 +736,10 @@ def decode_step_paged(q, k_pool, v_pool, page_table, seq_lens, lm, *, topk: int,
     need = decode_step_workspace_bytes(p)
     if ws is None and need > 0:
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if ws is not None:
+        _need(ws, "ws", dtype=torch.uint8, ndim=1)
+    _on_device(q, k_pool=k_pool, v_pool=v_pool, page_table=page_table, seq_lens=seq_lens, lm=lm,
+               idx=idx, sc=sc, out=out, lse=lse, ws=ws)
     _check("bsa_decode_step_paged",
            lib.bsa_decode_step_paged(ctypes.byref(p), _ptr(q), _ptr(k_pool), _ptr(v_pool),
                                      int(n_pages), _ptr(page_table), _ptr(seq_lens), _ptr(lm),

@@ -8,6 +8,7 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -39,9 +40,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found; the ROCm toolchain is required to build libbsa.so")
 
 
-def _compile(sources, out: str, verbose: bool) -> None:
-    tmp = out + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *[os.path.join(CSRC, s) for s in sources], "-o", tmp]
+def _run(cmd, verbose: bool) -> None:
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -51,6 +50,30 @@ def _compile(sources, out: str, verbose: bool) -> None:
         raise RuntimeError("hipcc failed:\n" + "\n".join(errs))
     if verbose and errs:
         print("\n".join(errs), file=sys.stderr)
+
+
+def _jobs() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def _compile(sources, out: str, verbose: bool, defines=()) -> None:
+    """Compile each source to an object file in parallel (each carries its own gfx950 code
+    object), then link them into one shared library."""
+    tag = os.path.splitext(os.path.basename(out))[0]
+    objdir = os.path.join(PKG, "_build", tag)
+    os.makedirs(objdir, exist_ok=True)
+    flags = [f for f in HIPCC_FLAGS if f != "-shared"] + [f"-D{d}" for d in defines]
+    objs = [os.path.join(objdir, os.path.splitext(s)[0] + ".o") for s in sources]
+    cmds = [[hipcc(), *flags, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(sources, objs)]
+    with ThreadPoolExecutor(max_workers=_jobs()) as ex:
+        for f in [ex.submit(_run, c, verbose) for c in cmds]:
+            f.result()
+    tmp = out + ".tmp"
+    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, out)
 
 

@@ -349,11 +349,16 @@ __global__ __launch_bounds__(HPW * 128) void attend_prefill_bf16_kernel(
 // phase one wave of each SIMD multiplies while the other exponentiates, and the SIMD overlaps the
 // two instead of alternating between them.  A barrier separates phases.
 //
-// LDS holds two staging units; unit a = {K of entry a, V of entry a-1} is read in phases 2a and
-// 2a+1 and copied straight from memory into LDS (global_load_lds, 1 KB per instruction, no
-// register round trip) during phases 2a-2 and 2a-1, the copies of all eight waves sharing the
-// 32 KB.  16-byte chunks are XOR-swizzled per row so the K fragment reads and the transposed V
-// reads are free of bank conflicts.
+// LDS holds kPpUnits (4) staging units of 32 KB; unit a = {K of entry a, V of entry a-1} is read
+// in phases 2a and 2a+1.  It is copied straight from memory into LDS (global_load_lds, 1 KB per
+// instruction, no register round trip) AHEAD = kPpUnits - 1 = 3 units in advance: during phases
+// 2a-6 and 2a-5, into the buffer of unit a-4, which was read for the last time in phase 2a-7.
+// So units a+1, a+2 and a+3 may be in flight while unit a is read.  Every wave issues exactly
+// SPW copy instructions per unit (half in each of the two phases), and the waits before a
+// barrier count those instructions (vmcnt = SPW or 2*SPW left in flight): both numbers, the
+// unit count and the even split, are what wait_units relies on.  16-byte chunks are
+// XOR-swizzled per row so the K fragment reads and the transposed V reads are free of bank
+// conflicts.
 template <int D, int MODE>
 __global__ __launch_bounds__(512) void attend_prefill_pp_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
@@ -456,26 +461,25 @@ __global__ __launch_bounds__(512) void attend_prefill_pp_kernel(
   // This wave's part of unit a: SPW copies of 1 KB (K slab, V slab, K slab, ...), issued in two
   // halves: copies x with x % 2 == h for half h (K slabs, then V slabs).
   const uint32_t u_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16*)&U[0][0];
-  // entries 0..63, one per lane: byte offset of the block a copy reads (the entry's block, or
-  // the current block for an invalid entry) and that block's last row inside the sequence
+  // entries 0..63, one per lane: the block a copy reads (the entry's block, or the current
+  // block for an invalid entry) and that block's last row inside the sequence.  The block's
+  // byte offset is formed in 64 bits from the wave-uniform index (a 32-bit offset would wrap
+  // past 2^32 bytes of one head's K or V).
   const int jcp = (jvec >= 0 && jvec <= c) ? jvec : c;
-  const uint32_t cp_off = (uint32_t)jcp * (uint32_t)(kBlock * D * 2);
   const int cp_lim = T - 1 - jcp * kBlock;
   auto copy_half = [&](int a, int hv) {
     const uint32_t dst = u_lds + (uint32_t)(a % kPpUnits) * (2 * TILE * 2);
     const int ae = hv == 0 ? min(a, nval - 1) : max(a - 1, 0);
-    uint32_t off;
-    int lim;
+    int j, lim;
     if (ae < kWave) {
-      off = (uint32_t)__builtin_amdgcn_readlane((int)cp_off, ae);
+      j = __builtin_amdgcn_readlane(jcp, ae);
       lim = __builtin_amdgcn_readlane(cp_lim, ae);
     } else {
-      int j = entry(ae);
+      j = entry(ae);
       j = j < 0 ? c : j;
-      off = (uint32_t)j * (uint32_t)(kBlock * D * 2);
       lim = T - 1 - j * kBlock;
     }
-    const char* blk = (hv == 0 ? kb : vb) + off;
+    const char* blk = (hv == 0 ? kb : vb) + (size_t)j * (size_t)(kBlock * D * 2);
 #pragma unroll
     for (int i = 0; i < SPW / 2; ++i) {
       const int sl = w + 8 * i;

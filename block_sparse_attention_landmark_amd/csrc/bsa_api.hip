@@ -592,4 +592,15 @@ bsa_status_t bsa_decode_step_paged(const bsa_params_t* params, const void* q,
                     "decode_step_paged");
 }
 
+size_t bsa_workspace_bytes(const bsa_params_t* params, int which) {
+  switch (which) {
+    case BSA_WS_SELECT: return bsa_select_workspace_bytes(params);
+    case BSA_WS_DECODE: return bsa_decode_workspace_bytes(params);
+    case BSA_WS_DECODE_STEP: return bsa_decode_step_workspace_bytes(params);
+    case BSA_WS_BACKWARD: return bsa_backward_workspace_bytes(params);
+    case BSA_WS_LSA_SELECT: return bsa_lsa_select_workspace_bytes(params);
+    default: return 0;
+  }
+}
+
 }  // extern "C"

@@ -78,7 +78,9 @@ typedef struct bsa_params {
 } bsa_params_t;
 
 /*
- * Landmarks: lm[b,g,j,:] = mean of k[b,g,t,:] over the tokens t of block j (a partial last
+ * Landmarks (LSA page, "The index stops scanning the whole context", paragraph 3: neighbouring
+ * keys are pooled before indexing; HiLS page, summary paragraph 2: per-chunk landmarks).
+ * lm[b,g,j,:] = mean of k[b,g,t,:] over the tokens t of block j (a partial last
  * block averages the tokens present), accumulated in float64 and rounded once, to nearest
  * even, to the dtype.
  *   k  [B,Hkv,Tk,D] (input)      lm [B,Hkv,NB,D] (output)
@@ -90,7 +92,11 @@ bsa_status_t bsa_pool_landmarks(const bsa_params_t* params, const void* k, void*
 size_t bsa_select_workspace_bytes(const bsa_params_t* params);
 
 /*
- * Selection.  Selector vector qbar = sum over the query heads of each kv group of the mean
+ * Selection (SAS page, summary paragraph 1 and "How to apply": a light selector scores the
+ * units of context and inference keeps the hard top-K; LSA page, first section, paragraphs 2
+ * and 4: each contiguous block is scored, the start of the context and a recent window are
+ * always attended; SAS page, summary paragraph 3: the current block is always kept).
+ * Selector vector qbar = sum over the query heads of each kv group of the mean
  * query of each 64-token query block (decode: of the one query token), kept in float32.
  * Scores S[c][j] = qbar_c . L_j for j <= c (no softmax scale).  Candidates are the blocks
  * n_sink <= j <= c - n_local; the K = min(topk, #candidates) highest scores are chosen, the
@@ -108,7 +114,11 @@ bsa_status_t bsa_select_topk(const bsa_params_t* params, const void* q, const vo
                              int32_t* idx, float* sc, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * Prefill attention (seq_q == seq_k == T).  For query token t of head h in block c = t/64 and
+ * Prefill attention (SAS page, summary paragraph 4: blockwise, FlashAttention-style, without
+ * the full square matrix; summary paragraph 3 and "Key facts" item 3: the SAS gate sits inside
+ * the softmax in log form, normalised against the current block; HiLS page, summary paragraph
+ * 2: per-chunk attention merged by the chunks' retrieval scores).
+ * seq_q == seq_k == T.  For query token t of head h in block c = t/64 and
  * the attended set A_c = row c of idx (entries must be ascending, <= c, end with c and be
  * followed only by -1 padding):
  *   PLAIN: o = sum_u softmax_u(scale * q.k_u) v_u over keys u in the blocks of A_c, u <= t;
@@ -128,7 +138,10 @@ bsa_status_t bsa_attend_prefill(const bsa_params_t* params, const void* q, const
 size_t bsa_decode_workspace_bytes(const bsa_params_t* params);
 
 /*
- * Decode attention (seq_q == 1): the query of each sequence is the token at position Tk - 1
+ * Decode attention (LSA page, "The index stops scanning the whole context", paragraph 1: per
+ * generated token the work is the attention over the selected blocks only; the passages of
+ * bsa_attend_prefill define the three modes).
+ * seq_q == 1: the query of each sequence is the token at position Tk - 1
  * and sees every key of its attended blocks; same PLAIN / SAS / HILS rules as prefill.  The
  * attended blocks are split over workgroups and the partial softmax states merged through
  * their log-sum-exp.
@@ -341,6 +354,23 @@ bsa_status_t bsa_attend_prefill_backward(const bsa_params_t* params, const void*
                                          const float* lse, const void* dout, void* dq, void* dk,
                                          void* dv, float* dsc, float* dlm, void* ws,
                                          size_t ws_bytes, void* stream);
+
+/*
+ * One query for every call that takes a workspace: which = BSA_WS_SELECT (bsa_select_topk),
+ * BSA_WS_DECODE (bsa_attend_decode, bsa_attend_decode_paged), BSA_WS_DECODE_STEP
+ * (bsa_decode_step, bsa_decode_step_paged), BSA_WS_BACKWARD (bsa_attend_prefill_backward) or
+ * BSA_WS_LSA_SELECT (bsa_lsa_select, bsa_lsa_tree_select).  Returns the same number as that
+ * call's own *_workspace_bytes function: 0 when the params are rejected, when `which` is
+ * unknown, or when the call needs no workspace for these params.
+ */
+typedef enum bsa_workspace_call {
+  BSA_WS_SELECT = 0,
+  BSA_WS_DECODE = 1,
+  BSA_WS_DECODE_STEP = 2,
+  BSA_WS_BACKWARD = 3,
+  BSA_WS_LSA_SELECT = 4
+} bsa_workspace_call_t;
+size_t bsa_workspace_bytes(const bsa_params_t* params, int which);
 
 /* Static description of a status code. */
 const char* bsa_status_string(int status);

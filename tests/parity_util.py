@@ -35,17 +35,25 @@ def host64(t: torch.Tensor) -> np.ndarray:
         else t.detach().cpu().numpy()
 
 
-def check_selection(gpu_row, s_row, c, topk, n_sink=1, n_local=2, where=""):
+def check_selection(gpu_row, s_row, c, topk, n_sink=1, n_local=2, where="", stats=None):
     """gpu_row: the device's attended set (int list, -1 padded).  s_row: oracle scores [NB].
 
-    Returns the device's attended set as an int64 array (valid entries only).
+    Returns the device's attended set as an int64 array (valid entries only).  With a `stats`
+    dict, counts the rows compared ("rows") and those that differ from the oracle's set only
+    inside the near-tie band ("excused").
     """
-    A_dev = np.array([j for j in gpu_row if j >= 0], dtype=np.int64)
+    gpu_row = np.asarray(gpu_row)
+    A_dev = gpu_row[gpu_row >= 0].astype(np.int64)
     A_ref, _ = O.select_row(s_row, c, topk, n_sink, n_local)
+    assert np.all(gpu_row[A_dev.size:] == -1), f"{where}: padding is not -1 after the valid prefix"
     assert np.all(np.diff(A_dev) > 0), f"{where}: attended set not ascending: {A_dev}"
     assert A_dev.size == A_ref.size, f"{where}: size {A_dev.size} != {A_ref.size}"
+    if stats is not None:
+        stats["rows"] = stats.get("rows", 0) + 1
     if np.array_equal(A_dev, A_ref):
         return A_dev
+    if stats is not None:
+        stats["excused"] = stats.get("excused", 0) + 1
     diff = np.setxor1d(A_dev, A_ref)
     cand = np.arange(n_sink, c - n_local + 1)
     order = np.lexsort((cand, -s_row[cand]))

@@ -142,6 +142,24 @@ def test_workspace_sizes_follow_the_shapes(lib):
     assert lib.bsa_decode_workspace_bytes(ctypes.byref(f)) == 0
 
 
+def test_unified_workspace_query_matches_each_call(lib):
+    """bsa_workspace_bytes(params, which) returns each call's own workspace figure."""
+    shapes = [_p(B=2, Hq=8, Hkv=2, seq_q=64 * 10, seq_k=64 * 10),
+              _p(B=3, Hq=16, Hkv=2, seq_q=1, seq_k=64 * 9 + 5, topk=4),
+              _p(B=32, Hq=64, Hkv=8, seq_q=1, seq_k=131072, topk=64),
+              _p(B=1, Hq=4, Hkv=1, seq_q=4096, seq_k=4096, topk=8, mode="sas"),
+              _p(D=80)]
+    own = [lib.bsa_select_workspace_bytes, lib.bsa_decode_workspace_bytes,
+           lib.bsa_decode_step_workspace_bytes, lib.bsa_backward_workspace_bytes,
+           lib.bsa_lsa_select_workspace_bytes]
+    for p in shapes:
+        for which, fn in enumerate(own):
+            assert lib.bsa_workspace_bytes(ctypes.byref(p), which) == fn(ctypes.byref(p))
+        assert lib.bsa_workspace_bytes(ctypes.byref(p), 5) == 0
+        assert lib.bsa_workspace_bytes(ctypes.byref(p), -1) == 0
+    assert lib.bsa_workspace_bytes(ctypes.byref(shapes[0]), 0) > 0
+
+
 def test_attend_validation(lib):
     def pre(p, **kw):
         a = dict(q=FAKE, k=FAKE, v=FAKE, lm=None, idx=FAKE, sc=None, out=FAKE, lse=None)

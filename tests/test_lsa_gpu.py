@@ -139,6 +139,37 @@ def _check_lsa_row(A_dev, qbar, L64, ref_index, c, K, ns, nl, seg, where):
     return np.array([unit_of[int(j)] if int(j) in unit_of else float(qbar @ L64[j]) for j in A_dev])
 
 
+@pytest.mark.parametrize("n_clusters", [16, 4, 1])
+def test_lsa_ward_tie_rule_on_device(n_clusters):
+    """Landmarks on a line at the integer positions 0..63 of each segment, in a seeded order:
+    neighbouring blocks tie exactly, every cluster stays an interval whose mean is a
+    half-integer (exact in float32), and costs that differ do so by more than 2 % -- so float32
+    rounding cannot reorder merges, and the device's merge sequence must equal the oracle's
+    exactly: among equal costs, the smallest pair of ids first."""
+    B, Hkv, D, seg = 1, 2, 64, 64
+    NS = 2
+    T = NS * seg * 64
+    r = np.random.default_rng(31)
+    pos = np.stack([np.stack([r.permutation(seg) for _ in range(NS)]) for _ in range(Hkv)])
+    k = torch.zeros((B, Hkv, T, D), dtype=torch.float32)
+    blk_pos = torch.from_numpy(pos.reshape(Hkv, NS * seg).astype(np.float32))    # [Hkv, NB]
+    k[0, :, :, 0] = blk_pos.repeat_interleave(64, dim=1)
+    k = k.to(torch.bfloat16).cuda()
+    lm = bsa.pool_landmarks(k)
+    index = bsa.lsa_build_index(lm, seg_blocks=seg, n_clusters=n_clusters)
+    torch.cuda.synchronize()
+    for g in range(Hkv):
+        L64 = host64(lm[0, g])
+        assert np.array_equal(L64[:, 0], pos[g].reshape(-1)), "landmarks are not the grid"
+        mrg = index["merges"][0, g].cpu().numpy()
+        for s_ in range(NS):
+            lo = s_ * seg
+            ref_members, ref_merges = O.ward_clusters(L64[lo:lo + seg], n_clusters)
+            got = [tuple(int(x) - lo for x in m) for m in mrg[s_]]
+            assert got == [tuple(m) for m in ref_merges], \
+                f"g{g} seg{s_}: device merges differ from the oracle's tie rule"
+
+
 LSA_SMALL = [
     # id,          B, Hq, Hkv, T,            D,   topk, seg, nc, data
     ("seg16",      1, 4,  1,   64 * 50 + 9,  128, 6,    16,  4,  "clustered"),

@@ -801,6 +801,81 @@ def test_ward_merges_are_greedy_minimal_sse_increases():
         clusters[a] = clusters[a] + clusters.pop(b)
 
 
+def _ward_brute_force_exact(points, n_clusters):
+    """Ward agglomeration by brute force in exact rational arithmetic: at every step each pair
+    of current clusters is tried, its merge cost is the increase of the total within-cluster
+    sum of squares computed from the member points themselves (no running means), and the
+    cheapest pair is merged; among pairs of exactly equal cost, the one with the smallest
+    (lowest member of the first, lowest member of the second) is merged.  Integer points, so
+    every cost is an exact Fraction and ties are decided exactly."""
+    from fractions import Fraction
+    pts = [[Fraction(int(x)) for x in row] for row in points]
+
+    def sse(members):
+        n = len(members)
+        dims = len(pts[0])
+        mean = [sum(pts[i][d] for i in members) / n for d in range(dims)]
+        return sum((pts[i][d] - mean[d]) ** 2 for i in members for d in range(dims))
+
+    clusters = {i: [i] for i in range(len(pts))}
+    merges = []
+    while len(clusters) > n_clusters:
+        best = None
+        ids = sorted(clusters)
+        for x_i, x in enumerate(ids):
+            for y in ids[x_i + 1:]:
+                cost = sse(clusters[x] + clusters[y]) - sse(clusters[x]) - sse(clusters[y])
+                key = (cost, x, y)
+                if best is None or key < best:
+                    best = key
+        _, a, b = best
+        clusters[a] = sorted(clusters[a] + clusters.pop(b))
+        merges.append((a, b))
+    return [clusters[i] for i in sorted(clusters)], merges
+
+
+def test_ward_tie_rule_closed_form_on_a_line():
+    """Eight points at 0..7 on a line: every neighbouring pair costs 1/2, so the first merges
+    are all ties and the smallest pair of ids goes first -- (0,1), (2,3), (4,5), (6,7) -- and
+    then the pairs of pairs (cost 4 each) -- (0,2), (4,6).  Taking the last or the largest
+    equal pair instead starts with (6,7)."""
+    X = np.arange(8, dtype=np.float64)[:, None]
+    members, merges = O.ward_clusters(X, 4)
+    assert merges == [(0, 1), (2, 3), (4, 5), (6, 7)]
+    assert [m.tolist() for m in members] == [[0, 1], [2, 3], [4, 5], [6, 7]]
+    members, merges = O.ward_clusters(X, 2)
+    assert merges == [(0, 1), (2, 3), (4, 5), (6, 7), (0, 2), (4, 6)]
+    assert [m.tolist() for m in members] == [[0, 1, 2, 3], [4, 5, 6, 7]]
+
+
+def test_ward_tie_rule_follows_ids_not_positions():
+    """Rows at positions 3, 0, 2, 1: the pairs of neighbours (rows 0,2), (1,3), (2,3) all cost
+    1/2; the smallest pair of ids is (0,2) (positions 3 and 2), not the leftmost pair of
+    positions (rows 1 and 3), which then merge second."""
+    X = np.array([[3.0], [0.0], [2.0], [1.0]])
+    members, merges = O.ward_clusters(X, 2)
+    assert merges == [(0, 2), (1, 3)]
+    assert [m.tolist() for m in members] == [[0, 2], [1, 3]]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_ward_tie_rule_matches_exact_brute_force_on_grids(seed):
+    """Points of a small integer grid (many exactly equal costs), rows in a seeded order: the
+    oracle's merges equal those of the exact rational brute force for every cluster count."""
+    r = _rng(900 + seed)
+    if seed % 2 == 0:
+        grid = np.array([[x, y] for x in range(4) for y in range(3)], dtype=np.float64)
+    else:
+        grid = np.array([[x] for x in range(10)], dtype=np.float64) * 2.0
+    X = grid[r.permutation(grid.shape[0])]
+    n = X.shape[0]
+    for k in (1, 2, n // 3, n // 2, n - 1):
+        members, merges = O.ward_clusters(X, k)
+        ref_members, ref_merges = _ward_brute_force_exact(X, k)
+        assert merges == ref_merges, (k, merges, ref_merges)
+        assert [m.tolist() for m in members] == ref_members
+
+
 def test_lsa_index_partitions_segments_and_centres_are_means():
     r = _rng(54)
     L = r.standard_normal((64 * 3 + 10, 6))

@@ -117,6 +117,55 @@ def _check_decode_pairs(q, kc, vc, res, lm_dev, pairs, *, mode, dtype, topk, n_s
     return worst
 
 
+def _check_all_sets_prefill(q, k, res, *, topk, n_sink, n_local, dtype, tag, groups=None):
+    """Every selection row of a prefill call (or of the listed (b, g) groups): the device's
+    attended sets against the oracle's selection on the oracle's own landmarks and selector
+    vectors, and every group's landmarks bit for bit.  Prints the rows excused as near ties."""
+    B, Hq, T, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    NQB = (T + 63) // 64
+    idx = res["idx"].cpu().numpy()
+    stats = {}
+    groups = [(b, g) for b in range(B) for g in range(Hkv)] if groups is None else groups
+    for (b, g) in groups:
+        lm_ref = O.landmarks(host64(k[b, g])[None, None], dtype)[0, 0]
+        check_landmarks(host64(res["lm"][b, g]), lm_ref, dtype, f"{tag} lm b{b} g{g}")
+        qbar = O.selector_vectors(host64(q[b, g * G:(g + 1) * G])[None], 1)[0, 0]   # [NQB, D]
+        S = O.block_scores(qbar, lm_ref)                                             # [NQB, NB]
+        del qbar
+        for c in range(NQB):
+            check_selection(idx[b, g, c], S[c], c, topk, n_sink, n_local,
+                            f"{tag} b{b} g{g} c{c}", stats)
+    _print(f"{tag}: attended sets of {stats.get('rows', 0)} rows checked, "
+           f"{stats.get('excused', 0)} differ only inside the near-tie band")
+    return stats
+
+
+def _check_all_sets_decode(q4, kc, lm_dev, results, *, topk, n_sink, n_local, dtype, tag):
+    """Every (sequence, kv head) of a decode batch: the attended sets of each result in
+    `results` (name -> result dict) against the oracle's selection, and every landmark row."""
+    B, Hq, _, D = q4.shape
+    Hkv, Tk = kc.shape[1], kc.shape[2]
+    G = Hq // Hkv
+    c = (Tk - 1) // 64
+    idx = {n: r["idx"].cpu().numpy() for n, r in results.items()}
+    stats = {n: {} for n in results}
+    for b in range(B):
+        qb = O.decode_selector_vectors(host64(q4[b:b + 1, :, 0]), Hkv)[0]             # [Hkv, D]
+        for g in range(Hkv):
+            lm_ref = O.landmarks(host64(kc[b, g])[None, None], dtype)[0, 0]
+            check_landmarks(host64(lm_dev[b, g]), lm_ref, dtype, f"{tag} lm b{b} g{g}")
+            s_row = O.block_scores(qb[g][None], lm_ref)[0]
+            for n in results:
+                check_selection(idx[n][b, g, 0], s_row, c, topk, n_sink, n_local,
+                                f"{tag} {n} b{b} g{g}", stats[n])
+    for n in results:
+        _print(f"{tag} ({n}): attended sets of {stats[n].get('rows', 0)} pairs checked, "
+               f"{stats[n].get('excused', 0)} differ only inside the near-tie band")
+    return stats
+
+
 # ---------------------------------------------------------------------------------------------
 # small shapes, every element
 # ---------------------------------------------------------------------------------------------
@@ -474,7 +523,9 @@ def _sample_rows(rng, B, Hkv, NQB, n):
     return sorted(rows)
 
 
-def _workload_prefill(name, n_rows, max_groups=None):
+def _workload_prefill(name, n_rows, max_groups=None, all_sets=None):
+    """The workload in the benchmark's launch configuration.  Attended sets: every row of the
+    groups in `all_sets` ("all" = every group); outputs: n_rows sampled rows (None = all)."""
     w = synth.WORKLOADS[name]
     B, Hq, Hkv, T, D = w["B"], w["Hq"], w["Hkv"], w["T"], w["D"]
     _print(f"workload {name}: generating")
@@ -484,6 +535,9 @@ def _workload_prefill(name, n_rows, max_groups=None):
     res = bsa.prefill(q, k, v, topk=w["topk"], mode=w["mode"], want_lse=(w["mode"] != "hils"))
     torch.cuda.synchronize()
     NQB = (T + 63) // 64
+    if all_sets is not None:
+        _check_all_sets_prefill(q, k, res, topk=w["topk"], n_sink=1, n_local=2, dtype=w["dtype"],
+                                tag=name, groups=None if all_sets == "all" else all_sets)
     rng = np.random.default_rng(1234)
     if n_rows is None:
         rows = [(b, g, c) for b in range(B) for g in range(Hkv) for c in range(NQB)]
@@ -492,7 +546,7 @@ def _workload_prefill(name, n_rows, max_groups=None):
         if max_groups is not None:
             keep = sorted({(b, g) for b, g, _ in rows})[:max_groups]
             rows = [r for r in rows if (r[0], r[1]) in keep]
-    _print(f"workload {name}: checking {len(rows)} rows")
+    _print(f"workload {name}: checking the outputs of {len(rows)} rows")
     worst = _check_prefill_rows(q, k, v, res, rows, mode=w["mode"], dtype=w["dtype"],
                                 topk=w["topk"], n_sink=1, n_local=2, tag=name)
     _print(f"workload {name}: worst max-abs {worst[0]:.3e} mean-rel {worst[1]:.3e}")
@@ -505,19 +559,26 @@ def test_workload_tiny_f32_4k_full():
     _workload_prefill("tiny_f32_4k", None)
 
 
-def test_workload_gqa_bf16_32k_sampled():
-    _workload_prefill("gqa_bf16_32k", 40)
+def test_workload_gqa_bf16_32k():
+    """Every row's attended set (8 groups x 512 query blocks); 40 sampled rows' outputs."""
+    _workload_prefill("gqa_bf16_32k", 40, all_sets="all")
 
 
-def test_workload_sas_bf16_128k_sampled():
-    _workload_prefill("sas_bf16_128k", 24, max_groups=4)
+def test_workload_sas_bf16_128k():
+    """Every row's attended set (8 groups x 2048 query blocks); outputs of 24 sampled rows
+    in at most 4 groups (the oracle's attention is the slow part)."""
+    _workload_prefill("sas_bf16_128k", 24, max_groups=4, all_sets="all")
 
 
-def test_workload_hils_bf16_1m_sampled():
-    _workload_prefill("hils_bf16_1m", 10, max_groups=2)
+def test_workload_hils_bf16_1m():
+    """Every row's attended set of the first and the last kv group (2 x 16384 query blocks,
+    rows of up to 16381 candidates); outputs of 10 sampled rows in 2 groups."""
+    _workload_prefill("hils_bf16_1m", 10, max_groups=2, all_sets=[(0, 0), (0, 7)])
 
 
-def test_workload_decode_bf16_32x128k_sampled():
+def test_workload_decode_bf16_32x128k():
+    """All 256 (sequence, kv head) pairs' attended sets on both decode paths against the
+    oracle's selection; outputs of 6 sampled pairs per path."""
     w = synth.WORKLOADS["decode_bf16_32x128k"]
     B, Hq, Hkv, Tk, D = w["B"], w["Hq"], w["Hkv"], w["T"], w["D"]
     _print("workload decode: generating")
@@ -530,16 +591,83 @@ def test_workload_decode_bf16_32x128k_sampled():
                    {(int(rng.integers(B)), int(rng.integers(Hkv))) for _ in range(4)})
     # the two calls (selection kernel, attention kernel) and the one-launch step that bench.py
     # times (selection and attention fused in one kernel per (sequence, kv head))
+    results = {}
     for name, run in (("two calls", bsa.decode), ("one-launch step", bsa.decode_step)):
-        res = run(q4, kc, vc, lm, topk=w["topk"], mode=w["mode"], want_lse=True)
-        torch.cuda.synchronize()
-        _print(f"workload decode ({name}): checking {pairs}")
+        results[name] = run(q4, kc, vc, lm, topk=w["topk"], mode=w["mode"], want_lse=True)
+    torch.cuda.synchronize()
+    _check_all_sets_decode(q4, kc, lm, results, topk=w["topk"], n_sink=1, n_local=2,
+                           dtype=w["dtype"], tag="workload decode")
+    for name, res in results.items():
+        _print(f"workload decode ({name}): checking the outputs of {pairs}")
         worst = _check_decode_pairs(q4, kc, vc, res, lm, pairs, mode=w["mode"], dtype=w["dtype"],
                                     topk=w["topk"], n_sink=1, n_local=2, tag=f"decode {name}")
         _print(f"workload decode ({name}): worst max-abs {worst[0]:.3e} mean-rel {worst[1]:.3e}")
-    del q, kc, vc, lm, res
+    del q, kc, vc, lm, results
     gc.collect()
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------------------------
+# top-K row lengths past the register-held keys: a workgroup of NT threads keeps up to 8 keys
+# per thread in registers; longer rows are ranked from keys cached in LDS
+# ---------------------------------------------------------------------------------------------
+
+def test_topk_prefill_rows_of_2049_to_4096_candidates():
+    """Prefill with 3000 key blocks: rows c >= 2051 have 2049..2997 candidates, past the 2048
+    keys the 256-thread top-K holds in registers.  Every row's set against the oracle and the
+    outputs of sampled long rows."""
+    B, Hq, Hkv, T, D, topk = 1, 4, 1, 64 * 3000 + 17, 64, 40
+    q, k, v = synth.make_prefill(B, Hq, Hkv, T, D, "bf16", "clustered", seed=21, device="cuda",
+                                 n_centres=64, n_aim=8)
+    res = bsa.prefill(q, k, v, topk=topk, mode="sas", want_lse=True)
+    torch.cuda.synchronize()
+    _check_all_sets_prefill(q, k, res, topk=topk, n_sink=1, n_local=2, dtype="bf16",
+                            tag="prefill 3000 blocks")
+    rows = [(0, 0, c) for c in (2050, 2051, 2052, 2600, 3000)]
+    _check_prefill_rows(q, k, v, res, rows, mode="sas", dtype="bf16", topk=topk, n_sink=1,
+                        n_local=2, tag="prefill 3000 blocks")
+
+
+def test_topk_fused_decode_rows_of_2049_to_4096_candidates():
+    """The one-launch decode step (256 pairs, so the fused kernel) with 3001 blocks per cache:
+    2998 candidates per row, past the 2048 keys its 256-thread top-K holds in registers."""
+    B, Hq, Hkv, Tk, D, topk = 32, 32, 8, 64 * 3000 + 5, 64, 48
+    q, kc, vc = synth.make_decode(B, Hq, Hkv, Tk, D, "bf16", "clustered", seed=22, device="cuda",
+                                  n_centres=64, n_aim=8)
+    q4 = q[:, :, None, :].contiguous()
+    lm = bsa.pool_landmarks(kc)
+    results = {"one-launch step": bsa.decode_step(q4, kc, vc, lm, topk=topk, mode="sas",
+                                                  want_lse=True),
+               "two calls": bsa.decode(q4, kc, vc, lm, topk=topk, mode="sas", want_lse=True)}
+    torch.cuda.synchronize()
+    _check_all_sets_decode(q4, kc, lm, results, topk=topk, n_sink=1, n_local=2, dtype="bf16",
+                           tag="decode 3001 blocks")
+    for name, res in results.items():
+        _check_decode_pairs(q4, kc, vc, res, lm, [(0, 0), (17, 3), (31, 7)], mode="sas",
+                            dtype="bf16", topk=topk, n_sink=1, n_local=2,
+                            tag=f"decode 3001 blocks {name}")
+    del q, kc, vc, lm, results
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def test_topk_decode_selection_rows_of_8193_to_16384_candidates():
+    """The one-kernel decode selection (1024 threads) with 12001 blocks: 11998 candidates,
+    past the 8192 keys it holds in registers; both decode paths (few pairs: the step launches
+    the same selection kernel and the split attention)."""
+    B, Hq, Hkv, Tk, D, topk = 2, 4, 1, 64 * 12000 + 3, 64, 64
+    q, kc, vc = synth.make_decode(B, Hq, Hkv, Tk, D, "bf16", "clustered", seed=23, device="cuda",
+                                  n_centres=256, n_aim=8)
+    q4 = q[:, :, None, :].contiguous()
+    lm = bsa.pool_landmarks(kc)
+    results = {"two calls": bsa.decode(q4, kc, vc, lm, topk=topk, mode="sas", want_lse=True),
+               "step": bsa.decode_step(q4, kc, vc, lm, topk=topk, mode="sas", want_lse=True)}
+    torch.cuda.synchronize()
+    _check_all_sets_decode(q4, kc, lm, results, topk=topk, n_sink=1, n_local=2, dtype="bf16",
+                           tag="decode 12001 blocks")
+    for name, res in results.items():
+        _check_decode_pairs(q4, kc, vc, res, lm, [(0, 0), (1, 0)], mode="sas", dtype="bf16",
+                            topk=topk, n_sink=1, n_local=2, tag=f"decode 12001 blocks {name}")
 
 
 def test_decode_beyond_fused_selection():
