@@ -310,8 +310,9 @@ def bench_lsa(torch, bsa, synth, name, tensors, steps, warmup, seg_blocks=64, n_
                 bsa.lsa_select(q, lm, index, topk=K, ws=ws, idx=idx, sc=sc)
         timed("build", build)
         timed("select", select)
-        timed("attend", lambda: bsa.attend_prefill(q, k, v, idx, sc, None, mode=mode, topk=K,
-                                                   out=out))
+        timed("attend", lambda: bsa.attend_prefill(q, k, v, idx, sc,
+                                                   lm if mode == "hils" else None, mode=mode,
+                                                   topk=K, out=out))
 
     for _ in range(warmup):
         step(False)
@@ -632,9 +633,15 @@ def main():
     if not args.no_decode:
         dec_paged = bench_decode_paged(torch, bsa, synth, args.steps, args.warmup)
         torch.cuda.empty_cache()
-    hils = None
+    hils = lsa_1m = lsa_tree_1m = None
     if not args.no_hils:
         hils, t = bench_prefill(torch, bsa, synth, "hils_bf16_1m", max(2, args.steps // 4), 1)
+        if not args.no_lsa:
+            # the clustered indexes where the pages motivate them: the scan over every landmark
+            # grows with the context (16384 landmarks per query block at 1M tokens)
+            lsa_1m = bench_lsa(torch, bsa, synth, "hils_bf16_1m", t, max(2, args.steps // 4), 1)
+            lsa_tree_1m = bench_lsa(torch, bsa, synth, "hils_bf16_1m", t,
+                                    max(2, args.steps // 4), 1, tree=True)
         del t
         torch.cuda.empty_cache()
     peaks = None
@@ -717,6 +724,10 @@ def main():
                                             "attend": hils["attn_ms"]},
                            "attended_tflops_attention_kernel": hils["attended_tflops_kernel"],
                            "frac_of_bf16_peak": hils["attended_tflops_kernel"] / PEAK_BF16_TFLOPS}
+    if lsa_1m is not None:
+        line["lsa_prefill_1m"] = dict(lsa_1m, scan_select_ms=hils["select_ms"])
+    if lsa_tree_1m is not None:
+        line["lsa_tree_prefill_1m"] = dict(lsa_tree_1m, scan_select_ms=hils["select_ms"])
     if peaks is not None:
         # the same achieved rates against the ceilings measured on this GPU in this run
         line["measured_peaks"] = peaks

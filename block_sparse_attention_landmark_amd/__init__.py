@@ -22,6 +22,7 @@ and ``prefill(q, k, v, ...)`` / ``decode(q, kc, vc, lm, ...)`` chain them (``pre
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -66,9 +67,25 @@ def library_path() -> str:
 def load_library():
     """Load libbsa.so (once).  Raises RuntimeError if it has not been built."""
     global _LIB
-    if _LIB is not None:
-        return _LIB
-    path = library_path()
+    if _LIB is None:
+        _LIB = _open(library_path())
+    return _LIB
+
+
+@contextlib.contextmanager
+def using_library(path: str):
+    """Route every call made inside the block through another build of the library (the
+    race-check build libbsa_sync.so, in the tests that compare the two builds' bits)."""
+    global _LIB
+    prev = load_library()
+    _LIB = _open(path)
+    try:
+        yield _LIB
+    finally:
+        _LIB = prev
+
+
+def _open(path: str):
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with "
                            "`python -m block_sparse_attention_landmark_amd.build`")
@@ -124,7 +141,6 @@ def load_library():
     lib.bsa_last_error.restype = ctypes.c_char_p
     lib.bsa_version.argtypes = []
     lib.bsa_version.restype = ctypes.c_int
-    _LIB = lib
     return lib
 
 

@@ -1,5 +1,7 @@
 """Build libbsa.so (the HIP kernels and the C-ABI) in-tree for gfx950 with hipcc, and beside it
-libbsa_peak.so (the benchmark's measured-ceiling probes, not part of the attention path).
+libbsa_peak.so (the benchmark's measured-ceiling probes, not part of the attention path) and
+libbsa_sync.so (the race-check build of the same sources: every direct-to-LDS copy fully
+synchronised, for the tests that compare its bits with libbsa.so's).
 
     python -m block_sparse_attention_landmark_amd.build
 """
@@ -15,6 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libbsa.so")
 PEAK_LIB = os.path.join(PKG, "libbsa_peak.so")
+SYNC_LIB = os.path.join(PKG, "libbsa_sync.so")
 PEAK_SOURCES = ["peak_probe.hip"]
 SOURCES = ["bsa_api.hip", "pool.hip", "select.hip", "attend_prefill.hip", "attend_decode.hip",
            "attend_f32.hip", "attend_backward.hip", "lsa.hip"]
@@ -60,28 +63,30 @@ def _jobs() -> int:
     return max(1, min(n, 16))
 
 
-def _compile(sources, out: str, verbose: bool, defines=()) -> None:
-    """Compile each source to an object file in parallel (each carries its own gfx950 code
-    object), then link them into one shared library."""
+def _plan(sources, out: str, defines=()):
+    """Compile commands (one object per source; each carries its own gfx950 code object) and
+    the link command of one shared library."""
     tag = os.path.splitext(os.path.basename(out))[0]
     objdir = os.path.join(PKG, "_build", tag)
     os.makedirs(objdir, exist_ok=True)
     flags = [f for f in HIPCC_FLAGS if f != "-shared"] + [f"-D{d}" for d in defines]
     objs = [os.path.join(objdir, os.path.splitext(s)[0] + ".o") for s in sources]
     cmds = [[hipcc(), *flags, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(sources, objs)]
-    with ThreadPoolExecutor(max_workers=_jobs()) as ex:
-        for f in [ex.submit(_run, c, verbose) for c in cmds]:
-            f.result()
-    tmp = out + ".tmp"
-    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-    os.replace(tmp, out)
+    link = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", out + ".tmp"]
+    return cmds, link, out
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source into libbsa.so next to this file, and the probes into
-    libbsa_peak.so; returns the path of libbsa.so."""
-    _compile(SOURCES, LIB, verbose)
-    _compile(PEAK_SOURCES, PEAK_LIB, verbose)
+    """Compile every source (in parallel) into libbsa.so next to this file, the probes into
+    libbsa_peak.so and the race-check build into libbsa_sync.so; returns libbsa.so's path."""
+    plans = [_plan(SOURCES, LIB), _plan(PEAK_SOURCES, PEAK_LIB),
+             _plan(SOURCES, SYNC_LIB, defines=("BSA_SYNC_COPIES",))]
+    with ThreadPoolExecutor(max_workers=_jobs()) as ex:
+        for f in [ex.submit(_run, c, verbose) for cmds, _, _ in plans for c in cmds]:
+            f.result()
+    for _, link, out in plans:
+        _run(link, verbose)
+        os.replace(out + ".tmp", out)
     return LIB
 
 

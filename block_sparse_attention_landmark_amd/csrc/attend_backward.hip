@@ -657,6 +657,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     const char* qg = reinterpret_cast<const char*>(q + row0 * D);
     const char* og = reinterpret_cast<const char*>(dout + row0 * D);
     const uint32_t st_lds = smem_lds + (uint32_t)((st % kBwdStages) * STAGE_B);
+    sync_copies_barrier();     // race-check build only (every wave issues every step's copies)
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
       const int slot = (i * 4 + w) * kWave + lane;
@@ -681,6 +682,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
       dma_lds<4>(reinterpret_cast<const char*>(src + row0), (uint32_t)(min(lane, rmax) * 4),
                  st_lds + 2 * TILE_B + (uint32_t)(w * kBlock * 4));
     }
+    sync_copies_barrier();
   };
 
   f32x16 dka[DT], dva[DT];

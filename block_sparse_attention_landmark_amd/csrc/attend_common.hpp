@@ -46,6 +46,9 @@ __device__ __forceinline__ void dma_lds(const char* gbase, uint32_t voff, uint32
   const uint32_t g_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)ga);
   const uint64_t gs = ((uint64_t)g_hi << 32) | (uint64_t)g_lo;
   uint32_t saved;
+#if defined(BSA_SYNC_COPIES)
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#endif
   if constexpr (BYTES == 16)
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
@@ -66,6 +69,20 @@ __device__ __forceinline__ void dma_lds(const char* gbase, uint32_t voff, uint32
         : "=&s"(saved)
         : "s"(la), "v"(voff), "s"(gs)
         : "memory");
+#if defined(BSA_SYNC_COPIES)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#endif
+#endif
+}
+
+// Race-check build (compiled with -DBSA_SYNC_COPIES, as libbsa_sync.so): every direct-to-LDS
+// copy first waits for all of its wave's LDS reads in flight and then for its own completion, so
+// no copy can overwrite a tile that the wave is still reading nor be read before it lands; the
+// kernels whose waves all issue the same copies add a workgroup barrier on both sides as well
+// (sync_copies_barrier).  The normal build must give the same bits.
+__device__ __forceinline__ void sync_copies_barrier() {
+#if defined(BSA_SYNC_COPIES)
+  __syncthreads();
 #endif
 }
 

@@ -480,12 +480,14 @@ __global__ __launch_bounds__(512) void attend_prefill_pp_kernel(
       lim = T - 1 - j * kBlock;
     }
     const char* blk = (hv == 0 ? kb : vb) + (size_t)j * (size_t)(kBlock * D * 2);
+    sync_copies_barrier();     // race-check build only (every wave issues every copy_half)
 #pragma unroll
     for (int i = 0; i < SPW / 2; ++i) {
       const int sl = w + 8 * i;
       dma_lds<16>(blk, (uint32_t)(min(crow[i], lim) * (D * 2) + (hv == 0 ? kcol[i] : vcol_[i])),
                 dst + (hv * TILE + sl * RPI * D) * 2);
     }
+    sync_copies_barrier();
   };
   auto copy_unit = [&](int a) {
     copy_half(a, 0);

@@ -51,6 +51,20 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, n)
 
 
+def test_race_check_build_exports_the_same_symbols():
+    """libbsa_sync.so (the same sources with every direct-to-LDS copy fully synchronised, used
+    by the race-check GPU tests) exports exactly libbsa.so's functions."""
+    from block_sparse_attention_landmark_amd import build as B
+    if not os.path.exists(B.SYNC_LIB):
+        pytest.fail("libbsa_sync.so is not built; run `python -m block_sparse_attention_landmark_amd.build`")
+    syms = []
+    for path in (bsa.library_path(), B.SYNC_LIB):
+        out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True,
+                             text=True, check=True).stdout
+        syms.append(set(re.findall(r"\bT (bsa_\w+)", out)))
+    assert syms[0] == syms[1]
+
+
 def test_peak_probe_library_exports_its_probes():
     """The benchmark's ceiling probes live in their own library, outside the attention ABI."""
     from block_sparse_attention_landmark_amd import build as B
