@@ -133,6 +133,8 @@ def _open(path: str):
     lib.bsa_lsa_tree_centres.restype = st
     lib.bsa_lsa_tree_select.argtypes = [P, vp, vp, i32, i32, i32, i32] + [vp] * 7 + [vp, ctypes.c_size_t, vp]
     lib.bsa_lsa_tree_select.restype = st
+    lib.bsa_attend_decode_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.bsa_attend_decode_noalloc.restype = st
     lib.bsa_workspace_bytes.argtypes = [P, ctypes.c_int]
     lib.bsa_workspace_bytes.restype = ctypes.c_size_t
     lib.bsa_status_string.argtypes = [ctypes.c_int]
@@ -337,6 +339,47 @@ def attend_decode(q, kc, vc, idx, sc=None, lm=None, *, mode="plain", topk=None, 
            lib.bsa_attend_decode(ctypes.byref(p), _ptr(q), _ptr(kc), _ptr(vc), _ptr(lm), _ptr(idx),
                                  _ptr(sc), _ptr(out), _ptr(lse), _ptr(ws),
                                  0 if ws is None else ws.numel(), _stream(q.device)))
+    return out, lse
+
+
+def attend_decode_noalloc(q, kc, vc, idx, sc=None, lm=None, *, mode="plain", topk=None,
+                          n_sink=1, n_local=2, scale=0.0, out=None, lse=None):
+    """attend_decode without a workspace: the library keeps the split partial states in its
+    static per-device scratch (4 MiB; larger needs are rejected).  For callers that cannot
+    allocate, so `out` (and `lse`, when wanted) should be passed in; calls on one device must
+    not overlap."""
+    lib = load_library()
+    _need(q, "q", ndim=4)
+    B, Hq, one, D = q.shape
+    if one != 1:
+        raise ValueError("q must be [B,Hq,1,D]")
+    _need(kc, "kc", dtype=q.dtype, ndim=4)
+    Hkv, Tk = kc.shape[1], kc.shape[2]
+    _need(kc, "kc", shape=(B, Hkv, Tk, D))
+    _need(vc, "vc", dtype=q.dtype, shape=(B, Hkv, Tk, D))
+    _need(idx, "idx", dtype=torch.int32, ndim=4)
+    NA = idx.shape[-1]
+    if topk is None:
+        topk = NA - n_sink - n_local
+    if NA != n_sink + n_local + topk:
+        raise ValueError(f"idx has {NA} entries per row, the call needs n_sink + n_local + topk")
+    _need(idx, "idx", shape=(B, Hkv, 1, NA))
+    if sc is not None:
+        _need(sc, "sc", dtype=torch.float32, shape=(B, Hkv, 1, NA))
+    if lm is not None:
+        _need(lm, "lm", dtype=q.dtype, shape=(B, Hkv, _nblocks(Tk), D))
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", dtype=q.dtype, shape=q.shape)
+    if lse is not None:
+        _need(lse, "lse", dtype=torch.float32, shape=(B, Hq))
+    _on_device(q, kc=kc, vc=vc, idx=idx, sc=sc, lm=lm, out=out, lse=lse)
+    p = make_params(B=B, Hq=Hq, Hkv=Hkv, D=D, seq_q=1, seq_k=Tk, dtype=q.dtype, topk=topk,
+                    n_sink=n_sink, n_local=n_local, scale=scale, mode=mode)
+    _check("bsa_attend_decode_noalloc",
+           lib.bsa_attend_decode_noalloc(ctypes.byref(p), _ptr(q), _ptr(kc), _ptr(vc), _ptr(lm),
+                                         _ptr(idx), _ptr(sc), _ptr(out), _ptr(lse),
+                                         _stream(q.device)))
     return out, lse
 
 

@@ -5,6 +5,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "attend_common.hpp"
 #include "bsa_internal.hpp"
@@ -505,6 +506,49 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
     for (int s = 0; s < nsplit; ++s) acc += col[(size_t)s * G * D] * sm[row][s];
     out[((size_t)b * Hkv * G + g * G + row) * D + d] = (OUT)acc;
   }
+}
+
+// =============================================================================================
+// static scratch for callers that cannot allocate
+// =============================================================================================
+// The split partial states of bsa_attend_decode_noalloc live in this file-scope array instead of
+// a caller's workspace: each device that runs the library holds its own copy for the life of the
+// process.  Host code never uses the array's name as an address: its device address is looked
+// up once per device (hipGetSymbolAddress, with that device current) and kept below.  Every
+// split writes its whole partial state before the merge reads it, so the array needs no
+// clearing between calls; calls that overlap on one device share it and race.
+constexpr int kScratchMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(hipStream_t st, void** ptr) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  int dev = cur;
+  if (st != nullptr) {
+    e = hipStreamGetDevice(st, &dev);
+    if (e != hipSuccess) return e;
+  }
+  if (dev < 0 || dev >= kScratchMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 // =============================================================================================

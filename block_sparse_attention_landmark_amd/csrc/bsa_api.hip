@@ -430,6 +430,38 @@ bsa_status_t bsa_attend_decode(const bsa_params_t* params, const void* q, const 
                     "attend_decode");
 }
 
+bsa_status_t bsa_attend_decode_noalloc(const bsa_params_t* params, const void* q, const void* kc,
+                                       const void* vc, const void* lm, const int32_t* idx,
+                                       const float* sc, void* out, float* lse, void* stream) {
+  bsa::Shape s;
+  BSA_TRY(make_shape(params, kDecode, &s));
+  BSA_TRY(check_ptr(q, "q"));
+  BSA_TRY(check_ptr(kc, "kc"));
+  BSA_TRY(check_ptr(vc, "vc"));
+  BSA_TRY(check_ptr(idx, "idx"));
+  BSA_TRY(check_ptr(out, "out"));
+  if (s.mode == BSA_MODE_SAS) BSA_TRY(check_ptr(sc, "sc"));
+  if (s.mode == BSA_MODE_HILS) {
+    BSA_TRY(check_ptr(lm, "lm"));
+    if (lse != nullptr) return fail(BSA_ERR_UNSUPPORTED, "lse is not defined for HILS; pass NULL");
+  }
+  if (lse != nullptr) BSA_TRY(check_ptr(lse, "lse"));
+  const size_t need = bsa::decode_ws_bytes(s);
+  if (need > bsa::kNoAllocScratchBytes)
+    return fail(BSA_ERR_WORKSPACE,
+                "these shapes need %zu bytes of split partials; the static scratch of "
+                "bsa_attend_decode_noalloc holds %zu bytes (use bsa_attend_decode with a workspace)",
+                need, bsa::kNoAllocScratchBytes);
+  hipStream_t st = (hipStream_t)stream;
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = bsa::noalloc_scratch(st, &ws);
+    if (e != hipSuccess) return fail(BSA_ERR_HIP, "static scratch lookup: %s", hipGetErrorString(e));
+  }
+  return hip_result(bsa::launch_attend_decode(s, q, kc, vc, lm, idx, sc, out, lse, ws, st),
+                    "attend_decode_noalloc");
+}
+
 // ---- paged (ragged) decode ----
 
 bsa_status_t bsa_pool_landmarks_paged(const bsa_params_t* params, const void* k_pool,

@@ -38,6 +38,10 @@ size_t select_ws_bytes(const Shape& s);
 // Workspace of bsa_attend_decode: split partials.
 int decode_splits(const Shape& s);
 size_t decode_ws_bytes(const Shape& s);
+// Static per-device scratch that bsa_attend_decode_noalloc uses in place of the workspace: its
+// size, and its device address on the device of stream st (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = size_t(4) << 20;
+hipError_t noalloc_scratch(hipStream_t st, void** ptr);
 
 hipError_t launch_pool_landmarks(const Shape& s, const void* k, void* lm, hipStream_t st);
 hipError_t launch_selector_vectors(const Shape& s, const void* q, float* qbar, hipStream_t st);

@@ -156,6 +156,22 @@ bsa_status_t bsa_attend_decode(const bsa_params_t* params, const void* q, const 
                                size_t ws_bytes, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): bsa_attend_decode without a workspace argument.  The
+ * split partial states that bsa_attend_decode keeps in the caller's workspace live instead in a
+ * static device array of 4 MiB (4194304 bytes) inside the library; each device that runs it
+ * holds its own copy until the process ends, and its address is looked up on the first call on
+ * that device (the device of `stream`).  The call allocates and frees nothing.  Shapes whose
+ * partial states need more than 4 MiB (bsa_decode_workspace_bytes(params) > 4194304) are
+ * rejected with BSA_ERR_WORKSPACE before anything is launched.  Every call on one device shares
+ * that array: calls that overlap on one device race (serialise them, e.g. on one stream).
+ * Arguments, results and errors otherwise as bsa_attend_decode.
+ */
+bsa_status_t bsa_attend_decode_noalloc(const bsa_params_t* params, const void* q, const void* kc,
+                                       const void* vc, const void* lm, const int32_t* idx,
+                                       const float* sc, void* out, float* lse, void* stream);
+
+/*
  * Paged, ragged decode: the serving layout, where sequences of different lengths share one pool
  * of 64-token pages (one page = one block, so a block never straddles two pages).
  *   k_pool, v_pool [n_pages, Hkv, 64, D]: page p of kv head g is the contiguous 64 x D tile at

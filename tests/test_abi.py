@@ -208,6 +208,24 @@ def test_attend_validation(lib):
     assert dec(d, vc=None) == NULL
 
 
+def test_noalloc_decode_validation(lib):
+    """The no-allocation decode call validates like bsa_attend_decode and rejects, before any
+    device work, shapes whose split partial states exceed its 4 MiB static scratch."""
+    def call(p, **kw):
+        a = dict(q=FAKE, kc=FAKE, vc=FAKE, lm=None, idx=FAKE, sc=None, out=FAKE, lse=None)
+        a.update(kw)
+        return lib.bsa_attend_decode_noalloc(ctypes.byref(p), a["q"], a["kc"], a["vc"], a["lm"],
+                                             a["idx"], a["sc"], a["out"], a["lse"], None)
+
+    big = _p(B=200, Hq=32, Hkv=1, seq_q=1, seq_k=384, topk=8)
+    assert lib.bsa_decode_workspace_bytes(ctypes.byref(big)) > 4 << 20
+    assert call(big) == WS
+    assert b"4194304" in lib.bsa_last_error()
+    assert call(_p(seq_q=1, seq_k=4096), vc=None) == NULL
+    assert call(_p()) == SHAPE                   # decode needs seq_q == 1
+    assert call(_p(seq_q=1, seq_k=4096, mode="sas")) == NULL   # SAS needs sc
+
+
 def test_decode_step_workspace_and_validation(lib):
     rnd = lambda x: (x + 255) // 256 * 256
     ws = lambda p: lib.bsa_decode_step_workspace_bytes(ctypes.byref(p))
