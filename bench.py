@@ -449,7 +449,24 @@ def bench_decode_paged(torch, bsa, synth, steps, warmup):
             ev_attn.stop()
             ev_two.pairs[-1][1] = ev_attn.pairs[-1][1]
 
-    for fn in (step, two_calls):
+    ev_ref, ev_refresh = Events(torch), Events(torch)
+
+    def step_with_refresh(record):
+        # a decode loop's step: the landmark of each sequence's newest token's block is
+        # refreshed (one block per sequence and kv head), then selection and attention
+        if record:
+            ev_ref.start()
+        bsa.update_landmarks_paged(k_pool, table, seq_lens, lm, 1)
+        if record:
+            ev_refresh.start()
+            ev_refresh.stop()
+        bsa.decode_step_paged(q, k_pool, v_pool, table, seq_lens, lm, topk=K, idx=idx, sc=sc,
+                              out=out, ws=ws_step)
+        if record:
+            ev_ref.stop()
+            ev_refresh.pairs[-1][0] = ev_ref.pairs[-1][0]
+
+    for fn in (step, two_calls, step_with_refresh):
         for _ in range(warmup):
             fn(False)
         for _ in range(steps):
@@ -466,7 +483,13 @@ def bench_decode_paged(torch, bsa, synth, steps, warmup):
            "us_per_step": step_us, "us_per_step_median": 1e3 * stat(ev_step.ms(), "median"),
            "us_per_step_min": 1e3 * min(ev_step.ms()), "two_call_us_per_step": two_us,
            "two_call_breakdown_us": {"select": two_us - attn_us, "attend": attn_us},
-           "hbm_gbps": nbytes / (step_us * 1e-6) / 1e9}
+           "hbm_gbps": nbytes / (step_us * 1e-6) / 1e9,
+           "with_landmark_refresh": {
+               "us_per_step": 1e3 * sum(ev_ref.ms()) / steps,
+               "refresh_us": 1e3 * sum(ev_refresh.ms()) / steps,
+               "what": "bsa_update_landmarks_paged (n_new = 1: the newest token's block of every "
+                       "sequence and kv head) then the one-launch paged step; re-pooling the whole "
+                       "cache instead is bsa_pool_landmarks_paged"}}
     res["roofline"] = {"bound": "hbm", "achieved": res["hbm_gbps"], "peak": PEAK_HBM_GBPS,
                        "unit": "GB/s", "frac": res["hbm_gbps"] / PEAK_HBM_GBPS,
                        "algorithmic_bytes": nbytes,

@@ -133,6 +133,12 @@ def _open(path: str):
     lib.bsa_lsa_tree_centres.restype = st
     lib.bsa_lsa_tree_select.argtypes = [P, vp, vp, i32, i32, i32, i32] + [vp] * 7 + [vp, ctypes.c_size_t, vp]
     lib.bsa_lsa_tree_select.restype = st
+    lib.bsa_update_landmarks.argtypes = [P, vp, i32, vp, vp]
+    lib.bsa_update_landmarks.restype = st
+    lib.bsa_update_landmarks_paged.argtypes = [P, vp, i32, vp, vp, i32, vp, vp]
+    lib.bsa_update_landmarks_paged.restype = st
+    lib.bsa_lsa_update_index.argtypes = [P, vp, i32, i32, i32, vp, vp, vp, vp, vp]
+    lib.bsa_lsa_update_index.restype = st
     lib.bsa_attend_decode_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.bsa_attend_decode_noalloc.restype = st
     lib.bsa_workspace_bytes.argtypes = [P, ctypes.c_int]
@@ -214,6 +220,22 @@ def pool_landmarks(k: torch.Tensor, out: torch.Tensor | None = None) -> torch.Te
     _check("bsa_pool_landmarks", lib.bsa_pool_landmarks(ctypes.byref(p), _ptr(k), _ptr(out),
                                                         _stream(k.device)))
     return out
+
+
+def update_landmarks(k: torch.Tensor, lm: torch.Tensor, n_new: int) -> torch.Tensor:
+    """Recompute, in place, the landmarks of the blocks holding the last n_new tokens of
+    k [B,Hkv,T,D] (the blocks that changed when those tokens were appended); returns lm."""
+    lib = load_library()
+    _need(k, "k", ndim=4)
+    B, Hkv, T, D = k.shape
+    _need(lm, "lm", dtype=k.dtype, shape=(B, Hkv, _nblocks(T), D))
+    if int(n_new) < 1:
+        raise ValueError("n_new must be >= 1")
+    _on_device(k, lm=lm)
+    p = make_params(B=B, Hq=Hkv, Hkv=Hkv, D=D, seq_q=T, seq_k=T, dtype=k.dtype)
+    _check("bsa_update_landmarks", lib.bsa_update_landmarks(ctypes.byref(p), _ptr(k), int(n_new),
+                                                            _ptr(lm), _stream(k.device)))
+    return lm
 
 
 def select_workspace_bytes(p: Params) -> int:
@@ -508,6 +530,28 @@ def _select_outputs(q, B, Hkv, R, NA, idx, sc):
     return idx, sc
 
 
+def lsa_update_index(lm: torch.Tensor, index: dict, first_segment: int) -> dict:
+    """Cluster, in place, only the segments first_segment .. NS-1 of an index from
+    lsa_build_index (the segments completed since it was built up to first_segment); the
+    clusters of earlier segments are kept as they are.  Returns the index."""
+    lib = load_library()
+    _need(lm, "lm", ndim=4)
+    B, Hkv, NB, D = lm.shape
+    _check_index(index, B, Hkv, NB, D)
+    seg, nc = int(index["seg_blocks"]), int(index["n_clusters"])
+    _need(index["merges"], "merges", dtype=torch.int32,
+          shape=(B, Hkv, NB // seg, max(seg - nc, 0), 2))
+    _on_device(lm, centres=index["centres"], members=index["members"],
+               offsets=index["offsets"], merges=index["merges"])
+    p = make_params(B=B, Hq=Hkv, Hkv=Hkv, D=D, seq_q=NB * 64, seq_k=NB * 64, dtype=lm.dtype)
+    _check("bsa_lsa_update_index",
+           lib.bsa_lsa_update_index(ctypes.byref(p), _ptr(lm), seg, nc, int(first_segment),
+                                    _ptr(index["centres"]), _ptr(index["members"]),
+                                    _ptr(index["offsets"]), _ptr(index["merges"]),
+                                    _stream(lm.device)))
+    return index
+
+
 def lsa_select(q: torch.Tensor, lm: torch.Tensor, index: dict, *, topk: int,
                seq_k: int | None = None, n_sink: int = 1, n_local: int = 2, ws=None, idx=None,
                sc=None):
@@ -703,6 +747,23 @@ def pool_landmarks_paged(k_pool, page_table, seq_lens, out=None):
                                         _ptr(page_table), _ptr(seq_lens), _ptr(out),
                                         _stream(k_pool.device)))
     return out
+
+
+def update_landmarks_paged(k_pool, page_table, seq_lens, lm, n_new: int):
+    """Recompute, in place, the landmarks [B,Hkv,NB,D] of the blocks holding each sequence's last
+    n_new tokens (after appending n_new tokens to every sequence of a paged batch); returns lm."""
+    lib = load_library()
+    n_pages, Hkv, D, B, NB = _paged_shapes(k_pool, page_table, seq_lens)
+    _need(lm, "lm", dtype=k_pool.dtype, shape=(B, Hkv, NB, D))
+    if int(n_new) < 1:
+        raise ValueError("n_new must be >= 1")
+    _on_device(k_pool, page_table=page_table, seq_lens=seq_lens, lm=lm)
+    p = make_params(B=B, Hq=Hkv, Hkv=Hkv, D=D, seq_q=NB * 64, seq_k=NB * 64, dtype=k_pool.dtype)
+    _check("bsa_update_landmarks_paged",
+           lib.bsa_update_landmarks_paged(ctypes.byref(p), _ptr(k_pool), int(n_pages),
+                                          _ptr(page_table), _ptr(seq_lens), int(n_new), _ptr(lm),
+                                          _stream(k_pool.device)))
+    return lm
 
 
 def select_topk_paged(q, lm, seq_lens, *, topk: int, n_sink: int = 1, n_local: int = 2,

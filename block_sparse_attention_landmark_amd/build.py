@@ -21,6 +21,8 @@ SYNC_LIB = os.path.join(PKG, "libbsa_sync.so")
 PEAK_SOURCES = ["peak_probe.hip"]
 SOURCES = ["bsa_api.hip", "pool.hip", "select.hip", "attend_prefill.hip", "attend_decode.hip",
            "attend_f32.hip", "attend_backward.hip", "lsa.hip"]
+# per-source code generation options (none at present)
+SOURCE_FLAGS = {}
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -71,7 +73,8 @@ def _plan(sources, out: str, defines=()):
     os.makedirs(objdir, exist_ok=True)
     flags = [f for f in HIPCC_FLAGS if f != "-shared"] + [f"-D{d}" for d in defines]
     objs = [os.path.join(objdir, os.path.splitext(s)[0] + ".o") for s in sources]
-    cmds = [[hipcc(), *flags, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(sources, objs)]
+    cmds = [[hipcc(), *flags, *SOURCE_FLAGS.get(s, []), "-c", os.path.join(CSRC, s), "-o", o]
+            for s, o in zip(sources, objs)]
     link = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", out + ".tmp"]
     return cmds, link, out
 

@@ -157,6 +157,17 @@ bsa_status_t bsa_pool_landmarks(const bsa_params_t* params, const void* k, void*
   return hip_result(bsa::launch_pool_landmarks(s, k, lm, (hipStream_t)stream), "pool_landmarks");
 }
 
+bsa_status_t bsa_update_landmarks(const bsa_params_t* params, const void* k, int32_t n_new,
+                                  void* lm, void* stream) {
+  bsa::Shape s;
+  BSA_TRY(make_shape(params, kPool, &s));
+  if (n_new < 1) return fail(BSA_ERR_SHAPE, "n_new must be >= 1 (got %d)", n_new);
+  BSA_TRY(check_ptr(k, "k"));
+  BSA_TRY(check_ptr(lm, "lm"));
+  return hip_result(bsa::launch_pool_landmarks(s, k, lm, (hipStream_t)stream, n_new),
+                    "update_landmarks");
+}
+
 size_t bsa_select_workspace_bytes(const bsa_params_t* params) {
   bsa::Shape s;
   if (make_shape(params, kSelect, &s) != BSA_OK) return 0;
@@ -238,6 +249,26 @@ bsa_status_t bsa_lsa_build_index(const bsa_params_t* params, const void* lm, int
   return hip_result(bsa::launch_lsa_build(s, lm, seg_blocks, n_clusters, centres, members, offsets,
                                           merges, (hipStream_t)stream),
                     "lsa_build_index");
+}
+
+bsa_status_t bsa_lsa_update_index(const bsa_params_t* params, const void* lm, int32_t seg_blocks,
+                                  int32_t n_clusters, int32_t first_segment, float* centres,
+                                  int32_t* members, int32_t* offsets, int32_t* merges,
+                                  void* stream) {
+  bsa::Shape s;
+  BSA_TRY(make_shape(params, kPool, &s));
+  BSA_TRY(check_lsa(s, seg_blocks, n_clusters));
+  if (first_segment < 0)
+    return fail(BSA_ERR_SHAPE, "first_segment must be >= 0 (got %d)", first_segment);
+  if (s.NB / seg_blocks <= first_segment) return ok();   // no segment to cluster
+  BSA_TRY(check_ptr(lm, "lm"));
+  BSA_TRY(check_ptr(centres, "centres"));
+  BSA_TRY(check_ptr(members, "members"));
+  BSA_TRY(check_ptr(offsets, "offsets"));
+  if (seg_blocks > n_clusters) BSA_TRY(check_ptr(merges, "merges"));
+  return hip_result(bsa::launch_lsa_build(s, lm, seg_blocks, n_clusters, centres, members, offsets,
+                                          merges, (hipStream_t)stream, first_segment),
+                    "lsa_update_index");
 }
 
 size_t bsa_lsa_select_workspace_bytes(const bsa_params_t* params) {
@@ -475,6 +506,22 @@ bsa_status_t bsa_pool_landmarks_paged(const bsa_params_t* params, const void* k_
   const bsa::Pages pg{page_table, seq_lens, n_pages};
   return hip_result(bsa::launch_pool_landmarks_paged(s, k_pool, pg, lm, (hipStream_t)stream),
                     "pool_landmarks_paged");
+}
+
+bsa_status_t bsa_update_landmarks_paged(const bsa_params_t* params, const void* k_pool,
+                                        int32_t n_pages, const int32_t* page_table,
+                                        const int32_t* seq_lens, int32_t n_new, void* lm,
+                                        void* stream) {
+  bsa::Shape s;
+  BSA_TRY(make_shape(params, kPool, &s));
+  BSA_TRY(check_paged(params, s, n_pages, page_table, seq_lens, true));
+  if (n_new < 1) return fail(BSA_ERR_SHAPE, "n_new must be >= 1 (got %d)", n_new);
+  BSA_TRY(check_ptr(k_pool, "k_pool"));
+  BSA_TRY(check_ptr(lm, "lm"));
+  const bsa::Pages pg{page_table, seq_lens, n_pages};
+  return hip_result(
+      bsa::launch_pool_landmarks_paged(s, k_pool, pg, lm, (hipStream_t)stream, n_new),
+      "update_landmarks_paged");
 }
 
 bsa_status_t bsa_select_topk_paged(const bsa_params_t* params, const void* q, const void* lm,

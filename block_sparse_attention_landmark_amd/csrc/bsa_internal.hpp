@@ -43,7 +43,9 @@ size_t decode_ws_bytes(const Shape& s);
 constexpr size_t kNoAllocScratchBytes = size_t(4) << 20;
 hipError_t noalloc_scratch(hipStream_t st, void** ptr);
 
-hipError_t launch_pool_landmarks(const Shape& s, const void* k, void* lm, hipStream_t st);
+// n_new > 0: only the blocks holding the last n_new tokens (of every sequence)
+hipError_t launch_pool_landmarks(const Shape& s, const void* k, void* lm, hipStream_t st,
+                                 int n_new = 0);
 hipError_t launch_selector_vectors(const Shape& s, const void* q, float* qbar, hipStream_t st);
 hipError_t launch_block_scores(const Shape& s, const float* qbar, const void* lm, float* scores,
                                hipStream_t st);
@@ -54,7 +56,7 @@ bool decode_select_fused(const Shape& s);
 hipError_t launch_decode_select(const Shape& s, const void* q, const void* lm, int32_t* idx,
                                 float* sc, hipStream_t st, const Pages* pg = nullptr);
 hipError_t launch_pool_landmarks_paged(const Shape& s, const void* k_pool, const Pages& pg,
-                                       void* lm, hipStream_t st);
+                                       void* lm, hipStream_t st, int n_new = 0);
 hipError_t launch_attend_prefill(const Shape& s, const void* q, const void* k, const void* v,
                                  const void* lm, const int32_t* idx, const float* sc, void* out,
                                  float* lse, hipStream_t st);
@@ -81,8 +83,10 @@ hipError_t launch_attend_backward(const Shape& s, const void* q, const void* k, 
 
 // Flat clustered (LSA) index: shape limits, index build, selection over it.
 bool lsa_shape_ok(const Shape& s, int seg, int nc);
+// segments seg0 .. NB / seg - 1 (seg0 > 0: only the segments completed since an earlier build)
 hipError_t launch_lsa_build(const Shape& s, const void* lm, int seg, int nc, float* centres,
-                            int32_t* members, int32_t* offsets, int32_t* merges, hipStream_t st);
+                            int32_t* members, int32_t* offsets, int32_t* merges, hipStream_t st,
+                            int seg0 = 0);
 hipError_t launch_lsa_select(const Shape& s, const void* q, const void* lm, int seg, int nc,
                              const float* centres, const int32_t* members,
                              const int32_t* offsets, int32_t* idx, float* sc, float* qbar,

@@ -41,7 +41,7 @@ __global__ __launch_bounds__(256) void lsa_ward_kernel(const TIN* __restrict__ l
                                                        int32_t* __restrict__ members,
                                                        int32_t* __restrict__ offsets,
                                                        int32_t* __restrict__ merges, int NB,
-                                                       int NS, int SEG, int NC) {
+                                                       int NS, int SEG, int NC, int seg0) {
   constexpr int MP = kLsaMaxSeg + 1;     // pitch of the transposed means: slot p of dim d at d*MP+p
   constexpr int S = kLsaMaxSeg;
   __shared__ float mt[D * MP];
@@ -54,7 +54,7 @@ __global__ __launch_bounds__(256) void lsa_ward_kernel(const TIN* __restrict__ l
   __shared__ float rv[4];
   __shared__ int ri[4];
   __shared__ int pick[2];
-  const int seg = blockIdx.x, bg = blockIdx.y;
+  const int seg = seg0 + blockIdx.x, bg = blockIdx.y;
   const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
   const int lo = seg * SEG;
   const TIN* L = lm + ((size_t)bg * NB + lo) * D;
@@ -758,15 +758,16 @@ bool lsa_shape_ok(const Shape& s, int seg, int nc) {
   return s.topk <= kLsaMaxK;
 }
 
+// segments seg0 .. NS-1 (seg0 > 0: the segments completed since the index was last updated)
 hipError_t launch_lsa_build(const Shape& s, const void* lm, int seg, int nc, float* centres,
                             int32_t* members, int32_t* offsets, int32_t* merges,
-                            hipStream_t st) {
+                            hipStream_t st, int seg0) {
   const int ns = s.NB / seg;
-  if (ns == 0) return hipSuccess;
-  dim3 grid(ns, s.B * s.Hkv);
+  if (ns <= seg0) return hipSuccess;
+  dim3 grid(ns - seg0, s.B * s.Hkv);
 #define BSA_WARD(D_, T_)                                                                     \
   hipLaunchKernelGGL((lsa_ward_kernel<D_, T_>), grid, dim3(256), 0, st, (const T_*)lm, centres, \
-                     members, offsets, merges, s.NB, ns, seg, nc)
+                     members, offsets, merges, s.NB, ns, seg, nc, seg0)
   if (s.D == 128) {
     if (s.bf16) BSA_WARD(128, bf16);
     else BSA_WARD(128, float);

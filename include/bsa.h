@@ -246,6 +246,31 @@ bsa_status_t bsa_decode_step_paged(const bsa_params_t* params, const void* q,
                                    float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Landmark refresh after tokens are appended (decode-time cache maintenance).  A block's pooled
+ * key depends only on its own tokens (LSA page, "The index stops scanning the whole context",
+ * paragraph 3: keys are pooled per block, and a block's index entry is fixed once the block is
+ * complete), so after n_new tokens are appended only the blocks holding them change: this call
+ * recomputes, for every (sequence, kv head), the landmarks of blocks (seq_k - n_new) / 64 ..
+ * NB - 1 of k [B,Hkv,seq_k,D] exactly as bsa_pool_landmarks computes them, and writes no other
+ * element of lm [B,Hkv,NB,D].  n_new >= 1 (n_new >= seq_k refreshes every block).
+ */
+bsa_status_t bsa_update_landmarks(const bsa_params_t* params, const void* k, int32_t n_new,
+                                  void* lm, void* stream);
+
+/*
+ * The same refresh for a paged, ragged batch (layouts of bsa_pool_landmarks_paged): sequence b,
+ * holding seq_lens[b] tokens of which the last n_new were appended since its landmarks were
+ * last computed, gets the landmarks of blocks (seq_lens[b] - n_new) / 64 .. (seq_lens[b]-1) / 64
+ * recomputed as bsa_pool_landmarks_paged computes them; blocks before them and past its last
+ * block are not written.  A decode loop that appends one token per sequence and step calls it
+ * with n_new = 1 (one block per sequence and kv head) instead of re-pooling the whole cache.
+ */
+bsa_status_t bsa_update_landmarks_paged(const bsa_params_t* params, const void* k_pool,
+                                        int32_t n_pages, const int32_t* page_table,
+                                        const int32_t* seq_lens, int32_t n_new, void* lm,
+                                        void* stream);
+
+/*
  * Flat clustered index over the landmarks (LSA page, "The index stops scanning the whole
  * context", paragraphs 3-5: similar pooled keys are grouped by Ward's algorithm once a block of
  * the context is complete, and kept as each cluster's centre plus the table of its positions).
@@ -266,6 +291,18 @@ bsa_status_t bsa_decode_step_paged(const bsa_params_t* params, const void* q,
 bsa_status_t bsa_lsa_build_index(const bsa_params_t* params, const void* lm, int32_t seg_blocks,
                                  int32_t n_clusters, float* centres, int32_t* members,
                                  int32_t* offsets, int32_t* merges, void* stream);
+
+/*
+ * Index maintenance (LSA page, "The index stops scanning the whole context", paragraph 3: once a
+ * block of the context is complete its clusters are computed and then kept): clusters only the
+ * completed segments first_segment .. NS-1 into the arrays of bsa_lsa_build_index (same layouts,
+ * same arithmetic) and writes nothing of the segments below first_segment, whose clusters stay
+ * as they were.  first_segment = 0 is bsa_lsa_build_index; first_segment >= NS writes nothing.
+ */
+bsa_status_t bsa_lsa_update_index(const bsa_params_t* params, const void* lm, int32_t seg_blocks,
+                                  int32_t n_clusters, int32_t first_segment, float* centres,
+                                  int32_t* members, int32_t* offsets, int32_t* merges,
+                                  void* stream);
 
 /* Workspace bytes of bsa_lsa_select (prefill: the selector vectors; decode: 0). */
 size_t bsa_lsa_select_workspace_bytes(const bsa_params_t* params);

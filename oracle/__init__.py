@@ -49,4 +49,7 @@ from .bsa_oracle import (  # noqa: F401
     lsa_select_row,
     lsa_tree_centres,
     lsa_tree_select_row,
+    update_landmarks,
+    update_landmarks_paged,
+    lsa_update_index,
 )

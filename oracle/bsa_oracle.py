@@ -843,3 +843,47 @@ def lsa_tree_select_row(qbar_c, L, index, c: int, topk: int, n_sink: int = 1, n_
     A = np.array(sorted(sink | local | set(chosen)), dtype=np.int64)
     sA = np.array([chosen[j] if j in chosen else float(qbar_c @ L[j]) for j in A])
     return A, sA
+
+
+# --------------------------------------------------------------------------------------
+# 12. decode-time maintenance
+# --------------------------------------------------------------------------------------
+#
+# LSA page, "The index stops scanning the whole context", paragraph 3: keys are pooled per block
+# and a block's clusters are computed once the block is complete and then kept.  A landmark is a
+# function of its own block's keys only, so appending tokens changes only the blocks that hold
+# them; a completed segment's clustering never changes.
+
+def update_landmarks(lm, k, n_new: int, dtype: str, block: int = BLOCK) -> np.ndarray:
+    """lm [B,H,NB,D] with the blocks holding the last n_new tokens of k [B,H,T,D] recomputed as
+    block means (rounded to dtype); every other block keeps its value from lm."""
+    B, H, T, D = k.shape
+    out = np.array(lm, dtype=np.float64, copy=True)
+    for j in range(max(T - n_new, 0) // block, n_blocks(T, block)):
+        lo, hi = j * block, min((j + 1) * block, T)
+        out[:, :, j, :] = round_to_dtype(k[:, :, lo:hi, :].mean(axis=2), dtype)
+    return out
+
+
+def update_landmarks_paged(lm, k_pool, page_table, seq_lens, n_new: int, dtype: str,
+                           block: int = BLOCK) -> np.ndarray:
+    """Paged layout: sequence b's blocks holding its last n_new tokens are recomputed from its
+    pages; its other blocks (and blocks past its end) keep their value from lm [B,Hkv,NB,D]."""
+    out = np.array(lm, dtype=np.float64, copy=True)
+    for b, L in enumerate(seq_lens):
+        L = int(L)
+        for j in range(max(L - n_new, 0) // block, (L - 1) // block + 1):
+            n = min(block, L - j * block)
+            out[b, :, j, :] = round_to_dtype(k_pool[int(page_table[b][j]), :, :n, :].mean(axis=1),
+                                             dtype)
+    return out
+
+
+def lsa_update_index(index, L: np.ndarray, first_segment: int, seg_blocks: int = 64,
+                     n_clusters: int = 16):
+    """The index of lsa_index after the segments first_segment .. NS-1 completed: the entries of
+    the earlier segments are kept as they are (the same objects), the new segments clustered."""
+    L = np.asarray(L, dtype=np.float64)
+    fresh = lsa_index(L, seg_blocks, n_clusters)
+    return list(index[:first_segment]) + fresh[first_segment:]
+

@@ -226,6 +226,30 @@ def test_noalloc_decode_validation(lib):
     assert call(_p(seq_q=1, seq_k=4096, mode="sas")) == NULL   # SAS needs sc
 
 
+def test_maintenance_validation(lib):
+    """The landmark refresh and index update calls reject bad counts and pointers before any
+    launch; an index update with no new segment launches nothing and succeeds."""
+    p = _p(seq_q=4096, seq_k=4096)
+    assert lib.bsa_update_landmarks(ctypes.byref(p), FAKE, 0, FAKE, None) == SHAPE
+    assert lib.bsa_update_landmarks(ctypes.byref(p), None, 1, FAKE, None) == NULL
+    assert lib.bsa_update_landmarks(ctypes.byref(p), FAKE, 1, MIS, None) == ALIGN
+    assert lib.bsa_update_landmarks_paged(ctypes.byref(p), FAKE, 10, FAKE, FAKE, 0, FAKE,
+                                          None) == SHAPE
+    assert lib.bsa_update_landmarks_paged(ctypes.byref(p), FAKE, 10, None, FAKE, 1, FAKE,
+                                          None) == NULL
+    assert lib.bsa_update_landmarks_paged(ctypes.byref(p), FAKE, 0, FAKE, FAKE, 1, FAKE,
+                                          None) == SHAPE
+    # 4096 tokens = 64 blocks = 4 segments of 16
+    up = lambda first, **kw: lib.bsa_lsa_update_index(
+        ctypes.byref(p), kw.get("lm", FAKE), 16, 4, first, kw.get("c", FAKE), FAKE, FAKE, FAKE,
+        None)
+    assert up(-1) == SHAPE
+    assert up(4, lm=None, c=None) == OK          # no segment completed since: nothing to do
+    assert up(2, c=None) == NULL
+    assert lib.bsa_lsa_update_index(ctypes.byref(p), FAKE, 16, 17, 0, FAKE, FAKE, FAKE, FAKE,
+                                    None) == UNSUP
+
+
 def test_decode_step_workspace_and_validation(lib):
     rnd = lambda x: (x + 255) // 256 * 256
     ws = lambda p: lib.bsa_decode_step_workspace_bytes(ctypes.byref(p))

@@ -989,3 +989,103 @@ def test_lsa_tree_beam_keeps_the_best_nodes():
     tail = set(range(n_elig * seg, c - 2 + 1))
     chosen = set(A.tolist()) - {0, c - 1, c}
     assert chosen == want | tail
+
+
+# ---------------------------------------------------------------------------------------------
+# decode-time maintenance: tail refresh of the landmarks, incremental LSA index
+# ---------------------------------------------------------------------------------------------
+
+def _brute_block_mean_bf16(rows):
+    """Mean of a list of key rows by plain Python (math.fsum per coordinate), rounded to bf16
+    by torch's own cast."""
+    import math
+    import torch
+    n = len(rows)
+    mean = [math.fsum(r[d] for r in rows) / n for d in range(len(rows[0]))]
+    return torch.tensor(mean, dtype=torch.float64).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def test_landmark_refresh_over_appends_equals_brute_force():
+    """Tokens appended in chunks of 1..70: after each append the landmarks refreshed over the
+    last n_new tokens equal the brute-force block means of everything so far, and the blocks
+    before the refreshed ones are left exactly as they were."""
+    r = _rng(960)
+    D = 3
+    k_all = r.standard_normal((1, 2, 330, D)) * 4
+    k_all = O.round_to_dtype(k_all, "bf16")
+    lm = np.zeros((1, 2, 0, D))
+    T = 0
+    for n_new in (1, 1, 5, 64, 3, 70, 1, 63, 2, 64, 56):
+        T += n_new
+        k = k_all[:, :, :T]
+        nb = O.n_blocks(T)
+        grown = np.full((1, 2, nb, D), np.nan)
+        grown[:, :, :lm.shape[2]] = lm
+        upd = O.update_landmarks(grown, k, n_new, "bf16")
+        first = (T - n_new) // 64
+        assert np.array_equal(upd[:, :, :first], grown[:, :, :first])
+        for h in range(2):
+            for j in range(nb):
+                rows = [list(k[0, h, t]) for t in range(64 * j, min(64 * j + 64, T))]
+                assert np.array_equal(upd[0, h, j], _brute_block_mean_bf16(rows)), (T, h, j)
+        lm = upd
+    assert T == 330
+
+
+def test_paged_landmark_refresh_per_sequence_equals_brute_force():
+    """Three sequences in shuffled pages grow one token per step for 130 steps: refreshing the
+    block of each sequence's new token keeps every landmark equal to the brute-force means of
+    that sequence's tokens; blocks past a sequence's end stay as they were (zero)."""
+    r = _rng(961)
+    D, Hkv = 2, 2
+    final = [70, 130, 200]
+    nblk = [O.n_blocks(L) for L in final]
+    NB = max(nblk)
+    n_pages = sum(nblk) + 2
+    pool = r.standard_normal((n_pages, Hkv, 64, D))
+    perm = r.permutation(n_pages)
+    table = np.zeros((3, NB), dtype=np.int64)
+    nxt = 0
+    for b in range(3):
+        for j in range(nblk[b]):
+            table[b, j] = perm[nxt]
+            nxt += 1
+    lens = [L - 130 if L > 130 else 0 for L in final]
+    lm = np.zeros((3, Hkv, NB, D))
+    lm[2:] = O.update_landmarks_paged(lm[2:], pool, table[2:], lens[2:], 10 ** 6, "f32")
+    for step in range(130):
+        for b in range(3):
+            if lens[b] < final[b]:
+                lens[b] += 1
+        active = [b for b in range(3) if lens[b] > 0]
+        sub = O.update_landmarks_paged(lm[active], pool, table[active], [lens[b] for b in active],
+                                       1, "f32")
+        lm[active] = sub
+    for b in range(3):
+        L = lens[b]
+        for h in range(Hkv):
+            for j in range(NB):
+                if j * 64 >= L:
+                    assert not lm[b, h, j].any()
+                    continue
+                rows = [pool[table[b, j], h, t] for t in range(min(64, L - 64 * j))]
+                want = O.round_to_dtype(np.mean(np.stack(rows), axis=0), "f32")
+                np.testing.assert_array_equal(lm[b, h, j], want)
+
+
+def test_lsa_update_index_keeps_old_segments_and_matches_full_build():
+    """Segments clustered as they complete: the updated index equals the index built on the
+    whole landmarks, and the earlier segments' entries are the very objects kept before."""
+    r = _rng(962)
+    L = r.standard_normal((64 * 5 + 10, 6))
+    old = O.lsa_index(L[:64 * 2 + 30], seg_blocks=64, n_clusters=16)
+    assert len(old) == 2
+    new = O.lsa_update_index(old, L, 2, seg_blocks=64, n_clusters=16)
+    full = O.lsa_index(L, seg_blocks=64, n_clusters=16)
+    assert len(new) == len(full) == 5
+    assert new[0] is old[0] and new[1] is old[1]
+    for (ma, ca, ga), (mb, cb, gb) in zip(new, full):
+        assert [m.tolist() for m in ma] == [m.tolist() for m in mb]
+        np.testing.assert_array_equal(ca, cb)
+        assert ga == gb
+
