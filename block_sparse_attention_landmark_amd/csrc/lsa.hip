@@ -25,6 +25,7 @@
 
 #include "bsa_common.hpp"
 #include "bsa_internal.hpp"
+#include "select_common.hpp"
 
 namespace bsa {
 
@@ -221,7 +222,11 @@ __device__ __forceinline__ void lsa_bitonic(uint64_t* key, int* pay, int m) {
 }
 
 // UCAP / KCAP: the units and chosen blocks one row can hold (LDS is sized by them, so a small
-// variant lets several rows share a CU)
+// variant lets several rows share a CU).  The units are laid out in id order (the clusters of
+// each segment by id, segments ascending, then the single blocks ascending), so the shared radix
+// top-K -- which takes the lower index first among equal scores -- ranks them by (score
+// descending, id ascending); only the min(K, units) best units are then sorted, since every unit
+// with a candidate block contributes at least one block.
 template <int D, typename TIN, int UCAP, int KCAP>
 __global__ __launch_bounds__(256) void lsa_select_kernel(
     const float* __restrict__ qbar, const TIN* __restrict__ q, const TIN* __restrict__ lm,
@@ -230,12 +235,19 @@ __global__ __launch_bounds__(256) void lsa_select_kernel(
     int Hkv, int G, int NB, int NS, int SEG, int NC, int R, int c_dec, int topk, int n_sink,
     int n_local, int NA) {
   __shared__ float qv[D];
-  // sort key: (order-preserving key of the score, inverted) << 32 | unit id; payload: unit index
-  // | candidate blocks << 16 (a unit's score is recovered from its key)
-  __shared__ uint64_t skey[UCAP];
-  __shared__ int spay[UCAP];
+  __shared__ float uscore[UCAP];     // unit score; -inf for a unit without candidate blocks
+  __shared__ int usize[UCAP];        // candidate blocks of the unit
+  __shared__ int32_t tsel[KCAP + 1]; // the best units (ascending unit index), then a dummy entry
+  __shared__ float tsc[KCAP + 1];
+  // sort space: (order-preserving key of the score, inverted) << 32 | unit index, payload = the
+  // unit; reused for the chosen blocks
+  __shared__ uint64_t skey[KCAP];
+  __shared__ int spay[KCAP];
   __shared__ int ch_blk[KCAP];
   __shared__ float ch_sc[KCAP];
+  __shared__ int hist[kTopkHistWords];
+  __shared__ int sbuf[4];
+  __shared__ int sh[2];
   __shared__ int wsum[4];
   const int row = blockIdx.x, bg = blockIdx.y;
   const int b = bg / Hkv, g = bg % Hkv;
@@ -266,8 +278,6 @@ __global__ __launch_bounds__(256) void lsa_select_kernel(
   const int single_lo = max(n_sink, n_elig * SEG);
   const int n_single = max(0, last - single_lo + 1);
   const int n_units = n_elig * NC + n_single;
-  int m = 1;
-  while (m < n_units) m <<= 1;
   // unit u: a cluster (u < n_elig * NC) or the single block single_lo + u - n_elig * NC; its
   // score is a dot product over D spread on LPU lanes (8 elements each), UPW units per wave
   constexpr int LPU = D / 8;
@@ -276,18 +286,20 @@ __global__ __launch_bounds__(256) void lsa_select_kernel(
   float qf[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) qf[e] = qv[sub * 8 + e];
-  for (int u0 = w * UPW; u0 < m; u0 += 4 * UPW) {
+  for (int u0 = w * UPW; u0 < n_units; u0 += 4 * UPW) {
     const int u = u0 + uw;
     float part = 0.0f;
     int size = 0;
-    uint32_t id = 0;
     if (u < n_elig * NC) {
       const int sg = u / NC, r = u % NC;
       const size_t sb = (size_t)bg * NS + sg;
       const int o0 = offsets[sb * (NC + 1) + r], o1 = offsets[sb * (NC + 1) + r + 1];
-      const int32_t* mem = members + sb * SEG;
-      for (int i = o0; i < o1; ++i) size += mem[i] >= n_sink;
-      id = (uint32_t)mem[o0];
+      if (sg * SEG < n_sink) {                  // a segment holding sink blocks: count members
+        const int32_t* mem = members + sb * SEG;
+        for (int i = o0; i < o1; ++i) size += mem[i] >= n_sink;
+      } else {
+        size = o1 - o0;                         // every member is a candidate
+      }
       const f32x4* ctr = reinterpret_cast<const f32x4*>(centres + (sb * NC + r) * D + sub * 8);
       const f32x4 c0 = ctr[0], c1 = ctr[1];
 #pragma unroll
@@ -298,24 +310,40 @@ __global__ __launch_bounds__(256) void lsa_select_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) part = fmaf(qf[e], (float)lrow[e], part);
       size = 1;
-      id = (uint32_t)j;
     }
 #pragma unroll
     for (int o = LPU / 2; o > 0; o >>= 1) part += __shfl_xor(part, o, kWave);
-    if (sub == 0 && u < m) {
-      uint64_t key = ~(uint64_t)0;
-      if (u < n_units && size > 0) key = ((uint64_t)(~float_key(part)) << 32) | id;
-      skey[u] = key;
-      spay[u] = u | (size << 16);
+    if (sub == 0 && u < n_units) {
+      uscore[u] = size > 0 ? part : -INFINITY;
+      usize[u] = size;
     }
   }
   __syncthreads();
-  lsa_bitonic(skey, spay, m);
+  // the best min(topk, units) units, ascending unit index (ties: the lower index)
+  const int KU = min(topk, n_units);
+  topk_select<256>([&](int u) { return u < n_units ? uscore[u] : 0.0f; },
+                   [&](int i) { return float_key(uscore[i]); }, n_units, KU, 0, 1, KU + 1, tsel,
+                   tsc, hist, sbuf, sh);
+  __syncthreads();
+  // those units in selection order: score descending, unit index ascending
+  int m = 1;
+  while (m < KU) m <<= 1;
+  for (int i = tid; i < m; i += 256) {
+    uint64_t key = ~(uint64_t)0;
+    int u = 0;
+    if (i < KU) {
+      u = tsel[i];
+      key = ((uint64_t)(~float_key(uscore[u])) << 32) | (uint32_t)u;
+    }
+    skey[i] = key;
+    spay[i] = u;
+  }
+  __syncthreads();
+  if (KU > 1) lsa_bitonic(skey, spay, m);
   // blocks taken from each unit in sorted order: exclusive prefix of sizes, capped at K
   const int per = (m + 255) / 256;
   int local_sum = 0;
-  for (int i = tid * per; i < min(m, (tid + 1) * per); ++i)
-    if (skey[i] != ~(uint64_t)0) local_sum += spay[i] >> 16;
+  for (int i = tid * per; i < min(KU, (tid + 1) * per); ++i) local_sum += usize[spay[i]];
   int incl = local_sum;
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
@@ -328,12 +356,11 @@ __global__ __launch_bounds__(256) void lsa_select_kernel(
   for (int v = 0; v < w; ++v) base += wsum[v];
   const int total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
   const int K = min(topk, total);
-  for (int i = tid * per; i < min(m, (tid + 1) * per); ++i) {
-    if (skey[i] == ~(uint64_t)0) continue;
-    const int u = spay[i] & 0xffff;
-    const int size = spay[i] >> 16;
-    const float uscore = key_float(~(uint32_t)(skey[i] >> 32));
-    if (base < K) {
+  for (int i = tid * per; i < min(KU, (tid + 1) * per); ++i) {
+    const int u = spay[i];
+    const int size = usize[u];
+    const float us = uscore[u];
+    if (base < K && size > 0) {
       const int take = min(size, K - base);
       if (u < n_elig * NC) {
         const int sg = u / NC, r = u % NC;
@@ -344,12 +371,12 @@ __global__ __launch_bounds__(256) void lsa_select_kernel(
         for (int x = o0; x < o1 && n < take; ++x)
           if (mem[x] >= n_sink) {
             ch_blk[base + n] = mem[x];
-            ch_sc[base + n] = uscore;
+            ch_sc[base + n] = us;
             ++n;
           }
       } else {
         ch_blk[base] = single_lo + (u - n_elig * NC);
-        ch_sc[base] = uscore;
+        ch_sc[base] = us;
       }
     }
     base += size;
