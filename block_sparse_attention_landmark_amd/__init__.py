@@ -98,6 +98,8 @@ def _open(path: str):
     lib.bsa_select_workspace_bytes.restype = ctypes.c_size_t
     lib.bsa_select_topk.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.bsa_select_topk.restype = st
+    lib.bsa_select_topk_fused.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.bsa_select_topk_fused.restype = st
     lib.bsa_attend_prefill.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.bsa_attend_prefill.restype = st
     lib.bsa_decode_workspace_bytes.argtypes = [P]
@@ -248,11 +250,13 @@ def decode_workspace_bytes(p: Params) -> int:
 
 def select_topk(q: torch.Tensor, lm: torch.Tensor, *, topk: int, seq_k: int | None = None,
                 n_sink: int = 1, n_local: int = 2, ws: torch.Tensor | None = None,
-                idx: torch.Tensor | None = None, sc: torch.Tensor | None = None):
+                idx: torch.Tensor | None = None, sc: torch.Tensor | None = None,
+                one_pass: bool = False):
     """Attended block sets.
 
     Prefill: q [B,Hq,T,D], lm [B,Hkv,ceil(T/64),D] -> idx, sc [B,Hkv,ceil(T/64),NA].
     Decode:  q [B,Hq,1,D], lm of the seq_k cached keys -> idx, sc [B,Hkv,1,NA].
+    one_pass=True calls bsa_select_topk_fused (bf16 prefill, topk <= 32) at any length.
     """
     lib = load_library()
     _need(q, "q", ndim=4)
@@ -276,9 +280,9 @@ def select_topk(q: torch.Tensor, lm: torch.Tensor, *, topk: int, seq_k: int | No
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     _need(ws, "ws", dtype=torch.uint8, ndim=1)
     _on_device(q, lm=lm, idx=idx, sc=sc, ws=ws)
-    _check("bsa_select_topk", lib.bsa_select_topk(ctypes.byref(p), _ptr(q), _ptr(lm), _ptr(idx),
-                                                  _ptr(sc), _ptr(ws), ws.numel(),
-                                                  _stream(q.device)))
+    name = "bsa_select_topk_fused" if one_pass else "bsa_select_topk"
+    _check(name, getattr(lib, name)(ctypes.byref(p), _ptr(q), _ptr(lm), _ptr(idx), _ptr(sc),
+                                    _ptr(ws), ws.numel(), _stream(q.device)))
     return idx, sc
 
 

@@ -49,6 +49,12 @@ hipError_t launch_pool_landmarks(const Shape& s, const void* k, void* lm, hipStr
 hipError_t launch_selector_vectors(const Shape& s, const void* q, float* qbar, hipStream_t st);
 hipError_t launch_block_scores(const Shape& s, const float* qbar, const void* lm, float* scores,
                                hipStream_t st);
+// Prefill rows of bf16 landmarks with K <= 32: scores and top-K in one kernel, no score workspace
+// (select_fused_ok: the kernel applies; select_fused: bsa_select_topk uses it).
+bool select_fused_ok(const Shape& s);
+bool select_fused(const Shape& s);
+hipError_t launch_select_fused(const Shape& s, const float* qbar, const void* lm, int32_t* idx,
+                               float* sc, hipStream_t st);
 hipError_t launch_topk(const Shape& s, const float* scores, int32_t* idx, float* sc,
                        hipStream_t st);
 // decode with bf16 landmarks: selector vector, scores and top-K in one kernel

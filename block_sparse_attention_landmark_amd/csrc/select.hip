@@ -26,7 +26,9 @@ __host__ __device__ inline size_t tri(size_t n) { return n * (n + 1) / 2; }
 size_t select_ws_qbar_bytes(const Shape& s) {
   return align256((size_t)s.B * s.Hkv * s.R * s.D * sizeof(float));
 }
+bool select_fused(const Shape& s);
 size_t select_ws_scores_bytes(const Shape& s) {
+  if (select_fused(s)) return 0;                 // scores never leave the selection kernel
   const size_t per = s.decode ? (size_t)s.NB : tri((size_t)s.R);
   return align256((size_t)s.B * s.Hkv * per * sizeof(float));
 }
@@ -292,6 +294,366 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
       [&](int i) { return cached ? skeys[i] : float_key(srow[n_sink + i]); }, c, topk, n_sink,
       n_local, NA, idx + ((size_t)bg * R + r) * NA, sc + ((size_t)bg * R + r) * NA, hist, sbuf,
       sh);
+}
+
+// ---------------------------------------------------------------------------------------------
+// prefill selection in one pass (bf16 landmarks, K <= 32): scores and top-K without the score
+// workspace.  One workgroup per (tile row of 64 query blocks, batch and kv group); its four
+// waves split every 64 x 64 score tile as score_strip_kernel does (same products in the same
+// order, so the same scores) and sweep the tile row's column tiles left to right.  Each (row,
+// column half) keeps in LDS a list of candidates, appended in block order, and a threshold key:
+// a candidate is appended only if its key is above the threshold, the K-th best key among the
+// candidates that column half has already seen.  That drops only candidates with K better ones
+// seen before them (on equal keys the earlier, lower block wins), which cannot be chosen.  A list
+// that could overflow at the next tile is cut to its K best and the threshold raised to its K-th
+// key.  At the end the two halves' lists of a row are merged in block order and cut to K.  The
+// forced entries (sinks, local window) and the rows whose candidates are all taken are written
+// while sweeping, the padding at the end: the same attended sets as topk_select writes.
+// ---------------------------------------------------------------------------------------------
+constexpr int kFusedCap = 96;        // list slots per (row, column half); a tile appends <= 32
+constexpr int kFusedMaxK = 32;
+
+// x from the lane jj apart within each group of 32 lanes (jj = 1, 2, 4, 8, 16)
+__device__ __forceinline__ uint32_t lane_xor32(uint32_t x, int jj) {
+  const int v = (int)x;
+  switch (jj) {
+    case 1: return (uint32_t)__builtin_amdgcn_mov_dpp(v, 0xB1, 0xf, 0xf, false);   // quad_perm 1,0,3,2
+    case 2: return (uint32_t)__builtin_amdgcn_mov_dpp(v, 0x4E, 0xf, 0xf, false);   // quad_perm 2,3,0,1
+    case 4: return (uint32_t)__builtin_amdgcn_ds_swizzle(v, 0x1F | (4 << 10));
+    case 8: return (uint32_t)__builtin_amdgcn_ds_swizzle(v, 0x1F | (8 << 10));
+    default: return (uint32_t)__builtin_amdgcn_ds_swizzle(v, 0x1F | (16 << 10));
+  }
+}
+
+// Cut a list of n <= 128 entries (scores ls[0..n), blocks lj[0..n)) to its K best by (key
+// descending, slot ascending), keeping their slot order; returns the K-th best key.  One list per
+// half-wave (l = lane % 32): both halves of a wave call it together, each with its own list, n
+// and K (1 <= K <= 32).  A list of n <= K entries is left as it is (the return value is then
+// meaningless).  Slot order is block order for every list cut here.
+__device__ __forceinline__ uint32_t cut_list(float* ls, uint16_t* lj, int n, int K, int l) {
+  float v[4];
+  int jv[4];
+  uint32_t key[4], x[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int slot = 32 * s + l;
+    const bool in = slot < n;
+    v[s] = in ? ls[slot] : 0.0f;
+    jv[s] = in ? (int)lj[slot] : 0;
+    key[s] = in ? float_key(v[s]) : 0u;    // empty slots sort last (no score has key 0)
+    x[s] = key[s];
+  }
+  // bitonic sort of the 128 keys, descending; element e = 32 s + l
+#pragma unroll
+  for (int k = 2; k <= 128; k <<= 1) {
+#pragma unroll
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      if (jj >= 32) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int t = s ^ (jj >> 5);
+          if (t > s) {
+            const bool desc = ((32 * s + l) & k) == 0;
+            const uint32_t mx = max(x[s], x[t]), mn = min(x[s], x[t]);
+            x[s] = desc ? mx : mn;
+            x[t] = desc ? mn : mx;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const uint32_t y = lane_xor32(x[s], jj);
+          const bool desc = ((32 * s + l) & k) == 0;
+          const bool lower = (l & jj) == 0;
+          x[s] = (lower == desc) ? max(x[s], y) : min(x[s], y);
+        }
+      }
+    }
+  }
+  const int lane = threadIdx.x % kWave;
+  const uint32_t tau = (uint32_t)__shfl((int)x[0], (lane & 32) + K - 1, kWave);
+  if (n <= K) return tau;
+  // keep every key above tau and the first (K - #above) equal to it, in slot order
+  const uint32_t below = (1u << l) - 1u;
+  const int hshift = lane & 32;
+  int n_gt = 0;
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    n_gt += __popcll(__ballot(key[s] > tau) >> hshift & 0xffffffffull);
+  const int need_eq = K - n_gt;
+  int eq_before = 0, pos_base = 0;
+  bool keep[4];
+  int pos[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const bool eq = key[s] == tau && 32 * s + l < n;
+    const uint32_t eqm = (uint32_t)(__ballot(eq) >> hshift);
+    const int eq_rank = eq_before + __popc(eqm & below);
+    keep[s] = key[s] > tau || (eq && eq_rank < need_eq);
+    eq_before += __popc(eqm);
+    const uint32_t km = (uint32_t)(__ballot(keep[s]) >> hshift);
+    pos[s] = pos_base + __popc(km & below);
+    pos_base += __popc(km);
+  }
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    if (keep[s]) {
+      ls[pos[s]] = v[s];
+      lj[pos[s]] = (uint16_t)jv[s];
+    }
+  return tau;
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void select_fused_kernel(
+    const float* __restrict__ qbar, const bf16* __restrict__ lm, int32_t* __restrict__ idx,
+    float* __restrict__ sc, int R, int NB, int topk, int n_sink, int n_local, int NA) {
+  constexpr int CAP = kFusedCap;
+  __shared__ float ls[64][2 * CAP];          // per row: column half h in slots h*CAP ..
+  __shared__ uint16_t lj[64][2 * CAP];
+  __shared__ int lcnt[64][2];
+  __shared__ float ltau[64][2];
+  // Workgroups are dealt round-robin over the 8 XCDs; with a multiple of 8 (batch, kv group)
+  // pairs, XCD x takes the pairs x, x + 8, .. so that each XCD's L2 serves one pair's landmarks
+  // at a time.  Heavy (long) tile rows first.
+  const int nT = (R + 63) / 64;
+  const int n_bg = (int)gridDim.y;
+  const int lin = (int)(blockIdx.x + gridDim.x * blockIdx.y);
+  int bg, tr;
+  if (n_bg % 8 == 0) {
+    const int k = lin / 8;
+    bg = (k / nT) * 8 + lin % 8;
+    tr = k % nT;
+  } else {
+    bg = lin / nT;
+    tr = lin % nT;
+  }
+  const int ti = nT - 1 - tr;
+  const int w = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int half = lane / 32;
+  const int l32 = lane % 32;
+  const int rh = w / 2, ch = w % 2;
+  const int row0 = ti * 64 + rh * 32;
+  const int last_row = min(row0 + 31, R - 1);
+  int32_t* oidx = idx + (size_t)bg * R * NA;
+  float* osc = sc + (size_t)bg * R * NA;
+  auto lrow = [&](int i) { return rh * 32 + 8 * (i / 4) + 4 * half + (i % 4); };
+
+  // threshold score per (row, column half), uniform in a half-wave: a candidate is appended only
+  // if its score is above it (on scores, float order is the key order)
+  f32x16 tau;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) tau[i] = -INFINITY;
+  if (l32 == 0) {                              // each wave owns the counts of its lists
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      lcnt[lrow(i)][ch] = 0;
+      ltau[lrow(i)][ch] = -INFINITY;
+    }
+  }
+
+  if (row0 < R) {
+    const int r = row0 + l32;
+    const float* qrow = qbar + ((size_t)bg * R + min(r, R - 1)) * D;
+    bf16x8 hi[D / 16], mid[D / 16], lo[D / 16];
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+      const int d0 = 16 * st + 8 * half;
+      f32x4 x0 = *reinterpret_cast<const f32x4*>(qrow + d0);
+      f32x4 x1 = *reinterpret_cast<const f32x4*>(qrow + d0 + 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float x = (e < 4) ? x0[e] : x1[e - 4];
+        if (r >= R) x = 0.0f;
+        const bf16 h = f2bf(x);
+        const float r1 = x - bf2f(h);        // exact in float32
+        const bf16 m = f2bf(r1);
+        hi[st][e] = h;
+        mid[st][e] = m;
+        lo[st][e] = f2bf(r1 - bf2f(m));      // the remaining <= 8 significant bits
+      }
+    }
+    auto load_l = [&](int tj, bf16x8* bl) {
+      const int j = tj * 64 + ch * 32 + l32;
+      const bf16* lrow_p = lm + ((size_t)bg * NB + min(j, NB - 1)) * D;
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st) {
+        bl[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(lrow_p + 16 * st + 8 * half));
+        if (j >= NB) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) bl[st][e] = f2bf(0.0f);
+        }
+      }
+    };
+    // the wave's rows take every candidate of an interior tile and keep K = topk < n
+    const bool rows_full = topk > 0 && row0 >= topk + n_local + n_sink && row0 + 31 < R;
+    const uint32_t below = (1u << l32) - 1u;
+    // column tile tj from the landmark fragments in cur, the next tile's loading into nxt;
+    // false past the wave's last tile
+    auto tile = [&](int tj, bf16x8* cur, bf16x8* nxt) -> bool {
+      const int col0 = tj * 64 + ch * 32;
+      if (tj > ti || col0 > last_row || col0 >= NB) return false;
+      const int j = col0 + l32;
+      if (tj + 1 <= ti) load_l(tj + 1, nxt);
+      f32x16 acc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st) {
+        acc = mfma32(hi[st], cur[st], acc);
+        acc = mfma32(mid[st], cur[st], acc);
+        acc = mfma32(lo[st], cur[st], acc);
+      }
+      uint32_t pbits = 0u;                     // bit i: append acc[i]
+      if (rows_full && col0 >= n_sink && col0 + 31 <= row0 - n_local) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pbits |= acc[i] > tau[i] ? (1u << i) : 0u;
+      } else {                                 // tiles holding forced entries or row ends
+#pragma unroll 1
+        for (int i = 0; i < 16; ++i) {
+          const int rr = row0 + 8 * (i / 4) + 4 * half + (i % 4);
+          if (rr >= R || j > rr || j >= NB) continue;
+          const float sv = acc[i];
+          const int n_sink_eff = min(n_sink, rr + 1);
+          const int n = max(0, rr - n_local - n_sink + 1);
+          const int K = min(topk, n);
+          const int loc_beg = max(n_sink, rr - n_local + 1);
+          int opos = -1;
+          if (j < n_sink_eff) opos = j;
+          else if (j >= loc_beg) opos = n_sink_eff + K + (j - loc_beg);
+          else if (K == n) opos = n_sink_eff + (j - n_sink);
+          else if (K > 0 && sv > tau[i]) pbits |= 1u << i;
+          if (opos >= 0) {
+            oidx[(size_t)rr * NA + opos] = j;
+            osc[(size_t)rr * NA + opos] = sv;
+          }
+        }
+      }
+      if (__any(pbits != 0u)) {
+        uint32_t cutm = 0u;                    // lists (bit i) that the next tile could overflow
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const bool pi = (pbits >> i) & 1u;
+          const uint32_t m = (uint32_t)(__ballot(pi) >> (32 * half));
+          if (__any(m != 0u)) {
+            int* cp = &lcnt[lrow(i)][ch];
+            const int c0 = *cp;
+            if (pi) {
+              const int slot = ch * CAP + c0 + __popc(m & below);
+              ls[lrow(i)][slot] = acc[i];
+              lj[lrow(i)][slot] = (uint16_t)j;
+            }
+            const int c1 = c0 + __popc(m);
+            if (l32 == 0) *cp = c1;
+            cutm |= (c1 > CAP - 32) ? (1u << i) : 0u;
+          }
+        }
+        uint32_t cuts = (uint32_t)(__builtin_amdgcn_readlane((int)cutm, 0) |
+                                   __builtin_amdgcn_readlane((int)cutm, 32));
+        if (cuts != 0u) {
+#pragma unroll 1
+          for (; cuts != 0u; cuts &= cuts - 1u) {
+            const int i = __builtin_ctz(cuts);
+            const int lr = rh * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+            const int rr = ti * 64 + lr;
+            const int K = max(1, min(topk, max(0, rr - n_local - n_sink + 1)));
+            const int c1 = lcnt[lr][ch];
+            const uint32_t t = cut_list(&ls[lr][ch * CAP], &lj[lr][ch * CAP], c1, K, l32);
+            if (l32 == 0 && c1 > K) {
+              lcnt[lr][ch] = K;
+              ltau[lr][ch] = key_float(t);
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < 16; ++i) tau[i] = ltau[lrow(i)][ch];
+        }
+      }
+      return true;
+    };
+    bf16x8 bl[D / 16], bn[D / 16];
+    load_l(0, bl);
+    for (int tj = 0;; tj += 2) {
+      if (!tile(tj, bl, bn)) break;
+      if (!tile(tj + 1, bn, bl)) break;
+    }
+  }
+  __syncthreads();
+
+  // per row (one half-wave each): merge the two lists in block order, cut to K, write the
+  // chosen entries and the padding
+  const int hw = w * 2 + half;
+  for (int r = hw; r < 64; r += 8) {
+    const int rr = ti * 64 + r;
+    if (rr >= R) break;
+    const int n_sink_eff = min(n_sink, rr + 1);
+    const int n = max(0, rr - n_local - n_sink + 1);
+    const int K = min(topk, n);
+    const int loc_beg = max(n_sink, rr - n_local + 1);
+    const int n_loc = max(0, rr - loc_beg + 1);
+    for (int p = n_sink_eff + K + n_loc + l32; p < NA; p += 32) {
+      oidx[(size_t)rr * NA + p] = -1;
+      osc[(size_t)rr * NA + p] = 0.0f;
+    }
+    if (K == 0 || K == n) continue;
+    const int a = lcnt[r][0], b = lcnt[r][1];
+    // list h holds blocks 64t + 32h + [0, 32) of tiles t in ascending order: an entry of list 0
+    // from tile t follows the entries of list 1 from tiles < t, one of list 1 those of list 0
+    // from tiles <= t
+    float v[4];
+    int jv[4], dst[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int h = u / 2;                      // u = 0, 1: list 0; 2, 3: list 1
+      const int p = (u % 2) * 32 + l32;
+      const int cn = h == 0 ? a : b, co = h == 0 ? b : a;
+      dst[u] = -1;
+      if (p < cn) {
+        v[u] = ls[r][h * CAP + p];
+        jv[u] = lj[r][h * CAP + p];
+        const int t = jv[u] / 64;
+        // entries of the other list with tile < t (list 0 asking) or <= t (list 1 asking)
+        int lo_i = 0, hi_i = co;
+        while (lo_i < hi_i) {
+          const int mid_i = (lo_i + hi_i) / 2;
+          const int to = lj[r][(1 - h) * CAP + mid_i] / 64;
+          if (h == 0 ? to < t : to <= t) lo_i = mid_i + 1;
+          else hi_i = mid_i;
+        }
+        dst[u] = p + lo_i;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (dst[u] >= 0) {
+        ls[r][dst[u]] = v[u];
+        lj[r][dst[u]] = (uint16_t)jv[u];
+      }
+    cut_list(&ls[r][0], &lj[r][0], a + b, K, l32);
+    if (l32 < K) {
+      oidx[(size_t)rr * NA + n_sink_eff + l32] = lj[r][l32];
+      osc[(size_t)rr * NA + n_sink_eff + l32] = ls[r][l32];
+    }
+  }
+}
+
+bool select_fused_ok(const Shape& s) {
+  return !s.decode && s.bf16 && s.topk <= kFusedMaxK && s.NB <= 65535 && s.R == s.NB;
+}
+// bsa_select_topk takes the one-pass kernel where it wins: rows of more than 4096 blocks (at 2048
+// blocks a tile row is too little work per workgroup and the two-kernel path is faster)
+bool select_fused(const Shape& s) { return select_fused_ok(s) && s.NB > 4096; }
+
+hipError_t launch_select_fused(const Shape& s, const float* qbar, const void* lm, int32_t* idx,
+                               float* sc, hipStream_t st) {
+  const dim3 grid((s.R + 63) / 64, s.B * s.Hkv);
+  if (s.D == 128)
+    hipLaunchKernelGGL(select_fused_kernel<128>, grid, dim3(256), 0, st, qbar, (const bf16*)lm,
+                       idx, sc, s.R, s.NB, s.topk, s.n_sink, s.n_local, s.NA);
+  else
+    hipLaunchKernelGGL(select_fused_kernel<64>, grid, dim3(256), 0, st, qbar, (const bf16*)lm,
+                       idx, sc, s.R, s.NB, s.topk, s.n_sink, s.n_local, s.NA);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------------------------

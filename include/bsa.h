@@ -108,10 +108,28 @@ size_t bsa_select_workspace_bytes(const bsa_params_t* params);
  *   lm   [B,Hkv,NB,D] landmarks of the Tk keys (bsa_pool_landmarks)
  *   idx  [B,Hkv,R,NA] int32 output, sc [B,Hkv,R,NA] float32 output
  *   ws   device workspace of at least bsa_select_workspace_bytes(params) bytes (the selector
- *        vectors and the score rows); contents on entry are ignored.
+ *        vectors; plus the float32 score rows, except where the one-pass selection below runs:
+ *        bf16 prefill rows with topk <= 32 and more than 4096 blocks); contents on entry are
+ *        ignored.
  */
 bsa_status_t bsa_select_topk(const bsa_params_t* params, const void* q, const void* lm,
                              int32_t* idx, float* sc, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The same selection as bsa_select_topk (same idx and sc, bit for bit) by one kernel that
+ * scores each tile row of the lower triangle and keeps, per row, only candidates that can still
+ * be among the K best, so no score rows are written (LSA page, "The index stops scanning the
+ * whole context", paragraph 2: the candidate search is what grows with the context; SAS page,
+ * summary paragraph 1: hard top-K).  bsa_select_topk uses it by itself for rows of more than
+ * 4096 blocks; this entry point takes it at any length.
+ *   Applies to prefill (seq_q == seq_k) with dtype BSA_BF16, topk <= 32 and at most 65535
+ *   blocks; otherwise BSA_ERR_UNSUPPORTED.
+ *   ws   device workspace of at least bsa_select_workspace_bytes(params) bytes (only the
+ *        selector vectors are used); contents on entry are ignored.
+ */
+bsa_status_t bsa_select_topk_fused(const bsa_params_t* params, const void* q, const void* lm,
+                                   int32_t* idx, float* sc, void* ws, size_t ws_bytes,
+                                   void* stream);
 
 /*
  * Prefill attention (SAS page, summary paragraph 4: blockwise, FlashAttention-style, without

@@ -142,6 +142,23 @@ def test_select_validation(lib):
     assert lib.bsa_select_workspace_bytes(ctypes.byref(bad)) == 0
 
 
+def test_select_one_pass_validation(lib):
+    def sel(p, ws=FAKE, nbytes=1 << 40, q=FAKE, idx=FAKE):
+        return lib.bsa_select_topk_fused(ctypes.byref(p), q, FAKE, idx, FAKE, ws, nbytes, None)
+
+    assert sel(_p(topk=33)) == UNSUP                              # K > 32
+    assert sel(_p(dtype=bsa.torch.float32)) == UNSUP              # float32 landmarks
+    assert sel(_p(seq_q=1, seq_k=640)) == UNSUP                   # a decode row
+    assert sel(_p(topk=-1)) == SHAPE
+    assert sel(_p(), q=None) == NULL
+    assert sel(_p(), idx=None) == NULL
+    p = _p(B=2, Hq=8, Hkv=2, seq_q=64 * 10, seq_k=64 * 10)
+    need = 2 * 2 * 10 * 128 * 4                                   # the selector vectors alone
+    assert sel(p, nbytes=need - 1) == WS
+    assert sel(p, ws=None) == WS
+    assert sel(p, ws=ctypes.c_void_p((1 << 20) + 16)) == ALIGN
+
+
 def test_workspace_sizes_follow_the_shapes(lib):
     # prefill: float32 selector vectors + lower-triangular float32 score rows
     p = _p(B=2, Hq=8, Hkv=2, seq_q=64 * 10, seq_k=64 * 10)
@@ -149,6 +166,16 @@ def test_workspace_sizes_follow_the_shapes(lib):
     scores = 2 * 2 * (10 * 11 // 2) * 4
     rnd = lambda x: (x + 255) // 256 * 256
     assert lib.bsa_select_workspace_bytes(ctypes.byref(p)) == rnd(qbar) + rnd(scores)
+    # rows of more than 4096 blocks, bf16, K <= 32: the one-pass selection, selector vectors only;
+    # K > 32 or float32 landmarks keep the score rows
+    nb = 4097
+    long_kw = dict(B=1, Hq=4, Hkv=2, seq_q=64 * nb, seq_k=64 * nb)
+    qbar_l = 2 * nb * 128 * 4
+    scores_l = 2 * (nb * (nb + 1) // 2) * 4
+    assert lib.bsa_select_workspace_bytes(ctypes.byref(_p(**long_kw, topk=32))) == rnd(qbar_l)
+    assert lib.bsa_select_workspace_bytes(ctypes.byref(_p(**long_kw, topk=33))) == rnd(qbar_l) + rnd(scores_l)
+    assert (lib.bsa_select_workspace_bytes(ctypes.byref(_p(**long_kw, topk=8, dtype=bsa.torch.float32)))
+            == rnd(qbar_l) + rnd(scores_l))
     d = _p(B=3, Hq=16, Hkv=2, seq_q=1, seq_k=64 * 9 + 5, topk=4)
     assert lib.bsa_select_workspace_bytes(ctypes.byref(d)) == rnd(3 * 2 * 128 * 4) + rnd(3 * 2 * 10 * 4)
     assert lib.bsa_decode_workspace_bytes(ctypes.byref(d)) > 0
