@@ -183,19 +183,19 @@ bsa_status_t bsa_select_topk(const bsa_params_t* params, const void* q, const vo
   BSA_TRY(check_ptr(idx, "idx"));
   BSA_TRY(check_ptr(sc, "sc"));
   const size_t need = bsa::select_ws_bytes(s);
-  if (ws == nullptr || ws_bytes < need)
-    return fail(BSA_ERR_WORKSPACE, "select workspace needs %zu bytes (got %zu%s)", need, ws_bytes,
-                ws == nullptr ? ", NULL pointer" : "");
-  if (((uintptr_t)ws & 255u) != 0) return fail(BSA_ERR_ALIGN, "ws is not 256-byte aligned");
+  if (need > 0) {
+    if (ws == nullptr || ws_bytes < need)
+      return fail(BSA_ERR_WORKSPACE, "select workspace needs %zu bytes (got %zu%s)", need,
+                  ws_bytes, ws == nullptr ? ", NULL pointer" : "");
+    if (((uintptr_t)ws & 255u) != 0) return fail(BSA_ERR_ALIGN, "ws is not 256-byte aligned");
+  }
   hipStream_t st = (hipStream_t)stream;
   if (bsa::decode_select_fused(s))
     return hip_result(bsa::launch_decode_select(s, q, lm, idx, sc, st), "select_topk");
+  if (bsa::select_fused(s))
+    return hip_result(bsa::launch_select_fused(s, q, lm, idx, sc, st), "select_topk");
   float* qbar = (float*)ws;
   hipError_t e = bsa::launch_selector_vectors(s, q, qbar, st);
-  if (bsa::select_fused(s)) {
-    if (e == hipSuccess) e = bsa::launch_select_fused(s, qbar, lm, idx, sc, st);
-    return hip_result(e, "select_topk");
-  }
   float* scores = (float*)((char*)ws + bsa::select_ws_qbar_bytes(s));
   if (e == hipSuccess) e = bsa::launch_block_scores(s, qbar, lm, scores, st);
   if (e == hipSuccess) e = bsa::launch_topk(s, scores, idx, sc, st);
@@ -215,16 +215,10 @@ bsa_status_t bsa_select_topk_fused(const bsa_params_t* params, const void* q, co
   BSA_TRY(check_ptr(lm, "lm"));
   BSA_TRY(check_ptr(idx, "idx"));
   BSA_TRY(check_ptr(sc, "sc"));
-  const size_t need = bsa::select_ws_qbar_bytes(s);
-  if (ws == nullptr || ws_bytes < need)
-    return fail(BSA_ERR_WORKSPACE, "select workspace needs %zu bytes (got %zu%s)", need, ws_bytes,
-                ws == nullptr ? ", NULL pointer" : "");
-  if (((uintptr_t)ws & 255u) != 0) return fail(BSA_ERR_ALIGN, "ws is not 256-byte aligned");
-  hipStream_t st = (hipStream_t)stream;
-  float* qbar = (float*)ws;
-  hipError_t e = bsa::launch_selector_vectors(s, q, qbar, st);
-  if (e == hipSuccess) e = bsa::launch_select_fused(s, qbar, lm, idx, sc, st);
-  return hip_result(e, "select_topk_fused");
+  (void)ws;                                    // no workspace: the kernel forms the selector vectors
+  (void)ws_bytes;
+  return hip_result(bsa::launch_select_fused(s, q, lm, idx, sc, (hipStream_t)stream),
+                    "select_topk_fused");
 }
 
 bsa_status_t bsa_attend_prefill(const bsa_params_t* params, const void* q, const void* k,

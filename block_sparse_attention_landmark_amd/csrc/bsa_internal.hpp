@@ -53,7 +53,7 @@ hipError_t launch_block_scores(const Shape& s, const float* qbar, const void* lm
 // (select_fused_ok: the kernel applies; select_fused: bsa_select_topk uses it).
 bool select_fused_ok(const Shape& s);
 bool select_fused(const Shape& s);
-hipError_t launch_select_fused(const Shape& s, const float* qbar, const void* lm, int32_t* idx,
+hipError_t launch_select_fused(const Shape& s, const void* q, const void* lm, int32_t* idx,
                                float* sc, hipStream_t st);
 hipError_t launch_topk(const Shape& s, const float* scores, int32_t* idx, float* sc,
                        hipStream_t st);

@@ -21,18 +21,20 @@
 namespace bsa {
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+bool select_fused(const Shape& s);
 __host__ __device__ inline size_t tri(size_t n) { return n * (n + 1) / 2; }
 
 size_t select_ws_qbar_bytes(const Shape& s) {
   return align256((size_t)s.B * s.Hkv * s.R * s.D * sizeof(float));
 }
-bool select_fused(const Shape& s);
 size_t select_ws_scores_bytes(const Shape& s) {
-  if (select_fused(s)) return 0;                 // scores never leave the selection kernel
   const size_t per = s.decode ? (size_t)s.NB : tri((size_t)s.R);
   return align256((size_t)s.B * s.Hkv * per * sizeof(float));
 }
-size_t select_ws_bytes(const Shape& s) { return select_ws_qbar_bytes(s) + select_ws_scores_bytes(s); }
+size_t select_ws_bytes(const Shape& s) {
+  if (select_fused(s)) return 0;                 // the one-pass kernel needs no workspace
+  return select_ws_qbar_bytes(s) + select_ws_scores_bytes(s);
+}
 
 // ---------------------------------------------------------------------------------------------
 // decode scores, bf16 landmarks: the one selection row of each (sequence, kv group) against
@@ -406,8 +408,9 @@ __device__ __forceinline__ uint32_t cut_list(float* ls, uint16_t* lj, int n, int
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void select_fused_kernel(
-    const float* __restrict__ qbar, const bf16* __restrict__ lm, int32_t* __restrict__ idx,
-    float* __restrict__ sc, int R, int NB, int topk, int n_sink, int n_local, int NA) {
+    const bf16* __restrict__ q, const bf16* __restrict__ lm, int32_t* __restrict__ idx,
+    float* __restrict__ sc, int Hq, int Hkv, int G, int T, int R, int NB, int topk, int n_sink,
+    int n_local, int NA) {
   constexpr int CAP = kFusedCap;
   __shared__ float ls[64][2 * CAP];          // per row: column half h in slots h*CAP ..
   __shared__ uint16_t lj[64][2 * CAP];
@@ -453,10 +456,58 @@ __global__ __launch_bounds__(256, 2) void select_fused_kernel(
     }
   }
 
-  if (row0 < R) {
+  // Selector vectors of the tile row's 64 query blocks, staged in the (not yet used) list space:
+  // for each block, the sum over the group's query heads of the mean over its tokens,
+  // accumulated in float64 and rounded once to float32, as the selector pass computes them.
+  float* sq = &ls[0][0];
+  static_assert(64 * D * sizeof(float) <= sizeof(ls), "selector vectors fit the list space");
+  {
+    constexpr int NC = D / 8;                  // 16-byte chunks of a row
+    constexpr int RS = 256 / NC;               // query blocks in flight per workgroup
+    constexpr int U = 16;                      // token rows loaded per batch
+    const int tid = threadIdx.x;
+    const int cc = tid % NC;
+    const int b = bg / Hkv, g = bg % Hkv;
+    for (int rl = tid / NC; rl < 64; rl += RS) {
+      const int qb = ti * 64 + rl;
+      double acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+      int ntok = 1;
+      if (qb < R) {
+        const int t0 = qb * kBlock;
+        ntok = min(kBlock, T - t0);
+        const int nrows = G * ntok;              // (head, token) rows of the block
+        for (int i0 = 0; i0 < nrows; i0 += U) {
+          u32x4 raw[U];
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const int i = min(i0 + u, nrows - 1);
+            const int hh = i / ntok, t = t0 + i % ntok;
+            raw[u] = *reinterpret_cast<const u32x4*>(
+                q + ((size_t)(b * Hq + g * G + hh) * T + t) * D + cc * 8);
+          }
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            if (i0 + u < nrows) {
+              const bf16x8 x = __builtin_bit_cast(bf16x8, raw[u]);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) acc[e] += (double)bf2f(x[e]);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sq[rl * D + cc * 8 + e] = qb < R ? (float)(acc[e] / (double)ntok) : 0.0f;
+    }
+  }
+  __syncthreads();
+
+  // each wave splits the selector vectors of its 32 rows into their three bf16 terms
+  bf16x8 hi[D / 16], mid[D / 16], lo[D / 16];
+  {
     const int r = row0 + l32;
-    const float* qrow = qbar + ((size_t)bg * R + min(r, R - 1)) * D;
-    bf16x8 hi[D / 16], mid[D / 16], lo[D / 16];
+    const float* qrow = sq + (rh * 32 + l32) * D;
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) {
       const int d0 = 16 * st + 8 * half;
@@ -474,6 +525,10 @@ __global__ __launch_bounds__(256, 2) void select_fused_kernel(
         lo[st][e] = f2bf(r1 - bf2f(m));      // the remaining <= 8 significant bits
       }
     }
+  }
+  __syncthreads();                             // the list space is free again
+
+  if (row0 < R) {
     auto load_l = [&](int tj, bf16x8* bl) {
       const int j = tj * 64 + ch * 32 + l32;
       const bf16* lrow_p = lm + ((size_t)bg * NB + min(j, NB - 1)) * D;
@@ -644,15 +699,16 @@ bool select_fused_ok(const Shape& s) {
 // blocks a tile row is too little work per workgroup and the two-kernel path is faster)
 bool select_fused(const Shape& s) { return select_fused_ok(s) && s.NB > 4096; }
 
-hipError_t launch_select_fused(const Shape& s, const float* qbar, const void* lm, int32_t* idx,
+hipError_t launch_select_fused(const Shape& s, const void* q, const void* lm, int32_t* idx,
                                float* sc, hipStream_t st) {
   const dim3 grid((s.R + 63) / 64, s.B * s.Hkv);
-  if (s.D == 128)
-    hipLaunchKernelGGL(select_fused_kernel<128>, grid, dim3(256), 0, st, qbar, (const bf16*)lm,
-                       idx, sc, s.R, s.NB, s.topk, s.n_sink, s.n_local, s.NA);
-  else
-    hipLaunchKernelGGL(select_fused_kernel<64>, grid, dim3(256), 0, st, qbar, (const bf16*)lm,
-                       idx, sc, s.R, s.NB, s.topk, s.n_sink, s.n_local, s.NA);
+#define BSA_SF(D_)                                                                               \
+  hipLaunchKernelGGL(select_fused_kernel<D_>, grid, dim3(256), 0, st, (const bf16*)q,           \
+                     (const bf16*)lm, idx, sc, s.Hq, s.Hkv, s.G, s.Tq, s.R, s.NB, s.topk,       \
+                     s.n_sink, s.n_local, s.NA)
+  if (s.D == 128) BSA_SF(128);
+  else BSA_SF(64);
+#undef BSA_SF
   return hipGetLastError();
 }
 

@@ -108,9 +108,9 @@ size_t bsa_select_workspace_bytes(const bsa_params_t* params);
  *   lm   [B,Hkv,NB,D] landmarks of the Tk keys (bsa_pool_landmarks)
  *   idx  [B,Hkv,R,NA] int32 output, sc [B,Hkv,R,NA] float32 output
  *   ws   device workspace of at least bsa_select_workspace_bytes(params) bytes (the selector
- *        vectors; plus the float32 score rows, except where the one-pass selection below runs:
- *        bf16 prefill rows with topk <= 32 and more than 4096 blocks); contents on entry are
- *        ignored.
+ *        vectors and the float32 score rows; none where the one-pass selection below runs: bf16
+ *        prefill rows with topk <= 32 and more than 4096 blocks; then ws may be NULL); contents
+ *        on entry are ignored.
  */
 bsa_status_t bsa_select_topk(const bsa_params_t* params, const void* q, const void* lm,
                              int32_t* idx, float* sc, void* ws, size_t ws_bytes, void* stream);
@@ -123,9 +123,8 @@ bsa_status_t bsa_select_topk(const bsa_params_t* params, const void* q, const vo
  * summary paragraph 1: hard top-K).  bsa_select_topk uses it by itself for rows of more than
  * 4096 blocks; this entry point takes it at any length.
  *   Applies to prefill (seq_q == seq_k) with dtype BSA_BF16, topk <= 32 and at most 65535
- *   blocks; otherwise BSA_ERR_UNSUPPORTED.
- *   ws   device workspace of at least bsa_select_workspace_bytes(params) bytes (only the
- *        selector vectors are used); contents on entry are ignored.
+ *   blocks; otherwise BSA_ERR_UNSUPPORTED.  The kernel forms the selector vectors itself.
+ *   ws, ws_bytes  unused (no workspace; may be NULL, 0).
  */
 bsa_status_t bsa_select_topk_fused(const bsa_params_t* params, const void* q, const void* lm,
                                    int32_t* idx, float* sc, void* ws, size_t ws_bytes,

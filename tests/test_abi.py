@@ -152,11 +152,7 @@ def test_select_one_pass_validation(lib):
     assert sel(_p(topk=-1)) == SHAPE
     assert sel(_p(), q=None) == NULL
     assert sel(_p(), idx=None) == NULL
-    p = _p(B=2, Hq=8, Hkv=2, seq_q=64 * 10, seq_k=64 * 10)
-    need = 2 * 2 * 10 * 128 * 4                                   # the selector vectors alone
-    assert sel(p, nbytes=need - 1) == WS
-    assert sel(p, ws=None) == WS
-    assert sel(p, ws=ctypes.c_void_p((1 << 20) + 16)) == ALIGN
+    # it takes no workspace: a NULL ws is no error (checked up to the launch on the GPU tests)
 
 
 def test_workspace_sizes_follow_the_shapes(lib):
@@ -166,13 +162,13 @@ def test_workspace_sizes_follow_the_shapes(lib):
     scores = 2 * 2 * (10 * 11 // 2) * 4
     rnd = lambda x: (x + 255) // 256 * 256
     assert lib.bsa_select_workspace_bytes(ctypes.byref(p)) == rnd(qbar) + rnd(scores)
-    # rows of more than 4096 blocks, bf16, K <= 32: the one-pass selection, selector vectors only;
-    # K > 32 or float32 landmarks keep the score rows
+    # rows of more than 4096 blocks, bf16, K <= 32: the one-pass selection, no workspace;
+    # K > 32 or float32 landmarks keep the selector vectors and score rows
     nb = 4097
     long_kw = dict(B=1, Hq=4, Hkv=2, seq_q=64 * nb, seq_k=64 * nb)
     qbar_l = 2 * nb * 128 * 4
     scores_l = 2 * (nb * (nb + 1) // 2) * 4
-    assert lib.bsa_select_workspace_bytes(ctypes.byref(_p(**long_kw, topk=32))) == rnd(qbar_l)
+    assert lib.bsa_select_workspace_bytes(ctypes.byref(_p(**long_kw, topk=32))) == 0
     assert lib.bsa_select_workspace_bytes(ctypes.byref(_p(**long_kw, topk=33))) == rnd(qbar_l) + rnd(scores_l)
     assert (lib.bsa_select_workspace_bytes(ctypes.byref(_p(**long_kw, topk=8, dtype=bsa.torch.float32)))
             == rnd(qbar_l) + rnd(scores_l))
