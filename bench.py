@@ -154,7 +154,7 @@ def bench_prefill(torch, bsa, synth, name, steps, warmup):
     sc = torch.empty((B, Hkv, NB, NA), dtype=torch.float32, device="cuda")
     out = torch.empty_like(q)
     p = bsa.make_params(B=B, Hq=Hq, Hkv=Hkv, D=D, seq_q=T, seq_k=T, dtype=q.dtype, topk=K)
-    ws = torch.empty(bsa.select_workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(max(bsa.select_workspace_bytes(p), 256), dtype=torch.uint8, device="cuda")
     ev_attn, ev_sel, ev_pool = Events(torch), Events(torch), Events(torch)
 
     def step(record):
@@ -287,7 +287,7 @@ def bench_lsa(torch, bsa, synth, name, tensors, steps, warmup, seg_blocks=64, n_
     if tree:
         bsa.lsa_build_tree(lm, index, fanout=fanout)
     p = bsa.make_params(B=B, Hq=Hq, Hkv=Hkv, D=D, seq_q=T, seq_k=T, dtype=q.dtype, topk=K)
-    ws = torch.empty(max(bsa.select_workspace_bytes(p), 256), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(max(bsa.lsa_select_workspace_bytes(p), 256), dtype=torch.uint8, device="cuda")
     ev = {n: Events(torch) for n in ("pool", "build", "select", "attend")}
 
     def step(record):
@@ -751,6 +751,8 @@ def main():
                            "tok_per_s": hils["tok_per_s"], "ms_per_step": hils["ms_per_step"],
                            "breakdown_ms": {"pool": hils["pool_ms"], "select": hils["select_ms"],
                                             "attend": hils["attn_ms"]},
+                           "select_path": "one-pass kernel (selector vectors, scores and top-K of "
+                                          "each tile row in one launch; no score workspace)",
                            "attended_tflops_attention_kernel": hils["attended_tflops_kernel"],
                            "frac_of_bf16_peak": hils["attended_tflops_kernel"] / PEAK_BF16_TFLOPS}
     if lsa_1m is not None:

@@ -248,6 +248,10 @@ def decode_workspace_bytes(p: Params) -> int:
     return int(load_library().bsa_decode_workspace_bytes(ctypes.byref(p)))
 
 
+def lsa_select_workspace_bytes(p: Params) -> int:
+    return int(load_library().bsa_lsa_select_workspace_bytes(ctypes.byref(p)))
+
+
 def select_topk(q: torch.Tensor, lm: torch.Tensor, *, topk: int, seq_k: int | None = None,
                 n_sink: int = 1, n_local: int = 2, ws: torch.Tensor | None = None,
                 idx: torch.Tensor | None = None, sc: torch.Tensor | None = None,
