@@ -464,7 +464,7 @@ __global__ __launch_bounds__(256, 2) void select_fused_kernel(
   {
     constexpr int NC = D / 8;                  // 16-byte chunks of a row
     constexpr int RS = 256 / NC;               // query blocks in flight per workgroup
-    constexpr int U = 16;                      // token rows loaded per batch
+    constexpr int U = 32;                      // token rows loaded per batch
     const int tid = threadIdx.x;
     const int cc = tid % NC;
     const int b = bg / Hkv, g = bg % Hkv;
