@@ -210,7 +210,7 @@ bsa_status_t bsa_select_topk_fused(const bsa_params_t* params, const void* q, co
   if (!bsa::select_fused_ok(s))
     return fail(BSA_ERR_UNSUPPORTED,
                 "the one-pass selection takes prefill rows of bf16 landmarks with topk <= 32 and "
-                "at most 65535 blocks");
+                "at most 65536 blocks");
   BSA_TRY(check_ptr(q, "q"));
   BSA_TRY(check_ptr(lm, "lm"));
   BSA_TRY(check_ptr(idx, "idx"));
@@ -245,10 +245,16 @@ bsa_status_t bsa_attend_prefill(const bsa_params_t* params, const void* q, const
 // ---- flat clustered (LSA) index ----
 
 namespace {
-bsa_status_t check_lsa(const bsa::Shape& s, int32_t seg_blocks, int32_t n_clusters) {
-  if (seg_blocks < 1 || seg_blocks > 64 || n_clusters < 1 || n_clusters > seg_blocks)
+bsa_status_t check_lsa_index(int32_t seg_blocks, int32_t n_clusters) {
+  if (!bsa::lsa_index_ok(seg_blocks, n_clusters))
     return fail(BSA_ERR_UNSUPPORTED, "need 1 <= n_clusters <= seg_blocks <= 64 (got %d, %d)",
                 n_clusters, seg_blocks);
+  return BSA_OK;
+}
+
+// the flat selection's limits
+bsa_status_t check_lsa(const bsa::Shape& s, int32_t seg_blocks, int32_t n_clusters) {
+  BSA_TRY(check_lsa_index(seg_blocks, n_clusters));
   if (!bsa::lsa_shape_ok(s, seg_blocks, n_clusters))
     return fail(BSA_ERR_UNSUPPORTED,
                 "the LSA selection sorts at most 8192 units per row (segments x n_clusters + "
@@ -262,7 +268,7 @@ bsa_status_t bsa_lsa_build_index(const bsa_params_t* params, const void* lm, int
                                  int32_t* offsets, int32_t* merges, void* stream) {
   bsa::Shape s;
   BSA_TRY(make_shape(params, kPool, &s));
-  BSA_TRY(check_lsa(s, seg_blocks, n_clusters));
+  BSA_TRY(check_lsa_index(seg_blocks, n_clusters));
   if (s.NB / seg_blocks == 0) return ok();       // no completed segment: nothing to build
   BSA_TRY(check_ptr(lm, "lm"));
   BSA_TRY(check_ptr(centres, "centres"));
@@ -280,7 +286,7 @@ bsa_status_t bsa_lsa_update_index(const bsa_params_t* params, const void* lm, in
                                   void* stream) {
   bsa::Shape s;
   BSA_TRY(make_shape(params, kPool, &s));
-  BSA_TRY(check_lsa(s, seg_blocks, n_clusters));
+  BSA_TRY(check_lsa_index(seg_blocks, n_clusters));
   if (first_segment < 0)
     return fail(BSA_ERR_SHAPE, "first_segment must be >= 0 (got %d)", first_segment);
   if (s.NB / seg_blocks <= first_segment) return ok();   // no segment to cluster
@@ -354,11 +360,12 @@ bsa_status_t bsa_lsa_tree_select(const bsa_params_t* params, const void* q, cons
                                  size_t ws_bytes, void* stream) {
   bsa::Shape s;
   BSA_TRY(make_shape(params, kSelect, &s));
-  BSA_TRY(check_lsa(s, seg_blocks, n_clusters));
+  BSA_TRY(check_lsa_index(seg_blocks, n_clusters));
   if (!bsa::lsa_tree_shape_ok(s, seg_blocks, n_clusters, fanout, beam))
     return fail(BSA_ERR_UNSUPPORTED,
-                "the LSA tree needs 1 <= beam <= 64, fanout >= 1, segments / fanout + fanout, "
-                "beam * fanout and beam * n_clusters at most 1024");
+                "the LSA tree needs topk <= 2048, 1 <= beam <= 64, fanout >= 1, and "
+                "segments / fanout + fanout, beam * fanout, beam * n_clusters and "
+                "beam + seg_blocks at most 1024");
   BSA_TRY(check_ptr(q, "q"));
   BSA_TRY(check_ptr(lm, "lm"));
   BSA_TRY(check_ptr(idx, "idx"));

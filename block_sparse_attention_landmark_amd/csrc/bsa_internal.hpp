@@ -88,6 +88,7 @@ hipError_t launch_attend_backward(const Shape& s, const void* q, const void* k, 
                                   hipStream_t st);
 
 // Flat clustered (LSA) index: shape limits, index build, selection over it.
+bool lsa_index_ok(int seg, int nc);
 bool lsa_shape_ok(const Shape& s, int seg, int nc);
 // segments seg0 .. NB / seg - 1 (seg0 > 0: only the segments completed since an earlier build)
 hipError_t launch_lsa_build(const Shape& s, const void* lm, int seg, int nc, float* centres,

@@ -713,7 +713,9 @@ __global__ __launch_bounds__(256) void lsa_tree_select_kernel(
 }
 
 bool lsa_tree_shape_ok(const Shape& s, int seg, int nc, int fan, int beam) {
-  if (!lsa_shape_ok(s, seg, nc) || fan < 1 || beam < 1 || beam > 64) return false;
+  // the beam search sorts one level's nodes at a time, whatever the number of segments
+  if (!lsa_index_ok(seg, nc) || s.topk > kLsaMaxK || fan < 1 || beam < 1 || beam > 64)
+    return false;
   const int ns = s.NB / seg;
   return ns / fan + fan <= 1024 && beam * fan <= 1024 && beam * nc <= 1024 &&
          beam + seg <= 1024;
@@ -778,8 +780,11 @@ hipError_t launch_lsa_tree_select(const Shape& s, const void* q, const void* lm,
 // ---------------------------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------------------------
+bool lsa_index_ok(int seg, int nc) { return seg >= 1 && seg <= kLsaMaxSeg && nc >= 1 && nc <= seg; }
+
+// the flat selection sorts every unit of a row at once
 bool lsa_shape_ok(const Shape& s, int seg, int nc) {
-  if (seg < 1 || seg > kLsaMaxSeg || nc < 1 || nc > seg) return false;
+  if (!lsa_index_ok(seg, nc)) return false;
   const int ns = s.NB / seg;
   if ((int64_t)ns * nc + seg > kLsaMaxUnits) return false;
   return s.topk <= kLsaMaxK;

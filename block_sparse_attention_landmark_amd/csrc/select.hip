@@ -693,7 +693,7 @@ __global__ __launch_bounds__(256, 2) void select_fused_kernel(
 }
 
 bool select_fused_ok(const Shape& s) {
-  return !s.decode && s.bf16 && s.topk <= kFusedMaxK && s.NB <= 65535 && s.R == s.NB;
+  return !s.decode && s.bf16 && s.topk <= kFusedMaxK && s.NB <= 65536 && s.R == s.NB;
 }
 // bsa_select_topk takes the one-pass kernel where it wins: rows of more than 4096 blocks (at 2048
 // blocks a tile row is too little work per workgroup and the two-kernel path is faster)

@@ -122,7 +122,7 @@ bsa_status_t bsa_select_topk(const bsa_params_t* params, const void* q, const vo
  * whole context", paragraph 2: the candidate search is what grows with the context; SAS page,
  * summary paragraph 1: hard top-K).  bsa_select_topk uses it by itself for rows of more than
  * 4096 blocks; this entry point takes it at any length.
- *   Applies to prefill (seq_q == seq_k) with dtype BSA_BF16, topk <= 32 and at most 65535
+ *   Applies to prefill (seq_q == seq_k) with dtype BSA_BF16, topk <= 32 and at most 65536
  *   blocks; otherwise BSA_ERR_UNSUPPORTED.  The kernel forms the selector vectors itself.
  *   ws, ws_bytes  unused (no workspace; may be NULL, 0).
  */
@@ -367,8 +367,9 @@ bsa_status_t bsa_lsa_tree_centres(const bsa_params_t* params, const void* lm,
  * become units, expanded with the not yet clustered candidate blocks exactly as in
  * bsa_lsa_select (same row layout and scores).  Arguments as bsa_lsa_select plus the tree
  * centres; ws: bsa_lsa_select_workspace_bytes.
- * Limits: those of bsa_lsa_select, 1 <= beam <= 64, fanout >= 1, and NS / fanout + fanout,
- * beam * fanout, beam * n_clusters each at most 1024.
+ * Limits: those of bsa_lsa_build_index, topk <= 2048, 1 <= beam <= 64, fanout >= 1, and
+ * NS / fanout + fanout, beam * fanout, beam * n_clusters and beam + seg_blocks each at most
+ * 1024 (no limit on NS * n_clusters: one level's nodes are sorted at a time).
  */
 bsa_status_t bsa_lsa_tree_select(const bsa_params_t* params, const void* q, const void* lm,
                                  int32_t seg_blocks, int32_t n_clusters, int32_t fanout,

@@ -320,3 +320,26 @@ def test_python_binding_rejects_cpu_tensors():
     import torch
     with pytest.raises(ValueError):
         bsa.pool_landmarks(torch.zeros(1, 1, 64, 64))
+
+
+def test_lsa_limits_flat_and_tree(lib):
+    """At 4M tokens (65536 blocks = 1024 segments of 64, 16 clusters each) the flat selection,
+    which sorts every unit of a row at once, rejects the shape; the index build and the tree
+    selection, which sorts one level's nodes at a time, take it (the checks below stop at a NULL
+    pointer or at "nothing to do", after the shape checks, without a launch)."""
+    big = _p(Hq=32, Hkv=8, seq_q=4194304, seq_k=4194304, topk=32)
+    assert lib.bsa_lsa_select(ctypes.byref(big), FAKE, FAKE, 64, 16, FAKE, FAKE, FAKE, FAKE,
+                              FAKE, FAKE, 1 << 40, None) == UNSUP
+    assert b"8192" in lib.bsa_last_error()
+    assert lib.bsa_lsa_update_index(ctypes.byref(big), FAKE, 64, 16, 1024, FAKE, FAKE, FAKE,
+                                    FAKE, None) == OK
+    assert lib.bsa_lsa_build_index(ctypes.byref(big), FAKE, 64, 16, None, FAKE, FAKE, FAKE,
+                                   None) == NULL
+    tree = lambda beam, q=FAKE: lib.bsa_lsa_tree_select(
+        ctypes.byref(big), q, FAKE, 64, 16, 8, beam, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+        FAKE, 1 << 40, None)
+    assert tree(8, q=None) == NULL
+    assert tree(65) == UNSUP
+    assert lib.bsa_lsa_tree_select(ctypes.byref(big), FAKE, FAKE, 64, 16, 1, 8, FAKE, FAKE, FAKE,
+                                   FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == UNSUP
+    assert b"1024" in lib.bsa_last_error()     # fanout 1: 1024 segments + 1 at the top level
