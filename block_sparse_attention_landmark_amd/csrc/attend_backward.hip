@@ -308,57 +308,89 @@ __global__ __launch_bounds__(HPW * 128) void bwd_dq_kernel(
       const int j = irow[a];
       gates_out[rowsel + a] = gate_of(a, j);
     }
-  if constexpr (MODE == 2) {
-    // retrieval weights softmax_j(scale q . L_j) of this wave's 32 rows over the attended
-    // chunks (at most 64), as in the forward: R^T = L Q^T on MFMA with the landmark rows in LDS
-    for (int ci = tid; ci < kBlock * C8; ci += NT) {
-      const int row = ci / C8, c8 = ci % C8;
-      u32x4 val = u32x4{0u, 0u, 0u, 0u};
-      const int jr = row < nval ? irow[row] : -1;
-      if (jr >= 0 && jr <= c)
-        val = *reinterpret_cast<const u32x4*>(lm + ((size_t)(b * Hkv + g) * NQB + jr) * D + c8 * 8);
-      *reinterpret_cast<u32x4*>(&Lb[row * KP + c8 * 8]) = val;
-    }
-    __syncthreads();
-    f32x16 rt[2];
+  // HiLS: retrieval logits (log2 units) of the entries e0 .. e0+63 for this wave's 32 rows
+  // (-inf past nval), R^T = L Q^T on MFMA as in the forward, and their weights
+  // softmax_j(scale q . L_j) over every attended chunk (max and 1 / sum carried over groups of
+  // 64) into this wave's table.  The landmark rows of the group held in Lb are read from LDS
+  // (from_lds); those of other groups straight from memory as A fragments.
+  float w_max = -INFINITY, w_inv = 0.0f;
+  auto hils_logits = [&](int e0, f32x16* rt, bool from_lds) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
+      const int e = e0 + kt * 32 + l32;
+      const int jr = e < nval ? irow[e] : -1;
+      const bool ok = jr >= 0 && jr <= c;
+      const bf16* lrow = lm + ((size_t)(b * Hkv + g) * NQB + (ok ? jr : 0)) * D + 8 * half;
 #pragma unroll
       for (int i = 0; i < 16; ++i) rt[kt][i] = 0.0f;
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Lb[(kt * 32 + l32) * KP + 16 * s + 8 * half]);
+        bf16x8 a;
+        if (from_lds) {
+          a = *reinterpret_cast<const bf16x8*>(&Lb[(kt * 32 + l32) * KP + 16 * s + 8 * half]);
+        } else {
+          u32x4 raw = *reinterpret_cast<const u32x4*>(lrow + 16 * s);
+          if (!ok) raw = u32x4{0u, 0u, 0u, 0u};
+          a = __builtin_bit_cast(bf16x8, raw);
+        }
         rt[kt] = mfma32(a, qf[s], rt[kt]);
       }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int slot = e0 + kt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+        rt[kt][i] = slot < nval ? rt[kt][i] * scale_log2 : -INFINITY;
+      }
     }
-    float mloc = -INFINITY;
+  };
+  auto hils_weights = [&](const f32x16* rt) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int slot = kt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-        const float x = slot < nval ? rt[kt][i] * scale_log2 : -INFINITY;
-        rt[kt][i] = x;
-        mloc = fmaxf(mloc, x);
+        wbuf[(w * 64 + slot) * 32 + l32] = fast_exp2(rt[kt][i] - w_max) * w_inv;
       }
-    const float M = wave_max_xor32(mloc);
+  };
+  // HiLS: the landmark rows of the entries e0 .. e0+63 into Lb (zero rows past nval)
+  auto stage_landmarks = [&](int e0) {
+    for (int ci = tid; ci < kBlock * C8; ci += NT) {
+      const int row = ci / C8, c8 = ci % C8;
+      const int e = e0 + row;
+      u32x4 val = u32x4{0u, 0u, 0u, 0u};
+      const int jr = e < nval ? irow[e] : -1;
+      if (jr >= 0 && jr <= c)
+        val = *reinterpret_cast<const u32x4*>(lm + ((size_t)(b * Hkv + g) * NQB + jr) * D + c8 * 8);
+      *reinterpret_cast<u32x4*>(&Lb[row * KP + c8 * 8]) = val;
+    }
+  };
+  const int ngr = (nval + 63) / 64;              // HiLS: groups of 64 entries
+  if constexpr (MODE == 2) {
+    stage_landmarks(0);
+    __syncthreads();
+    f32x16 rt[2];
     float den = 0.0f;
+    for (int gi = 0; gi < ngr; ++gi) {
+      hils_logits(gi * 64, rt, gi == 0);
+      float mloc = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float e = fast_exp2(rt[kt][i] - M);
-        rt[kt][i] = e;
-        den += e;
-      }
-    const float inv = 1.0f / wave_sum_xor32(den);
+        for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, rt[kt][i]);
+      const float m_new = fmaxf(w_max, wave_max_xor32(mloc));
+      float dsum = 0.0f;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int slot = kt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-        wbuf[(w * 64 + slot) * 32 + l32] = rt[kt][i] * inv;
-      }
+        for (int i = 0; i < 16; ++i) dsum += fast_exp2(rt[kt][i] - m_new);
+      dsum = wave_sum_xor32(dsum);
+      den = gi == 0 ? dsum : den * fast_exp2(w_max - m_new) + dsum;
+      w_max = m_new;
+    }
+    if (ngr > 0) {
+      w_inv = 1.0f / den;
+      if (ngr > 1) hils_logits(0, rt, true);
+      hils_weights(rt);
+    }
   }
 
   u32x4 kreg[CPT], vreg[CPT];
@@ -402,6 +434,13 @@ __global__ __launch_bounds__(HPW * 128) void bwd_dq_kernel(
   for (int a = 0; a < nval; ++a) {
     const int buf = a & 1;
     const int j = irow[a];
+    if constexpr (MODE == 2) {
+      if (a > 0 && a % 64 == 0) {               // the weights of the next 64 entries
+        f32x16 rt[2];
+        hils_logits(a, rt, false);
+        hils_weights(rt);
+      }
+    }
     if (j >= 0 && j <= c) {
       const bf16* Kb = Ks[buf];
       const bf16* Vb = Vs[buf];
@@ -447,7 +486,7 @@ __global__ __launch_bounds__(HPW * 128) void bwd_dq_kernel(
         dwp = wave_sum_xor32(dwp);
         const float inv_l = l > 0.0f ? 1.0f / l : 0.0f;
         const float dwv = dwp * inv_l;
-        const float wj = wbuf[(w * 64 + a) * 32 + l32];
+        const float wj = wbuf[(w * 64 + a % 64) * 32 + l32];
         g_acc = fmaf(wj, dwv, g_acc);
         const float coef = wj * inv_l;
 #pragma unroll
@@ -460,7 +499,7 @@ __global__ __launch_bounds__(HPW * 128) void bwd_dq_kernel(
           const bool live = row_ok && l > 0.0f && wj > 0.0f;
           hstat[hi] = live ? mxs + log2f(l) - log2f(wj) : 0.0f;
           hstat[hs_n + hi] = live ? dwv : 0.0f;
-          dwbuf[(w * 64 + a) * 32 + l32] = dwv;
+          dwbuf[(w * 64 + a % 64) * 32 + l32] = dwv;
         }
       } else {
         const float gb = gate_of(a, j) - lse2;
@@ -502,30 +541,47 @@ __global__ __launch_bounds__(HPW * 128) void bwd_dq_kernel(
     __syncthreads();
   }
   if constexpr (MODE == 2) {
-    // retrieval-score gradients dr_j = w_j (dw_j - sum_i w_i dw_i), kept for the key side
-    if (half == 0)
-      for (int a = 0; a < nval; ++a) {
-        const float wj = wbuf[(w * 64 + a) * 32 + l32];
-        const float drv = row_ok ? wj * (dwbuf[(w * 64 + a) * 32 + l32] - g_acc) : 0.0f;
-        hstat[2 * hs_n + (((size_t)(b * Hq + h) * NQB + c) * NA + a) * kBlock + (w % 2) * 32 + l32] = drv;
-        wbuf[(w * 64 + a) * 32 + l32] = drv;
+    // per group of 64 entries: the retrieval-score gradients dr_j = w_j (dw_j - sum_i w_i dw_i),
+    // kept for the key side, then dQ^T += L^T dR^T with the group's landmark rows in LDS
+    for (int gi = 0; gi < ngr; ++gi) {
+      const int e0 = gi * 64;
+      if (ngr > 1) {                             // one group: its weights are still in the table
+        f32x16 rt[2];
+        hils_logits(e0, rt, false);
+        hils_weights(rt);
       }
-    // dQ^T += L^T dR^T over the attended chunks, 16 per k-step; the transposed landmark reads
-    // put chunks 16ks + 4half + {0..3} and 16ks + 8 + 4half + {0..3} in a lane's k slots, and the
-    // retrieval-score gradients are taken in the same order
+      if (half == 0)
+        for (int a = e0; a < min(nval, e0 + 64); ++a) {
+          const int sl = (w * 64 + a - e0) * 32 + l32;
+          const size_t hi = (((size_t)(b * Hq + h) * NQB + c) * NA + a) * kBlock + (w % 2) * 32 + l32;
+          // dw of this row and entry: from the table (one group), else as stored for the key side
+          const float dwj = ngr > 1 ? hstat[hs_n + hi] : dwbuf[sl];
+          const float wj = wbuf[sl];
+          const float drv = row_ok ? wj * (dwj - g_acc) : 0.0f;
+          hstat[2 * hs_n + hi] = drv;
+          wbuf[sl] = drv;
+        }
+      if (gi > 0) {                              // group 0's rows are still in Lb
+        __syncthreads();                         // the previous group's rows have been read
+        stage_landmarks(e0);
+        __syncthreads();
+      }
+      // the transposed landmark reads put chunks 16ks + 4half + {0..3} and 16ks + 8 + 4half +
+      // {0..3} in a lane's k slots, and the retrieval-score gradients are taken in that order
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 rb;
+      for (int ks = 0; ks < 4; ++ks) {
+        bf16x8 rb;
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        rb[e] = f2bf(wbuf[(w * 64 + 16 * ks + 4 * half + (e % 4) + 8 * (e / 4)) * 32 + l32]);
-      const bf16* l0 = Lb + (16 * ks + 4 * half + vrow) * KP + vcol;
+        for (int e = 0; e < 8; ++e)
+          rb[e] = f2bf(wbuf[(w * 64 + 16 * ks + 4 * half + (e % 4) + 8 * (e / 4)) * 32 + l32]);
+        const bf16* l0 = Lb + (16 * ks + 4 * half + vrow) * KP + vcol;
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        const i16x4 x0 = lds_read_tr16(l0 + dt * 32);
-        const i16x4 x1 = lds_read_tr16(l0 + 8 * KP + dt * 32);
-        const bf16x8 al = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
-        dqa[dt] = mfma32(al, rb, dqa[dt]);
+        for (int dt = 0; dt < D / 32; ++dt) {
+          const i16x4 x0 = lds_read_tr16(l0 + dt * 32);
+          const i16x4 x1 = lds_read_tr16(l0 + 8 * KP + dt * 32);
+          const bf16x8 al = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+          dqa[dt] = mfma32(al, rb, dqa[dt]);
+        }
       }
     }
   }

@@ -45,7 +45,9 @@ constexpr float kPpSumLimit = 65536.0f;   // see the vector phase of the ping-po
 constexpr int kPpUnits = 4;       // staging units in LDS for the ping-pong prefill kernel (a power
                                    // of two keeps the unit addressing cheap)
 
-template <int D, int MODE, int HPW>
+// WIDE (HiLS with more than 64 attended entries): the merge weights are taken 64 entries at a
+// time, the table refreshed inside the entry loop; the common case keeps that code out of it.
+template <int D, int MODE, int HPW, bool WIDE>
 __global__ __launch_bounds__(HPW * 128) void attend_prefill_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ lm, const int32_t* __restrict__ idx, const float* __restrict__ sc,
@@ -136,11 +138,55 @@ __global__ __launch_bounds__(HPW * 128) void attend_prefill_bf16_kernel(
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
 
+  // HiLS: retrieval logits (log2 units) of the entries e0 .. e0+63 for this wave's 32 query rows
+  // (-inf past nval): R^T = L Q^T on MFMA; register i of tile kt holds entry
+  // e0 + kt*32 + 8*(i/4) + 4*half + i%4.  The landmark rows of the first 64 entries are staged in
+  // LDS once (from_lds); those of later entries are read straight from memory as A fragments.
+  float w_max = 0.0f, w_inv = 0.0f;            // HiLS: the rows' max logit and 1 / sum
+  auto hils_logits = [&](int e0, f32x16* rt, bool from_lds) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int e = e0 + kt * 32 + l32;
+      const int jr = e < nval ? irow[e] : -1;
+      const bool ok = jr >= 0 && jr <= c;
+      const bf16* lrow = lm + ((size_t)(b * Hkv + g) * NQB + (ok ? jr : 0)) * D + 8 * half;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) rt[kt][i] = 0.0f;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        bf16x8 a;
+        if (from_lds) {
+          a = *reinterpret_cast<const bf16x8*>(&Ks[1][(kt * 32 + l32) * KP + 16 * s + 8 * half]);
+        } else {
+          u32x4 raw = *reinterpret_cast<const u32x4*>(lrow + 16 * s);
+          if (!ok) raw = u32x4{0u, 0u, 0u, 0u};
+          a = __builtin_bit_cast(bf16x8, raw);
+        }
+        rt[kt] = mfma32(a, qf[s], rt[kt]);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int slot = e0 + kt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+        rt[kt][i] = slot < nval ? rt[kt][i] * scale_log2 : -INFINITY;
+      }
+    }
+  };
+  // the weights w_j = 2^(r_j - max) / sum of the entries in rt into this wave's table
+  auto hils_weights = [&](const f32x16* rt) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int slot = kt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+        wbuf[(w * 64 + slot) * 32 + l32] = fast_exp2(rt[kt][i] - w_max) * w_inv;
+      }
+  };
+
   if (nval > 0) load_tile(0);
 
   if constexpr (MODE == 2) {
-    // retrieval weights of every attended chunk for this wave's 32 query rows (landmark rows
-    // staged in the second K buffer, which the pipeline first writes after the next barrier)
+    // landmark rows of the first 64 entries, staged in the second K buffer (which the pipeline
+    // first writes after the next barrier)
     for (int ci = tid; ci < kBlock * C8; ci += NT) {
       const int row = ci / C8, c8 = ci % C8;
       u32x4 val = u32x4{0u, 0u, 0u, 0u};
@@ -150,46 +196,34 @@ __global__ __launch_bounds__(HPW * 128) void attend_prefill_bf16_kernel(
       *reinterpret_cast<u32x4*>(&Ks[1][row * KP + c8 * 8]) = val;
     }
     __syncthreads();
+    // softmax of the retrieval logits over every attended chunk, 64 entries at a time: the max
+    // and the sum are carried from one group of 64 to the next (one group: a plain max and sum)
+    const int ngr = WIDE ? (nval + 63) / 64 : min(nval, 1);
     f32x16 rt[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) rt[kt][i] = 0.0f;
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[1][(kt * 32 + l32) * KP + 16 * s + 8 * half]);
-        rt[kt] = mfma32(a, qf[s], rt[kt]);
-      }
-    }
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int slot = kt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-        const float x = slot < nval ? rt[kt][i] * scale_log2 : -INFINITY;
-        rt[kt][i] = x;
-        mloc = fmaxf(mloc, x);
-      }
-    const float M = wave_max_xor32(mloc);
     float den = 0.0f;
+    w_max = -INFINITY;
+    for (int gi = 0; gi < ngr; ++gi) {
+      hils_logits(gi * 64, rt, !WIDE || gi == 0);
+      float mloc = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float e = fast_exp2(rt[kt][i] - M);
-        rt[kt][i] = e;
-        den += e;
-      }
-    den = wave_sum_xor32(den);
-    const float inv = 1.0f / den;
+        for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, rt[kt][i]);
+      const float m_new = fmaxf(w_max, wave_max_xor32(mloc));
+      float dsum = 0.0f;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int slot = kt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-        wbuf[(w * 64 + slot) * 32 + l32] = rt[kt][i] * inv;
-      }
+        for (int i = 0; i < 16; ++i) dsum += fast_exp2(rt[kt][i] - m_new);
+      dsum = wave_sum_xor32(dsum);
+      den = gi == 0 ? dsum : den * fast_exp2(w_max - m_new) + dsum;
+      w_max = m_new;
+    }
+    if (ngr > 0) {
+      w_inv = 1.0f / den;
+      if (WIDE && ngr > 1) hils_logits(0, rt, true);
+      hils_weights(rt);
+    }
   }
 
   if (nval > 0) store_tile(0);
@@ -201,6 +235,13 @@ __global__ __launch_bounds__(HPW * 128) void attend_prefill_bf16_kernel(
   for (int a = 0; a < nval; ++a) {
     const int buf = a & 1;
     const int j = irow[a];
+    if constexpr (MODE == 2 && WIDE) {
+      if (a > 0 && a % 64 == 0) {               // the weights of the next 64 entries
+        f32x16 rt[2];
+        hils_logits(a, rt, false);
+        hils_weights(rt);
+      }
+    }
     if (j >= 0 && j <= c) {
       const bf16* Kb = Ks[buf];
       const bf16* Vb = Vs[buf];
@@ -253,7 +294,7 @@ __global__ __launch_bounds__(HPW * 128) void attend_prefill_bf16_kernel(
             lsum += e;
           }
         const float lj = wave_sum_xor32(lsum);
-        const float coef = wbuf[(w * 64 + a) * 32 + l32] / lj;
+        const float coef = wbuf[(w * 64 + a % 64) * 32 + l32] / lj;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -725,14 +766,15 @@ static void launch_prefill_bf16_d(const Shape& s, const void* q, const void* k, 
   const int n_hc = s.G / hpw;
   dim3 grid(s.R, s.Hkv * n_hc, s.B);
   const float sl2 = s.scale * kLog2e;
-#define BSA_PF(MODE, HPW)                                                                      \
-  hipLaunchKernelGGL((attend_prefill_bf16_kernel<D, MODE, HPW>), grid, dim3(HPW * 128), 0, st, \
-                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)lm, idx, sc,  \
+#define BSA_PF(MODE, HPW, WIDE)                                                                \
+  hipLaunchKernelGGL((attend_prefill_bf16_kernel<D, MODE, HPW, WIDE>), grid, dim3(HPW * 128), 0, \
+                     st, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)lm, idx, sc, \
                      (bf16*)out, lse, s.Hq, s.Hkv, s.G, s.Tq, s.R, s.NA, n_hc, sl2)
-#define BSA_PF_MODE(HPW)              \
-  if (s.mode == 0) BSA_PF(0, HPW);    \
-  else if (s.mode == 1) BSA_PF(1, HPW); \
-  else BSA_PF(2, HPW);
+#define BSA_PF_MODE(HPW)                          \
+  if (s.mode == 0) BSA_PF(0, HPW, false);         \
+  else if (s.mode == 1) BSA_PF(1, HPW, false);    \
+  else if (s.NA > 64) BSA_PF(2, HPW, true);       \
+  else BSA_PF(2, HPW, false);
 #define BSA_PP(MODE)                                                                           \
   hipLaunchKernelGGL((attend_prefill_pp_kernel<D, MODE>), grid, dim3(512), 0, st,         \
                      (const bf16*)q, (const bf16*)k, (const bf16*)v, idx, sc, (bf16*)out, lse, \

@@ -86,9 +86,6 @@ bsa_status_t make_shape(const bsa_params_t* p, Call call, bsa::Shape* s) {
   x.bf16 = p->dtype == BSA_DTYPE_BF16;
   x.scale = (p->scale == 0.0f) ? (float)(1.0 / sqrt((double)p->head_dim)) : p->scale;
   if (call == kPrefill || call == kDecode) {
-    if (x.mode == BSA_MODE_HILS && x.NA > 64 && (call == kPrefill) && x.bf16)
-      return fail(BSA_ERR_UNSUPPORTED, "HILS prefill supports n_sink + n_local + topk <= 64 (got %d)",
-                  x.NA);
     if (call == kDecode && x.bf16 && x.G > 32)
       return fail(BSA_ERR_UNSUPPORTED, "bf16 decode supports heads_q / heads_kv <= 32 (got %d)", x.G);
   }
@@ -398,9 +395,6 @@ namespace {
 bsa_status_t backward_shape(const bsa_params_t* params, bsa::Shape* s) {
   BSA_TRY(make_shape(params, kPrefill, s));
   if (!s->bf16) return fail(BSA_ERR_UNSUPPORTED, "the backward pass is implemented for bf16 only");
-  if (s->mode == BSA_MODE_HILS && s->NA > 64)
-    return fail(BSA_ERR_UNSUPPORTED, "the HILS backward supports n_sink + n_local + topk <= 64 (got %d)",
-                s->NA);
   if (s->NB > 65535)
     return fail(BSA_ERR_UNSUPPORTED, "the backward pass supports at most 65535 key blocks (got %d)",
                 s->NB);

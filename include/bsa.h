@@ -141,7 +141,7 @@ bsa_status_t bsa_select_topk_fused(const bsa_params_t* params, const void* q, co
  *   PLAIN: o = sum_u softmax_u(scale * q.k_u) v_u over keys u in the blocks of A_c, u <= t;
  *   SAS:   the logit of each key of block j != c gets + log sigmoid(sc_j - sc_c);
  *   HILS:  o = sum_{j in A_c} w_j o_j, o_j = softmax attention over the keys u <= t of block
- *          j alone, w = softmax_j(scale * q.L_j); needs lm and NA <= 64.
+ *          j alone, w = softmax_j(scale * q.L_j); needs lm.
  *   q [B,Hq,T,D], k/v [B,Hkv,T,D], lm [B,Hkv,NB,D] (HILS only, else may be NULL),
  *   idx/sc [B,Hkv,R,NA] from bsa_select_topk (sc may be NULL for PLAIN and HILS),
  *   out [B,Hq,T,D] output, lse [B,Hq,T] float32 output = log of the softmax denominator
@@ -414,10 +414,10 @@ size_t bsa_backward_workspace_bytes(const bsa_params_t* params);
  *   ignored);
  *   ws: device workspace of bsa_backward_workspace_bytes(params) bytes, 256-byte aligned;
  *       contents on entry are ignored.
- * Limits: at most 65535 key blocks; R * NA < 2^31; HILS: NA <= 64.  Sums over many query
- * blocks (dk, dv, dlm) are taken in a fixed order when a key block is attended by at most
- * 4096 query blocks; beyond that their float32 rounding may differ between runs.  dsc
- * accumulates with float32 atomics and its rounding may differ between runs.
+ * Limits: at most 65535 key blocks; R * NA < 2^31.  Sums over many query blocks (dk, dv,
+ * dlm) are taken in a fixed order when a key block is attended by at most 4096 query blocks;
+ * beyond that their float32 rounding may differ between runs.  dsc accumulates with float32
+ * atomics and its rounding may differ between runs.
  */
 bsa_status_t bsa_attend_prefill_backward(const bsa_params_t* params, const void* q,
                                          const void* k, const void* v, const void* lm,

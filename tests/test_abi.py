@@ -207,7 +207,8 @@ def test_attend_validation(lib):
     assert pre(_p(mode="sas")) == NULL           # SAS needs sc
     assert pre(_p(mode="hils")) == NULL          # HILS needs lm
     assert pre(_p(mode="hils"), lm=FAKE, lse=FAKE) == UNSUP
-    assert pre(_p(mode="hils", topk=62), lm=FAKE) == UNSUP   # NA > 64 for bf16 HILS prefill
+    # more than 64 attended chunks per row are taken (the check stops at the missing idx)
+    assert pre(_p(mode="hils", topk=140), lm=FAKE, idx=None) == NULL
     assert pre(_p(seq_q=1)) == SHAPE
     assert pre(_p(), out=MIS) == ALIGN
     p = _p()

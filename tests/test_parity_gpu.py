@@ -185,8 +185,10 @@ SMALL_PREFILL = [
     ("g4_nqb8_d64",  1, 4,  1,   64 * 8,      64,  "bf16", 2,   1, 2, "clustered"),
     ("t1",           1, 4,  1,   1,           128, "bf16", 2,   1, 2, "iid"),
     ("t64",          1, 4,  1,   64,          64,  "bf16", 2,   1, 2, "iid"),
-    # rows of up to 73 attended entries: entries past the 64th are read from memory in the loop
+    # rows of up to 73 and 139 attended entries: past the 64th, PLAIN / SAS read entries from
+    # memory in the loop and HiLS takes its merge weights 64 entries at a time
     ("g4_na73",      1, 4,  1,   64 * 90 + 7, 64,  "bf16", 70,  1, 2, "iid"),
+    ("g4_na139",     1, 4,  1,   64 * 150 + 5, 128, "bf16", 136, 1, 2, "clustered"),
     ("f32_g2",       1, 2,  1,   64 * 8 + 5,  64,  "f32",  2,   1, 2, "iid"),
     ("f32_d128",     1, 1,  1,   64 * 5,      128, "f32",  1,   1, 2, "iid"),
     ("f32_t65",      1, 4,  1,   65,          64,  "f32",  2,   1, 2, "iid"),
@@ -197,8 +199,6 @@ SMALL_PREFILL = [
 @pytest.mark.parametrize("case", SMALL_PREFILL, ids=[c[0] for c in SMALL_PREFILL])
 def test_prefill_small(case, mode):
     name, B, Hq, Hkv, T, D, dtype, topk, ns, nl, data = case
-    if mode == "hils" and dtype == "bf16" and ns + nl + topk > 64:
-        pytest.skip("bf16 HILS prefill holds at most 64 attended chunks per row")
     _print(f"prefill {name} {mode}")
     q, k, v = synth.make_prefill(B, Hq, Hkv, T, D, dtype, data, seed=3, device="cuda", n_centres=16,
                                  n_aim=4)
