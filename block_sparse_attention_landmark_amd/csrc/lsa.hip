@@ -236,7 +236,7 @@ __global__ __launch_bounds__(256) void lsa_select_kernel(
     int n_local, int NA) {
   __shared__ float qv[D];
   __shared__ float uscore[UCAP];     // unit score; -inf for a unit without candidate blocks
-  __shared__ int usize[UCAP];        // candidate blocks of the unit
+  __shared__ uint16_t usize[UCAP];   // candidate blocks of the unit (at most kLsaMaxSeg)
   __shared__ int32_t tsel[KCAP + 1]; // the best units (ascending unit index), then a dummy entry
   __shared__ float tsc[KCAP + 1];
   // sort space: (order-preserving key of the score, inverted) << 32 | unit index, payload = the
@@ -286,36 +286,47 @@ __global__ __launch_bounds__(256) void lsa_select_kernel(
   float qf[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) qf[e] = qv[sub * 8 + e];
-  for (int u0 = w * UPW; u0 < n_units; u0 += 4 * UPW) {
-    const int u = u0 + uw;
-    float part = 0.0f;
-    int size = 0;
-    if (u < n_elig * NC) {
-      const int sg = u / NC, r = u % NC;
-      const size_t sb = (size_t)bg * NS + sg;
-      const int o0 = offsets[sb * (NC + 1) + r], o1 = offsets[sb * (NC + 1) + r + 1];
-      if (sg * SEG < n_sink) {                  // a segment holding sink blocks: count members
-        const int32_t* mem = members + sb * SEG;
-        for (int i = o0; i < o1; ++i) size += mem[i] >= n_sink;
-      } else {
-        size = o1 - o0;                         // every member is a candidate
+  // UB units per lane group in flight (their loads issued together)
+  constexpr int UB = 4;
+  for (int u0 = w * UPW; u0 < n_units; u0 += 4 * UPW * UB) {
+    float part[UB];
+    int size[UB];
+#pragma unroll
+    for (int k = 0; k < UB; ++k) {
+      const int u = u0 + uw + k * 4 * UPW;
+      part[k] = 0.0f;
+      size[k] = 0;
+      if (u < n_elig * NC) {
+        const int sg = u / NC, r = u % NC;
+        const size_t sb = (size_t)bg * NS + sg;
+        const int o0 = offsets[sb * (NC + 1) + r], o1 = offsets[sb * (NC + 1) + r + 1];
+        if (sg * SEG < n_sink) {                // a segment holding sink blocks: count members
+          const int32_t* mem = members + sb * SEG;
+          for (int i = o0; i < o1; ++i) size[k] += mem[i] >= n_sink;
+        } else {
+          size[k] = o1 - o0;                    // every member is a candidate
+        }
+        const f32x4* ctr = reinterpret_cast<const f32x4*>(centres + (sb * NC + r) * D + sub * 8);
+        const f32x4 c0 = ctr[0], c1 = ctr[1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) part[k] = fmaf(qf[e], c0[e], fmaf(qf[4 + e], c1[e], part[k]));
+      } else if (u < n_units) {
+        const int j = single_lo + (u - n_elig * NC);
+        const TIN* lrow = Lg + (size_t)j * D + sub * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part[k] = fmaf(qf[e], (float)lrow[e], part[k]);
+        size[k] = 1;
       }
-      const f32x4* ctr = reinterpret_cast<const f32x4*>(centres + (sb * NC + r) * D + sub * 8);
-      const f32x4 c0 = ctr[0], c1 = ctr[1];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) part = fmaf(qf[e], c0[e], fmaf(qf[4 + e], c1[e], part));
-    } else if (u < n_units) {
-      const int j = single_lo + (u - n_elig * NC);
-      const TIN* lrow = Lg + (size_t)j * D + sub * 8;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) part = fmaf(qf[e], (float)lrow[e], part);
-      size = 1;
     }
 #pragma unroll
-    for (int o = LPU / 2; o > 0; o >>= 1) part += __shfl_xor(part, o, kWave);
-    if (sub == 0 && u < n_units) {
-      uscore[u] = size > 0 ? part : -INFINITY;
-      usize[u] = size;
+    for (int k = 0; k < UB; ++k) {
+      const int u = u0 + uw + k * 4 * UPW;
+#pragma unroll
+      for (int o = LPU / 2; o > 0; o >>= 1) part[k] += __shfl_xor(part[k], o, kWave);
+      if (sub == 0 && u < n_units) {
+        uscore[u] = size[k] > 0 ? part[k] : -INFINITY;
+        usize[u] = (uint16_t)size[k];
+      }
     }
   }
   __syncthreads();
@@ -821,14 +832,17 @@ hipError_t launch_lsa_select(const Shape& s, const void* q, const void* lm, int 
   }
   const int ns = s.NB / seg;
   dim3 grid(s.R, s.B * s.Hkv);
-  const bool small = ns * nc + seg <= 1024 && s.topk <= 256;
+  const int units = ns * nc + seg;
+  const bool small_k = s.topk <= 256;
 #define BSA_LSEL(D_, T_, U_, K_)                                                                 \
   hipLaunchKernelGGL((lsa_select_kernel<D_, T_, U_, K_>), grid, dim3(256), 0, st, qbar,           \
                      (const T_*)q, (const T_*)lm, centres, members, offsets, idx, sc, s.Hq, s.Hkv, \
                      s.G, s.NB, ns, seg, nc, s.R, s.decode ? s.c_dec : -1, s.topk, s.n_sink,       \
                      s.n_local, s.NA)
-#define BSA_LSEL_CAP(D_, T_)                          \
-  if (small) BSA_LSEL(D_, T_, 1024, 256);             \
+#define BSA_LSEL_CAP(D_, T_)                                  \
+  if (units <= 1024 && small_k) BSA_LSEL(D_, T_, 1024, 256);    \
+  else if (units <= 4608 && small_k) BSA_LSEL(D_, T_, 4608, 256); \
+  else if (small_k) BSA_LSEL(D_, T_, kLsaMaxUnits, 256);        \
   else BSA_LSEL(D_, T_, kLsaMaxUnits, kLsaMaxK);
   if (s.D == 128) {
     if (s.bf16) {
