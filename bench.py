@@ -289,6 +289,7 @@ def bench_lsa(torch, bsa, synth, name, tensors, steps, warmup, seg_blocks=64, n_
     p = bsa.make_params(B=B, Hq=Hq, Hkv=Hkv, D=D, seq_q=T, seq_k=T, dtype=q.dtype, topk=K)
     ws = torch.empty(max(bsa.lsa_select_workspace_bytes(p), 256), dtype=torch.uint8, device="cuda")
     ev = {n: Events(torch) for n in ("pool", "build", "select", "attend")}
+    exact_idx, _ = bsa.select_topk(q, lm, topk=K)  # the per-block top-K, for the agreement figure
 
     def step(record):
         def timed(n, fn):
@@ -335,9 +336,21 @@ def bench_lsa(torch, bsa, synth, name, tensors, steps, warmup, seg_blocks=64, n_
         what = (f"the flat clustered index: {NS} segments of {seg_blocks} landmarks x "
                 f"{n_clusters} Ward clusters per kv group; a query block scores at most "
                 f"{NS * n_clusters + seg_blocks} units instead of {NB} landmarks")
+    # rows past the first K + 3 blocks choose exactly K candidates (after the one sink block):
+    # the share of the exact top-K's blocks that the index chooses too, over 512 spread rows
+    rows = torch.linspace(K + 3, NB - 1, 512, device="cuda").long().unique()
+    a = exact_idx[:, :, rows, 1:1 + K]
+    b = idx[:, :, rows, 1:1 + K]
+    agree = (a.unsqueeze(-1) == b.unsqueeze(-2)).any(-1).float().mean().item()
     res = {"workload": f"{name} with {what}",
            "tok_per_s": B * T * steps / wall, "ms_per_step": wall * 1e3 / steps,
-           "breakdown_ms": ms}
+           "breakdown_ms": ms,
+           "agreement_with_exact_topk": {
+               "value": agree, "rows": int(rows.numel()) * B * Hkv,
+               "what": "share of the blocks the per-block top-K chooses that the index chooses "
+                       "too (synthetic keys: each block drawn round its own random centre, so "
+                       "a cluster's centre averages unrelated blocks)"}}
+    del exact_idx
     log(f"[bench] lsa: {json.dumps(res)}")
     return res
 
