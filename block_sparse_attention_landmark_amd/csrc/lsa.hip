@@ -723,6 +723,404 @@ __global__ __launch_bounds__(256) void lsa_tree_select_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// beam search with one wave per prefill selection row
+// ---------------------------------------------------------------------------------------------
+// The per-row work of lsa_tree_select_kernel is a few hundred short dot products and five sorts
+// of at most a few hundred keys; with a workgroup per row every sorting stage is a barrier.  Here
+// each wave owns one row and sorts in its registers (element e = 64 s + lane, lane exchanges by
+// shuffles), four rows per workgroup and no barrier at all.  Scores (the same lanes per node, the
+// same multiply-add order and shuffle tree), keys, tie rule and expansion are those of
+// lsa_tree_select_kernel, so both give the same rows bit for bit.
+
+// makes a wave's LDS writes visible to its other lanes before they read them
+__device__ __forceinline__ void lsa_wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// one wave sorts key[0..m) ascending with its payload, m a power of two <= 256
+__device__ __forceinline__ void lsa_bitonic_wave(uint64_t* key, int* pay, int m) {
+  const int lane = threadIdx.x % kWave;
+  const int nreg = m > kWave ? m / kWave : 1;
+  uint64_t kv[4];
+  int pv[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int e = s * kWave + lane;
+    const bool in = s < nreg && e < m;
+    kv[s] = in ? key[e] : ~(uint64_t)0;
+    pv[s] = in ? pay[e] : 0;
+  }
+  for (int k = 2; k <= m; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j >= kWave) {                            // partner in another register of this lane
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int t = s ^ (j / kWave);
+          if (t > s && t < nreg) {
+            const bool up = ((s * kWave + lane) & k) == 0;
+            if ((kv[s] > kv[t]) == up) {
+              const uint64_t a = kv[s];
+              kv[s] = kv[t];
+              kv[t] = a;
+              const int b = pv[s];
+              pv[s] = pv[t];
+              pv[t] = b;
+            }
+          }
+        }
+      } else {                                     // partner in lane ^ j, same register
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          if (s < nreg) {
+            const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)kv[s], j, kWave);
+            const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(kv[s] >> 32), j, kWave);
+            const int op = __shfl_xor(pv[s], j, kWave);
+            const uint64_t o = ((uint64_t)hi << 32) | lo;
+            const bool up = ((s * kWave + lane) & k) == 0;
+            const bool lower = (lane & j) == 0;
+            if (lower == up ? o < kv[s] : o > kv[s]) {
+              kv[s] = o;
+              pv[s] = op;
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int e = s * kWave + lane;
+    if (s < nreg && e < m) {
+      key[e] = kv[s];
+      pay[e] = pv[s];
+    }
+  }
+}
+
+constexpr int kTreeWaveCap = 256;                  // nodes of one level, units, chosen blocks
+
+template <int D, typename TIN>
+__global__ __launch_bounds__(256) void lsa_tree_select_wave_kernel(
+    const float* __restrict__ qbar, const TIN* __restrict__ lm, const float* __restrict__ centres,
+    const int32_t* __restrict__ members, const int32_t* __restrict__ offsets,
+    const float* __restrict__ seg_c, const float* __restrict__ grp_c, int32_t* __restrict__ idx,
+    float* __restrict__ sc, int NB, int NS, int NG, int SEG, int NC, int FAN, int BEAM, int R,
+    int topk, int n_sink, int n_local, int NA) {
+  constexpr int CAP = kTreeWaveCap;
+  __shared__ float qv_s[4][D];
+  __shared__ uint64_t skey_s[4][CAP];
+  __shared__ int spay_s[4][CAP];
+  __shared__ int cand_s[4][CAP];
+  __shared__ int kept_s[4][64];
+  __shared__ int ch_blk_s[4][CAP];
+  __shared__ float ch_sc_s[4][CAP];
+  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int row = blockIdx.x * 4 + w;
+  const int bg = blockIdx.y;
+  if (row >= R) return;                            // no barrier follows: the wave may leave
+  float* qv = qv_s[w];
+  uint64_t* skey = skey_s[w];
+  int* spay = spay_s[w];
+  int* cand = cand_s[w];
+  int* kept = kept_s[w];
+  int* ch_blk = ch_blk_s[w];
+  float* ch_sc = ch_sc_s[w];
+  const int c = row;
+  const TIN* Lg = lm + (size_t)bg * NB * D;
+  for (int d = lane; d < D; d += kWave) qv[d] = qbar[((size_t)bg * R + row) * D + d];
+  lsa_wave_sync();
+  constexpr int LPU = D / 8;
+  constexpr int UPW = kWave / LPU;
+  constexpr int UB = 4;
+  const int sub = lane % LPU, uw = lane / LPU;
+  float qf[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) qf[e] = qv[sub * 8 + e];
+  // Score n nodes (centre row ctr(u), id id_of(u), candidate size size_of(u), 0: not a unit) and
+  // sort them by (score desc, id asc); returns the sort length
+  auto score_sort = [&](int n, auto ctr, auto id_of, auto size_of) {
+    int m = 1;
+    while (m < n) m <<= 1;
+    for (int u0 = 0; u0 < m; u0 += UPW * UB) {    // UB nodes per lane group in flight
+      float part[UB];
+#pragma unroll
+      for (int t = 0; t < UB; ++t) {
+        const int u = u0 + uw + t * UPW;
+        part[t] = 0.0f;
+        if (u < n) {
+          const f32x4* cp = reinterpret_cast<const f32x4*>(ctr(u) + sub * 8);
+          const f32x4 c0 = cp[0], c1 = cp[1];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) part[t] = fmaf(qf[e], c0[e], fmaf(qf[4 + e], c1[e], part[t]));
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < UB; ++t) {
+        const int u = u0 + uw + t * UPW;
+#pragma unroll
+        for (int o = LPU / 2; o > 0; o >>= 1) part[t] += __shfl_xor(part[t], o, kWave);
+        if (sub == 0 && u < m) {
+          uint64_t key = ~(uint64_t)0;
+          int size = 0;
+          if (u < n) {
+            size = size_of(u);
+            if (size > 0) key = ((uint64_t)(~float_key(part[t])) << 32) | (uint32_t)id_of(u);
+          }
+          skey[u] = key;
+          spay[u] = u | (size << 16);
+        }
+      }
+    }
+    lsa_wave_sync();
+    lsa_bitonic_wave(skey, spay, m);
+    lsa_wave_sync();
+    return m;
+  };
+
+  const int last = c - n_local;
+  const int n_elig = min(NS, max(0, (last + 1) / SEG));
+  const int n_grp = min(NG, n_elig / FAN);
+  const int n_left = n_elig - n_grp * FAN;
+  // level 1: whole groups, and the eligible segments not in a whole group
+  int ncand;
+  {
+    const int n = n_grp + n_left;
+    score_sort(n,
+               [&](int u) { return u < n_grp ? grp_c + ((size_t)bg * NG + u) * D
+                                             : seg_c + ((size_t)bg * NS + n_grp * FAN + (u - n_grp)) * D; },
+               [&](int u) { return u < n_grp ? u * FAN * SEG : (n_grp * FAN + (u - n_grp)) * SEG; },
+               [&](int) { return 1; });
+    // candidate segments of the kept nodes: lane i < beam writes its node's children at the
+    // exclusive prefix of the child counts
+    const int nk = min(BEAM, n);
+    int u = 0, cnt = 0;
+    if (lane < nk) {
+      u = spay[lane] & 0xffff;
+      cnt = u < n_grp ? FAN : 1;
+    }
+    const int incl = wave_inclusive_scan(cnt);
+    ncand = __shfl(incl, kWave - 1, kWave);
+    if (lane < nk) {
+      const int o = incl - cnt;
+      if (u < n_grp)
+        for (int t = 0; t < FAN; ++t) cand[o + t] = u * FAN + t;
+      else
+        cand[o] = n_grp * FAN + (u - n_grp);
+    }
+    lsa_wave_sync();
+  }
+  // level 2: segments
+  int nseg;
+  {
+    const int n = ncand;
+    score_sort(n, [&](int u) { return seg_c + ((size_t)bg * NS + cand[u]) * D; },
+               [&](int u) { return cand[u] * SEG; }, [&](int) { return 1; });
+    nseg = min(BEAM, n);
+    if (lane < nseg) kept[lane] = cand[spay[lane] & 0xffff];
+    lsa_wave_sync();
+  }
+  // level 3: the clusters of the kept segments; the kept clusters become units
+  int n_cl;
+  {
+    const int n = nseg * NC;
+    auto cl_off = [&](int u, int k) {
+      const size_t sb = (size_t)bg * NS + kept[u / NC];
+      return offsets[sb * (NC + 1) + u % NC + k];
+    };
+    score_sort(n, [&](int u) { return centres + (((size_t)bg * NS + kept[u / NC]) * NC + u % NC) * D; },
+               [&](int u) { return members[((size_t)bg * NS + kept[u / NC]) * SEG + cl_off(u, 0)]; },
+               [&](int u) {
+                 const int o0 = cl_off(u, 0), o1 = cl_off(u, 1);
+                 if (kept[u / NC] * SEG >= n_sink) return o1 - o0;   // no sink block here
+                 const int32_t* mem = members + ((size_t)bg * NS + kept[u / NC]) * SEG;
+                 int sz = 0;
+                 for (int i = o0; i < o1; ++i) sz += mem[i] >= n_sink;
+                 return sz;
+               });
+    const int nk = min(BEAM, n);
+    const bool live = lane < nk && skey[lane] != ~(uint64_t)0;
+    const uint64_t lm_ = __ballot(live);
+    const int o = __popcll(lm_ & ((1ull << lane) - 1ull));
+    if (live) cand[o] = spay[lane] & 0xffff;
+    n_cl = __popcll(lm_);
+    lsa_wave_sync();
+  }
+  // units: the kept clusters (cand[u] = segment slot * NC + cluster) and the not yet clustered
+  // candidate blocks, sorted by (score desc, id asc) and expanded to K blocks
+  const int single_lo = max(n_sink, n_elig * SEG);
+  const int n_single = max(0, last - single_lo + 1);
+  const int n_units = n_cl + n_single;
+  auto unit_members = [&](int u, int& o0, int& o1) -> const int32_t* {
+    const int cu = cand[u];
+    const size_t sb = (size_t)bg * NS + kept[cu / NC];
+    o0 = offsets[sb * (NC + 1) + cu % NC];
+    o1 = offsets[sb * (NC + 1) + cu % NC + 1];
+    return members + sb * SEG;
+  };
+  int m = 1;
+  while (m < n_units) m <<= 1;
+  for (int u0 = 0; u0 < m; u0 += UPW * UB) {
+    float part[UB];
+    int size[UB];
+    uint32_t id[UB];
+#pragma unroll
+    for (int t = 0; t < UB; ++t) {
+      const int u = u0 + uw + t * UPW;
+      part[t] = 0.0f;
+      size[t] = 0;
+      id[t] = 0;
+      if (u < n_cl) {
+        int o0, o1;
+        const int32_t* mem = unit_members(u, o0, o1);
+        if (kept[cand[u] / NC] * SEG >= n_sink) {
+          size[t] = o1 - o0;
+        } else {
+          for (int i = o0; i < o1; ++i) size[t] += mem[i] >= n_sink;
+        }
+        id[t] = (uint32_t)mem[o0];
+        const int cu = cand[u];
+        const f32x4* cp = reinterpret_cast<const f32x4*>(
+            centres + (((size_t)bg * NS + kept[cu / NC]) * NC + cu % NC) * D + sub * 8);
+        const f32x4 c0 = cp[0], c1 = cp[1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) part[t] = fmaf(qf[e], c0[e], fmaf(qf[4 + e], c1[e], part[t]));
+      } else if (u < n_units) {
+        const int j = single_lo + (u - n_cl);
+        const TIN* lrow = Lg + (size_t)j * D + sub * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part[t] = fmaf(qf[e], (float)lrow[e], part[t]);
+        size[t] = 1;
+        id[t] = (uint32_t)j;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < UB; ++t) {
+      const int u = u0 + uw + t * UPW;
+#pragma unroll
+      for (int o = LPU / 2; o > 0; o >>= 1) part[t] += __shfl_xor(part[t], o, kWave);
+      if (sub == 0 && u < m) {
+        uint64_t key = ~(uint64_t)0;
+        if (u < n_units && size[t] > 0) key = ((uint64_t)(~float_key(part[t])) << 32) | id[t];
+        skey[u] = key;
+        spay[u] = u | (size[t] << 16);
+      }
+    }
+  }
+  lsa_wave_sync();
+  lsa_bitonic_wave(skey, spay, m);
+  lsa_wave_sync();
+  // blocks taken from each unit in sorted order: lane l holds sorted entries 4l .. 4l+3
+  int sz4[4], local_sum = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = 4 * lane + k;
+    sz4[k] = (i < m && skey[i] != ~(uint64_t)0) ? (spay[i] >> 16) : 0;
+    local_sum += sz4[k];
+  }
+  const int incl = wave_inclusive_scan(local_sum);
+  const int total = __shfl(incl, kWave - 1, kWave);
+  const int K = min(topk, total);
+  int base = incl - local_sum;
+  // single blocks are written by the lanes that hold them; the chosen clusters (at most beam) are
+  // collected and then expanded by the whole wave, one member per lane
+  int n_take = 0;                                  // chosen clusters so far (wave-uniform)
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = 4 * lane + k;
+    const bool chosen = sz4[k] > 0 && base < K;
+    const int u = chosen ? (spay[i] & 0xffff) : 0;
+    const bool is_cl = chosen && u < n_cl;
+    if (chosen && !is_cl) {
+      ch_blk[base] = single_lo + (u - n_cl);
+      ch_sc[base] = key_float(~(uint32_t)(skey[i] >> 32));
+    }
+    const uint64_t bm = __ballot(is_cl);
+    if (is_cl) {                                  // slot in the wave's list of chosen clusters
+      const int t = n_take + __popcll(bm & ((1ull << lane) - 1ull));
+      cand[CAP / 2 + t] = i;                       // sorted position (cand's upper half is free)
+      kept[32 + (t & 31)] = base;                  // (t < beam <= 32 here; see the launcher)
+    }
+    n_take += __popcll(bm);
+    base += sz4[k];
+  }
+  lsa_wave_sync();
+  for (int t = 0; t < n_take; ++t) {
+    const int i = cand[CAP / 2 + t];
+    const int b0 = kept[32 + t];
+    const int u = spay[i] & 0xffff;
+    const int take = min(spay[i] >> 16, K - b0);
+    const float uscore = key_float(~(uint32_t)(skey[i] >> 32));
+    int o0, o1;
+    const int32_t* mem = unit_members(u, o0, o1);
+    const int x = o0 + lane;
+    const int v = x < o1 ? mem[x] : -1;
+    const bool ok = v >= n_sink;
+    const int r = __popcll(__ballot(ok) & ((1ull << lane) - 1ull));
+    if (ok && r < take) {
+      ch_blk[b0 + r] = v;
+      ch_sc[b0 + r] = uscore;
+    }
+  }
+  lsa_wave_sync();
+  // chosen blocks ascending (the sort space is reused: block in the key, slot as payload)
+  int mk = 1;
+  while (mk < K) mk <<= 1;
+  for (int i = lane; i < mk; i += kWave) {
+    skey[i] = i < K ? (uint64_t)(uint32_t)ch_blk[i] : ~(uint64_t)0;
+    spay[i] = i;
+  }
+  lsa_wave_sync();
+  if (K > 1) lsa_bitonic_wave(skey, spay, mk);
+  lsa_wave_sync();
+  // row: sink blocks, chosen blocks, local window, padding
+  const int n_s = min(n_sink, c + 1);
+  const int l0 = max(n_s, c - n_local + 1);
+  const int n_l = max(0, c - l0 + 1);
+  const size_t rb = ((size_t)bg * R + row) * NA;
+  auto dot_lm = [&](int j) {
+    // the landmark row through 16-byte loads, then the products in dimension order
+    constexpr int EPV = 16 / sizeof(TIN);
+    u32x4 raw[D / EPV];
+#pragma unroll
+    for (int t = 0; t < D / EPV; ++t)
+      raw[t] = *reinterpret_cast<const u32x4*>(Lg + (size_t)j * D + t * EPV);
+    float acc = 0.0f;
+#pragma unroll
+    for (int t = 0; t < D / EPV; ++t) {
+      const TIN* x = reinterpret_cast<const TIN*>(&raw[t]);
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) acc = fmaf(qv[t * EPV + e], (float)x[e], acc);
+    }
+    return acc;
+  };
+  for (int i = lane; i < NA; i += kWave) {
+    int j = -1;
+    float s = 0.0f;
+    if (i < n_s) {
+      j = i;
+      s = dot_lm(j);
+    } else if (i < n_s + K) {
+      const int slot = spay[i - n_s];
+      j = ch_blk[slot];
+      s = ch_sc[slot];
+    } else if (i < n_s + K + n_l) {
+      j = l0 + (i - n_s - K);
+      s = dot_lm(j);
+    }
+    idx[rb + i] = j;
+    sc[rb + i] = s;
+  }
+}
+
+bool lsa_tree_wave_ok(const Shape& s, int seg, int nc, int fan, int beam) {
+  const int ns = s.NB / seg;
+  constexpr int cap = kTreeWaveCap;
+  return !s.decode && s.topk <= cap && beam <= 32 && ns / fan + fan <= cap && beam * fan <= cap &&
+         beam * nc <= cap && beam + seg <= cap;
+}
+
 bool lsa_tree_shape_ok(const Shape& s, int seg, int nc, int fan, int beam) {
   // the beam search sorts one level's nodes at a time, whatever the number of segments
   if (!lsa_index_ok(seg, nc) || s.topk > kLsaMaxK || fan < 1 || beam < 1 || beam > 64)
@@ -761,6 +1159,22 @@ hipError_t launch_lsa_tree_select(const Shape& s, const void* q, const void* lm,
     if (e != hipSuccess) return e;
   }
   const int ns = s.NB / seg;
+  if (lsa_tree_wave_ok(s, seg, nc, fan, beam)) {
+    dim3 grid((s.R + 3) / 4, s.B * s.Hkv);
+#define BSA_TW(D_, T_)                                                                         \
+  hipLaunchKernelGGL((lsa_tree_select_wave_kernel<D_, T_>), grid, dim3(256), 0, st, qbar,        \
+                     (const T_*)lm, centres, members, offsets, seg_c, grp_c, idx, sc, s.NB, ns,   \
+                     ns / fan, seg, nc, fan, beam, s.R, s.topk, s.n_sink, s.n_local, s.NA)
+    if (s.D == 128) {
+      if (s.bf16) BSA_TW(128, bf16);
+      else BSA_TW(128, float);
+    } else {
+      if (s.bf16) BSA_TW(64, bf16);
+      else BSA_TW(64, float);
+    }
+#undef BSA_TW
+    return hipGetLastError();
+  }
   dim3 grid(s.R, s.B * s.Hkv);
 #define BSA_TS(D_, T_, K_)                                                                       \
   hipLaunchKernelGGL((lsa_tree_select_kernel<D_, T_, K_>), grid, dim3(256), 0, st, qbar,          \
