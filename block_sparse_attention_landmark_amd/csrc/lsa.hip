@@ -801,14 +801,18 @@ __device__ __forceinline__ void lsa_bitonic_wave(uint64_t* key, int* pay, int m)
 
 constexpr int kTreeWaveCap = 256;                  // nodes of one level, units, chosen blocks
 
-template <int D, typename TIN>
-__global__ __launch_bounds__(256) void lsa_tree_select_wave_kernel(
+// CAP (128 or 256) bounds a level's nodes, the units and the chosen blocks of a row; LDS is sized
+// by it, so the smaller variant holds more rows per CU.  The row chain is latency-bound, so the
+// register budget is held to eight waves per SIMD (a few registers spill; 20 % faster at 1M
+// tokens than four waves per SIMD without spills).
+template <int D, typename TIN, int CAP>
+__global__ __launch_bounds__(256, 8) void lsa_tree_select_wave_kernel(
     const float* __restrict__ qbar, const TIN* __restrict__ lm, const float* __restrict__ centres,
     const int32_t* __restrict__ members, const int32_t* __restrict__ offsets,
     const float* __restrict__ seg_c, const float* __restrict__ grp_c, int32_t* __restrict__ idx,
     float* __restrict__ sc, int NB, int NS, int NG, int SEG, int NC, int FAN, int BEAM, int R,
     int topk, int n_sink, int n_local, int NA) {
-  constexpr int CAP = kTreeWaveCap;
+  static_assert(CAP <= kTreeWaveCap && CAP / 2 >= 64, "sort width and chosen-cluster slots");
   __shared__ float qv_s[4][D];
   __shared__ uint64_t skey_s[4][CAP];
   __shared__ int spay_s[4][CAP];
@@ -1080,18 +1084,23 @@ __global__ __launch_bounds__(256) void lsa_tree_select_wave_kernel(
   const int n_l = max(0, c - l0 + 1);
   const size_t rb = ((size_t)bg * R + row) * NA;
   auto dot_lm = [&](int j) {
-    // the landmark row through 16-byte loads, then the products in dimension order
+    // the landmark row through 16-byte loads, eight at a time, then the products in dimension
+    // order
     constexpr int EPV = 16 / sizeof(TIN);
-    u32x4 raw[D / EPV];
-#pragma unroll
-    for (int t = 0; t < D / EPV; ++t)
-      raw[t] = *reinterpret_cast<const u32x4*>(Lg + (size_t)j * D + t * EPV);
+    constexpr int NV = D / EPV, BATCH = NV < 8 ? NV : 8;
     float acc = 0.0f;
 #pragma unroll
-    for (int t = 0; t < D / EPV; ++t) {
-      const TIN* x = reinterpret_cast<const TIN*>(&raw[t]);
+    for (int t0 = 0; t0 < NV; t0 += BATCH) {
+      u32x4 raw[BATCH];
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) acc = fmaf(qv[t * EPV + e], (float)x[e], acc);
+      for (int t = 0; t < BATCH; ++t)
+        raw[t] = *reinterpret_cast<const u32x4*>(Lg + (size_t)j * D + (t0 + t) * EPV);
+#pragma unroll
+      for (int t = 0; t < BATCH; ++t) {
+        const TIN* x = reinterpret_cast<const TIN*>(&raw[t]);
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) acc = fmaf(qv[(t0 + t) * EPV + e], (float)x[e], acc);
+      }
     }
     return acc;
   };
@@ -1114,11 +1123,12 @@ __global__ __launch_bounds__(256) void lsa_tree_select_wave_kernel(
   }
 }
 
-bool lsa_tree_wave_ok(const Shape& s, int seg, int nc, int fan, int beam) {
+// the widest level, unit list or chosen list of a row (0 if the wave kernel does not apply)
+static int lsa_tree_wave_cap(const Shape& s, int seg, int nc, int fan, int beam) {
+  if (s.decode || beam > 32) return 0;
   const int ns = s.NB / seg;
-  constexpr int cap = kTreeWaveCap;
-  return !s.decode && s.topk <= cap && beam <= 32 && ns / fan + fan <= cap && beam * fan <= cap &&
-         beam * nc <= cap && beam + seg <= cap;
+  const int need = max(max(s.topk, ns / fan + fan), max(max(beam * fan, beam * nc), beam + seg));
+  return need <= 128 ? 128 : need <= kTreeWaveCap ? kTreeWaveCap : 0;
 }
 
 bool lsa_tree_shape_ok(const Shape& s, int seg, int nc, int fan, int beam) {
@@ -1159,19 +1169,29 @@ hipError_t launch_lsa_tree_select(const Shape& s, const void* q, const void* lm,
     if (e != hipSuccess) return e;
   }
   const int ns = s.NB / seg;
-  if (lsa_tree_wave_ok(s, seg, nc, fan, beam)) {
+  if (const int cap = lsa_tree_wave_cap(s, seg, nc, fan, beam)) {
     dim3 grid((s.R + 3) / 4, s.B * s.Hkv);
-#define BSA_TW(D_, T_)                                                                         \
-  hipLaunchKernelGGL((lsa_tree_select_wave_kernel<D_, T_>), grid, dim3(256), 0, st, qbar,        \
+#define BSA_TW(D_, T_, C_)                                                                     \
+  hipLaunchKernelGGL((lsa_tree_select_wave_kernel<D_, T_, C_>), grid, dim3(256), 0, st, qbar,    \
                      (const T_*)lm, centres, members, offsets, seg_c, grp_c, idx, sc, s.NB, ns,   \
                      ns / fan, seg, nc, fan, beam, s.R, s.topk, s.n_sink, s.n_local, s.NA)
+#define BSA_TWC(D_, T_)                       \
+  if (cap == 128) BSA_TW(D_, T_, 128);        \
+  else BSA_TW(D_, T_, kTreeWaveCap);
     if (s.D == 128) {
-      if (s.bf16) BSA_TW(128, bf16);
-      else BSA_TW(128, float);
+      if (s.bf16) {
+        BSA_TWC(128, bf16)
+      } else {
+        BSA_TWC(128, float)
+      }
     } else {
-      if (s.bf16) BSA_TW(64, bf16);
-      else BSA_TW(64, float);
+      if (s.bf16) {
+        BSA_TWC(64, bf16)
+      } else {
+        BSA_TWC(64, float)
+      }
     }
+#undef BSA_TWC
 #undef BSA_TW
     return hipGetLastError();
   }
