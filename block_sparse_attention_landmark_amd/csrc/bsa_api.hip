@@ -300,7 +300,7 @@ bsa_status_t bsa_lsa_update_index(const bsa_params_t* params, const void* lm, in
 size_t bsa_lsa_select_workspace_bytes(const bsa_params_t* params) {
   bsa::Shape s;
   if (make_shape(params, kSelect, &s) != BSA_OK) return 0;
-  return s.decode ? 0 : bsa::select_ws_qbar_bytes(s);
+  return s.decode ? 0 : bsa::select_ws_qbar_bytes(s) + bsa::lsa_ws_score_bytes(s);
 }
 
 bsa_status_t bsa_lsa_select(const bsa_params_t* params, const void* q, const void* lm,
@@ -327,7 +327,8 @@ bsa_status_t bsa_lsa_select(const bsa_params_t* params, const void* q, const voi
     if (((uintptr_t)ws & 255u) != 0) return fail(BSA_ERR_ALIGN, "ws is not 256-byte aligned");
   }
   return hip_result(bsa::launch_lsa_select(s, q, lm, seg_blocks, n_clusters, centres, members,
-                                           offsets, idx, sc, (float*)ws, (hipStream_t)stream),
+                                           offsets, idx, sc, (float*)ws, ws_bytes,
+                                           (hipStream_t)stream),
                     "lsa_select");
 }
 

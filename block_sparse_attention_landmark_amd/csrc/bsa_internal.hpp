@@ -94,10 +94,11 @@ bool lsa_shape_ok(const Shape& s, int seg, int nc);
 hipError_t launch_lsa_build(const Shape& s, const void* lm, int seg, int nc, float* centres,
                             int32_t* members, int32_t* offsets, int32_t* merges, hipStream_t st,
                             int seg0 = 0);
+size_t lsa_ws_score_bytes(const Shape& s);
 hipError_t launch_lsa_select(const Shape& s, const void* q, const void* lm, int seg, int nc,
                              const float* centres, const int32_t* members,
                              const int32_t* offsets, int32_t* idx, float* sc, float* qbar,
-                             hipStream_t st);
+                             size_t ws_bytes, hipStream_t st);
 
 // LSA tree index: shape limits, node centres, beam-search selection.
 bool lsa_tree_shape_ok(const Shape& s, int seg, int nc, int fan, int beam);

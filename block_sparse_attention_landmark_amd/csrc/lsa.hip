@@ -23,6 +23,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "bsa_common.hpp"
 #include "bsa_internal.hpp"
 #include "select_common.hpp"
@@ -32,6 +34,7 @@ namespace bsa {
 constexpr int kLsaMaxSeg = 64;          // landmarks per segment held in LDS
 constexpr int kLsaMaxUnits = 8192;      // units one selection row can sort
 constexpr int kLsaMaxK = 2048;          // blocks one selection row can choose
+constexpr size_t kLsaScoreBuf = 256u << 20;  // bytes of precomputed cluster scores per call
 
 // ---------------------------------------------------------------------------------------------
 // Ward clustering of one segment
@@ -227,13 +230,18 @@ __device__ __forceinline__ void lsa_bitonic(uint64_t* key, int* pay, int m) {
 // top-K -- which takes the lower index first among equal scores -- ranks them by (score
 // descending, id ascending); only the min(K, units) best units are then sorted, since every unit
 // with a candidate block contributes at least one block.
-template <int D, typename TIN, int UCAP, int KCAP>
+//
+// PRE: the cluster scores of rows row0 .. row0 + gridDim.x - 1 were formed beforehand by
+// lsa_unit_scores_kernel (upre, nrows x NS*NC per (sequence, kv group)) and the clusters'
+// candidate counts by lsa_unit_sizes_kernel (usizes); the single blocks are still scored here.
+template <int D, typename TIN, int UCAP, int KCAP, bool PRE>
 __global__ __launch_bounds__(256) void lsa_select_kernel(
     const float* __restrict__ qbar, const TIN* __restrict__ q, const TIN* __restrict__ lm,
     const float* __restrict__ centres, const int32_t* __restrict__ members,
     const int32_t* __restrict__ offsets, int32_t* __restrict__ idx, float* __restrict__ sc, int Hq,
     int Hkv, int G, int NB, int NS, int SEG, int NC, int R, int c_dec, int topk, int n_sink,
-    int n_local, int NA) {
+    int n_local, int NA, const float* __restrict__ upre, const uint16_t* __restrict__ usizes,
+    int row0, int nrows) {
   __shared__ float qv[D];
   __shared__ float uscore[UCAP];     // unit score; -inf for a unit without candidate blocks
   __shared__ uint16_t usize[UCAP];   // candidate blocks of the unit (at most kLsaMaxSeg)
@@ -249,7 +257,7 @@ __global__ __launch_bounds__(256) void lsa_select_kernel(
   __shared__ int sbuf[4];
   __shared__ int sh[2];
   __shared__ int wsum[4];
-  const int row = blockIdx.x, bg = blockIdx.y;
+  const int row = row0 + (int)blockIdx.x, bg = blockIdx.y;
   const int b = bg / Hkv, g = bg % Hkv;
   const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
   const int c = c_dec >= 0 ? c_dec : row;
@@ -286,9 +294,20 @@ __global__ __launch_bounds__(256) void lsa_select_kernel(
   float qf[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) qf[e] = qv[sub * 8 + e];
+  int u_first = 0;                                 // first unit scored by the loop below
+  if constexpr (PRE) {
+    const float* urow = upre + ((size_t)bg * nrows + (row - row0)) * (size_t)(NS * NC);
+    const uint16_t* usz = usizes + (size_t)bg * NS * NC;
+    for (int u = tid; u < n_elig * NC; u += 256) {
+      const int size = usz[u];
+      uscore[u] = size > 0 ? urow[u] : -INFINITY;
+      usize[u] = (uint16_t)size;
+    }
+    u_first = n_elig * NC;
+  }
   // UB units per lane group in flight (their loads issued together)
   constexpr int UB = 4;
-  for (int u0 = w * UPW; u0 < n_units; u0 += 4 * UPW * UB) {
+  for (int u0 = u_first + w * UPW; u0 < n_units; u0 += 4 * UPW * UB) {
     float part[UB];
     int size[UB];
 #pragma unroll
@@ -806,7 +825,7 @@ constexpr int kTreeWaveCap = 256;                  // nodes of one level, units,
 // register budget is held to eight waves per SIMD (a few registers spill; 20 % faster at 1M
 // tokens than four waves per SIMD without spills).
 template <int D, typename TIN, int CAP>
-__global__ __launch_bounds__(256, 8) void lsa_tree_select_wave_kernel(
+__global__ __launch_bounds__(256, CAP == 128 ? 8 : 4) void lsa_tree_select_wave_kernel(
     const float* __restrict__ qbar, const TIN* __restrict__ lm, const float* __restrict__ centres,
     const int32_t* __restrict__ members, const int32_t* __restrict__ offsets,
     const float* __restrict__ seg_c, const float* __restrict__ grp_c, int32_t* __restrict__ idx,
@@ -1223,6 +1242,92 @@ hipError_t launch_lsa_tree_select(const Shape& s, const void* q, const void* lm,
 }
 
 // ---------------------------------------------------------------------------------------------
+// cluster scores of many rows at once (flat index, large indexes)
+// ---------------------------------------------------------------------------------------------
+// A row of a large flat index scores thousands of centres; one workgroup per row reads every
+// centre from L2 once per row.  Here one workgroup scores 64 rows against 64 centres on MFMA, as
+// the block scores are formed: each wave takes 32 rows x 32 centres, the selector vectors split
+// into three bf16 terms (hi, mid, lo) and the float32 centres likewise, and the six products down
+// to 2^-24 of the leading one accumulate in float32.  scores[bg][r - row0][u] is written for the
+// clusters u of the segments lying wholly at or before row r's last candidate block.
+template <int D>
+__global__ __launch_bounds__(256) void lsa_unit_scores_kernel(
+    const float* __restrict__ qbar, const float* __restrict__ centres, float* __restrict__ scores,
+    int R, int NS, int SEG, int NC, int n_local, int row0, int nrows) {
+  const int bg = blockIdx.z;
+  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int half = lane / 32, l32 = lane % 32;
+  const int UC = NS * NC;
+  const int rbase = row0 + (int)blockIdx.x * 64 + (w / 2) * 32;   // this wave's first row
+  const int rlast = row0 + nrows - 1;
+  if (rbase > rlast) return;                       // no barrier in this kernel
+  auto n_units = [&](int r) { return min(NS, max(0, (r - n_local + 1) / SEG)) * NC; };
+  const int u0 = (int)blockIdx.y * 64 + (w % 2) * 32;
+  if (u0 >= n_units(min(rbase + 31, rlast))) return;   // eligibility only grows with the row
+  auto split3 = [](const float* src, bf16x8& h8, bf16x8& m8, bf16x8& l8, bool zero) {
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
+    const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = zero ? 0.0f : ((e < 4) ? x0[e] : x1[e - 4]);
+      const bf16 h = f2bf(x);
+      const float r1 = x - bf2f(h);                // exact in float32
+      const bf16 m = f2bf(r1);
+      h8[e] = h;
+      m8[e] = m;
+      l8[e] = f2bf(r1 - bf2f(m));
+    }
+  };
+  const int r = rbase + l32;
+  const float* qrow = qbar + ((size_t)bg * R + min(r, rlast)) * D;
+  const int u = u0 + l32;
+  const float* crow = centres + ((size_t)bg * UC + min(u, UC - 1)) * D;
+  f32x16 acc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) {
+    const int d0 = 16 * st + 8 * half;
+    bf16x8 qh, qm, ql, ch, cm, cl;
+    split3(qrow + d0, qh, qm, ql, r > rlast);
+    split3(crow + d0, ch, cm, cl, u >= UC);
+    acc = mfma32(qh, ch, acc);
+    acc = mfma32(qm, ch, acc);
+    acc = mfma32(ql, ch, acc);
+    acc = mfma32(qh, cm, acc);
+    acc = mfma32(qm, cm, acc);
+    acc = mfma32(qh, cl, acc);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int rr = rbase + 8 * (i / 4) + 4 * half + (i % 4);
+    if (rr <= rlast && u < n_units(rr))
+      scores[((size_t)bg * nrows + (rr - row0)) * UC + u] = acc[i];
+  }
+}
+
+// candidate blocks of every cluster (members >= n_sink), one thread per cluster: the same for
+// every row, so formed once per call for the precomputed-score selection
+__global__ __launch_bounds__(256) void lsa_unit_sizes_kernel(const int32_t* __restrict__ members,
+                                                             const int32_t* __restrict__ offsets,
+                                                             uint16_t* __restrict__ usizes, int NS,
+                                                             int SEG, int NC, int n_sink) {
+  const int bg = blockIdx.y;
+  const int u = blockIdx.x * 256 + threadIdx.x;
+  if (u >= NS * NC) return;
+  const int sg = u / NC, r = u % NC;
+  const size_t sb = (size_t)bg * NS + sg;
+  const int o0 = offsets[sb * (NC + 1) + r], o1 = offsets[sb * (NC + 1) + r + 1];
+  int size = o1 - o0;
+  if (sg * SEG < n_sink) {                         // a segment holding sink blocks
+    const int32_t* mem = members + sb * SEG;
+    size = 0;
+    for (int i = o0; i < o1; ++i) size += mem[i] >= n_sink;
+  }
+  usizes[(size_t)bg * NS * NC + u] = (uint16_t)size;
+}
+
+// ---------------------------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------------------------
 bool lsa_index_ok(int seg, int nc) { return seg >= 1 && seg <= kLsaMaxSeg && nc >= 1 && nc <= seg; }
@@ -1256,43 +1361,89 @@ hipError_t launch_lsa_build(const Shape& s, const void* lm, int seg, int nc, flo
   return hipGetLastError();
 }
 
+// workspace behind the selector vectors: the clusters' candidate counts (at most NB per
+// (sequence, kv group)), then a buffer of precomputed cluster scores
+static size_t lsa_ws_sizes_bytes(const Shape& s) {
+  return ((size_t)s.B * s.Hkv * s.NB * sizeof(uint16_t) + 255) & ~(size_t)255;
+}
+size_t lsa_ws_score_bytes(const Shape& s) {
+  if (s.decode) return 0;
+  const size_t full = (size_t)s.B * s.Hkv * s.R * s.NB * sizeof(float);
+  return lsa_ws_sizes_bytes(s) + (((full < kLsaScoreBuf ? full : kLsaScoreBuf) + 255) & ~(size_t)255);
+}
+
 hipError_t launch_lsa_select(const Shape& s, const void* q, const void* lm, int seg, int nc,
                              const float* centres, const int32_t* members,
                              const int32_t* offsets, int32_t* idx, float* sc, float* qbar,
-                             hipStream_t st) {
+                             size_t ws_bytes, hipStream_t st) {
   if (!s.decode) {
     const hipError_t e = launch_selector_vectors(s, q, qbar, st);
     if (e != hipSuccess) return e;
   }
   const int ns = s.NB / seg;
-  dim3 grid(s.R, s.B * s.Hkv);
-  const int units = ns * nc + seg;
+  const int uc = ns * nc;                        // cluster units of a row at most
+  const int units = uc + seg;
   const bool small_k = s.topk <= 256;
+  // large indexes: rows' cluster scores on MFMA first, in chunks of rows that fit the score
+  // buffer behind the selector vectors in the workspace
+  const size_t qb = s.decode ? 0 : select_ws_qbar_bytes(s);
+  const size_t szb = s.decode ? 0 : lsa_ws_sizes_bytes(s);
+  const size_t buf = ws_bytes > qb + szb ? ws_bytes - qb - szb : 0;
+  const size_t per_row = (size_t)s.B * s.Hkv * uc * sizeof(float);
+  const int chunk = (!s.decode && uc > 1024 && per_row > 0)
+                        ? (int)std::min<size_t>(buf / per_row, (size_t)s.R) : 0;
+  uint16_t* usizes = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(qbar) + qb);
+  float* upre = reinterpret_cast<float*>(reinterpret_cast<char*>(qbar) + qb + szb);
+  const int nchunks = chunk >= 64 ? (s.R + chunk - 1) / chunk : 1;
+  if (chunk >= 64)
+    hipLaunchKernelGGL(lsa_unit_sizes_kernel, dim3((uc + 255) / 256, s.B * s.Hkv), dim3(256), 0,
+                       st, members, offsets, usizes, ns, seg, nc, s.n_sink);
+  for (int ci = 0; ci < nchunks; ++ci) {
+    const bool pre = chunk >= 64;
+    const int row0 = pre ? ci * chunk : 0;
+    const int nrows = pre ? std::min(chunk, s.R - row0) : s.R;
+    if (pre) {
+      dim3 g1((nrows + 63) / 64, (uc + 63) / 64, s.B * s.Hkv);
+      if (s.D == 128)
+        hipLaunchKernelGGL(lsa_unit_scores_kernel<128>, g1, dim3(256), 0, st, qbar, centres, upre,
+                           s.R, ns, seg, nc, s.n_local, row0, nrows);
+      else
+        hipLaunchKernelGGL(lsa_unit_scores_kernel<64>, g1, dim3(256), 0, st, qbar, centres, upre,
+                           s.R, ns, seg, nc, s.n_local, row0, nrows);
+    }
+    dim3 grid(nrows, s.B * s.Hkv);
 #define BSA_LSEL(D_, T_, U_, K_)                                                                 \
-  hipLaunchKernelGGL((lsa_select_kernel<D_, T_, U_, K_>), grid, dim3(256), 0, st, qbar,           \
-                     (const T_*)q, (const T_*)lm, centres, members, offsets, idx, sc, s.Hq, s.Hkv, \
-                     s.G, s.NB, ns, seg, nc, s.R, s.decode ? s.c_dec : -1, s.topk, s.n_sink,       \
-                     s.n_local, s.NA)
-#define BSA_LSEL_CAP(D_, T_)                                  \
+  if (pre)                                                                                       \
+    hipLaunchKernelGGL((lsa_select_kernel<D_, T_, U_, K_, true>), grid, dim3(256), 0, st, qbar,   \
+                       (const T_*)q, (const T_*)lm, centres, members, offsets, idx, sc, s.Hq,     \
+                       s.Hkv, s.G, s.NB, ns, seg, nc, s.R, s.decode ? s.c_dec : -1, s.topk,        \
+                       s.n_sink, s.n_local, s.NA, upre, usizes, row0, nrows);                      \
+  else                                                                                           \
+    hipLaunchKernelGGL((lsa_select_kernel<D_, T_, U_, K_, false>), grid, dim3(256), 0, st, qbar,  \
+                       (const T_*)q, (const T_*)lm, centres, members, offsets, idx, sc, s.Hq,     \
+                       s.Hkv, s.G, s.NB, ns, seg, nc, s.R, s.decode ? s.c_dec : -1, s.topk,        \
+                       s.n_sink, s.n_local, s.NA, nullptr, nullptr, 0, nrows)
+#define BSA_LSEL_CAP(D_, T_)                                    \
   if (units <= 1024 && small_k) BSA_LSEL(D_, T_, 1024, 256);    \
   else if (units <= 4608 && small_k) BSA_LSEL(D_, T_, 4608, 256); \
   else if (small_k) BSA_LSEL(D_, T_, kLsaMaxUnits, 256);        \
   else BSA_LSEL(D_, T_, kLsaMaxUnits, kLsaMaxK);
-  if (s.D == 128) {
-    if (s.bf16) {
-      BSA_LSEL_CAP(128, bf16)
+    if (s.D == 128) {
+      if (s.bf16) {
+        BSA_LSEL_CAP(128, bf16)
+      } else {
+        BSA_LSEL_CAP(128, float)
+      }
     } else {
-      BSA_LSEL_CAP(128, float)
+      if (s.bf16) {
+        BSA_LSEL_CAP(64, bf16)
+      } else {
+        BSA_LSEL_CAP(64, float)
+      }
     }
-  } else {
-    if (s.bf16) {
-      BSA_LSEL_CAP(64, bf16)
-    } else {
-      BSA_LSEL_CAP(64, float)
-    }
-  }
 #undef BSA_LSEL_CAP
 #undef BSA_LSEL
+  }
   return hipGetLastError();
 }
 

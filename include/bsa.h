@@ -321,7 +321,13 @@ bsa_status_t bsa_lsa_update_index(const bsa_params_t* params, const void* lm, in
                                   int32_t* members, int32_t* offsets, int32_t* merges,
                                   void* stream);
 
-/* Workspace bytes of bsa_lsa_select (prefill: the selector vectors; decode: 0). */
+/*
+ * Workspace bytes of bsa_lsa_select and bsa_lsa_tree_select (decode: 0).  Prefill: the selector
+ * vectors (B*Hkv*R*D float32, rounded up to 256 bytes), then, used by bsa_lsa_select alone, a
+ * table of the clusters' candidate counts and a buffer of at most 256 MiB for precomputed
+ * cluster scores.  Both selections accept any workspace of at least the selector vectors'
+ * bytes; bsa_lsa_select uses the rest when given all of it.
+ */
 size_t bsa_lsa_select_workspace_bytes(const bsa_params_t* params);
 
 /*
@@ -337,7 +343,13 @@ size_t bsa_lsa_select_workspace_bytes(const bsa_params_t* params);
  * Row c lists the sink blocks, the chosen blocks ascending, the local window, then -1; sc holds
  * a chosen block's unit score and qbar . L_j for sink and local blocks (0 in the padding).
  *   q, lm: as for bsa_select_topk; centres, members, offsets: from bsa_lsa_build_index with the
- *   same seg_blocks and n_clusters (may be NULL when NS = 0); ws: bsa_lsa_select_workspace_bytes.
+ *   same seg_blocks and n_clusters (may be NULL when NS = 0); ws: device workspace, 256-byte
+ *   aligned, of at least the selector vectors' bytes (see bsa_lsa_select_workspace_bytes).
+ *   With more than 1024 clusters per row and room for at least 64 rows of cluster scores after
+ *   the selector vectors and the count table, the cluster scores are first formed for tiles of
+ *   rows on MFMA (the selector vector and the centres each split into three bf16 terms; the six
+ *   leading products summed in float32), chunk by chunk; otherwise each row computes them as
+ *   float32 dot products.  The two differ only in the last bits of a score.
  * Limits: as bsa_lsa_build_index, plus NS * n_clusters + seg_blocks <= 8192 and topk <= 2048.
  */
 bsa_status_t bsa_lsa_select(const bsa_params_t* params, const void* q, const void* lm,

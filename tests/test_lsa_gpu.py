@@ -228,6 +228,46 @@ def test_lsa_prefill_small(case, mode):
                     check_out(dev[hh], ref, "bf16", f"{where} h{hh}")
 
 
+def test_lsa_large_index_precomputed_unit_scores():
+    """An index of more than 1024 clusters per row (8-block segments of 8 clusters over 1100
+    blocks): the cluster scores are formed for tiles of rows on MFMA first, in chunks of rows
+    that fit the workspace.  One chunk and several chunks give the same rows bit for bit; both,
+    and the per-row path taken when the workspace holds only the selector vectors, match the
+    oracle's selection over the device's partition (near ties excepted)."""
+    B, Hq, Hkv, T, D, topk, seg, nc = 1, 4, 2, 64 * 1100 + 9, 128, 12, 8, 8
+    q, k, _ = synth.make_prefill(B, Hq, Hkv, T, D, "bf16", "clustered", seed=21, device="cuda",
+                                 n_centres=64, n_aim=4)
+    lm = bsa.pool_landmarks(k)
+    index = bsa.lsa_build_index(lm, seg_blocks=seg, n_clusters=nc)
+    R = (T + 63) // 64
+    NS = R // seg
+    assert NS * nc > 1024
+    qb = (B * Hkv * R * D * 4 + 255) // 256 * 256            # the selector vectors
+    per_row = B * Hkv * NS * nc * 4
+    runs = {}
+    for name, nbytes in (("one_chunk", None), ("chunks_of_200", qb + 200 * per_row),
+                         ("per_row", qb)):
+        ws = None if nbytes is None else torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        runs[name] = bsa.lsa_select(q, lm, index, topk=topk, ws=ws)
+    torch.cuda.synchronize()
+    a, b2 = runs["one_chunk"], runs["chunks_of_200"]
+    assert torch.equal(a[0], b2[0]) and torch.equal(a[1], b2[1]), "chunking changed the rows"
+    qbar = O.selector_vectors(host64(q), Hkv)
+    for name in ("one_chunk", "per_row"):
+        idx = runs[name][0].cpu().numpy()
+        sc = runs[name][1].cpu().numpy()
+        for g in range(Hkv):
+            L64 = host64(lm[0, g])
+            ref_index = _dev_index(index, L64, 0, g)
+            for c in range(R):
+                row = idx[0, g, c]
+                A = row[row >= 0].astype(np.int64)
+                where = f"large index {name} g{g} c{c}"
+                _check_lsa_row(A, qbar[0, g, c], L64, ref_index, c, topk, 1, 2, seg, where)
+                np.testing.assert_allclose(sc[0, g, c, A.size - 1], float(qbar[0, g, c] @ L64[c]),
+                                           rtol=1e-5, atol=1e-5, err_msg=where)
+
+
 def test_lsa_decode_matches_prefill_rows():
     """Decode selection from the index = the oracle's selection for the query at Tk - 1."""
     B, Hq, Hkv, Tk, D, topk, seg, nc = 4, 8, 2, 64 * 70 + 21, 128, 9, 16, 4
