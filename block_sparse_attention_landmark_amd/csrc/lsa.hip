@@ -824,12 +824,17 @@ constexpr int kTreeWaveCap = 256;                  // nodes of one level, units,
 // by it, so the smaller variant holds more rows per CU.  The row chain is latency-bound, so the
 // register budget is held to eight waves per SIMD (a few registers spill; 20 % faster at 1M
 // tokens than four waves per SIMD without spills).
-template <int D, typename TIN, int CAP>
+//
+// FUSEQ (bf16): the wave forms its row's selector vector from Q itself -- the sum over the
+// group's heads of the mean over the block's tokens, summed in float64 and rounded once to
+// float32, as the selector-vector pass does -- so Q is read while other rows search the tree.
+template <int D, typename TIN, int CAP, bool FUSEQ>
 __global__ __launch_bounds__(256, CAP == 128 ? 8 : 4) void lsa_tree_select_wave_kernel(
-    const float* __restrict__ qbar, const TIN* __restrict__ lm, const float* __restrict__ centres,
-    const int32_t* __restrict__ members, const int32_t* __restrict__ offsets,
-    const float* __restrict__ seg_c, const float* __restrict__ grp_c, int32_t* __restrict__ idx,
-    float* __restrict__ sc, int NB, int NS, int NG, int SEG, int NC, int FAN, int BEAM, int R,
+    const float* __restrict__ qbar, const TIN* __restrict__ q, const TIN* __restrict__ lm,
+    const float* __restrict__ centres, const int32_t* __restrict__ members,
+    const int32_t* __restrict__ offsets, const float* __restrict__ seg_c,
+    const float* __restrict__ grp_c, int32_t* __restrict__ idx, float* __restrict__ sc, int Hq,
+    int Hkv, int G, int T, int NB, int NS, int NG, int SEG, int NC, int FAN, int BEAM, int R,
     int topk, int n_sink, int n_local, int NA) {
   static_assert(CAP <= kTreeWaveCap && CAP / 2 >= 64, "sort width and chosen-cluster slots");
   __shared__ float qv_s[4][D];
@@ -852,7 +857,44 @@ __global__ __launch_bounds__(256, CAP == 128 ? 8 : 4) void lsa_tree_select_wave_
   float* ch_sc = ch_sc_s[w];
   const int c = row;
   const TIN* Lg = lm + (size_t)bg * NB * D;
-  for (int d = lane; d < D; d += kWave) qv[d] = qbar[((size_t)bg * R + row) * D + d];
+  if constexpr (FUSEQ) {
+    constexpr int NCH = D / 8;                     // 16-byte chunks of a row
+    constexpr int RGW = kWave / NCH;               // (head, token) rows in flight per load
+    constexpr int NL = 8;                          // loads in flight per lane
+    const int chunk = lane % NCH, rg = lane / NCH;
+    const int b = bg / Hkv, g = bg % Hkv;
+    const int t0 = c * kBlock, ntok = min(kBlock, T - t0);
+    const int nr = G * ntok;
+    double acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+    for (int r0 = rg; r0 < nr; r0 += RGW * NL) {
+      u32x4 raw[NL];
+#pragma unroll
+      for (int k = 0; k < NL; ++k) {
+        const int rr = min(r0 + k * RGW, nr - 1);
+        const int hh = rr / ntok, t = t0 + rr % ntok;
+        raw[k] = *reinterpret_cast<const u32x4*>(q + ((size_t)(b * Hq + g * G + hh) * T + t) * D +
+                                                 chunk * 8);
+      }
+#pragma unroll
+      for (int k = 0; k < NL; ++k)
+        if (r0 + k * RGW < nr) {
+          const bf16x8 x = __builtin_bit_cast(bf16x8, raw[k]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] += (double)bf2f(x[e]);
+        }
+    }
+#pragma unroll
+    for (int o = NCH; o < kWave; o <<= 1)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], o, kWave);
+    if (rg == 0)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[chunk * 8 + e] = (float)(acc[e] / (double)ntok);
+  } else {
+    for (int d = lane; d < D; d += kWave) qv[d] = qbar[((size_t)bg * R + row) * D + d];
+  }
   lsa_wave_sync();
   constexpr int LPU = D / 8;
   constexpr int UPW = kWave / LPU;
@@ -1183,20 +1225,23 @@ hipError_t launch_lsa_tree_select(const Shape& s, const void* q, const void* lm,
                                   int fan, int beam, const float* centres, const int32_t* members,
                                   const int32_t* offsets, const float* seg_c, const float* grp_c,
                                   int32_t* idx, float* sc, float* qbar, hipStream_t st) {
-  if (!s.decode) {
+  const int ns = s.NB / seg;
+  const int cap = lsa_tree_wave_cap(s, seg, nc, fan, beam);
+  // the wave kernel forms bf16 rows' selector vectors itself; otherwise the selector pass first
+  if (!s.decode && !(cap && s.bf16)) {
     const hipError_t e = launch_selector_vectors(s, q, qbar, st);
     if (e != hipSuccess) return e;
   }
-  const int ns = s.NB / seg;
-  if (const int cap = lsa_tree_wave_cap(s, seg, nc, fan, beam)) {
+  if (cap) {
     dim3 grid((s.R + 3) / 4, s.B * s.Hkv);
-#define BSA_TW(D_, T_, C_)                                                                     \
-  hipLaunchKernelGGL((lsa_tree_select_wave_kernel<D_, T_, C_>), grid, dim3(256), 0, st, qbar,    \
-                     (const T_*)lm, centres, members, offsets, seg_c, grp_c, idx, sc, s.NB, ns,   \
-                     ns / fan, seg, nc, fan, beam, s.R, s.topk, s.n_sink, s.n_local, s.NA)
-#define BSA_TWC(D_, T_)                       \
-  if (cap == 128) BSA_TW(D_, T_, 128);        \
-  else BSA_TW(D_, T_, kTreeWaveCap);
+#define BSA_TW(D_, T_, C_, F_)                                                                 \
+  hipLaunchKernelGGL((lsa_tree_select_wave_kernel<D_, T_, C_, F_>), grid, dim3(256), 0, st, qbar, \
+                     (const T_*)q, (const T_*)lm, centres, members, offsets, seg_c, grp_c, idx,   \
+                     sc, s.Hq, s.Hkv, s.G, s.Tq, s.NB, ns, ns / fan, seg, nc, fan, beam, s.R,     \
+                     s.topk, s.n_sink, s.n_local, s.NA)
+#define BSA_TWC(D_, T_)                                          \
+  if (cap == 128) BSA_TW(D_, T_, 128, (sizeof(T_) == 2));        \
+  else BSA_TW(D_, T_, kTreeWaveCap, (sizeof(T_) == 2));
     if (s.D == 128) {
       if (s.bf16) {
         BSA_TWC(128, bf16)
