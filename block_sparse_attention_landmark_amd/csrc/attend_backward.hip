@@ -263,11 +263,10 @@ __global__ __launch_bounds__(HPW * 128) void bwd_dq_kernel(
   __shared__ __attribute__((aligned(16))) bf16 Ks[2][kBlock * KP];
   __shared__ __attribute__((aligned(16))) bf16 Vs[2][kBlock * KP];
   // HiLS: landmark rows of the attended chunks, and per (wave, entry, row) the retrieval weight
-  // (overwritten by the retrieval-score gradient after the entry loop) and dw = dout . o_j
-  static_assert(MODE != 2 || HPW <= 2, "the HiLS tables fit LDS for at most two heads");
+  // (overwritten by the retrieval-score gradient after the entry loop); dw = dout . o_j of each
+  // (row, entry) is kept in the row statistics for the key side and read back from there
   __shared__ __attribute__((aligned(16))) bf16 Lb[MODE == 2 ? kBlock * KP : 8];
   __shared__ float wbuf[MODE == 2 ? NWAVE * 64 * 32 : 1];
-  __shared__ float dwbuf[MODE == 2 ? NWAVE * 64 * 32 : 1];
   float g_acc = 0.0f;                  // HiLS: sum_j w_j dw_j = dout . o, accumulated exactly
 
   const int c = NQB - 1 - (int)blockIdx.x;   // heavy (late) query blocks first
@@ -499,7 +498,6 @@ __global__ __launch_bounds__(HPW * 128) void bwd_dq_kernel(
           const bool live = row_ok && l > 0.0f && wj > 0.0f;
           hstat[hi] = live ? mxs + log2f(l) - log2f(wj) : 0.0f;
           hstat[hs_n + hi] = live ? dwv : 0.0f;
-          dwbuf[(w * 64 + a % 64) * 32 + l32] = dwv;
         }
       } else {
         const float gb = gate_of(a, j) - lse2;
@@ -554,8 +552,9 @@ __global__ __launch_bounds__(HPW * 128) void bwd_dq_kernel(
         for (int a = e0; a < min(nval, e0 + 64); ++a) {
           const int sl = (w * 64 + a - e0) * 32 + l32;
           const size_t hi = (((size_t)(b * Hq + h) * NQB + c) * NA + a) * kBlock + (w % 2) * 32 + l32;
-          // dw of this row and entry: from the table (one group), else as stored for the key side
-          const float dwj = ngr > 1 ? hstat[hs_n + hi] : dwbuf[sl];
+          // dw of this row and entry as stored for the key side (0 where the weight is 0, and
+          // there dr is 0 either way)
+          const float dwj = hstat[hs_n + hi];
           const float wj = wbuf[sl];
           const float drv = row_ok ? wj * (dwj - g_acc) : 0.0f;
           hstat[2 * hs_n + hi] = drv;
@@ -1053,7 +1052,7 @@ static hipError_t launch_backward_d(const Shape& s, const void* q, const void* k
                      s.NA, s.NB, n_entries);
   hipLaunchKernelGGL(bwd_sort_kernel, dim3(s.NB, BG), dim3(256), 0, st, W.cnt_off, W.list, s.R,
                      s.NA, s.NB);
-  const int hpw = (s.G % 4 == 0 && s.mode != 2) ? 4 : (s.G % 2 == 0) ? 2 : 1;
+  const int hpw = (s.G % 4 == 0) ? 4 : (s.G % 2 == 0) ? 2 : 1;
   const int n_hc = s.G / hpw;
 #define BSA_DQ(MODE, HPW)                                                                        \
   hipLaunchKernelGGL((bwd_dq_kernel<D, MODE, HPW>), dim3(s.R, s.Hkv * n_hc, s.B), dim3(HPW * 128),\
@@ -1067,8 +1066,7 @@ static hipError_t launch_backward_d(const Shape& s, const void* q, const void* k
   if (s.mode == 1) {
     BSA_DQ_H(1)
   } else if (s.mode == 2) {
-    if (hpw >= 2) BSA_DQ(2, 2);
-    else BSA_DQ(2, 1);
+    BSA_DQ_H(2)
   } else {
     BSA_DQ_H(0)
   }
