@@ -842,15 +842,16 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     }
     if constexpr (MODE == 2) {
       // dL_j += sum over this wave's rows of dr_t q_t, from the transposed Q fragments (rows in
-      // the same permuted order as the P registers); one key tile's waves suffice
-      if (kh == 0) {
-        const float* Rb = Lb + 2 * kBlock;
+      // the same permuted order as the P registers); both key tiles' waves hold them, so each
+      // takes half of the d tiles
+      const float* Rb = Lb + 2 * kBlock;
+      auto dl_tiles = [&](int dt0) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const f32x4 r0 = *reinterpret_cast<const f32x4*>(&Rb[tb + 16 * ks]);
           const f32x4 r1 = *reinterpret_cast<const f32x4*>(&Rb[tb + 16 * ks + 8]);
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
+          for (int dt = dt0; dt < dt0 + DT / 2; ++dt) {
             const bf16x4 q0 = __builtin_bit_cast(bf16x4, tr[ks][dt][2]);
             const bf16x4 q1 = __builtin_bit_cast(bf16x4, tr[ks][dt][3]);
 #pragma unroll
@@ -860,7 +861,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
             }
           }
         }
-      }
+      };
+      if (kh == 0) dl_tiles(0);
+      else dl_tiles(DT / 2);
     }
   }
   __syncthreads();   // stages free (the last wait was vmcnt(0))
@@ -883,22 +886,24 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
         red[kh * RED + ((DT + dt) * 16 + i) * kWave + lane] = dva[dt][i];
       }
     if constexpr (MODE == 2) {
-      if (kh == 0 && half == 0)
+      if (half == 0)
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) Lred[dt * 32 + l32] = dlv[dt];
+        for (int dt = 0; dt < DT; ++dt)
+          if (dt / (DT / 2) == kh) Lred[dt * 32 + l32] = dlv[dt];
     }
   }
   __syncthreads();
   if constexpr (MODE == 2) {
     // the two row halves of dL_j: written directly for a single work item, else as a partial
-    if (kh == 0 && th == 0 && half == 0)
+    if (th == 0 && half == 0)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int d = dt * 32 + l32;
-        const float val = dlv[dt] + Lred[d];
-        if (nch == 1) dlm[((size_t)bg * NB + j) * D + d] = val * scale;
-        else partL[((size_t)bg * max_work + wi) * D + d] = val;
-      }
+      for (int dt = 0; dt < DT; ++dt)
+        if (dt / (DT / 2) == kh) {
+          const int d = dt * 32 + l32;
+          const float val = dlv[dt] + Lred[d];
+          if (nch == 1) dlm[((size_t)bg * NB + j) * D + d] = val * scale;
+          else partL[((size_t)bg * max_work + wi) * D + d] = val;
+        }
   }
   constexpr int FP = D + 4;                      // row pitch (floats) of the [key][d] tiles
   float* F = red + 2 * RED;                      // [2][64][FP]: dK then dV
