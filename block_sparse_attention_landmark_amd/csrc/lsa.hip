@@ -746,11 +746,14 @@ __global__ __launch_bounds__(256) void lsa_tree_select_kernel(
 // beam search with one wave per prefill selection row
 // ---------------------------------------------------------------------------------------------
 // The per-row work of lsa_tree_select_kernel is a few hundred short dot products and five sorts
-// of at most a few hundred keys; with a workgroup per row every sorting stage is a barrier.  Here
-// each wave owns one row and sorts in its registers (element e = 64 s + lane, lane exchanges by
-// shuffles), four rows per workgroup and no barrier at all.  Scores (the same lanes per node, the
-// same multiply-add order and shuffle tree), keys, tie rule and expansion are those of
-// lsa_tree_select_kernel, so both give the same rows bit for bit.
+// of at most a few hundred keys: a latency-bound chain of loads.  Here each wave owns one row
+// (four rows per workgroup, no barrier at all, eight waves per SIMD): each level's nodes are
+// sorted in the wave's registers (element e = 64 s + lane, lane exchanges by shuffles), node
+// loads are batched, a cluster's candidate count comes from its offsets unless its segment holds
+// sink blocks, a chosen cluster is expanded by the whole wave, and landmark rows are read 16
+// bytes at a time.  Scores (the same lanes per node, the same multiply-add order and shuffle
+// tree), keys, tie rule and expansion are those of lsa_tree_select_kernel, so both give the same
+// rows bit for bit.
 
 // makes a wave's LDS writes visible to its other lanes before they read them
 __device__ __forceinline__ void lsa_wave_sync() {
@@ -827,7 +830,9 @@ constexpr int kTreeWaveCap = 256;                  // nodes of one level, units,
 //
 // FUSEQ (bf16): the wave forms its row's selector vector from Q itself -- the sum over the
 // group's heads of the mean over the block's tokens, summed in float64 and rounded once to
-// float32, as the selector-vector pass does -- so Q is read while other rows search the tree.
+// float32, as the selector-vector pass does (the float64 sums of bf16 values are exact unless
+// their magnitudes span more than about 2^40, so the different summation order gives the same
+// vector) -- and Q is read while other rows search the tree.
 template <int D, typename TIN, int CAP, bool FUSEQ>
 __global__ __launch_bounds__(256, CAP == 128 ? 8 : 4) void lsa_tree_select_wave_kernel(
     const float* __restrict__ qbar, const TIN* __restrict__ q, const TIN* __restrict__ lm,
