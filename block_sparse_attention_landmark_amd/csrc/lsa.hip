@@ -1297,8 +1297,9 @@ hipError_t launch_lsa_tree_select(const Shape& s, const void* q, const void* lm,
 // A row of a large flat index scores thousands of centres; one workgroup per row reads every
 // centre from L2 once per row.  Here one workgroup scores 64 rows against 64 centres on MFMA, as
 // the block scores are formed: each wave takes 32 rows x 32 centres, the selector vectors split
-// into three bf16 terms (hi, mid, lo) and the float32 centres likewise, and the six products down
-// to 2^-24 of the leading one accumulate in float32.  scores[bg][r - row0][u] is written for the
+// into three bf16 terms (hi, mid, lo) and the float32 centres likewise, and the six products of
+// order 2^-16 or more of the leading one (the three dropped are 2^-24 and below) accumulate in
+// float32.  scores[bg][r - row0][u] is written for the
 // clusters u of the segments lying wholly at or before row r's last candidate block.
 template <int D>
 __global__ __launch_bounds__(256) void lsa_unit_scores_kernel(
