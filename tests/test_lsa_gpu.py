@@ -431,6 +431,8 @@ LSA_TREE = [
     ("t_b2",     2, 4,  2,   64 * 90,      64,  9,    8,   4,  3,   2),
     ("t_seg16",  1, 8,  2,   64 * 300,     128, 20,   16,  4,  4,   4),
     ("t_wide",   1, 4,  1,   64 * 100,     128, 8,    8,   2,  2,   64),
+    # a top level of 133 nodes (262 segments in pairs): the one-wave kernel's 256-entry lists
+    ("t_level133", 1, 4, 1,  64 * 2100 + 5, 64,  8,    8,   2,  2,   4),
 ]
 
 
