@@ -467,6 +467,42 @@ def test_lsa_tree_prefill_small(case, mode):
                               f"{tag} b{b} g{g} c{c} h{hh}")
 
 
+@pytest.mark.parametrize("tree", [False, True], ids=["flat", "tree"])
+def test_lsa_float32_inputs(tree):
+    """float32 q, k, v: the selector-vector pass feeds the flat and the one-wave tree selection
+    (their float32 instances), and the float32 attention kernel attends the chosen sets."""
+    B, Hq, Hkv, T, D, topk, seg, nc, fan, beam = 1, 4, 2, 64 * 70 + 5, 64, 6, 8, 3, 2, 3
+    q, k, v = synth.make_prefill(B, Hq, Hkv, T, D, "f32", "clustered", seed=14, device="cuda",
+                                 n_centres=16, n_aim=4)
+    res = bsa.prefill_lsa(q, k, v, topk=topk, seg_blocks=seg, n_clusters=nc, want_lse=True,
+                          tree=tree, fanout=fan, beam=beam)
+    torch.cuda.synchronize()
+    tag = "f32 " + ("tree" if tree else "flat")
+    qbar = O.selector_vectors(host64(q), Hkv)
+    idx = res["idx"].cpu().numpy()
+    if tree:
+        _check_tree(res, q, res["lm"], topk, seg, fan, beam, tag)
+    G = Hq // Hkv
+    for g in range(Hkv):
+        L64 = host64(res["lm"][0, g])
+        ref_index = _dev_index(res["index"], L64, 0, g)
+        K64, V64 = host64(k[0, g]), host64(v[0, g])
+        for c in range((T + 63) // 64):
+            A = idx[0, g, c][idx[0, g, c] >= 0].astype(np.int64)
+            if not tree:
+                _check_lsa_row(A, qbar[0, g, c], L64, ref_index, c, topk, 1, 2, seg,
+                               f"{tag} g{g} c{c}")
+            if c % 7:
+                continue
+            lo, hi = c * 64, min(c * 64 + 64, T)
+            for hh in range(G):
+                ref, lse_ref = O.attend_rows(host64(q[0, g * G + hh, lo:hi]), np.arange(lo, hi),
+                                             K64, V64, A, np.zeros(A.size), 1.0 / math.sqrt(D))
+                where = f"{tag} g{g} c{c} h{hh}"
+                check_out(host64(res["out"][0, g * G + hh, lo:hi]), ref, "f32", where)
+                check_lse(host64(res["lse"][0, g * G + hh, lo:hi]), lse_ref, "f32", where)
+
+
 def test_lsa_tree_wide_beam_equals_flat_on_device():
     """A beam wider than every level gives the flat index's sets, bit for bit, on the device."""
     q, k, v = synth.make_prefill(1, 4, 1, 64 * 100, 128, "bf16", "clustered", seed=13,
