@@ -782,15 +782,18 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
       l4[i4] = *reinterpret_cast<const f32x4*>(&Lb[tb + 8 * i4]);
       d4[i4] = *reinterpret_cast<const f32x4*>(&Db[tb + 8 * i4]);
     }
-    // S = Q K^T and dP = dO V^T for rows th*32..+32 and this wave's 32 keys
+    // S = Q K^T and dP = dO V^T for rows th*32..+32 and this wave's 32 keys.  The products are
+    // written in dependency order -- S, dP, P, dV^T += dO^T P, dx, dK^T += Q^T dx -- so that the
+    // compiler can overlap the vector work with independent products of the same step (one
+    // wave per SIMD: nothing else fills the matrix core meanwhile); every accumulator sums its
+    // products in k-step order.
     f32x16 sa, pa;
 #pragma unroll
     for (int i = 0; i < 16; ++i) sa[i] = pa[i] = 0.0f;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      sa = mfma32(qa[s], kb[s], sa);
-      pa = mfma32(oa[s], vb[s], pa);
-    }
+    for (int s = 0; s < D / 16; ++s) sa = mfma32(qa[s], kb[s], sa);
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) pa = mfma32(oa[s], vb[s], pa);
     i16x4 tr[2][DT][4];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -804,13 +807,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
         tr[ks][dt][3] = lds_read_tr16(Qb + bwd_tile_off<D>(r0 + 8, col));
       }
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, D / 8 + 8, 0);     // A operands, lse, Delta
-#pragma unroll
-    for (int s = 0; s < D / 8; ++s) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // one S or dP product
-      __builtin_amdgcn_sched_group_barrier(0x100, DT, 0);          // DT transposed reads
-    }
-    // P and dx; register i holds row t = th*32 + 8 (i / 4) + 4 half + i % 4
+    // P; register i holds row t = th*32 + 8 (i / 4) + 4 half + i % 4
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
 #pragma unroll
@@ -818,28 +815,39 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
         const int tq = c * kBlock + tb + 8 * i4 + e;
         const bool vis = tq < T && ku <= tq;
         const float bias = MODE == 2 ? -l4[i4][e] : gb - l4[i4][e] * kLog2e;
-        const float p = vis ? fast_exp2(fmaf(sa[4 * i4 + e], scale_log2, bias)) : 0.0f;
-        sa[4 * i4 + e] = p;
-        pa[4 * i4 + e] = p * (pa[4 * i4 + e] - d4[i4][e]);
+        sa[4 * i4 + e] = vis ? fast_exp2(fmaf(sa[4 * i4 + e], scale_log2, bias)) : 0.0f;
       }
     }
-    // dV^T += dO^T P and dK^T += Q^T dx over this wave's 32 rows (2 k-steps of 16)
+    bf16x8 pb[2], xb[2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 pb, xb;
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pb[e] = f2bf(sa[8 * ks + e]);
-        xb[e] = f2bf(pa[8 * ks + e]);
-      }
+      for (int e = 0; e < 8; ++e) pb[ks][e] = f2bf(sa[8 * ks + e]);
+    // dV^T += dO^T P over this wave's 32 rows (2 k-steps of 16)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const bf16x8 ao = __builtin_bit_cast(bf16x8, __builtin_shufflevector(tr[ks][dt][0], tr[ks][dt][1], 0, 1, 2, 3, 4, 5, 6, 7));
-        const bf16x8 aq = __builtin_bit_cast(bf16x8, __builtin_shufflevector(tr[ks][dt][2], tr[ks][dt][3], 0, 1, 2, 3, 4, 5, 6, 7));
-        dva[dt] = mfma32(ao, pb, dva[dt]);
-        dka[dt] = mfma32(aq, xb, dka[dt]);
+        dva[dt] = mfma32(ao, pb[ks], dva[dt]);
       }
-    }
+    // dx = P (dP - Delta)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pa[4 * i4 + e] = sa[4 * i4 + e] * (pa[4 * i4 + e] - d4[i4][e]);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xb[ks][e] = f2bf(pa[8 * ks + e]);
+    // dK^T += Q^T dx
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x8 aq = __builtin_bit_cast(bf16x8, __builtin_shufflevector(tr[ks][dt][2], tr[ks][dt][3], 0, 1, 2, 3, 4, 5, 6, 7));
+        dka[dt] = mfma32(aq, xb[ks], dka[dt]);
+      }
     if constexpr (MODE == 2) {
       // dL_j += sum over this wave's rows of dr_t q_t, from the transposed Q fragments (rows in
       // the same permuted order as the P registers); both key tiles' waves hold them, so each
