@@ -753,9 +753,43 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
   const int vcol = 16 * ((lane / 16) % 2) + 4 * (lane % 4);
   for (int s = 0; s < kBwdAhead; ++s)
     if (s < nsteps) issue(s);
-  for (int st = 0; st < nsteps; ++st) {
-    bwd_wait_copies(NPS * (min(nsteps - 1, st + kBwdAhead - 1) - st));
+  const int arow = th * 32 + l32;
+  const int tb = th * 32 + 4 * half;
+  // S = Q K^T and dP = dO V^T of step st for rows th*32..+32 and this wave's 32 keys, from its
+  // stage; each accumulator sums its products in k-step order
+  auto s_dp = [&](int st, f32x16& sa, f32x16& pa) {
+    const char* stg = smem + (st % kBwdStages) * STAGE_B;
+    const bf16* Qb = reinterpret_cast<const bf16*>(stg);
+    const bf16* Ob = reinterpret_cast<const bf16*>(stg + TILE_B);
+    bf16x8 qa[D / 16], oa[D / 16];
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      const int off = bwd_tile_off<D>(arow, 16 * s + 8 * half);
+      qa[s] = *reinterpret_cast<const bf16x8*>(&Qb[off]);
+      oa[s] = *reinterpret_cast<const bf16x8*>(&Ob[off]);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sa[i] = pa[i] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) sa = mfma32(qa[s], kb[s], sa);
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) pa = mfma32(oa[s], vb[s], pa);
+  };
+  // Software pipeline over the steps (one wave per SIMD, so nothing else fills the matrix
+  // core): iteration st forms S and dP of step st + 1 -- products that need nothing of step
+  // st -- while the vector work of step st (P, dx) runs, then step st's dV and dK products.
+  // So stages st and st + 1 are read in iteration st, and the copies of step st + 1 must have
+  // landed at its start; steps st + 2 and st + 3 may still be in flight.
+  f32x16 sa, pa;
+  if (nsteps > 0) {
+    bwd_wait_copies(NPS * min(nsteps - 1, kBwdAhead - 1));   // step 0 has landed
     __syncthreads();
+    s_dp(0, sa, pa);
+  }
+  for (int st = 0; st < nsteps; ++st) {
+    if (st + 1 < nsteps)                        // step st + 1 has landed
+      bwd_wait_copies(NPS * (min(nsteps - 1, st + kBwdAhead - 1) - (st + 1)));
+    __syncthreads();                            // and every wave is done with stage st - 1
     if (st + kBwdAhead < nsteps) issue(st + kBwdAhead);
     const char* stg = smem + (st % kBwdStages) * STAGE_B;
     const bf16* Qb = reinterpret_cast<const bf16*>(stg);
@@ -764,36 +798,45 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     const float* Db = Lb + kBlock;
     const int c = Ec[st / G];
     const float gb = Eg[st / G];
-    // LDS fragments of the step, ordered for a single wave per SIMD: the A operands of S and dP
-    // and the row statistics first, then the transposed operands of dV and dK interleaved with
-    // the S and dP products so that their latency hides behind the matrix work
-    const int arow = th * 32 + l32;
+    // Step st + 1's stage: its Q and dO rows, the A operands of its S and dP products (in the
+    // last step this reads a stage that holds no step; those products are discarded).
+    const char* stn = smem + ((st + 1) % kBwdStages) * STAGE_B;
+    const bf16* Qn = reinterpret_cast<const bf16*>(stn);
+    const bf16* On = reinterpret_cast<const bf16*>(stn + TILE_B);
     bf16x8 qa[D / 16], oa[D / 16];
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
       const int off = bwd_tile_off<D>(arow, 16 * s + 8 * half);
-      qa[s] = *reinterpret_cast<const bf16x8*>(&Qb[off]);
-      oa[s] = *reinterpret_cast<const bf16x8*>(&Ob[off]);
+      qa[s] = *reinterpret_cast<const bf16x8*>(&Qn[off]);
+      oa[s] = *reinterpret_cast<const bf16x8*>(&On[off]);
     }
-    const int tb = th * 32 + 4 * half;
     f32x4 l4[4], d4[4];
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
       l4[i4] = *reinterpret_cast<const f32x4*>(&Lb[tb + 8 * i4]);
       d4[i4] = *reinterpret_cast<const f32x4*>(&Db[tb + 8 * i4]);
     }
-    // S = Q K^T and dP = dO V^T for rows th*32..+32 and this wave's 32 keys.  The products are
-    // written in dependency order -- S, dP, P, dV^T += dO^T P, dx, dK^T += Q^T dx -- so that the
-    // compiler can overlap the vector work with independent products of the same step (one
-    // wave per SIMD: nothing else fills the matrix core meanwhile); every accumulator sums its
-    // products in k-step order.
-    f32x16 sa, pa;
+    // P and dx of step st in 16 / (D / 16) element chunks, each issued behind one S (then dP)
+    // product of step st + 1: the products need nothing of step st, so the matrix core and the
+    // vector unit work side by side.  Register i holds row t = th*32 + 8 (i / 4) + 4 half + i % 4.
+    constexpr int PC = 16 / (D / 16);            // elements per chunk
+    f32x16 sn, pn;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sa[i] = pa[i] = 0.0f;
+    for (int i = 0; i < 16; ++i) sn[i] = pn[i] = 0.0f;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) sa = mfma32(qa[s], kb[s], sa);
+    for (int s = 0; s < D / 16; ++s) {
+      sn = mfma32(qa[s], kb[s], sn);
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) pa = mfma32(oa[s], vb[s], pa);
+      for (int r = s * PC; r < (s + 1) * PC; ++r) {
+        const int i4 = r / 4, e = r % 4;
+        const int tq = c * kBlock + tb + 8 * i4 + e;
+        const bool vis = tq < T && ku <= tq;
+        const float bias = MODE == 2 ? -l4[i4][e] : gb - l4[i4][e] * kLog2e;
+        sa[r] = vis ? fast_exp2(fmaf(sa[r], scale_log2, bias)) : 0.0f;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // the transposed operands of step st's dV and dK products
     i16x4 tr[2][DT][4];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -807,22 +850,22 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
         tr[ks][dt][3] = lds_read_tr16(Qb + bwd_tile_off<D>(r0 + 8, col));
       }
     }
-    // P; register i holds row t = th*32 + 8 (i / 4) + 4 half + i % 4
+    // dx = P (dP - Delta)
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
+    for (int s = 0; s < D / 16; ++s) {
+      pn = mfma32(oa[s], vb[s], pn);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int tq = c * kBlock + tb + 8 * i4 + e;
-        const bool vis = tq < T && ku <= tq;
-        const float bias = MODE == 2 ? -l4[i4][e] : gb - l4[i4][e] * kLog2e;
-        sa[4 * i4 + e] = vis ? fast_exp2(fmaf(sa[4 * i4 + e], scale_log2, bias)) : 0.0f;
-      }
+      for (int r = s * PC; r < (s + 1) * PC; ++r) pa[r] = sa[r] * (pa[r] - d4[r / 4][r % 4]);
+      __builtin_amdgcn_sched_barrier(0);
     }
     bf16x8 pb[2], xb[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pb[ks][e] = f2bf(sa[8 * ks + e]);
+      for (int e = 0; e < 8; ++e) {
+        pb[ks][e] = f2bf(sa[8 * ks + e]);
+        xb[ks][e] = f2bf(pa[8 * ks + e]);
+      }
     // dV^T += dO^T P over this wave's 32 rows (2 k-steps of 16)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
@@ -831,15 +874,6 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
         const bf16x8 ao = __builtin_bit_cast(bf16x8, __builtin_shufflevector(tr[ks][dt][0], tr[ks][dt][1], 0, 1, 2, 3, 4, 5, 6, 7));
         dva[dt] = mfma32(ao, pb[ks], dva[dt]);
       }
-    // dx = P (dP - Delta)
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) pa[4 * i4 + e] = sa[4 * i4 + e] * (pa[4 * i4 + e] - d4[i4][e]);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) xb[ks][e] = f2bf(pa[8 * ks + e]);
     // dK^T += Q^T dx
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
@@ -873,6 +907,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
       if (kh == 0) dl_tiles(0);
       else dl_tiles(DT / 2);
     }
+    sa = sn;
+    pa = pn;
   }
   __syncthreads();   // stages free (the last wait was vmcnt(0))
 
