@@ -514,9 +514,10 @@ __global__ __launch_bounds__(HPW * 128) void bwd_dq_kernel(
             dgs += x;
           }
         // gate gradient of this entry: the sum over the wave's rows and keys
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) dgs += __shfl_xor(dgs, o, kWave);
-        if (lane == 0 && MODE == 1) atomicAdd(&dg[rowsel + a], dgs);
+        if constexpr (MODE == 1) {
+          const float tot = wave_sum64(dgs);
+          if (lane == 0) atomicAdd(&dg[rowsel + a], tot);
+        }
       }
       // dQ^T += K^T dx^T: the K tile read transposed, dx^T from the score registers
 #pragma unroll

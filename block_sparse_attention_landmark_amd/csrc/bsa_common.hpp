@@ -74,6 +74,25 @@ __device__ __forceinline__ float wave_sum_xor32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Sum over the 64 lanes of a wave, the result in every lane, without LDS round trips: two DPP
+// steps within quads (quad_perm [1,0,3,2], [2,3,0,1]), two rotations within 16-lane rows
+// (row_ror 4, 8; each lane then holds its row's sum), and the four row sums read by readlane.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum64(float x) {
+  x += dpp_f32<0xB1>(x);
+  x += dpp_f32<0x4E>(x);
+  x += dpp_f32<0x124>(x);
+  x += dpp_f32<0x128>(x);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // log(sigmoid(x)) without overflow: min(x, 0) - log1p(exp(-|x|))
