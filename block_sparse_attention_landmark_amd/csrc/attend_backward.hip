@@ -441,6 +441,9 @@ __global__ __launch_bounds__(HPW * 128) void bwd_dq_kernel(
       }
     }
     if (j >= 0 && j <= c) {
+      // a block before the query block, all of whose rows are in the sequence, has no masked
+      // key; for the others the masked scores are set to -inf (exp2 then gives 0)
+      const bool full = j < c && (c + 1) * kBlock <= T;
       const bf16* Kb = Ks[buf];
       const bf16* Vb = Vs[buf];
       f32x16 st[2], dp[2];
@@ -457,6 +460,15 @@ __global__ __launch_bounds__(HPW * 128) void bwd_dq_kernel(
           dp[kt] = mfma32(vfr, df[s], dp[kt]);
         }
       }
+      if (!full) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = j * kBlock + kt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+            if (!(row_ok && key <= tq)) st[kt][i] = -INFINITY;
+          }
+      }
       if constexpr (MODE == 2) {
         // HiLS: softmax of the row over this chunk's visible keys alone (P), dw = dout . o_j,
         // dx = w_j P (dP - dw); dr_j = w_j (dw_j - sum_i w_i dw_i) is formed after the loop
@@ -464,11 +476,7 @@ __global__ __launch_bounds__(HPW * 128) void bwd_dq_kernel(
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = j * kBlock + kt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-            if (!(row_ok && key <= tq)) st[kt][i] = -INFINITY;
-            mx = fmaxf(mx, st[kt][i]);
-          }
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[kt][i]);
         mx = wave_max_xor32(mx);
         const float mxs = mx == -INFINITY ? 0.0f : mx * scale_log2;
         float l = 0.0f, dwp = 0.0f;
@@ -476,7 +484,7 @@ __global__ __launch_bounds__(HPW * 128) void bwd_dq_kernel(
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const float p = st[kt][i] == -INFINITY ? 0.0f : fast_exp2(fmaf(st[kt][i], scale_log2, -mxs));
+            const float p = fast_exp2(fmaf(st[kt][i], scale_log2, -mxs));
             st[kt][i] = p;
             l += p;
             dwp = fmaf(p, dp[kt][i], dwp);
@@ -506,9 +514,7 @@ __global__ __launch_bounds__(HPW * 128) void bwd_dq_kernel(
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int key = j * kBlock + kt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-            const bool vis = row_ok && key <= tq;
-            const float p = vis ? fast_exp2(fmaf(st[kt][i], scale_log2, gb)) : 0.0f;
+            const float p = fast_exp2(fmaf(st[kt][i], scale_log2, gb));
             const float x = p * (dp[kt][i] - dlt);
             st[kt][i] = x;
             dgs += x;
@@ -799,6 +805,15 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     const float* Db = Lb + kBlock;
     const int c = Ec[st / G];
     const float gb = Eg[st / G];
+    // a query block after the key block, all of whose rows are in the sequence, sees every key;
+    // for the others the masked scores are set to -inf here (exp2 then gives 0)
+    if (!(c > j && (c + 1) * kBlock <= T)) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int tq = c * kBlock + tb + 8 * (r / 4) + r % 4;
+        if (!(tq < T && ku <= tq)) sa[r] = -INFINITY;
+      }
+    }
     // Step st + 1's stage: its Q and dO rows, the A operands of its S and dP products (in the
     // last step this reads a stage that holds no step; those products are discarded).
     const char* stn = smem + ((st + 1) % kBwdStages) * STAGE_B;
@@ -830,10 +845,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
 #pragma unroll
       for (int r = s * PC; r < (s + 1) * PC; ++r) {
         const int i4 = r / 4, e = r % 4;
-        const int tq = c * kBlock + tb + 8 * i4 + e;
-        const bool vis = tq < T && ku <= tq;
         const float bias = MODE == 2 ? -l4[i4][e] : gb - l4[i4][e] * kLog2e;
-        sa[r] = vis ? fast_exp2(fmaf(sa[r], scale_log2, bias)) : 0.0f;
+        sa[r] = fast_exp2(fmaf(sa[r], scale_log2, bias));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
