@@ -257,10 +257,14 @@ __global__ __launch_bounds__(HPW * 128) void bwd_dq_kernel(
     int n_hc, float scale_log2, float scale) {
   constexpr int NT = HPW * 128;
   constexpr int NWAVE = HPW * 2;
-  constexpr int KP = D + 8;            // tile row pitch (elements)
+  constexpr int KP = D + 8;            // V and landmark tile row pitch (elements)
+  // K tile row pitch: K is read both as rows (S) and transposed (dQ).  At D = 128, rows 12 banks
+  // apart keep the row reads free of bank conflicts and the transposed reads of 32 lanes at most
+  // two to a bank (rows 4 banks apart, as D + 8 gives, put up to four on one bank)
+  constexpr int KPK = D == 128 ? D + 24 : D + 8;
   constexpr int C8 = D / 8;
   constexpr int CPT = kBlock * C8 / NT;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][kBlock * KP];
+  __shared__ __attribute__((aligned(16))) bf16 Ks[2][kBlock * KPK];
   __shared__ __attribute__((aligned(16))) bf16 Vs[2][kBlock * KP];
   // HiLS: landmark rows of the attended chunks, and per (wave, entry, row) the retrieval weight
   // (overwritten by the retrieval-score gradient after the entry loop); dw = dout . o_j of each
@@ -413,7 +417,7 @@ __global__ __launch_bounds__(HPW * 128) void bwd_dq_kernel(
     for (int i = 0; i < CPT; ++i) {
       const int ci = tid + i * NT;
       const int row = ci / C8, c8 = ci % C8;
-      *reinterpret_cast<u32x4*>(&Ks[buf][row * KP + c8 * 8]) = kreg[i];
+      *reinterpret_cast<u32x4*>(&Ks[buf][row * KPK + c8 * 8]) = kreg[i];
       *reinterpret_cast<u32x4*>(&Vs[buf][row * KP + c8 * 8]) = vreg[i];
     }
   };
@@ -453,9 +457,9 @@ __global__ __launch_bounds__(HPW * 128) void bwd_dq_kernel(
         for (int i = 0; i < 16; ++i) st[kt][i] = dp[kt][i] = 0.0f;
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
-          const int off = (kt * 32 + l32) * KP + 16 * s + 8 * half;
-          const bf16x8 kfr = *reinterpret_cast<const bf16x8*>(&Kb[off]);
-          const bf16x8 vfr = *reinterpret_cast<const bf16x8*>(&Vb[off]);
+          const int col = 16 * s + 8 * half;
+          const bf16x8 kfr = *reinterpret_cast<const bf16x8*>(&Kb[(kt * 32 + l32) * KPK + col]);
+          const bf16x8 vfr = *reinterpret_cast<const bf16x8*>(&Vb[(kt * 32 + l32) * KP + col]);
           st[kt] = mfma32(kfr, qf[s], st[kt]);
           dp[kt] = mfma32(vfr, df[s], dp[kt]);
         }
@@ -531,11 +535,11 @@ __global__ __launch_bounds__(HPW * 128) void bwd_dq_kernel(
         bf16x8 xb;
 #pragma unroll
         for (int e = 0; e < 8; ++e) xb[e] = f2bf(st[ks / 2][8 * (ks % 2) + e]);
-        const bf16* k0 = Kb + (16 * ks + 4 * half + vrow) * KP + vcol;
+        const bf16* k0 = Kb + (16 * ks + 4 * half + vrow) * KPK + vcol;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
           const i16x4 x0 = lds_read_tr16(k0 + dt * 32);
-          const i16x4 x1 = lds_read_tr16(k0 + 8 * KP + dt * 32);
+          const i16x4 x1 = lds_read_tr16(k0 + 8 * KPK + dt * 32);
           const bf16x8 ak = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
           dqa[dt] = mfma32(ak, xb, dqa[dt]);
         }
