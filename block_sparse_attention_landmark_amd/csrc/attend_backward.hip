@@ -649,8 +649,10 @@ __device__ __forceinline__ void bwd_wait_copies(int left) {
 #undef BSA_VM
 }
 
+// (at D = 64 a wave's registers fit two workgroups per CU; at D = 128 one wave per SIMD holds
+// about 420)
 template <int D, int MODE>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     const float* __restrict__ gates, const int* __restrict__ cnt_off,
